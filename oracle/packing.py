@@ -1,0 +1,89 @@
+"""The packed record layout, written from its specification.
+
+A record holds bit-planes of 32-bit little-endian words followed (in a
+separate array) by float16 scalars:
+
+  plane p, coordinate j  ->  bit (j mod 32) of word (j div 32) of plane p
+
+Key record (TurboQuant-prod, b bits):  planes 0..b-2 carry bit p of the
+(b-1)-bit index, plane b-1 carries the QJL bits z (bit 1 <=> (S r)_i >= 0);
+scalars = (float16 n, float16 gamma).
+Value record (TurboQuant-MSE, b bits): planes 0..b-1 carry bit p of the
+index; scalars = (float16 n).
+
+This matches the storage accounting the first page uses (indices packed at b
+bits per coordinate, one sign bit per projection row, float16 norms).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def pack_bits(bits) -> np.ndarray:
+    """[N, L] booleans (L a multiple of 32) -> [N, L/32] uint32 words."""
+    bits = np.asarray(bits, dtype=bool)
+    n, length = bits.shape
+    if length % 32:
+        raise ValueError("length must be a multiple of 32")
+    b = bits.reshape(n, length // 32, 32).astype(np.uint64)
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    return (b * weights).sum(axis=2).astype(np.uint32)
+
+
+def unpack_bits(words) -> np.ndarray:
+    words = np.asarray(words, dtype=np.uint32)
+    n, w = words.shape
+    shifts = np.arange(32, dtype=np.uint32)
+    return ((words[:, :, None] >> shifts[None, None, :]) & 1).astype(bool).reshape(n, w * 32)
+
+
+def index_planes(idx, nbits: int) -> np.ndarray:
+    """[N, d] indices -> [N, nbits, d/32] words, plane p = bit p."""
+    idx = np.asarray(idx, dtype=np.int64)
+    return np.stack([pack_bits((idx >> p) & 1) for p in range(nbits)], axis=1) if nbits else \
+        np.zeros((idx.shape[0], 0, idx.shape[1] // 32), np.uint32)
+
+
+def planes_to_index(planes) -> np.ndarray:
+    planes = np.asarray(planes, dtype=np.uint32)
+    n, nb, w = planes.shape
+    idx = np.zeros((n, w * 32), dtype=np.int64)
+    for p in range(nb):
+        idx |= unpack_bits(planes[:, p, :]).astype(np.int64) << p
+    return idx
+
+
+def pack_key(code, nbits_idx: int):
+    """ProdCode -> (planes [N, nbits_idx + 1, d/32] uint32, scalars [N, 2] float16)."""
+    planes = np.concatenate([index_planes(code.idx, nbits_idx),
+                             pack_bits(code.z)[:, None, :]], axis=1)
+    scalars = np.stack([code.n, code.gamma], axis=1).astype(np.float16)
+    return planes, scalars
+
+
+def pack_value(code, nbits: int):
+    """MseCode -> (planes [N, nbits, d/32] uint32, scalars [N, 1] float16)."""
+    return index_planes(code.idx, nbits), code.n.astype(np.float16)[:, None]
+
+
+def unpack_key(planes, scalars, nbits_idx: int):
+    """-> (idx [N, d], z [N, m] bool, n [N], gamma [N]) with float16 scalars as float64."""
+    planes = np.asarray(planes, np.uint32)
+    idx = planes_to_index(planes[:, :nbits_idx, :])
+    z = unpack_bits(planes[:, nbits_idx, :])
+    s = np.asarray(scalars, np.float16).astype(np.float64)
+    return idx, z, s[:, 0], s[:, 1]
+
+
+def unpack_value(planes, scalars, nbits: int):
+    idx = planes_to_index(np.asarray(planes, np.uint32)[:, :nbits, :])
+    return idx, np.asarray(scalars, np.float16).astype(np.float64)[:, 0]
+
+
+def key_record_bytes(d_rot: int, m: int, bits: int) -> int:
+    """(b-1) index planes + m sign bits + two float16 scalars."""
+    return (bits - 1) * d_rot // 8 + m // 8 + 4
+
+
+def value_record_bytes(d_rot: int, bits: int) -> int:
+    return bits * d_rot // 8 + 2

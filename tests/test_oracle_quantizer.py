@@ -1,0 +1,120 @@
+"""Pins for oracle.quantizer and oracle.packing."""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import codebook as cb
+from oracle import packing as pk
+from oracle import quantizer as qz
+from oracle import transforms as tr
+from tests.conftest import read_golden
+from tq_inputs import gaussian_matrix, haar_orthogonal
+
+
+@pytest.mark.parametrize("bits", [1, 2])
+def test_brute_force_nearest_codeword_d8(bits):
+    # over all 2^(8b) product codewords, the nearest one is the per-coordinate
+    # cell index (the product codebook of section 6 of the explainer page)
+    d = 8
+    c, b = cb.lloyd_max(d, bits)
+    rg = np.random.default_rng(7)
+    y = rg.standard_normal((25, d))
+    y /= np.linalg.norm(y, axis=1, keepdims=True)
+    words = np.array(list(itertools.product(range(2 ** bits), repeat=d)))
+    cw = c[words]                                   # [K^d, d]
+    for v in y:
+        best = words[np.argmin(((cw - v) ** 2).sum(axis=1))]
+        assert np.array_equal(qz.cell_index(v[None, :], b)[0], best)
+
+
+def test_cell_index_ties_go_up():
+    b = np.array([-0.5, 0.0, 0.5])
+    assert qz.cell_index(np.array([[-0.5, 0.0, 0.5, -0.6, 0.7]]), b).tolist() == [[1, 2, 3, 0, 3]]
+
+
+def test_zero_vector():
+    d = 32
+    c, b = cb.lloyd_max(d, 2)
+    rot = tr.DenseRotation(haar_orthogonal(d, 0))
+    code = qz.encode_prod(np.zeros((1, d)), rot, gaussian_matrix(d, d, 0), c, b)
+    assert code.n[0] == 0
+    assert np.all(code.idx == 2)
+    assert abs(code.gamma[0] - np.float16(np.sqrt(d) * c[2])) < 1e-3
+
+
+def test_mse_falls_about_4x_per_bit_and_matches_distortion():
+    d = 128
+    rg = np.random.default_rng(5)
+    x = rg.standard_normal((3000, d)) * np.exp(rg.standard_normal(d))[None, :]
+    rot = tr.DenseRotation(haar_orthogonal(d, 11))
+    from oracle.estimator import dequantize
+    errs = []
+    for bits in (1, 2, 3, 4):
+        c, b = cb.lloyd_max(d, bits)
+        code = qz.encode_mse(x, rot, c, b, storage=False)
+        xt = dequantize(code.idx, code.n, rot, c)
+        e = ((x - xt) ** 2).sum(1) / (x ** 2).sum(1)
+        m, se = e.mean(), e.std(ddof=1) / np.sqrt(len(e))
+        # the random rotation makes any fixed input look uniform on the sphere
+        assert abs(m - d * cb.distortion(d, c, b)) < 4 * se + 1e-4
+        errs.append(m)
+    ratios = np.array(errs[:-1]) / np.array(errs[1:])
+    assert np.all((ratios > 2.9) & (ratios < 4.2))
+
+
+def test_residual_energy_is_b_minus_1_distortion():
+    # E||r||^2 = d * D(b-1) for the prod residual
+    d, bits = 64, 3
+    c, b = cb.lloyd_max(d, bits - 1)
+    rg = np.random.default_rng(9)
+    x = rg.standard_normal((4000, d))
+    rot = tr.DenseRotation(haar_orthogonal(d, 4))
+    code = qz.encode_prod(x, rot, gaussian_matrix(d, d, 4), c, b, storage=False)
+    g2 = code.gamma ** 2
+    assert abs(g2.mean() - d * cb.distortion(d, c, b)) < 4 * g2.std() / np.sqrt(len(g2))
+
+
+def test_float16_storage_rounds_to_nearest_even():
+    one = 1.0
+    ulp = 2.0 ** -10
+    v = np.array([one + ulp / 2, one + 1.5 * ulp, one + ulp / 2 + 1e-9, 65519.0, 2.0 ** -25 * 1.0000001])
+    out = qz._store(v, True)
+    assert out[0] == 1.0                 # midpoint -> even
+    assert out[1] == 1.0 + 2 * ulp       # midpoint -> even (up)
+    assert out[2] == 1.0 + ulp           # above midpoint -> up
+    assert out[3] == 65504.0
+    assert out[4] == 2.0 ** -24          # subnormal range, above the midpoint
+
+
+def test_pack_hand_built_words():
+    idx = np.zeros((1, 64), np.int64)
+    idx[0, 0] = 1          # plane 0, word 0, bit 0
+    idx[0, 33] = 2         # plane 1, word 1, bit 1
+    idx[0, 31] = 3         # both planes, word 0, bit 31
+    planes = pk.index_planes(idx, 2)
+    assert planes.shape == (1, 2, 2)
+    assert planes[0, 0].tolist() == [1 | (1 << 31), 0]
+    assert planes[0, 1].tolist() == [1 << 31, 2]
+    assert np.array_equal(pk.planes_to_index(planes), idx)
+
+
+def test_pack_roundtrip_random():
+    rg = np.random.default_rng(2)
+    idx = rg.integers(0, 8, size=(7, 128))
+    z = rg.integers(0, 2, size=(7, 128)).astype(bool)
+    code = qz.ProdCode(idx=idx, z=z, n=rg.random(7) * 10, gamma=rg.random(7), y=None, proj=None)
+    planes, scal = pk.pack_key(code, 3)
+    i2, z2, n2, g2 = pk.unpack_key(planes, scal, 3)
+    assert np.array_equal(i2, idx) and np.array_equal(z2, z)
+    assert np.allclose(n2, code.n, rtol=1e-3) and np.allclose(g2, code.gamma, rtol=1e-3, atol=1e-4)
+
+
+def test_record_sizes_reproduce_printed_compression_ratios():
+    # key = (b-1) d index bits + d sign bits + 2 float16; value = b d bits + 1 float16,
+    # against 2 float16 vectors of d = 128 per token-head
+    for bits, ratio in read_golden("compression.txt"):
+        bits = int(bits)
+        r = (2 * 128 * 2) / (pk.key_record_bytes(128, 128, bits) + pk.value_record_bytes(128, bits))
+        assert round(r, 1) == float(ratio)
+    assert pk.key_record_bytes(128, 128, 3) == 52 and pk.value_record_bytes(128, 3) == 50
