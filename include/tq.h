@@ -1,0 +1,164 @@
+/*
+ * tq.h -- C ABI of the TurboQuant hot path on MI355X (gfx950).
+ *
+ * TurboQuant (Zandieh et al., "TurboQuant: Online Vector Quantization with
+ * Near-optimal Distortion Rate", ICLR 2026) compresses vectors by a random
+ * rotation followed by per-coordinate Lloyd-Max quantization; keys also get a
+ * 1-bit QJL sign projection of the residual so that inner products with a
+ * full-precision query are estimated without bias.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device memory owned by the caller.  The library
+ *     never allocates, frees or keeps a pointer after a call returns, never
+ *     synchronises the device, and enqueues all work on the given stream
+ *     (a hipStream_t passed as void*; NULL is the null stream).
+ *   - Host pointers are read during the call only.
+ *   - Every argument is validated on the host before anything is launched.
+ *     A bad argument returns TQ_ERR_INVALID_ARG, a shape the kernels do not
+ *     implement returns TQ_ERR_UNSUPPORTED, and in both cases nothing is
+ *     launched.  A failed launch returns TQ_ERR_HIP.  tq_last_error() gives a
+ *     thread-local message for the last non-OK status.
+ *   - Calls hold no global mutable state and may be made from any thread.
+ *
+ * Packed records (the layout the pages' storage accounting implies: b bits
+ * per coordinate of codes, one sign bit per projection row, float16 norms):
+ *   bit-planes of 32-bit little-endian words, coordinate j of plane p at bit
+ *   (j mod 32) of word (j div 32):
+ *     key   (prod, b bits)  planes[0 .. b-2] = bit p of the (b-1)-bit index,
+ *                           planes[b-1]      = QJL bits, 1 <=> (S r)_i >= 0;
+ *                           scalars = { float16 n = ||x||, float16 gamma = ||r|| }
+ *     value (mse,  b bits)  planes[0 .. b-1] = bit p of the b-bit index;
+ *                           scalars = { float16 n }
+ *   A cache holds the planes of all records in one array, u32
+ *   [records][planes][d_rot/32], and the scalars in another, f16
+ *   [records][scalars]; record r of segment s is s * seg_stride + t.
+ *   At d = 128, b = 3 a key record is 48 + 4 bytes and a value 48 + 2 bytes.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1,
+  TQ_ERR_UNSUPPORTED = 2,
+  TQ_ERR_HIP = 3
+} tq_status;
+
+typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 } tq_rot;
+typedef enum { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
+
+/* Parameters of one quantizer (one for keys, one for values).
+ *   d       input dimension
+ *   d_rot   rotated dimension: == d for the dense rotation; a power of two
+ *           >= d for the Hadamard rotation (inputs are zero-padded at the end)
+ *   m       QJL projection rows; must equal d_rot (prod only, else ignored)
+ *   bits    total bit budget b: prod uses b-1 index bits plus 1 QJL bit
+ *           (2 <= b <= 4), mse uses b index bits (1 <= b <= 4)
+ *   rot     TQ_ROT_DENSE or TQ_ROT_HADAMARD
+ *   pi      device f32 [d_rot][d] row-major, y = pi * u   (dense; else NULL)
+ *   eps     device f32 [d_rot] of +1/-1                  (hadamard; else NULL)
+ *   s       device f32 [m][d_rot] row-major, the Gaussian QJL matrix (prod; NULL for mse)
+ *   centroids   HOST f32 [2^bq] ascending, bq = index bits, unit-sphere units
+ *   boundaries  HOST f32 [2^bq - 1], centroids[i] < boundaries[i] < centroids[i+1]
+ * The score and attend kernels also require the codebook to be odd-symmetric
+ * (centroids[2^bq-1-i] == -centroids[i], boundaries likewise), which every
+ * Lloyd-Max codebook of this density is (TQ_ERR_UNSUPPORTED otherwise). */
+typedef struct {
+  int d;
+  int d_rot;
+  int m;
+  int bits;
+  int rot;
+  const float* pi;
+  const float* eps;
+  const float* s;
+  const float* centroids;
+  const float* boundaries;
+} tq_params;
+
+/* A packed cache, device memory owned by the caller (layout above).
+ * seg_stride is the number of records between consecutive segments; it is
+ * used by tq_scores / tq_attend and ignored by the encoders. */
+typedef struct {
+  void* planes;
+  void* scalars;
+  int64_t seg_stride;
+} tq_cache;
+
+const char* tq_status_string(tq_status s);
+const char* tq_last_error(void);
+
+/* Lloyd-Max codebook for one coordinate of a uniformly rotated unit vector
+ * in R^d, whose density is Gamma(d/2)/(sqrt(pi) Gamma((d-1)/2)) (1-x^2)^((d-3)/2)
+ * on [-1, 1] (blog notes on the TurboQuant paper, Lemma 1 and eq. (4); the
+ * explainer page, section 5: boundaries at midpoints, centroids at the
+ * conditional means).  d == 0 gives the N(0,1) codebook (the limit of
+ * sqrt(d) * c as d grows).  Host only, float64, deterministic, exactly
+ * odd-symmetric.  d in {0} U [2, 65536], 1 <= bits <= 4.
+ * centroids: host double[2^bits] (ascending), boundaries: host double[2^bits-1]. */
+tq_status tq_build_codebook(int d, int bits, double* centroids, double* boundaries);
+
+/* Number of 32-bit plane words and float16 scalars in one record. */
+tq_status tq_key_layout(const tq_params* p, int* planes, int* words_per_plane, int* scalars);
+tq_status tq_value_layout(const tq_params* p, int* planes, int* words_per_plane, int* scalars);
+
+/* TurboQuant-prod encode of n vectors (keys) into a packed cache.
+ * Blog notes on the paper, the Q_prod definition; explainer page section 8:
+ *   n_x = ||x||, u = x/n_x (0 if n_x = 0), y = rot(u),
+ *   idx = #{boundaries <= y} at b-1 bits, r = y - c[idx], gamma = ||r||,
+ *   z = [S r >= 0]; stores float16 n_x and gamma (round to nearest even).
+ * x      device [n][ld_x] of dtype (f32 or f16), rows are vectors, ld_x >= d
+ * slot   device int64 [n] record index for each vector, or NULL for 0..n-1
+ * out    cache with planes/scalars of p's key layout; every written record
+ *        index must lie inside the caller's arrays (not checked on device)
+ * Supported: d_rot = 128 (dense or Hadamard) and Hadamard d_rot = 2048. */
+tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+                         int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
+
+/* TurboQuant-MSE encode (values): as above without the QJL stage, b index bits. */
+tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+                        int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
+
+/* Workspace bytes tq_scores needs for segs segments of group query heads. */
+size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
+
+/* Asymmetric scores of query heads against packed prod keys (explainer
+ * page section 8; blog notes, the prod estimator read with ||r||_2):
+ *   s[h][t] = n_t ( <rot(q_h), c[idx_t]> + gamma_t sqrt(pi/2)/m <S rot(q_h), 2 z_t - 1> )
+ * for query head h of segment h / group and token t < len[h / group].
+ * q       device f32 [segs*group][d]
+ * keys    packed prod cache, segment s at records s*seg_stride + t
+ * len     device int32 [segs] valid tokens per segment (<= T), or NULL for T
+ * scores  device f32 [segs*group][T]; entries with t >= len are not written
+ * ws      device workspace of at least tq_scores_workspace() bytes, 256-B aligned */
+tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
+                    const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Workspace bytes tq_attend needs. */
+size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T);
+
+/* Softmax attention of query heads over a packed cache (first page, usage
+ * pattern 1: scores from the compressed keys, softmax, weighted sum of the
+ * MSE-dequantized values):
+ *   p = softmax_t(scale * s[h][t]) over t < len,  o[h] = sum_t p_t n_v,t rot_v^T(c_v[idx_v,t])
+ * computed as one rot_v^T per head after accumulating in the rotated domain.
+ * out     device f32 [segs*group][d]; a segment with len 0 gives zeros
+ * Other arguments as for tq_scores; vals is the packed mse value cache with
+ * the same seg_stride convention. */
+tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs,
+                    int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
+                    float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

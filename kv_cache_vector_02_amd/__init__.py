@@ -1,0 +1,214 @@
+"""Python binding of libtq (the TurboQuant hot path for MI355X / gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libtq.so, reached through its C ABI (include/tq.h), with the same names.
+PyTorch provides device memory and the current stream.  There is no fallback:
+if libtq.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP = 0, 1, 2, 3
+TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
+TQ_F32, TQ_F16 = 0, 1
+
+EXPORTED = (
+    "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
+    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_scores_workspace",
+    "tq_scores", "tq_attend_workspace", "tq_attend",
+)
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+def _status_name(s):
+    return {0: "TQ_OK", 1: "TQ_ERR_INVALID_ARG", 2: "TQ_ERR_UNSUPPORTED", 3: "TQ_ERR_HIP"}.get(s, str(s))
+
+
+class tq_params(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("d_rot", ctypes.c_int), ("m", ctypes.c_int),
+                ("bits", ctypes.c_int), ("rot", ctypes.c_int),
+                ("pi", ctypes.c_void_p), ("eps", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p)]
+
+
+class tq_cache(ctypes.Structure):
+    _fields_ = [("planes", ctypes.c_void_p), ("scalars", ctypes.c_void_p),
+                ("seg_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtq.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m kv_cache_vector_02_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        P = ctypes.POINTER(tq_params)
+        L.tq_status_string.restype = ctypes.c_char_p
+        L.tq_status_string.argtypes = [ci]
+        L.tq_last_error.restype = ctypes.c_char_p
+        L.tq_last_error.argtypes = []
+        L.tq_build_codebook.argtypes = [ci, ci, vp, vp]
+        L.tq_key_layout.argtypes = [P, vp, vp, vp]
+        L.tq_value_layout.argtypes = [P, vp, vp, vp]
+        for f in (L.tq_encode_prod, L.tq_encode_mse):
+            f.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp]
+        L.tq_scores_workspace.restype = sz
+        L.tq_scores_workspace.argtypes = [P, ci, ci]
+        L.tq_scores.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp, sz, vp]
+        L.tq_attend_workspace.restype = sz
+        L.tq_attend_workspace.argtypes = [P, P, ci, ci, i64]
+        L.tq_attend.argtypes = [P, P, vp, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
+                                vp, vp, sz, vp]
+        for name in EXPORTED:
+            if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace",
+                            "tq_attend_workspace"):
+                getattr(L, name).restype = ci
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != TQ_OK:
+        raise TQError(status, lib().tq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def build_codebook(d: int, bits: int):
+    """(centroids [2^bits], boundaries [2^bits - 1]) float64, see tq_build_codebook."""
+    c = np.zeros(2 ** bits, np.float64)
+    b = np.zeros(2 ** bits - 1, np.float64)
+    _check(lib().tq_build_codebook(int(d), int(bits), c.ctypes.data, b.ctypes.data))
+    return c, b
+
+
+@dataclass
+class Params:
+    """Owns what a tq_params points to: device matrices and the host codebook."""
+    d: int
+    bits: int
+    rot: int
+    centroids: np.ndarray                 # float32 host
+    boundaries: np.ndarray                # float32 host
+    pi: Optional[object] = None           # torch float32 [d_rot][d] on the GPU
+    eps: Optional[object] = None          # torch float32 [d_rot]
+    s: Optional[object] = None            # torch float32 [m][d_rot]
+    d_rot: int = 0
+    m: int = 0
+    _c: tq_params = field(default=None, repr=False)
+
+    def __post_init__(self):
+        self.centroids = np.ascontiguousarray(self.centroids, np.float32)
+        self.boundaries = np.ascontiguousarray(self.boundaries, np.float32)
+        if not self.d_rot:
+            self.d_rot = self.d
+        if not self.m:
+            self.m = self.d_rot
+        self._c = tq_params(self.d, self.d_rot, self.m, self.bits, self.rot,
+                            None if self.pi is None else self.pi.data_ptr(),
+                            None if self.eps is None else self.eps.data_ptr(),
+                            None if self.s is None else self.s.data_ptr(),
+                            self.centroids.ctypes.data, self.boundaries.ctypes.data)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def key_layout(p: Params):
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().tq_key_layout(p.c, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def value_layout(p: Params):
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().tq_value_layout(p.c, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+@dataclass
+class Cache:
+    """A packed cache in device memory: planes int32 [records, P, W], scalars float16 [records, S]."""
+    planes: object
+    scalars: object
+    seg_stride: int = 0
+
+    @property
+    def c(self):
+        return tq_cache(self.planes.data_ptr(), self.scalars.data_ptr(), int(self.seg_stride))
+
+
+def alloc_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
+    import torch
+    P, W, S = layout
+    return Cache(torch.zeros((records, P, W), dtype=torch.int32, device=device),
+                 torch.zeros((records, S), dtype=torch.float16, device=device), seg_stride)
+
+
+def _dtype_code(x):
+    import torch
+    if x.dtype == torch.float16:
+        return TQ_F16
+    if x.dtype == torch.float32:
+        return TQ_F32
+    raise TypeError("x must be float16 or float32")
+
+
+def encode_prod(p: Params, x, out: Cache, slot=None, stream=None):
+    """tq_encode_prod on the rows of x (2-D, row stride x.stride(0))."""
+    _check(lib().tq_encode_prod(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
+                                _ptr(slot), _stream(stream)))
+
+
+def encode_mse(p: Params, x, out: Cache, slot=None, stream=None):
+    _check(lib().tq_encode_mse(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
+                               _ptr(slot), _stream(stream)))
+
+
+def scores_workspace(kp: Params, segs: int, group: int) -> int:
+    return int(lib().tq_scores_workspace(kp.c, segs, group))
+
+
+def scores(kp: Params, q, segs: int, group: int, keys: Cache, T: int, out, ws, length=None,
+           stream=None):
+    _check(lib().tq_scores(kp.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def attend_workspace(kp: Params, vp: Params, segs: int, group: int, T: int) -> int:
+    return int(lib().tq_attend_workspace(kp.c, vp.c, segs, group, int(T)))
+
+
+def attend(kp: Params, vp: Params, q, segs: int, group: int, keys: Cache, vals: Cache, T: int,
+           scale: float, out, ws, length=None, stream=None):
+    _check(lib().tq_attend(kp.c, vp.c, _ptr(q), segs, group, keys.c, vals.c, _ptr(length), int(T),
+                           float(scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)))

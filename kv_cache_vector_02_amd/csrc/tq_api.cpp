@@ -1,0 +1,204 @@
+// Host side of the C ABI: argument validation, codebook marshalling, dispatch.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tq_status fail(tq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+tq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TQ_OK;
+  return fail(TQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int index_bits(const tq_params* p, bool prod) { return prod ? p->bits - 1 : p->bits; }
+
+// Common checks of a parameter block; fills the kernel codebook.
+tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool need_symmetric) {
+  if (!p) return fail(TQ_ERR_INVALID_ARG, "params is NULL");
+  if (p->d < 1) return fail(TQ_ERR_INVALID_ARG, "d must be >= 1 (got %d)", p->d);
+  if (p->rot != TQ_ROT_DENSE && p->rot != TQ_ROT_HADAMARD)
+    return fail(TQ_ERR_INVALID_ARG, "rot must be TQ_ROT_DENSE or TQ_ROT_HADAMARD");
+  if (p->rot == TQ_ROT_DENSE) {
+    if (p->d_rot != p->d) return fail(TQ_ERR_INVALID_ARG, "dense rotation needs d_rot == d");
+    if (!p->pi) return fail(TQ_ERR_INVALID_ARG, "dense rotation needs pi");
+    if (!aligned(p->pi, 16)) return fail(TQ_ERR_INVALID_ARG, "pi must be 16-byte aligned");
+  } else {
+    if (p->d_rot < p->d || (p->d_rot & (p->d_rot - 1)))
+      return fail(TQ_ERR_INVALID_ARG, "hadamard d_rot must be a power of two >= d");
+    if (!p->eps) return fail(TQ_ERR_INVALID_ARG, "hadamard rotation needs eps");
+  }
+  if (prod) {
+    if (p->bits < 2 || p->bits > 4)
+      return fail(TQ_ERR_INVALID_ARG, "prod bits must be in [2, 4] (got %d)", p->bits);
+    if (p->m != p->d_rot) return fail(TQ_ERR_INVALID_ARG, "m must equal d_rot");
+    if (!p->s) return fail(TQ_ERR_INVALID_ARG, "prod needs the QJL matrix s");
+    if (!aligned(p->s, 16)) return fail(TQ_ERR_INVALID_ARG, "s must be 16-byte aligned");
+  } else if (p->bits < 1 || p->bits > 4) {
+    return fail(TQ_ERR_INVALID_ARG, "mse bits must be in [1, 4] (got %d)", p->bits);
+  }
+  if (!p->centroids || !p->boundaries)
+    return fail(TQ_ERR_INVALID_ARG, "codebook centroids/boundaries are NULL");
+  const int bq = index_bits(p, prod);
+  const int K = 1 << bq;
+  std::memset(cb, 0, sizeof(*cb));
+  for (int i = 0; i < K; ++i) {
+    float c = p->centroids[i];
+    if (!std::isfinite(c)) return fail(TQ_ERR_INVALID_ARG, "centroid %d is not finite", i);
+    cb->c[i] = c;
+  }
+  for (int i = 0; i + 1 < K; ++i) {
+    float b = p->boundaries[i];
+    if (!(p->centroids[i] < b && b < p->centroids[i + 1]))
+      return fail(TQ_ERR_INVALID_ARG, "boundary %d must lie strictly between centroids %d and %d",
+                  i, i, i + 1);
+    cb->b[i] = b;
+  }
+  if (need_symmetric) {
+    for (int i = 0; i < K; ++i)
+      if (p->centroids[K - 1 - i] != -p->centroids[i])
+        return fail(TQ_ERR_UNSUPPORTED, "scores/attend need an odd-symmetric codebook");
+    for (int i = 0; i + 1 < K; ++i)
+      if (p->boundaries[K - 2 - i] != -p->boundaries[i])
+        return fail(TQ_ERR_UNSUPPORTED, "scores/attend need odd-symmetric boundaries");
+  }
+  return TQ_OK;
+}
+
+tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, int64_t n,
+                 int64_t ld_x, tq_cache out, const int64_t* slot, void* stream) {
+  tq::EncodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  tq_status st = check_params(p, prod, &a.cb, false);
+  if (st != TQ_OK) return st;
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n must be >= 0");
+  if (dtype != TQ_F32 && dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "dtype must be TQ_F32 or TQ_F16");
+  if (ld_x < p->d) return fail(TQ_ERR_INVALID_ARG, "ld_x must be >= d");
+  const size_t esz = dtype == TQ_F16 ? 2 : 4;
+  if (n == 0) return TQ_OK;
+  if (!x || !out.planes || !out.scalars) return fail(TQ_ERR_INVALID_ARG, "x and the cache arrays must be non-NULL");
+  if (!aligned(x, 16) || (ld_x * esz) % 16)
+    return fail(TQ_ERR_INVALID_ARG, "x must be 16-byte aligned with rows a multiple of 16 bytes");
+  if (!aligned(out.planes, 16) || !aligned(out.scalars, 4))
+    return fail(TQ_ERR_INVALID_ARG, "cache planes must be 16-byte and scalars 4-byte aligned");
+  if (slot && !aligned(slot, 8)) return fail(TQ_ERR_INVALID_ARG, "slot must be 8-byte aligned");
+  a.x = x;
+  a.f16_in = dtype == TQ_F16;
+  a.n = n;
+  a.ld_x = ld_x;
+  a.d = p->d;
+  a.pi = p->pi;
+  a.eps = p->eps;
+  a.s = prod ? p->s : nullptr;
+  a.bq = index_bits(p, prod);
+  a.prod = prod;
+  a.planes = (uint32_t*)out.planes;
+  a.scalars = (uint16_t*)out.scalars;
+  a.slot = slot;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->rot == TQ_ROT_DENSE && p->d == 128)
+    return hip_status(tq::launch_encode_dense128(a, s), "encode launch");
+  return fail(TQ_ERR_UNSUPPORTED, "encode supports the dense rotation at d = 128 (got rot %d, d %d, d_rot %d)",
+              p->rot, p->d, p->d_rot);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP";
+  }
+  return "unknown tq_status";
+}
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+tq_status tq_build_codebook(int d, int bits, double* centroids, double* boundaries) {
+  if (!(d == 0 || (d >= 2 && d <= 65536))) return fail(TQ_ERR_INVALID_ARG, "d must be 0 or in [2, 65536]");
+  if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "bits must be in [1, 4]");
+  if (!centroids || !boundaries) return fail(TQ_ERR_INVALID_ARG, "output arrays are NULL");
+  return tq::build_codebook(d, bits, centroids, boundaries);
+}
+
+tq_status tq_key_layout(const tq_params* p, int* planes, int* words, int* scalars) {
+  tq::Codebook cb;
+  tq_status st = check_params(p, true, &cb, false);
+  if (st != TQ_OK) return st;
+  if (planes) *planes = p->bits;
+  if (words) *words = p->d_rot / 32;
+  if (scalars) *scalars = 2;
+  return TQ_OK;
+}
+
+tq_status tq_value_layout(const tq_params* p, int* planes, int* words, int* scalars) {
+  tq::Codebook cb;
+  tq_status st = check_params(p, false, &cb, false);
+  if (st != TQ_OK) return st;
+  if (planes) *planes = p->bits;
+  if (words) *words = p->d_rot / 32;
+  if (scalars) *scalars = 1;
+  return TQ_OK;
+}
+
+tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+                         tq_cache out, const int64_t* slot, void* stream) {
+  return encode(p, true, x, dtype, n, ld_x, out, slot, stream);
+}
+
+tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+                        tq_cache out, const int64_t* slot, void* stream) {
+  return encode(p, false, x, dtype, n, ld_x, out, slot, stream);
+}
+
+size_t tq_scores_workspace(const tq_params* kp, int segs, int group) {
+  (void)kp;
+  if (segs <= 0 || group <= 0) return 0;
+  return tq::scores128_workspace(segs, group);
+}
+
+tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
+                    const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
+                    void* stream) {
+  (void)kp; (void)q; (void)segs; (void)group; (void)keys; (void)len; (void)T; (void)scores;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return fail(TQ_ERR_UNSUPPORTED, "tq_scores is not built yet");
+}
+
+size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T) {
+  (void)kp; (void)vp;
+  if (segs <= 0 || group <= 0 || T <= 0) return 0;
+  return tq::attend128_workspace(segs, group, T);
+}
+
+tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs, int group,
+                    tq_cache keys, tq_cache vals, const int32_t* len, int64_t T, float scale,
+                    float* out, void* ws, size_t ws_bytes, void* stream) {
+  (void)kp; (void)vp; (void)q; (void)segs; (void)group; (void)keys; (void)vals; (void)len;
+  (void)T; (void)scale; (void)out; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(TQ_ERR_UNSUPPORTED, "tq_attend is not built yet");
+}
+
+}  // extern "C"

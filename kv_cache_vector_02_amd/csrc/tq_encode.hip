@@ -1,0 +1,326 @@
+// TurboQuant encode kernels for gfx950 (MI355X), dense rotation, d = 128.
+//
+// Per vector x (blog notes on the TurboQuant paper: Q_mse and Q_prod; the
+// explainer page, sections 6 and 8):
+//   n = ||x||, u = x / n, y = Pi u, idx_j = #{beta_k <= y_j}           (Q_mse)
+//   r = y - c[idx], gamma = ||r||, z = [S r >= 0]                        (Q_prod)
+//
+// Layout of the work: one wave owns a tile of 32 vectors (NT = 1) or 64
+// (NT = 2).  Both rotations are dense 128x128 contractions on the matrix cores
+// (v_mfma_f32_32x32x16_f16):
+//   GEMM1  Y^T = (16 Pi) . X^T      A = Pi fragments from LDS, B = x rows
+//   GEMM2  Z^T = S . (256 R)^T      A = S fragments from LDS, B = residuals
+// Float32 accuracy comes from splitting the fixed matrices into fp16 hi + lo
+// (and fp32 operands likewise): Pi_hi x + Pi_lo x for fp16 inputs (x is exact
+// in fp16), three products for fp32 operands (the lo*lo term, ~2^-22, is
+// dropped).  The power-of-two prescales keep the lo parts out of the fp16
+// subnormal range and are undone exactly.
+//
+// The A rows are permuted so that, in the accumulator layout, lane
+// (v = lane % 32, h = lane / 32) holds coordinates 64 h + 16 mt + r of vector
+// v in register r of row tile mt.  A lane therefore owns the whole 32-bit
+// plane words 2h and 2h+1 of its vector: bit packing is a shift-or per
+// coordinate with no cross-lane traffic, and the GEMM1 accumulators are
+// already in the B layout GEMM2 needs (K slot e of MFMA ks2 in lane half h is
+// coordinate 64 h + 8 ks2 + e, the same map GEMM1 uses for x).
+#include <algorithm>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int D = 128;
+constexpr float PI_SCALE = 16.f;   // 2^4
+constexpr float R_SCALE = 256.f;   // 2^8
+constexpr float U_SCALE = 64.f;    // 2^6 (fp32 inputs, after normalising)
+constexpr int FRAGS = 4 * 8 * 2 * 64;  // half8 per 128x128 matrix (hi and lo)
+
+__device__ __forceinline__ int frag_index(int mt, int ks, int part, int lane) {
+  return ((mt * 8 + ks) * 2 + part) * 64 + lane;
+}
+
+// Output row rho of a 32-row tile -> the coordinate it stands for.
+__device__ __forceinline__ int row_coord(int rho, int mt) {
+  int h = (rho >> 2) & 1;
+  int r = ((rho >> 3) << 2) | (rho & 3);
+  return 64 * h + 16 * mt + r;
+}
+
+// M is [128][128] float32 row-major.  Fragment (mt, ks) of lane l holds
+// scale * M[row_coord(l % 32, mt)][64 (l / 32) + 8 ks + e], e = 0..7, as hi, lo.
+__device__ void build_frags(half8* lds, const float* __restrict__ M, float scale) {
+  for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
+    const int lane = f & 63, ks = (f >> 6) & 7, mt = f >> 9;
+    const int row = row_coord(lane & 31, mt);
+    const int k0 = 64 * (lane >> 5) + 8 * ks;
+    const float4* src = reinterpret_cast<const float4*>(M + row * D + k0);
+    const float4 p = src[0], q = src[1];
+    const float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+    half8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      _Float16 h, l;
+      split_f16(v[e] * scale, h, l);
+      hi[e] = h;
+      lo[e] = l;
+    }
+    lds[frag_index(mt, ks, 0, lane)] = hi;
+    lds[frag_index(mt, ks, 1, lane)] = lo;
+  }
+}
+
+template <int BQ>
+__device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, float& chat) {
+  idx = 0;
+  chat = cb.c[0];
+#pragma unroll
+  for (int k = 0; k < (1 << BQ) - 1; ++k) {
+    const bool ge = y >= cb.b[k];
+    idx += ge ? 1 : 0;
+    chat = ge ? cb.c[k + 1] : chat;
+  }
+}
+
+template <bool PROD, int BQ, bool F16IN, int NT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
+  extern __shared__ half8 lds[];
+  half8* fpi = lds;
+  half8* fs = lds + FRAGS;
+  build_frags(fpi, a.pi, PI_SCALE);
+  if (PROD) build_frags(fs, a.s, 1.f);
+  __syncthreads();
+
+  constexpr int P = PROD ? BQ + 1 : BQ;     // planes per record
+  constexpr int VT = 32 * NT;               // vectors per wave tile
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int v = lane & 31;
+  const int h = lane >> 5;
+  const int64_t ntiles = (a.n + VT - 1) / VT;
+
+  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles;
+       tile += (int64_t)gridDim.x * WAVES) {
+    // The fragment reads below are loop-invariant; without this barrier the
+    // compiler hoists all of them (256 registers) out of the loop and spills.
+    asm volatile("" ::: "memory");
+    // ---- load 64 coordinates (64 h .. 64 h + 63) of each vector, norms ----
+    half8 xh[NT][8];
+    half8 xl[NT][8];   // fp32 inputs only
+    float yscale[NT], nrm[NT];
+    int64_t vec[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      vec[nt] = tile * VT + nt * 32 + v;
+      const bool valid = vec[nt] < a.n;
+      float s2 = 0.f;
+      if (F16IN) {
+        const uint4* src = reinterpret_cast<const uint4*>(
+            static_cast<const _Float16*>(a.x) + (valid ? vec[nt] : 0) * a.ld_x + 64 * h);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          uint4 w = valid ? src[ks] : make_uint4(0, 0, 0, 0);
+          half8 hv = __builtin_bit_cast(half8, w);
+          xh[nt][ks] = hv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s2 += (float)hv[e] * (float)hv[e];
+        }
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(
+            static_cast<const float*>(a.x) + (valid ? vec[nt] : 0) * a.ld_x + 64 * h);
+        float xv[64];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float4 w = valid ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+          xv[4 * i] = w.x; xv[4 * i + 1] = w.y; xv[4 * i + 2] = w.z; xv[4 * i + 3] = w.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 64; ++i) s2 += xv[i] * xv[i];
+        s2 += shfl_xor_f(s2, 32);
+        const float n = sqrtf(s2);
+        const float inv = n > 0.f ? U_SCALE / n : 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            _Float16 hi, lo;
+            split_f16(xv[8 * ks + e] * inv, hi, lo);
+            xh[nt][ks][e] = hi;
+            xl[nt][ks][e] = lo;
+          }
+        }
+        nrm[nt] = n;
+        yscale[nt] = 1.f / (U_SCALE * PI_SCALE);
+        continue;
+      }
+      s2 += shfl_xor_f(s2, 32);
+      const float n = sqrtf(s2);
+      nrm[nt] = n;
+      yscale[nt] = n > 0.f ? 1.f / (n * PI_SCALE) : 0.f;
+    }
+
+    // ---- GEMM1 per row tile, then quantize, pack, residual ----
+    uint32_t iw[NT][BQ][2];
+    half8 rh[NT][8], rl[NT][8];
+    float g2[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      g2[nt] = 0.f;
+#pragma unroll
+      for (int p = 0; p < BQ; ++p) iw[nt][p][0] = iw[nt][p][1] = 0u;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const half8 ahi = fpi[frag_index(mt, ks, 0, lane)];
+        const half8 alo = fpi[frag_index(mt, ks, 1, lane)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[nt] = mfma32x32x16(ahi, xh[nt][ks], acc[nt]);
+          acc[nt] = mfma32x32x16(alo, xh[nt][ks], acc[nt]);
+          if (!F16IN) acc[nt] = mfma32x32x16(ahi, xl[nt][ks], acc[nt]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float y = acc[nt][r] * yscale[nt];
+          int idx;
+          float chat;
+          quantize<BQ>(y, a.cb, idx, chat);
+          const int pos = 16 * (mt & 1) + r;
+#pragma unroll
+          for (int p = 0; p < BQ; ++p) iw[nt][p][mt >> 1] |= (uint32_t)((idx >> p) & 1) << pos;
+          if (PROD) {
+            const float res = y - chat;
+            g2[nt] += res * res;
+            _Float16 hi, lo;
+            split_f16(res * R_SCALE, hi, lo);
+            const int ks2 = 2 * mt + (r >> 3);
+            rh[nt][ks2][r & 7] = hi;
+            rl[nt][ks2][r & 7] = lo;
+          }
+        }
+      }
+    }
+
+    // ---- GEMM2 (QJL signs) ----
+    uint32_t sw[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sw[nt][0] = sw[nt][1] = 0u;
+    if (PROD) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        f32x16 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const half8 shi = fs[frag_index(it, ks, 0, lane)];
+          const half8 slo = fs[frag_index(it, ks, 1, lane)];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[nt] = mfma32x32x16(shi, rh[nt][ks], acc[nt]);
+            acc[nt] = mfma32x32x16(slo, rh[nt][ks], acc[nt]);
+            acc[nt] = mfma32x32x16(shi, rl[nt][ks], acc[nt]);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sw[nt][it >> 1] |= (acc[nt][r] >= 0.f ? 1u : 0u) << (16 * (it & 1) + r);
+        }
+      }
+    }
+
+    // ---- store records ----
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float g = 0.f;
+      if (PROD) {
+        float t = g2[nt] + shfl_xor_f(g2[nt], 32);
+        g = sqrtf(t);
+      }
+      if (vec[nt] < a.n) {
+        const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
+        uint2* dst = reinterpret_cast<uint2*>(a.planes + rec * (P * 4)) + h;
+#pragma unroll
+        for (int p = 0; p < BQ; ++p) dst[2 * p] = make_uint2(iw[nt][p][0], iw[nt][p][1]);
+        if (PROD) dst[2 * BQ] = make_uint2(sw[nt][0], sw[nt][1]);
+        if (h == 0) {
+          if (PROD) {
+            reinterpret_cast<uint32_t*>(a.scalars)[rec] =
+                (uint32_t)f16_bits(nrm[nt]) | ((uint32_t)f16_bits(g) << 16);
+          } else {
+            a.scalars[rec] = f16_bits(nrm[nt]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool PROD, int BQ, bool F16IN>
+hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
+  constexpr int NT = 1, WAVES = 8;
+  auto kern = encode_dense128<PROD, BQ, F16IN, NT, WAVES>;
+  const size_t lds = (PROD ? 2 : 1) * FRAGS * sizeof(half8);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 256;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t ntiles = (a.n + 32 * NT - 1) / (32 * NT);
+  const int64_t want = (ntiles + WAVES - 1) / WAVES;
+  const int blocks_per_cu = PROD ? 1 : 2;
+  const int grid = (int)std::min<int64_t>(want, (int64_t)cus * blocks_per_cu);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream) {
+  if (a.prod) {
+    if (a.f16_in) {
+      switch (a.bq) {
+        case 1: return launch_one<true, 1, true>(a, stream);
+        case 2: return launch_one<true, 2, true>(a, stream);
+        case 3: return launch_one<true, 3, true>(a, stream);
+      }
+    } else {
+      switch (a.bq) {
+        case 1: return launch_one<true, 1, false>(a, stream);
+        case 2: return launch_one<true, 2, false>(a, stream);
+        case 3: return launch_one<true, 3, false>(a, stream);
+      }
+    }
+  } else {
+    if (a.f16_in) {
+      switch (a.bq) {
+        case 1: return launch_one<false, 1, true>(a, stream);
+        case 2: return launch_one<false, 2, true>(a, stream);
+        case 3: return launch_one<false, 3, true>(a, stream);
+        case 4: return launch_one<false, 4, true>(a, stream);
+      }
+    } else {
+      switch (a.bq) {
+        case 1: return launch_one<false, 1, false>(a, stream);
+        case 2: return launch_one<false, 2, false>(a, stream);
+        case 3: return launch_one<false, 3, false>(a, stream);
+        case 4: return launch_one<false, 4, false>(a, stream);
+      }
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

@@ -1,0 +1,78 @@
+// Internal declarations shared by the host API and the HIP kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+tq_status build_codebook(int d, int bits, double* centroids, double* boundaries);
+
+// Codebook by value: it travels in the kernel argument buffer (scalar
+// registers / constant cache), never in device memory.
+struct Codebook {
+  float c[16];   // centroids, ascending
+  float b[16];   // boundaries (2^bq - 1 used)
+};
+
+struct EncodeArgs {
+  const void* x;
+  int f16_in;          // 1: x is float16, 0: float32
+  int64_t n;
+  int64_t ld_x;        // elements between rows of x
+  int d;               // input dimension (<= d_rot)
+  const float* pi;     // dense rotation [d_rot][d]
+  const float* eps;    // hadamard signs [d_rot]
+  const float* s;      // QJL matrix [d_rot][d_rot] (prod only)
+  Codebook cb;
+  int bq;              // index bits
+  int prod;            // 1: keys (prod), 0: values (mse)
+  uint32_t* planes;    // [records][P][d_rot/32]
+  uint16_t* scalars;   // [records][S] float16 bit patterns
+  const int64_t* slot; // record of vector i, or null
+};
+
+hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream);
+
+struct ScoreArgs {
+  const float* q;        // [segs*group][d]
+  int segs, group, d;
+  const float* pi;       // rotation of the keys (dense)
+  const float* eps;      // hadamard signs
+  int rot;
+  const float* s;        // QJL matrix
+  Codebook cb;
+  int bq;
+  const uint32_t* planes;
+  const uint16_t* scalars;
+  int64_t seg_stride;
+  const int32_t* len;
+  int64_t T;
+  float* scores;
+  void* ws;
+};
+
+hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream);
+size_t scores128_workspace(int segs, int group);
+
+struct AttendArgs {
+  ScoreArgs k;           // query + key side (scores field unused)
+  const float* pi_v;     // value rotation (dense)
+  const float* eps_v;
+  int rot_v;
+  Codebook cb_v;
+  int bq_v;
+  const uint32_t* planes_v;
+  const uint16_t* scalars_v;
+  int64_t seg_stride_v;
+  float scale;
+  float* out;
+  void* ws;
+};
+
+hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream);
+size_t attend128_workspace(int segs, int group, int64_t T);
+
+}  // namespace tq

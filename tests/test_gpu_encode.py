@@ -1,0 +1,93 @@
+"""GPU parity of tq_encode_prod / tq_encode_mse against the oracle."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import Setup, compare_encode, torch
+from tq_inputs import kv_tensor, tiny_vectors
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def test_tiny_config_prod_b3_fp32():
+    # N=4096, d=128, fp32 N(0,1) with 4 outlier channels x20, seed 0; prod at b=3
+    _log("encode tiny prod b3 fp32")
+    x = tiny_vectors(4096, 128, seed=0)
+    st = Setup(bits=3, prod=True, seed=0)
+    planes, scal = st.encode_gpu(x)
+    stats = compare_encode(st, planes, scal, st.encode_oracle(x))
+    _log(f"  {stats}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_prod_bits_dtypes_ragged(bits, dtype):
+    _log(f"encode prod b{bits} {dtype} ragged")
+    x = kv_tensor(1, 1, 1000, 128, seed=1)[0, 0]
+    x = x if dtype == "f16" else x.astype(np.float32)
+    st = Setup(bits=bits, prod=True, seed=1)
+    planes, scal = st.encode_gpu(x)
+    compare_encode(st, planes, scal, st.encode_oracle(x))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_mse_bits_dtypes_ragged(bits, dtype):
+    _log(f"encode mse b{bits} {dtype} ragged")
+    x = kv_tensor(1, 1, 777, 128, seed=2, value=True)[0, 0]
+    x = x if dtype == "f16" else x.astype(np.float32)
+    st = Setup(bits=bits, prod=False, seed=2, purpose_pi=4)
+    planes, scal = st.encode_gpu(x)
+    compare_encode(st, planes, scal, st.encode_oracle(x))
+
+
+def test_zero_vectors_and_slots():
+    _log("encode zero vectors + slots")
+    rg = np.random.default_rng(3)
+    x = rg.standard_normal((70, 128)).astype(np.float32)
+    x[[0, 5, 69]] = 0.0
+    slot = rg.permutation(100)[:70]
+    st = Setup(bits=3, prod=True, seed=3)
+    planes, scal = st.encode_gpu(x, slot=slot, records=100)
+    ocode = st.encode_oracle(x)
+    compare_encode(st, planes[slot], scal[slot], ocode)
+    untouched = np.setdiff1d(np.arange(100), slot)
+    assert not planes[untouched].any() and not scal[untouched].view(np.uint16).any()
+    assert np.all(scal[slot[[0, 5, 69]], 0] == 0)
+
+
+def test_strided_rows():
+    _log("encode strided rows")
+    T = torch()
+    x = kv_tensor(1, 1, 300, 128, seed=4)[0, 0]
+    big = np.zeros((300, 192), np.float16)
+    big[:, :128] = x
+    st = Setup(bits=3, prod=True, seed=4)
+    xt = T.from_numpy(big).cuda()[:, :128]
+    import kv_cache_vector_02_amd as tq
+    cache = tq.alloc_cache(st.layout(), 300)
+    tq.encode_prod(st.params, xt, cache)
+    T.cuda.synchronize()
+    planes = cache.planes.cpu().numpy().view(np.uint32)
+    compare_encode(st, planes, cache.scalars.cpu().numpy(), st.encode_oracle(x))
+
+
+def test_qwen_shaped_full_size_sampled():
+    # 36 layers x 2 KV heads x 8192 tokens x 128, fp16, prod b=3 keys and mse b=3
+    # values at full size in one launch each; the oracle checks a seeded sample
+    _log("encode qwen-shaped full size (sampled)")
+    T = torch()
+    k = kv_tensor(36, 2, 8192, 128, seed=1).reshape(-1, 128)
+    v = kv_tensor(36, 2, 8192, 128, seed=1, value=True).reshape(-1, 128)
+    rg = np.random.default_rng(0)
+    sample = np.sort(rg.choice(k.shape[0], 3000, replace=False))
+    sample[-1] = k.shape[0] - 1
+    for x, prod in ((k, True), (v, False)):
+        st = Setup(bits=3, prod=prod, seed=1, purpose_pi=2 if prod else 4)
+        planes, scal = st.encode_gpu(x)
+        compare_encode(st, planes[sample], scal[sample], st.encode_oracle(x[sample]))
+        del planes, scal
+        T.cuda.empty_cache()
