@@ -182,9 +182,39 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group) {
 tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
                     const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
                     void* stream) {
-  (void)kp; (void)q; (void)segs; (void)group; (void)keys; (void)len; (void)T; (void)scores;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return fail(TQ_ERR_UNSUPPORTED, "tq_scores is not built yet");
+  tq::ScoreArgs a;
+  std::memset(&a, 0, sizeof(a));
+  tq_status st = check_params(kp, true, &a.cb, true);
+  if (st != TQ_OK) return st;
+  if (segs < 0 || group < 1 || T < 0) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
+  if (segs == 0 || T == 0) return TQ_OK;
+  if (kp->d_rot != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports d_rot = 128 (got %d)", kp->d_rot);
+  if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports up to 16 query heads per segment");
+  if (!q || !keys.planes || !keys.scalars || !scores || !ws)
+    return fail(TQ_ERR_INVALID_ARG, "q, keys, scores and ws must be non-NULL");
+  if (keys.seg_stride < T && segs > 1) return fail(TQ_ERR_INVALID_ARG, "keys.seg_stride must be >= T");
+  if (!aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(ws, 256) || !aligned(q, 4) ||
+      !aligned(scores, 4))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (planes 16 B, scalars 4 B, ws 256 B)");
+  const size_t need = tq::scores128_workspace(segs, group);
+  if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
+  a.q = q;
+  a.segs = segs;
+  a.group = group;
+  a.d = kp->d;
+  a.pi = kp->pi;
+  a.eps = kp->eps;
+  a.rot = kp->rot;
+  a.s = kp->s;
+  a.bq = kp->bits - 1;
+  a.planes = (const uint32_t*)keys.planes;
+  a.scalars = (const uint16_t*)keys.scalars;
+  a.seg_stride = keys.seg_stride;
+  a.len = len;
+  a.T = T;
+  a.scores = scores;
+  a.ws = ws;
+  return hip_status(tq::launch_scores128(a, (hipStream_t)stream), "scores launch");
 }
 
 size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T) {
