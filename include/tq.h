@@ -23,14 +23,16 @@
  * Packed records (the layout the pages' storage accounting implies: b bits
  * per coordinate of codes, one sign bit per projection row, float16 norms):
  *   bit-planes of 32-bit little-endian words, coordinate j of plane p at bit
- *   (j mod 32) of word (j div 32):
- *     key   (prod, b bits)  planes[0 .. b-2] = bit p of the (b-1)-bit index,
- *                           planes[b-1]      = QJL bits, 1 <=> (S r)_i >= 0;
+ *   (j mod 32) of word (j div 32) of that plane; the P planes of a record are
+ *   interleaved word by word, word w of plane p being u32 number w * P + p of
+ *   the record (the P words covering one group of 32 coordinates are adjacent):
+ *     key   (prod, b bits)  planes 0 .. b-2 = bit p of the (b-1)-bit index,
+ *                           plane b-1      = QJL bits, 1 <=> (S r)_i >= 0;
  *                           scalars = { float16 n = ||x||, float16 gamma = ||r|| }
- *     value (mse,  b bits)  planes[0 .. b-1] = bit p of the b-bit index;
+ *     value (mse,  b bits)  planes 0 .. b-1 = bit p of the b-bit index;
  *                           scalars = { float16 n }
- *   A cache holds the planes of all records in one array, u32
- *   [records][planes][d_rot/32], and the scalars in another, f16
+ *   A cache holds the plane words of all records in one array, u32
+ *   [records][d_rot/32][P], and the scalars in another, f16
  *   [records][scalars]; record r of segment s is s * seg_stride + t.
  *   At d = 128, b = 3 a key record is 48 + 4 bytes and a value 48 + 2 bytes.
  */

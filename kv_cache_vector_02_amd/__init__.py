@@ -156,7 +156,8 @@ def value_layout(p: Params):
 
 @dataclass
 class Cache:
-    """A packed cache in device memory: planes int32 [records, P, W], scalars float16 [records, S]."""
+    """A packed cache in device memory: plane words int32 [records, W, P] (word w of
+    plane p at w * P + p), scalars float16 [records, S]."""
     planes: object
     scalars: object
     seg_stride: int = 0
@@ -169,7 +170,7 @@ class Cache:
 def alloc_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
     import torch
     P, W, S = layout
-    return Cache(torch.zeros((records, P, W), dtype=torch.int32, device=device),
+    return Cache(torch.zeros((records, W, P), dtype=torch.int32, device=device),
                  torch.zeros((records, S), dtype=torch.float16, device=device), seg_stride)
 
 

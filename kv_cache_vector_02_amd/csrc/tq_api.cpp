@@ -45,6 +45,7 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
     if (p->d_rot < p->d || (p->d_rot & (p->d_rot - 1)))
       return fail(TQ_ERR_INVALID_ARG, "hadamard d_rot must be a power of two >= d");
     if (!p->eps) return fail(TQ_ERR_INVALID_ARG, "hadamard rotation needs eps");
+    if (!aligned(p->eps, 16)) return fail(TQ_ERR_INVALID_ARG, "eps must be 16-byte aligned");
   }
   if (prod) {
     if (p->bits < 2 || p->bits > 4)
@@ -188,14 +189,15 @@ tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq
   if (st != TQ_OK) return st;
   if (segs < 0 || group < 1 || T < 0) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
   if (segs == 0 || T == 0) return TQ_OK;
-  if (kp->d_rot != 128) return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports d_rot = 128 (got %d)", kp->d_rot);
+  if (kp->d != 128 || kp->d_rot != 128)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports d = d_rot = 128 (got %d, %d)", kp->d, kp->d_rot);
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports up to 16 query heads per segment");
   if (!q || !keys.planes || !keys.scalars || !scores || !ws)
     return fail(TQ_ERR_INVALID_ARG, "q, keys, scores and ws must be non-NULL");
   if (keys.seg_stride < T && segs > 1) return fail(TQ_ERR_INVALID_ARG, "keys.seg_stride must be >= T");
-  if (!aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(ws, 256) || !aligned(q, 4) ||
+  if (!aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(ws, 256) || !aligned(q, 16) ||
       !aligned(scores, 4))
-    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (planes 16 B, scalars 4 B, ws 256 B)");
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
   const size_t need = tq::scores128_workspace(segs, group);
   if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
   a.q = q;

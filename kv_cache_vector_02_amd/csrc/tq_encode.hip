@@ -19,7 +19,8 @@
 // The A rows are permuted so that, in the accumulator layout, lane
 // (v = lane % 32, h = lane / 32) holds coordinates 64 h + 16 mt + r of vector
 // v in register r of row tile mt.  A lane therefore owns the whole 32-bit
-// plane words 2h and 2h+1 of its vector: bit packing is a shift-or per
+// plane words 2h and 2h+1 of its vector (a contiguous 8P bytes of the record,
+// whose planes are interleaved word by word): bit packing is a shift-or per
 // coordinate with no cross-lane traffic, and the GEMM1 accumulators are
 // already in the B layout GEMM2 needs (K slot e of MFMA ks2 in lane half h is
 // coordinate 64 h + 8 ks2 + e, the same map GEMM1 uses for x).
@@ -250,10 +251,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       }
       if (vec[nt] < a.n) {
         const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
-        uint2* dst = reinterpret_cast<uint2*>(a.planes + rec * (P * 4)) + h;
+        // record order: word w of plane p at w * P + p; this lane owns words
+        // 2h and 2h+1 of every plane, i.e. the 2P contiguous u32 from 2h * P
+        uint32_t out[2 * P];
 #pragma unroll
-        for (int p = 0; p < BQ; ++p) dst[2 * p] = make_uint2(iw[nt][p][0], iw[nt][p][1]);
-        if (PROD) dst[2 * BQ] = make_uint2(sw[nt][0], sw[nt][1]);
+        for (int p = 0; p < BQ; ++p) {
+          out[p] = iw[nt][p][0];
+          out[P + p] = iw[nt][p][1];
+        }
+        if (PROD) {
+          out[BQ] = sw[nt][0];
+          out[P + BQ] = sw[nt][1];
+        }
+        uint2* dst = reinterpret_cast<uint2*>(a.planes + rec * (P * 4) + 2 * h * P);
+#pragma unroll
+        for (int i = 0; i < P; ++i) dst[i] = make_uint2(out[2 * i], out[2 * i + 1]);
         if (h == 0) {
           if (PROD) {
             reinterpret_cast<uint32_t*>(a.scalars)[rec] =

@@ -61,100 +61,202 @@ struct PrepArgs {
   uint8_t* ws;
 };
 
-__device__ float block_max(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, red[i]);
-  return r;
+// One workgroup (4 waves) per segment.  Both 128x128 products run on the
+// matrix cores (v_mfma_f32_16x16x32_bf16) with bf16 hi/lo splits of both
+// operands (three products, ~2^-16 relative, far below the 2^-14 integer
+// quantisation that follows; bf16 keeps fp32's range, so no rescaling):
+//   q_rot^T = Pi . Q^T         (dense; the Hadamard form uses +-eps entries)
+//   q_proj^T = S . q_rot^T
+// wave w owns output rows 32 w .. 32 w + 31, heads on the N axis.  Every
+// global operand is loaded up front (one memory round trip); the per-head
+// statistics reduce in registers, then the int8 A-operand fragments are
+// assembled in LDS and copied out with 16-byte stores.
+constexpr int MAXG = 16;
+constexpr int QLD = MAXG + 1;
+constexpr int MAXFRAG = 2 * 10 * 1024;   // MT <= 2, F <= 10
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split8_bf16(const float* v, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)v[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(v[e] - (float)h);
+  }
 }
 
-__device__ float block_sum(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float r = 0.f;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r += red[i];
-  return r;
+__device__ __forceinline__ f32x4 mfma3_bf16(const float* av, const float* bv, f32x4 acc) {
+  bf16x8 ah, al, bh, bl;
+  split8_bf16(av, ah, al);
+  split8_bf16(bv, bh, bl);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+  return acc;
 }
 
-// One workgroup (128 threads) per segment: rotate and project each query head,
-// quantise the plane weights and scatter them into the A-operand fragments.
-__global__ __launch_bounds__(128) void prep_queries128(PrepArgs a) {
-  __shared__ float qs[D], qrot[D], qproj[D];
-  __shared__ float red[4];
+__device__ __forceinline__ void unpack8(float4 a, float4 b, float* v) {
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <bool HAD>
+__global__ __launch_bounds__(256) void prep_queries128(PrepArgs a) {
+  __shared__ float qr[D * QLD], qp[D * QLD];
+  __shared__ __align__(16) uint8_t frag[MAXFRAG];
+  __shared__ float part[4][MAXG][4];
+  __shared__ float stat[MAXG][4];
   const int seg = blockIdx.x;
-  const int j = threadIdx.x;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = a.group;
   const int np = mse_planes(a.bq);
   const int F = 2 * (np + 1);
-  uint8_t* base = a.ws + (size_t)seg * pack_bytes(a.mt, F);
-  // zero the fragments (rows of heads beyond the group stay zero)
-  {
-    uint4* z = reinterpret_cast<uint4*>(base);
-    const int n16 = (int)(pack_frag_bytes(a.mt, F) / 16);
-    for (int i = j; i < n16; i += blockDim.x) z[i] = make_uint4(0, 0, 0, 0);
+  const int fbytes = (int)pack_frag_bytes(a.mt, F);
+  const bool live = col < G;
+
+  // ---- every global operand of this lane, in flight together ----
+  float4 qv[8], mv[16], sv[16];
+  const float4* qh = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + (live ? col : 0)) * D);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    qv[2 * ks] = qh[(32 * ks + 8 * kq) / 4];
+    qv[2 * ks + 1] = qh[(32 * ks + 8 * kq) / 4 + 1];
   }
-  float* consts = reinterpret_cast<float*>(base + pack_frag_bytes(a.mt, F));
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int row = 16 * (2 * wave + mi) + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 32 * ks + 8 * kq;
+      if (HAD) {
+        mv[(mi * 4 + ks) * 2] = reinterpret_cast<const float4*>(a.eps)[k0 / 4];
+        mv[(mi * 4 + ks) * 2 + 1] = reinterpret_cast<const float4*>(a.eps)[k0 / 4 + 1];
+      } else {
+        const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)row * D + k0);
+        mv[(mi * 4 + ks) * 2] = prow[0];
+        mv[(mi * 4 + ks) * 2 + 1] = prow[1];
+      }
+      const float4* srow = reinterpret_cast<const float4*>(a.s + (size_t)row * D + k0);
+      sv[(mi * 4 + ks) * 2] = srow[0];
+      sv[(mi * 4 + ks) * 2 + 1] = srow[1];
+    }
+  }
+  for (int i = t; i < fbytes / 16; i += blockDim.x) reinterpret_cast<uint4*>(frag)[i] = make_uint4(0, 0, 0, 0);
+
+  // ---- q_rot^T = Pi . Q^T ----
+  float rmax = 0.f, rsum = 0.f;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int mt = 2 * wave + mi;
+    const int j = 16 * mt + col;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 32 * ks + 8 * kq;
+      float av[8], bv[8];
+      unpack8(mv[(mi * 4 + ks) * 2], mv[(mi * 4 + ks) * 2 + 1], av);
+      if (HAD) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = (__popc(j & (k0 + e)) & 1) ? -av[e] : av[e];
+      }
+      unpack8(qv[2 * ks], qv[2 * ks + 1], bv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bv[e] = live ? bv[e] : 0.f;
+      acc = mfma3_bf16(av, bv, acc);
+    }
+    const float sc = HAD ? rsqrtf((float)D) : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[r] * sc;
+      qr[(16 * mt + 4 * kq + r) * QLD + col] = v;
+      rmax = fmaxf(rmax, fabsf(v));
+      rsum += v;
+    }
+  }
   __syncthreads();
-  for (int hh = 0; hh < a.group; ++hh) {
-    const float* qh = a.q + ((size_t)seg * a.group + hh) * a.d;
-    qs[j] = j < a.d ? qh[j] : 0.f;
-    __syncthreads();
-    float acc = 0.f;
-    if (a.rot == TQ_ROT_DENSE) {
-      const float* row = a.pi + (size_t)j * a.d;
-      for (int k = 0; k < a.d; ++k) acc += row[k] * qs[k];
-    } else {
-      for (int k = 0; k < a.d; ++k) acc += ((__popc(j & k) & 1) ? -1.f : 1.f) * a.eps[k] * qs[k];
-      acc *= rsqrtf((float)a.d_rot);
+  // ---- q_proj^T = S . q_rot^T ----
+  float pmax = 0.f, psum = 0.f;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int mt = 2 * wave + mi;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 32 * ks + 8 * kq;
+      float av[8], bv[8];
+      unpack8(sv[(mi * 4 + ks) * 2], sv[(mi * 4 + ks) * 2 + 1], av);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bv[e] = qr[(k0 + e) * QLD + col];
+      acc = mfma3_bf16(av, bv, acc);
     }
-    qrot[j] = acc;
-    __syncthreads();
-    float pacc = 0.f;
-    {
-      const float* row = a.s + (size_t)j * D;
-      for (int k = 0; k < D; ++k) pacc += row[k] * qrot[k];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      qp[(16 * mt + 4 * kq + r) * QLD + col] = acc[r];
+      pmax = fmaxf(pmax, fabsf(acc[r]));
+      psum += acc[r];
     }
-    qproj[j] = pacc;
+  }
+  // ---- per-head statistics: lanes col, col+16, col+32, col+48 of every wave ----
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    rmax = fmaxf(rmax, __shfl_xor(rmax, o, 64));
+    pmax = fmaxf(pmax, __shfl_xor(pmax, o, 64));
+    rsum += __shfl_xor(rsum, o, 64);
+    psum += __shfl_xor(psum, o, 64);
+  }
+  if (kq == 0) {
+    part[wave][col][0] = rmax;
+    part[wave][col][1] = rsum;
+    part[wave][col][2] = pmax;
+    part[wave][col][3] = psum;
+  }
+  __syncthreads();
+  if (t < MAXG) {
+    float mx = 0.f, sr = 0.f, px = 0.f, sp = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      mx = fmaxf(mx, part[w][t][0]);
+      sr += part[w][t][1];
+      px = fmaxf(px, part[w][t][2]);
+      sp += part[w][t][3];
+    }
     float umax = 0.f;
     for (int p = 0; p < np; ++p) umax = fmaxf(umax, fabsf(2.f * a.u[p]));
-    const float mmax = block_max(fabsf(qrot[j]) * umax, red);
-    const float pmax = block_max(fabsf(2.f * pacc), red);
-    const float qsum = block_sum(qrot[j], red);
-    const float psum = block_sum(pacc, red);
-    const float sig_m = mmax > 0.f ? mmax / QMAX : 1.f;
-    const float sig_q = pmax > 0.f ? pmax / QMAX : 1.f;
-    const int mt = hh >> 3;
-    const int hl = hh & 7;
-    if (j == 0) {
-      float* c = consts + (size_t)hh * 4;
-      c[0] = sig_m;
-      c[1] = -a.usum * qsum;
-      c[2] = sig_q;
-      c[3] = -psum;
-    }
-    // coordinate j -> (kg, word bit) -> (m, k, i)
+    const float mm = mx * umax, pm = 2.f * px;
+    stat[t][0] = mm > 0.f ? mm / QMAX : 1.f;
+    stat[t][1] = -a.usum * sr;
+    stat[t][2] = pm > 0.f ? pm / QMAX : 1.f;
+    stat[t][3] = -sp;
+  }
+  __syncthreads();
+  // ---- quantise and scatter into the LDS fragments ----
+  {
+    const int j = t & (D - 1);
+    const int hs = t >> 7;
     const int kg = j >> 5, b = j & 31;
-    const int i = b >> 3, m = (b & 7) >> 2, k = b & 3;
-    for (int p = 0; p <= np; ++p) {
-      const float w = p < np ? 2.f * a.u[p] * qrot[j] : 2.f * pacc;
-      const float sig = p < np ? sig_m : sig_q;
-      const int qi = (int)rintf(w / sig);
-      const int hi = (qi + 64) >> 7;
-      const int lo = qi - 128 * hi;
-      for (int sl = 0; sl < 2; ++sl) {
-        const int rho = 2 * hl + sl;
-        const size_t off = (((size_t)mt * F + 2 * p + m) * 64 + rho + 16 * kg) * 16 + 4 * k + i;
-        base[off] = (uint8_t)(int8_t)(sl == 0 ? hi : lo);
+    const int bi = b >> 3, m = (b & 7) >> 2, k = b & 3;
+    for (int h = hs; h < G; h += 2) {
+      const int mt = h >> 3, hl = h & 7;
+      const float inv_m = 1.f / stat[h][0], inv_q = 1.f / stat[h][2];
+      for (int p = 0; p <= np; ++p) {
+        const float w = p < np ? 2.f * a.u[p] * qr[j * QLD + h] * inv_m : 2.f * qp[j * QLD + h] * inv_q;
+        const int qi = (int)rintf(fminf(fmaxf(w, -QMAX), QMAX));
+        const int hi = (qi + 64) >> 7;
+        const int lo = qi - 128 * hi;
+        const int off = ((mt * F + 2 * p + m) * 64 + 2 * hl + 16 * kg) * 16 + 4 * k + bi;
+        frag[off] = (uint8_t)(int8_t)hi;
+        frag[off + 16] = (uint8_t)(int8_t)lo;   // row 2 hl + 1 is the next lane
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
+  uint8_t* base = a.ws + (size_t)seg * pack_bytes(a.mt, F);
+  for (int i = t; i < fbytes / 16; i += blockDim.x)
+    reinterpret_cast<uint4*>(base)[i] = reinterpret_cast<const uint4*>(frag)[i];
+  float* consts = reinterpret_cast<float*>(base + fbytes);
+  if (t < G * 4) consts[t] = stat[t >> 2][t & 3];
 }
 
 struct Score128Args {
@@ -175,11 +277,34 @@ __device__ __forceinline__ void expand8(uint32_t w, uint32_t e[8]) {
   for (int k = 0; k < 8; ++k) e[k] = (w >> k) & 0x01010101u;
 }
 
+template <int P>
+struct Words;
+template <>
+struct Words<2> {
+  typedef uint32_t v __attribute__((ext_vector_type(2), aligned(4)));
+};
+template <>
+struct Words<3> {
+  typedef uint32_t v __attribute__((ext_vector_type(3), aligned(4)));
+};
+template <>
+struct Words<4> {
+  typedef uint32_t v __attribute__((ext_vector_type(4), aligned(4)));
+};
+
+constexpr int SROW = 40;   // LDS row stride (floats) of the output transpose tile
+
+// One workgroup = 4 waves = chunk_tiles 16-token tiles of one segment.  A wave
+// takes pairs of adjacent tiles (32 tokens); the 32 x 8 outputs of a 16-row
+// tile pass through a per-wave LDS tile so that each lane stores 4 consecutive
+// tokens of one head (16 bytes) and a store covers whole 128-byte lines.
 template <int BQ, int MT>
 __global__ __launch_bounds__(256) void scores128(Score128Args a) {
   constexpr int NP = mse_planes(BQ);      // MSE planes after the parity plane
   constexpr int F = 2 * (NP + 1);         // MFMAs per tile per 16-row tile
   constexpr int P = BQ + 1;               // stored planes per key record
+  typedef typename Words<P>::v wvec;
+  __shared__ __align__(16) float sbuf[4][MT][8 * SROW];
   const int seg = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -206,28 +331,40 @@ __global__ __launch_bounds__(256) void scores128(Score128Args a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) cst[mt][e][c] = consts[(mt * 8 + 2 * kg + e) * 4 + c];
 
-  const uint32_t* seg_planes = a.planes + seg * a.seg_stride * (P * 4);
-  const uint32_t* seg_scal = reinterpret_cast<const uint32_t*>(a.scalars) + seg * a.seg_stride;
-  float* out = a.scores + (size_t)seg * a.group * a.T;
+  // segment bases (uniform) and 32-bit per-lane offsets
+  const uint32_t* seg_planes = a.planes + (seg * a.seg_stride + tok0) * (P * 4) + kg * P;
+  const uint32_t* seg_scal = reinterpret_cast<const uint32_t*>(a.scalars) + seg * a.seg_stride + tok0;
+  float* out = a.scores + (size_t)seg * a.group * a.T + tok0;
 
-  for (int tile = wave; tile < a.chunk_tiles; tile += 4) {
-    const int64_t t = tok0 + (int64_t)tile * 16 + t16;
-    if (tok0 + (int64_t)tile * 16 >= len) break;
-    const bool valid = t < len;
+  int ntok = (int)(len - tok0 < (int64_t)a.chunk_tiles * 16 ? len - tok0 : (int64_t)a.chunk_tiles * 16);
+  const int npairs = (ntok + 31) / 32;
+  const int lastt = ntok - 1;
+  // loads are unconditional, clamped to the last valid token, so no
+  // exec-masked branches surround them
+  auto load = [&](int tt, wvec& w, uint32_t& sc) {
+    const int t = tt < lastt ? tt : lastt;
+    w = *reinterpret_cast<const wvec*>(seg_planes + t * (P * 4));
+    sc = seg_scal[t];
+  };
+  // one 16-token tile -> LDS rows (heads 2 kg, 2 kg + 1), columns col0 + t16
+  auto compute = [&](int tt, wvec wl, uint32_t scl, int col0) {
+    const bool valid = tt < ntok;
     uint32_t w[P];
 #pragma unroll
-    for (int p = 0; p < P; ++p) w[p] = valid ? seg_planes[t * (P * 4) + p * 4 + kg] : 0u;
-    const uint32_t sc = valid ? seg_scal[t] : 0u;
-
+    for (int p = 0; p < P; ++p) w[p] = valid ? wl[p] : 0u;
     i32x4 am[MT], aq[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int p = 0; p <= NP; ++p) {
       uint32_t word;
-      if (p == NP) word = w[BQ];                       // QJL signs
-      else if (p < BQ) word = w[p];                    // single index bits
-      else word = w[0] ^ w[1] ^ w[2];                  // parity of 3 bits
+      if (p == NP) {
+        word = w[BQ];                                  // QJL signs
+      } else if (p < BQ) {
+        word = w[p];                                   // single index bits
+      } else {
+        if constexpr (BQ == 3) word = w[0] ^ w[1] ^ w[2];   // parity of 3 bits
+      }
       uint32_t e[8];
       expand8(word, e);
 #pragma unroll
@@ -240,19 +377,57 @@ __global__ __launch_bounds__(256) void scores128(Score128Args a) {
         }
       }
     }
-    if (!valid) continue;
-    const float n = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc & 0xffff));
-    const float gk = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc >> 16)) * a.kappa;
+    const float n = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl & 0xffff));
+    const float gk = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl >> 16)) * a.kappa;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int head = mt * 8 + 2 * kg + e;
         const float mse = (float)(am[mt][2 * e] * 128 + am[mt][2 * e + 1]) * cst[mt][e][0] + cst[mt][e][1];
         const float qjl = (float)(aq[mt][2 * e] * 128 + aq[mt][2 * e + 1]) * cst[mt][e][2] + cst[mt][e][3];
-        if (head < a.group) out[(size_t)head * a.T + t] = n * fmaf(gk, qjl, mse);
+        sbuf[wave][mt][(2 * kg + e) * SROW + col0 + t16] = n * fmaf(gk, qjl, mse);
       }
     }
+  };
+  // lanes 8 h' + c store tokens 4c .. 4c+3 of head h' of the pair
+  auto flush = [&](int pbase) {
+    const int hr = lane >> 3, c4 = 4 * (lane & 7);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int head = mt * 8 + hr;
+      if (head >= a.group) continue;
+      const float4 v = *reinterpret_cast<const float4*>(&sbuf[wave][mt][hr * SROW + c4]);
+      float* dst = out + (size_t)head * a.T + pbase + c4;
+      if (pbase + c4 + 3 < ntok) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        if (pbase + c4 < ntok) dst[0] = v.x;
+        if (pbase + c4 + 1 < ntok) dst[1] = v.y;
+        if (pbase + c4 + 2 < ntok) dst[2] = v.z;
+      }
+    }
+  };
+
+  wvec w0, w1, w2, w3;
+  uint32_t s0, s1, s2, s3;
+  int pr = wave;
+  load(32 * pr + t16, w0, s0);
+  load(32 * pr + 16 + t16, w1, s1);
+  load(32 * (pr + 4) + t16, w2, s2);
+  load(32 * (pr + 4) + 16 + t16, w3, s3);
+  for (; pr < npairs; pr += 8) {
+    compute(32 * pr + t16, w0, s0, 0);
+    compute(32 * pr + 16 + t16, w1, s1, 16);
+    load(32 * (pr + 8) + t16, w0, s0);
+    load(32 * (pr + 8) + 16 + t16, w1, s1);
+    flush(32 * pr);
+    if (pr + 4 < npairs) {
+      compute(32 * (pr + 4) + t16, w2, s2, 0);
+      compute(32 * (pr + 4) + 16 + t16, w3, s3, 16);
+      flush(32 * (pr + 4));
+    }
+    load(32 * (pr + 12) + t16, w2, s2);
+    load(32 * (pr + 12) + 16 + t16, w3, s3);
   }
 }
 
@@ -309,7 +484,10 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
   p.bq = a.bq;
   p.mt = (a.group + 7) / 8;
   p.ws = static_cast<uint8_t*>(a.ws);
-  hipLaunchKernelGGL(prep_queries128, dim3(a.segs), dim3(128), 0, stream, p);
+  if (a.rot == TQ_ROT_HADAMARD)
+    hipLaunchKernelGGL(prep_queries128<true>, dim3(a.segs), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(prep_queries128<false>, dim3(a.segs), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   Score128Args s;

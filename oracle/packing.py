@@ -3,7 +3,10 @@
 A record holds bit-planes of 32-bit little-endian words followed (in a
 separate array) by float16 scalars:
 
-  plane p, coordinate j  ->  bit (j mod 32) of word (j div 32) of plane p
+  plane p, coordinate j  ->  bit (j mod 32) of word (j div 32) of plane p,
+  and word w of plane p is 32-bit word w * P + p of the record (P planes):
+  the planes are interleaved word by word, so the P words that cover the same
+  32 coordinates are adjacent.
 
 Key record (TurboQuant-prod, b bits):  planes 0..b-2 carry bit p of the
 (b-1)-bit index, plane b-1 carries the QJL bits z (bit 1 <=> (S r)_i >= 0);
@@ -38,13 +41,14 @@ def unpack_bits(words) -> np.ndarray:
 
 
 def index_planes(idx, nbits: int) -> np.ndarray:
-    """[N, d] indices -> [N, nbits, d/32] words, plane p = bit p."""
+    """[N, d] indices -> [N, nbits, d/32] words, plane p = bit p (plane-major view)."""
     idx = np.asarray(idx, dtype=np.int64)
     return np.stack([pack_bits((idx >> p) & 1) for p in range(nbits)], axis=1) if nbits else \
         np.zeros((idx.shape[0], 0, idx.shape[1] // 32), np.uint32)
 
 
 def planes_to_index(planes) -> np.ndarray:
+    """Plane-major [N, nbits, d/32] words -> [N, d] indices."""
     planes = np.asarray(planes, dtype=np.uint32)
     n, nb, w = planes.shape
     idx = np.zeros((n, w * 32), dtype=np.int64)
@@ -53,30 +57,40 @@ def planes_to_index(planes) -> np.ndarray:
     return idx
 
 
+def interleave(plane_major) -> np.ndarray:
+    """[N, P, W] plane-major words -> [N, W, P] record order (word w of plane p at w*P + p)."""
+    return np.ascontiguousarray(np.asarray(plane_major, np.uint32).transpose(0, 2, 1))
+
+
+def deinterleave(record) -> np.ndarray:
+    """[N, W, P] record order -> [N, P, W] plane-major words."""
+    return np.ascontiguousarray(np.asarray(record, np.uint32).transpose(0, 2, 1))
+
+
 def pack_key(code, nbits_idx: int):
-    """ProdCode -> (planes [N, nbits_idx + 1, d/32] uint32, scalars [N, 2] float16)."""
+    """ProdCode -> (planes [N, d/32, nbits_idx + 1] uint32 in record order, scalars [N, 2] float16)."""
     planes = np.concatenate([index_planes(code.idx, nbits_idx),
                              pack_bits(code.z)[:, None, :]], axis=1)
     scalars = np.stack([code.n, code.gamma], axis=1).astype(np.float16)
-    return planes, scalars
+    return interleave(planes), scalars
 
 
 def pack_value(code, nbits: int):
-    """MseCode -> (planes [N, nbits, d/32] uint32, scalars [N, 1] float16)."""
-    return index_planes(code.idx, nbits), code.n.astype(np.float16)[:, None]
+    """MseCode -> (planes [N, d/32, nbits] uint32 in record order, scalars [N, 1] float16)."""
+    return interleave(index_planes(code.idx, nbits)), code.n.astype(np.float16)[:, None]
 
 
 def unpack_key(planes, scalars, nbits_idx: int):
-    """-> (idx [N, d], z [N, m] bool, n [N], gamma [N]) with float16 scalars as float64."""
-    planes = np.asarray(planes, np.uint32)
-    idx = planes_to_index(planes[:, :nbits_idx, :])
-    z = unpack_bits(planes[:, nbits_idx, :])
+    """Record-order planes -> (idx [N, d], z [N, m] bool, n [N], gamma [N]), scalars as float64."""
+    pm = deinterleave(planes)
+    idx = planes_to_index(pm[:, :nbits_idx, :])
+    z = unpack_bits(pm[:, nbits_idx, :])
     s = np.asarray(scalars, np.float16).astype(np.float64)
     return idx, z, s[:, 0], s[:, 1]
 
 
 def unpack_value(planes, scalars, nbits: int):
-    idx = planes_to_index(np.asarray(planes, np.uint32)[:, :nbits, :])
+    idx = planes_to_index(deinterleave(planes)[:, :nbits, :])
     return idx, np.asarray(scalars, np.float16).astype(np.float64)[:, 0]
 
 

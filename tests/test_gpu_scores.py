@@ -159,3 +159,15 @@ def smoke_scores_attend():
     except ImportError:
         return
     smoke_attend()
+
+
+@pytest.mark.parametrize("qscale", [1e-3, 3e3])
+def test_query_magnitude_extremes(qscale):
+    _log(f"scores query scale {qscale}")
+    x = kv_tensor(1, 1, 600, 128, seed=7)[0, 0]
+    st = Setup(bits=3, prod=True, seed=7)
+    cache, (idx, z, n, g) = oracle_key_cache(st, x)
+    q = gaussian_queries(8, 128, seed=7) * np.float32(qscale)
+    got = gpu_scores(st, q, 1, 8, cache, 600)
+    ref = est.prod_scores(q, idx, z, n, g, st.rot, st.s, st.c32)
+    check_rows(got, ref)

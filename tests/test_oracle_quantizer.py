@@ -97,6 +97,9 @@ def test_pack_hand_built_words():
     assert planes[0, 0].tolist() == [1 | (1 << 31), 0]
     assert planes[0, 1].tolist() == [1 << 31, 2]
     assert np.array_equal(pk.planes_to_index(planes), idx)
+    # record order interleaves the planes word by word: w0p0 w0p1 w1p0 w1p1
+    rec = pk.interleave(planes).reshape(1, -1)
+    assert rec[0].tolist() == [1 | (1 << 31), 1 << 31, 0, 2]
 
 
 def test_pack_roundtrip_random():
@@ -105,6 +108,11 @@ def test_pack_roundtrip_random():
     z = rg.integers(0, 2, size=(7, 128)).astype(bool)
     code = qz.ProdCode(idx=idx, z=z, n=rg.random(7) * 10, gamma=rg.random(7), y=None, proj=None)
     planes, scal = pk.pack_key(code, 3)
+    assert planes.shape == (7, 4, 4)
+    # word w of plane p sits at w * P + p of the record
+    pm = pk.index_planes(idx, 3)
+    assert np.array_equal(planes.reshape(7, -1)[:, 1 * 4 + 2], pm[:, 2, 1])
+    assert np.array_equal(planes.reshape(7, -1)[:, 3 * 4 + 3], pk.pack_bits(z)[:, 3])
     i2, z2, n2, g2 = pk.unpack_key(planes, scal, 3)
     assert np.array_equal(i2, idx) and np.array_equal(z2, z)
     assert np.allclose(n2, code.n, rtol=1e-3) and np.allclose(g2, code.gamma, rtol=1e-3, atol=1e-4)
