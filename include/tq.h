@@ -31,9 +31,14 @@
  *                           scalars = { float16 n = ||x||, float16 gamma = ||r|| }
  *     value (mse,  b bits)  planes 0 .. b-1 = bit p of the b-bit index;
  *                           scalars = { float16 n }
- *   A cache holds the plane words of all records in one array, u32
+ *   A key cache holds the plane words of all records in one array, u32
  *   [records][d_rot/32][P], and the scalars in another, f16
  *   [records][scalars]; record r of segment s is s * seg_stride + t.
+ *   A value cache stores the same bits transposed in blocks of 32 records
+ *   (values are read along tokens): u32 [ceil(records/32)][d_rot][P], word
+ *   (B, j, p) holding in bit i the bit p of the index of record 32 B + i at
+ *   coordinate j; scalars f16 [records][1].  seg_stride of a value cache must
+ *   be a multiple of 32 so that segments start on a block.
  *   At d = 128, b = 3 a key record is 48 + 4 bytes and a value 48 + 2 bytes.
  */
 #ifndef TQ_H
@@ -124,7 +129,11 @@ tq_status tq_value_layout(const tq_params* p, int* planes, int* words_per_plane,
 tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
                          int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
-/* TurboQuant-MSE encode (values): as above without the QJL stage, b index bits. */
+/* TurboQuant-MSE encode (values): as above without the QJL stage, b index
+ * bits, written in the blocked value layout.  A group of 32 vectors that fills
+ * one aligned block (slot NULL, or slots base + 0..31 with base a multiple of
+ * 32) is written with whole-word stores; any other record is updated with
+ * per-bit atomic clear/set, so partial blocks keep their other records. */
 tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
                         int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
@@ -153,8 +162,11 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
  *   p = softmax_t(scale * s[h][t]) over t < len,  o[h] = sum_t p_t n_v,t rot_v^T(c_v[idx_v,t])
  * computed as one rot_v^T per head after accumulating in the rotated domain.
  * out     device f32 [segs*group][d]; a segment with len 0 gives zeros
- * Other arguments as for tq_scores; vals is the packed mse value cache with
- * the same seg_stride convention. */
+ * vals    packed mse value cache (block layout), vals.seg_stride a multiple of
+ *         32 and, like keys.seg_stride, >= T; its scalars must cover
+ *         segs * seg_stride records
+ * Other arguments as for tq_scores.  Supported: d = 128, group <= 16, value
+ * bits 1..3. */
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs,
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);

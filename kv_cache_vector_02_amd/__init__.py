@@ -174,6 +174,15 @@ def alloc_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
                  torch.zeros((records, S), dtype=torch.float16, device=device), seg_stride)
 
 
+def alloc_value_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
+    """A value cache: block words int32 [ceil(records/32), d_rot, P] (bit i of word
+    (B, j, p) = bit p of record 32 B + i at coordinate j), scalars float16 [records, 1]."""
+    import torch
+    P, W, S = layout
+    return Cache(torch.zeros(((records + 31) // 32, 32 * W, P), dtype=torch.int32, device=device),
+                 torch.zeros((records, S), dtype=torch.float16, device=device), seg_stride)
+
+
 def _dtype_code(x):
     import torch
     if x.dtype == torch.float16:

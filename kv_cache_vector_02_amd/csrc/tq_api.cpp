@@ -228,9 +228,56 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs, int group,
                     tq_cache keys, tq_cache vals, const int32_t* len, int64_t T, float scale,
                     float* out, void* ws, size_t ws_bytes, void* stream) {
-  (void)kp; (void)vp; (void)q; (void)segs; (void)group; (void)keys; (void)vals; (void)len;
-  (void)T; (void)scale; (void)out; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(TQ_ERR_UNSUPPORTED, "tq_attend is not built yet");
+  tq::AttendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  tq_status st = check_params(kp, true, &a.k.cb, true);
+  if (st != TQ_OK) return st;
+  st = check_params(vp, false, &a.cb_v, true);
+  if (st != TQ_OK) return st;
+  if (segs < 0 || group < 1 || T < 0) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
+  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "scale must be finite");
+  if (segs == 0) return TQ_OK;
+  if (kp->d != 128 || kp->d_rot != 128 || vp->d != 128 || vp->d_rot != 128)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports d = d_rot = 128 for keys and values");
+  if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports up to 16 query heads per segment");
+  if (vp->bits > 3) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports value bits 1..3");
+  if (!q || !keys.planes || !keys.scalars || !vals.planes || !vals.scalars || !out || !ws)
+    return fail(TQ_ERR_INVALID_ARG, "q, keys, vals, out and ws must be non-NULL");
+  if (vals.seg_stride % 32) return fail(TQ_ERR_INVALID_ARG, "vals.seg_stride must be a multiple of 32");
+  if (segs > 1 && (keys.seg_stride < T || vals.seg_stride < T))
+    return fail(TQ_ERR_INVALID_ARG, "seg_stride must be >= T for keys and values");
+  if (!aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(vals.planes, 16) ||
+      !aligned(vals.scalars, 4) || !aligned(ws, 256) || !aligned(q, 16) || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
+  if (T == 0) return fail(TQ_ERR_INVALID_ARG, "T must be >= 1");
+  const size_t need = tq::attend128_workspace(segs, group, T);
+  if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
+  a.k.q = q;
+  a.k.segs = segs;
+  a.k.group = group;
+  a.k.d = kp->d;
+  a.k.pi = kp->pi;
+  a.k.eps = kp->eps;
+  a.k.rot = kp->rot;
+  a.k.s = kp->s;
+  a.k.bq = kp->bits - 1;
+  a.k.planes = (const uint32_t*)keys.planes;
+  a.k.scalars = (const uint16_t*)keys.scalars;
+  a.k.seg_stride = keys.seg_stride;
+  a.k.len = len;
+  a.k.T = T;
+  a.k.ws = ws;
+  a.pi_v = vp->pi;
+  a.eps_v = vp->eps;
+  a.rot_v = vp->rot;
+  a.bq_v = vp->bits;
+  a.planes_v = (const uint32_t*)vals.planes;
+  a.scalars_v = (const uint16_t*)vals.scalars;
+  a.seg_stride_v = vals.seg_stride;
+  a.scale = scale;
+  a.out = out;
+  a.ws = ws;
+  return hip_status(tq::launch_attend128(a, (hipStream_t)stream), "attend launch");
 }
 
 }  // extern "C"

@@ -161,6 +161,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       yscale[nt] = n > 0.f ? 1.f / (n * PI_SCALE) : 0.f;
     }
 
+    // ---- values: one aligned, fully valid 32-record block per tile? ----
+    bool vfast = false;
+    int64_t vblock = 0;
+    uint32_t vlo[BQ], vhi[BQ];
+    if (!PROD) {
+      static_assert(PROD || NT == 1, "value tiles are 32 vectors");
+      const int64_t r0 = a.slot ? a.slot[tile * 32 < a.n ? tile * 32 : 0] : tile * 32;
+      const bool mine = vec[0] < a.n && (a.slot ? a.slot[vec[0]] : vec[0]) == r0 + v;
+      vfast = (r0 % 32) == 0 && __all(mine);
+      vblock = r0 / 32;
+#pragma unroll
+      for (int p = 0; p < BQ; ++p) vlo[p] = vhi[p] = 0u;
+    }
     // ---- GEMM1 per row tile, then quantize, pack, residual ----
     uint32_t iw[NT][BQ][2];
     half8 rh[NT][8], rl[NT][8];
@@ -198,6 +211,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           const int pos = 16 * (mt & 1) + r;
 #pragma unroll
           for (int p = 0; p < BQ; ++p) iw[nt][p][mt >> 1] |= (uint32_t)((idx >> p) & 1) << pos;
+          if (!PROD) {
+            if (vfast) {
+              // bit v of the ballot = vector v at coordinate 16 mt + r (lanes
+              // 0-31) or 64 + 16 mt + r (lanes 32-63): two block words
+#pragma unroll
+              for (int p = 0; p < BQ; ++p) {
+                const uint64_t m = __ballot((idx >> p) & 1);
+                const bool here = lane == 16 * mt + r;
+                vlo[p] = here ? (uint32_t)m : vlo[p];
+                vhi[p] = here ? (uint32_t)(m >> 32) : vhi[p];
+              }
+            } else if (vec[nt] < a.n) {
+              const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
+              uint32_t* wp = a.planes + (rec >> 5) * (D * BQ) + (64 * h + 16 * mt + r) * BQ;
+              const uint32_t bit = 1u << (rec & 31);
+#pragma unroll
+              for (int p = 0; p < BQ; ++p) {
+                atomicAnd(wp + p, ~bit);
+                if ((idx >> p) & 1) atomicOr(wp + p, bit);
+              }
+            }
+          }
           if (PROD) {
             const float res = y - chat;
             g2[nt] += res * res;
@@ -248,6 +283,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       if (PROD) {
         float t = g2[nt] + shfl_xor_f(g2[nt], 32);
         g = sqrtf(t);
+      }
+      if (!PROD) {
+        if (vfast) {
+          // lane L holds the words of coordinates L and 64 + L, planes contiguous
+          uint32_t* base = a.planes + vblock * (D * BQ);
+#pragma unroll
+          for (int p = 0; p < BQ; ++p) {
+            base[lane * BQ + p] = vlo[p];
+            base[(64 + lane) * BQ + p] = vhi[p];
+          }
+        }
+        if (vec[nt] < a.n && h == 0) a.scalars[a.slot ? a.slot[vec[nt]] : vec[nt]] = f16_bits(nrm[nt]);
+        continue;
       }
       if (vec[nt] < a.n) {
         const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];

@@ -14,6 +14,13 @@ scalars = (float16 n, float16 gamma).
 Value record (TurboQuant-MSE, b bits): planes 0..b-1 carry bit p of the
 index; scalars = (float16 n).
 
+Value caches use the same bits transposed within blocks of 32 records: for
+block B (records 32 B .. 32 B + 31), coordinate j and plane p there is one
+32-bit word, word number (j * P + p) of the block, whose bit i is bit p of the
+index of record 32 B + i at coordinate j.  The float16 norms stay one per
+record.  (Keys are read along coordinates, values along tokens; each layout
+puts the bits a reader needs in one word.)
+
 This matches the storage accounting the first page uses (indices packed at b
 bits per coordinate, one sign bit per projection row, float16 norms).
 """
@@ -101,3 +108,31 @@ def key_record_bytes(d_rot: int, m: int, bits: int) -> int:
 
 def value_record_bytes(d_rot: int, bits: int) -> int:
     return bits * d_rot // 8 + 2
+
+
+def pack_value_blocks(idx, nbits: int) -> np.ndarray:
+    """[N, d] value indices -> [ceil(N/32), d, nbits] uint32 blocked words.
+
+    Word (B, j, p) bit i = bit p of idx[32 B + i, j]; records past N are zero.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    n, d = idx.shape
+    nb = (n + 31) // 32
+    pad = np.zeros((nb * 32, d), np.int64)
+    pad[:n] = idx
+    out = np.zeros((nb, d, nbits), np.uint32)
+    for p in range(nbits):
+        bits = ((pad >> p) & 1).reshape(nb, 32, d)          # [B, i, j]
+        out[:, :, p] = pack_bits(bits.transpose(0, 2, 1).reshape(nb * d, 32)).reshape(nb, d)
+    return out
+
+
+def unpack_value_blocks(words, n: int) -> np.ndarray:
+    """[NB, d, nbits] blocked words -> [n, d] indices."""
+    words = np.asarray(words, np.uint32)
+    nb, d, nbits = words.shape
+    idx = np.zeros((nb * 32, d), np.int64)
+    for p in range(nbits):
+        bits = unpack_bits(words[:, :, p].reshape(nb * d, 1)).reshape(nb, d, 32)   # [B, j, i]
+        idx |= bits.transpose(0, 2, 1).reshape(nb * 32, d).astype(np.int64) << p
+    return idx[:n]

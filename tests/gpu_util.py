@@ -57,11 +57,16 @@ class Setup:
     def layout(self):
         return tq.key_layout(self.params) if self.prod else tq.value_layout(self.params)
 
-    def encode_gpu(self, x_np, slot=None, records=None):
+    def alloc(self, records, seg_stride=0):
+        if self.prod:
+            return tq.alloc_cache(self.layout(), records, seg_stride)
+        return tq.alloc_value_cache(self.layout(), records, seg_stride)
+
+    def encode_gpu(self, x_np, slot=None, records=None, cache=None):
         T = torch()
         x = T.from_numpy(np.ascontiguousarray(x_np)).cuda()
         n = x.shape[0]
-        cache = tq.alloc_cache(self.layout(), records or n)
+        cache = cache or self.alloc(records or n)
         sl = None if slot is None else T.from_numpy(np.asarray(slot, np.int64)).cuda()
         (tq.encode_prod if self.prod else tq.encode_mse)(self.params, x, cache, slot=sl)
         T.cuda.synchronize()
@@ -93,15 +98,23 @@ def _f16_ulp_apart(a, b):
     return np.abs(ai - bi)
 
 
+def value_indices(planes_blocks, records):
+    """GPU value cache words [NB, d, P] -> indices [records, d] via the oracle's unpacking."""
+    return pk.unpack_value_blocks(planes_blocks, records)
+
+
 def compare_encode(setup: Setup, planes, scal, ocode):
-    """Check a GPU encode against the oracle; returns a dict of statistics."""
+    """Check a GPU encode against the oracle; returns a dict of statistics.
+
+    For keys ``planes`` are record words; for values, pass the indices
+    already unpacked from the block layout (value_indices)."""
     bq = setup.bq
     n = planes.shape[0]
     stats = {}
     if setup.prod:
         idx, z, nn, gg = pk.unpack_key(planes, scal, bq)
     else:
-        idx, nn = pk.unpack_value(planes, scal, bq)
+        idx = planes          # value indices, already unpacked from the block layout
     # indices
     mism = idx != ocode.idx
     if bq and np.any(mism):

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from tests.gpu_util import Setup, compare_encode, torch
+from tests.gpu_util import Setup, compare_encode, torch, value_indices
 from tq_inputs import kv_tensor, tiny_vectors
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +41,7 @@ def test_mse_bits_dtypes_ragged(bits, dtype):
     x = x if dtype == "f16" else x.astype(np.float32)
     st = Setup(bits=bits, prod=False, seed=2, purpose_pi=4)
     planes, scal = st.encode_gpu(x)
-    compare_encode(st, planes, scal, st.encode_oracle(x))
+    compare_encode(st, value_indices(planes, len(x)), scal, st.encode_oracle(x))
 
 
 def test_zero_vectors_and_slots():
@@ -88,6 +88,34 @@ def test_qwen_shaped_full_size_sampled():
     for x, prod in ((k, True), (v, False)):
         st = Setup(bits=3, prod=prod, seed=1, purpose_pi=2 if prod else 4)
         planes, scal = st.encode_gpu(x)
+        if not prod:
+            planes = value_indices(planes, len(x))
         compare_encode(st, planes[sample], scal[sample], st.encode_oracle(x[sample]))
         del planes, scal
         T.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["aligned_slots", "scattered_slots", "ragged"])
+def test_value_block_paths(mode):
+    # whole-block stores for aligned groups of 32, per-bit atomics otherwise;
+    # the cache is pre-filled so stale bits of re-encoded records must clear
+    _log(f"encode values, {mode}")
+    rg = np.random.default_rng(8)
+    records = 256
+    st = Setup(bits=3, prod=False, seed=8, purpose_pi=4)
+    old = kv_tensor(1, 1, records, 128, seed=9, value=True)[0, 0]
+    cache = st.alloc(records)
+    st.encode_gpu(old, cache=cache)
+    x = kv_tensor(1, 1, 100 if mode == "ragged" else 96, 128, seed=10, value=True)[0, 0]
+    if mode == "aligned_slots":
+        slot = np.concatenate([np.arange(64, 128), np.arange(192, 224)])
+    elif mode == "scattered_slots":
+        slot = rg.permutation(records)[: len(x)]
+    else:
+        slot = None
+    planes, scal = st.encode_gpu(x, slot=slot, cache=cache)
+    idx = value_indices(planes, records)
+    where = np.arange(len(x)) if slot is None else slot
+    compare_encode(st, idx[where], scal[where], st.encode_oracle(x))
+    rest = np.setdiff1d(np.arange(records), where)
+    compare_encode(st, idx[rest], scal[rest], st.encode_oracle(old[rest]))

@@ -126,3 +126,19 @@ def test_record_sizes_reproduce_printed_compression_ratios():
         r = (2 * 128 * 2) / (pk.key_record_bytes(128, 128, bits) + pk.value_record_bytes(128, bits))
         assert round(r, 1) == float(ratio)
     assert pk.key_record_bytes(128, 128, 3) == 52 and pk.value_record_bytes(128, 3) == 50
+
+
+def test_value_blocks_hand_built_and_roundtrip():
+    idx = np.zeros((40, 64), np.int64)
+    idx[0, 0] = 1          # block 0, coord 0, plane 0, bit 0
+    idx[5, 3] = 2          # block 0, coord 3, plane 1, bit 5
+    idx[33, 63] = 3        # block 1, coord 63, planes 0 and 1, bit 1
+    w = pk.pack_value_blocks(idx, 2)
+    assert w.shape == (2, 64, 2)
+    assert w[0, 0, 0] == 1 and w[0, 0, 1] == 0
+    assert w[0, 3, 1] == 1 << 5 and w[0, 3, 0] == 0
+    assert w[1, 63, 0] == 2 and w[1, 63, 1] == 2
+    assert np.count_nonzero(w) == 4
+    rg = np.random.default_rng(4)
+    r = rg.integers(0, 8, size=(77, 128))
+    assert np.array_equal(pk.unpack_value_blocks(pk.pack_value_blocks(r, 3), 77), r)
