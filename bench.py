@@ -1,0 +1,211 @@
+"""Throughput of the TurboQuant hot path on one MI355X.
+
+Workload: a Qwen2.5-3B-shaped KV cache, 36 layers x 2 KV heads x 8192 tokens
+x head_dim 128 in float16 (synthetic: N(0,1) times lognormal(0, 0.5)
+per-channel scales, 2% of channels x10), keys TurboQuant-prod at b = 3,
+values TurboQuant-MSE at b = 3, dense random rotations; single-token decode
+with 16 query heads per layer (GQA 8), softmax scale 1/sqrt(128).
+
+One step = encode one batch's keys and values (tq_encode_prod, tq_encode_mse)
++ score and attend over a batch encoded two steps earlier (tq_scores,
+tq_attend).  Three batches rotate so that the decode side reads packed data
+that is not resident in the 256 MB Infinity Cache.  Kernel times come from
+HIP events on the stream the library launches on.
+
+Prints one JSON line.  `value` is the packed-KV score bandwidth of tq_scores
+(packed keys read + scores written + queries read, per call, over the call's
+average duration).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 matrix peak (the encode's instruction)
+
+L_, H_, T_, D_ = 36, 2, 8192, 128
+G_ = 8
+BITS = 3
+SEED = 1
+
+
+def make_params(torch, tq, prod, seed):
+    from tq_inputs import gaussian_matrix, haar_orthogonal
+    c, b = tq.build_codebook(D_, BITS - 1 if prod else BITS)
+    pi = torch.from_numpy(haar_orthogonal(D_, seed, 2 if prod else 4)).cuda()
+    s = torch.from_numpy(gaussian_matrix(D_, D_, seed, 3)).cuda() if prod else None
+    return tq.Params(d=D_, bits=BITS, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b, pi=pi, s=s)
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The oracle (float64 NumPy) on a bounded sample of the same workload."""
+    from oracle import estimator as est
+    from oracle import packing as pk
+    from oracle import codebook as cb
+    from oracle import quantizer as qz
+    from oracle import transforms as tr
+    from tq_inputs import gaussian_matrix, gaussian_queries, haar_orthogonal, kv_tensor
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    ck, bk = cb.lloyd_max(D_, BITS - 1)
+    rot = tr.DenseRotation(haar_orthogonal(D_, SEED, 2))
+    s = gaussian_matrix(D_, D_, SEED, 3)
+    x = kv_tensor(1, H_, T_, D_, seed=SEED)[0]            # one layer: 2 segments
+    q = gaussian_queries(H_ * G_, D_, seed=SEED)
+    t0 = time.perf_counter()
+    code = qz.encode_prod(x.reshape(-1, D_), rot, s, ck, bk)
+    t_enc = time.perf_counter() - t0
+    planes, scal = pk.pack_key(code, BITS - 1)
+    idx, z, n, g = pk.unpack_key(planes, scal, BITS - 1)
+    reps, t_sc = 0, 0.0
+    while t_sc < budget_s / 2 or reps == 0:
+        t0 = time.perf_counter()
+        for h in range(H_):
+            sl = slice(h * T_, (h + 1) * T_)
+            est.prod_scores(q[h * G_:(h + 1) * G_], idx[sl], z[sl], n[sl], g[sl], rot, s, ck)
+        t_sc += time.perf_counter() - t0
+        reps += 1
+    score_bytes = H_ * T_ * 52 + H_ * G_ * T_ * 4
+    return {
+        "value": round(reps * score_bytes / t_sc / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"one layer (2 KV heads x 8192 tokens, 8 query heads each): oracle prod_scores "
+                   f"repeated {reps}x over {t_sc:.1f} s; oracle encode of those 16384 keys took "
+                   f"{t_enc:.2f} s ({2 * T_ / t_enc:.0f} vectors/s)"),
+        "encode_vectors_per_s": round(2 * T_ / t_enc, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the hot path has no cross-GPU step here "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_vector_02_amd as tq
+    from tq_inputs import gaussian_queries, kv_tensor
+
+    torch.cuda.set_device(0)
+    pk_ = make_params(torch, tq, True, SEED)
+    pv_ = make_params(torch, tq, False, SEED)
+    segs = L_ * H_
+    N = segs * T_
+    R = 3
+    k_host = torch.from_numpy(kv_tensor(L_, H_, T_, D_, seed=SEED).reshape(N, D_))
+    v_host = torch.from_numpy(kv_tensor(L_, H_, T_, D_, seed=SEED, value=True).reshape(N, D_))
+    kx = [k_host.cuda() for _ in range(R)]
+    vx = [v_host.cuda() for _ in range(R)]
+    kc = [tq.alloc_cache(tq.key_layout(pk_), N, seg_stride=T_) for _ in range(R)]
+    vc = [tq.alloc_value_cache(tq.value_layout(pv_), N, seg_stride=T_) for _ in range(R)]
+    q = torch.from_numpy(gaussian_queries(segs * G_, D_, seed=SEED)).cuda()
+    scores = torch.empty((segs * G_, T_), dtype=torch.float32, device="cuda")
+    out = torch.empty((segs * G_, D_), dtype=torch.float32, device="cuda")
+    ws_s = torch.empty(tq.scores_workspace(pk_, segs, G_), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(tq.attend_workspace(pk_, pv_, segs, G_, T_), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / np.sqrt(D_)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(i, rec=None):
+        e = i % R
+        d = (i + 1) % R           # encoded two steps ago
+        marks = [ev() for _ in range(5)] if rec is not None else None
+        if marks:
+            marks[0].record()
+        tq.encode_prod(pk_, kx[e], kc[e])
+        if marks:
+            marks[1].record()
+        tq.encode_mse(pv_, vx[e], vc[e])
+        if marks:
+            marks[2].record()
+        tq.scores(pk_, q, segs, G_, kc[d], T_, scores, ws_s)
+        if marks:
+            marks[3].record()
+        tq.attend(pk_, pv_, q, segs, G_, kc[d], vc[d], T_, scale, out, ws_a)
+        if marks:
+            marks[4].record()
+            rec.append(marks)
+
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    rec = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dur = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(4)] for m in rec])   # ms
+    t_ek, t_ev, t_sc, t_at = dur.mean(axis=0)
+    ms_step = wall * 1e3 / args.steps
+
+    score_bytes = N * 52 + segs * G_ * T_ * 4 + segs * G_ * D_ * 4
+    score_gbs = score_bytes / (t_sc * 1e-3) / 1e9
+    attend_bytes = N * (52 + 50) + segs * G_ * D_ * 8
+    attend_gbs = attend_bytes / (t_at * 1e-3) / 1e9
+    enc_rate = 2 * N / ((t_ek + t_ev) * 1e-3)
+    enc_tflops = (N * 2 * 2 * D_ * D_ + N * 2 * D_ * D_) / ((t_ek + t_ev) * 1e-3) / 1e12
+    enc_exec_tflops = (N * 5 * 2 * D_ * D_ + N * 2 * 2 * D_ * D_) / ((t_ek + t_ev) * 1e-3) / 1e12
+
+    result = {
+        "metric": "packed-KV score GB/s (frac HBM peak) + encoded vectors/sec, d=128 b=3",
+        "value": round(score_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen2.5-3b-shaped kv cache: 36 layers x 2 kv heads x 8192 tokens x 128, fp16; "
+                        "keys prod b=3, values mse b=3, dense rotation; 16 query heads per layer (gqa 8)",
+            "tokens": T_, "layers": L_, "kv_heads": H_, "head_dim": D_, "query_heads_per_kv_head": G_,
+            "bits": BITS,
+        },
+        "frac_hbm_peak": round(score_gbs / HBM_PEAK_GBS, 4),
+        "encoded_vectors_per_s": round(enc_rate, 1),
+        "kernels_ms": {"encode_prod": round(t_ek, 5), "encode_mse": round(t_ev, 5),
+                       "scores": round(t_sc, 5), "attend": round(t_at, 5)},
+        "attend_GBps": round(attend_gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tq_scores (query prep + score kernel)",
+                     "bytes_per_launch": score_bytes},
+        "roofline_encode": {"bound": "mfma", "achieved": round(enc_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(enc_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                            "executed_TFLOPs": round(enc_exec_tflops, 2),
+                            "note": "algorithmic 2 x 2 d^2 flops per key and 2 d^2 per value; the kernels "
+                                    "run fp16 hi/lo MFMA passes (5 per key product pair, 2 per value)"},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
