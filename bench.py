@@ -121,8 +121,8 @@ def main():
     q = torch.from_numpy(gaussian_queries(segs * G_, D_, seed=SEED)).cuda()
     scores = torch.empty((segs * G_, T_), dtype=torch.float32, device="cuda")
     out = torch.empty((segs * G_, D_), dtype=torch.float32, device="cuda")
-    ws_s = torch.empty(tq.scores_workspace(pk_, segs, G_), dtype=torch.uint8, device="cuda")
-    ws_a = torch.empty(tq.attend_workspace(pk_, pv_, segs, G_, T_), dtype=torch.uint8, device="cuda")
+    ws_s = tq.alloc_workspace(tq.scores_workspace(pk_, segs, G_))
+    ws_a = tq.alloc_workspace(tq.attend_workspace(pk_, pv_, segs, G_, T_))
     scale = 1.0 / np.sqrt(D_)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)

@@ -148,7 +148,11 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
  * keys    packed prod cache, segment s at records s*seg_stride + t
  * len     device int32 [segs] valid tokens per segment (<= T), or NULL for T
  * scores  device f32 [segs*group][T]; entries with t >= len are not written
- * ws      device workspace of at least tq_scores_workspace() bytes, 256-B aligned */
+ * ws      device workspace of at least tq_scores_workspace() bytes, 256-B
+ *         aligned, no initial contents required; it receives each segment's
+ *         query pack (rotated and projected query heads quantised to the
+ *         matrix-core operand), so one call in flight per workspace.
+ * Two launches on the stream: the query pack, then the streaming score pass. */
 tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
                     const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
                     void* stream);
@@ -165,8 +169,10 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
  * vals    packed mse value cache (block layout), vals.seg_stride a multiple of
  *         32 and, like keys.seg_stride, >= T; its scalars must cover
  *         segs * seg_stride records
- * Other arguments as for tq_scores.  Supported: d = 128, group <= 16, value
- * bits 1..3. */
+ * Other arguments as for tq_scores (ws: tq_attend_workspace() bytes).  Three
+ * launches: the query pack, the streaming pass (one log-sum-exp partial per
+ * workgroup) and the per-segment merge with the inverse value rotation.
+ * Supported: d = 128, group <= 16, value bits 1..3. */
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs,
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);

@@ -207,6 +207,13 @@ def scores_workspace(kp: Params, segs: int, group: int) -> int:
     return int(lib().tq_scores_workspace(kp.c, segs, group))
 
 
+def alloc_workspace(nbytes: int, device="cuda"):
+    """A device workspace of nbytes (zero-filled; the library needs no initial
+    contents)."""
+    import torch
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def scores(kp: Params, q, segs: int, group: int, keys: Cache, T: int, out, ws, length=None,
            stream=None):
     _check(lib().tq_scores(kp.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),

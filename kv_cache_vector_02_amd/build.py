@@ -29,6 +29,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-result", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# decode kernels: matrix-core results straight into VGPRs (no AGPR read-back)
+EXTRA = {"tq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -40,7 +42,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         msg = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -200,6 +200,9 @@ tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
   const size_t need = tq::scores128_workspace(segs, group);
   if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
+  const int64_t stride = segs == 1 && keys.seg_stride < T ? T : keys.seg_stride;
+  if (stride * 16 * kp->bits >= (1ll << 31) || (int64_t)group * T * 4 >= (1ll << 31))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_scores addresses at most 2 GiB of keys and of scores per segment");
   a.q = q;
   a.segs = segs;
   a.group = group;
@@ -211,7 +214,7 @@ tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq
   a.bq = kp->bits - 1;
   a.planes = (const uint32_t*)keys.planes;
   a.scalars = (const uint16_t*)keys.scalars;
-  a.seg_stride = keys.seg_stride;
+  a.seg_stride = stride;
   a.len = len;
   a.T = T;
   a.scores = scores;
@@ -252,6 +255,10 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   if (T == 0) return fail(TQ_ERR_INVALID_ARG, "T must be >= 1");
   const size_t need = tq::attend128_workspace(segs, group, T);
   if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
+  const int64_t kstride = segs == 1 && keys.seg_stride < T ? T : keys.seg_stride;
+  const int64_t vstride = segs == 1 && vals.seg_stride < T ? (T + 31) / 32 * 32 : vals.seg_stride;
+  if (kstride * 16 * kp->bits >= (1ll << 31) || vstride * 16 * vp->bits >= (1ll << 31))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attend addresses at most 2 GiB of keys and of values per segment");
   a.k.q = q;
   a.k.segs = segs;
   a.k.group = group;
@@ -263,7 +270,7 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   a.k.bq = kp->bits - 1;
   a.k.planes = (const uint32_t*)keys.planes;
   a.k.scalars = (const uint16_t*)keys.scalars;
-  a.k.seg_stride = keys.seg_stride;
+  a.k.seg_stride = kstride;
   a.k.len = len;
   a.k.T = T;
   a.k.ws = ws;
@@ -273,7 +280,7 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   a.bq_v = vp->bits;
   a.planes_v = (const uint32_t*)vals.planes;
   a.scalars_v = (const uint16_t*)vals.scalars;
-  a.seg_stride_v = vals.seg_stride;
+  a.seg_stride_v = vstride;
   a.scale = scale;
   a.out = out;
   a.ws = ws;

@@ -33,6 +33,7 @@
 // group kg (= lane / 16) of every MFMA reads plane word kg (coordinates
 // 32 kg .. 32 kg + 31); MFMA m in {0, 1} of a plane takes expansion dwords
 // k = 4m .. 4m+3, dword k byte i being bit 8 i + k of the word.
+#include <atomic>
 #include <cmath>
 
 #include "tq_device.h"
@@ -67,19 +68,19 @@ struct PrepArgs {
   uint8_t* ws;
 };
 
-// One workgroup (4 waves) per segment.  Both 128x128 products run on the
+// One workgroup (8 waves) per segment.  Both 128x128 products run on the
 // matrix cores (v_mfma_f32_16x16x32_bf16) with bf16 hi/lo splits of both
-// operands (three products, ~2^-16 relative, far below the 2^-14 integer
+// operands (three products, ~2^-16 relative, far below the 2^-21 integer
 // quantisation that follows; bf16 keeps fp32's range, so no rescaling):
 //   q_rot^T = Pi . Q^T         (dense; the Hadamard form uses +-eps entries)
 //   q_proj^T = S . q_rot^T
-// wave w owns output rows 32 w .. 32 w + 31, heads on the N axis.  Every
-// global operand is loaded up front (one memory round trip); the per-head
-// statistics reduce in registers, then the int8 A-operand fragments are
-// assembled in LDS and copied out with 16-byte stores.
+// wave w owns output rows 16 w .. 16 w + 15, heads on the N axis.  Every
+// global operand is loaded up front (one memory round trip); per-head
+// statistics reduce through shuffles and LDS; the quantiser then builds whole
+// A-operand dwords (four coordinates, one slice) and stores them to the pack.
 constexpr int MAXG = 16;
-constexpr int QLD = MAXG + 1;
-constexpr int MAXFRAG = 4 * 10 * 1024;   // MT <= 4, F <= 10
+constexpr int QTS = D + 4;               // LDS row stride (floats) of the head-major q tiles
+constexpr int PREP_THREADS = 512;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -92,28 +93,39 @@ __device__ __forceinline__ void split8_bf16(const float* v, bf16x8& hi, bf16x8& 
   }
 }
 
-__device__ __forceinline__ f32x4 mfma3_bf16(const float* av, const float* bv, f32x4 acc) {
-  bf16x8 ah, al, bh, bl;
-  split8_bf16(av, ah, al);
-  split8_bf16(bv, bh, bl);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-  return acc;
-}
-
 __device__ __forceinline__ void unpack8(float4 a, float4 b, float* v) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// 21-bit integer weight -> int8 slices hi, mid, lo with q = 2^14 hi + 2^7 mid + lo
+__device__ __forceinline__ void slices3(float w, int& hi, int& mid, int& lo) {
+  const int qi = (int)rintf(fminf(fmaxf(w, -QMAX3), QMAX3));
+  hi = (qi + 8192) >> 14;
+  const int rem = qi - 16384 * hi;
+  mid = (rem + 64) >> 7;
+  lo = rem - 128 * mid;
+}
+
+__device__ __forceinline__ uint32_t pack4(int b0, int b1, int b2, int b3) {
+  return (uint32_t)(b0 & 0xff) | ((uint32_t)(b1 & 0xff) << 8) | ((uint32_t)(b2 & 0xff) << 16) |
+         ((uint32_t)b3 << 24);
+}
+
+struct PrepLds {
+  float qr[MAXG * QTS];      // q_rot[head][coordinate]
+  float qp[MAXG * QTS];      // q_proj[head][coordinate]
+  float part[8][MAXG][4];
+  float stat[MAXG][4];
+};
+
+// Segment seg's query pack -> dst (all 512 threads of the workgroup).
 template <bool HAD>
-__global__ __launch_bounds__(256) void prep_queries128(PrepArgs a) {
-  __shared__ float qr[D * QLD], qp[D * QLD];
-  __shared__ __align__(16) uint8_t frag[MAXFRAG];
-  __shared__ float part[4][MAXG][4];
-  __shared__ float stat[MAXG][4];
-  const int seg = blockIdx.x;
+__device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L, uint8_t* dst) {
+  float* qr = L.qr;
+  float* qp = L.qp;
+  auto& part = L.part;
+  auto& stat = L.stat;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int col = lane & 15, kq = lane >> 4;
@@ -122,107 +134,101 @@ __global__ __launch_bounds__(256) void prep_queries128(PrepArgs a) {
   const int F = 2 * (np + 1);
   const int fbytes = (int)pack_frag_bytes(a.mt, F);
   const bool live = col < G;
+  const int row = 16 * wave + col;        // A-operand row of this lane
 
   // ---- every global operand of this lane, in flight together ----
-  float4 qv[8], mv[16], sv[16];
+  float4 qv[8], mv[8], sv[8];
   const float4* qh = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + (live ? col : 0)) * D);
+  const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)(HAD ? 0 : row) * D);
+  const float4* srow = reinterpret_cast<const float4*>(a.s + (size_t)row * D);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    qv[2 * ks] = qh[(32 * ks + 8 * kq) / 4];
-    qv[2 * ks + 1] = qh[(32 * ks + 8 * kq) / 4 + 1];
-  }
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int row = 16 * (2 * wave + mi) + col;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int k0 = 32 * ks + 8 * kq;
-      if (HAD) {
-        mv[(mi * 4 + ks) * 2] = reinterpret_cast<const float4*>(a.eps)[k0 / 4];
-        mv[(mi * 4 + ks) * 2 + 1] = reinterpret_cast<const float4*>(a.eps)[k0 / 4 + 1];
-      } else {
-        const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)row * D + k0);
-        mv[(mi * 4 + ks) * 2] = prow[0];
-        mv[(mi * 4 + ks) * 2 + 1] = prow[1];
-      }
-      const float4* srow = reinterpret_cast<const float4*>(a.s + (size_t)row * D + k0);
-      sv[(mi * 4 + ks) * 2] = srow[0];
-      sv[(mi * 4 + ks) * 2 + 1] = srow[1];
+    const int k4 = (32 * ks + 8 * kq) / 4;
+    qv[2 * ks] = qh[k4];
+    qv[2 * ks + 1] = qh[k4 + 1];
+    if (HAD) {
+      mv[2 * ks] = reinterpret_cast<const float4*>(a.eps)[k4];
+      mv[2 * ks + 1] = reinterpret_cast<const float4*>(a.eps)[k4 + 1];
+    } else {
+      mv[2 * ks] = prow[k4];
+      mv[2 * ks + 1] = prow[k4 + 1];
     }
+    sv[2 * ks] = srow[k4];
+    sv[2 * ks + 1] = srow[k4 + 1];
   }
-  for (int i = t; i < fbytes / 16; i += blockDim.x) reinterpret_cast<uint4*>(frag)[i] = make_uint4(0, 0, 0, 0);
 
-  // ---- q_rot^T = Pi . Q^T ----
-  float rmax = 0.f, rsum = 0.f;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int mt = 2 * wave + mi;
-    const int j = 16 * mt + col;
+  // ---- q_rot^T = Pi . Q^T, rows 16 wave + 4 kq + r, head col ----
+  {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int k0 = 32 * ks + 8 * kq;
       float av[8], bv[8];
-      unpack8(mv[(mi * 4 + ks) * 2], mv[(mi * 4 + ks) * 2 + 1], av);
+      unpack8(mv[2 * ks], mv[2 * ks + 1], av);
       if (HAD) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) av[e] = (__popc(j & (k0 + e)) & 1) ? -av[e] : av[e];
+        for (int e = 0; e < 8; ++e) av[e] = (__popc(row & (k0 + e)) & 1) ? -av[e] : av[e];
       }
       unpack8(qv[2 * ks], qv[2 * ks + 1], bv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) bv[e] = live ? bv[e] : 0.f;
-      acc = mfma3_bf16(av, bv, acc);
+      bf16x8 ah, al, bh, bl;
+      split8_bf16(av, ah, al);
+      split8_bf16(bv, bh, bl);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
     }
     const float sc = HAD ? rsqrtf((float)D) : 1.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = acc[r] * sc;
-      qr[(16 * mt + 4 * kq + r) * QLD + col] = v;
-      rmax = fmaxf(rmax, fabsf(v));
-      rsum += v;
+    float4 v = {acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc};
+    *reinterpret_cast<float4*>(&qr[col * QTS + 16 * wave + 4 * kq]) = v;
+    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    float sm = (v.x + v.y) + (v.z + v.w);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    sm += __shfl_xor(sm, 16, 64);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    sm += __shfl_xor(sm, 32, 64);
+    if (kq == 0) {
+      part[wave][col][0] = mx;
+      part[wave][col][1] = sm;
     }
   }
   __syncthreads();
   // ---- q_proj^T = S . q_rot^T ----
-  float pmax = 0.f, psum = 0.f;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int mt = 2 * wave + mi;
+  {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int k0 = 32 * ks + 8 * kq;
       float av[8], bv[8];
-      unpack8(sv[(mi * 4 + ks) * 2], sv[(mi * 4 + ks) * 2 + 1], av);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bv[e] = qr[(k0 + e) * QLD + col];
-      acc = mfma3_bf16(av, bv, acc);
+      unpack8(sv[2 * ks], sv[2 * ks + 1], av);
+      const float4* src = reinterpret_cast<const float4*>(&qr[col * QTS + k0]);
+      unpack8(src[0], src[1], bv);
+      bf16x8 ah, al, bh, bl;
+      split8_bf16(av, ah, al);
+      split8_bf16(bv, bh, bl);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      qp[(16 * mt + 4 * kq + r) * QLD + col] = acc[r];
-      pmax = fmaxf(pmax, fabsf(acc[r]));
-      psum += acc[r];
+    float4 v = {acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<float4*>(&qp[col * QTS + 16 * wave + 4 * kq]) = v;
+    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    float sm = (v.x + v.y) + (v.z + v.w);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    sm += __shfl_xor(sm, 16, 64);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    sm += __shfl_xor(sm, 32, 64);
+    if (kq == 0) {
+      part[wave][col][2] = mx;
+      part[wave][col][3] = sm;
     }
-  }
-  // ---- per-head statistics: lanes col, col+16, col+32, col+48 of every wave ----
-#pragma unroll
-  for (int o = 16; o < 64; o <<= 1) {
-    rmax = fmaxf(rmax, __shfl_xor(rmax, o, 64));
-    pmax = fmaxf(pmax, __shfl_xor(pmax, o, 64));
-    rsum += __shfl_xor(rsum, o, 64);
-    psum += __shfl_xor(psum, o, 64);
-  }
-  if (kq == 0) {
-    part[wave][col][0] = rmax;
-    part[wave][col][1] = rsum;
-    part[wave][col][2] = pmax;
-    part[wave][col][3] = psum;
   }
   __syncthreads();
   if (t < MAXG) {
     float mx = 0.f, sr = 0.f, px = 0.f, sp = 0.f;
-    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
       mx = fmaxf(mx, part[w][t][0]);
       sr += part[w][t][1];
       px = fmaxf(px, part[w][t][2]);
@@ -237,35 +243,43 @@ __global__ __launch_bounds__(256) void prep_queries128(PrepArgs a) {
     stat[t][3] = -sp;
   }
   __syncthreads();
-  // ---- quantise and scatter into the LDS fragments ----
-  {
-    const int j = t & (D - 1);
-    const int hs = t >> 7;
-    const int kg = j >> 5, b = j & 31;
-    const int bi = b >> 3, m = (b & 7) >> 2, k = b & 3;
-    for (int h = hs; h < G; h += 2) {
-      const int mt = h >> 2, hl = h & 3;
-      const float inv_m = 1.f / stat[h][0], inv_q = 1.f / stat[h][2];
-      for (int p = 0; p <= np; ++p) {
-        const float w = p < np ? 2.f * a.u[p] * qr[j * QLD + h] * inv_m : 2.f * qp[j * QLD + h] * inv_q;
-        const int qi = (int)rintf(fminf(fmaxf(w, -QMAX3), QMAX3));
-        const int hi = (qi + 8192) >> 14;
-        const int rem = qi - 16384 * hi;
-        const int mid = (rem + 64) >> 7;
-        const int lo = rem - 128 * mid;
-        const int off = ((mt * F + 2 * p + m) * 64 + 4 * hl + 16 * kg) * 16 + 4 * k + bi;
-        frag[off] = (uint8_t)(int8_t)hi;        // rows 4 hl, 4 hl + 1, 4 hl + 2 are
-        frag[off + 16] = (uint8_t)(int8_t)mid;  // consecutive lanes
-        frag[off + 32] = (uint8_t)(int8_t)lo;
-      }
+  // ---- quantise: one item = (tile mt, fragment f = 2 p + m, lane group kg,
+  // head hl, dword k); its four bytes bi = 0..3 are coordinates
+  // 32 kg + 8 bi + 4 m + k, and its slices are lanes 16 kg + 4 hl + {0, 1, 2}
+  // (lane 16 kg + 4 hl + 3 is the zero row) ----
+  const int nitems = a.mt * F * 64;
+  for (int it = t; it < nitems; it += PREP_THREADS) {
+    const int k = it & 3, hl = (it >> 2) & 3, kg = (it >> 4) & 3;
+    const int f = (it >> 6) % F, mt = (it >> 6) / F;
+    const int p = f >> 1, m = f & 1;
+    const int h = 4 * mt + hl;
+    uint32_t d0 = 0, d1 = 0, d2 = 0;
+    if (h < G) {
+      const float* src = p < np ? &qr[h * QTS] : &qp[h * QTS];
+      const float up = p == 0 ? a.u[0] : p == 1 ? a.u[1] : p == 2 ? a.u[2] : a.u[3];
+      const float wsc = p < np ? 2.f * up / stat[h][0] : 2.f / stat[h][2];
+      int s0[4], s1[4], s2[4];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) slices3(src[32 * kg + 8 * bi + 4 * m + k] * wsc, s0[bi], s1[bi], s2[bi]);
+      d0 = pack4(s0[0], s0[1], s0[2], s0[3]);
+      d1 = pack4(s1[0], s1[1], s1[2], s1[3]);
+      d2 = pack4(s2[0], s2[1], s2[2], s2[3]);
     }
+    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst) + ((mt * F + f) * 64 + 16 * kg + 4 * hl) * 4 + k;
+    d32[0] = d0;
+    d32[4] = d1;
+    d32[8] = d2;
+    d32[12] = 0u;
   }
-  __syncthreads();
-  uint8_t* base = a.ws + (size_t)seg * pack_bytes(a.mt, F);
-  for (int i = t; i < fbytes / 16; i += blockDim.x)
-    reinterpret_cast<uint4*>(base)[i] = reinterpret_cast<const uint4*>(frag)[i];
-  float* consts = reinterpret_cast<float*>(base + fbytes);
+  float* consts = reinterpret_cast<float*>(dst + fbytes);
   if (t < a.mt * 4 * 4) consts[t] = t < G * 4 ? stat[t >> 2][t & 3] : 0.f;
+}
+
+template <bool HAD>
+__global__ __launch_bounds__(PREP_THREADS) void prep_queries128(PrepArgs a) {
+  __shared__ PrepLds L;
+  const int F = 2 * (mse_planes(a.bq) + 1);
+  prep_pack<HAD>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
 }
 
 struct Score128Args {
@@ -307,28 +321,95 @@ struct Words<4> {
 
 constexpr int SROW = 40;   // LDS row stride (floats) of the output transpose tile
 
-// One workgroup = 4 waves = chunk_tiles 16-token tiles of one segment.  A wave
-// takes pairs of adjacent tiles (32 tokens); the 32 x 8 outputs of a 16-row
-// tile pass through a per-wave LDS tile so that each lane stores 4 consecutive
+// Raw buffer access: a 128-bit descriptor (base, byte size) in scalar
+// registers and a per-lane byte offset (the scalar offset operand stays 0: the
+// range check covers the per-lane offset only).  Reads at or past the size
+// return zero and writes there are dropped, which bounds every access without
+// per-lane clamps; OOB_OFFSET marks a lane whose access must not happen.
+// Descriptor sizes stay below 2^31 (checked on the host) so that OOB_OFFSET
+// plus an access width never wraps into range.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_FLAGS = 0x00020000;    // raw 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_FLAGS);
+}
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
+  return b <= 0 ? 0u : (b >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)b);
+}
+
+template <int P>
+__device__ __forceinline__ typename Words<P>::v load_words(rsrc_t r, uint32_t voff) {
+  typedef typename Words<P>::v wv;
+  if constexpr (P == 1) {
+    wv w;
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+    return w;
+  } else if constexpr (P == 2) {
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+  } else if constexpr (P == 3) {
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0));
+  } else {
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+  }
+}
+
+__device__ __forceinline__ int combine3(i32x4 acc) {
+  return (acc[0] * 128 + acc[1]) * 128 + acc[2];   // 2^14 hi + 2^7 mid + lo
+}
+
+// Workgroup = 8 waves = chunk_tiles 16-token tiles of one segment.  A wave
+// takes pairs of adjacent tiles (32 tokens), pairs wave, wave + 8, ...,
+// with RING pairs of loads in flight; the 32 x 8 outputs of a 16-row tile
+// pass through a per-wave LDS tile so that each lane stores 4 consecutive
 // tokens of one head (16 bytes) and a store covers whole 128-byte lines.
+constexpr int SC_WAVES = 8;
+
 template <int BQ, int MT>
-__global__ __launch_bounds__(256) void scores128(Score128Args a) {
+__global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
   constexpr int NP = mse_planes(BQ);      // MSE planes after the parity plane
   constexpr int F = 2 * (NP + 1);         // MFMAs per tile per 16-row tile
   constexpr int P = BQ + 1;               // stored planes per key record
+  constexpr uint32_t RB = 16 * P;         // plane bytes per key record
+  constexpr int RING = 4;
   typedef typename Words<P>::v wvec;
-  __shared__ __align__(16) float sbuf[4][MT * 4 * SROW];
-  const int seg = blockIdx.y;
+  __shared__ __align__(16) float sbufs[SC_WAVES][MT * 4 * SROW];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15;
   const int kg = lane >> 4;
+  const int seg = blockIdx.y;
   const int64_t len = a.len ? (int64_t)a.len[seg] : a.T;
   const int64_t tok0 = (int64_t)blockIdx.x * a.chunk_tiles * 16;
   if (tok0 >= len) return;
 
-  // query fragments and per-head constants for this segment
+  const int64_t rec0 = seg * a.seg_stride + tok0;
+  const rsrc_t rk = make_rsrc(a.planes + rec0 * (P * 4), clamp_bytes((a.seg_stride - tok0) * RB));
+  const rsrc_t rs = make_rsrc(a.scalars + rec0 * 2, clamp_bytes((a.seg_stride - tok0) * 4));
+  const rsrc_t ro = make_rsrc(a.scores + (size_t)seg * a.group * a.T + tok0,
+                              clamp_bytes(((int64_t)(a.group - 1) * a.T + a.T - tok0) * 4));
+  const uint32_t vk = t16 * RB + kg * (P * 4);
+  const uint32_t vs = t16 * 4;
+  const int ntok = (int)(len - tok0 < (int64_t)a.chunk_tiles * 16 ? len - tok0 : (int64_t)a.chunk_tiles * 16);
+  const int npairs = (ntok + 31) / 32;
+
+  wvec wr[RING][2];
+  uint32_t sr[RING][2];
+  auto issue_ring = [&]() {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      const uint32_t tb = (uint32_t)(32 * (wave + SC_WAVES * j));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        wr[j][h] = load_words<P>(rk, vk + (tb + 16 * h) * RB);
+        sr[j][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + (tb + 16 * h) * 4, 0, 0);
+      }
+    }
+  };
+  issue_ring();
   const uint8_t* pack = a.ws + (size_t)seg * pack_bytes(MT, F);
+
   i32x4 afr[MT][F];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -336,33 +417,18 @@ __global__ __launch_bounds__(256) void scores128(Score128Args a) {
     for (int f = 0; f < F; ++f)
       afr[mt][f] = reinterpret_cast<const i32x4*>(pack)[(mt * F + f) * 64 + lane];
   const float* consts = reinterpret_cast<const float*>(pack + pack_frag_bytes(MT, F));
-  float cst[MT][4];     // head 4 mt + kg: sigma_mse, const_mse, sigma_qjl, const_qjl
+  float cst[MT][4];     // head 4 mt + kg: sigma_mse, const_mse, kappa sigma_qjl, kappa const_qjl
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) cst[mt][c] = consts[(mt * 4 + kg) * 4 + c];
+    cst[mt][2] *= a.kappa;
+    cst[mt][3] *= a.kappa;
+  }
+  float* sbuf = sbufs[wave];
 
-  // segment bases (uniform) and 32-bit per-lane offsets
-  const uint32_t* seg_planes = a.planes + (seg * a.seg_stride + tok0) * (P * 4) + kg * P;
-  const uint32_t* seg_scal = reinterpret_cast<const uint32_t*>(a.scalars) + seg * a.seg_stride + tok0;
-  float* out = a.scores + (size_t)seg * a.group * a.T + tok0;
-
-  int ntok = (int)(len - tok0 < (int64_t)a.chunk_tiles * 16 ? len - tok0 : (int64_t)a.chunk_tiles * 16);
-  const int npairs = (ntok + 31) / 32;
-  const int lastt = ntok - 1;
-  // loads are unconditional, clamped to the last valid token, so no
-  // exec-masked branches surround them
-  auto load = [&](int tt, wvec& w, uint32_t& sc) {
-    const int t = tt < lastt ? tt : lastt;
-    w = *reinterpret_cast<const wvec*>(seg_planes + t * (P * 4));
-    sc = seg_scal[t];
-  };
-  // one 16-token tile -> LDS rows (heads 2 kg, 2 kg + 1), columns col0 + t16
-  auto compute = [&](int tt, wvec wl, uint32_t scl, int col0) {
-    const bool valid = tt < ntok;
-    uint32_t w[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) w[p] = valid ? wl[p] : 0u;
+  // one 16-token tile -> LDS rows (heads 4 mt + kg), columns col0 + t16
+  auto compute = [&](wvec w, uint32_t scl, int col0) {
     i32x4 am[MT], aq[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
@@ -389,63 +455,70 @@ __global__ __launch_bounds__(256) void scores128(Score128Args a) {
       }
     }
     const float n = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl & 0xffff));
-    const float gk = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl >> 16)) * a.kappa;
+    const float g = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl >> 16));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int im = am[mt][0] * 16384 + am[mt][1] * 128 + am[mt][2];
-      const int iq = aq[mt][0] * 16384 + aq[mt][1] * 128 + aq[mt][2];
-      const float mse = (float)im * cst[mt][0] + cst[mt][1];
-      const float qjl = (float)iq * cst[mt][2] + cst[mt][3];
-      sbuf[wave][(4 * mt + kg) * SROW + col0 + t16] = n * fmaf(gk, qjl, mse);
+      const float mse = fmaf((float)combine3(am[mt]), cst[mt][0], cst[mt][1]);
+      const float qjl = fmaf((float)combine3(aq[mt]), cst[mt][2], cst[mt][3]);
+      sbuf[(4 * mt + kg) * SROW + col0 + t16] = n * fmaf(g, qjl, mse);
     }
   };
-  // lanes 8 h' + c store tokens 4c .. 4c+3 of head 8 r + h' of the pair
+  // lanes 8 h' + c store tokens 4c .. 4c+3 of head 8 r + h' of the pair;
+  // padded heads and tokens past ntok get an offset past the descriptor
+  const int hr = lane >> 3, c4 = 4 * (lane & 7);
   auto flush = [&](int pbase) {
-    const int hr = lane >> 3, c4 = 4 * (lane & 7);
+    const bool full = pbase + 32 <= ntok;
 #pragma unroll
     for (int rr = 0; rr < (MT + 1) / 2; ++rr) {
       const int head = rr * 8 + hr;
-      if (head >= a.group) continue;
-      const float4 v = *reinterpret_cast<const float4*>(&sbuf[wave][head * SROW + c4]);
-      float* dst = out + (size_t)head * a.T + pbase + c4;
-      if (pbase + c4 + 3 < ntok) {
-        *reinterpret_cast<float4*>(dst) = v;
+      const int hread = head < MT * 4 ? head : 0;
+      const float4 v = *reinterpret_cast<const float4*>(&sbuf[hread * SROW + c4]);
+      const uint32_t vo = (uint32_t)(head * a.T + pbase + c4) * 4u;
+      const bool live = head < a.group;
+      if (full) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), ro, live ? vo : OOB_OFFSET, 0, 0);
       } else {
-        if (pbase + c4 < ntok) dst[0] = v.x;
-        if (pbase + c4 + 1 < ntok) dst[1] = v.y;
-        if (pbase + c4 + 2 < ntok) dst[2] = v.z;
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t o = live && pbase + c4 + e < ntok ? vo + 4 * e : OOB_OFFSET;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, vv[e]), ro, o, 0, 0);
+        }
       }
     }
   };
 
-  wvec w0, w1, w2, w3;
-  uint32_t s0, s1, s2, s3;
-  int pr = wave;
-  load(32 * pr + t16, w0, s0);
-  load(32 * pr + 16 + t16, w1, s1);
-  load(32 * (pr + 4) + t16, w2, s2);
-  load(32 * (pr + 4) + 16 + t16, w3, s3);
-  for (; pr < npairs; pr += 8) {
-    compute(32 * pr + t16, w0, s0, 0);
-    compute(32 * pr + 16 + t16, w1, s1, 16);
-    load(32 * (pr + 8) + t16, w0, s0);
-    load(32 * (pr + 8) + 16 + t16, w1, s1);
-    flush(32 * pr);
-    if (pr + 4 < npairs) {
-      compute(32 * (pr + 4) + t16, w2, s2, 0);
-      compute(32 * (pr + 4) + 16 + t16, w3, s3, 16);
-      flush(32 * (pr + 4));
+  for (int i = 0;; i += RING) {
+#pragma unroll
+    for (int j = 0; j < RING; ++j) {
+      const int pr = wave + SC_WAVES * (i + j);
+      if (pr >= npairs) return;
+      compute(wr[j][0], sr[j][0], 0);
+      compute(wr[j][1], sr[j][1], 16);
+      const uint32_t tb = (uint32_t)(32 * (pr + SC_WAVES * RING));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        wr[j][h] = load_words<P>(rk, vk + (tb + 16 * h) * RB);
+        sr[j][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + (tb + 16 * h) * 4, 0, 0);
+      }
+      flush(32 * pr);
     }
-    load(32 * (pr + 12) + t16, w2, s2);
-    load(32 * (pr + 12) + 16 + t16, w3, s3);
   }
 }
 
+int device_cus();
+int occupancy(const void* kernel, int threads);
+int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax);
+
+// Grid: (workgroups per segment, segments), sized so that the whole grid is
+// resident at once; a workgroup's span is a multiple of 8 waves x 32 tokens.
 template <int BQ, int MT>
-hipError_t launch_scores(const Score128Args& s, int segs, hipStream_t stream) {
-  const int64_t tiles = (s.T + 15) / 16;
-  const int64_t chunks = (tiles + s.chunk_tiles - 1) / s.chunk_tiles;
-  hipLaunchKernelGGL((scores128<BQ, MT>), dim3((unsigned)chunks, (unsigned)segs), dim3(256), 0, stream, s);
+hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
+  static const int nb = occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT>), SC_WAVES * 64);
+  const int64_t span = split_span(segs, s.T, nb * device_cus(), 32 * SC_WAVES, (s.T + 255) / 256);
+  s.chunk_tiles = (int)(span / 16);
+  const int64_t chunks = (s.T + span - 1) / span;
+  hipLaunchKernelGGL((scores128<BQ, MT>), dim3((unsigned)chunks, (unsigned)segs), dim3(SC_WAVES * 64), 0, stream, s);
   return hipGetLastError();
 }
 
@@ -472,6 +545,36 @@ void walsh_coefficients(const Codebook& cb, int bq, float u[4], float* usum) {
   *usum = (float)tot;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Resident workgroups per compute unit of a kernel at the given block size.
+int occupancy(const void* kernel, int threads) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb <= 0) nb = 1;
+  return nb;
+}
+
+// Split each segment's T tokens over k workgroups so that segs * k fills the
+// device once: span = tokens per workgroup, a multiple of gran.
+int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax) {
+  int64_t k = resident / (segs > 0 ? segs : 1);
+  if (k < 1) k = 1;
+  if (k > kmax) k = kmax;
+  const int64_t per = (T + k - 1) / k;
+  int64_t span = (per + gran - 1) / gran * gran;
+  return span < gran ? gran : span;
+}
+
 }  // namespace
 
 size_t scores128_workspace(int segs, int group) {
@@ -479,7 +582,7 @@ size_t scores128_workspace(int segs, int group) {
   return (size_t)segs * pack_bytes(mt, 2 * (mse_planes(3) + 1));   // sized for the widest key
 }
 
-hipError_t launch_scores128_prep(const ScoreArgs& a, hipStream_t stream) {
+static PrepArgs make_prep(const ScoreArgs& a) {
   PrepArgs p;
   p.q = a.q;
   p.segs = a.segs;
@@ -494,10 +597,15 @@ hipError_t launch_scores128_prep(const ScoreArgs& a, hipStream_t stream) {
   p.bq = a.bq;
   p.mt = (a.group + 3) / 4;
   p.ws = static_cast<uint8_t*>(a.ws);
+  return p;
+}
+
+hipError_t launch_scores128_prep(const ScoreArgs& a, hipStream_t stream) {
+  const PrepArgs p = make_prep(a);
   if (a.rot == TQ_ROT_HADAMARD)
-    hipLaunchKernelGGL(prep_queries128<true>, dim3(a.segs), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prep_queries128<true>, dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(prep_queries128<false>, dim3(a.segs), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prep_queries128<false>, dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -515,7 +623,7 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
   s.group = a.group;
   s.kappa = (float)(std::sqrt(M_PI / 2.0) / D);
   s.scores = a.scores;
-  s.chunk_tiles = 32;
+  s.chunk_tiles = 0;   // set by the launcher
   switch (a.bq * 10 + mt) {
     case 11: return launch_scores<1, 1>(s, a.segs, stream);
     case 12: return launch_scores<1, 2>(s, a.segs, stream);
@@ -551,14 +659,18 @@ namespace {
 // P' as the bit sums, so quantisation errors enter only through the
 // zero-mean centroids.
 //
-// Work split: a workgroup (4 waves) covers 512 tokens of one segment; a wave
-// owns one group of 128 tokens (8 key tiles; 4 value blocks).  The waves'
-// partials (m, l, o~) merge in LDS, one partial per (segment, chunk, head)
-// goes to the workspace, and attend_combine128 merges the chunks (log-sum-exp)
-// and applies Pi_v^T.
+// Work split: grid (chunks, segments); a workgroup (4 waves) covers `span`
+// tokens of one segment, sized so that the grid is resident at once, and a
+// wave takes its 128-token groups w, w + 4, ... (8 key tiles; 4 value blocks),
+// folding each into a running (m, l, o~) (online softmax).  The next group's
+// key words are requested once the current scores exist and its value words
+// once the current value sums are done, so loads overlap the arithmetic.  The
+// waves' partials merge in LDS, one partial per (segment, chunk, head) goes to
+// the workspace, and attend_combine128 merges the chunks (log-sum-exp),
+// normalises and applies Pi_v^T.
 // ---------------------------------------------------------------------------
 constexpr int PST = 132;        // partial: m, l, 2 pad, o~[128]
-constexpr int ACHUNK = 512;     // tokens per attend workgroup
+constexpr int AGRAN = 512;      // span granule: 4 waves x 128 tokens
 
 struct Attend128Args {
   const uint8_t* pack;          // key-side query fragments (prep_queries128)
@@ -576,38 +688,52 @@ struct Attend128Args {
   float vu[4];                  // value Walsh coefficients, odd subsets
   float vusum;
   float* part;                  // [segs][nchunks][group][PST]
-  int nchunks;
+  int nchunks;                  // workgroups per segment
+  int64_t span;                 // tokens per workgroup (multiple of AGRAN)
 };
 
-// position of group token tt in the A-operand byte rows (matches the value
-// expansion: block tt / 32, bit b -> MFMA (b % 8) / 4, dword b % 4, byte b / 8)
-__device__ __forceinline__ int vperm(int tt) {
-  const int b = tt & 31;
-  return (tt & ~31) + 16 * ((b & 7) >> 2) + 4 * (b & 3) + (b >> 3);
+__device__ __forceinline__ float f16lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffff)); }
+__device__ __forceinline__ float f16hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+
+// The P' A operand: row 4 kg + slice, byte position of group token tt
+//   32 (tt / 32) + 16 m + 4 k + i,  b = tt % 32 = 8 i + 4 m + k
+// (the value expansion's K-slot order).  Lane (t16, kg) owns tokens
+// 16 tile + t16; tiles 2 c and 2 c + 1 land in bytes i and i + 2 of dword
+// 8 c + 4 m + k with i = t16 / 8, and lane t16 ^ 8 owns the other two bytes,
+// so one rotate by 8 within a 16-lane row completes the dword.
+__device__ __forceinline__ uint32_t pair_bytes(int lo, int hi, int shift) {
+  return ((uint32_t)(lo & 0xff) | ((uint32_t)(hi & 0xff) << 16)) << shift;
+}
+__device__ __forceinline__ uint32_t row_ror8(uint32_t v) {
+  // DPP row_ror:8 (0x128): lane i of each 16-lane row reads lane (i + 8) % 16
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
 }
 
 template <int BQK, int BQV, int KMT>
-__global__ __launch_bounds__(256) void attend128(Attend128Args a) {
+__global__ __launch_bounds__(256, 2) void attend128(Attend128Args a) {
   constexpr int NPK = mse_planes(BQK);
   constexpr int FK = 2 * (NPK + 1);
   constexpr int PK = BQK + 1;
+  constexpr uint32_t RBK = 16 * PK;           // key plane bytes per record
   constexpr int NPV = mse_planes(BQV);
   constexpr int PV = BQV;
-  constexpr int NH = KMT * 4;               // heads of the 16-row tiles (4 each)
+  constexpr uint32_t VBB = D * PV * 4;        // value bytes per 32-token block
+  constexpr int NH = KMT * 4;                 // heads of the 16-row tiles (4 each)
   typedef typename Words<PK>::v kvec;
   typedef typename Words<PV>::v vvec;
   __shared__ float sred[4][NH][PST];
-  __shared__ __align__(16) uint8_t pq[4][KMT][16][128];
+  __shared__ __align__(16) uint32_t pq[4][KMT][16][32];   // A rows of P', 128 bytes each
   __shared__ float vnorm[4][128];
   const int seg = blockIdx.y;
   const int chunk = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15;
   const int kg = lane >> 4;
   const int64_t len = a.len ? (int64_t)a.len[seg] : a.T;
-  const int64_t g0 = (int64_t)chunk * ACHUNK + 128 * wave;
-  const int ntok = (int)(len - g0 <= 0 ? 0 : (len - g0 < 128 ? len - g0 : 128));
+  const int64_t c0 = (int64_t)chunk * a.span;
+  const int64_t c1 = len < c0 + a.span ? len : c0 + a.span;
+  const int ngroups = c1 > c0 ? (int)((c1 - c0 + 127) / 128) : 0;
 
   // lane group kg holds head 4 mt + kg on both sides
   float o_st[KMT][8], m_st[KMT], l_st[KMT];
@@ -618,58 +744,66 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o_st[mt][nt] = 0.f;
   }
+  // slice row 3 of every head stays zero
+#pragma unroll
+  for (int mt = 0; mt < KMT; ++mt) *reinterpret_cast<uint2*>(&pq[wave][mt][4 * kg + 3][2 * t16]) = make_uint2(0u, 0u);
 
-  if (ntok > 0) {
-    // ---- every global load of the group, in flight together ----
-    const int last = ntok - 1;
-    const uint32_t* kbase = a.kplanes + (seg * a.kstride + g0) * (PK * 4) + kg * PK;
-    const uint32_t* ksbase = reinterpret_cast<const uint32_t*>(a.kscal) + seg * a.kstride + g0;
-    kvec kw[8];
-    uint32_t ks[8];
+  // key-side fragments and constants (head 4 mt + kg)
+  const uint8_t* pack = a.pack + (size_t)seg * pack_bytes(KMT, FK);
+  i32x4 afr[KMT][FK];
+#pragma unroll
+  for (int mt = 0; mt < KMT; ++mt)
+#pragma unroll
+    for (int f = 0; f < FK; ++f)
+      afr[mt][f] = reinterpret_cast<const i32x4*>(pack)[(mt * FK + f) * 64 + lane];
+  const float* consts = reinterpret_cast<const float*>(pack + pack_frag_bytes(KMT, FK));
+  float cst[KMT][4];
+#pragma unroll
+  for (int mt = 0; mt < KMT; ++mt) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cst[mt][c] = consts[(mt * 4 + kg) * 4 + c] * (c < 2 ? a.scale2 : a.scale2 * a.kappa);
+  }
+
+  const int64_t krec0 = seg * a.kstride + c0;
+  const rsrc_t rk = make_rsrc(a.kplanes + krec0 * (PK * 4), clamp_bytes((a.kstride - c0) * RBK));
+  const rsrc_t rks = make_rsrc(a.kscal + krec0 * 2, clamp_bytes((a.kstride - c0) * 4));
+  const int64_t vrec0 = seg * a.vstride + c0;   // multiple of 32
+  const rsrc_t rv = make_rsrc(a.vplanes + (vrec0 / 32) * (D * PV), clamp_bytes((a.vstride - c0) / 32 * VBB));
+  const rsrc_t rvs = make_rsrc(a.vscal + vrec0, clamp_bytes((a.vstride - c0) * 2));
+  const uint32_t vko = t16 * RBK + kg * (PK * 4);
+  const uint32_t vkso = t16 * 4;
+  const uint32_t vvo = (kg * D + t16) * (PV * 4);
+  const uint32_t vno = lane * 4;
+
+  kvec kw[8];
+  uint32_t ks[8];
+  vvec vw[8];
+  uint32_t vn2;
+  auto load_keys = [&](int g) {
 #pragma unroll
     for (int tile = 0; tile < 8; ++tile) {
-      int tt = tile * 16 + t16;
-      tt = tt < last ? tt : last;
-      kw[tile] = *reinterpret_cast<const kvec*>(kbase + tt * (PK * 4));
-      ks[tile] = ksbase[tt];
+      const uint32_t tok = (uint32_t)(128 * g + 16 * tile);
+      kw[tile] = load_words<PK>(rk, vko + tok * RBK);
+      ks[tile] = __builtin_amdgcn_raw_buffer_load_b32(rks, vkso + tok * 4, 0, 0);
     }
-    // value block kg of the group (clamped to the last block holding tokens)
-    const int vb = kg < (last >> 5) ? kg : (last >> 5);
-    const uint32_t* vbase = a.vplanes + ((seg * a.vstride + g0) / 32 + vb) * (D * PV) + t16 * PV;
-    vvec vw[8];
+  };
+  auto load_vals = [&](int g) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) vw[nt] = *reinterpret_cast<const vvec*>(vbase + 16 * nt * PV);
-    {
-      int tt = 2 * lane;
-      tt = tt < last ? tt : (last & ~1);
-      const uint32_t nn = *reinterpret_cast<const uint32_t*>(a.vscal + seg * a.vstride + g0 + tt);
-      vnorm[wave][2 * lane] = 2 * lane < ntok ? (float)__builtin_bit_cast(_Float16, (uint16_t)(nn & 0xffff)) : 0.f;
-      vnorm[wave][2 * lane + 1] =
-          2 * lane + 1 < ntok ? (float)__builtin_bit_cast(_Float16, (uint16_t)(nn >> 16)) : 0.f;
-    }
-    // key-side fragments and constants (head 4 mt + kg)
-    const uint8_t* pack = a.pack + (size_t)seg * pack_bytes(KMT, FK);
-    i32x4 afr[KMT][FK];
-#pragma unroll
-    for (int mt = 0; mt < KMT; ++mt)
-#pragma unroll
-      for (int f = 0; f < FK; ++f)
-        afr[mt][f] = reinterpret_cast<const i32x4*>(pack)[(mt * FK + f) * 64 + lane];
-    const float* consts = reinterpret_cast<const float*>(pack + pack_frag_bytes(KMT, FK));
-    float cst[KMT][4];
-#pragma unroll
-    for (int mt = 0; mt < KMT; ++mt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) cst[mt][c] = consts[(mt * 4 + kg) * 4 + c];
+    for (int nt = 0; nt < 8; ++nt) vw[nt] = load_words<PV>(rv, vvo + (uint32_t)(4 * g) * VBB + nt * 16 * (PV * 4));
+    vn2 = __builtin_amdgcn_raw_buffer_load_b32(rvs, vno + (uint32_t)(256 * g), 0, 0);
+  };
+  load_keys(wave);
+  load_vals(wave);
 
-    // ---- phase 1: scores of the 8 key tiles (token t16 + 16 tile, head 4 mt + kg) ----
+  for (int g = wave; g < ngroups; g += 4) {
+    const int ntok = (int)(c1 - c0 - 128 * g < 128 ? c1 - c0 - 128 * g : 128);
+    vnorm[wave][2 * lane] = 2 * lane < ntok ? f16lo(vn2) : 0.f;
+    vnorm[wave][2 * lane + 1] = 2 * lane + 1 < ntok ? f16hi(vn2) : 0.f;
+
+    // ---- phase 1: logits (log2 units) of the 8 key tiles, token t16 + 16 tile ----
     float sc[8][KMT];
 #pragma unroll
     for (int tile = 0; tile < 8; ++tile) {
-      const bool valid = tile * 16 + t16 < ntok;
-      uint32_t w[PK];
-#pragma unroll
-      for (int p = 0; p < PK; ++p) w[p] = valid ? kw[tile][p] : 0u;
       i32x4 am[KMT], aq[KMT];
 #pragma unroll
       for (int mt = 0; mt < KMT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
@@ -677,11 +811,11 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
       for (int p = 0; p <= NPK; ++p) {
         uint32_t word;
         if (p == NPK) {
-          word = w[BQK];
+          word = kw[tile][BQK];
         } else if (p < BQK) {
-          word = w[p];
+          word = kw[tile][p];
         } else {
-          if constexpr (BQK == 3) word = w[0] ^ w[1] ^ w[2];
+          if constexpr (BQK == 3) word = kw[tile][0] ^ kw[tile][1] ^ kw[tile][2];
         }
         uint32_t e8[8];
         expand8(word, e8);
@@ -695,23 +829,24 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
           }
         }
       }
-      const float n = (float)__builtin_bit_cast(_Float16, (uint16_t)(ks[tile] & 0xffff));
-      const float gk = (float)__builtin_bit_cast(_Float16, (uint16_t)(ks[tile] >> 16)) * a.kappa;
+      const bool valid = tile * 16 + t16 < ntok;
+      const float n = f16lo(ks[tile]), gm = f16hi(ks[tile]);
 #pragma unroll
       for (int mt = 0; mt < KMT; ++mt) {
-        const int im = am[mt][0] * 16384 + am[mt][1] * 128 + am[mt][2];
-        const int iq = aq[mt][0] * 16384 + aq[mt][1] * 128 + aq[mt][2];
-        const float mse = (float)im * cst[mt][0] + cst[mt][1];
-        const float qjl = (float)iq * cst[mt][2] + cst[mt][3];
-        sc[tile][mt] = valid ? n * fmaf(gk, qjl, mse) * a.scale2 : -INFINITY;
+        const float mse = fmaf((float)combine3(am[mt]), cst[mt][0], cst[mt][1]);
+        const float qjl = fmaf((float)combine3(aq[mt]), cst[mt][2], cst[mt][3]);
+        sc[tile][mt] = valid ? n * fmaf(gm, qjl, mse) : -INFINITY;
       }
     }
+    load_keys(g + 4);
 
     // ---- phase 2: softmax statistics and the int8 P' rows ----
     float vn[8];
 #pragma unroll
     for (int tile = 0; tile < 8; ++tile) vn[tile] = vnorm[wave][tile * 16 + t16];
     float fsig[KMT];
+    const int bsh = 8 * (t16 >> 3);
+    const int dw0 = 4 * ((t16 >> 2) & 1) + (t16 & 3);
 #pragma unroll
     for (int mt = 0; mt < KMT; ++mt) {
       float mx = -INFINITY;
@@ -719,10 +854,12 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
       for (int tile = 0; tile < 8; ++tile) mx = fmaxf(mx, sc[tile][mt]);
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mref = fmaxf(m_st[mt], mx);           // running reference
+      const float alpha = __builtin_amdgcn_exp2f(m_st[mt] - mref);   // 0 on the first group
       float pv[8], ls = 0.f, pmax = 0.f;
 #pragma unroll
       for (int tile = 0; tile < 8; ++tile) {
-        const float pp = exp2f(sc[tile][mt] - mx);
+        const float pp = __builtin_amdgcn_exp2f(sc[tile][mt] - mref);
         ls += pp;
         pv[tile] = pp * vn[tile];
         pmax = fmaxf(pmax, pv[tile]);
@@ -736,26 +873,33 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
       const float inv = 1.f / sig;
       int qsum = 0;
 #pragma unroll
-      for (int tile = 0; tile < 8; ++tile) {
-        const int qi = (int)rintf(fminf(pv[tile] * inv, QMAX3));
-        qsum += qi;
-        const int hi = (qi + 8192) >> 14;
-        const int rem = qi - 16384 * hi;
-        const int mid = (rem + 64) >> 7;
-        const int lo = rem - 128 * mid;
-        const int pos = vperm(tile * 16 + t16);
-        pq[wave][mt][4 * kg][pos] = (uint8_t)(int8_t)hi;
-        pq[wave][mt][4 * kg + 1][pos] = (uint8_t)(int8_t)mid;
-        pq[wave][mt][4 * kg + 2][pos] = (uint8_t)(int8_t)lo;
-        pq[wave][mt][4 * kg + 3][pos] = 0;
+      for (int c = 0; c < 4; ++c) {
+        int s0[2], s1[2], s2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int qi = (int)rintf(fminf(pv[2 * c + h] * inv, QMAX3));
+          qsum += qi;
+          s0[h] = (qi + 8192) >> 14;
+          const int rem = qi - 16384 * s0[h];
+          s1[h] = (rem + 64) >> 7;
+          s2[h] = rem - 128 * s1[h];
+        }
+        const uint32_t d0 = pair_bytes(s0[0], s0[1], bsh);
+        const uint32_t d1 = pair_bytes(s1[0], s1[1], bsh);
+        const uint32_t d2 = pair_bytes(s2[0], s2[1], bsh);
+        const int dw = 8 * c + dw0;
+        pq[wave][mt][4 * kg][dw] = d0 | row_ror8(d0);
+        pq[wave][mt][4 * kg + 1][dw] = d1 | row_ror8(d1);
+        pq[wave][mt][4 * kg + 2][dw] = d2 | row_ror8(d2);
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) qsum += __shfl_xor(qsum, o, 64);
-      m_st[mt] = mx;
-      l_st[mt] = ls;
+      m_st[mt] = mref;
+      l_st[mt] = fmaf(alpha, l_st[mt], ls);
       fsig[mt] = sig;
+      const float cv0 = -a.vusum * sig * (float)qsum;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) o_st[mt][nt] = -a.vusum * sig * (float)qsum;
+      for (int nt = 0; nt < 8; ++nt) o_st[mt][nt] = fmaf(alpha, o_st[mt][nt], cv0);
     }
 
     // ---- phase 3: A operands (row = lane % 16, token bytes of block kg) ----
@@ -763,7 +907,7 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
 #pragma unroll
     for (int mt = 0; mt < KMT; ++mt)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) pa[mt][m] = *reinterpret_cast<const i32x4*>(&pq[wave][mt][t16][32 * kg + 16 * m]);
+      for (int m = 0; m < 2; ++m) pa[mt][m] = *reinterpret_cast<const i32x4*>(&pq[wave][mt][t16][8 * kg + 4 * m]);
 
     // ---- phase 4: value planes, each folded with its Walsh weight ----
 #pragma unroll
@@ -795,14 +939,13 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
       for (int mt = 0; mt < KMT; ++mt) {
         const float f = w2 * fsig[mt];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          o_st[mt][nt] = fmaf((float)(acc[mt][nt][0] * 16384 + acc[mt][nt][1] * 128 + acc[mt][nt][2]), f,
-                              o_st[mt][nt]);
+        for (int nt = 0; nt < 8; ++nt) o_st[mt][nt] = fmaf((float)combine3(acc[mt][nt]), f, o_st[mt][nt]);
       }
     }
+    load_vals(g + 4);
   }
 
-  // ---- phase 5: merge the four waves' partials in LDS ----
+  // ---- phase 5: merge the four waves' partials in LDS, publish the chunk's ----
 #pragma unroll
   for (int mt = 0; mt < KMT; ++mt) {
     float* r = sred[wave][4 * mt + kg];
@@ -829,7 +972,7 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
         const int src = c == 1 ? 1 : c + 2;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float wt = exp2f(sred[w][h][0] - M);     // 0 for empty waves
+          const float wt = __builtin_amdgcn_exp2f(sred[w][h][0] - M);     // 0 for empty waves
           v += wt * sred[w][h][src];
         }
       }
@@ -843,50 +986,135 @@ __global__ __launch_bounds__(256) void attend128(Attend128Args a) {
 struct Combine128Args {
   const float* part;
   int nchunks, group, d;
-  const int32_t* len;
-  int64_t T;
   int rot;
   const float* pi_v;
   const float* eps_v;
   float* out;
 };
 
-// One workgroup (128 threads) per query head: log-sum-exp merge of the chunk
-// partials, normalisation, then the inverse rotation o = Pi_v^T o~.
-__global__ __launch_bounds__(128) void attend_combine128(Combine128Args a) {
-  __shared__ float ot[D];
-  const int hg = blockIdx.x;               // seg * group + head
-  const int seg = hg / a.group, h = hg % a.group;
-  const int j = threadIdx.x;
-  const int64_t len = a.len ? (int64_t)a.len[seg] : a.T;
-  const int nch = (int)((len + ACHUNK - 1) / ACHUNK);
-  const float* base = a.part + (size_t)seg * a.nchunks * a.group * PST + (size_t)h * PST;
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, base[(size_t)c * a.group * PST]);
-  float L = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int c = 0; c < nch; ++c) {
-      const float* pc = base + (size_t)c * a.group * PST;
-      const float wt = exp2f(pc[0] - M);
-      L += wt * pc[1];
-      acc += wt * pc[4 + j];
+// One workgroup (256 threads) per segment: log-sum-exp merge of the chunk
+// partials of every head into LDS, then o = Pi_v^T o~ with Pi_v staged in
+// LDS (dense) or the inverse sign-flipped Hadamard transform.  Pi_v and the
+// partials of up to 8 chunks are requested together, so a segment with at
+// most 8 chunks costs one memory round trip.
+constexpr int CMB_G = 16;
+constexpr int CMB_B = 8;       // chunks merged per batch of loads
+__global__ __launch_bounds__(256, 1) void attend_combine128(Combine128Args a) {
+  __shared__ __align__(16) float pis[D * D];
+  __shared__ __align__(16) float ot[CMB_G][D];
+  const int seg = blockIdx.x;
+  const int t = threadIdx.x;
+  const bool dense = a.rot == TQ_ROT_DENSE;
+  if (dense) {
+    // Pi_v -> LDS by the direct global-to-LDS path: lane i of a wave's
+    // instruction fills 16 bytes at the wave's LDS base + 16 i
+    const int w = t >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(a.pi_v + (size_t)(256 * i + t) * 4),
+          (__attribute__((address_space(3))) void*)(pis + (256 * i + 64 * w) * 4), 16, 0, 0);
+  }
+  const float* pseg = a.part + (size_t)seg * a.nchunks * a.group * PST;
+  const int j4 = 4 * (t & 31);
+  for (int hb = 0; hb < a.group; hb += 8) {
+    const int h = hb + (t >> 5);
+    const int hc = h < a.group ? h : a.group - 1;
+    float M = -INFINITY, L = 0.f;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < a.nchunks; cb += CMB_B) {
+      float mc[CMB_B], lc[CMB_B];
+      float4 oc[CMB_B];
+#pragma unroll
+      for (int u = 0; u < CMB_B; ++u) {
+        const int c = cb + u < a.nchunks ? cb + u : a.nchunks - 1;
+        const float* pc = pseg + ((size_t)c * a.group + hc) * PST;
+        mc[u] = pc[0];
+        lc[u] = pc[1];
+        oc[u] = *reinterpret_cast<const float4*>(pc + 4 + j4);
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < CMB_B; ++u) {
+        if (cb + u >= a.nchunks) mc[u] = -INFINITY;
+        Mb = fmaxf(Mb, mc[u]);
+      }
+      if (Mb == -INFINITY) continue;
+      const float r = __builtin_amdgcn_exp2f(M - Mb);      // 0 while M is -inf
+      L *= r;
+      acc.x *= r;
+      acc.y *= r;
+      acc.z *= r;
+      acc.w *= r;
+#pragma unroll
+      for (int u = 0; u < CMB_B; ++u) {
+        const float wt = __builtin_amdgcn_exp2f(mc[u] - Mb);   // 0 for empty chunks
+        L = fmaf(wt, lc[u], L);
+        acc.x = fmaf(wt, oc[u].x, acc.x);
+        acc.y = fmaf(wt, oc[u].y, acc.y);
+        acc.z = fmaf(wt, oc[u].z, acc.z);
+        acc.w = fmaf(wt, oc[u].w, acc.w);
+      }
+      M = Mb;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (h < a.group)
+      *reinterpret_cast<float4*>(&ot[h][j4]) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the direct-to-LDS loads have landed
+  __syncthreads();
+  const int j = t & (D - 1), h0 = t >> 7;
+  if (j >= a.d) return;
+  for (int hb = 0; hb < a.group; hb += 8) {
+    float o[4] = {0.f, 0.f, 0.f, 0.f};     // heads hb + h0 + 2 i
+    int hh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hh[i] = hb + h0 + 2 * i < a.group ? hb + h0 + 2 * i : 0;
+    if (dense) {
+      for (int k = 0; k < D; k += 4) {
+        const float p0 = pis[k * D + j], p1 = pis[(k + 1) * D + j];
+        const float p2 = pis[(k + 2) * D + j], p3 = pis[(k + 3) * D + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 v = *reinterpret_cast<const float4*>(&ot[hh[i]][k]);
+          o[i] = fmaf(p0, v.x, fmaf(p1, v.y, fmaf(p2, v.z, fmaf(p3, v.w, o[i]))));
+        }
+      }
+    } else {
+      for (int k = 0; k < D; ++k) {
+        const bool neg = __popc(j & k) & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = ot[hh[i]][k];
+          o[i] += neg ? -v : v;
+        }
+      }
+      const float sg = a.eps_v[j] * rsqrtf((float)D);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= sg;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = hb + h0 + 2 * i;
+      if (h < a.group) a.out[((size_t)seg * a.group + h) * a.d + j] = o[i];
     }
   }
-  ot[j] = L > 0.f ? acc / L : 0.f;
-  __syncthreads();
-  if (j >= a.d) return;
-  float o = 0.f;
-  if (a.rot == TQ_ROT_DENSE) {
-    for (int k = 0; k < D; ++k) o = fmaf(a.pi_v[(size_t)k * a.d + j], ot[k], o);
-  } else {
-    for (int k = 0; k < D; ++k) o += ((__popc(j & k) & 1) ? -ot[k] : ot[k]);
-    o *= a.eps_v[j] * rsqrtf((float)D);
-  }
-  a.out[(size_t)hg * a.d + j] = o;
+}
+
+// Most workgroups per segment the workspace provides for: enough to fill a
+// device of 4096 resident workgroups, never more than T / AGRAN.
+int64_t attend_kmax(int segs, int64_t T) {
+  int64_t k = (4096 + segs - 1) / (segs > 0 ? segs : 1);
+  const int64_t kt = (T + AGRAN - 1) / AGRAN;
+  if (k > kt) k = kt;
+  return k < 1 ? 1 : k;
 }
 
 template <int BQK, int BQV, int MT>
-hipError_t launch_attend(const Attend128Args& s, int segs, hipStream_t stream) {
+hipError_t launch_attend(Attend128Args& s, int segs, hipStream_t stream) {
+  static const int nb = occupancy(reinterpret_cast<const void*>(&attend128<BQK, BQV, MT>), 256);
+  s.span = split_span(segs, s.T, nb * device_cus(), AGRAN, attend_kmax(segs, s.T));
+  s.nchunks = (int)((s.T + s.span - 1) / s.span);
   hipLaunchKernelGGL((attend128<BQK, BQV, MT>), dim3((unsigned)s.nchunks, (unsigned)segs), dim3(256), 0,
                      stream, s);
   return hipGetLastError();
@@ -894,18 +1122,22 @@ hipError_t launch_attend(const Attend128Args& s, int segs, hipStream_t stream) {
 
 size_t attend_pack_bytes(int segs, int group) { return scores128_workspace(segs, group); }
 
+size_t attend_part_bytes(int segs, int group, int64_t T) {
+  return ((size_t)segs * attend_kmax(segs, T) * group * PST * sizeof(float) + 255) / 256 * 256;
+}
+
 }  // namespace
 
 size_t attend128_workspace(int segs, int group, int64_t T) {
-  const int64_t nch = (T + ACHUNK - 1) / ACHUNK;
-  return attend_pack_bytes(segs, group) + (size_t)segs * nch * group * PST * sizeof(float);
+  return attend_pack_bytes(segs, group) + attend_part_bytes(segs, group, T);
 }
 
 hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(a.ws);
   hipError_t e = launch_scores128_prep(a.k, stream);
   if (e != hipSuccess) return e;
   Attend128Args s;
-  s.pack = static_cast<const uint8_t*>(a.ws);
+  s.pack = ws;
   s.kplanes = a.k.planes;
   s.kscal = a.k.scalars;
   s.kstride = a.k.seg_stride;
@@ -918,8 +1150,9 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   s.kappa = (float)(std::sqrt(M_PI / 2.0) / D);
   s.scale2 = a.scale * 1.4426950408889634f;
   walsh_coefficients(a.cb_v, a.bq_v, s.vu, &s.vusum);
-  s.nchunks = (int)((a.k.T + ACHUNK - 1) / ACHUNK);
-  s.part = reinterpret_cast<float*>(static_cast<uint8_t*>(a.ws) + attend_pack_bytes(a.k.segs, a.k.group));
+  s.part = reinterpret_cast<float*>(ws + attend_pack_bytes(a.k.segs, a.k.group));
+  s.nchunks = 0;   // set by the launcher
+  s.span = 0;
   const int mt = (a.k.group + 3) / 4;
   switch ((a.k.bq * 10 + a.bq_v) * 10 + mt) {
     case 111: e = launch_attend<1, 1, 1>(s, a.k.segs, stream); break;
@@ -966,13 +1199,11 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   c.nchunks = s.nchunks;
   c.group = a.k.group;
   c.d = a.k.d;
-  c.len = a.k.len;
-  c.T = a.k.T;
   c.rot = a.rot_v;
   c.pi_v = a.pi_v;
   c.eps_v = a.eps_v;
   c.out = a.out;
-  hipLaunchKernelGGL(attend_combine128, dim3((unsigned)(a.k.segs * a.k.group)), dim3(128), 0, stream, c);
+  hipLaunchKernelGGL(attend_combine128, dim3((unsigned)a.k.segs), dim3(256), 0, stream, c);
   return hipGetLastError();
 }
 
