@@ -17,17 +17,20 @@
 // are sums of query weights selected by key bits: an integer contraction.
 //
 // Matrix-core form.  Each weight vector is quantised per head to an integer
-// of 21 bits, q = 2^14 hi + 2^7 mid + lo (hi in [-127, 127], mid and lo in
-// [-64, 63]), and the three int8 slices become rows 4 h' + {0, 1, 2} of the A
-// operand of v_mfma_i32_16x16x64_i8 (4 heads per 16-row tile; row 4 h' + 3 is
-// zero).  Key bits become the B operand: bytes in {0, 1}, tokens on the N
-// axis.  The int32 accumulators are exact, and so is 2^14 hi + 2^7 mid + lo in
-// int32; the epilogue rescales, adds the constants and applies n_t and
-// gamma_t.  Lane group kg of the 16x16 accumulator holds rows 4 kg .. 4 kg + 3,
-// i.e. the three slices of head kg of the tile, for token lane % 16: the
-// epilogue needs no cross-lane work.  (21 bits keep the scores within ~1e-6
-// of float arithmetic, which the softmax of the attention kernel needs: an
-// error in a score becomes an error in an exponent.)
+// written in base 256 with int8 digits (each in [-128, 127]): two digits,
+// q = 256 hi + lo, for 16 bits, or three, q = 65536 hi + 256 mid + lo, for 24
+// bits.  The digits become rows of the A operand of v_mfma_i32_16x16x64_i8:
+// with two, rows 2 h' + {0, 1} (8 heads per 16-row tile); with three, rows
+// 4 h' + {0, 1, 2} (4 heads per tile, row 4 h' + 3 zero).  Key bits become the
+// B operand: bytes in {0, 1}, tokens on the N axis.  The int32 accumulators
+// are exact (at most 128 terms, |sum| < 2^14 per digit row), and so is the
+// base-256 recombination; the epilogue rescales, adds the constants and
+// applies n_t and gamma_t.  Lane group kg of the 16x16 accumulator holds rows
+// 4 kg .. 4 kg + 3, i.e. all digits of its heads for token lane % 16: the
+// epilogue needs no cross-lane work.  Scores of keys with 1 or 2 MSE bits use
+// two digits (within ~1e-4 of float arithmetic relative to the row maximum,
+// half the matrix work); 3 MSE bits and the attention kernel use three (an
+// error in a score becomes an error in an exponent there).
 //
 // K-slot map (any permutation is valid as long as A and B share it): lane
 // group kg (= lane / 16) of every MFMA reads plane word kg (coordinates
@@ -43,15 +46,15 @@ namespace tq {
 namespace {
 
 constexpr int D = 128;
-constexpr float QMAX = 16256.f;     // 127 * 2^7: two int8 slices (value side of attend)
-constexpr float QMAX3 = 2080768.f;  // 127 * 2^14: three int8 slices (query weights)
+constexpr float QMAX2 = 32512.f;     // 127 * 2^8: two base-256 int8 digits
+constexpr float QMAX3 = 8323072.f;   // 127 * 2^16: three base-256 int8 digits
 
 __host__ __device__ constexpr int mse_planes(int bq) { return bq == 3 ? 4 : bq; }
 
 // Bytes of one segment's query pack: fragments then per-head constants.
 __host__ __device__ constexpr size_t pack_frag_bytes(int mt, int f) { return (size_t)mt * f * 64 * 16; }
 __host__ __device__ constexpr size_t pack_bytes(int mt, int f) {
-  return (pack_frag_bytes(mt, f) + (size_t)mt * 4 * 4 * sizeof(float) + 255) / 256 * 256;
+  return (pack_frag_bytes(mt, f) + (size_t)mt * 8 * 4 * sizeof(float) + 255) / 256 * 256;
 }
 
 struct PrepArgs {
@@ -64,7 +67,8 @@ struct PrepArgs {
   float u[4];      // Walsh coefficients of the odd-subset planes
   float usum;
   int bq;
-  int mt;          // 16-row tiles per segment (4 heads each)
+  int slices;      // base-256 digits per weight: 2 (8 heads per tile) or 3 (4 heads)
+  int mt;          // 16-row tiles per segment
   uint8_t* ws;
 };
 
@@ -98,13 +102,20 @@ __device__ __forceinline__ void unpack8(float4 a, float4 b, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// 21-bit integer weight -> int8 slices hi, mid, lo with q = 2^14 hi + 2^7 mid + lo
+// integer weight -> balanced base-256 int8 digits: q = 65536 hi + 256 mid + lo;
+// the two low digits span [-32896, 32639], hence the offset of hi
 __device__ __forceinline__ void slices3(float w, int& hi, int& mid, int& lo) {
   const int qi = (int)rintf(fminf(fmaxf(w, -QMAX3), QMAX3));
-  hi = (qi + 8192) >> 14;
-  const int rem = qi - 16384 * hi;
-  mid = (rem + 64) >> 7;
-  lo = rem - 128 * mid;
+  hi = (qi + 32896) >> 16;
+  const int rem = qi - 65536 * hi;
+  mid = (rem + 128) >> 8;
+  lo = rem - 256 * mid;
+}
+// q = 256 hi + lo
+__device__ __forceinline__ void slices2(float w, int& hi, int& lo) {
+  const int qi = (int)rintf(fminf(fmaxf(w, -QMAX2), QMAX2));
+  hi = (qi + 128) >> 8;
+  lo = qi - 256 * hi;
 }
 
 __device__ __forceinline__ uint32_t pack4(int b0, int b1, int b2, int b3) {
@@ -237,42 +248,58 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
     float umax = 0.f;
     for (int p = 0; p < np; ++p) umax = fmaxf(umax, fabsf(2.f * a.u[p]));
     const float mm = mx * umax, pm = 2.f * px;
-    stat[t][0] = mm > 0.f ? mm / QMAX3 : 1.f;
+    const float qmax = a.slices == 2 ? QMAX2 : QMAX3;
+    stat[t][0] = mm > 0.f ? mm / qmax : 1.f;
     stat[t][1] = -a.usum * sr;
-    stat[t][2] = pm > 0.f ? pm / QMAX3 : 1.f;
+    stat[t][2] = pm > 0.f ? pm / qmax : 1.f;
     stat[t][3] = -sp;
   }
   __syncthreads();
   // ---- quantise: one item = (tile mt, fragment f = 2 p + m, lane group kg,
-  // head hl, dword k); its four bytes bi = 0..3 are coordinates
-  // 32 kg + 8 bi + 4 m + k, and its slices are lanes 16 kg + 4 hl + {0, 1, 2}
-  // (lane 16 kg + 4 hl + 3 is the zero row) ----
-  const int nitems = a.mt * F * 64;
+  // head hl of the tile's lane group, dword k); its four bytes bi = 0..3 are
+  // coordinates 32 kg + 8 bi + 4 m + k, and its digits go to lanes
+  // 16 kg + R hl + r (R = rows per head; rows past the digits stay zero) ----
+  const int R = a.slices == 2 ? 2 : 4;          // A rows per head
+  const int HPG = 4 / R;                        // heads per lane group
+  const int nitems = a.mt * F * 256 / R;        // 64 lanes x 4 dwords per fragment, R per item
   for (int it = t; it < nitems; it += PREP_THREADS) {
-    const int k = it & 3, hl = (it >> 2) & 3, kg = (it >> 4) & 3;
-    const int f = (it >> 6) % F, mt = (it >> 6) / F;
+    const int k = it & 3;
+    const int hl = (it >> 2) % (4 * HPG);       // head within the tile
+    const int rest = (it >> 2) / (4 * HPG);
+    const int kg = rest & 3;
+    const int f = (rest >> 2) % F, mt = (rest >> 2) / F;
     const int p = f >> 1, m = f & 1;
-    const int h = 4 * mt + hl;
-    uint32_t d0 = 0, d1 = 0, d2 = 0;
+    const int h = 4 * HPG * mt + hl;
+    uint32_t d[3] = {0u, 0u, 0u};
     if (h < G) {
       const float* src = p < np ? &qr[h * QTS] : &qp[h * QTS];
       const float up = p == 0 ? a.u[0] : p == 1 ? a.u[1] : p == 2 ? a.u[2] : a.u[3];
       const float wsc = p < np ? 2.f * up / stat[h][0] : 2.f / stat[h][2];
       int s0[4], s1[4], s2[4];
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) slices3(src[32 * kg + 8 * bi + 4 * m + k] * wsc, s0[bi], s1[bi], s2[bi]);
-      d0 = pack4(s0[0], s0[1], s0[2], s0[3]);
-      d1 = pack4(s1[0], s1[1], s1[2], s1[3]);
-      d2 = pack4(s2[0], s2[1], s2[2], s2[3]);
+      for (int bi = 0; bi < 4; ++bi) {
+        const float w = src[32 * kg + 8 * bi + 4 * m + k] * wsc;
+        if (R == 2) {
+          slices2(w, s0[bi], s1[bi]);
+          s2[bi] = 0;
+        } else {
+          slices3(w, s0[bi], s1[bi], s2[bi]);
+        }
+      }
+      d[0] = pack4(s0[0], s0[1], s0[2], s0[3]);
+      d[1] = pack4(s1[0], s1[1], s1[2], s1[3]);
+      d[2] = pack4(s2[0], s2[1], s2[2], s2[3]);
     }
-    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst) + ((mt * F + f) * 64 + 16 * kg + 4 * hl) * 4 + k;
-    d32[0] = d0;
-    d32[4] = d1;
-    d32[8] = d2;
-    d32[12] = 0u;
+    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst) + ((mt * F + f) * 64 + 16 * kg + R * hl) * 4 + k;
+    d32[0] = d[0];
+    d32[4] = d[1];
+    if (R == 4) {
+      d32[8] = d[2];
+      d32[12] = 0u;
+    }
   }
   float* consts = reinterpret_cast<float*>(dst + fbytes);
-  if (t < a.mt * 4 * 4) consts[t] = t < G * 4 ? stat[t >> 2][t & 3] : 0.f;
+  if (t < a.mt * 16 / R * 4) consts[t] = t < G * 4 ? stat[t >> 2][t & 3] : 0.f;
 }
 
 template <bool HAD>
@@ -356,7 +383,19 @@ __device__ __forceinline__ typename Words<P>::v load_words(rsrc_t r, uint32_t vo
 }
 
 __device__ __forceinline__ int combine3(i32x4 acc) {
-  return (acc[0] * 128 + acc[1]) * 128 + acc[2];   // 2^14 hi + 2^7 mid + lo
+  return (acc[0] * 256 + acc[1]) * 256 + acc[2];   // 65536 hi + 256 mid + lo
+}
+// The same in fp32, for accumulators of more than 256 digit terms (four MSE
+// planes of 128 coordinates), whose 65536 hi would leave int32; the top digit
+// is exact and the sum rounds once at 2^-24 relative.
+__device__ __forceinline__ float combine3f(i32x4 acc) {
+  return fmaf((float)acc[0], 65536.f, fmaf((float)acc[1], 256.f, (float)acc[2]));
+}
+// Recombined MSE accumulator of NP planes (three digits).
+template <int NP>
+__device__ __forceinline__ float mse_digits(i32x4 acc) {
+  if constexpr (NP > 2) return combine3f(acc);
+  else return (float)combine3(acc);
 }
 
 // Workgroup = 8 waves = chunk_tiles 16-token tiles of one segment.  A wave
@@ -366,15 +405,18 @@ __device__ __forceinline__ int combine3(i32x4 acc) {
 // tokens of one head (16 bytes) and a store covers whole 128-byte lines.
 constexpr int SC_WAVES = 8;
 
-template <int BQ, int MT>
+template <int BQ, int MT, int S>
 __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
   constexpr int NP = mse_planes(BQ);      // MSE planes after the parity plane
   constexpr int F = 2 * (NP + 1);         // MFMAs per tile per 16-row tile
   constexpr int P = BQ + 1;               // stored planes per key record
   constexpr uint32_t RB = 16 * P;         // plane bytes per key record
-  constexpr int RING = 4;
+  constexpr int RING = 4;                 // pairs of loads in flight per wave
+  constexpr int ROUND = 8;                // pairs per straight-line round
+  constexpr int HL = S == 2 ? 2 : 1;      // heads per lane group per 16-row tile
+  constexpr int NH = MT * 4 * HL;         // heads covered by the tiles
   typedef typename Words<P>::v wvec;
-  __shared__ __align__(16) float sbufs[SC_WAVES][MT * 4 * SROW];
+  __shared__ __align__(16) float sbufs[SC_WAVES][NH * SROW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15;
@@ -396,18 +438,14 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
 
   wvec wr[RING][2];
   uint32_t sr[RING][2];
-  auto issue_ring = [&]() {
+  auto load_pair = [&](int slot, int pr) {
+    const uint32_t tb = (uint32_t)(32 * pr);
 #pragma unroll
-    for (int j = 0; j < RING; ++j) {
-      const uint32_t tb = (uint32_t)(32 * (wave + SC_WAVES * j));
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        wr[j][h] = load_words<P>(rk, vk + (tb + 16 * h) * RB);
-        sr[j][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + (tb + 16 * h) * 4, 0, 0);
-      }
+    for (int h = 0; h < 2; ++h) {
+      wr[slot][h] = load_words<P>(rk, vk + (tb + 16 * h) * RB);
+      sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + (tb + 16 * h) * 4, 0, 0);
     }
   };
-  issue_ring();
   const uint8_t* pack = a.ws + (size_t)seg * pack_bytes(MT, F);
 
   i32x4 afr[MT][F];
@@ -417,14 +455,17 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
     for (int f = 0; f < F; ++f)
       afr[mt][f] = reinterpret_cast<const i32x4*>(pack)[(mt * F + f) * 64 + lane];
   const float* consts = reinterpret_cast<const float*>(pack + pack_frag_bytes(MT, F));
-  float cst[MT][4];     // head 4 mt + kg: sigma_mse, const_mse, kappa sigma_qjl, kappa const_qjl
+  // head 4 HL mt + HL kg + hh: sigma_mse, const_mse, kappa sigma_qjl, kappa const_qjl
+  float cst[MT][HL][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) cst[mt][c] = consts[(mt * 4 + kg) * 4 + c];
-    cst[mt][2] *= a.kappa;
-    cst[mt][3] *= a.kappa;
-  }
+    for (int hh = 0; hh < HL; ++hh) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cst[mt][hh][c] = consts[(4 * HL * mt + HL * kg + hh) * 4 + c];
+      cst[mt][hh][2] *= a.kappa;
+      cst[mt][hh][3] *= a.kappa;
+    }
   float* sbuf = sbufs[wave];
 
   // one 16-token tile -> LDS rows (heads 4 mt + kg), columns col0 + t16
@@ -458,9 +499,14 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
     const float g = (float)__builtin_bit_cast(_Float16, (uint16_t)(scl >> 16));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const float mse = fmaf((float)combine3(am[mt]), cst[mt][0], cst[mt][1]);
-      const float qjl = fmaf((float)combine3(aq[mt]), cst[mt][2], cst[mt][3]);
-      sbuf[(4 * mt + kg) * SROW + col0 + t16] = n * fmaf(g, qjl, mse);
+#pragma unroll
+      for (int hh = 0; hh < HL; ++hh) {
+        const float im = S == 2 ? (float)(am[mt][2 * hh] * 256 + am[mt][2 * hh + 1]) : mse_digits<NP>(am[mt]);
+        const int iq = S == 2 ? aq[mt][2 * hh] * 256 + aq[mt][2 * hh + 1] : combine3(aq[mt]);
+        const float mse = fmaf(im, cst[mt][hh][0], cst[mt][hh][1]);
+        const float qjl = fmaf((float)iq, cst[mt][hh][2], cst[mt][hh][3]);
+        sbuf[(4 * HL * mt + HL * kg + hh) * SROW + col0 + t16] = n * fmaf(g, qjl, mse);
+      }
     }
   };
   // lanes 8 h' + c store tokens 4c .. 4c+3 of head 8 r + h' of the pair;
@@ -469,9 +515,9 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
   auto flush = [&](int pbase) {
     const bool full = pbase + 32 <= ntok;
 #pragma unroll
-    for (int rr = 0; rr < (MT + 1) / 2; ++rr) {
+    for (int rr = 0; rr < (NH + 7) / 8; ++rr) {
       const int head = rr * 8 + hr;
-      const int hread = head < MT * 4 ? head : 0;
+      const int hread = head < NH ? head : 0;
       const float4 v = *reinterpret_cast<const float4*>(&sbuf[hread * SROW + c4]);
       const uint32_t vo = (uint32_t)(head * a.T + pbase + c4) * 4u;
       const bool live = head < a.group;
@@ -488,19 +534,20 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
     }
   };
 
-  for (int i = 0;; i += RING) {
+  // rounds of ROUND pairs per wave, straight-line inside a round: loads run
+  // RING pairs ahead and never across a round boundary, so every wait on a
+  // slot counts exactly the loads issued after it
+  const int mine = npairs > wave ? (npairs - wave + SC_WAVES - 1) / SC_WAVES : 0;
+  for (int r0 = 0; r0 < mine; r0 += ROUND) {
 #pragma unroll
-    for (int j = 0; j < RING; ++j) {
-      const int pr = wave + SC_WAVES * (i + j);
-      if (pr >= npairs) return;
-      compute(wr[j][0], sr[j][0], 0);
-      compute(wr[j][1], sr[j][1], 16);
-      const uint32_t tb = (uint32_t)(32 * (pr + SC_WAVES * RING));
+    for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * (r0 + j));
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        wr[j][h] = load_words<P>(rk, vk + (tb + 16 * h) * RB);
-        sr[j][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + (tb + 16 * h) * 4, 0, 0);
-      }
+    for (int j = 0; j < ROUND; ++j) {
+      if (r0 + j >= mine) break;
+      const int pr = wave + SC_WAVES * (r0 + j);
+      compute(wr[j % RING][0], sr[j % RING][0], 0);
+      compute(wr[j % RING][1], sr[j % RING][1], 16);
+      if (j + RING < ROUND) load_pair(j % RING, pr + SC_WAVES * RING);
       flush(32 * pr);
     }
   }
@@ -512,13 +559,13 @@ int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax
 
 // Grid: (workgroups per segment, segments), sized so that the whole grid is
 // resident at once; a workgroup's span is a multiple of 8 waves x 32 tokens.
-template <int BQ, int MT>
+template <int BQ, int MT, int S>
 hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
-  static const int nb = occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT>), SC_WAVES * 64);
+  static const int nb = occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S>), SC_WAVES * 64);
   const int64_t span = split_span(segs, s.T, nb * device_cus(), 32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   const int64_t chunks = (s.T + span - 1) / span;
-  hipLaunchKernelGGL((scores128<BQ, MT>), dim3((unsigned)chunks, (unsigned)segs), dim3(SC_WAVES * 64), 0, stream, s);
+  hipLaunchKernelGGL((scores128<BQ, MT, S>), dim3((unsigned)chunks, (unsigned)segs), dim3(SC_WAVES * 64), 0, stream, s);
   return hipGetLastError();
 }
 
@@ -582,7 +629,11 @@ size_t scores128_workspace(int segs, int group) {
   return (size_t)segs * pack_bytes(mt, 2 * (mse_planes(3) + 1));   // sized for the widest key
 }
 
-static PrepArgs make_prep(const ScoreArgs& a) {
+// Digits per quantised query weight for the score pass: 2 when the keys carry
+// 1 or 2 MSE bits, else 3 (the attention pass always takes 3).
+static int score_slices(int bq) { return bq <= 2 ? 2 : 3; }
+
+static PrepArgs make_prep(const ScoreArgs& a, int slices) {
   PrepArgs p;
   p.q = a.q;
   p.segs = a.segs;
@@ -595,13 +646,14 @@ static PrepArgs make_prep(const ScoreArgs& a) {
   p.s = a.s;
   walsh_coefficients(a.cb, a.bq, p.u, &p.usum);
   p.bq = a.bq;
-  p.mt = (a.group + 3) / 4;
+  p.slices = slices;
+  p.mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   p.ws = static_cast<uint8_t*>(a.ws);
   return p;
 }
 
-hipError_t launch_scores128_prep(const ScoreArgs& a, hipStream_t stream) {
-  const PrepArgs p = make_prep(a);
+hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream) {
+  const PrepArgs p = make_prep(a, slices);
   if (a.rot == TQ_ROT_HADAMARD)
     hipLaunchKernelGGL(prep_queries128<true>, dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
   else
@@ -610,9 +662,10 @@ hipError_t launch_scores128_prep(const ScoreArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
-  hipError_t e = launch_scores128_prep(a, stream);
+  const int slices = score_slices(a.bq);
+  hipError_t e = launch_scores128_prep(a, slices, stream);
   if (e != hipSuccess) return e;
-  const int mt = (a.group + 3) / 4;
+  const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   Score128Args s;
   s.ws = static_cast<const uint8_t*>(a.ws);
   s.planes = a.planes;
@@ -625,18 +678,14 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
   s.scores = a.scores;
   s.chunk_tiles = 0;   // set by the launcher
   switch (a.bq * 10 + mt) {
-    case 11: return launch_scores<1, 1>(s, a.segs, stream);
-    case 12: return launch_scores<1, 2>(s, a.segs, stream);
-    case 13: return launch_scores<1, 3>(s, a.segs, stream);
-    case 14: return launch_scores<1, 4>(s, a.segs, stream);
-    case 21: return launch_scores<2, 1>(s, a.segs, stream);
-    case 22: return launch_scores<2, 2>(s, a.segs, stream);
-    case 23: return launch_scores<2, 3>(s, a.segs, stream);
-    case 24: return launch_scores<2, 4>(s, a.segs, stream);
-    case 31: return launch_scores<3, 1>(s, a.segs, stream);
-    case 32: return launch_scores<3, 2>(s, a.segs, stream);
-    case 33: return launch_scores<3, 3>(s, a.segs, stream);
-    case 34: return launch_scores<3, 4>(s, a.segs, stream);
+    case 11: return launch_scores<1, 1, 2>(s, a.segs, stream);
+    case 12: return launch_scores<1, 2, 2>(s, a.segs, stream);
+    case 21: return launch_scores<2, 1, 2>(s, a.segs, stream);
+    case 22: return launch_scores<2, 2, 2>(s, a.segs, stream);
+    case 31: return launch_scores<3, 1, 3>(s, a.segs, stream);
+    case 32: return launch_scores<3, 2, 3>(s, a.segs, stream);
+    case 33: return launch_scores<3, 3, 3>(s, a.segs, stream);
+    case 34: return launch_scores<3, 4, 3>(s, a.segs, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -652,9 +701,9 @@ namespace {
 // The value sum stays in the rotated domain (Pi_v^T is linear and is applied
 // once per head at the end) and uses the same Walsh form as the keys:
 //   sum_t P'_t c_v[idx_t,j] = sum_S u_S (2 sum_t P'_t x_S,tj - sum_t P'_t),
-// P'_t = p_t n_v,t, a contraction over tokens: A = P' (three int8 slices per
-// head, 21 bits relative to the group maximum, rows 4 h' + slice as for the
-// keys), B = value bits, whose block layout gives each lane one coordinate
+// P'_t = p_t n_v,t, a contraction over tokens: A = P' (three base-256 int8
+// digits per head, 24 bits relative to the group maximum, rows 4 h' + digit as
+// for the keys), B = value bits, whose block layout gives each lane one coordinate
 // across 32 tokens in one word.  The constant term uses the same quantised
 // P' as the bit sums, so quantisation errors enter only through the
 // zero-mean centroids.
@@ -779,26 +828,31 @@ __global__ __launch_bounds__(256, 2) void attend128(Attend128Args a) {
   uint32_t ks[8];
   vvec vw[8];
   uint32_t vn2;
+  // the issue order is pinned (scheduling barriers) so that the prologue and
+  // the loop body leave the same outstanding loads at the loop header, which
+  // lets each wait count only the loads it needs
   auto load_keys = [&](int g) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tile = 0; tile < 8; ++tile) {
       const uint32_t tok = (uint32_t)(128 * g + 16 * tile);
       kw[tile] = load_words<PK>(rk, vko + tok * RBK);
       ks[tile] = __builtin_amdgcn_raw_buffer_load_b32(rks, vkso + tok * 4, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto load_vals = [&](int g) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) vw[nt] = load_words<PV>(rv, vvo + (uint32_t)(4 * g) * VBB + nt * 16 * (PV * 4));
     vn2 = __builtin_amdgcn_raw_buffer_load_b32(rvs, vno + (uint32_t)(256 * g), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
   load_keys(wave);
   load_vals(wave);
 
   for (int g = wave; g < ngroups; g += 4) {
     const int ntok = (int)(c1 - c0 - 128 * g < 128 ? c1 - c0 - 128 * g : 128);
-    vnorm[wave][2 * lane] = 2 * lane < ntok ? f16lo(vn2) : 0.f;
-    vnorm[wave][2 * lane + 1] = 2 * lane + 1 < ntok ? f16hi(vn2) : 0.f;
 
     // ---- phase 1: logits (log2 units) of the 8 key tiles, token t16 + 16 tile ----
     float sc[8][KMT];
@@ -833,7 +887,7 @@ __global__ __launch_bounds__(256, 2) void attend128(Attend128Args a) {
       const float n = f16lo(ks[tile]), gm = f16hi(ks[tile]);
 #pragma unroll
       for (int mt = 0; mt < KMT; ++mt) {
-        const float mse = fmaf((float)combine3(am[mt]), cst[mt][0], cst[mt][1]);
+        const float mse = fmaf(mse_digits<NPK>(am[mt]), cst[mt][0], cst[mt][1]);
         const float qjl = fmaf((float)combine3(aq[mt]), cst[mt][2], cst[mt][3]);
         sc[tile][mt] = valid ? n * fmaf(gm, qjl, mse) : -INFINITY;
       }
@@ -841,6 +895,8 @@ __global__ __launch_bounds__(256, 2) void attend128(Attend128Args a) {
     load_keys(g + 4);
 
     // ---- phase 2: softmax statistics and the int8 P' rows ----
+    vnorm[wave][2 * lane] = 2 * lane < ntok ? f16lo(vn2) : 0.f;
+    vnorm[wave][2 * lane + 1] = 2 * lane + 1 < ntok ? f16hi(vn2) : 0.f;
     float vn[8];
 #pragma unroll
     for (int tile = 0; tile < 8; ++tile) vn[tile] = vnorm[wave][tile * 16 + t16];
@@ -878,11 +934,11 @@ __global__ __launch_bounds__(256, 2) void attend128(Attend128Args a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int qi = (int)rintf(fminf(pv[2 * c + h] * inv, QMAX3));
-          qsum += qi;
-          s0[h] = (qi + 8192) >> 14;
-          const int rem = qi - 16384 * s0[h];
-          s1[h] = (rem + 64) >> 7;
-          s2[h] = rem - 128 * s1[h];
+          qsum += qi;                                   // <= 128 * 127 * 2^16 < 2^31
+          s0[h] = (qi + 32896) >> 16;                   // balanced digits, as slices3
+          const int rem = qi - 65536 * s0[h];
+          s1[h] = (rem + 128) >> 8;
+          s2[h] = rem - 256 * s1[h];
         }
         const uint32_t d0 = pair_bytes(s0[0], s0[1], bsh);
         const uint32_t d1 = pair_bytes(s1[0], s1[1], bsh);
@@ -1134,7 +1190,7 @@ size_t attend128_workspace(int segs, int group, int64_t T) {
 
 hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(a.ws);
-  hipError_t e = launch_scores128_prep(a.k, stream);
+  hipError_t e = launch_scores128_prep(a.k, 3, stream);
   if (e != hipSuccess) return e;
   Attend128Args s;
   s.pack = ws;

@@ -55,7 +55,7 @@ struct ScoreArgs {
 };
 
 hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream);
-hipError_t launch_scores128_prep(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream);
 size_t scores128_workspace(int segs, int group);
 
 struct AttendArgs {
