@@ -114,10 +114,11 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   a.planes = (uint32_t*)out.planes;
   a.scalars = (uint16_t*)out.scalars;
   a.slot = slot;
+  a.had = p->rot == TQ_ROT_HADAMARD;
   hipStream_t s = (hipStream_t)stream;
-  if (p->rot == TQ_ROT_DENSE && p->d == 128)
+  if (p->d == 128 && p->d_rot == 128)
     return hip_status(tq::launch_encode_dense128(a, s), "encode launch");
-  return fail(TQ_ERR_UNSUPPORTED, "encode supports the dense rotation at d = 128 (got rot %d, d %d, d_rot %d)",
+  return fail(TQ_ERR_UNSUPPORTED, "encode supports d = d_rot = 128 (got rot %d, d %d, d_rot %d)",
               p->rot, p->d, p->d_rot);
 }
 

@@ -1,4 +1,5 @@
-// TurboQuant encode kernels for gfx950 (MI355X), dense rotation, d = 128.
+// TurboQuant encode kernels for gfx950 (MI355X), d = d_rot = 128, dense or
+// sign-flipped Hadamard rotation.
 //
 // Per vector x (blog notes on the TurboQuant paper: Q_mse and Q_prod; the
 // explainer page, sections 6 and 8):
@@ -15,6 +16,13 @@
 // in fp16), three products for fp32 operands (the lo*lo term, ~2^-22, is
 // dropped).  The power-of-two prescales keep the lo parts out of the fp16
 // subnormal range and are undone exactly.
+//
+// Sign-flipped Hadamard rotation (explainer page, the random Hadamard variant;
+// blog notes, the fast rotation): y = H diag(eps) u / sqrt(128) with the
+// Sylvester H, H[j][k] = (-1)^popcount(j & k).  At d = 128 it runs through the
+// same GEMM1 as the matrix 16 H diag(eps), whose entries +-16 are exact in
+// fp16 (no lo part, one pass for fp16 inputs); 1/sqrt(128) joins the output
+// scale.
 //
 // The A rows are permuted so that, in the accumulator layout, lane
 // (v = lane % 32, h = lane / 32) holds coordinates 64 h + 16 mt + r of vector
@@ -36,6 +44,7 @@ constexpr int D = 128;
 constexpr float PI_SCALE = 16.f;   // 2^4
 constexpr float R_SCALE = 256.f;   // 2^8
 constexpr float U_SCALE = 64.f;    // 2^6 (fp32 inputs, after normalising)
+constexpr float HAD_SCALE = 0.08838834764831845f;   // 1 / sqrt(128)
 constexpr int FRAGS = 4 * 8 * 2 * 64;  // half8 per 128x128 matrix (hi and lo)
 
 __device__ __forceinline__ int frag_index(int mt, int ks, int part, int lane) {
@@ -49,16 +58,27 @@ __device__ __forceinline__ int row_coord(int rho, int mt) {
   return 64 * h + 16 * mt + r;
 }
 
-// M is [128][128] float32 row-major.  Fragment (mt, ks) of lane l holds
-// scale * M[row_coord(l % 32, mt)][64 (l / 32) + 8 ks + e], e = 0..7, as hi, lo.
-__device__ void build_frags(half8* lds, const float* __restrict__ M, float scale) {
+// M is [128][128] float32 row-major (or, with eps, the matrix H diag(eps)).
+// Fragment (mt, ks) of lane l holds scale * M[row_coord(l % 32, mt)][64 (l / 32)
+// + 8 ks + e], e = 0..7, as hi, lo.
+__device__ void build_frags(half8* lds, const float* __restrict__ M, float scale, const float* eps = nullptr) {
   for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
     const int lane = f & 63, ks = (f >> 6) & 7, mt = f >> 9;
     const int row = row_coord(lane & 31, mt);
     const int k0 = 64 * (lane >> 5) + 8 * ks;
-    const float4* src = reinterpret_cast<const float4*>(M + row * D + k0);
-    const float4 p = src[0], q = src[1];
-    const float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+    float v[8];
+    if (eps) {
+      const float4* src = reinterpret_cast<const float4*>(eps + k0);
+      const float4 p = src[0], q = src[1];
+      const float e8[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__popc(row & (k0 + e)) & 1) ? -e8[e] : e8[e];
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(M + row * D + k0);
+      const float4 p = src[0], q = src[1];
+      v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+      v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+    }
     half8 hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -84,12 +104,12 @@ __device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, 
   }
 }
 
-template <bool PROD, int BQ, bool F16IN, int NT, int WAVES>
+template <bool PROD, int BQ, bool F16IN, int NT, int WAVES, bool HAD>
 __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   extern __shared__ half8 lds[];
   half8* fpi = lds;
   half8* fs = lds + FRAGS;
-  build_frags(fpi, a.pi, PI_SCALE);
+  build_frags(fpi, a.pi, PI_SCALE, HAD ? a.eps : nullptr);
   if (PROD) build_frags(fs, a.s, 1.f);
   __syncthreads();
 
@@ -152,13 +172,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           }
         }
         nrm[nt] = n;
-        yscale[nt] = 1.f / (U_SCALE * PI_SCALE);
+        yscale[nt] = (HAD ? HAD_SCALE : 1.f) / (U_SCALE * PI_SCALE);
         continue;
       }
       s2 += shfl_xor_f(s2, 32);
       const float n = sqrtf(s2);
       nrm[nt] = n;
-      yscale[nt] = n > 0.f ? 1.f / (n * PI_SCALE) : 0.f;
+      yscale[nt] = n > 0.f ? (HAD ? HAD_SCALE : 1.f) / (n * PI_SCALE) : 0.f;
     }
 
     // ---- values: one aligned, fully valid 32-record block per tile? ----
@@ -196,7 +216,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           acc[nt] = mfma32x32x16(ahi, xh[nt][ks], acc[nt]);
-          acc[nt] = mfma32x32x16(alo, xh[nt][ks], acc[nt]);
+          if (!HAD) acc[nt] = mfma32x32x16(alo, xh[nt][ks], acc[nt]);   // +-16 has no lo part
           if (!F16IN) acc[nt] = mfma32x32x16(ahi, xl[nt][ks], acc[nt]);
         }
       }
@@ -327,10 +347,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   }
 }
 
-template <bool PROD, int BQ, bool F16IN>
+template <bool PROD, int BQ, bool F16IN, bool HAD>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   constexpr int NT = 1, WAVES = 8;
-  auto kern = encode_dense128<PROD, BQ, F16IN, NT, WAVES>;
+  auto kern = encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD>;
   const size_t lds = (PROD ? 2 : 1) * FRAGS * sizeof(half8);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -346,41 +366,46 @@ hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream) {
+template <bool HAD>
+hipError_t launch_rot(const EncodeArgs& a, hipStream_t stream) {
   if (a.prod) {
     if (a.f16_in) {
       switch (a.bq) {
-        case 1: return launch_one<true, 1, true>(a, stream);
-        case 2: return launch_one<true, 2, true>(a, stream);
-        case 3: return launch_one<true, 3, true>(a, stream);
+        case 1: return launch_one<true, 1, true, HAD>(a, stream);
+        case 2: return launch_one<true, 2, true, HAD>(a, stream);
+        case 3: return launch_one<true, 3, true, HAD>(a, stream);
       }
     } else {
       switch (a.bq) {
-        case 1: return launch_one<true, 1, false>(a, stream);
-        case 2: return launch_one<true, 2, false>(a, stream);
-        case 3: return launch_one<true, 3, false>(a, stream);
+        case 1: return launch_one<true, 1, false, HAD>(a, stream);
+        case 2: return launch_one<true, 2, false, HAD>(a, stream);
+        case 3: return launch_one<true, 3, false, HAD>(a, stream);
       }
     }
   } else {
     if (a.f16_in) {
       switch (a.bq) {
-        case 1: return launch_one<false, 1, true>(a, stream);
-        case 2: return launch_one<false, 2, true>(a, stream);
-        case 3: return launch_one<false, 3, true>(a, stream);
-        case 4: return launch_one<false, 4, true>(a, stream);
+        case 1: return launch_one<false, 1, true, HAD>(a, stream);
+        case 2: return launch_one<false, 2, true, HAD>(a, stream);
+        case 3: return launch_one<false, 3, true, HAD>(a, stream);
+        case 4: return launch_one<false, 4, true, HAD>(a, stream);
       }
     } else {
       switch (a.bq) {
-        case 1: return launch_one<false, 1, false>(a, stream);
-        case 2: return launch_one<false, 2, false>(a, stream);
-        case 3: return launch_one<false, 3, false>(a, stream);
-        case 4: return launch_one<false, 4, false>(a, stream);
+        case 1: return launch_one<false, 1, false, HAD>(a, stream);
+        case 2: return launch_one<false, 2, false, HAD>(a, stream);
+        case 3: return launch_one<false, 3, false, HAD>(a, stream);
+        case 4: return launch_one<false, 4, false, HAD>(a, stream);
       }
     }
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream) {
+  return a.had ? launch_rot<true>(a, stream) : launch_rot<false>(a, stream);
 }
 
 }  // namespace tq

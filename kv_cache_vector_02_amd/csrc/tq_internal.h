@@ -29,6 +29,7 @@ struct EncodeArgs {
   Codebook cb;
   int bq;              // index bits
   int prod;            // 1: keys (prod), 0: values (mse)
+  int had;             // 1: sign-flipped Hadamard rotation (eps), 0: dense (pi)
   uint32_t* planes;    // [records][P][d_rot/32]
   uint16_t* scalars;   // [records][S] float16 bit patterns
   const int64_t* slot; // record of vector i, or null

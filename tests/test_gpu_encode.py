@@ -119,3 +119,18 @@ def test_value_block_paths(mode):
     compare_encode(st, idx[where], scal[where], st.encode_oracle(x))
     rest = np.setdiff1d(np.arange(records), where)
     compare_encode(st, idx[rest], scal[rest], st.encode_oracle(old[rest]))
+
+
+@pytest.mark.parametrize("prod,bits", [(True, 2), (True, 3), (True, 4), (False, 1), (False, 2), (False, 3),
+                                       (False, 4)])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_hadamard_rotation(prod, bits, dtype):
+    # sign-flipped Hadamard rotation at d = d_rot = 128, ragged count
+    _log(f"encode hadamard {'prod' if prod else 'mse'} b{bits} {dtype}")
+    x = kv_tensor(1, 1, 900, 128, seed=6, value=not prod)[0, 0]
+    x = x if dtype == "f16" else x.astype(np.float32)
+    st = Setup(bits=bits, prod=prod, seed=6, rot="hadamard", purpose_eps=5 if prod else 6)
+    planes, scal = st.encode_gpu(x)
+    if not prod:
+        planes = value_indices(planes, len(x))
+    _log(f"  {compare_encode(st, planes, scal, st.encode_oracle(x))}")
