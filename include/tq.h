@@ -172,7 +172,7 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
  * Other arguments as for tq_scores (ws: tq_attend_workspace() bytes).  Three
  * launches: the query pack, the streaming pass (one log-sum-exp partial per
  * workgroup) and the per-segment merge with the inverse value rotation.
- * Supported: d = 128, group <= 16, value bits 1..3. */
+ * Supported: d = 128, group <= 16, value bits 1..4. */
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs,
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);

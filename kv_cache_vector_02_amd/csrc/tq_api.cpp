@@ -244,7 +244,6 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   if (kp->d != 128 || kp->d_rot != 128 || vp->d != 128 || vp->d_rot != 128)
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports d = d_rot = 128 for keys and values");
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports up to 16 query heads per segment");
-  if (vp->bits > 3) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports value bits 1..3");
   if (!q || !keys.planes || !keys.scalars || !vals.planes || !vals.scalars || !out || !ws)
     return fail(TQ_ERR_INVALID_ARG, "q, keys, vals, out and ws must be non-NULL");
   if (vals.seg_stride % 32) return fail(TQ_ERR_INVALID_ARG, "vals.seg_stride must be a multiple of 32");

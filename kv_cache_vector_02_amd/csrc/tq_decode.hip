@@ -49,7 +49,13 @@ constexpr int D = 128;
 constexpr float QMAX2 = 32512.f;     // 127 * 2^8: two base-256 int8 digits
 constexpr float QMAX3 = 8323072.f;   // 127 * 2^16: three base-256 int8 digits
 
-__host__ __device__ constexpr int mse_planes(int bq) { return bq == 3 ? 4 : bq; }
+// Odd subsets of the bq index bits (the Walsh planes of an odd-symmetric
+// codebook), in plane order: the single bits, then for 3 bits their parity
+// and for 4 bits the four three-bit parities.
+__host__ __device__ constexpr int mse_planes(int bq) { return bq == 3 ? 4 : bq == 4 ? 8 : bq; }
+__host__ __device__ constexpr int plane_subset(int bq, int p) {
+  return p < bq ? 1 << p : bq == 3 ? 7 : (p == 4 ? 7 : p == 5 ? 11 : p == 6 ? 13 : 14);
+}
 
 // Bytes of one segment's query pack: fragments then per-head constants.
 __host__ __device__ constexpr size_t pack_frag_bytes(int mt, int f) { return (size_t)mt * f * 64 * 16; }
@@ -64,7 +70,7 @@ struct PrepArgs {
   const float* pi;
   const float* eps;
   const float* s;
-  float u[4];      // Walsh coefficients of the odd-subset planes
+  float u[8];      // Walsh coefficients of the odd-subset planes
   float usum;
   int bq;
   int slices;      // base-256 digits per weight: 2 (8 heads per tile) or 3 (4 heads)
@@ -569,21 +575,19 @@ hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
   return hipGetLastError();
 }
 
-void walsh_coefficients(const Codebook& cb, int bq, float u[4], float* usum) {
+void walsh_coefficients(const Codebook& cb, int bq, float u[8], float* usum) {
   // u_S = 2^-bq sum_idx c[idx] prod_{p in S} (2 bit_p(idx) - 1), odd S in the plane order
   const int K = 1 << bq;
-  int subsets[4];
-  int ns = 0;
-  for (int p = 0; p < bq; ++p) subsets[ns++] = 1 << p;
-  if (bq == 3) subsets[ns++] = 7;
+  const int ns = mse_planes(bq);
   double tot = 0;
-  for (int s = 0; s < 4; ++s) u[s] = 0.f;
+  for (int s = 0; s < 8; ++s) u[s] = 0.f;
   for (int s = 0; s < ns; ++s) {
+    const int sub = plane_subset(bq, s);
     double acc = 0;
     for (int idx = 0; idx < K; ++idx) {
       double chi = 1;
       for (int p = 0; p < bq; ++p)
-        if (subsets[s] >> p & 1) chi *= ((idx >> p) & 1) ? 1.0 : -1.0;
+        if (sub >> p & 1) chi *= ((idx >> p) & 1) ? 1.0 : -1.0;
       acc += cb.c[idx] * chi;
     }
     u[s] = (float)(acc / K);
@@ -734,7 +738,7 @@ struct Attend128Args {
   int group;
   float kappa;
   float scale2;                 // softmax scale * log2(e)
-  float vu[4];                  // value Walsh coefficients, odd subsets
+  float vu[8];                  // value Walsh coefficients, odd subsets
   float vusum;
   float* part;                  // [segs][nchunks][group][PST]
   int nchunks;                  // workgroups per segment
@@ -759,7 +763,7 @@ __device__ __forceinline__ uint32_t row_ror8(uint32_t v) {
 }
 
 template <int BQK, int BQV, int KMT>
-__global__ __launch_bounds__(256, 2) void attend128(Attend128Args a) {
+__global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args a) {
   constexpr int NPK = mse_planes(BQK);
   constexpr int FK = 2 * (NPK + 1);
   constexpr int PK = BQK + 1;
@@ -979,7 +983,10 @@ __global__ __launch_bounds__(256, 2) void attend128(Attend128Args a) {
         if (sp < BQV) {
           word = vw[nt][sp];
         } else {
-          if constexpr (BQV == 3) word = vw[nt][0] ^ vw[nt][1] ^ vw[nt][2];
+          word = 0u;
+#pragma unroll
+          for (int p = 0; p < BQV; ++p)
+            if (plane_subset(BQV, sp) >> p & 1) word ^= vw[nt][p];
         }
         uint32_t e8[8];
         expand8(word, e8);
@@ -1247,6 +1254,18 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
     case 332: e = launch_attend<3, 3, 2>(s, a.k.segs, stream); break;
     case 333: e = launch_attend<3, 3, 3>(s, a.k.segs, stream); break;
     case 334: e = launch_attend<3, 3, 4>(s, a.k.segs, stream); break;
+    case 141: e = launch_attend<1, 4, 1>(s, a.k.segs, stream); break;
+    case 142: e = launch_attend<1, 4, 2>(s, a.k.segs, stream); break;
+    case 143: e = launch_attend<1, 4, 3>(s, a.k.segs, stream); break;
+    case 144: e = launch_attend<1, 4, 4>(s, a.k.segs, stream); break;
+    case 241: e = launch_attend<2, 4, 1>(s, a.k.segs, stream); break;
+    case 242: e = launch_attend<2, 4, 2>(s, a.k.segs, stream); break;
+    case 243: e = launch_attend<2, 4, 3>(s, a.k.segs, stream); break;
+    case 244: e = launch_attend<2, 4, 4>(s, a.k.segs, stream); break;
+    case 341: e = launch_attend<3, 4, 1>(s, a.k.segs, stream); break;
+    case 342: e = launch_attend<3, 4, 2>(s, a.k.segs, stream); break;
+    case 343: e = launch_attend<3, 4, 3>(s, a.k.segs, stream); break;
+    case 344: e = launch_attend<3, 4, 4>(s, a.k.segs, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

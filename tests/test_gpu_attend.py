@@ -60,7 +60,7 @@ def _setups(bk, bv, rot="dense", seed=5):
     return sk, sv
 
 
-@pytest.mark.parametrize("bk,bv", [(3, 3), (2, 2), (4, 3), (3, 1), (2, 3)])
+@pytest.mark.parametrize("bk,bv", [(3, 3), (2, 2), (4, 3), (3, 1), (2, 3), (4, 4), (2, 4)])
 @pytest.mark.parametrize("group", [1, 4, 8, 16])
 def test_segments_groups_bits_lengths(bk, bv, group):
     _log(f"attend bk{bk} bv{bv} G{group}")
