@@ -98,7 +98,7 @@ def test_encode_validation_without_launch():
     p._c.d, p._c.d_rot, p._c.m = 96, 96, 96
     assert _encode_raw(p, ld=96) == tq.TQ_ERR_UNSUPPORTED   # valid, but no kernel for d=96
     msg = tq.lib().tq_last_error().decode()
-    assert "d = 128" in msg
+    assert "d = d_rot = 128" in msg
 
 
 def test_codebook_order_is_validated():
