@@ -129,6 +129,23 @@ tq_status tq_value_layout(const tq_params* p, int* planes, int* words_per_plane,
 tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
                          int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
+/* Workspace bytes tq_encode_prod_ws needs for n vectors: 0 at d_rot = 128;
+ * at d_rot = 2048 (Hadamard) the QJL matrix split into fp16 hi/lo (16 MiB)
+ * plus a chunk of up to 32768 residual rows (fp16 hi/lo, 128 KiB each). */
+size_t tq_encode_workspace(const tq_params* p, int64_t n);
+
+/* tq_encode_prod with a caller-owned workspace (device, 256-B aligned, no
+ * initial contents, at least tq_encode_workspace(p, n) bytes, one call in
+ * flight per workspace).  Needed for the retrieval configuration, d_rot = 2048
+ * with the sign-flipped Hadamard rotation (d <= 2048, a multiple of 8,
+ * zero-padded): pass 1 runs the 2048-point Walsh-Hadamard transform in
+ * registers (one wave per vector) and quantises; pass 2 forms the QJL
+ * projection S r of each chunk of residuals on the matrix cores.  Records use
+ * the key layout of tq_key_layout (W = 64 words per plane). */
+tq_status tq_encode_prod_ws(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+                            int64_t ld_x, tq_cache out, const int64_t* slot, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* TurboQuant-MSE encode (values): as above without the QJL stage, b index
  * bits, written in the blocked value layout.  A group of 32 vectors that fills
  * one aligned block (slot NULL, or slots base + 0..31 with base a multiple of

@@ -23,7 +23,8 @@ TQ_F32, TQ_F16 = 0, 1
 
 EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
-    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_scores_workspace",
+    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_workspace", "tq_encode_prod_ws",
+    "tq_scores_workspace",
     "tq_scores", "tq_attend_workspace", "tq_attend",
 )
 
@@ -71,8 +72,11 @@ def lib():
         L.tq_value_layout.argtypes = [P, vp, vp, vp]
         for f in (L.tq_encode_prod, L.tq_encode_mse):
             f.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp]
+        L.tq_encode_prod_ws.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp, sz, vp]
         L.tq_scores_workspace.restype = sz
         L.tq_scores_workspace.argtypes = [P, ci, ci]
+        L.tq_encode_workspace.restype = sz
+        L.tq_encode_workspace.argtypes = [P, i64]
         L.tq_scores.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp, sz, vp]
         L.tq_attend_workspace.restype = sz
         L.tq_attend_workspace.argtypes = [P, P, ci, ci, i64]
@@ -80,7 +84,7 @@ def lib():
                                 vp, vp, sz, vp]
         for name in EXPORTED:
             if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace",
-                            "tq_attend_workspace"):
+                            "tq_attend_workspace", "tq_encode_workspace"):
                 getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -192,10 +196,20 @@ def _dtype_code(x):
     raise TypeError("x must be float16 or float32")
 
 
-def encode_prod(p: Params, x, out: Cache, slot=None, stream=None):
-    """tq_encode_prod on the rows of x (2-D, row stride x.stride(0))."""
-    _check(lib().tq_encode_prod(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
-                                _ptr(slot), _stream(stream)))
+def encode_workspace(p: Params, n: int) -> int:
+    return int(lib().tq_encode_workspace(p.c, int(n)))
+
+
+def encode_prod(p: Params, x, out: Cache, slot=None, stream=None, ws=None):
+    """tq_encode_prod on the rows of x (2-D, row stride x.stride(0)); with ws,
+    tq_encode_prod_ws (needed at d_rot = 2048)."""
+    if ws is None:
+        _check(lib().tq_encode_prod(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
+                                    _ptr(slot), _stream(stream)))
+    else:
+        _check(lib().tq_encode_prod_ws(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
+                                       _ptr(slot), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)))
 
 
 def encode_mse(p: Params, x, out: Cache, slot=None, stream=None):

@@ -85,7 +85,7 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
 }
 
 tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, int64_t n,
-                 int64_t ld_x, tq_cache out, const int64_t* slot, void* stream) {
+                 int64_t ld_x, tq_cache out, const int64_t* slot, void* ws, size_t ws_bytes, void* stream) {
   tq::EncodeArgs a;
   std::memset(&a, 0, sizeof(a));
   tq_status st = check_params(p, prod, &a.cb, false);
@@ -118,8 +118,17 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   hipStream_t s = (hipStream_t)stream;
   if (p->d == 128 && p->d_rot == 128)
     return hip_status(tq::launch_encode_dense128(a, s), "encode launch");
-  return fail(TQ_ERR_UNSUPPORTED, "encode supports d = d_rot = 128 (got rot %d, d %d, d_rot %d)",
-              p->rot, p->d, p->d_rot);
+  if (prod && p->rot == TQ_ROT_HADAMARD && p->d_rot == 2048) {
+    if (p->d % 8) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs d a multiple of 8 (got %d)", p->d);
+    const size_t need = tq::encode2k_workspace(n);
+    if (!ws) return fail(TQ_ERR_INVALID_ARG, "d_rot = 2048 encode needs a workspace (tq_encode_prod_ws)");
+    if (!aligned(ws, 256)) return fail(TQ_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+    if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
+    return hip_status(tq::launch_encode2k(a, ws, s), "encode launch");
+  }
+  return fail(TQ_ERR_UNSUPPORTED,
+              "encode supports d = d_rot = 128, and prod with the Hadamard rotation at d_rot = 2048 "
+              "(got %s, rot %d, d %d, d_rot %d)", prod ? "prod" : "mse", p->rot, p->d, p->d_rot);
 }
 
 }  // namespace
@@ -167,12 +176,23 @@ tq_status tq_value_layout(const tq_params* p, int* planes, int* words, int* scal
 
 tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
                          tq_cache out, const int64_t* slot, void* stream) {
-  return encode(p, true, x, dtype, n, ld_x, out, slot, stream);
+  return encode(p, true, x, dtype, n, ld_x, out, slot, nullptr, 0, stream);
+}
+
+size_t tq_encode_workspace(const tq_params* p, int64_t n) {
+  if (!p || n <= 0) return 0;
+  if (p->d_rot == 2048 && p->rot == TQ_ROT_HADAMARD) return tq::encode2k_workspace(n);
+  return 0;
+}
+
+tq_status tq_encode_prod_ws(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+                            tq_cache out, const int64_t* slot, void* ws, size_t ws_bytes, void* stream) {
+  return encode(p, true, x, dtype, n, ld_x, out, slot, ws, ws_bytes, stream);
 }
 
 tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
                         tq_cache out, const int64_t* slot, void* stream) {
-  return encode(p, false, x, dtype, n, ld_x, out, slot, stream);
+  return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream);
 }
 
 size_t tq_scores_workspace(const tq_params* kp, int segs, int group) {

@@ -1,0 +1,276 @@
+// TurboQuant-prod encode at d_rot = 2048, sign-flipped Hadamard rotation
+// (retrieval embeddings: d <= 2048, zero-padded to the Hadamard order).
+//
+// Per vector x (blog notes on the paper: Q_prod; explainer page, the random
+// Hadamard rotation):
+//   n = ||x||, u = x / n, y = H diag(eps) pad(u) / sqrt(2048),
+//   idx_j = #{beta_k <= y_j}, r = y - c[idx], gamma = ||r||, z = [S r >= 0].
+//
+// Pass 1, one wave per vector: lane l holds coordinates 32 l .. 32 l + 31.
+// The Walsh-Hadamard transform runs in registers: butterflies on index bits
+// 0..4 stay inside a lane, bits 5..10 pair lane l with lane l ^ 2^(b-5)
+// (cross-lane shuffles).  Plane word w of a record covers coordinates
+// 32 w .. 32 w + 31, so lane l builds word l of every index plane by itself.
+// The residual goes to the workspace as fp16 hi + lo (prescaled by 2^8).
+//
+// Pass 2, the QJL projection of a chunk of residuals, C = R S^T (M = vectors,
+// N = K = 2048), on v_mfma_f32_32x32x16_f16 with fp16 hi/lo operands (three
+// products, ~2^-22 relative).  A workgroup (4 waves) owns a 128 x 128 tile of
+// C; a wave owns 64 x 64.  Lane l of a 32 x 32 accumulator holds column l % 32
+// for 16 rows, so the sign bits of a row's 32 columns are one ballot: the
+// epilogue writes whole QJL plane words.  Consecutive workgroups share an
+// M tile and the workgroup-to-XCD assignment (id mod 8) gives each XCD two
+// fixed 128-row slices of S, which stay in its L2.
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int D2 = 2048;
+constexpr int VPL = 32;                  // coordinates per lane
+constexpr float R2_SCALE = 256.f;        // 2^8, keeps the residual's lo part normal in fp16
+constexpr float INV_SQRT_D2 = 0.02209708691207961f;   // 1 / sqrt(2048)
+constexpr int SIGN_TILE = 128;
+
+__global__ __launch_bounds__(256) void split_s_f16(const float* __restrict__ s, _Float16* hi, _Float16* lo,
+                                                    int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    _Float16 h, l;
+    split_f16(s[i], h, l);
+    hi[i] = h;
+    lo[i] = l;
+  }
+}
+
+template <int BQ>
+__device__ __forceinline__ void quantize2k(float y, const Codebook& cb, int& idx, float& chat) {
+  idx = 0;
+  chat = cb.c[0];
+#pragma unroll
+  for (int k = 0; k < (1 << BQ) - 1; ++k) {
+    const bool ge = y >= cb.b[k];
+    idx += ge ? 1 : 0;
+    chat = ge ? cb.c[k + 1] : chat;
+  }
+}
+
+template <int BQ, bool F16IN>
+__global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
+  constexpr int P = BQ + 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t vec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);    // chunk-local
+  if (vec >= a.cn) return;
+  const int64_t gv = a.v0 + vec;
+  const int j0 = VPL * lane;
+  float v[VPL];
+  if (F16IN) {
+    const _Float16* src = static_cast<const _Float16*>(a.x) + gv * a.ld_x + j0;
+#pragma unroll
+    for (int i = 0; i < VPL; i += 8) {
+      half8 h = {};
+      if (j0 + i < a.d) h = *reinterpret_cast<const half8*>(src + i);   // d is a multiple of 8
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i + e] = (float)h[e];
+    }
+  } else {
+    const float* src = static_cast<const float*>(a.x) + gv * a.ld_x + j0;
+#pragma unroll
+    for (int i = 0; i < VPL; i += 4) {
+      float4 f = {0.f, 0.f, 0.f, 0.f};
+      if (j0 + i < a.d) f = *reinterpret_cast<const float4*>(src + i);   // d is a multiple of 4
+      v[i] = f.x; v[i + 1] = f.y; v[i + 2] = f.z; v[i + 3] = f.w;
+    }
+  }
+  float s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) s2 = fmaf(v[i], v[i], s2);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s2 += shfl_xor_f(s2, o);
+  const float n = sqrtf(s2);
+  const float inv = n > 0.f ? 1.f / n : 0.f;
+  {
+    const float4* e4 = reinterpret_cast<const float4*>(a.eps + j0);
+#pragma unroll
+    for (int i = 0; i < VPL; i += 4) {
+      const float4 e = e4[i / 4];
+      v[i] *= inv * e.x; v[i + 1] *= inv * e.y; v[i + 2] *= inv * e.z; v[i + 3] *= inv * e.w;
+    }
+  }
+  // Walsh-Hadamard butterflies: (a, b) -> (a + b, a - b) on every index bit
+#pragma unroll
+  for (int b = 0; b < 5; ++b) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      if (i & (1 << b)) continue;
+      const float p = v[i], q = v[i | (1 << b)];
+      v[i] = p + q;
+      v[i | (1 << b)] = p - q;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const bool upper = (lane >> b) & 1;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const float o = shfl_xor_f(v[i], 1 << b);
+      v[i] = upper ? o - v[i] : v[i] + o;
+    }
+  }
+  // quantise, pack this lane's plane words, residual
+  uint32_t w[BQ];
+#pragma unroll
+  for (int p = 0; p < BQ; ++p) w[p] = 0u;
+  float g2 = 0.f;
+  half8 rh[VPL / 8], rl[VPL / 8];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const float y = v[i] * INV_SQRT_D2;
+    int idx;
+    float chat;
+    quantize2k<BQ>(y, a.cb, idx, chat);
+#pragma unroll
+    for (int p = 0; p < BQ; ++p) w[p] |= (uint32_t)((idx >> p) & 1) << i;
+    const float r = y - chat;
+    g2 = fmaf(r, r, g2);
+    _Float16 h, l;
+    split_f16(r * R2_SCALE, h, l);
+    rh[i / 8][i % 8] = h;
+    rl[i / 8][i % 8] = l;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) g2 += shfl_xor_f(g2, o);
+  half8* rhi = reinterpret_cast<half8*>(a.r_hi + vec * D2 + j0);
+  half8* rlo = reinterpret_cast<half8*>(a.r_lo + vec * D2 + j0);
+#pragma unroll
+  for (int q = 0; q < VPL / 8; ++q) {
+    rhi[q] = rh[q];
+    rlo[q] = rl[q];
+  }
+  const int64_t rec = a.slot ? a.slot[gv] : gv;
+  uint32_t* dst = a.planes + rec * (P * (D2 / 32)) + lane * P;
+#pragma unroll
+  for (int p = 0; p < BQ; ++p) dst[p] = w[p];
+  if (lane == 0)
+    reinterpret_cast<uint32_t*>(a.scalars)[rec] = (uint32_t)f16_bits(n) | ((uint32_t)f16_bits(sqrtf(g2)) << 16);
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void encode2k_signs(Encode2kArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t mw = (int64_t)blockIdx.y * SIGN_TILE + 64 * (wave >> 1);   // chunk-local vector rows
+  const int iw = blockIdx.x * SIGN_TILE + 64 * (wave & 1);                 // output coordinates
+  const int l32 = lane & 31, kh = lane >> 5;
+  const _Float16* ah = a.r_hi + (mw + l32) * D2 + 8 * kh;
+  const _Float16* al = a.r_lo + (mw + l32) * D2 + 8 * kh;
+  const _Float16* bh = a.s_hi + (int64_t)(iw + l32) * D2 + 8 * kh;
+  const _Float16* bl = a.s_lo + (int64_t)(iw + l32) * D2 + 8 * kh;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  for (int k0 = 0; k0 < D2; k0 += 16) {
+    half8 Ah[2], Al[2], Bh[2], Bl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      Ah[t] = *reinterpret_cast<const half8*>(ah + (int64_t)32 * t * D2 + k0);
+      Al[t] = *reinterpret_cast<const half8*>(al + (int64_t)32 * t * D2 + k0);
+      Bh[t] = *reinterpret_cast<const half8*>(bh + (int64_t)32 * t * D2 + k0);
+      Bl[t] = *reinterpret_cast<const half8*>(bl + (int64_t)32 * t * D2 + k0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = mfma32x32x16(Ah[i], Bh[j], acc[i][j]);
+        acc[i][j] = mfma32x32x16(Al[i], Bh[j], acc[i][j]);
+        acc[i][j] = mfma32x32x16(Ah[i], Bl[j], acc[i][j]);
+      }
+  }
+  // signs: ballot over the 32 columns of each accumulator row
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t word = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint64_t m = __ballot(acc[i][j][r] >= 0.f);
+        word = lane == r ? (uint32_t)m : word;
+        word = lane == 32 + r ? (uint32_t)(m >> 32) : word;
+      }
+      // lane r (< 16) holds row 8 (r / 4) + r % 4, lane 32 + r row 8 (r / 4) + 4 + r % 4
+      const int r = lane & 31;
+      if (r < 16) {
+        const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
+        const int64_t m = mw + 32 * i + row;
+        if (m < a.cn) {
+          const int64_t gv = a.v0 + m;
+          const int64_t rec = a.slot ? a.slot[gv] : gv;
+          a.planes[rec * (P * (D2 / 32)) + ((iw + 32 * j) / 32) * P + (P - 1)] = word;
+        }
+      }
+    }
+}
+
+template <int BQ>
+hipError_t run_chunks(const Encode2kArgs& base, bool f16, hipStream_t stream) {
+  Encode2kArgs a = base;
+  for (int64_t v0 = 0; v0 < base.n; v0 += base.chunk) {
+    a.v0 = v0;
+    a.cn = base.n - v0 < base.chunk ? base.n - v0 : base.chunk;
+    const unsigned g1 = (unsigned)((a.cn + 3) / 4);
+    if (f16)
+      hipLaunchKernelGGL((encode2k_pass1<BQ, true>), dim3(g1), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((encode2k_pass1<BQ, false>), dim3(g1), dim3(256), 0, stream, a);
+    const dim3 g2(D2 / SIGN_TILE, (unsigned)((a.cn + SIGN_TILE - 1) / SIGN_TILE));
+    hipLaunchKernelGGL((encode2k_signs<BQ + 1>), g2, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+int64_t encode2k_chunk(int64_t n) { return n < 32768 ? (n + SIGN_TILE - 1) / SIGN_TILE * SIGN_TILE : 32768; }
+
+size_t encode2k_workspace(int64_t n) {
+  // S hi + lo, then the residual chunk hi + lo, all fp16
+  return (size_t)2 * D2 * D2 * sizeof(_Float16) + (size_t)2 * encode2k_chunk(n) * D2 * sizeof(_Float16);
+}
+
+hipError_t launch_encode2k(const EncodeArgs& e, void* ws, hipStream_t stream) {
+  Encode2kArgs a;
+  a.x = e.x;
+  a.ld_x = e.ld_x;
+  a.d = e.d;
+  a.n = e.n;
+  a.eps = e.eps;
+  a.cb = e.cb;
+  a.planes = e.planes;
+  a.scalars = e.scalars;
+  a.slot = e.slot;
+  a.chunk = encode2k_chunk(e.n);
+  _Float16* w = static_cast<_Float16*>(ws);
+  a.s_hi = w;
+  a.s_lo = w + (size_t)D2 * D2;
+  a.r_hi = w + (size_t)2 * D2 * D2;
+  a.r_lo = a.r_hi + (size_t)a.chunk * D2;
+  a.v0 = 0;
+  a.cn = 0;
+  hipLaunchKernelGGL(split_s_f16, dim3(1024), dim3(256), 0, stream, e.s, a.s_hi, a.s_lo, (int64_t)D2 * D2);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  switch (e.bq) {
+    case 1: return run_chunks<1>(a, e.f16_in, stream);
+    case 2: return run_chunks<2>(a, e.f16_in, stream);
+    case 3: return run_chunks<3>(a, e.f16_in, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

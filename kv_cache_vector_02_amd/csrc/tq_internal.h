@@ -37,6 +37,25 @@ struct EncodeArgs {
 
 hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream);
 
+// Prod encode at d_rot = 2048 (Hadamard): chunked two-pass path with a workspace.
+struct Encode2kArgs {
+  const void* x;
+  int64_t ld_x;
+  int d;
+  int64_t n;           // vectors in the call
+  int64_t v0, cn;      // current chunk: first vector, count
+  int64_t chunk;       // vectors per chunk (multiple of 128 rows of residual space)
+  const float* eps;
+  Codebook cb;
+  uint32_t* planes;
+  uint16_t* scalars;
+  const int64_t* slot;
+  _Float16 *s_hi, *s_lo;   // [2048][2048]
+  _Float16 *r_hi, *r_lo;   // [chunk][2048], prescaled residuals
+};
+size_t encode2k_workspace(int64_t n);
+hipError_t launch_encode2k(const EncodeArgs& a, void* ws, hipStream_t stream);
+
 struct ScoreArgs {
   const float* q;        // [segs*group][d]
   int segs, group, d;

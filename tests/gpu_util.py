@@ -68,7 +68,11 @@ class Setup:
         n = x.shape[0]
         cache = cache or self.alloc(records or n)
         sl = None if slot is None else T.from_numpy(np.asarray(slot, np.int64)).cuda()
-        (tq.encode_prod if self.prod else tq.encode_mse)(self.params, x, cache, slot=sl)
+        if self.prod and self.d_rot == 2048:
+            ws = tq.alloc_workspace(tq.encode_workspace(self.params, n))
+            tq.encode_prod(self.params, x, cache, slot=sl, ws=ws)
+        else:
+            (tq.encode_prod if self.prod else tq.encode_mse)(self.params, x, cache, slot=sl)
         T.cuda.synchronize()
         planes = cache.planes.cpu().numpy().view(np.uint32)
         scal = cache.scalars.cpu().numpy()
