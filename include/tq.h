@@ -194,6 +194,24 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes tq_scores_topk needs. */
+size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k);
+
+/* Top-k retrieval by the asymmetric estimator (the estimator of tq_scores) over
+ * T prod records 0..T-1 encoded at d_rot = 2048 with the sign-flipped Hadamard
+ * rotation (tq_encode_prod_ws), for nq queries:
+ *   idx[i][0..k)  record indices of the k largest s(q_i, t), best first,
+ *                 ties to the lower index (int64, device)
+ *   val[i][0..k)  those estimates (float32, device)
+ * q       device f32 [nq][d], d a multiple of 4, zero-padded to 2048
+ * keys    record t at keys.planes + t * record words (seg_stride unused)
+ * ws      device workspace of tq_scores_topk_workspace() bytes, 256-B aligned
+ * Supported: 1 <= k <= 16, T >= k; keys with b = 2, 3 or 4 bits.
+ * Launches: query transform, projection GEMM and quantisation; per block of
+ * 65536 records the bit-plane score GEMM and a per-query top-k; a final merge. */
+tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache keys, int64_t T, int k,
+                         int64_t* idx, float* val, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

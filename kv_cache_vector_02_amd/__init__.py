@@ -25,7 +25,7 @@ EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
     "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
-    "tq_scores", "tq_attend_workspace", "tq_attend",
+    "tq_scores", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
 )
 
 
@@ -78,13 +78,16 @@ def lib():
         L.tq_encode_workspace.restype = sz
         L.tq_encode_workspace.argtypes = [P, i64]
         L.tq_scores.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp, sz, vp]
+        L.tq_scores_topk_workspace.restype = sz
+        L.tq_scores_topk_workspace.argtypes = [P, ci, i64, ci]
+        L.tq_scores_topk.argtypes = [P, vp, ci, tq_cache, i64, ci, vp, vp, vp, sz, vp]
         L.tq_attend_workspace.restype = sz
         L.tq_attend_workspace.argtypes = [P, P, ci, ci, i64]
         L.tq_attend.argtypes = [P, P, vp, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
                                 vp, vp, sz, vp]
         for name in EXPORTED:
             if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace",
-                            "tq_attend_workspace", "tq_encode_workspace"):
+                            "tq_attend_workspace", "tq_encode_workspace", "tq_scores_topk_workspace"):
                 getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -243,3 +246,13 @@ def attend(kp: Params, vp: Params, q, segs: int, group: int, keys: Cache, vals: 
     _check(lib().tq_attend(kp.c, vp.c, _ptr(q), segs, group, keys.c, vals.c, _ptr(length), int(T),
                            float(scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)))
+
+
+def topk_workspace(kp: Params, nq: int, T: int, k: int) -> int:
+    return int(lib().tq_scores_topk_workspace(kp.c, int(nq), int(T), int(k)))
+
+
+def scores_topk(kp: Params, q, keys: Cache, T: int, k: int, idx, val, ws, stream=None):
+    """tq_scores_topk: idx int64 [nq][k], val float32 [nq][k] (device tensors)."""
+    _check(lib().tq_scores_topk(kp.c, _ptr(q), q.shape[0], keys.c, int(T), int(k), _ptr(idx), _ptr(val),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

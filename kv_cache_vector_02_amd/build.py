@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtq.so")
 
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_encode2k.hip", "tq_decode.hip"]
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_encode2k.hip", "tq_decode.hip", "tq_retrieval.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -30,7 +30,8 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 # decode kernels: matrix-core results straight into VGPRs (no AGPR read-back)
-EXTRA = {"tq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"tq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "tq_retrieval.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -307,4 +307,48 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   return hip_status(tq::launch_attend128(a, (hipStream_t)stream), "attend launch");
 }
 
+size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k) {
+  if (!kp || nq <= 0 || T <= 0 || k <= 0) return 0;
+  return tq::topk2k_workspace(nq, T, k, kp->bits - 1);
+}
+
+tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache keys, int64_t T, int k,
+                         int64_t* idx, float* val, void* ws, size_t ws_bytes, void* stream) {
+  tq::Codebook cb;
+  tq_status st = check_params(kp, true, &cb, true);
+  if (st != TQ_OK) return st;
+  if (nq < 0 || T < 0 || k < 1) return fail(TQ_ERR_INVALID_ARG, "need nq >= 0, T >= 0, k >= 1");
+  if (nq == 0) return TQ_OK;
+  if (kp->rot != TQ_ROT_HADAMARD || kp->d_rot != 2048)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports the Hadamard rotation at d_rot = 2048");
+  if (kp->d % 4) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk needs d a multiple of 4 (got %d)", kp->d);
+  if (k > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports k <= 16");
+  if (T < k) return fail(TQ_ERR_INVALID_ARG, "need T >= k");
+  if (!q || !keys.planes || !keys.scalars || !idx || !val || !ws)
+    return fail(TQ_ERR_INVALID_ARG, "q, keys, idx, val and ws must be non-NULL");
+  if (!aligned(q, 16) || !aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(ws, 256) ||
+      !aligned(idx, 8) || !aligned(val, 4))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
+  const size_t need = tq::topk2k_workspace(nq, T, k, kp->bits - 1);
+  if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
+  tq::TopkLaunch L;
+  L.q = q;
+  L.nq = nq;
+  L.d = kp->d;
+  L.bq = kp->bits - 1;
+  L.k = k;
+  L.eps = kp->eps;
+  L.s = kp->s;
+  float u8[8];
+  tq::walsh_coefficients(cb, L.bq, u8, &L.usum);
+  for (int i = 0; i < 4; ++i) L.u[i] = u8[i];
+  L.planes = (const uint32_t*)keys.planes;
+  L.scalars = (const uint16_t*)keys.scalars;
+  L.T = T;
+  L.idx = idx;
+  L.val = val;
+  L.ws = ws;
+  return hip_status(tq::launch_topk2k(L, (hipStream_t)stream), "top-k launch");
+}
+
 }  // extern "C"

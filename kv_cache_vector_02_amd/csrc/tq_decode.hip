@@ -333,60 +333,7 @@ __device__ __forceinline__ void expand8(uint32_t w, uint32_t e[8]) {
   for (int k = 0; k < 8; ++k) e[k] = (w >> k) & 0x01010101u;
 }
 
-template <int P>
-struct Words;
-template <>
-struct Words<1> {
-  typedef uint32_t v __attribute__((ext_vector_type(1), aligned(4)));
-};
-template <>
-struct Words<2> {
-  typedef uint32_t v __attribute__((ext_vector_type(2), aligned(4)));
-};
-template <>
-struct Words<3> {
-  typedef uint32_t v __attribute__((ext_vector_type(3), aligned(4)));
-};
-template <>
-struct Words<4> {
-  typedef uint32_t v __attribute__((ext_vector_type(4), aligned(4)));
-};
-
 constexpr int SROW = 40;   // LDS row stride (floats) of the output transpose tile
-
-// Raw buffer access: a 128-bit descriptor (base, byte size) in scalar
-// registers and a per-lane byte offset (the scalar offset operand stays 0: the
-// range check covers the per-lane offset only).  Reads at or past the size
-// return zero and writes there are dropped, which bounds every access without
-// per-lane clamps; OOB_OFFSET marks a lane whose access must not happen.
-// Descriptor sizes stay below 2^31 (checked on the host) so that OOB_OFFSET
-// plus an access width never wraps into range.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int RSRC_FLAGS = 0x00020000;    // raw 32-bit data format
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_FLAGS);
-}
-constexpr uint32_t OOB_OFFSET = 0x80000000u;
-__device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
-  return b <= 0 ? 0u : (b >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)b);
-}
-
-template <int P>
-__device__ __forceinline__ typename Words<P>::v load_words(rsrc_t r, uint32_t voff) {
-  typedef typename Words<P>::v wv;
-  if constexpr (P == 1) {
-    wv w;
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
-    return w;
-  } else if constexpr (P == 2) {
-    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
-  } else if constexpr (P == 3) {
-    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0));
-  } else {
-    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-  }
-}
 
 __device__ __forceinline__ int combine3(i32x4 acc) {
   return (acc[0] * 256 + acc[1]) * 256 + acc[2];   // 65536 hi + 256 mid + lo
@@ -575,6 +522,8 @@ hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
   return hipGetLastError();
 }
 
+}  // namespace
+
 void walsh_coefficients(const Codebook& cb, int bq, float u[8], float* usum) {
   // u_S = 2^-bq sum_idx c[idx] prod_{p in S} (2 bit_p(idx) - 1), odd S in the plane order
   const int K = 1 << bq;
@@ -595,6 +544,8 @@ void walsh_coefficients(const Codebook& cb, int bq, float u[8], float* usum) {
   }
   *usum = (float)tot;
 }
+
+namespace {
 
 // Compute units of the current device (cached per device).
 int device_cus() {

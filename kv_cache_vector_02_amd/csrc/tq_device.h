@@ -43,4 +43,83 @@ __device__ __forceinline__ void split_f16(float t, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(t - (float)hi);
 }
 
+template <int P>
+struct Words;
+template <>
+struct Words<1> {
+  typedef uint32_t v __attribute__((ext_vector_type(1), aligned(4)));
+};
+template <>
+struct Words<2> {
+  typedef uint32_t v __attribute__((ext_vector_type(2), aligned(4)));
+};
+template <>
+struct Words<3> {
+  typedef uint32_t v __attribute__((ext_vector_type(3), aligned(4)));
+};
+template <>
+struct Words<4> {
+  typedef uint32_t v __attribute__((ext_vector_type(4), aligned(4)));
+};
+
+// Raw buffer access: a 128-bit descriptor (base, byte size) in scalar
+// registers and a per-lane byte offset (the scalar offset operand stays 0: the
+// range check covers the per-lane offset only).  Reads at or past the size
+// return zero and writes there are dropped, which bounds every access without
+// per-lane clamps; OOB_OFFSET marks a lane whose access must not happen.
+// Descriptor sizes stay below 2^31 (checked on the host) so that OOB_OFFSET
+// plus an access width never wraps into range.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_FLAGS = 0x00020000;    // raw 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_FLAGS);
+}
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
+  return b <= 0 ? 0u : (b >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)b);
+}
+
+template <int P>
+__device__ __forceinline__ typename Words<P>::v load_words(rsrc_t r, uint32_t voff) {
+  typedef typename Words<P>::v wv;
+  if constexpr (P == 1) {
+    wv w;
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+    return w;
+  } else if constexpr (P == 2) {
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+  } else if constexpr (P == 3) {
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0));
+  } else {
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+  }
+}
+
+// In-register Walsh-Hadamard transform of order 2048 across one wave: lane l
+// holds coordinates 32 l + i in v[i].  Butterflies (a, b) -> (a + b, a - b) on
+// index bits 0..4 stay in the lane; bits 5..10 pair lane l with lane
+// l ^ 2^(b-5).  The result is H v with the Sylvester H (no 1/sqrt scale).
+__device__ __forceinline__ void fwht2048_wave(float v[32], int lane) {
+#pragma unroll
+  for (int b = 0; b < 5; ++b) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i & (1 << b)) continue;
+      const float p = v[i], q = v[i | (1 << b)];
+      v[i] = p + q;
+      v[i | (1 << b)] = p - q;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const bool upper = (lane >> b) & 1;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float o = shfl_xor_f(v[i], 1 << b);
+      v[i] = upper ? o - v[i] : v[i] + o;
+    }
+  }
+}
+
 }  // namespace tq

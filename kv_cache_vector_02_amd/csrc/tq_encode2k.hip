@@ -97,26 +97,7 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
       v[i] *= inv * e.x; v[i + 1] *= inv * e.y; v[i + 2] *= inv * e.z; v[i + 3] *= inv * e.w;
     }
   }
-  // Walsh-Hadamard butterflies: (a, b) -> (a + b, a - b) on every index bit
-#pragma unroll
-  for (int b = 0; b < 5; ++b) {
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      if (i & (1 << b)) continue;
-      const float p = v[i], q = v[i | (1 << b)];
-      v[i] = p + q;
-      v[i | (1 << b)] = p - q;
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const bool upper = (lane >> b) & 1;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const float o = shfl_xor_f(v[i], 1 << b);
-      v[i] = upper ? o - v[i] : v[i] + o;
-    }
-  }
+  fwht2048_wave(v, lane);
   // quantise, pack this lane's plane words, residual
   uint32_t w[BQ];
 #pragma unroll

@@ -54,6 +54,28 @@ struct Encode2kArgs {
   _Float16 *r_hi, *r_lo;   // [chunk][2048], prescaled residuals
 };
 size_t encode2k_workspace(int64_t n);
+
+// Walsh coefficients u_S of the odd subsets of an odd-symmetric codebook of bq
+// index bits (plane order) and their sum.
+void walsh_coefficients(const Codebook& cb, int bq, float u[8], float* usum);
+
+// Top-k retrieval at d_rot = 2048 (Hadamard keys).
+struct TopkLaunch {
+  const float* q;          // [nq][d]
+  int nq, d, bq, k;
+  const float* eps;
+  const float* s;
+  float u[4];
+  float usum;
+  const uint32_t* planes;  // records, key layout with W = 64
+  const uint16_t* scalars;
+  int64_t T;
+  int64_t* idx;            // [nq][k]
+  float* val;              // [nq][k]
+  void* ws;
+};
+size_t topk2k_workspace(int nq, int64_t T, int k, int bq);
+hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream);
 hipError_t launch_encode2k(const EncodeArgs& a, void* ws, hipStream_t stream);
 
 struct ScoreArgs {
