@@ -19,6 +19,7 @@ average duration).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 matrix peak (the encode's instruction)
 
+# HBM bytes per launch of the score kernel, read by rocprofv3 (FETCH_SIZE and
+# WRITE_SIZE, each in its own run) and scaled by the factor the same counters
+# give for a plain device copy of known size (bench.py --copy-calibration);
+# valid only for the decode source they were measured on.
+# HBM bytes per score-pass launch from rocprofv3 counters: FETCH_SIZE 16595.5 KiB
+# x 1.99982 (a 256 MiB copy reads as 131084 KiB) + WRITE_SIZE 18432.0 KiB x 1.0
+# (the copy writes 262144 KiB); valid only for the kernel source it was taken on
+SCORE_TRAFFIC = {"tq_decode.hip sha256": "6f93a2014e77ea9534d231734bcfee85a26c7eb654eb27361cc7b5a24b26fc8b",
+                 "bytes_per_launch": 52858841}
+
 L_, H_, T_, D_ = 36, 2, 8192, 128
 G_ = 8
 BITS = 3
@@ -44,6 +55,24 @@ def make_params(torch, tq, prod, seed):
     pi = torch.from_numpy(haar_orthogonal(D_, seed, 2 if prod else 4)).cuda()
     s = torch.from_numpy(gaussian_matrix(D_, D_, seed, 3)).cuda() if prod else None
     return tq.Params(d=D_, bits=BITS, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b, pi=pi, s=s)
+
+
+def score_traffic():
+    path = os.path.join(ROOT, "kv_cache_vector_02_amd", "csrc", "tq_decode.hip")
+    with open(path, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return SCORE_TRAFFIC["bytes_per_launch"] if digest == SCORE_TRAFFIC["tq_decode.hip sha256"] else None
+
+
+def copy_calibration(torch):
+    """A plain 256 MiB device-to-device copy, five times: the known-size kernel
+    against which rocprofv3's FETCH_SIZE and WRITE_SIZE are scaled."""
+    a = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4, "copies": 5}), flush=True)
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -96,6 +125,8 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the known-size copy used to scale the traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the hot path has no cross-GPU step here "
@@ -105,6 +136,9 @@ def main():
     import torch
     import kv_cache_vector_02_amd as tq
     from tq_inputs import gaussian_queries, kv_tensor
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     torch.cuda.set_device(0)
     pk_ = make_params(torch, tq, True, SEED)
@@ -130,7 +164,7 @@ def main():
     def step(i, rec=None):
         e = i % R
         d = (i + 1) % R           # encoded two steps ago
-        marks = [ev() for _ in range(5)] if rec is not None else None
+        marks = [ev() for _ in range(6)] if rec is not None else None
         if marks:
             marks[0].record()
         tq.encode_prod(pk_, kx[e], kc[e])
@@ -139,12 +173,16 @@ def main():
         tq.encode_mse(pv_, vx[e], vc[e])
         if marks:
             marks[2].record()
-        tq.scores(pk_, q, segs, G_, kc[d], T_, scores, ws_s)
+        # tq_scores as its two halves so that the score kernel is timed alone
+        tq.scores_prepare(pk_, q, segs, G_, ws_s)
         if marks:
             marks[3].record()
-        tq.attend(pk_, pv_, q, segs, G_, kc[d], vc[d], T_, scale, out, ws_a)
+        tq.scores_prepared(pk_, segs, G_, kc[d], T_, scores, ws_s)
         if marks:
             marks[4].record()
+        tq.attend(pk_, pv_, q, segs, G_, kc[d], vc[d], T_, scale, out, ws_a)
+        if marks:
+            marks[5].record()
             rec.append(marks)
 
     for i in range(max(args.warmup, R)):
@@ -156,12 +194,32 @@ def main():
         step(args.warmup + i, rec)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dur = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(4)] for m in rec])   # ms
-    t_ek, t_ev, t_sc, t_at = dur.mean(axis=0)
+    dur = np.array([[m[j].elapsed_time(m[j + 1]) for j in range(5)] for m in rec])   # ms
+    t_ek, t_ev, t_prep, t_sk_call, t_at = dur.mean(axis=0)
+    t_sc = t_prep + t_sk_call
     ms_step = wall * 1e3 / args.steps
+    # the score kernel alone: back-to-back score passes between one pair of
+    # events, so the per-launch figure carries no event overhead; the passes
+    # walk 12 copies of an encoded cache (12 x 30.7 MB, more than the 256 MB
+    # memory-side cache) so that every pass reads its keys from HBM
+    burst = 12
+    kb = [tq.Cache(kc[0].planes.clone(), kc[0].scalars.clone(), T_) for _ in range(burst)]
+    for c in kb:
+        tq.scores_prepared(pk_, segs, G_, c, T_, scores, ws_s)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for c in kb:
+        tq.scores_prepared(pk_, segs, G_, c, T_, scores, ws_s)
+    e1.record()
+    torch.cuda.synchronize()
+    t_sk = e0.elapsed_time(e1) / burst
+    del kb
 
     score_bytes = N * 52 + segs * G_ * T_ * 4 + segs * G_ * D_ * 4
-    score_gbs = score_bytes / (t_sc * 1e-3) / 1e9
+    score_gbs = score_bytes / (t_sc * 1e-3) / 1e9                 # whole tq_scores call
+    kernel_bytes = N * 52 + segs * G_ * T_ * 4                      # the score pass reads keys, writes scores
+    kernel_gbs = kernel_bytes / (t_sk * 1e-3) / 1e9
     attend_bytes = N * (52 + 50) + segs * G_ * D_ * 8
     attend_gbs = attend_bytes / (t_at * 1e-3) / 1e9
     enc_rate = 2 * N / ((t_ek + t_ev) * 1e-3)
@@ -190,12 +248,14 @@ def main():
         "frac_hbm_peak": round(score_gbs / HBM_PEAK_GBS, 4),
         "encoded_vectors_per_s": round(enc_rate, 1),
         "kernels_ms": {"encode_prod": round(t_ek, 5), "encode_mse": round(t_ev, 5),
-                       "scores": round(t_sc, 5), "attend": round(t_at, 5)},
+                       "scores_prepare": round(t_prep, 5), "scores_pass_call": round(t_sk_call, 5),
+                       "scores_kernel_burst": round(t_sk, 5),
+                       "attend": round(t_at, 5)},
         "attend_GBps": round(attend_gbs, 1),
-        "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "tq_scores (query prep + score kernel)",
-                     "bytes_per_launch": score_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": score_traffic(),
+                     "kernel": "scores128 (score pass of tq_scores, all 72 segments in one launch)",
+                     "bytes_per_launch": kernel_bytes},
         "roofline_encode": {"bound": "mfma", "achieved": round(enc_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(enc_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                             "executed_TFLOPs": round(enc_exec_tflops, 2),

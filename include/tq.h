@@ -174,6 +174,16 @@ tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq
                     const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* The two halves of tq_scores, for callers that time them apart or score the
+ * same queries against several caches: tq_scores_prepare writes the query
+ * pack of every segment into ws (arguments as for tq_scores);
+ * tq_scores_prepared streams the keys against the pack ws holds (from the last
+ * tq_scores_prepare with the same kp, segs and group on this workspace). */
+tq_status tq_scores_prepare(const tq_params* kp, const float* q, int segs, int group, void* ws,
+                            size_t ws_bytes, void* stream);
+tq_status tq_scores_prepared(const tq_params* kp, int segs, int group, tq_cache keys, const int32_t* len,
+                             int64_t T, float* scores, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes tq_attend needs. */
 size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T);
 

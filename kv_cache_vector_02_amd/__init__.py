@@ -25,7 +25,7 @@ EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
     "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
-    "tq_scores", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
+    "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
 )
 
 
@@ -78,6 +78,8 @@ def lib():
         L.tq_encode_workspace.restype = sz
         L.tq_encode_workspace.argtypes = [P, i64]
         L.tq_scores.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp, sz, vp]
+        L.tq_scores_prepare.argtypes = [P, vp, ci, ci, vp, sz, vp]
+        L.tq_scores_prepared.argtypes = [P, ci, ci, tq_cache, vp, i64, vp, vp, sz, vp]
         L.tq_scores_topk_workspace.restype = sz
         L.tq_scores_topk_workspace.argtypes = [P, ci, i64, ci]
         L.tq_scores_topk.argtypes = [P, vp, ci, tq_cache, i64, ci, vp, vp, vp, sz, vp]
@@ -235,6 +237,17 @@ def scores(kp: Params, q, segs: int, group: int, keys: Cache, T: int, out, ws, l
            stream=None):
     _check(lib().tq_scores(kp.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def scores_prepare(kp: Params, q, segs: int, group: int, ws, stream=None):
+    _check(lib().tq_scores_prepare(kp.c, _ptr(q), segs, group, _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+def scores_prepared(kp: Params, segs: int, group: int, keys: Cache, T: int, out, ws, length=None,
+                    stream=None):
+    _check(lib().tq_scores_prepared(kp.c, segs, group, keys.c, _ptr(length), int(T), _ptr(out), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def attend_workspace(kp: Params, vp: Params, segs: int, group: int, T: int) -> int:

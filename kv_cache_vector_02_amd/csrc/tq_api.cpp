@@ -201,46 +201,82 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group) {
   return tq::scores128_workspace(segs, group);
 }
 
-tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
-                    const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
-                    void* stream) {
-  tq::ScoreArgs a;
-  std::memset(&a, 0, sizeof(a));
-  tq_status st = check_params(kp, true, &a.cb, true);
+// Validation and argument set-up shared by the score entry points; q may be
+// NULL when need_q is false (score pass over an already prepared pack).
+static tq_status score_args(const tq_params* kp, const float* q, bool need_q, int segs, int group,
+                            tq_cache keys, bool need_keys, const int32_t* len, int64_t T, float* scores,
+                            bool need_scores, void* ws, size_t ws_bytes, tq::ScoreArgs* a, bool* nothing) {
+  std::memset(a, 0, sizeof(*a));
+  *nothing = false;
+  tq_status st = check_params(kp, true, &a->cb, true);
   if (st != TQ_OK) return st;
   if (segs < 0 || group < 1 || T < 0) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
-  if (segs == 0 || T == 0) return TQ_OK;
+  if (segs == 0 || (need_keys && T == 0)) {
+    *nothing = true;
+    return TQ_OK;
+  }
   if (kp->d != 128 || kp->d_rot != 128)
     return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports d = d_rot = 128 (got %d, %d)", kp->d, kp->d_rot);
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports up to 16 query heads per segment");
-  if (!q || !keys.planes || !keys.scalars || !scores || !ws)
+  if ((need_q && !q) || (need_keys && (!keys.planes || !keys.scalars)) || (need_scores && !scores) || !ws)
     return fail(TQ_ERR_INVALID_ARG, "q, keys, scores and ws must be non-NULL");
-  if (keys.seg_stride < T && segs > 1) return fail(TQ_ERR_INVALID_ARG, "keys.seg_stride must be >= T");
-  if (!aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(ws, 256) || !aligned(q, 16) ||
-      !aligned(scores, 4))
+  if (need_keys && keys.seg_stride < T && segs > 1) return fail(TQ_ERR_INVALID_ARG, "keys.seg_stride must be >= T");
+  if ((need_keys && (!aligned(keys.planes, 16) || !aligned(keys.scalars, 4))) || !aligned(ws, 256) ||
+      (need_q && !aligned(q, 16)) || (need_scores && !aligned(scores, 4)))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
   const size_t need = tq::scores128_workspace(segs, group);
   if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
   const int64_t stride = segs == 1 && keys.seg_stride < T ? T : keys.seg_stride;
-  if (stride * 16 * kp->bits >= (1ll << 31) || (int64_t)group * T * 4 >= (1ll << 31))
+  if (need_keys && (stride * 16 * kp->bits >= (1ll << 31) || (int64_t)group * T * 4 >= (1ll << 31)))
     return fail(TQ_ERR_UNSUPPORTED, "tq_scores addresses at most 2 GiB of keys and of scores per segment");
-  a.q = q;
-  a.segs = segs;
-  a.group = group;
-  a.d = kp->d;
-  a.pi = kp->pi;
-  a.eps = kp->eps;
-  a.rot = kp->rot;
-  a.s = kp->s;
-  a.bq = kp->bits - 1;
-  a.planes = (const uint32_t*)keys.planes;
-  a.scalars = (const uint16_t*)keys.scalars;
-  a.seg_stride = stride;
-  a.len = len;
-  a.T = T;
-  a.scores = scores;
-  a.ws = ws;
+  a->q = q;
+  a->segs = segs;
+  a->group = group;
+  a->d = kp->d;
+  a->pi = kp->pi;
+  a->eps = kp->eps;
+  a->rot = kp->rot;
+  a->s = kp->s;
+  a->bq = kp->bits - 1;
+  a->planes = (const uint32_t*)keys.planes;
+  a->scalars = (const uint16_t*)keys.scalars;
+  a->seg_stride = stride;
+  a->len = len;
+  a->T = T;
+  a->scores = scores;
+  a->ws = ws;
+  return TQ_OK;
+}
+
+tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
+                    const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
+                    void* stream) {
+  tq::ScoreArgs a;
+  bool nothing;
+  tq_status st = score_args(kp, q, true, segs, group, keys, true, len, T, scores, true, ws, ws_bytes, &a, &nothing);
+  if (st != TQ_OK || nothing) return st;
   return hip_status(tq::launch_scores128(a, (hipStream_t)stream), "scores launch");
+}
+
+tq_status tq_scores_prepare(const tq_params* kp, const float* q, int segs, int group, void* ws,
+                            size_t ws_bytes, void* stream) {
+  tq::ScoreArgs a;
+  bool nothing;
+  tq_cache none = {nullptr, nullptr, 0};
+  tq_status st = score_args(kp, q, true, segs, group, none, false, nullptr, 1, nullptr, false, ws, ws_bytes, &a,
+                            &nothing);
+  if (st != TQ_OK || nothing) return st;
+  return hip_status(tq::launch_scores128_prepare(a, (hipStream_t)stream), "scores prepare launch");
+}
+
+tq_status tq_scores_prepared(const tq_params* kp, int segs, int group, tq_cache keys, const int32_t* len,
+                             int64_t T, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  tq::ScoreArgs a;
+  bool nothing;
+  tq_status st = score_args(kp, nullptr, false, segs, group, keys, true, len, T, scores, true, ws, ws_bytes, &a,
+                            &nothing);
+  if (st != TQ_OK || nothing) return st;
+  return hip_status(tq::launch_scores128_prepared(a, (hipStream_t)stream), "scores launch");
 }
 
 size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T) {

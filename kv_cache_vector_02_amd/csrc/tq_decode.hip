@@ -391,12 +391,15 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
 
   wvec wr[RING][2];
   uint32_t sr[RING][2];
+  // pairs past this workgroup's span get the out-of-range offset: zeros, and
+  // no memory traffic (no over-read of the next span)
   auto load_pair = [&](int slot, int pr) {
+    const bool ok = pr < npairs;
     const uint32_t tb = (uint32_t)(32 * pr);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      wr[slot][h] = load_words<P>(rk, vk + (tb + 16 * h) * RB);
-      sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + (tb + 16 * h) * 4, 0, 0);
+      wr[slot][h] = load_words<P>(rk, ok ? vk + (tb + 16 * h) * RB : OOB_OFFSET);
+      sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? vs + (tb + 16 * h) * 4 : OOB_OFFSET, 0, 0);
     }
   };
   const uint8_t* pack = a.ws + (size_t)seg * pack_bytes(MT, F);
@@ -617,9 +620,17 @@ hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t str
 }
 
 hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
-  const int slices = score_slices(a.bq);
-  hipError_t e = launch_scores128_prep(a, slices, stream);
+  hipError_t e = launch_scores128_prepare(a, stream);
   if (e != hipSuccess) return e;
+  return launch_scores128_prepared(a, stream);
+}
+
+hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream) {
+  return launch_scores128_prep(a, score_slices(a.bq), stream);
+}
+
+hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream) {
+  const int slices = score_slices(a.bq);
   const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   Score128Args s;
   s.ws = static_cast<const uint8_t*>(a.ws);
@@ -786,21 +797,25 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
   // the issue order is pinned (scheduling barriers) so that the prologue and
   // the loop body leave the same outstanding loads at the loop header, which
   // lets each wait count only the loads it needs
+  // groups past the span get the out-of-range offset (zeros, no traffic)
   auto load_keys = [&](int g) {
+    const bool ok = g < ngroups;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tile = 0; tile < 8; ++tile) {
       const uint32_t tok = (uint32_t)(128 * g + 16 * tile);
-      kw[tile] = load_words<PK>(rk, vko + tok * RBK);
-      ks[tile] = __builtin_amdgcn_raw_buffer_load_b32(rks, vkso + tok * 4, 0, 0);
+      kw[tile] = load_words<PK>(rk, ok ? vko + tok * RBK : OOB_OFFSET);
+      ks[tile] = __builtin_amdgcn_raw_buffer_load_b32(rks, ok ? vkso + tok * 4 : OOB_OFFSET, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   auto load_vals = [&](int g) {
+    const bool ok = g < ngroups;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) vw[nt] = load_words<PV>(rv, vvo + (uint32_t)(4 * g) * VBB + nt * 16 * (PV * 4));
-    vn2 = __builtin_amdgcn_raw_buffer_load_b32(rvs, vno + (uint32_t)(256 * g), 0, 0);
+    for (int nt = 0; nt < 8; ++nt)
+      vw[nt] = load_words<PV>(rv, ok ? vvo + (uint32_t)(4 * g) * VBB + nt * 16 * (PV * 4) : OOB_OFFSET);
+    vn2 = __builtin_amdgcn_raw_buffer_load_b32(rvs, ok ? vno + (uint32_t)(256 * g) : OOB_OFFSET, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   load_keys(wave);

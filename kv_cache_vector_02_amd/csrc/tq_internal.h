@@ -97,6 +97,8 @@ struct ScoreArgs {
 };
 
 hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream);    // query pack only
+hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream);   // score pass only
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream);
 size_t scores128_workspace(int segs, int group);
 

@@ -171,3 +171,31 @@ def test_query_magnitude_extremes(qscale):
     got = gpu_scores(st, q, 1, 8, cache, 600)
     ref = est.prod_scores(q, idx, z, n, g, st.rot, st.s, st.c32)
     check_rows(got, ref)
+
+
+def test_prepare_then_prepared_equals_scores():
+    # the two halves of tq_scores give the same scores; the pack serves two caches
+    _log("scores prepare + prepared")
+    Tt = torch()
+    segs, T_, G = 4, 777, 8
+    st = Setup(bits=3, prod=True, seed=11)
+    x1 = kv_tensor(1, segs, T_, 128, seed=11)[0].reshape(-1, 128)
+    x2 = kv_tensor(1, segs, T_, 128, seed=12)[0].reshape(-1, 128)
+    c1, f1 = oracle_key_cache(st, x1, seg_stride=T_)
+    c2, f2 = oracle_key_cache(st, x2, seg_stride=T_)
+    q = gaussian_queries(segs * G, 128, seed=11)
+    qd = Tt.from_numpy(q).cuda()
+    ws = tq.alloc_workspace(tq.scores_workspace(st.params, segs, G))
+    tq.scores_prepare(st.params, qd, segs, G, ws)
+    outs = []
+    for c in (c1, c2):
+        o = Tt.full((segs * G, T_), float("nan"), dtype=Tt.float32, device="cuda")
+        tq.scores_prepared(st.params, segs, G, c, T_, o, ws)
+        outs.append(o.cpu().numpy())
+    for c, got in ((c1, outs[0]), (c2, outs[1])):
+        assert np.array_equal(got, gpu_scores(st, q, segs, G, c, T_))
+    for (idx, z, n, g), got in ((f1, outs[0]), (f2, outs[1])):
+        for s in range(segs):
+            rows = slice(s * G, (s + 1) * G)
+            sl = slice(s * T_, (s + 1) * T_)
+            check_rows(got[rows], est.prod_scores(q[rows], idx[sl], z[sl], n[sl], g[sl], st.rot, st.s, st.c32))
