@@ -134,10 +134,12 @@ struct PrepLds {
   float qp[MAXG * QTS];      // q_proj[head][coordinate]
   float part[8][MAXG][4];
   float stat[MAXG][4];
+  float wsc[9][MAXG];        // weight scale per (plane, head); row 8 is the QJL plane
 };
 
-// Segment seg's query pack -> dst (all 512 threads of the workgroup).
-template <bool HAD>
+// Segment seg's query pack -> dst (all 512 threads of the workgroup); S is the
+// number of base-256 digits per weight.
+template <bool HAD, int S>
 __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L, uint8_t* dst) {
   float* qr = L.qr;
   float* qp = L.qp;
@@ -173,6 +175,8 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
     sv[2 * ks] = srow[k4];
     sv[2 * ks + 1] = srow[k4 + 1];
   }
+  // keep all of them ahead of the first product (one memory round trip)
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- q_rot^T = Pi . Q^T, rows 16 wave + 4 kq + r, head col ----
   {
@@ -252,71 +256,82 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
       sp += part[w][t][3];
     }
     float umax = 0.f;
-    for (int p = 0; p < np; ++p) umax = fmaxf(umax, fabsf(2.f * a.u[p]));
+#pragma unroll
+    for (int p = 0; p < 8; ++p) umax = p < np ? fmaxf(umax, fabsf(2.f * a.u[p])) : umax;
     const float mm = mx * umax, pm = 2.f * px;
-    const float qmax = a.slices == 2 ? QMAX2 : QMAX3;
-    stat[t][0] = mm > 0.f ? mm / qmax : 1.f;
+    const float qmax = S == 2 ? QMAX2 : QMAX3;
+    const float sm = mm > 0.f ? mm / qmax : 1.f, sq = pm > 0.f ? pm / qmax : 1.f;
+    stat[t][0] = sm;
     stat[t][1] = -a.usum * sr;
-    stat[t][2] = pm > 0.f ? pm / qmax : 1.f;
+    stat[t][2] = sq;
     stat[t][3] = -sp;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) L.wsc[p][t] = 2.f * a.u[p] / sm;
+    L.wsc[8][t] = 2.f / sq;
   }
   __syncthreads();
   // ---- quantise: one item = (tile mt, fragment f = 2 p + m, lane group kg,
-  // head hl of the tile's lane group, dword k); its four bytes bi = 0..3 are
-  // coordinates 32 kg + 8 bi + 4 m + k, and its digits go to lanes
-  // 16 kg + R hl + r (R = rows per head; rows past the digits stay zero) ----
-  const int R = a.slices == 2 ? 2 : 4;          // A rows per head
-  const int HPG = 4 / R;                        // heads per lane group
-  const int nitems = a.mt * F * 256 / R;        // 64 lanes x 4 dwords per fragment, R per item
+  // head hl of the tile) covers the 16 coordinates 32 kg + 8 bi + 4 m + k
+  // (bi, k = 0..3), byte bi of dword k of the A operand of lanes
+  // 16 kg + R hl + r, r = the digit (R rows per head; a fourth row stays zero) ----
+  constexpr int R = S == 2 ? 2 : 4;             // A rows per head
+  constexpr int HT = 16 / R;                    // heads per 16-row tile
+  const int nitems = a.mt * F * 4 * HT;
   for (int it = t; it < nitems; it += PREP_THREADS) {
-    const int k = it & 3;
-    const int hl = (it >> 2) % (4 * HPG);       // head within the tile
-    const int rest = (it >> 2) / (4 * HPG);
+    const int hl = it % HT, rest = it / HT;
     const int kg = rest & 3;
     const int f = (rest >> 2) % F, mt = (rest >> 2) / F;
     const int p = f >> 1, m = f & 1;
-    const int h = 4 * HPG * mt + hl;
-    uint32_t d[3] = {0u, 0u, 0u};
-    if (h < G) {
-      const float* src = p < np ? &qr[h * QTS] : &qp[h * QTS];
-      const float up = p == 0 ? a.u[0] : p == 1 ? a.u[1] : p == 2 ? a.u[2] : a.u[3];
-      const float wsc = p < np ? 2.f * up / stat[h][0] : 2.f / stat[h][2];
+    const int h = HT * mt + hl;
+    const bool live = h < G;
+    const int hs = live ? h : 0;
+    const float* src = (p < np ? qr : qp) + hs * QTS + 32 * kg + 4 * m;
+    const float wsc = live ? L.wsc[p < np ? p : 8][hs] : 0.f;
+    float4 v[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) v[bi] = *reinterpret_cast<const float4*>(src + 8 * bi);
+    uint32_t d0[4], d1[4], d2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
       int s0[4], s1[4], s2[4];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        const float w = src[32 * kg + 8 * bi + 4 * m + k] * wsc;
-        if (R == 2) {
+        const float w = v[bi][k] * wsc;
+        if constexpr (S == 2) {
           slices2(w, s0[bi], s1[bi]);
           s2[bi] = 0;
         } else {
           slices3(w, s0[bi], s1[bi], s2[bi]);
         }
       }
-      d[0] = pack4(s0[0], s0[1], s0[2], s0[3]);
-      d[1] = pack4(s1[0], s1[1], s1[2], s1[3]);
-      d[2] = pack4(s2[0], s2[1], s2[2], s2[3]);
+      d0[k] = pack4(s0[0], s0[1], s0[2], s0[3]);
+      d1[k] = pack4(s1[0], s1[1], s1[2], s1[3]);
+      d2[k] = pack4(s2[0], s2[1], s2[2], s2[3]);
     }
-    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst) + ((mt * F + f) * 64 + 16 * kg + R * hl) * 4 + k;
-    d32[0] = d[0];
-    d32[4] = d[1];
-    if (R == 4) {
-      d32[8] = d[2];
-      d32[12] = 0u;
+    i32x4* row = reinterpret_cast<i32x4*>(dst) + (mt * F + f) * 64 + 16 * kg + R * hl;
+    row[0] = i32x4{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3]};
+    row[1] = i32x4{(int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
+    if constexpr (R == 4) {
+      row[2] = i32x4{(int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3]};
+      row[3] = i32x4{0, 0, 0, 0};
     }
   }
   float* consts = reinterpret_cast<float*>(dst + fbytes);
   if (t < a.mt * 16 / R * 4) consts[t] = t < G * 4 ? stat[t >> 2][t & 3] : 0.f;
 }
 
-template <bool HAD>
-__global__ __launch_bounds__(PREP_THREADS) void prep_queries128(PrepArgs a) {
+// (at most two waves per SIMD: the register budget keeps every operand load
+// of a lane in flight at once)
+template <bool HAD, int S>
+__global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void prep_queries128(PrepArgs a) {
   __shared__ PrepLds L;
   const int F = 2 * (mse_planes(a.bq) + 1);
-  prep_pack<HAD>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
+  prep_pack<HAD, S>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
 }
 
 struct Score128Args {
-  const uint8_t* ws;
+  const uint8_t* ws;            // query packs (prep_queries128)
   const uint32_t* planes;
   const uint16_t* scalars;
   int64_t seg_stride;
@@ -521,7 +536,8 @@ hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
   const int64_t span = split_span(segs, s.T, nb * device_cus(), 32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   const int64_t chunks = (s.T + span - 1) / span;
-  hipLaunchKernelGGL((scores128<BQ, MT, S>), dim3((unsigned)chunks, (unsigned)segs), dim3(SC_WAVES * 64), 0, stream, s);
+  hipLaunchKernelGGL((scores128<BQ, MT, S>), dim3((unsigned)chunks, (unsigned)segs), dim3(SC_WAVES * 64), 0,
+                     stream, s);
   return hipGetLastError();
 }
 
@@ -612,10 +628,14 @@ static PrepArgs make_prep(const ScoreArgs& a, int slices) {
 
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream) {
   const PrepArgs p = make_prep(a, slices);
-  if (a.rot == TQ_ROT_HADAMARD)
-    hipLaunchKernelGGL(prep_queries128<true>, dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
-  else
-    hipLaunchKernelGGL(prep_queries128<false>, dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
+  const bool had = a.rot == TQ_ROT_HADAMARD;
+  if (slices == 2) {
+    if (had) hipLaunchKernelGGL((prep_queries128<true, 2>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
+    else hipLaunchKernelGGL((prep_queries128<false, 2>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
+  } else {
+    if (had) hipLaunchKernelGGL((prep_queries128<true, 3>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
+    else hipLaunchKernelGGL((prep_queries128<false, 3>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
