@@ -12,9 +12,17 @@ tq_attend).  Three batches rotate so that the decode side reads packed data
 that is not resident in the 256 MB Infinity Cache.  Kernel times come from
 HIP events on the stream the library launches on.
 
+The decode calls are also timed as back-to-back bursts: a spin kernel holds
+the stream while the host queues 12 calls over 12 copies of the packed cache
+(more than the 256 MB memory-side cache), and one pair of events brackets
+the burst, so no host gap or event overhead enters the per-call figure.
+
 Prints one JSON line.  `value` is the packed-KV score bandwidth of tq_scores
-(packed keys read + scores written + queries read, per call, over the call's
-average duration).
+(packed keys read + scores written + queries read, per call, over the
+average call duration of the burst: query prep + score pass).  `roofline`
+is the score-pass kernel alone (keys read + scores written) against HBM
+peak; `large_cache` repeats the score pass on a Llama-3.1-8B-shaped cache
+(436 MB of keys), where launch overheads amortise.
 """
 from __future__ import annotations
 
@@ -35,13 +43,11 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 matrix peak (the encode's instructi
 
 # HBM bytes per launch of the score kernel, read by rocprofv3 (FETCH_SIZE and
 # WRITE_SIZE, each in its own run) and scaled by the factor the same counters
-# give for a plain device copy of known size (bench.py --copy-calibration);
-# valid only for the decode source they were measured on.
-# HBM bytes per score-pass launch from rocprofv3 counters: FETCH_SIZE 16595.5 KiB
-# x 1.99982 (a 256 MiB copy reads as 131084 KiB) + WRITE_SIZE 18432.0 KiB x 1.0
-# (the copy writes 262144 KiB); valid only for the kernel source it was taken on
-SCORE_TRAFFIC = {"tq_decode.hip sha256": "6f93a2014e77ea9534d231734bcfee85a26c7eb654eb27361cc7b5a24b26fc8b",
-                 "bytes_per_launch": 52858841}
+# give for a plain device copy of known size (bench.py --copy-calibration):
+# FETCH_SIZE 16588.0 KiB x 1.99982 (a 256 MiB copy reads as 131083.5 KiB) +
+# WRITE_SIZE 18432.0 KiB x 1.0.  Valid only for the decode source measured.
+SCORE_TRAFFIC = {"tq_decode.hip sha256": "a44fc9a6c545201e0834425ce33ab5f8ee8e4dfbe1cd4078e26a763515fd8036",
+                 "bytes_per_launch": 52843612}
 
 L_, H_, T_, D_ = 36, 2, 8192, 128
 G_ = 8
@@ -73,6 +79,58 @@ def copy_calibration(torch):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4, "copies": 5}), flush=True)
+
+
+def large_cache_scores(torch, tq, pk_, ev):
+    """The score pass on a Llama-3.1-8B-shaped cache: 32 layers x 8 KV heads x
+    32768 tokens (8.4 M keys, 436 MB packed at b = 3, dense rotation), 4 query
+    heads per KV head (134 MB of scores).  One layer of synthetic keys is
+    encoded and its packed records are copied into every layer's slots."""
+    from tq_inputs import gaussian_queries, kv_tensor
+    L, H, T, G = 32, 8, 32768, 4
+    segs = L * H
+    N = segs * T
+    x = torch.from_numpy(kv_tensor(1, H, T, D_, seed=3).reshape(-1, D_)).cuda()
+    one = tq.alloc_cache(tq.key_layout(pk_), H * T, seg_stride=T)
+    tq.encode_prod(pk_, x, one)
+    kc = tq.alloc_cache(tq.key_layout(pk_), N, seg_stride=T)
+    for l in range(L):
+        kc.planes[l * H * T:(l + 1) * H * T].copy_(one.planes)
+        kc.scalars[l * H * T:(l + 1) * H * T].copy_(one.scalars)
+    del x, one
+    q = torch.from_numpy(gaussian_queries(segs * G, D_, seed=3)).cuda()
+    out = torch.empty((segs * G, T), dtype=torch.float32, device="cuda")
+    ws = tq.alloc_workspace(tq.scores_workspace(pk_, segs, G))
+
+    def burst(fn, reps=4):
+        fn()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(2_000_000)
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_call = burst(lambda: tq.scores(pk_, q, segs, G, kc, T, out, ws))
+    tq.scores_prepare(pk_, q, segs, G, ws)
+    t_pass = burst(lambda: tq.scores_prepared(pk_, segs, G, kc, T, out, ws))
+    pass_bytes = N * 52 + segs * G * T * 4
+    call_bytes = pass_bytes + segs * G * D_ * 4
+    del kc, out, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": "llama-3.1-8b-shaped kv cache: 32 layers x 8 kv heads x 32768 tokens x 128; keys prod b=3, "
+                    "dense rotation; 4 query heads per kv head; one launch over all 256 segments",
+        "score_pass_ms": round(t_pass, 5),
+        "score_pass_GBps": round(pass_bytes / (t_pass * 1e-3) / 1e9, 1),
+        "score_pass_frac_hbm_peak": round(pass_bytes / (t_pass * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tq_scores_call_ms": round(t_call, 5),
+        "tq_scores_call_GBps": round(call_bytes / (t_call * 1e-3) / 1e9, 1),
+        "bytes_per_pass": pass_bytes,
+    }
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -125,6 +183,7 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-large", action="store_true", help="skip the Llama-shaped score-pass line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the known-size copy used to scale the traffic counters")
     args = ap.parse_args()
@@ -272,6 +331,8 @@ def main():
                             "note": "algorithmic 2 x 2 d^2 flops per key and 2 d^2 per value; the kernels "
                                     "run fp16 hi/lo MFMA passes (5 per key product pair, 2 per value)"},
     }
+    if not args.skip_large:
+        result["large_cache"] = large_cache_scores(torch, tq, pk_, ev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
