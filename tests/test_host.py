@@ -108,3 +108,25 @@ def test_codebook_order_is_validated():
     p = tq.Params(d=128, bits=3, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=bad)
     p._c.pi, p._c.s = 0x10000, 0x20000
     assert _encode_raw(p) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_balanced_base256_digits_cover_the_weight_range():
+    """The query weights of the integer contractions are split into balanced
+    base-256 digits: q = 65536 hi + 256 mid + lo with hi = (q + 32896) >> 16,
+    mid = (rem + 128) >> 8, lo = rem - 256 mid (three digits, |q| <= 127 * 2^16),
+    and q = 256 hi + lo with hi = (q + 128) >> 8 (two digits, |q| <= 127 * 2^8).
+    Every integer of each range must give int8 digits that recombine exactly."""
+    q = np.arange(-127 * 65536, 127 * 65536 + 1, dtype=np.int64)
+    hi = (q + 32896) >> 16
+    rem = q - 65536 * hi
+    mid = (rem + 128) >> 8
+    lo = rem - 256 * mid
+    for dgt in (hi, mid, lo):
+        assert dgt.min() >= -128 and dgt.max() <= 127
+    assert np.array_equal(65536 * hi + 256 * mid + lo, q)
+    q2 = np.arange(-127 * 256, 127 * 256 + 1, dtype=np.int64)
+    hi2 = (q2 + 128) >> 8
+    lo2 = q2 - 256 * hi2
+    for dgt in (hi2, lo2):
+        assert dgt.min() >= -128 and dgt.max() <= 127
+    assert np.array_equal(256 * hi2 + lo2, q2)
