@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 matrix peak (the encode's instruction)
+INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 matrix peak (the retrieval score GEMM's instruction)
 
 # HBM bytes per launch of the score kernel, read by rocprofv3 (FETCH_SIZE and
 # WRITE_SIZE, each in its own run) and scaled by the factor the same counters
@@ -133,6 +134,73 @@ def large_cache_scores(torch, tq, pk_, ev):
     }
 
 
+def retrieval_line(torch, tq, ev):
+    """Top-10 retrieval: 1,000,000 x 1536 unit vectors from a 64-component
+    Gaussian mixture (synthetic stand-in for an embedding corpus), zero-padded
+    to 2048, sign-flipped Hadamard rotation, TurboQuant-prod at b = 2 and
+    b = 4; 1000 queries from the same mixture.  Times the encode of the whole
+    database and the top-10 call; recall@10 is against exact float32 inner
+    products on the GPU (torch matmul, reference only)."""
+    from tq_inputs import gaussian_matrix, mixture_database, sign_vector
+    N, NQ, K, D, DR = 1_000_000, 1000, 10, 1536, 2048
+    db, qs = mixture_database(N, D, seed=4, n_queries=NQ)
+    x = torch.from_numpy(db).cuda()
+    q = torch.from_numpy(qs).cuda()
+    del db
+    # exact top-10 for recall (float32 GEMM in query chunks)
+    exact = []
+    for i in range(0, NQ, 250):
+        exact.append(torch.topk(q[i:i + 250] @ x.T, K, dim=1).indices)
+    exact = torch.cat(exact).cpu().numpy()
+    eps = torch.from_numpy(sign_vector(DR, 4, 5)).cuda()
+    s = torch.from_numpy(gaussian_matrix(DR, DR, 4, 3)).cuda()
+    out = {"workload": "1,000,000 x 1536 mixture embeddings -> 2048 (hadamard), prod keys, 1000 queries, top-10"}
+    for bits in (2, 4):
+        c, b = tq.build_codebook(DR, bits - 1)
+        p = tq.Params(d=D, d_rot=DR, m=DR, bits=bits, rot=tq.TQ_ROT_HADAMARD, centroids=c, boundaries=b,
+                      eps=eps, s=s)
+        cache = tq.alloc_cache(tq.key_layout(p), N)
+        ws_e = tq.alloc_workspace(tq.encode_workspace(p, N))
+        tq.encode_prod(p, x, cache, ws=ws_e)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        tq.encode_prod(p, x, cache, ws=ws_e)
+        e1.record()
+        torch.cuda.synchronize()
+        t_enc = e0.elapsed_time(e1)
+        del ws_e
+        idx = torch.empty((NQ, K), dtype=torch.int64, device="cuda")
+        val = torch.empty((NQ, K), dtype=torch.float32, device="cuda")
+        ws_t = tq.alloc_workspace(tq.topk_workspace(p, NQ, N, K))
+        tq.scores_topk(p, q, cache, N, K, idx, val, ws_t)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(3):
+            tq.scores_topk(p, q, cache, N, K, idx, val, ws_t)
+        e1.record()
+        torch.cuda.synchronize()
+        t_topk = e0.elapsed_time(e1) / 3
+        got = idx.cpu().numpy()
+        recall = float(np.mean([len(set(a) & set(b)) / K for a, b in zip(got, exact)]))
+        planes = 1 + (bits - 1 if bits - 1 < 3 else 4)          # MSE Walsh planes + the QJL plane
+        digits = 2 if bits - 1 <= 2 else 3
+        int_ops = 2.0 * NQ * N * DR * planes * digits                # int8 MACs x 2 executed by the score GEMM
+        out[f"b{bits}"] = {
+            "encode_ms": round(t_enc, 4), "encoded_vectors_per_s": round(N / (t_enc * 1e-3), 1),
+            "topk_ms": round(t_topk, 4), "query_records_per_s": round(NQ * N / (t_topk * 1e-3), 1),
+            "score_gemm_int8_TOPS_executed": round(int_ops / (t_topk * 1e-3) / 1e12, 1),
+            "frac_int8_mfma_peak": round(int_ops / (t_topk * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+            "recall_at_10_vs_exact": round(recall, 4),
+        }
+        del cache, ws_t, idx, val
+        torch.cuda.empty_cache()
+    del x, q
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (float64 NumPy) on a bounded sample of the same workload."""
     from oracle import estimator as est
@@ -184,6 +252,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-large", action="store_true", help="skip the Llama-shaped score-pass line")
+    ap.add_argument("--skip-retrieval", action="store_true", help="skip the 1M x 1536 top-10 retrieval line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the known-size copy used to scale the traffic counters")
     args = ap.parse_args()
@@ -333,6 +402,10 @@ def main():
     }
     if not args.skip_large:
         result["large_cache"] = large_cache_scores(torch, tq, pk_, ev)
+    if not args.skip_retrieval:
+        del kx, vx, kc, vc
+        torch.cuda.empty_cache()
+        result["retrieval"] = retrieval_line(torch, tq, ev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
