@@ -120,9 +120,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   const int v = lane & 31;
   const int h = lane >> 5;
   const int64_t ntiles = (a.n + VT - 1) / VT;
+  const int64_t stride = (int64_t)gridDim.x * WAVES;
 
-  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles;
-       tile += (int64_t)gridDim.x * WAVES) {
+  // The codebook in VGPRs: as kernel arguments it would hold 32 SGPRs, which
+  // the comparison masks of the quantiser need.
+  Codebook cbv;
+#pragma unroll
+  for (int k = 0; k < (1 << BQ); ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(cbv.c[k]) : "s"(a.cb.c[k]));
+#pragma unroll
+  for (int k = 0; k < (1 << BQ) - 1; ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(cbv.b[k]) : "s"(a.cb.b[k]));
+
+  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
     // The fragment reads below are loop-invariant; without this barrier the
     // compiler hoists all of them (256 registers) out of the loop and spills.
     asm volatile("" ::: "memory");
@@ -225,24 +233,40 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float y = acc[nt][r] * yscale[nt];
+          if (!PROD && vfast) {
+            // The comparison masks are wave ballots of [y >= beta_k] (bit v:
+            // vector v at coordinate 16 mt + r for lanes 0-31, 64 + 16 mt + r
+            // for lanes 32-63).  The index is their count c, a thermometer
+            // code: bit p of c = (sum over j >= 1 of [c >= j 2^p]) mod 2, the
+            // xor of the masks k with k + 1 a multiple of 2^p.  Each plane's
+            // two block words come from scalar xors, written into lane
+            // 16 mt + r.
+            uint64_t ge[(1 << BQ) - 1];
+#pragma unroll
+            for (int k = 0; k < (1 << BQ) - 1; ++k) ge[k] = __ballot(y >= cbv.b[k]);
+#pragma unroll
+            for (int p = 0; p < BQ; ++p) {
+              uint64_t m = 0;
+#pragma unroll
+              for (int k = 0; k < (1 << BQ) - 1; ++k)
+                if (((k + 1) & ((1 << p) - 1)) == 0) m ^= ge[k];
+              const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+              asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(vlo[p]) : "s"(mlo), "i"(16 * mt + r));
+              asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(vhi[p]) : "s"(mhi), "i"(16 * mt + r));
+            }
+            continue;
+          }
           int idx;
           float chat;
-          quantize<BQ>(y, a.cb, idx, chat);
+          quantize<BQ>(y, cbv, idx, chat);
+          // materialise idx here: otherwise the comparison masks stay live
+          // until the bit packing below and spill
+          asm volatile("" : "+v"(idx));
           const int pos = 16 * (mt & 1) + r;
 #pragma unroll
           for (int p = 0; p < BQ; ++p) iw[nt][p][mt >> 1] |= (uint32_t)((idx >> p) & 1) << pos;
           if (!PROD) {
-            if (vfast) {
-              // bit v of the ballot = vector v at coordinate 16 mt + r (lanes
-              // 0-31) or 64 + 16 mt + r (lanes 32-63): two block words
-#pragma unroll
-              for (int p = 0; p < BQ; ++p) {
-                const uint64_t m = __ballot((idx >> p) & 1);
-                const bool here = lane == 16 * mt + r;
-                vlo[p] = here ? (uint32_t)m : vlo[p];
-                vhi[p] = here ? (uint32_t)(m >> 32) : vhi[p];
-              }
-            } else if (vec[nt] < a.n) {
+            if (vec[nt] < a.n) {
               const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
               uint32_t* wp = a.planes + (rec >> 5) * (D * BQ) + (64 * h + 16 * mt + r) * BQ;
               const uint32_t bit = 1u << (rec & 31);
