@@ -692,12 +692,16 @@ namespace {
 // The value sum stays in the rotated domain (Pi_v^T is linear and is applied
 // once per head at the end) and uses the same Walsh form as the keys:
 //   sum_t P'_t c_v[idx_t,j] = sum_S u_S (2 sum_t P'_t x_S,tj - sum_t P'_t),
-// P'_t = p_t n_v,t, a contraction over tokens: A = P' (three base-256 int8
-// digits per head, 24 bits relative to the group maximum, rows 4 h' + digit as
-// for the keys), B = value bits, whose block layout gives each lane one coordinate
-// across 32 tokens in one word.  The constant term uses the same quantised
-// P' as the bit sums, so quantisation errors enter only through the
-// zero-mean centroids.
+// P'_t = p_t n_v,t, a contraction over tokens: A = P' (two base-256 int8
+// digits per head, 16 bits relative to the group maximum: a weight error of
+// 2^-16 moves the output by at most that fraction, unlike a score error,
+// which the exponential amplifies, so the key side keeps three digits), B =
+// value bits, whose block layout gives each lane one coordinate across 32
+// tokens in one word.  One 16-row value tile holds 8 heads: head 4 mt + kg,
+// digit d in row 4 kg + 2 (mt % 2) + d of tile mt / 2, so its results land in
+// the lane group that holds the head's softmax state.  The constant term uses
+// the same quantised P' as the bit sums, so quantisation errors enter only
+// through the zero-mean centroids.
 //
 // Work split: grid (chunks, segments); a workgroup (4 waves) covers `span`
 // tokens of one segment, sized so that the grid is resident at once, and a
@@ -759,10 +763,11 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
   constexpr int PV = BQV;
   constexpr uint32_t VBB = D * PV * 4;        // value bytes per 32-token block
   constexpr int NH = KMT * 4;                 // heads of the 16-row tiles (4 each)
+  constexpr int VMT = (KMT + 1) / 2;          // value-side tiles: 8 heads x 2 digits of P' each
   typedef typename Words<PK>::v kvec;
   typedef typename Words<PV>::v vvec;
   __shared__ float sred[4][NH][PST];
-  __shared__ __align__(16) uint32_t pq[4][KMT][16][32];   // A rows of P', 128 bytes each
+  __shared__ __align__(16) uint32_t pq[4][VMT][16][32];   // A rows of P', 128 bytes each
   __shared__ float vnorm[4][128];
   const int seg = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -784,9 +789,10 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o_st[mt][nt] = 0.f;
   }
-  // slice row 3 of every head stays zero
-#pragma unroll
-  for (int mt = 0; mt < KMT; ++mt) *reinterpret_cast<uint2*>(&pq[wave][mt][4 * kg + 3][2 * t16]) = make_uint2(0u, 0u);
+  // value tile vt holds head 4 mt + kg (mt = 2 vt + j) digit d in row
+  // 4 kg + 2 j + d; the rows of a missing second head (odd KMT) stay zero
+  if constexpr (KMT % 2) *reinterpret_cast<uint4*>(&pq[wave][VMT - 1][4 * kg + 2 + (t16 >> 3)][4 * (t16 & 7)]) =
+      make_uint4(0u, 0u, 0u, 0u);
 
   // key-side fragments and constants (head 4 mt + kg)
   const uint8_t* pack = a.pack + (size_t)seg * pack_bytes(KMT, FK);
@@ -920,28 +926,24 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
         ls += __shfl_xor(ls, o, 64);
         pmax = fmaxf(pmax, __shfl_xor(pmax, o, 64));
       }
-      const float sig = pmax > 0.f ? pmax / QMAX3 : 1.f;
+      const float sig = pmax > 0.f ? pmax / QMAX2 : 1.f;
       const float inv = 1.f / sig;
       int qsum = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        int s0[2], s1[2], s2[2];
+        int s0[2], s1[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int qi = (int)rintf(fminf(pv[2 * c + h] * inv, QMAX3));
-          qsum += qi;                                   // <= 128 * 127 * 2^16 < 2^31
-          s0[h] = (qi + 32896) >> 16;                   // balanced digits, as slices3
-          const int rem = qi - 65536 * s0[h];
-          s1[h] = (rem + 128) >> 8;
-          s2[h] = rem - 256 * s1[h];
+          const int qi = (int)rintf(fminf(pv[2 * c + h] * inv, QMAX2));
+          qsum += qi;                                   // <= 128 * 127 * 2^8
+          s0[h] = (qi + 128) >> 8;                      // balanced digits, as slices2
+          s1[h] = qi - 256 * s0[h];
         }
         const uint32_t d0 = pair_bytes(s0[0], s0[1], bsh);
         const uint32_t d1 = pair_bytes(s1[0], s1[1], bsh);
-        const uint32_t d2 = pair_bytes(s2[0], s2[1], bsh);
         const int dw = 8 * c + dw0;
-        pq[wave][mt][4 * kg][dw] = d0 | row_ror8(d0);
-        pq[wave][mt][4 * kg + 1][dw] = d1 | row_ror8(d1);
-        pq[wave][mt][4 * kg + 2][dw] = d2 | row_ror8(d2);
+        pq[wave][mt / 2][4 * kg + 2 * (mt % 2)][dw] = d0 | row_ror8(d0);
+        pq[wave][mt / 2][4 * kg + 2 * (mt % 2) + 1][dw] = d1 | row_ror8(d1);
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) qsum += __shfl_xor(qsum, o, 64);
@@ -954,20 +956,20 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
     }
 
     // ---- phase 3: A operands (row = lane % 16, token bytes of block kg) ----
-    i32x4 pa[KMT][2];
+    i32x4 pa[VMT][2];
 #pragma unroll
-    for (int mt = 0; mt < KMT; ++mt)
+    for (int vt = 0; vt < VMT; ++vt)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) pa[mt][m] = *reinterpret_cast<const i32x4*>(&pq[wave][mt][t16][8 * kg + 4 * m]);
+      for (int m = 0; m < 2; ++m) pa[vt][m] = *reinterpret_cast<const i32x4*>(&pq[wave][vt][t16][8 * kg + 4 * m]);
 
     // ---- phase 4: value planes, each folded with its Walsh weight ----
 #pragma unroll
     for (int sp = 0; sp < NPV; ++sp) {
-      i32x4 acc[KMT][8];
+      i32x4 acc[VMT][8];
 #pragma unroll
-      for (int mt = 0; mt < KMT; ++mt)
+      for (int vt = 0; vt < VMT; ++vt)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = i32x4{0, 0, 0, 0};
+        for (int nt = 0; nt < 8; ++nt) acc[vt][nt] = i32x4{0, 0, 0, 0};
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         uint32_t word;
@@ -985,15 +987,18 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
         for (int m = 0; m < 2; ++m) {
           const i32x4 bv = {(int)e8[4 * m], (int)e8[4 * m + 1], (int)e8[4 * m + 2], (int)e8[4 * m + 3]};
 #pragma unroll
-          for (int mt = 0; mt < KMT; ++mt) acc[mt][nt] = mfma16x16x64i8(pa[mt][m], bv, acc[mt][nt]);
+          for (int vt = 0; vt < VMT; ++vt) acc[vt][nt] = mfma16x16x64i8(pa[vt][m], bv, acc[vt][nt]);
         }
       }
       const float w2 = 2.f * a.vu[sp];
+      // accumulator register 2 j + d of lane group kg: head 4 (2 vt + j) + kg, digit d
 #pragma unroll
       for (int mt = 0; mt < KMT; ++mt) {
         const float f = w2 * fsig[mt];
+        const int vt = mt / 2, j = mt % 2;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) o_st[mt][nt] = fmaf((float)combine3(acc[mt][nt]), f, o_st[mt][nt]);
+        for (int nt = 0; nt < 8; ++nt)
+          o_st[mt][nt] = fmaf((float)(acc[vt][nt][2 * j] * 256 + acc[vt][nt][2 * j + 1]), f, o_st[mt][nt]);
       }
     }
     load_vals(g + 4);
