@@ -47,7 +47,7 @@ INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 matrix peak (the retrieval score GE
 # give for a plain device copy of known size (bench.py --copy-calibration):
 # FETCH_SIZE 16588.0 KiB x 1.99982 (a 256 MiB copy reads as 131083.5 KiB) +
 # WRITE_SIZE 18432.0 KiB x 1.0.  Valid only for the decode source measured.
-SCORE_TRAFFIC = {"tq_decode.hip sha256": "a44fc9a6c545201e0834425ce33ab5f8ee8e4dfbe1cd4078e26a763515fd8036",
+SCORE_TRAFFIC = {"tq_decode.hip sha256": "14c6d2d23de8ba2791f66519363488f0fa694fc0d0391c4c16e527585ff402eb",
                  "bytes_per_launch": 52843612}
 
 L_, H_, T_, D_ = 36, 2, 8192, 128

@@ -212,26 +212,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
       for (int p = 0; p < BQ; ++p) iw[nt][p][0] = iw[nt][p][1] = 0u;
     }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x16 acc[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const half8 ahi = fpi[frag_index(mt, ks, 0, lane)];
-        const half8 alo = fpi[frag_index(mt, ks, 1, lane)];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          acc[nt] = mfma32x32x16(ahi, xh[nt][ks], acc[nt]);
-          if (!HAD) acc[nt] = mfma32x32x16(alo, xh[nt][ks], acc[nt]);   // +-16 has no lo part
-          if (!F16IN) acc[nt] = mfma32x32x16(ahi, xl[nt][ks], acc[nt]);
-        }
-      }
+    // GEMM1 software-pipelined: the 16 products of row tile mt + 1 are
+    // issued between the epilogue steps of row tile mt
+    auto mma = [&](f32x16* acc, int mt, int ks) {
+      const half8 ahi = fpi[frag_index(mt, ks, 0, lane)];
+      const half8 alo = fpi[frag_index(mt, ks, 1, lane)];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        acc[nt] = mfma32x32x16(ahi, xh[nt][ks], acc[nt]);
+        if (!HAD) acc[nt] = mfma32x32x16(alo, xh[nt][ks], acc[nt]);   // +-16 has no lo part
+        if (!F16IN) acc[nt] = mfma32x32x16(ahi, xl[nt][ks], acc[nt]);
+      }
+    };
+    auto epi = [&](const f32x16* acc, int mt, int nt, int r) {
           const float y = acc[nt][r] * yscale[nt];
           if (!PROD && vfast) {
             // The comparison masks are wave ballots of [y >= beta_k] (bit v:
@@ -254,7 +247,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
               asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(vlo[p]) : "s"(mlo), "i"(16 * mt + r));
               asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(vhi[p]) : "s"(mhi), "i"(16 * mt + r));
             }
-            continue;
+            return;
           }
           int idx;
           float chat;
@@ -286,9 +279,29 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             rh[nt][ks2][r & 7] = hi;
             rl[nt][ks2][r & 7] = lo;
           }
-        }
+    };
+    f32x16 accA[NT], accB[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) accA[nt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) mma(accA, 0, ks);
+#pragma unroll
+    for (int mt = 1; mt < 4; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) accB[nt] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if ((i & 1) == 0) mma(accB, mt, i >> 1);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) epi(accA, mt - 1, nt, i);
       }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) accA[nt] = accB[nt];
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) epi(accA, 3, nt, i);
 
     // ---- GEMM2 (QJL signs) ----
     uint32_t sw[NT][2];

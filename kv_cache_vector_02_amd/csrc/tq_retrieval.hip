@@ -422,10 +422,8 @@ __global__ __launch_bounds__(256) void r_topk(TopkArgs a) {
   }
   const float* vr = a.val + (int64_t)row * a.ld;
   const int64_t* ir = a.idx ? a.idx + (int64_t)row * a.ld : nullptr;
-  for (int64_t e = t; e < a.n; e += 256) {
-    const float v = vr[e];
-    const int64_t i = ir ? ir[e] : a.base + e;
-    if (!better(v, i, bv[KMAX - 1], bi[KMAX - 1])) continue;
+  auto consider = [&](float v, int64_t i) {
+    if (!better(v, i, bv[KMAX - 1], bi[KMAX - 1])) return;
     // insert, keeping bv sorted best first
     float cv = v;
     int64_t ci = i;
@@ -440,7 +438,30 @@ __global__ __launch_bounds__(256) void r_topk(TopkArgs a) {
         ci = ti;
       }
     }
+  };
+  int64_t e0 = 0;
+  if (!ir && (a.ld & 3) == 0) {
+    // a block of scores: 16-byte loads, four per thread in flight (the
+    // result does not depend on the visiting order: ties go by index)
+    const float4* v4 = reinterpret_cast<const float4*>(vr);
+    const int64_t n4 = a.n >> 2;
+    for (int64_t q = t; q < n4; q += 4 * 256) {
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = q + 256 * u < n4 ? v4[q + 256 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (q + 256 * u >= n4) break;
+        const int64_t i0 = a.base + 4 * (q + 256 * u);
+        consider(x[u].x, i0);
+        consider(x[u].y, i0 + 1);
+        consider(x[u].z, i0 + 2);
+        consider(x[u].w, i0 + 3);
+      }
+    }
+    e0 = 4 * n4;
   }
+  for (int64_t e = e0 + t; e < a.n; e += 256) consider(vr[e], ir ? ir[e] : a.base + e);
   int head = 0;
   for (int r = 0; r < a.k; ++r) {
     float hv = -INFINITY;
