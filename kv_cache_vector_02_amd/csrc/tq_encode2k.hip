@@ -152,24 +152,45 @@ __global__ __launch_bounds__(256) void encode2k_signs(Encode2kArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  for (int k0 = 0; k0 < D2; k0 += 16) {
-    half8 Ah[2], Al[2], Bh[2], Bl[2];
+  // operands of k step s + 2 are requested before step s is multiplied:
+  // three register sets in a ring (the loop unrolled by three so that each
+  // set's role is fixed), scheduling barriers keeping every request ahead
+  half8 Ah[3][2], Al[3][2], Bh[3][2], Bl[3][2];
+  auto fetch = [&](int b, int step) {
+    const int k0 = 16 * step;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      Ah[t] = *reinterpret_cast<const half8*>(ah + (int64_t)32 * t * D2 + k0);
-      Al[t] = *reinterpret_cast<const half8*>(al + (int64_t)32 * t * D2 + k0);
-      Bh[t] = *reinterpret_cast<const half8*>(bh + (int64_t)32 * t * D2 + k0);
-      Bl[t] = *reinterpret_cast<const half8*>(bl + (int64_t)32 * t * D2 + k0);
+      Ah[b][t] = *reinterpret_cast<const half8*>(ah + (int64_t)32 * t * D2 + k0);
+      Al[b][t] = *reinterpret_cast<const half8*>(al + (int64_t)32 * t * D2 + k0);
+      Bh[b][t] = *reinterpret_cast<const half8*>(bh + (int64_t)32 * t * D2 + k0);
+      Bl[b][t] = *reinterpret_cast<const half8*>(bl + (int64_t)32 * t * D2 + k0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mma = [&](int b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma32x32x16(Ah[i], Bh[j], acc[i][j]);
-        acc[i][j] = mfma32x32x16(Al[i], Bh[j], acc[i][j]);
-        acc[i][j] = mfma32x32x16(Ah[i], Bl[j], acc[i][j]);
+        acc[i][j] = mfma32x32x16(Ah[b][i], Bh[b][j], acc[i][j]);
+        acc[i][j] = mfma32x32x16(Al[b][i], Bh[b][j], acc[i][j]);
+        acc[i][j] = mfma32x32x16(Ah[b][i], Bl[b][j], acc[i][j]);
       }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int STEPS = D2 / 16;   // 128 = 3 * 42 + 2
+  fetch(0, 0);
+  fetch(1, 1);
+  for (int s0 = 0; s0 + 4 < STEPS; s0 += 3) {
+    fetch(2, s0 + 2);
+    mma(0);
+    fetch(0, s0 + 3);
+    mma(1);
+    fetch(1, s0 + 4);
+    mma(2);
   }
+  mma(0);   // step STEPS - 2
+  mma(1);   // step STEPS - 1
   // signs: ballot over the 32 columns of each accumulator row
 #pragma unroll
   for (int i = 0; i < 2; ++i)
