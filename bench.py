@@ -134,6 +134,87 @@ def large_cache_scores(torch, tq, pk_, ev):
     }
 
 
+def batched_decode_line(torch, tq, pk_, pv_, ev):
+    """One serving step of a batched decode: 64 sequences x 8 KV heads x 8192
+    cached tokens (keys prod b = 3, values mse b = 3), 32 query heads per
+    sequence (GQA 4).  A step encodes each sequence's new token (512 keys and
+    512 values, written at slot 8192 of their segments) and attends over the
+    8193 tokens.  The cache holds one sequence's synthetic keys and values
+    encoded into all 64 sequences' slots (the timing does not depend on the
+    values)."""
+    from tq_inputs import gaussian_queries, kv_tensor
+    B, H, T0, G = 64, 8, 8192, 4
+    segs, stride = B * H, 8224
+    kc = tq.alloc_cache(tq.key_layout(pk_), segs * stride, seg_stride=stride)
+    vc = tq.alloc_value_cache(tq.value_layout(pv_), segs * stride, seg_stride=stride)
+    xk = torch.from_numpy(kv_tensor(1, H, T0, D_, seed=5).reshape(-1, D_)).cuda()
+    xv = torch.from_numpy(kv_tensor(1, H, T0, D_, seed=5, value=True).reshape(-1, D_)).cuda()
+    base = torch.arange(H, device="cuda")[:, None] * stride + torch.arange(T0, device="cuda")[None, :]
+    for b in range(B):
+        sl = (base + b * H * stride).reshape(-1).contiguous()
+        tq.encode_prod(pk_, xk, kc, slot=sl)
+        tq.encode_mse(pv_, xv, vc, slot=sl)
+    del xk, xv
+    # step i appends each sequence's token i at slot T0 + i (fresh records)
+    # and attends over T0 + i + 1 tokens
+    reps = 10
+    seg_base = torch.arange(segs, device="cuda", dtype=torch.int64) * stride
+    new_slots = [seg_base + T0 + i for i in range(reps + 1)]
+    lens = [torch.full((segs,), T0 + i + 1, dtype=torch.int32, device="cuda") for i in range(reps + 1)]
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    xk_new = [torch.randn((segs, D_), generator=gen, device="cuda").half() for _ in range(reps + 1)]
+    xv_new = [torch.randn((segs, D_), generator=gen, device="cuda").half() for _ in range(reps + 1)]
+    q = torch.from_numpy(gaussian_queries(segs * G, D_, seed=5)).cuda()
+    out = torch.empty((segs * G, D_), dtype=torch.float32, device="cuda")
+    ws = tq.alloc_workspace(tq.attend_workspace(pk_, pv_, segs, G, T0 + reps + 1))
+    scale = 1.0 / np.sqrt(D_)
+
+    def step(i):
+        tq.encode_prod(pk_, xk_new[i], kc, slot=new_slots[i])
+        tq.encode_mse(pv_, xv_new[i], vc, slot=new_slots[i])
+        tq.attend(pk_, pv_, q, segs, G, kc, vc, T0 + i + 1, scale, out, ws, length=lens[i])
+
+    step(0)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(2_000_000)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for i in range(1, reps + 1):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps
+    step_bytes = segs * (T0 + 1 + reps // 2) * (52 + 50) + 2 * segs * D_ * 2 + segs * 102 + segs * G * D_ * 8
+    del kc, vc, ws, out
+    torch.cuda.empty_cache()
+    return {
+        "workload": "batched decode: 64 sequences x 8 kv heads x 8192 cached tokens, 32 query heads per sequence "
+                    "(gqa 4); per step encode 512 new keys + 512 new values into fresh slots, attend over 8193..8202 tokens",
+        "step_ms": round(t, 4),
+        "step_GBps": round(step_bytes / (t * 1e-3) / 1e9, 1),
+        "tokens_per_s": round(B / (t * 1e-3), 1),
+        "bytes_per_step": step_bytes,
+    }
+
+
+def copy_rate(torch, ev):
+    """A plain 1 GiB device-to-device copy (torch), for the measured-copy fraction."""
+    a = torch.empty(256 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 5
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * (256 << 20) * 4 / (t * 1e-3) / 1e9
+
+
 def retrieval_line(torch, tq, ev):
     """Top-10 retrieval: 1,000,000 x 1536 unit vectors from a 64-component
     Gaussian mixture (synthetic stand-in for an embedding corpus), zero-padded
@@ -253,6 +334,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-large", action="store_true", help="skip the Llama-shaped score-pass line")
     ap.add_argument("--skip-retrieval", action="store_true", help="skip the 1M x 1536 top-10 retrieval line")
+    ap.add_argument("--skip-batched", action="store_true", help="skip the batched-decode step line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the known-size copy used to scale the traffic counters")
     args = ap.parse_args()
@@ -400,8 +482,15 @@ def main():
                             "note": "algorithmic 2 x 2 d^2 flops per key and 2 d^2 per value; the kernels "
                                     "run fp16 hi/lo MFMA passes (5 per key product pair, 2 per value)"},
     }
+    copy_gbs = copy_rate(torch, ev)
+    result["hbm_copy_GBps_measured"] = round(copy_gbs, 1)
+    result["roofline"]["frac_of_measured_copy"] = round(kernel_gbs / copy_gbs, 4)
     if not args.skip_large:
         result["large_cache"] = large_cache_scores(torch, tq, pk_, ev)
+        result["large_cache"]["score_pass_frac_of_measured_copy"] = round(
+            result["large_cache"]["score_pass_GBps"] / copy_gbs, 4)
+    if not args.skip_batched:
+        result["batched_decode"] = batched_decode_line(torch, tq, pk_, pv_, ev)
     if not args.skip_retrieval:
         del kx, vx, kc, vc
         torch.cuda.empty_cache()

@@ -104,7 +104,9 @@ __device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, 
   }
 }
 
-template <bool PROD, int BQ, bool F16IN, int NT, int WAVES, bool HAD>
+// SLOTS: values written through a slot map (any record order), whose tiles
+// may take the per-bit path; without it only a ragged last tile can.
+template <bool PROD, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS>
 __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   extern __shared__ half8 lds[];
   half8* fpi = lds;
@@ -191,12 +193,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 
     // ---- values: one aligned, fully valid 32-record block per tile? ----
     bool vfast = false;
-    int64_t vblock = 0;
+    int64_t vblock = 0, vrec = 0;
     uint32_t vlo[BQ], vhi[BQ];
     if (!PROD) {
       static_assert(PROD || NT == 1, "value tiles are 32 vectors");
       const int64_t r0 = a.slot ? a.slot[tile * 32 < a.n ? tile * 32 : 0] : tile * 32;
-      const bool mine = vec[0] < a.n && (a.slot ? a.slot[vec[0]] : vec[0]) == r0 + v;
+      // this lane's record, read once (the per-bit path below would otherwise
+      // re-read it after every batch of atomics)
+      vrec = vec[0] < a.n ? (a.slot ? a.slot[vec[0]] : vec[0]) : 0;
+      const bool mine = vec[0] < a.n && vrec == r0 + v;
       vfast = (r0 % 32) == 0 && __all(mine);
       vblock = r0 / 32;
 #pragma unroll
@@ -222,6 +227,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         acc[nt] = mfma32x32x16(ahi, xh[nt][ks], acc[nt]);
         if (!HAD) acc[nt] = mfma32x32x16(alo, xh[nt][ks], acc[nt]);   // +-16 has no lo part
         if (!F16IN) acc[nt] = mfma32x32x16(ahi, xl[nt][ks], acc[nt]);
+      }
+    };
+    // per-bit value path: this lane's current words of the 16 coordinates of
+    // a row tile, read before its epilogue.  Only this lane writes its bit of
+    // a word (records are distinct), so a plain read shows that bit exactly
+    // and only the bits that change need an atomic.
+    uint32_t oldw[SLOTS ? 16 * BQ : 1];
+    auto load_old = [&](int mt) {
+      if (PROD || !SLOTS || vfast || vec[0] >= a.n) return;
+      const uint4* src = reinterpret_cast<const uint4*>(a.planes + (vrec >> 5) * (D * BQ) + (64 * h + 16 * mt) * BQ);
+#pragma unroll
+      for (int q = 0; q < 4 * BQ; ++q) {
+        const uint4 w = src[q];
+        oldw[4 * q] = w.x;
+        oldw[4 * q + 1] = w.y;
+        oldw[4 * q + 2] = w.z;
+        oldw[4 * q + 3] = w.w;
       }
     };
     auto epi = [&](const f32x16* acc, int mt, int nt, int r) {
@@ -260,13 +282,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           for (int p = 0; p < BQ; ++p) iw[nt][p][mt >> 1] |= (uint32_t)((idx >> p) & 1) << pos;
           if (!PROD) {
             if (vec[nt] < a.n) {
-              const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
-              uint32_t* wp = a.planes + (rec >> 5) * (D * BQ) + (64 * h + 16 * mt + r) * BQ;
-              const uint32_t bit = 1u << (rec & 31);
+              // blocks shared with other vectors: an atomic for each bit
+              // that changes (with a slot map), else one per bit
+              uint32_t* wp = a.planes + (vrec >> 5) * (D * BQ) + (64 * h + 16 * mt + r) * BQ;
+              const uint32_t sh = (uint32_t)(vrec & 31);
 #pragma unroll
               for (int p = 0; p < BQ; ++p) {
-                atomicAnd(wp + p, ~bit);
-                if ((idx >> p) & 1) atomicOr(wp + p, bit);
+                const uint32_t nb = (uint32_t)(idx >> p) & 1u;
+                const bool change = SLOTS ? nb != ((oldw[r * BQ + p] >> sh) & 1u) : true;
+                if (change) {
+                  if (nb) atomicOr(wp + p, 1u << sh);
+                  else atomicAnd(wp + p, ~(1u << sh));
+                }
               }
             }
           }
@@ -289,6 +316,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
     for (int mt = 1; mt < 4; ++mt) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) accB[nt] = f32x16{};
+      load_old(mt - 1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if ((i & 1) == 0) mma(accB, mt, i >> 1);
@@ -298,6 +326,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) accA[nt] = accB[nt];
     }
+    load_old(3);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -387,7 +416,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 template <bool PROD, int BQ, bool F16IN, bool HAD>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   constexpr int NT = 1, WAVES = 8;
-  auto kern = encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD>;
+  auto kern = PROD || !a.slot ? encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD, false>
+                              : encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD, !PROD>;
   const size_t lds = (PROD ? 2 : 1) * FRAGS * sizeof(half8);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

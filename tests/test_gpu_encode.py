@@ -121,6 +121,25 @@ def test_value_block_paths(mode):
     compare_encode(st, idx[rest], scal[rest], st.encode_oracle(old[rest]))
 
 
+def test_value_blocks_shared_across_workgroups():
+    # 4096 values whose slots interleave: vector i goes to token i // 128 of
+    # block i % 128, so every 32-token block is written bit by bit by 32
+    # vectors from 32 different wave tiles spread over many workgroups; the
+    # cache is pre-filled, so every bit is either set or cleared concurrently
+    _log("encode values, blocks shared by many workgroups")
+    st = Setup(bits=3, prod=False, seed=11, purpose_pi=4)
+    records = 4096
+    old = kv_tensor(1, 1, records, 128, seed=12, value=True)[0, 0]
+    cache = st.alloc(records)
+    st.encode_gpu(old, cache=cache)
+    x = kv_tensor(1, 1, records, 128, seed=13, value=True)[0, 0]
+    i = np.arange(records)
+    slot = (i % 128) * 32 + i // 128
+    planes, scal = st.encode_gpu(x, slot=slot, cache=cache)
+    idx = value_indices(planes, records)
+    compare_encode(st, idx[slot], scal[slot], st.encode_oracle(x))
+
+
 @pytest.mark.parametrize("prod,bits", [(True, 2), (True, 3), (True, 4), (False, 1), (False, 2), (False, 3),
                                        (False, 4)])
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
