@@ -219,7 +219,8 @@ def retrieval_line(torch, tq, ev):
     """Top-10 retrieval: 1,000,000 x 1536 unit vectors from a 64-component
     Gaussian mixture (synthetic stand-in for an embedding corpus), zero-padded
     to 2048, sign-flipped Hadamard rotation, TurboQuant-prod at b = 2 and
-    b = 4; 1000 queries from the same mixture.  Times the encode of the whole
+    b = 4 and MSE-only records at b = 2 and 4; 1000 queries from the same
+    mixture.  Times the encode of the whole
     database and the top-10 call; recall@10 is against exact float32 inner
     products on the GPU (torch matmul, reference only)."""
     from tq_inputs import gaussian_matrix, mixture_database, sign_vector
@@ -235,18 +236,26 @@ def retrieval_line(torch, tq, ev):
     exact = torch.cat(exact).cpu().numpy()
     eps = torch.from_numpy(sign_vector(DR, 4, 5)).cuda()
     s = torch.from_numpy(gaussian_matrix(DR, DR, 4, 3)).cuda()
-    out = {"workload": "1,000,000 x 1536 mixture embeddings -> 2048 (hadamard), prod keys, 1000 queries, top-10"}
-    for bits in (2, 4):
-        c, b = tq.build_codebook(DR, bits - 1)
+    out = {"workload": "1,000,000 x 1536 mixture embeddings -> 2048 (hadamard), prod keys (b2, b4) and "
+                       "MSE-only records (mse_b2, mse_b4), 1000 queries, top-10"}
+    for prod, bits in ((True, 2), (True, 4), (False, 2), (False, 4)):
+        bq = bits - 1 if prod else bits
+        c, b = tq.build_codebook(DR, bq)
         p = tq.Params(d=D, d_rot=DR, m=DR, bits=bits, rot=tq.TQ_ROT_HADAMARD, centroids=c, boundaries=b,
-                      eps=eps, s=s)
-        cache = tq.alloc_cache(tq.key_layout(p), N)
-        ws_e = tq.alloc_workspace(tq.encode_workspace(p, N))
-        tq.encode_prod(p, x, cache, ws=ws_e)
+                      eps=eps, s=s if prod else None)
+        if prod:
+            cache = tq.alloc_cache(tq.key_layout(p), N)
+            ws_e = tq.alloc_workspace(tq.encode_workspace(p, N))
+            enc = lambda: tq.encode_prod(p, x, cache, ws=ws_e)
+        else:
+            cache = tq.alloc_value_cache(tq.value_layout(p), N)      # per-record layout at d_rot = 2048
+            ws_e = None
+            enc = lambda: tq.encode_mse(p, x, cache)
+        enc()
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
         e0.record()
-        tq.encode_prod(p, x, cache, ws=ws_e)
+        enc()
         e1.record()
         torch.cuda.synchronize()
         t_enc = e0.elapsed_time(e1)
@@ -265,10 +274,10 @@ def retrieval_line(torch, tq, ev):
         t_topk = e0.elapsed_time(e1) / 3
         got = idx.cpu().numpy()
         recall = float(np.mean([len(set(a) & set(b)) / K for a, b in zip(got, exact)]))
-        planes = 1 + (bits - 1 if bits - 1 < 3 else 4)          # MSE Walsh planes + the QJL plane
-        digits = 2 if bits - 1 <= 2 else 3
+        planes = (1 if prod else 0) + {1: 1, 2: 2, 3: 4, 4: 8}[bq]   # MSE Walsh planes (+ the QJL plane)
+        digits = 2 if bq <= 2 else 3
         int_ops = 2.0 * NQ * N * DR * planes * digits                # int8 MACs x 2 executed by the score GEMM
-        out[f"b{bits}"] = {
+        out[("b" if prod else "mse_b") + str(bits)] = {
             "encode_ms": round(t_enc, 4), "encoded_vectors_per_s": round(N / (t_enc * 1e-3), 1),
             "topk_ms": round(t_topk, 4), "query_records_per_s": round(NQ * N / (t_topk * 1e-3), 1),
             "score_gemm_int8_TOPS_executed": round(int_ops / (t_topk * 1e-3) / 1e12, 1),

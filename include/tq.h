@@ -150,7 +150,12 @@ tq_status tq_encode_prod_ws(const tq_params* p, const void* x, tq_dtype dtype, i
  * bits, written in the blocked value layout.  A group of 32 vectors that fills
  * one aligned block (slot NULL, or slots base + 0..31 with base a multiple of
  * 32) is written with whole-word stores; any other record is updated with
- * per-bit atomic clear/set, so partial blocks keep their other records. */
+ * per-bit atomic clear/set, so partial blocks keep their other records.
+ * At d_rot = 2048 with the sign-flipped Hadamard rotation (d a multiple of 8,
+ * d <= 2048) the records instead use the per-record key layout of
+ * tq_key_layout with b planes and one fp16 scalar ||x||_2 per record (no
+ * workspace, one launch, one wave per vector); these are the MSE-only
+ * retrieval records read by tq_scores_topk. */
 tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
                         int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
@@ -209,14 +214,16 @@ size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k);
 
 /* Top-k retrieval by the asymmetric estimator (the estimator of tq_scores) over
  * T prod records 0..T-1 encoded at d_rot = 2048 with the sign-flipped Hadamard
- * rotation (tq_encode_prod_ws), for nq queries:
+ * rotation (tq_encode_prod_ws), for nq queries.  With kp->s == NULL the records
+ * are MSE-only (tq_encode_mse at d_rot = 2048) and the estimate is the MSE
+ * inner product n_t <rot(q), c[idx_t]> (b index bits, b = 1..4):
  *   idx[i][0..k)  record indices of the k largest s(q_i, t), best first,
  *                 ties to the lower index (int64, device)
  *   val[i][0..k)  those estimates (float32, device)
  * q       device f32 [nq][d], d a multiple of 4, zero-padded to 2048
  * keys    record t at keys.planes + t * record words (seg_stride unused)
  * ws      device workspace of tq_scores_topk_workspace() bytes, 256-B aligned
- * Supported: 1 <= k <= 16, T >= k; keys with b = 2, 3 or 4 bits.
+ * Supported: 1 <= k <= 16, T >= k; prod keys with b = 2, 3 or 4 bits.
  * Launches: query transform, projection GEMM and quantisation; per block of
  * 65536 records the bit-plane score GEMM and a per-query top-k; a final merge. */
 tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache keys, int64_t T, int k,

@@ -185,9 +185,12 @@ def alloc_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
 
 def alloc_value_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
     """A value cache: block words int32 [ceil(records/32), d_rot, P] (bit i of word
-    (B, j, p) = bit p of record 32 B + i at coordinate j), scalars float16 [records, 1]."""
+    (B, j, p) = bit p of record 32 B + i at coordinate j), scalars float16 [records, 1].
+    At d_rot = 2048 MSE records keep the per-record key layout [records, 64, P]."""
     import torch
     P, W, S = layout
+    if W == 64:
+        return alloc_cache(layout, records, seg_stride, device)
     return Cache(torch.zeros(((records + 31) // 32, 32 * W, P), dtype=torch.int32, device=device),
                  torch.zeros((records, S), dtype=torch.float16, device=device), seg_stride)
 

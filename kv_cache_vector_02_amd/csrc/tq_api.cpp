@@ -126,8 +126,12 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
     if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
     return hip_status(tq::launch_encode2k(a, ws, s), "encode launch");
   }
+  if (!prod && p->rot == TQ_ROT_HADAMARD && p->d_rot == 2048) {
+    if (p->d % 8) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs d a multiple of 8 (got %d)", p->d);
+    return hip_status(tq::launch_encode2k_mse(a, s), "encode launch");
+  }
   return fail(TQ_ERR_UNSUPPORTED,
-              "encode supports d = d_rot = 128, and prod with the Hadamard rotation at d_rot = 2048 "
+              "encode supports d = d_rot = 128, and the Hadamard rotation at d_rot = 2048 "
               "(got %s, rot %d, d %d, d_rot %d)", prod ? "prod" : "mse", p->rot, p->d, p->d_rot);
 }
 
@@ -181,7 +185,7 @@ tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int6
 
 size_t tq_encode_workspace(const tq_params* p, int64_t n) {
   if (!p || n <= 0) return 0;
-  if (p->d_rot == 2048 && p->rot == TQ_ROT_HADAMARD) return tq::encode2k_workspace(n);
+  if (p->d_rot == 2048 && p->rot == TQ_ROT_HADAMARD && p->s) return tq::encode2k_workspace(n);
   return 0;
 }
 
@@ -345,13 +349,16 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
 
 size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k) {
   if (!kp || nq <= 0 || T <= 0 || k <= 0) return 0;
-  return tq::topk2k_workspace(nq, T, k, kp->bits - 1);
+  const bool qjl = kp->s != nullptr;
+  return tq::topk2k_workspace(nq, T, k, qjl ? kp->bits - 1 : kp->bits, qjl);
 }
 
 tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache keys, int64_t T, int k,
                          int64_t* idx, float* val, void* ws, size_t ws_bytes, void* stream) {
+  // with the QJL matrix s: prod keys; without it: MSE-only records
   tq::Codebook cb;
-  tq_status st = check_params(kp, true, &cb, true);
+  const bool qjl = kp && kp->s;
+  tq_status st = check_params(kp, qjl, &cb, true);
   if (st != TQ_OK) return st;
   if (nq < 0 || T < 0 || k < 1) return fail(TQ_ERR_INVALID_ARG, "need nq >= 0, T >= 0, k >= 1");
   if (nq == 0) return TQ_OK;
@@ -365,19 +372,19 @@ tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache k
   if (!aligned(q, 16) || !aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(ws, 256) ||
       !aligned(idx, 8) || !aligned(val, 4))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
-  const size_t need = tq::topk2k_workspace(nq, T, k, kp->bits - 1);
+  const int bq = index_bits(kp, qjl);
+  const size_t need = tq::topk2k_workspace(nq, T, k, bq, qjl);
   if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
   tq::TopkLaunch L;
   L.q = q;
   L.nq = nq;
   L.d = kp->d;
-  L.bq = kp->bits - 1;
+  L.bq = bq;
+  L.qjl = qjl;
   L.k = k;
   L.eps = kp->eps;
   L.s = kp->s;
-  float u8[8];
-  tq::walsh_coefficients(cb, L.bq, u8, &L.usum);
-  for (int i = 0; i < 4; ++i) L.u[i] = u8[i];
+  tq::walsh_coefficients(cb, L.bq, L.u, &L.usum);
   L.planes = (const uint32_t*)keys.planes;
   L.scalars = (const uint16_t*)keys.scalars;
   L.T = T;

@@ -55,9 +55,12 @@ __device__ __forceinline__ void quantize2k(float y, const Codebook& cb, int& idx
   }
 }
 
-template <int BQ, bool F16IN>
+// PROD: key records (BQ index planes + the QJL plane, written by the
+// projection pass; scalars n and gamma) with the residual to the workspace;
+// otherwise MSE records (BQ planes, scalar n) and nothing else.
+template <int BQ, bool F16IN, bool PROD>
 __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
-  constexpr int P = BQ + 1;
+  constexpr int P = PROD ? BQ + 1 : BQ;
   const int lane = threadIdx.x & 63;
   const int64_t vec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);    // chunk-local
   if (vec >= a.cn) return;
@@ -112,28 +115,36 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
     quantize2k<BQ>(y, a.cb, idx, chat);
 #pragma unroll
     for (int p = 0; p < BQ; ++p) w[p] |= (uint32_t)((idx >> p) & 1) << i;
-    const float r = y - chat;
-    g2 = fmaf(r, r, g2);
-    _Float16 h, l;
-    split_f16(r * R2_SCALE, h, l);
-    rh[i / 8][i % 8] = h;
-    rl[i / 8][i % 8] = l;
+    if (PROD) {
+      const float r = y - chat;
+      g2 = fmaf(r, r, g2);
+      _Float16 h, l;
+      split_f16(r * R2_SCALE, h, l);
+      rh[i / 8][i % 8] = h;
+      rl[i / 8][i % 8] = l;
+    }
   }
+  if (PROD) {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) g2 += shfl_xor_f(g2, o);
-  half8* rhi = reinterpret_cast<half8*>(a.r_hi + vec * D2 + j0);
-  half8* rlo = reinterpret_cast<half8*>(a.r_lo + vec * D2 + j0);
+    for (int o = 1; o < 64; o <<= 1) g2 += shfl_xor_f(g2, o);
+    half8* rhi = reinterpret_cast<half8*>(a.r_hi + vec * D2 + j0);
+    half8* rlo = reinterpret_cast<half8*>(a.r_lo + vec * D2 + j0);
 #pragma unroll
-  for (int q = 0; q < VPL / 8; ++q) {
-    rhi[q] = rh[q];
-    rlo[q] = rl[q];
+    for (int q = 0; q < VPL / 8; ++q) {
+      rhi[q] = rh[q];
+      rlo[q] = rl[q];
+    }
   }
   const int64_t rec = a.slot ? a.slot[gv] : gv;
   uint32_t* dst = a.planes + rec * (P * (D2 / 32)) + lane * P;
 #pragma unroll
   for (int p = 0; p < BQ; ++p) dst[p] = w[p];
-  if (lane == 0)
-    reinterpret_cast<uint32_t*>(a.scalars)[rec] = (uint32_t)f16_bits(n) | ((uint32_t)f16_bits(sqrtf(g2)) << 16);
+  if (lane == 0) {
+    if (PROD)
+      reinterpret_cast<uint32_t*>(a.scalars)[rec] = (uint32_t)f16_bits(n) | ((uint32_t)f16_bits(sqrtf(g2)) << 16);
+    else
+      a.scalars[rec] = f16_bits(n);
+  }
 }
 
 template <int P>
@@ -225,9 +236,9 @@ hipError_t run_chunks(const Encode2kArgs& base, bool f16, hipStream_t stream) {
     a.cn = base.n - v0 < base.chunk ? base.n - v0 : base.chunk;
     const unsigned g1 = (unsigned)((a.cn + 3) / 4);
     if (f16)
-      hipLaunchKernelGGL((encode2k_pass1<BQ, true>), dim3(g1), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((encode2k_pass1<BQ, true, true>), dim3(g1), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((encode2k_pass1<BQ, false>), dim3(g1), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((encode2k_pass1<BQ, false, true>), dim3(g1), dim3(256), 0, stream, a);
     const dim3 g2(D2 / SIGN_TILE, (unsigned)((a.cn + SIGN_TILE - 1) / SIGN_TILE));
     hipLaunchKernelGGL((encode2k_signs<BQ + 1>), g2, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -243,6 +254,38 @@ int64_t encode2k_chunk(int64_t n) { return n < 32768 ? (n + SIGN_TILE - 1) / SIG
 size_t encode2k_workspace(int64_t n) {
   // S hi + lo, then the residual chunk hi + lo, all fp16
   return (size_t)2 * D2 * D2 * sizeof(_Float16) + (size_t)2 * encode2k_chunk(n) * D2 * sizeof(_Float16);
+}
+
+template <int BQ>
+hipError_t run_mse(const Encode2kArgs& a, bool f16, hipStream_t stream) {
+  const unsigned g1 = (unsigned)((a.cn + 3) / 4);
+  if (f16)
+    hipLaunchKernelGGL((encode2k_pass1<BQ, true, false>), dim3(g1), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((encode2k_pass1<BQ, false, false>), dim3(g1), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode2k_mse(const EncodeArgs& e, hipStream_t stream) {
+  Encode2kArgs a = {};
+  a.x = e.x;
+  a.ld_x = e.ld_x;
+  a.d = e.d;
+  a.n = e.n;
+  a.eps = e.eps;
+  a.cb = e.cb;
+  a.planes = e.planes;
+  a.scalars = e.scalars;
+  a.slot = e.slot;
+  a.v0 = 0;
+  a.cn = e.n;
+  switch (e.bq) {
+    case 1: return run_mse<1>(a, e.f16_in, stream);
+    case 2: return run_mse<2>(a, e.f16_in, stream);
+    case 3: return run_mse<3>(a, e.f16_in, stream);
+    case 4: return run_mse<4>(a, e.f16_in, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_encode2k(const EncodeArgs& e, void* ws, hipStream_t stream) {

@@ -59,13 +59,16 @@ size_t encode2k_workspace(int64_t n);
 // index bits (plane order) and their sum.
 void walsh_coefficients(const Codebook& cb, int bq, float u[8], float* usum);
 
-// Top-k retrieval at d_rot = 2048 (Hadamard keys).
+// Top-k retrieval at d_rot = 2048 (Hadamard records): prod keys (qjl = 1,
+// bq = b - 1 index planes + the QJL plane, scalars n and gamma) or MSE-only
+// records (qjl = 0, bq = b planes, scalar n).
 struct TopkLaunch {
   const float* q;          // [nq][d]
   int nq, d, bq, k;
+  int qjl;
   const float* eps;
-  const float* s;
-  float u[4];
+  const float* s;          // prod only
+  float u[8];
   float usum;
   const uint32_t* planes;  // records, key layout with W = 64
   const uint16_t* scalars;
@@ -74,9 +77,11 @@ struct TopkLaunch {
   float* val;              // [nq][k]
   void* ws;
 };
-size_t topk2k_workspace(int nq, int64_t T, int k, int bq);
+size_t topk2k_workspace(int nq, int64_t T, int k, int bq, int qjl);
 hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream);
 hipError_t launch_encode2k(const EncodeArgs& a, void* ws, hipStream_t stream);
+// MSE records at d_rot = 2048 (Hadamard): one pass, no workspace.
+hipError_t launch_encode2k_mse(const EncodeArgs& a, hipStream_t stream);
 
 struct ScoreArgs {
   const float* q;        // [segs*group][d]

@@ -38,8 +38,14 @@ constexpr float RQMAX3 = 8323072.f;      // 127 * 2^16
 constexpr int RTQ = 4;                   // query row tiles per score workgroup
 constexpr int KMAX = 16;                 // largest k
 
-__host__ __device__ constexpr int r_planes(int bq) { return bq == 3 ? 4 : bq; }          // MSE Walsh planes
-__host__ __device__ constexpr int r_frags(int bq) { return 2 * (r_planes(bq) + 1); }      // per chunk per row tile
+__host__ __device__ constexpr int r_planes(int bq) { return bq == 3 ? 4 : bq == 4 ? 8 : bq; }   // MSE Walsh planes
+// Odd subsets of the bq index bits in plane order: single bits, then the
+// parity of 3 bits, or for 4 bits the four three-bit parities.
+__host__ __device__ constexpr int r_subset(int bq, int p) {
+  return p < bq ? 1 << p : bq == 3 ? 7 : (p == 4 ? 7 : p == 5 ? 11 : p == 6 ? 13 : 14);
+}
+// A fragments per chunk per row tile: two per MSE plane, two for the QJL plane
+__host__ __device__ constexpr int r_frags(int bq, int qjl) { return 2 * (r_planes(bq) + qjl); }
 __host__ __device__ constexpr int r_slices(int bq) { return bq <= 2 ? 2 : 3; }
 __host__ __device__ constexpr int r_qpt(int bq) { return bq <= 2 ? 8 : 4; }              // queries per row tile
 
@@ -47,9 +53,10 @@ struct RetrArgs {
   const float* q;          // [nq][ld_q]
   int nq, nqp, d, ld_q;    // nqp: queries padded to whole score workgroups
   int bq;
+  int qjl;                 // 1: prod keys (QJL plane), 0: MSE-only records
   const float* eps;        // [2048]
-  const float* s;          // [2048][2048]
-  float u[4];
+  const float* s;          // [2048][2048], prod only
+  float u[8];
   float usum;
   float kappa;
   // workspace
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
   const int lane = threadIdx.x & 63;
   const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (q >= a.nqp) return;
-  const int np = r_planes(a.bq), F = r_frags(a.bq), S = r_slices(a.bq), qpt = r_qpt(a.bq);
+  const int np = r_planes(a.bq), F = r_frags(a.bq, a.qjl), S = r_slices(a.bq), qpt = r_qpt(a.bq);
   const int R = S == 2 ? 2 : 4;                       // A rows per query
   const bool live = q < a.nq;
   float vr[32], vp[32];
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     vr[i] = live ? a.qrot[(int64_t)q * D2 + 32 * lane + i] : 0.f;
-    vp[i] = live ? a.qproj[(int64_t)q * D2 + 32 * lane + i] : 0.f;
+    vp[i] = live && a.qjl ? a.qproj[(int64_t)q * D2 + 32 * lane + i] : 0.f;
     mx = fmaxf(mx, fabsf(vr[i]));
     px = fmaxf(px, fabsf(vp[i]));
     sr += vr[i];
@@ -230,8 +237,10 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
   }
   const int rt = q / qpt, qq = q % qpt;
   const int c = lane >> 2, kg = lane & 3;
-  for (int p = 0; p <= np; ++p) {
-    const float up = p == 0 ? a.u[0] : p == 1 ? a.u[1] : p == 2 ? a.u[2] : a.u[3];
+  for (int p = 0; p < np + a.qjl; ++p) {
+    float up = a.u[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) up = p == i ? a.u[i] : up;
     const float wsc = p < np ? 2.f * up / sm : 2.f / sq;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -273,10 +282,10 @@ struct ScoreBlockArgs {
   float* scores;             // [nq][rc]
 };
 
-template <int BQ>
+template <int BQ, int QJL>
 __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
-  constexpr int NP = r_planes(BQ), F = r_frags(BQ), S = r_slices(BQ), QPT = r_qpt(BQ);
-  constexpr int P = BQ + 1;
+  constexpr int NP = r_planes(BQ), F = r_frags(BQ, QJL), S = r_slices(BQ), QPT = r_qpt(BQ);
+  constexpr int P = BQ + QJL;
   constexpr int HL = S == 2 ? 2 : 1;            // queries per lane group per row tile
   constexpr int FR = RTQ * F * 64;              // 16-byte fragment units per chunk per workgroup
   constexpr int LPT = FR / 256;                 // of them per thread
@@ -322,20 +331,21 @@ __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
       wn[1] = rec_words(c + 1, 1);
     }
 #pragma unroll
-    for (int p = 0; p <= NP; ++p) {
+    for (int p = 0; p < NP + QJL; ++p) {
       uint32_t e0[8], e1[8];
-      uint32_t x0, x1;
+      uint32_t x0 = 0u, x1 = 0u;
       if (p == NP) {
-        x0 = w0[BQ];
-        x1 = w1[BQ];
-      } else if (p < BQ) {
-        x0 = w0[p];
-        x1 = w1[p];
-      } else {
-        if constexpr (BQ == 3) {
-          x0 = w0[0] ^ w0[1] ^ w0[2];
-          x1 = w1[0] ^ w1[1] ^ w1[2];
+        if constexpr (QJL) {
+          x0 = w0[BQ];
+          x1 = w1[BQ];
         }
+      } else {
+#pragma unroll
+        for (int b = 0; b < BQ; ++b)
+          if (r_subset(BQ, p) >> b & 1) {
+            x0 ^= w0[b];
+            x1 ^= w1[b];
+          }
       }
       expand8r(x0, e0);
       expand8r(x1, e1);
@@ -362,7 +372,7 @@ __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
   for (int ct = 0; ct < 2; ++ct) {
     const int64_t rec = rec0 + 16 * ct + t16;
     if (rec >= a.T || rec >= a.r0 + a.rc) continue;
-    const uint32_t sc = reinterpret_cast<const uint32_t*>(a.scalars)[rec];
+    const uint32_t sc = QJL ? reinterpret_cast<const uint32_t*>(a.scalars)[rec] : (uint32_t)a.scalars[rec];
     const float n = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc & 0xffff));
     const float g = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc >> 16));
 #pragma unroll
@@ -381,8 +391,13 @@ __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
         }
         const float* cq = a.consts + 4 * q;
         const float mse = fmaf(im, cq[0], cq[1]);
-        const float qjl = fmaf(iq, cq[2], cq[3]);
-        a.scores[(int64_t)q * a.rc + (rec - a.r0)] = n * fmaf(g, qjl, mse);
+        if constexpr (QJL) {
+          const float qjl = fmaf(iq, cq[2], cq[3]);
+          a.scores[(int64_t)q * a.rc + (rec - a.r0)] = n * fmaf(g, qjl, mse);
+        } else {
+          (void)iq;
+          a.scores[(int64_t)q * a.rc + (rec - a.r0)] = n * mse;
+        }
       }
     }
   }
@@ -493,10 +508,10 @@ __global__ __launch_bounds__(256) void r_topk(TopkArgs a) {
   }
 }
 
-template <int BQ>
+template <int BQ, int QJL>
 hipError_t score_blocks(const ScoreBlockArgs& b, int nrt, hipStream_t stream) {
   const dim3 grid((unsigned)((b.rc + 127) / 128), (unsigned)((nrt + RTQ - 1) / RTQ));
-  hipLaunchKernelGGL((r_score_block<BQ>), grid, dim3(256), 0, stream, b);
+  hipLaunchKernelGGL((r_score_block<BQ, QJL>), grid, dim3(256), 0, stream, b);
   return hipGetLastError();
 }
 
@@ -510,7 +525,7 @@ static int padded_queries(int nq, int bq) {
   return (nq + per - 1) / per * per;
 }
 
-size_t topk2k_workspace(int nq, int64_t T, int k, int bq) {
+size_t topk2k_workspace(int nq, int64_t T, int k, int bq, int qjl) {
   const int nqp = (padded_queries(nq, bq) + 127) / 128 * 128;
   const int64_t rc = block_records(T);
   const int64_t nch = (T + rc - 1) / rc;
@@ -522,7 +537,7 @@ size_t topk2k_workspace(int nq, int64_t T, int k, int bq) {
   add((size_t)2 * nqp * D2 * 2);             // q hi, lo
   add((size_t)nqp * 4);                      // scale
   add((size_t)nqp * D2 * 4);                 // q_proj
-  add((size_t)nrt * NCH * r_frags(bq) * 1024);   // fragments
+  add((size_t)nrt * NCH * r_frags(bq, qjl) * 1024);   // fragments
   add((size_t)nqp * 16);                     // constants
   add((size_t)nq * rc * 4);                  // score block
   add((size_t)nq * nch * k * 12);            // candidates
@@ -539,9 +554,10 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   a.d = L.d;
   a.ld_q = L.d;
   a.bq = bq;
+  a.qjl = L.qjl;
   a.eps = L.eps;
   a.s = L.s;
-  for (int i = 0; i < 4; ++i) a.u[i] = L.u[i];
+  for (int i = 0; i < 8; ++i) a.u[i] = L.u[i];
   a.usum = L.usum;
   a.kappa = (float)(std::sqrt(M_PI / 2.0) / D2);
   const int64_t rc = block_records(L.T);
@@ -560,16 +576,16 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   a.ql = a.qh + (size_t)a.nqp * D2;
   a.qscale = reinterpret_cast<float*>(take((size_t)a.nqp * 4));
   a.qproj = reinterpret_cast<float*>(take((size_t)a.nqp * D2 * 4));
-  a.pack = take((size_t)nrt * NCH * r_frags(bq) * 1024);
+  a.pack = take((size_t)nrt * NCH * r_frags(bq, L.qjl) * 1024);
   a.consts = reinterpret_cast<float*>(take((size_t)a.nqp * 16));
   float* block = reinterpret_cast<float*>(take((size_t)L.nq * rc * 4));
   uint8_t* cand = take((size_t)L.nq * nch * L.k * 12);
   float* cval = reinterpret_cast<float*>(cand);
   int64_t* cidx = reinterpret_cast<int64_t*>(cand + (size_t)L.nq * nch * L.k * 4);
 
-  hipLaunchKernelGGL(r_split_s, dim3(1024), dim3(256), 0, stream, L.s, a.s_hi, a.s_lo, (int64_t)D2 * D2);
+  if (L.qjl) hipLaunchKernelGGL(r_split_s, dim3(1024), dim3(256), 0, stream, L.s, a.s_hi, a.s_lo, (int64_t)D2 * D2);
   hipLaunchKernelGGL(r_rotate, dim3((unsigned)(a.nqp / 4)), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(r_project, dim3(D2 / 128, (unsigned)(a.nqp / 128)), dim3(256), 0, stream, a);
+  if (L.qjl) hipLaunchKernelGGL(r_project, dim3(D2 / 128, (unsigned)(a.nqp / 128)), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(r_pack, dim3((unsigned)(padded_queries(L.nq, bq) / 4)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -584,10 +600,14 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   b.scores = block;
   for (int64_t ch = 0; ch < nch; ++ch) {
     b.r0 = ch * rc;
-    switch (bq) {
-      case 1: e = score_blocks<1>(b, nrt, stream); break;
-      case 2: e = score_blocks<2>(b, nrt, stream); break;
-      case 3: e = score_blocks<3>(b, nrt, stream); break;
+    switch (bq * 2 + L.qjl) {
+      case 3: e = score_blocks<1, 1>(b, nrt, stream); break;
+      case 5: e = score_blocks<2, 1>(b, nrt, stream); break;
+      case 7: e = score_blocks<3, 1>(b, nrt, stream); break;
+      case 2: e = score_blocks<1, 0>(b, nrt, stream); break;
+      case 4: e = score_blocks<2, 0>(b, nrt, stream); break;
+      case 6: e = score_blocks<3, 0>(b, nrt, stream); break;
+      case 8: e = score_blocks<4, 0>(b, nrt, stream); break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -1,11 +1,15 @@
 """GPU parity of the retrieval configuration: 1536-dimensional unit-norm
 embeddings from a 64-component Gaussian mixture, zero-padded to 2048 and
 rotated by the sign-flipped Hadamard transform, TurboQuant-prod at b = 2 and
-b = 4 (1 and 3 MSE bits + QJL), against the oracle."""
+b = 4 (1 and 3 MSE bits + QJL) and MSE-only records at b = 1..4, against the
+oracle."""
 import numpy as np
 import pytest
 
-from tests.gpu_util import Setup, compare_encode
+import kv_cache_vector_02_amd as tq
+from oracle import estimator as est
+from oracle import packing as pk
+from tests.gpu_util import Setup, compare_encode, torch
 from tq_inputs import mixture_database
 
 pytestmark = pytest.mark.gpu
@@ -15,8 +19,8 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def _setup(bits, seed=4):
-    return Setup(d=1536, d_rot=2048, bits=bits, prod=True, rot="hadamard", seed=seed)
+def _setup(bits, seed=4, prod=True):
+    return Setup(d=1536, d_rot=2048, bits=bits, prod=prod, rot="hadamard", seed=seed)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
@@ -40,10 +44,39 @@ def test_encode_2048_chunks_and_slots():
     _log(f"  {compare_encode(st, planes[slot[rows]], scal[slot[rows]], st.encode_oracle(db[rows]))}")
 
 
-import kv_cache_vector_02_amd as tq                       # noqa: E402
-from oracle import estimator as est                       # noqa: E402
-from oracle import packing as pk                          # noqa: E402
-from tests.gpu_util import torch                          # noqa: E402
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_encode_2048_mse(bits):
+    # MSE-only records: b index planes per 32 coordinates, scalar ||x||
+    _log(f"retrieval MSE encode b{bits}: 3000 x 1536 -> 2048")
+    db, _ = mixture_database(3000, 1536, seed=8)
+    st = _setup(bits, seed=8, prod=False)
+    planes, scal = st.encode_gpu(db)
+    assert planes.shape == (3000, 64, bits)
+    idx = pk.unpack_value(planes, scal, bits)[0]
+    _log(f"  {compare_encode(st, idx, scal, st.encode_oracle(db))}")
+
+
+def test_encode_2048_mse_slots_f16():
+    # float16 input rows with a row stride, records scattered by slot
+    Tt = torch()
+    _log("retrieval MSE encode, f16 strided input, scattered slots")
+    n = 5000
+    db, _ = mixture_database(n, 1536, seed=10)
+    st = _setup(3, seed=10, prod=False)
+    slot = np.random.default_rng(10).permutation(n + 64)[:n]
+    wide = Tt.zeros((n, 1600), dtype=Tt.float16, device="cuda")
+    wide[:, :1536] = Tt.from_numpy(db).cuda().half()
+    x = wide[:, :1536]
+    cache = st.alloc(n + 64)
+    tq.encode_mse(st.params, x, cache, slot=Tt.from_numpy(slot.astype(np.int64)).cuda())
+    Tt.cuda.synchronize()
+    planes = cache.planes.cpu().numpy().view(np.uint32)[slot]
+    scal = cache.scalars.cpu().numpy()[slot]
+    idx = pk.unpack_value(planes, scal, 3)[0]
+    x64 = x.float().cpu().numpy()
+    _log(f"  {compare_encode(st, idx, scal, st.encode_oracle(x64))}")
+
+
 
 REL_TOL = 1e-3
 
@@ -68,6 +101,16 @@ def _oracle_cache(st, x):
     planes, scal = pk.pack_key(code, st.bq)
     cache = tq.Cache(Tt.from_numpy(planes.view(np.int32)).cuda(), Tt.from_numpy(scal).cuda(), 0)
     return cache, (code.idx, code.z, code.n, code.gamma)
+
+
+def _oracle_mse_cache(st, x):
+    """Oracle-encoded MSE-only records -> (device cache, (idx, n))."""
+    Tt = torch()
+    code = st.encode_oracle(x)
+    code.n = code.n.astype(np.float16).astype(np.float64)
+    planes, scal = pk.pack_value(code, st.bq)
+    cache = tq.Cache(Tt.from_numpy(planes.view(np.int32)).cuda(), Tt.from_numpy(scal).cuda(), 0)
+    return cache, (code.idx, code.n)
 
 
 def _check_topk(got_idx, got_val, ref_scores, k):
@@ -95,6 +138,35 @@ def test_topk_exact_small(bits):
     _check_topk(got_idx, got_val, ref, 10)
     ref_top = est.topk(ref, 10)[0]
     _log(f"  index sets equal to the oracle's: {np.mean([set(a) == set(b) for a, b in zip(got_idx, ref_top)]):.3f}")
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_topk_mse_exact_small(bits):
+    # MSE-only records (no QJL matrix in the parameters): the estimate is
+    # n <rot(q), c[idx]>; 20000 records across a ragged tail, 37 queries
+    _log(f"retrieval MSE-only top-10 b{bits}: 20000 records, 37 queries")
+    db, qs = mixture_database(20000, 1536, seed=11, n_queries=37)
+    st = _setup(bits, seed=11, prod=False)
+    cache, (idx, n) = _oracle_mse_cache(st, db)
+    got_idx, got_val = _gpu_topk(st, qs, cache, len(db), 10)
+    ref = est.mse_scores(qs, idx, n, st.rot, st.c32)
+    _check_topk(got_idx, got_val, ref, 10)
+
+
+def test_topk_mse_several_blocks_k16():
+    # GPU-encoded MSE records over three score blocks, checked against the
+    # oracle's estimate from the GPU's own indices and norms (which the encode
+    # tests pin to the oracle's)
+    _log("retrieval MSE-only top-16 over 3 score blocks (GPU encode)")
+    db, qs = mixture_database(140000, 1536, seed=12, n_queries=9)
+    st = _setup(4, seed=12, prod=False)
+    Tt = torch()
+    cache = st.alloc(len(db))
+    tq.encode_mse(st.params, Tt.from_numpy(db).cuda(), cache)
+    got_idx, got_val = _gpu_topk(st, qs, cache, len(db), 16)
+    idx, n = pk.unpack_value(cache.planes.cpu().numpy().view(np.uint32), cache.scalars.cpu().numpy(), 4)
+    ref = est.mse_scores(qs, idx, n, st.rot, st.c32)
+    _check_topk(got_idx, got_val, ref, 16)
 
 
 def test_topk_several_blocks_k16():
