@@ -47,8 +47,8 @@ INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 matrix peak (the retrieval score GE
 # give for a plain device copy of known size (bench.py --copy-calibration):
 # FETCH_SIZE 16588.0 KiB x 1.99982 (a 256 MiB copy reads as 131083.5 KiB) +
 # WRITE_SIZE 18432.0 KiB x 1.0.  Valid only for the decode source measured.
-SCORE_TRAFFIC = {"tq_decode.hip sha256": "14c6d2d23de8ba2791f66519363488f0fa694fc0d0391c4c16e527585ff402eb",
-                 "bytes_per_launch": 52843612}
+SCORE_TRAFFIC = {"tq_decode.hip sha256": "c9092f05fe3e589743b1a257a3baaaada1f307ea9572d38cde33fc9c8f71f2f7",
+                 "bytes_per_launch": 52862042}
 
 L_, H_, T_, D_ = 36, 2, 8192, 128
 G_ = 8

@@ -18,7 +18,9 @@
  *     implement returns TQ_ERR_UNSUPPORTED, and in both cases nothing is
  *     launched.  A failed launch returns TQ_ERR_HIP.  tq_last_error() gives a
  *     thread-local message for the last non-OK status.
- *   - Calls hold no global mutable state and may be made from any thread.
+ *   - Calls may be made from any thread.  The only process-wide state is an
+ *     atomic counter of tq_scores tickets and the tq_debug_set_pack_wait
+ *     bound (an atomic integer); nothing else outlives a call.
  *
  * Packed records (the layout the pages' storage accounting implies: b bits
  * per coordinate of codes, one sign bit per projection row, float16 norms):
@@ -173,8 +175,14 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
  * ws      device workspace of at least tq_scores_workspace() bytes, 256-B
  *         aligned, no initial contents required; it receives each segment's
  *         query pack (rotated and projected query heads quantised to the
- *         matrix-core operand), so one call in flight per workspace.
- * Two launches on the stream: the query pack, then the streaming score pass. */
+ *         matrix-core operand) and two hand-over words per segment, so one
+ *         call in flight per workspace.
+ * One launch on the stream: per segment, the first workgroup builds the query
+ * pack while the others already stream their first keys; they take the pack
+ * when its workgroup signals it (a per-call ticket in the workspace, release
+ * and acquire at device scope), or, if it has not come within a bounded wait
+ * (tq_debug_set_pack_wait), build the same pack themselves.  Each call leaves
+ * the hand-over words cleared, so a captured launch can be replayed. */
 tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
                     const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
                     void* stream);
@@ -188,6 +196,12 @@ tq_status tq_scores_prepare(const tq_params* kp, const float* q, int segs, int g
                             size_t ws_bytes, void* stream);
 tq_status tq_scores_prepared(const tq_params* kp, int segs, int group, tq_cache keys, const int32_t* len,
                              int64_t T, float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* Testing control of tq_scores: the bound, in microseconds, on a workgroup's
+ * wait for its segment's query pack (default 200; process-wide, thread-safe).
+ * 0 makes every workgroup build the pack itself, the path taken when the wait
+ * runs out; results are the same either way. */
+void tq_debug_set_pack_wait(int microseconds);
 
 /* Workspace bytes tq_attend needs. */
 size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T);

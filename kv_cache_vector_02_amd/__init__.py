@@ -26,6 +26,7 @@ EXPORTED = (
     "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
+    "tq_debug_set_pack_wait",
 )
 
 
@@ -87,9 +88,12 @@ def lib():
         L.tq_attend_workspace.argtypes = [P, P, ci, ci, i64]
         L.tq_attend.argtypes = [P, P, vp, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
                                 vp, vp, sz, vp]
+        L.tq_debug_set_pack_wait.restype = None
+        L.tq_debug_set_pack_wait.argtypes = [ci]
         for name in EXPORTED:
             if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace",
-                            "tq_attend_workspace", "tq_encode_workspace", "tq_scores_topk_workspace"):
+                            "tq_attend_workspace", "tq_encode_workspace", "tq_scores_topk_workspace",
+                            "tq_debug_set_pack_wait"):
                 getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -251,6 +255,12 @@ def scores_prepared(kp: Params, segs: int, group: int, keys: Cache, T: int, out,
                     stream=None):
     _check(lib().tq_scores_prepared(kp.c, segs, group, keys.c, _ptr(length), int(T), _ptr(out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def debug_set_pack_wait(microseconds: int):
+    """tq_debug_set_pack_wait: bound on a tq_scores workgroup's wait for its
+    segment's query pack (0: every workgroup builds the pack itself)."""
+    lib().tq_debug_set_pack_wait(int(microseconds))
 
 
 def attend_workspace(kp: Params, vp: Params, segs: int, group: int, T: int) -> int:

@@ -347,6 +347,8 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   return hip_status(tq::launch_attend128(a, (hipStream_t)stream), "attend launch");
 }
 
+void tq_debug_set_pack_wait(int microseconds) { tq::set_pack_wait_us(microseconds); }
+
 size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k) {
   if (!kp || nq <= 0 || T <= 0 || k <= 0) return 0;
   const bool qjl = kp->s != nullptr;

@@ -37,6 +37,7 @@
 // 32 kg .. 32 kg + 31); MFMA m in {0, 1} of a plane takes expansion dwords
 // k = 4m .. 4m+3, dword k byte i being bit 8 i + k of the word.
 #include <atomic>
+#include <chrono>
 #include <cmath>
 
 #include "tq_device.h"
@@ -138,8 +139,10 @@ struct PrepLds {
 };
 
 // Segment seg's query pack -> dst (all 512 threads of the workgroup); S is the
-// number of base-256 digits per weight.
-template <bool HAD, int S>
+// number of base-256 digits per weight; CPOL the cache policy of the pack's
+// stores (the one-launch scores write it device-coherent for the workgroups
+// of other XCDs).
+template <bool HAD, int S, int CPOL = 0>
 __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L, uint8_t* dst) {
   float* qr = L.qr;
   float* qp = L.qp;
@@ -152,31 +155,38 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   const int np = mse_planes(a.bq);
   const int F = 2 * (np + 1);
   const int fbytes = (int)pack_frag_bytes(a.mt, F);
-  const bool live = col < G;
+  const rsrc_t rdst = make_rsrc(dst, (uint32_t)pack_bytes(a.mt, F));
   const int row = 16 * wave + col;        // A-operand row of this lane
+  static_assert(MAXG * 32 == PREP_THREADS, "one float4 of the query heads per thread");
 
-  // ---- every global operand of this lane, in flight together ----
-  float4 qv[8], mv[8], sv[8];
-  const float4* qh = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + (live ? col : 0)) * D);
+  // ---- every global operand in flight together: the segment's query heads
+  // once per workgroup (one float4 per thread, for the LDS), this lane's rows
+  // of Pi and S ----
+  float4 mv[8], sv[8];
+  const int qh = t >> 5, q4 = t & 31;      // head, float4 within the head (16 x 32 = 512 threads)
+  float4 qv = {0.f, 0.f, 0.f, 0.f};
+  if (qh < G) qv = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + qh) * D)[q4];
   const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)(HAD ? 0 : row) * D);
   const float4* srow = reinterpret_cast<const float4*>(a.s + (size_t)row * D);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int k4 = (32 * ks + 8 * kq) / 4;
-    qv[2 * ks] = qh[k4];
-    qv[2 * ks + 1] = qh[k4 + 1];
+    const int k4a = 8 * ks + 2 * kq, k4b = k4a + 1;      // coordinates 32 ks + 8 kq + 0..7
     if (HAD) {
-      mv[2 * ks] = reinterpret_cast<const float4*>(a.eps)[k4];
-      mv[2 * ks + 1] = reinterpret_cast<const float4*>(a.eps)[k4 + 1];
+      mv[2 * ks] = reinterpret_cast<const float4*>(a.eps)[k4a];
+      mv[2 * ks + 1] = reinterpret_cast<const float4*>(a.eps)[k4b];
     } else {
-      mv[2 * ks] = prow[k4];
-      mv[2 * ks + 1] = prow[k4 + 1];
+      mv[2 * ks] = prow[k4a];
+      mv[2 * ks + 1] = prow[k4b];
     }
-    sv[2 * ks] = srow[k4];
-    sv[2 * ks + 1] = srow[k4 + 1];
+    sv[2 * ks] = srow[k4a];
+    sv[2 * ks + 1] = srow[k4b];
   }
   // keep all of them ahead of the first product (one memory round trip)
   __builtin_amdgcn_sched_barrier(0);
+  // the query heads go to the q_proj rows of the LDS (free until the second
+  // product; heads past G are zero)
+  *reinterpret_cast<float4*>(&qp[qh * QTS + 4 * q4]) = qv;
+  __syncthreads();
 
   // ---- q_rot^T = Pi . Q^T, rows 16 wave + 4 kq + r, head col ----
   {
@@ -190,9 +200,8 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
 #pragma unroll
         for (int e = 0; e < 8; ++e) av[e] = (__popc(row & (k0 + e)) & 1) ? -av[e] : av[e];
       }
-      unpack8(qv[2 * ks], qv[2 * ks + 1], bv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bv[e] = live ? bv[e] : 0.f;
+      const float4* qs = reinterpret_cast<const float4*>(&qp[col * QTS + k0]);
+      unpack8(qs[0], qs[1], bv);
       bf16x8 ah, al, bh, bl;
       split8_bf16(av, ah, al);
       split8_bf16(bv, bh, bl);
@@ -308,16 +317,19 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
       d1[k] = pack4(s1[0], s1[1], s1[2], s1[3]);
       d2[k] = pack4(s2[0], s2[1], s2[2], s2[3]);
     }
-    i32x4* row = reinterpret_cast<i32x4*>(dst) + (mt * F + f) * 64 + 16 * kg + R * hl;
-    row[0] = i32x4{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3]};
-    row[1] = i32x4{(int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
+    const uint32_t ro = (uint32_t)(((mt * F + f) * 64 + 16 * kg + R * hl) * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3]}, rdst, ro, 0, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]}, rdst, ro + 16, 0,
+                                           CPOL);
     if constexpr (R == 4) {
-      row[2] = i32x4{(int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3]};
-      row[3] = i32x4{0, 0, 0, 0};
+      __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)d2[0], (int)d2[1], (int)d2[2], (int)d2[3]}, rdst, ro + 32,
+                                             0, CPOL);
+      __builtin_amdgcn_raw_buffer_store_b128(i32x4{0, 0, 0, 0}, rdst, ro + 48, 0, CPOL);
     }
   }
-  float* consts = reinterpret_cast<float*>(dst + fbytes);
-  if (t < a.mt * 16 / R * 4) consts[t] = t < G * 4 ? stat[t >> 2][t & 3] : 0.f;
+  if (t < a.mt * 16 / R * 4)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, t < G * 4 ? stat[t >> 2][t & 3] : 0.f), rdst,
+                                          (uint32_t)(fbytes + 4 * t), 0, CPOL);
 }
 
 // (at most two waves per SIMD: the register budget keeps every operand load
@@ -328,6 +340,48 @@ void prep_queries128(PrepArgs a) {
   __shared__ PrepLds L;
   const int F = 2 * (mse_planes(a.bq) + 1);
   prep_pack<HAD, S>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
+}
+
+// One-launch scores: the first workgroup of each segment builds the query
+// pack while the segment's other workgroups already have their first keys in
+// flight.  Per segment two words in the workspace hand the pack over:
+//   flag  the ticket (a per-call number, odd, from the host) of the launch
+//         whose pack is complete; written by the producer after a release
+//         fence, read by the consumers before an acquire fence
+//   done  (ticket low 32 bits) << 32 | workgroups of that launch past the
+//         flag; the last one clears both words, so a replayed launch (same
+//         ticket) never finds the flag already set
+// A consumer waits a bounded time; if the flag has not come it builds the
+// pack itself (the same bytes as the producer's) and goes on.
+struct ScoreSync {
+  uint64_t flag;
+  uint64_t done;
+};
+
+// Waits at most `ticks` of the 100 MHz constant clock (0: not at all).
+__device__ __forceinline__ bool wait_ticket(uint64_t* flag, uint64_t ticket, long long ticks) {
+  if (ticks <= 0) return false;
+  const long long t0 = wall_clock64();
+  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ticket) {
+    if (wall_clock64() - t0 > ticks) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return true;
+}
+
+// Counts this workgroup past the flag; the last of nwg clears the words.
+__device__ __forceinline__ void sync_done(ScoreSync* s, uint64_t ticket, uint32_t nwg) {
+  const uint64_t tag = ticket << 32;
+  uint64_t v = __hip_atomic_load(&s->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t nv;
+  do {
+    nv = (v >> 32) == (ticket & 0xffffffffull) ? v + 1 : (tag | 1ull);
+  } while (!__hip_atomic_compare_exchange_strong(&s->done, &v, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT));
+  if ((uint32_t)nv == nwg) {
+    __hip_atomic_store(&s->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&s->done, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 struct Score128Args {
@@ -341,6 +395,12 @@ struct Score128Args {
   float kappa;
   float* scores;
   int chunk_tiles;   // 16-token tiles per workgroup
+  // one-launch form only
+  int chunks;        // consumer workgroups per segment
+  PrepArgs prep;     // query side (prep.ws = the packs)
+  ScoreSync* sync;   // [segs]
+  uint64_t ticket;
+  long long wait_ticks;   // consumers' bound on the wait for the pack
 };
 
 __device__ __forceinline__ void expand8(uint32_t w, uint32_t e[8]) {
@@ -348,7 +408,7 @@ __device__ __forceinline__ void expand8(uint32_t w, uint32_t e[8]) {
   for (int k = 0; k < 8; ++k) e[k] = (w >> k) & 0x01010101u;
 }
 
-// Cache policy of the score stores: the sc1 (system-coherence) bit, which
+// Cache policy of the score stores: the sc1 (device-scope coherence) bit, which
 // measured about 5% faster than the default write-back policy for the
 // 19 MB of scores a decode step writes (less left dirty in L2 at kernel end).
 constexpr int CPOL_SC1 = 16;
@@ -378,8 +438,11 @@ __device__ __forceinline__ float mse_digits(i32x4 acc) {
 // tokens of one head (16 bytes) and a store covers whole 128-byte lines.
 constexpr int SC_WAVES = 8;
 
-template <int BQ, int MT, int S>
-__global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
+// FUSED: the one-launch form (1-D grid: segs producers, then segs x chunks
+// consumers); HAD selects the producer's rotation.
+template <int BQ, int MT, int S, bool FUSED, bool HAD>
+__global__ __launch_bounds__(SC_WAVES * 64) __attribute__((amdgpu_waves_per_eu(FUSED && MT == 1 ? 4 : 1)))
+void scores128(Score128Args a) {
   constexpr int NP = mse_planes(BQ);      // MSE planes after the parity plane
   constexpr int F = 2 * (NP + 1);         // MFMAs per tile per 16-row tile
   constexpr int P = BQ + 1;               // stored planes per key record
@@ -389,15 +452,46 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
   constexpr int HL = S == 2 ? 2 : 1;      // heads per lane group per 16-row tile
   constexpr int NH = MT * 4 * HL;         // heads covered by the tiles
   typedef typename Words<P>::v wvec;
-  __shared__ __align__(16) float sbufs[SC_WAVES][NH * SROW];
+  constexpr int SBUF = SC_WAVES * NH * SROW;                    // floats of the output tiles
+  constexpr int PREPF = (int)((sizeof(PrepLds) + 15) / 16 * 4);   // floats of the producer's scratch
+  constexpr int PACKF = (int)(pack_bytes(MT, F) / 4);                  // floats of one query pack
+  constexpr int SMEM0 = FUSED && PREPF > SBUF ? PREPF : SBUF;
+  constexpr int SMEM = FUSED && PACKF > SMEM0 ? PACKF : SMEM0;
+  __shared__ __align__(16) float smem[SMEM + (FUSED ? 4 : 0)];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15;
   const int kg = lane >> 4;
-  const int seg = blockIdx.y;
+  int seg, chunk;
+  if constexpr (FUSED) {
+    const int b = blockIdx.x;
+    if (b < a.prep.segs) {
+      // producer of segment b: the pack with device-coherent stores, every
+      // store complete, then the flag
+      prep_pack<HAD, S, CPOL_SC1>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
+                                  a.prep.ws + (size_t)b * pack_bytes(MT, F));
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        __hip_atomic_store(&a.sync[b].flag, a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        sync_done(&a.sync[b], a.ticket, (uint32_t)a.chunks + 1u);
+      }
+      return;
+    }
+    seg = (b - a.prep.segs) / a.chunks;
+    chunk = (b - a.prep.segs) % a.chunks;
+  } else {
+    seg = blockIdx.y;
+    chunk = blockIdx.x;
+  }
   const int64_t len = a.len ? (int64_t)a.len[seg] : a.T;
-  const int64_t tok0 = (int64_t)blockIdx.x * a.chunk_tiles * 16;
-  if (tok0 >= len) return;
+  const int64_t tok0 = (int64_t)chunk * a.chunk_tiles * 16;
+  if (tok0 >= len) {
+    if constexpr (FUSED)
+      if (threadIdx.x == 0) sync_done(&a.sync[seg], a.ticket, (uint32_t)a.chunks + 1u);
+    return;
+  }
 
   const int64_t rec0 = seg * a.seg_stride + tok0;
   const rsrc_t rk = make_rsrc(a.planes + rec0 * (P * 4), clamp_bytes((a.seg_stride - tok0) * RB));
@@ -423,14 +517,52 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
     }
   };
   const uint8_t* pack = a.ws + (size_t)seg * pack_bytes(MT, F);
+  const int mine = npairs > wave ? (npairs - wave + SC_WAVES - 1) / SC_WAVES : 0;
+  // the first round's keys go out before the pack is read (pairs past the
+  // span read zeros without memory traffic)
+#pragma unroll
+  for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * j);
+  if constexpr (FUSED) {
+    int* got = reinterpret_cast<int*>(smem + SMEM);
+    if (threadIdx.x == 0) {
+      *got = wait_ticket(&a.sync[seg].flag, a.ticket, a.wait_ticks) ? 1 : 0;
+      sync_done(&a.sync[seg], a.ticket, (uint32_t)a.chunks + 1u);
+    }
+    __syncthreads();
+    if (!*got) {
+      // no pack within the wait: build it here (the same bytes the producer
+      // writes), then request the first keys again
+      prep_pack<HAD, S, CPOL_SC1>(a.prep, seg, *reinterpret_cast<PrepLds*>(smem), const_cast<uint8_t*>(pack));
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * j);
+    }
+  }
 
+  // the pack: in the one-launch form it was written in this launch, possibly
+  // through another XCD's L2, so the workgroup reads it once with
+  // device-coherent loads into the LDS and the waves take their fragments
+  // from there; otherwise each wave reads its fragments (L2 hits)
+  const rsrc_t rp = make_rsrc(pack, (uint32_t)pack_bytes(MT, F));
+  const uint8_t* lpack = reinterpret_cast<const uint8_t*>(smem);
+  if constexpr (FUSED) {
+    for (int u = threadIdx.x; u < PACKF / 4; u += SC_WAVES * 64)
+      reinterpret_cast<i32x4*>(smem)[u] =
+          __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(16 * u), 0, CPOL_SC1));
+    __syncthreads();
+  }
   i32x4 afr[MT][F];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int f = 0; f < F; ++f)
-      afr[mt][f] = reinterpret_cast<const i32x4*>(pack)[(mt * F + f) * 64 + lane];
-  const float* consts = reinterpret_cast<const float*>(pack + pack_frag_bytes(MT, F));
+    for (int f = 0; f < F; ++f) {
+      const uint32_t off = (uint32_t)(((mt * F + f) * 64 + lane) * 16);
+      if constexpr (FUSED)
+        afr[mt][f] = *reinterpret_cast<const i32x4*>(lpack + off);
+      else
+        afr[mt][f] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+    }
   // head 4 HL mt + HL kg + hh: sigma_mse, const_mse, kappa sigma_qjl, kappa const_qjl
   float cst[MT][HL][4];
 #pragma unroll
@@ -438,11 +570,18 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
 #pragma unroll
     for (int hh = 0; hh < HL; ++hh) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cst[mt][hh][c] = consts[(4 * HL * mt + HL * kg + hh) * 4 + c];
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t off = (uint32_t)(pack_frag_bytes(MT, F) + ((4 * HL * mt + HL * kg + hh) * 4 + c) * 4);
+        if constexpr (FUSED)
+          cst[mt][hh][c] = *reinterpret_cast<const float*>(lpack + off);
+        else
+          cst[mt][hh][c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, 0));
+      }
       cst[mt][hh][2] *= a.kappa;
       cst[mt][hh][3] *= a.kappa;
     }
-  float* sbuf = sbufs[wave];
+  if constexpr (FUSED) __syncthreads();   // every wave has its fragments: the LDS turns into output tiles
+  float* sbuf = smem + wave * (NH * SROW);
 
   // one 16-token tile -> LDS rows (heads 4 mt + kg), columns col0 + t16
   auto compute = [&](wvec w, uint32_t scl, int col0) {
@@ -513,10 +652,11 @@ __global__ __launch_bounds__(SC_WAVES * 64) void scores128(Score128Args a) {
   // rounds of ROUND pairs per wave, straight-line inside a round: loads run
   // RING pairs ahead and never across a round boundary, so every wait on a
   // slot counts exactly the loads issued after it
-  const int mine = npairs > wave ? (npairs - wave + SC_WAVES - 1) / SC_WAVES : 0;
   for (int r0 = 0; r0 < mine; r0 += ROUND) {
+    if (r0 > 0) {
 #pragma unroll
-    for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * (r0 + j));
+      for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * (r0 + j));
+    }
 #pragma unroll
     for (int j = 0; j < ROUND; ++j) {
       if (r0 + j >= mine) break;
@@ -537,12 +677,27 @@ int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax
 // resident at once; a workgroup's span is a multiple of 8 waves x 32 tokens.
 template <int BQ, int MT, int S>
 hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
-  static const int nb = occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S>), SC_WAVES * 64);
+  static const int nb = occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false>), SC_WAVES * 64);
   const int64_t span = split_span(segs, s.T, nb * device_cus(), 32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   const int64_t chunks = (s.T + span - 1) / span;
-  hipLaunchKernelGGL((scores128<BQ, MT, S>), dim3((unsigned)chunks, (unsigned)segs), dim3(SC_WAVES * 64), 0,
-                     stream, s);
+  hipLaunchKernelGGL((scores128<BQ, MT, S, false, false>), dim3((unsigned)chunks, (unsigned)segs),
+                     dim3(SC_WAVES * 64), 0, stream, s);
+  return hipGetLastError();
+}
+
+// One-launch form: the producers take one resident slot per segment, the
+// consumers split the tokens over the rest.
+template <int BQ, int MT, int S, bool HAD>
+hipError_t launch_scores_fused(Score128Args& s, int segs, hipStream_t stream) {
+  static const int nb =
+      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, true, HAD>), SC_WAVES * 64);
+  const int resident = nb * device_cus() - segs;
+  const int64_t span = split_span(segs, s.T, resident > segs ? resident : segs, 32 * SC_WAVES, (s.T + 255) / 256);
+  s.chunk_tiles = (int)(span / 16);
+  s.chunks = (int)((s.T + span - 1) / span);
+  const int64_t nwg = (int64_t)segs * (s.chunks + 1);
+  hipLaunchKernelGGL((scores128<BQ, MT, S, true, HAD>), dim3((unsigned)nwg), dim3(SC_WAVES * 64), 0, stream, s);
   return hipGetLastError();
 }
 
@@ -603,9 +758,27 @@ int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax
 
 }  // namespace
 
-size_t scores128_workspace(int segs, int group) {
+// Query packs of every segment (sized for the widest key), then the
+// one-launch hand-over words.
+static size_t scores128_pack_region(int segs, int group) {
   const int mt = (group + 3) / 4;
-  return (size_t)segs * pack_bytes(mt, 2 * (mse_planes(3) + 1));   // sized for the widest key
+  return (size_t)segs * pack_bytes(mt, 2 * (mse_planes(3) + 1));
+}
+
+size_t scores128_workspace(int segs, int group) {
+  return scores128_pack_region(segs, group) + ((size_t)segs * sizeof(ScoreSync) + 255) / 256 * 256;
+}
+
+// The consumers' bound on the wait for the pack, in microseconds.
+static std::atomic<int> g_pack_wait_us{200};
+
+void set_pack_wait_us(int us) { g_pack_wait_us.store(us < 0 ? 0 : us, std::memory_order_relaxed); }
+
+// Per-call tickets of the one-launch form: odd (never the cleared value 0),
+// distinct across calls in the process.
+static uint64_t next_ticket() {
+  static std::atomic<uint64_t> t{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2 + 1};
+  return t.fetch_add(2, std::memory_order_relaxed);
 }
 
 // Digits per quantised query weight for the score pass: 2 when the keys carry
@@ -644,20 +817,8 @@ hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t str
   return hipGetLastError();
 }
 
-hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
-  hipError_t e = launch_scores128_prepare(a, stream);
-  if (e != hipSuccess) return e;
-  return launch_scores128_prepared(a, stream);
-}
-
-hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream) {
-  return launch_scores128_prep(a, score_slices(a.bq), stream);
-}
-
-hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream) {
-  const int slices = score_slices(a.bq);
-  const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
-  Score128Args s;
+static Score128Args score_pass_args(const ScoreArgs& a) {
+  Score128Args s = {};
   s.ws = static_cast<const uint8_t*>(a.ws);
   s.planes = a.planes;
   s.scalars = a.scalars;
@@ -668,6 +829,47 @@ hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream) {
   s.kappa = (float)(std::sqrt(M_PI / 2.0) / D);
   s.scores = a.scores;
   s.chunk_tiles = 0;   // set by the launcher
+  return s;
+}
+
+hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
+  const int slices = score_slices(a.bq);
+  const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
+  Score128Args s = score_pass_args(a);
+  s.prep = make_prep(a, slices);
+  s.sync = reinterpret_cast<ScoreSync*>(static_cast<uint8_t*>(a.ws) + scores128_pack_region(a.segs, a.group));
+  s.ticket = next_ticket();
+  s.wait_ticks = 100LL * g_pack_wait_us.load(std::memory_order_relaxed);   // 100 MHz clock
+  const bool had = a.rot == TQ_ROT_HADAMARD;
+  switch (a.bq * 100 + mt * 10 + (had ? 1 : 0)) {
+    case 110: return launch_scores_fused<1, 1, 2, false>(s, a.segs, stream);
+    case 111: return launch_scores_fused<1, 1, 2, true>(s, a.segs, stream);
+    case 120: return launch_scores_fused<1, 2, 2, false>(s, a.segs, stream);
+    case 121: return launch_scores_fused<1, 2, 2, true>(s, a.segs, stream);
+    case 210: return launch_scores_fused<2, 1, 2, false>(s, a.segs, stream);
+    case 211: return launch_scores_fused<2, 1, 2, true>(s, a.segs, stream);
+    case 220: return launch_scores_fused<2, 2, 2, false>(s, a.segs, stream);
+    case 221: return launch_scores_fused<2, 2, 2, true>(s, a.segs, stream);
+    case 310: return launch_scores_fused<3, 1, 3, false>(s, a.segs, stream);
+    case 311: return launch_scores_fused<3, 1, 3, true>(s, a.segs, stream);
+    case 320: return launch_scores_fused<3, 2, 3, false>(s, a.segs, stream);
+    case 321: return launch_scores_fused<3, 2, 3, true>(s, a.segs, stream);
+    case 330: return launch_scores_fused<3, 3, 3, false>(s, a.segs, stream);
+    case 331: return launch_scores_fused<3, 3, 3, true>(s, a.segs, stream);
+    case 340: return launch_scores_fused<3, 4, 3, false>(s, a.segs, stream);
+    case 341: return launch_scores_fused<3, 4, 3, true>(s, a.segs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream) {
+  return launch_scores128_prep(a, score_slices(a.bq), stream);
+}
+
+hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream) {
+  const int slices = score_slices(a.bq);
+  const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
+  Score128Args s = score_pass_args(a);
   switch (a.bq * 10 + mt) {
     case 11: return launch_scores<1, 1, 2>(s, a.segs, stream);
     case 12: return launch_scores<1, 2, 2>(s, a.segs, stream);

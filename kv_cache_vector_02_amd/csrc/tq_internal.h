@@ -106,6 +106,7 @@ hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream);    
 hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream);   // score pass only
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream);
 size_t scores128_workspace(int segs, int group);
+void set_pack_wait_us(int us);   // one-launch scores: consumers' wait bound
 
 struct AttendArgs {
   ScoreArgs k;           // query + key side (scores field unused)

@@ -199,3 +199,89 @@ def test_prepare_then_prepared_equals_scores():
             rows = slice(s * G, (s + 1) * G)
             sl = slice(s * T_, (s + 1) * T_)
             check_rows(got[rows], est.prod_scores(q[rows], idx[sl], z[sl], n[sl], g[sl], st.rot, st.s, st.c32))
+
+
+def _oracle_rows(st, q, fields, segs, G, T_, stride=None):
+    idx, z, n, g = fields
+    stride = stride or T_
+    ref = np.empty((segs * G, T_))
+    for s in range(segs):
+        sl = slice(s * stride, s * stride + T_)
+        ref[s * G:(s + 1) * G] = est.prod_scores(q[s * G:(s + 1) * G], idx[sl], z[sl], n[sl], g[sl],
+                                                 st.rot, st.s, st.c32)
+    return ref
+
+
+def test_one_launch_workspace_reused_across_calls():
+    # one workspace (sized for the largest call) serves calls with new queries
+    # and other segment / group counts in turn: no call may see an earlier
+    # call's query pack or hand-over words
+    _log("scores: one workspace, calls with changing queries and shapes")
+    Tt = torch()
+    T_ = 900
+    st = Setup(bits=3, prod=True, seed=13)
+    x = kv_tensor(1, 6, T_, 128, seed=13)[0].reshape(-1, 128)
+    cache, fields = oracle_key_cache(st, x, seg_stride=T_)
+    ws = tq.alloc_workspace(max(tq.scores_workspace(st.params, s, g) for s, g in ((6, 8), (3, 16), (6, 4))))
+    for i, (segs, G) in enumerate(((6, 8), (6, 8), (3, 16), (6, 4), (6, 8))):
+        q = gaussian_queries(segs * G, 128, seed=100 + i)
+        out = Tt.full((segs * G, T_), float("nan"), dtype=Tt.float32, device="cuda")
+        tq.scores(st.params, Tt.from_numpy(q).cuda(), segs, G, cache, T_, out, ws)
+        Tt.cuda.synchronize()
+        worst = check_rows(out.cpu().numpy(), _oracle_rows(st, q, fields, segs, G, T_))
+        _log(f"  call {i} segs {segs} G {G}: worst rel {worst:.2e}")
+
+
+def test_one_launch_pack_built_by_every_workgroup():
+    # the path a workgroup takes when its wait for the pack runs out: with a
+    # zero wait every workgroup builds the pack itself; the scores are the
+    # same bytes as with the hand-over
+    _log("scores: every workgroup builds its own pack (zero wait)")
+    Tt = torch()
+    segs, T_, G = 5, 3000, 8
+    st = Setup(bits=3, prod=True, seed=14)
+    x = kv_tensor(1, segs, T_, 128, seed=14)[0].reshape(-1, 128)
+    cache, fields = oracle_key_cache(st, x, seg_stride=T_)
+    q = gaussian_queries(segs * G, 128, seed=14)
+    base = gpu_scores(st, q, segs, G, cache, T_)
+    tq.debug_set_pack_wait(0)
+    try:
+        got = gpu_scores(st, q, segs, G, cache, T_)
+        got2 = gpu_scores(st, q, segs, G, cache, T_)
+    finally:
+        tq.debug_set_pack_wait(200)
+    assert np.array_equal(got, base) and np.array_equal(got2, base)
+    check_rows(got, _oracle_rows(st, q, fields, segs, G, T_))
+
+
+def test_one_launch_graph_replays_see_new_queries():
+    # a captured tq_scores replayed with new query values between replays (the
+    # same launch, so the same ticket): each replay must use its own pack
+    _log("scores: graph replays with changing queries")
+    Tt = torch()
+    segs, T_, G = 4, 2000, 8
+    st = Setup(bits=3, prod=True, seed=15)
+    x = kv_tensor(1, segs, T_, 128, seed=15)[0].reshape(-1, 128)
+    cache, fields = oracle_key_cache(st, x, seg_stride=T_)
+    qs = [gaussian_queries(segs * G, 128, seed=200 + i) for i in range(4)]
+    qd = Tt.from_numpy(qs[0]).cuda()
+    out = Tt.zeros((segs * G, T_), dtype=Tt.float32, device="cuda")
+    ws = tq.alloc_workspace(tq.scores_workspace(st.params, segs, G))
+    side = Tt.cuda.Stream()
+    side.wait_stream(Tt.cuda.current_stream())
+    with Tt.cuda.stream(side):            # warm-up outside the capture
+        tq.scores(st.params, qd, segs, G, cache, T_, out, ws)
+    Tt.cuda.current_stream().wait_stream(side)
+    Tt.cuda.synchronize()
+    graph = Tt.cuda.CUDAGraph()
+    with Tt.cuda.graph(graph):
+        tq.scores(st.params, qd, segs, G, cache, T_, out, ws)
+    Tt.cuda.synchronize()
+    for i, q in enumerate(qs):
+        qd.copy_(Tt.from_numpy(q))
+        graph.replay()
+        Tt.cuda.synchronize()
+        got = out.cpu().numpy()
+        eager = gpu_scores(st, q, segs, G, cache, T_)
+        assert np.array_equal(got, eager), f"replay {i} differs from the eager call"
+        check_rows(got, _oracle_rows(st, q, fields, segs, G, T_))
