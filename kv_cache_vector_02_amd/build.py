@@ -30,7 +30,10 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 # decode kernels: matrix-core results straight into VGPRs (no AGPR read-back)
-EXTRA = {"tq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+# encode: the epilogue loops must unroll fully (lane indices and plane bit
+# positions are immediates); the default pragma threshold is below their size
+EXTRA = {"tq_encode.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+         "tq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "tq_retrieval.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -92,6 +92,24 @@ __device__ void build_frags(half8* lds, const float* __restrict__ M, float scale
   }
 }
 
+// Lane mask of [y >= b] (ordered: false for NaN), one v_cmp into an SGPR pair.
+__device__ __forceinline__ uint64_t ge_mask(float y, float b) { return __builtin_amdgcn_fcmpf(y, b, 3); }
+
+// m[lane] ? t : f
+__device__ __forceinline__ float select_mask(uint64_t m, float t, float f) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(f), "v"(t), "s"(m));
+  return r;
+}
+
+// 2 w + m[lane]: one add with the mask as carry-in
+__device__ __forceinline__ uint32_t shift_in(uint32_t w, uint64_t m) {
+  uint32_t r;
+  uint64_t carry;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry) : "v"(w), "s"(m));
+  return r;
+}
+
 template <int BQ>
 __device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, float& chat) {
   idx = 0;
@@ -149,14 +167,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       if (F16IN) {
         const uint4* src = reinterpret_cast<const uint4*>(
             static_cast<const _Float16*>(a.x) + (valid ? vec[nt] : 0) * a.ld_x + 64 * h);
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};   // four chains instead of one 64-long one
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           uint4 w = valid ? src[ks] : make_uint4(0, 0, 0, 0);
           half8 hv = __builtin_bit_cast(half8, w);
           xh[nt][ks] = hv;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s2 += (float)hv[e] * (float)hv[e];
+          for (int e = 0; e < 8; ++e) s4[e & 3] += (float)hv[e] * (float)hv[e];
         }
+        s2 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       } else {
         const float4* src = reinterpret_cast<const float4*>(
             static_cast<const float*>(a.x) + (valid ? vec[nt] : 0) * a.ld_x + 64 * h);
@@ -166,8 +186,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           float4 w = valid ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
           xv[4 * i] = w.x; xv[4 * i + 1] = w.y; xv[4 * i + 2] = w.z; xv[4 * i + 3] = w.w;
         }
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 64; ++i) s2 += xv[i] * xv[i];
+        for (int i = 0; i < 64; ++i) s4[i & 3] += xv[i] * xv[i];
+        s2 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         s2 += shfl_xor_f(s2, 32);
         const float n = sqrtf(s2);
         const float inv = n > 0.f ? U_SCALE / n : 0.f;
@@ -266,20 +288,43 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
               for (int k = 0; k < (1 << BQ) - 1; ++k)
                 if (((k + 1) & ((1 << p) - 1)) == 0) m ^= ge[k];
               const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-              asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(vlo[p]) : "s"(mlo), "i"(16 * mt + r));
-              asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(vhi[p]) : "s"(mhi), "i"(16 * mt + r));
+              // the mask may come straight from a VALU compare (one plane: m
+              // is the comparison itself); a writelane reading an SGPR that a
+              // VALU instruction has just written needs wait states, which the
+              // compiler does not insert in front of inline asm
+              if (p == 0)
+                asm volatile("s_nop 4\n\tv_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %4"
+                             : "+v"(vlo[p]), "+v"(vhi[p])
+                             : "s"(mlo), "s"(mhi), "i"(16 * mt + r));
+              else
+                asm volatile("v_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %4"
+                             : "+v"(vlo[p]), "+v"(vhi[p])
+                             : "s"(mlo), "s"(mhi), "i"(16 * mt + r));
             }
             return;
           }
-          int idx;
-          float chat;
-          quantize<BQ>(y, cbv, idx, chat);
-          // materialise idx here: otherwise the comparison masks stay live
-          // until the bit packing below and spill
-          asm volatile("" : "+v"(idx));
-          const int pos = 16 * (mt & 1) + r;
+          // idx = #{k : y >= beta_k} is a thermometer code, so bit p of idx
+          // is the xor of the comparisons k with k + 1 a multiple of 2^p (the
+          // xors run on the lane masks).  Each plane word takes its bits in
+          // ascending coordinate order as w = 2 w + bit (one carry-in add per
+          // bit) and is bit-reversed once before the store.
+          uint64_t ge[(1 << BQ) - 1];
+          float chat = cbv.c[0];
 #pragma unroll
-          for (int p = 0; p < BQ; ++p) iw[nt][p][mt >> 1] |= (uint32_t)((idx >> p) & 1) << pos;
+          for (int k = 0; k < (1 << BQ) - 1; ++k) {
+            ge[k] = ge_mask(y, cbv.b[k]);
+            chat = select_mask(ge[k], cbv.c[k + 1], chat);
+          }
+          uint64_t bit[BQ];
+#pragma unroll
+          for (int p = 0; p < BQ; ++p) {
+            uint64_t x = 0;
+#pragma unroll
+            for (int k = 0; k < (1 << BQ) - 1; ++k)
+              if (((k + 1) & ((1 << p) - 1)) == 0) x ^= ge[k];
+            bit[p] = x;
+            iw[nt][p][mt >> 1] = shift_in(iw[nt][p][mt >> 1], x);
+          }
           if (!PROD) {
             if (vec[nt] < a.n) {
               // blocks shared with other vectors: an atomic for each bit
@@ -288,7 +333,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
               const uint32_t sh = (uint32_t)(vrec & 31);
 #pragma unroll
               for (int p = 0; p < BQ; ++p) {
-                const uint32_t nb = (uint32_t)(idx >> p) & 1u;
+                const uint32_t nb = (uint32_t)(bit[p] >> lane) & 1u;
                 const bool change = SLOTS ? nb != ((oldw[r * BQ + p] >> sh) & 1u) : true;
                 if (change) {
                   if (nb) atomicOr(wp + p, 1u << sh);
@@ -356,8 +401,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sw[nt][it >> 1] |= (acc[nt][r] >= 0.f ? 1u : 0u) << (16 * (it & 1) + r);
+          for (int r = 0; r < 16; ++r)   // ascending coordinate order, reversed before the store
+            sw[nt][it >> 1] = shift_in(sw[nt][it >> 1], ge_mask(acc[nt][r], 0.f));
         }
       }
     }
@@ -390,12 +435,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         uint32_t out[2 * P];
 #pragma unroll
         for (int p = 0; p < BQ; ++p) {
-          out[p] = iw[nt][p][0];
-          out[P + p] = iw[nt][p][1];
+          out[p] = __builtin_bitreverse32(iw[nt][p][0]);
+          out[P + p] = __builtin_bitreverse32(iw[nt][p][1]);
         }
         if (PROD) {
-          out[BQ] = sw[nt][0];
-          out[P + BQ] = sw[nt][1];
+          out[BQ] = __builtin_bitreverse32(sw[nt][0]);
+          out[P + BQ] = __builtin_bitreverse32(sw[nt][1]);
         }
         uint2* dst = reinterpret_cast<uint2*>(a.planes + rec * (P * 4) + 2 * h * P);
 #pragma unroll
