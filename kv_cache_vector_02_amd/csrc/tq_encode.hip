@@ -157,7 +157,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
     // ---- load 64 coordinates (64 h .. 64 h + 63) of each vector, norms ----
     half8 xh[NT][8];
     half8 xl[NT][8];   // fp32 inputs only
-    float yscale[NT], nrm[NT];
+    // ysc: output scale of GEMM1 (y = ysc acc); inv = 1 / ysc.  A zero vector
+    // (acc = 0) takes ysc = inv = 1, so that y = 0 and r = -c[idx] as defined.
+    float ysc[NT], inv[NT], nrm[NT];
     int64_t vec[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -170,8 +172,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         float s4[4] = {0.f, 0.f, 0.f, 0.f};   // four chains instead of one 64-long one
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          uint4 w = valid ? src[ks] : make_uint4(0, 0, 0, 0);
-          half8 hv = __builtin_bit_cast(half8, w);
+          half8 hv = __builtin_bit_cast(half8, valid ? src[ks] : make_uint4(0, 0, 0, 0));
           xh[nt][ks] = hv;
 #pragma unroll
           for (int e = 0; e < 8; ++e) s4[e & 3] += (float)hv[e] * (float)hv[e];
@@ -192,25 +193,42 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         s2 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         s2 += shfl_xor_f(s2, 32);
         const float n = sqrtf(s2);
-        const float inv = n > 0.f ? U_SCALE / n : 0.f;
+        const float un = n > 0.f ? U_SCALE / n : 0.f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             _Float16 hi, lo;
-            split_f16(xv[8 * ks + e] * inv, hi, lo);
+            split_f16(xv[8 * ks + e] * un, hi, lo);
             xh[nt][ks][e] = hi;
             xl[nt][ks][e] = lo;
           }
         }
         nrm[nt] = n;
-        yscale[nt] = (HAD ? HAD_SCALE : 1.f) / (U_SCALE * PI_SCALE);
+        ysc[nt] = (HAD ? HAD_SCALE : 1.f) / (U_SCALE * PI_SCALE);
+        inv[nt] = (U_SCALE * PI_SCALE) / (HAD ? HAD_SCALE : 1.f);
         continue;
       }
       s2 += shfl_xor_f(s2, 32);
       const float n = sqrtf(s2);
       nrm[nt] = n;
-      yscale[nt] = n > 0.f ? (HAD ? HAD_SCALE : 1.f) / (n * PI_SCALE) : 0.f;
+      ysc[nt] = n > 0.f ? (HAD ? HAD_SCALE : 1.f) / (n * PI_SCALE) : 1.f;
+      inv[nt] = n > 0.f ? (n * PI_SCALE) / (HAD ? HAD_SCALE : 1.f) : 1.f;
+    }
+    // keys: the scale goes into the codebook instead of every coordinate, so
+    // the raw accumulator is compared with beta / ysc and the residual is
+    // ysc (acc - c[idx] / ysc), scaled once in its fp16 split (the decisions
+    // move by a rounding step at most, inside the boundary band)
+    float bsc[NT][(1 << BQ) - 1], csc[NT][1 << BQ], rsc[NT];
+    if (PROD) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int k = 0; k < (1 << BQ) - 1; ++k) bsc[nt][k] = cbv.b[k] * inv[nt];
+#pragma unroll
+        for (int k = 0; k < (1 << BQ); ++k) csc[nt][k] = cbv.c[k] * inv[nt];
+        rsc[nt] = R_SCALE * ysc[nt];
+      }
     }
 
     // ---- values: one aligned, fully valid 32-record block per tile? ----
@@ -269,7 +287,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       }
     };
     auto epi = [&](const f32x16* acc, int mt, int nt, int r) {
-          const float y = acc[nt][r] * yscale[nt];
+          const float y = PROD ? acc[nt][r] : acc[nt][r] * ysc[nt];   // keys: unscaled
           if (!PROD && vfast) {
             // The comparison masks are wave ballots of [y >= beta_k] (bit v:
             // vector v at coordinate 16 mt + r for lanes 0-31, 64 + 16 mt + r
@@ -309,11 +327,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           // ascending coordinate order as w = 2 w + bit (one carry-in add per
           // bit) and is bit-reversed once before the store.
           uint64_t ge[(1 << BQ) - 1];
-          float chat = cbv.c[0];
+          float chat = PROD ? csc[nt][0] : cbv.c[0];
 #pragma unroll
           for (int k = 0; k < (1 << BQ) - 1; ++k) {
-            ge[k] = ge_mask(y, cbv.b[k]);
-            chat = select_mask(ge[k], cbv.c[k + 1], chat);
+            ge[k] = ge_mask(y, PROD ? bsc[nt][k] : cbv.b[k]);
+            chat = select_mask(ge[k], PROD ? csc[nt][k + 1] : cbv.c[k + 1], chat);
           }
           uint64_t bit[BQ];
 #pragma unroll
@@ -343,10 +361,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             }
           }
           if (PROD) {
-            const float res = y - chat;
-            g2[nt] += res * res;
+            const float d = y - chat;      // residual / ysc
+            g2[nt] += d * d;
             _Float16 hi, lo;
-            split_f16(res * R_SCALE, hi, lo);
+            split_f16(d * rsc[nt], hi, lo);
             const int ks2 = 2 * mt + (r >> 3);
             rh[nt][ks2][r & 7] = hi;
             rl[nt][ks2][r & 7] = lo;
@@ -413,7 +431,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       float g = 0.f;
       if (PROD) {
         float t = g2[nt] + shfl_xor_f(g2[nt], 32);
-        g = sqrtf(t);
+        g = sqrtf(t) * ysc[nt];
       }
       if (!PROD) {
         if (vfast) {
