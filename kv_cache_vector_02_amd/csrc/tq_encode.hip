@@ -476,24 +476,36 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   }
 }
 
-template <bool PROD, int BQ, bool F16IN, bool HAD>
-hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
-  constexpr int NT = 1, WAVES = 8;
+template <bool PROD, int BQ, bool F16IN, bool HAD, int WAVES>
+hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
+  constexpr int NT = 1;
   auto kern = PROD || !a.slot ? encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD, false>
                               : encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD, !PROD>;
   const size_t lds = (PROD ? 2 : 1) * FRAGS * sizeof(half8);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  int dev = 0, cus = 256;
-  hipGetDevice(&dev);
-  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t ntiles = (a.n + 32 * NT - 1) / (32 * NT);
   const int64_t want = (ntiles + WAVES - 1) / WAVES;
   const int blocks_per_cu = PROD ? 1 : 2;
   const int grid = (int)std::min<int64_t>(want, (int64_t)cus * blocks_per_cu);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
+}
+
+// Workgroups of 8 waves share one copy of the fragments per compute unit; a
+// small batch (under two tiles per compute unit, e.g. one appended token per
+// sequence) takes one-wave workgroups instead, so that its tiles (and, for
+// values written through a slot map, their per-bit atomics) spread over as
+// many compute units as there are tiles.
+template <bool PROD, int BQ, bool F16IN, bool HAD>
+hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
+  int dev = 0, cus = 256;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t ntiles = (a.n + 31) / 32;
+  if (ntiles < 2 * (int64_t)cus) return launch_waves<PROD, BQ, F16IN, HAD, 1>(a, cus, stream);
+  return launch_waves<PROD, BQ, F16IN, HAD, 8>(a, cus, stream);
 }
 
 template <bool HAD>
