@@ -60,35 +60,50 @@ __device__ __forceinline__ int row_coord(int rho, int mt) {
 
 // M is [128][128] float32 row-major (or, with eps, the matrix H diag(eps)).
 // Fragment (mt, ks) of lane l holds scale * M[row_coord(l % 32, mt)][64 (l / 32)
-// + 8 ks + e], e = 0..7, as hi, lo.
+// + 8 ks + e], e = 0..7, as hi, lo.  NTHR threads build the 2048 fragments,
+// each requesting up to 8 fragments' operands before splitting any of them
+// (a small workgroup would otherwise wait out one memory round trip per
+// fragment).
+template <int NTHR>
 __device__ void build_frags(half8* lds, const float* __restrict__ M, float scale, const float* eps = nullptr) {
-  for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
-    const int lane = f & 63, ks = (f >> 6) & 7, mt = f >> 9;
-    const int row = row_coord(lane & 31, mt);
-    const int k0 = 64 * (lane >> 5) + 8 * ks;
-    float v[8];
-    if (eps) {
-      const float4* src = reinterpret_cast<const float4*>(eps + k0);
-      const float4 p = src[0], q = src[1];
-      const float e8[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  constexpr int TOTAL = 4 * 8 * 64;
+  constexpr int PER = TOTAL / NTHR;
+  constexpr int U = PER < 8 ? PER : 8;
+  static_assert(TOTAL % NTHR == 0 && PER % U == 0, "fragments per thread");
+  for (int b0 = 0; b0 < PER; b0 += U) {
+    float4 p[U], q[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (__popc(row & (k0 + e)) & 1) ? -e8[e] : e8[e];
-    } else {
-      const float4* src = reinterpret_cast<const float4*>(M + row * D + k0);
-      const float4 p = src[0], q = src[1];
-      v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
-      v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+    for (int u = 0; u < U; ++u) {
+      const int f = threadIdx.x + (b0 + u) * NTHR;
+      const int lane = f & 63, ks = (f >> 6) & 7, mt = f >> 9;
+      const int row = row_coord(lane & 31, mt);
+      const int k0 = 64 * (lane >> 5) + 8 * ks;
+      const float4* src = reinterpret_cast<const float4*>(eps ? eps + k0 : M + row * D + k0);
+      p[u] = src[0];
+      q[u] = src[1];
     }
-    half8 hi, lo;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      _Float16 h, l;
-      split_f16(v[e] * scale, h, l);
-      hi[e] = h;
-      lo[e] = l;
+    for (int u = 0; u < U; ++u) {
+      const int f = threadIdx.x + (b0 + u) * NTHR;
+      const int lane = f & 63, ks = (f >> 6) & 7, mt = f >> 9;
+      const int row = row_coord(lane & 31, mt);
+      const int k0 = 64 * (lane >> 5) + 8 * ks;
+      float v[8] = {p[u].x, p[u].y, p[u].z, p[u].w, q[u].x, q[u].y, q[u].z, q[u].w};
+      if (eps) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__popc(row & (k0 + e)) & 1) ? -v[e] : v[e];
+      }
+      half8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        _Float16 h, l;
+        split_f16(v[e] * scale, h, l);
+        hi[e] = h;
+        lo[e] = l;
+      }
+      lds[frag_index(mt, ks, 0, lane)] = hi;
+      lds[frag_index(mt, ks, 1, lane)] = lo;
     }
-    lds[frag_index(mt, ks, 0, lane)] = hi;
-    lds[frag_index(mt, ks, 1, lane)] = lo;
   }
 }
 
@@ -129,8 +144,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   extern __shared__ half8 lds[];
   half8* fpi = lds;
   half8* fs = lds + FRAGS;
-  build_frags(fpi, a.pi, PI_SCALE, HAD ? a.eps : nullptr);
-  if (PROD) build_frags(fs, a.s, 1.f);
+  build_frags<64 * WAVES>(fpi, a.pi, PI_SCALE, HAD ? a.eps : nullptr);
+  if (PROD) build_frags<64 * WAVES>(fs, a.s, 1.f);
   __syncthreads();
 
   constexpr int P = PROD ? BQ + 1 : BQ;     // planes per record
