@@ -275,7 +275,7 @@ def retrieval_line(torch, tq, ev):
         got = idx.cpu().numpy()
         recall = float(np.mean([len(set(a) & set(b)) / K for a, b in zip(got, exact)]))
         planes = (1 if prod else 0) + {1: 1, 2: 2, 3: 4, 4: 8}[bq]   # MSE Walsh planes (+ the QJL plane)
-        digits = 2 if bq <= 2 else 3
+        digits = 2                                                    # base-256 digits per query weight
         int_ops = 2.0 * NQ * N * DR * planes * digits                # int8 MACs x 2 executed by the score GEMM
         out[("b" if prod else "mse_b") + str(bits)] = {
             "encode_ms": round(t_enc, 4), "encoded_vectors_per_s": round(N / (t_enc * 1e-3), 1),

@@ -1,15 +1,19 @@
-// Top-k retrieval over TurboQuant-prod keys at d_rot = 2048 (sign-flipped
-// Hadamard rotation): for each query q, the k records of largest estimated
-// inner product
-//   s(q, t) = n_t ( <Pi q, c[idx_t]> + gamma_t sqrt(pi/2)/m <S Pi q, 2 z_t - 1> )
+// Top-k retrieval at d_rot = 2048 (sign-flipped Hadamard rotation) over
+// TurboQuant-prod keys or MSE-only records: for each query q, the k records of
+// largest estimated inner product
+//   prod:  s(q, t) = n_t ( <Pi q, c[idx_t]> + gamma_t sqrt(pi/2)/m <S Pi q, 2 z_t - 1> )
+//   MSE:   s(q, t) = n_t <Pi q, c[idx_t]>
 // (explainer page, section 8; blog notes, the prod estimator read with the
 // stored ||r||_2), ties to the lower record index.
 //
-// Query side (three launches): the 2048-point Walsh-Hadamard transform per
-// query in registers; q_proj = S q_rot as a 2048 x 2048 fp16 hi/lo MFMA GEMM
-// over all queries; then per query the statistics and the quantised weights,
-// written as int8 A-operand fragments of v_mfma_i32_16x16x64_i8 in balanced
-// base 256 (2 digits, 16 bits, for 1-2 MSE bits; 3 digits, 24 bits, for 3).
+// Query side (three launches, two without the QJL matrix): the 2048-point
+// Walsh-Hadamard transform per query in registers; q_proj = S q_rot as a
+// 2048 x 2048 fp16 hi/lo MFMA GEMM over all queries; then per query the
+// statistics and the quantised weights, written as int8 A-operand fragments
+// of v_mfma_i32_16x16x64_i8 in balanced base 256, two digits (16 bits
+// relative to the query's largest weight; the rounding errors of 2048
+// coordinates average down, and the estimates stay within 1e-3 of the row
+// maximum at every bit width).
 //
 // Record side, per chunk of records (two launches): the bit-plane contraction
 // of the query weights with the records' bits (the same Walsh-plane form as
@@ -17,12 +21,12 @@
 // B operand) writes a score block [queries][records]; then one workgroup per
 // query keeps the block's top k.  A last launch merges the chunks' candidates.
 //
-// Score GEMM tiling: a workgroup (4 waves) holds 4 query row tiles (32 queries
-// at 2 digits, 16 at 3) and 128 records (2 column tiles of 16 per wave); the
-// K loop runs over 16 chunks of 128 coordinates, the query fragments of the
-// next chunk going global -> registers -> LDS while the current chunk is
-// computed.  Consecutive workgroups walk records with the same queries, whose
-// fragments stay in L2.
+// Score GEMM tiling: a workgroup (4 waves) holds 4 query row tiles (32
+// queries) and 128 records (2 column tiles of 16 per wave); the K loop runs
+// over 16 chunks of 128 coordinates, the query fragments of the next chunk
+// going global -> registers -> LDS while the current chunk is computed.
+// Consecutive workgroups walk records with the same queries, whose fragments
+// stay in L2.
 #include <cmath>
 
 #include "tq_device.h"
@@ -34,7 +38,6 @@ namespace {
 constexpr int D2 = 2048;
 constexpr int NCH = D2 / 128;            // 128-coordinate chunks
 constexpr float RQMAX2 = 32512.f;        // 127 * 2^8
-constexpr float RQMAX3 = 8323072.f;      // 127 * 2^16
 constexpr int RTQ = 4;                   // query row tiles per score workgroup
 constexpr int KMAX = 16;                 // largest k
 
@@ -46,8 +49,7 @@ __host__ __device__ constexpr int r_subset(int bq, int p) {
 }
 // A fragments per chunk per row tile: two per MSE plane, two for the QJL plane
 __host__ __device__ constexpr int r_frags(int bq, int qjl) { return 2 * (r_planes(bq) + qjl); }
-__host__ __device__ constexpr int r_slices(int bq) { return bq <= 2 ? 2 : 3; }
-__host__ __device__ constexpr int r_qpt(int bq) { return bq <= 2 ? 8 : 4; }              // queries per row tile
+constexpr int RQPT = 8;                  // queries per row tile (two A rows each)
 
 struct RetrArgs {
   const float* q;          // [nq][ld_q]
@@ -180,19 +182,11 @@ __global__ __launch_bounds__(256) void r_project(RetrArgs a) {
       }
 }
 
-__device__ __forceinline__ void digits(float w, int S, int& d0, int& d1, int& d2) {
-  if (S == 2) {
-    const int qi = (int)rintf(fminf(fmaxf(w, -RQMAX2), RQMAX2));
-    d0 = (qi + 128) >> 8;
-    d1 = qi - 256 * d0;
-    d2 = 0;
-  } else {
-    const int qi = (int)rintf(fminf(fmaxf(w, -RQMAX3), RQMAX3));
-    d0 = (qi + 32896) >> 16;
-    const int rem = qi - 65536 * d0;
-    d1 = (rem + 128) >> 8;
-    d2 = rem - 256 * d1;
-  }
+// integer weight -> balanced base-256 int8 digits: q = 256 d0 + d1
+__device__ __forceinline__ void digits(float w, int& d0, int& d1) {
+  const int qi = (int)rintf(fminf(fmaxf(w, -RQMAX2), RQMAX2));
+  d0 = (qi + 128) >> 8;
+  d1 = qi - 256 * d0;
 }
 
 // One wave per (padded) query: statistics, then the int8 digit fragments.
@@ -203,8 +197,8 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
   const int lane = threadIdx.x & 63;
   const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (q >= a.nqp) return;
-  const int np = r_planes(a.bq), F = r_frags(a.bq, a.qjl), S = r_slices(a.bq), qpt = r_qpt(a.bq);
-  const int R = S == 2 ? 2 : 4;                       // A rows per query
+  const int np = r_planes(a.bq), F = r_frags(a.bq, a.qjl);
+  constexpr int R = 2;                                // A rows (digits) per query
   const bool live = q < a.nq;
   float vr[32], vp[32];
   float mx = 0.f, sr = 0.f, px = 0.f, sp = 0.f;
@@ -226,7 +220,7 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
   }
   float umax = 0.f;
   for (int p = 0; p < np; ++p) umax = fmaxf(umax, fabsf(2.f * a.u[p]));
-  const float qm = S == 2 ? RQMAX2 : RQMAX3;
+  const float qm = RQMAX2;
   const float sm = mx * umax > 0.f ? mx * umax / qm : 1.f;
   const float sq = px > 0.f ? 2.f * px / qm : 1.f;
   if (lane == 0) {
@@ -235,7 +229,7 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
     a.consts[4 * q + 2] = live ? sq * a.kappa : 0.f;
     a.consts[4 * q + 3] = live ? -sp * a.kappa : 0.f;
   }
-  const int rt = q / qpt, qq = q % qpt;
+  const int rt = q / RQPT, qq = q % RQPT;
   const int c = lane >> 2, kg = lane & 3;
   for (int p = 0; p < np + a.qjl; ++p) {
     float up = a.u[0];
@@ -247,18 +241,17 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
       uint8_t* frag = a.pack + ((((int64_t)rt * NCH + c) * F + 2 * p + m) * 64) * 16;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        int dd[3][4];
+        int dd[R][4];
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
           const int b = 8 * ib + 4 * m + k;
           const float w = live ? (p < np ? vr[b] : vp[b]) * wsc : 0.f;
-          digits(w, S, dd[0][ib], dd[1][ib], dd[2][ib]);
+          digits(w, dd[0][ib], dd[1][ib]);
         }
+#pragma unroll
         for (int r = 0; r < R; ++r) {
-          uint32_t word = 0u;
-          if (r < S)
-            word = (uint32_t)(dd[r][0] & 0xff) | ((uint32_t)(dd[r][1] & 0xff) << 8) |
-                   ((uint32_t)(dd[r][2] & 0xff) << 16) | ((uint32_t)(dd[r][3] & 0xff) << 24);
+          const uint32_t word = (uint32_t)(dd[r][0] & 0xff) | ((uint32_t)(dd[r][1] & 0xff) << 8) |
+                                ((uint32_t)(dd[r][2] & 0xff) << 16) | ((uint32_t)(dd[r][3] & 0xff) << 24);
           *reinterpret_cast<uint32_t*>(frag + 16 * (16 * kg + R * qq + r) + 4 * k) = word;
         }
       }
@@ -284,9 +277,9 @@ struct ScoreBlockArgs {
 
 template <int BQ, int QJL>
 __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
-  constexpr int NP = r_planes(BQ), F = r_frags(BQ, QJL), S = r_slices(BQ), QPT = r_qpt(BQ);
+  constexpr int NP = r_planes(BQ), F = r_frags(BQ, QJL), QPT = RQPT;
   constexpr int P = BQ + QJL;
-  constexpr int HL = S == 2 ? 2 : 1;            // queries per lane group per row tile
+  constexpr int HL = 2;                         // queries per lane group per row tile
   constexpr int FR = RTQ * F * 64;              // 16-byte fragment units per chunk per workgroup
   constexpr int LPT = FR / 256;                 // of them per thread
   typedef typename Words<P>::v wvec;
@@ -381,14 +374,9 @@ __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
       for (int hh = 0; hh < HL; ++hh) {
         const int q = (rt0 + r) * QPT + HL * kg + hh;
         if (q >= a.nq) continue;
-        float im, iq;
-        if (S == 2) {
-          im = (float)(am[r][ct][2 * hh] * 256 + am[r][ct][2 * hh + 1]);
-          iq = (float)(aq[r][ct][2 * hh] * 256 + aq[r][ct][2 * hh + 1]);
-        } else {
-          im = fmaf((float)am[r][ct][0], 65536.f, fmaf((float)am[r][ct][1], 256.f, (float)am[r][ct][2]));
-          iq = fmaf((float)aq[r][ct][0], 65536.f, fmaf((float)aq[r][ct][1], 256.f, (float)aq[r][ct][2]));
-        }
+        // int32: |hi digit sum| <= 127 x 2048 x 8 planes, times 256 stays below 2^31
+        const float im = (float)(am[r][ct][2 * hh] * 256 + am[r][ct][2 * hh + 1]);
+        const float iq = (float)(aq[r][ct][2 * hh] * 256 + aq[r][ct][2 * hh + 1]);
         const float* cq = a.consts + 4 * q;
         const float mse = fmaf(im, cq[0], cq[1]);
         if constexpr (QJL) {
@@ -521,7 +509,8 @@ hipError_t score_blocks(const ScoreBlockArgs& b, int nrt, hipStream_t stream) {
 static int64_t block_records(int64_t T) { return T < 65536 ? (T + 127) / 128 * 128 : 65536; }
 
 static int padded_queries(int nq, int bq) {
-  const int per = r_qpt(bq) * RTQ;   // queries per score workgroup
+  (void)bq;
+  const int per = RQPT * RTQ;   // queries per score workgroup
   return (nq + per - 1) / per * per;
 }
 
@@ -529,7 +518,7 @@ size_t topk2k_workspace(int nq, int64_t T, int k, int bq, int qjl) {
   const int nqp = (padded_queries(nq, bq) + 127) / 128 * 128;
   const int64_t rc = block_records(T);
   const int64_t nch = (T + rc - 1) / rc;
-  const int nrt = padded_queries(nq, bq) / r_qpt(bq);
+  const int nrt = padded_queries(nq, bq) / RQPT;
   size_t s = 0;
   auto add = [&](size_t b) { s += (b + 255) / 256 * 256; };
   add((size_t)2 * D2 * D2 * 2);              // S hi, lo
@@ -562,7 +551,7 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   a.kappa = (float)(std::sqrt(M_PI / 2.0) / D2);
   const int64_t rc = block_records(L.T);
   const int64_t nch = (L.T + rc - 1) / rc;
-  const int nrt = padded_queries(L.nq, bq) / r_qpt(bq);
+  const int nrt = padded_queries(L.nq, bq) / RQPT;
   uint8_t* w = static_cast<uint8_t*>(L.ws);
   auto take = [&](size_t b) {
     uint8_t* p = w;
