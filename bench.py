@@ -291,6 +291,48 @@ def retrieval_line(torch, tq, ev):
     return out
 
 
+def quality_report(torch, tq):
+    """Compressed-cache quality at 2, 3 and 4 bits, through the library end to end.
+
+    Synthetic analogs of the "turboquant-pytorch" page's usage patterns and
+    bit-width table: attention fidelity (2048 random unit keys, 100 random unit
+    queries, d = 128, temperature 1), needle trials (20 haystacks of 8192 random
+    unit keys), and the cosine of tq_attend's output to exact attention over
+    decoder-shaped keys and values (4 segments x 2048 tokens, 8 query heads
+    each, temperature 1/sqrt(d)).  Keys prod (b-1 MSE bits + 1 QJL bit, m = d),
+    values MSE at b bits."""
+    from kv_cache_vector_02_amd import quality
+    from tq_inputs import (QUERIES, gaussian_matrix, gaussian_queries, haar_orthogonal, kv_tensor,
+                           needle_haystacks, unit_gaussian)
+
+    def params(bits, prod, seed):
+        c, b = tq.build_codebook(D_, bits - 1 if prod else bits)
+        pi = torch.from_numpy(haar_orthogonal(D_, seed, 2 if prod else 4)).cuda()
+        s = torch.from_numpy(gaussian_matrix(D_, D_, seed, 3)).cuda() if prod else None
+        return tq.Params(d=D_, bits=bits, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b, pi=pi, s=s)
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    keys = dev(unit_gaussian(2048, D_, seed=11))
+    qs = dev(unit_gaussian(100, D_, seed=11, purpose=QUERIES))
+    hay, hq, _ = needle_haystacks(20, 8192, D_, seed=13)
+    hay, hq = dev(hay), dev(hq)
+    xk = dev(kv_tensor(1, 4, 2048, D_, seed=14)[0])
+    xv = dev(kv_tensor(1, 4, 2048, D_, seed=14, value=True)[0])
+    oq = dev(gaussian_queries(32, D_, seed=14))
+    rows = []
+    for bits in (2, 3, 4):
+        kp = params(bits, True, 11)
+        r = quality.attention_fidelity(kp, keys, qs)
+        found, _, _ = quality.needle(params(bits, True, 13), hay, hq)
+        cos, _, _ = quality.output_fidelity(params(bits, True, 14), params(bits, False, 14), xk, xv, oq, 8,
+                                            1.0 / np.sqrt(D_))
+        rows.append({"bits": bits, "attention_cosine": round(r["mean_cosine"], 6),
+                     "top1": round(r["top1_rate"], 3), "needle_found": int(found.sum()), "needle_trials": 20,
+                     "output_cosine": round(float(cos.mean()), 6)})
+    torch.cuda.synchronize()
+    return rows
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (float64 NumPy) on a bounded sample of the same workload."""
     from oracle import estimator as est
@@ -344,6 +386,8 @@ def main():
     ap.add_argument("--skip-large", action="store_true", help="skip the Llama-shaped score-pass line")
     ap.add_argument("--skip-retrieval", action="store_true", help="skip the 1M x 1536 top-10 retrieval line")
     ap.add_argument("--skip-batched", action="store_true", help="skip the batched-decode step line")
+    ap.add_argument("--quality", action="store_true",
+                    help="only print the compressed-cache quality table (fidelity, needle, attention output)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the known-size copy used to scale the traffic counters")
     args = ap.parse_args()
@@ -357,6 +401,10 @@ def main():
     from tq_inputs import gaussian_queries, kv_tensor
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.quality:
+        torch.cuda.set_device(0)
+        print(json.dumps({"quality": quality_report(torch, tq)}), flush=True)
         return
 
     torch.cuda.set_device(0)

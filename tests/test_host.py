@@ -130,3 +130,16 @@ def test_balanced_base256_digits_cover_the_weight_range():
     for dgt in (hi2, lo2):
         assert dgt.min() >= -128 and dgt.max() <= 127
     assert np.array_equal(256 * hi2 + lo2, q2)
+
+
+def test_needle_inputs():
+    # random unit haystacks; the needle sits at its seeded position and is the
+    # exact nearest key of its query at the pages' noise level (0.1)
+    from tq_inputs import needle_haystacks
+    hay, q, pos = needle_haystacks(5, 512, 128, seed=2)
+    assert hay.shape == (5, 512, 128) and q.shape == (5, 128) and pos.shape == (5,)
+    np.testing.assert_allclose(np.linalg.norm(hay, axis=-1), 1.0, atol=1e-6)
+    np.testing.assert_allclose(np.linalg.norm(q, axis=-1), 1.0, atol=1e-6)
+    s = np.einsum("tld,td->tl", hay.astype(np.float64), q.astype(np.float64))
+    assert np.array_equal(s.argmax(1), pos)
+    assert np.all(s[np.arange(5), pos] > 0.5)     # about 1 / sqrt(1 + 0.01 d)

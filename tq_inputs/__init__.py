@@ -29,6 +29,8 @@ MIXTURE_LABELS = 10
 DATA_V = 11
 OUTLIER_CHANNELS_V = 12
 CHANNEL_SCALES_V = 13
+NEEDLE_POSITIONS = 14
+NEEDLE_NOISE = 15
 
 
 def rng(seed: int, purpose: int) -> np.random.Generator:
@@ -62,6 +64,29 @@ def sign_vector(d: int, seed: int, purpose: int = EPS_K) -> np.ndarray:
 
 def gaussian_queries(n: int, d: int, seed: int, purpose: int = QUERIES) -> np.ndarray:
     return np.ascontiguousarray(rng(seed, purpose).standard_normal((n, d)).astype(np.float32))
+
+
+def unit_gaussian(n: int, d: int, seed: int, purpose: int = DATA) -> np.ndarray:
+    """n rows drawn from N(0, I_d) and scaled to unit length, float32 (random unit keys and queries)."""
+    z = rng(seed, purpose).standard_normal((n, d))
+    return np.ascontiguousarray((z / np.linalg.norm(z, axis=1, keepdims=True)).astype(np.float32))
+
+
+def needle_haystacks(trials: int, seq_len: int, d: int, seed: int, noise: float = 0.1):
+    """Needle-in-a-haystack trials: (haystacks [trials, seq_len, d], queries [trials, d], position [trials]).
+
+    Each haystack is seq_len random unit vectors; each query is a random unit
+    vector; at a seeded position per trial the haystack row is replaced by the
+    unit vector along query + noise * N(0, I_d), a key close to the query.
+    """
+    hay = unit_gaussian(trials * seq_len, d, seed, DATA).reshape(trials, seq_len, d)
+    q = unit_gaussian(trials, d, seed, QUERIES)
+    pos = rng(seed, NEEDLE_POSITIONS).integers(0, seq_len, size=trials)
+    nz = rng(seed, NEEDLE_NOISE).standard_normal((trials, d))
+    needle = q.astype(np.float64) + noise * nz
+    needle /= np.linalg.norm(needle, axis=1, keepdims=True)
+    hay[np.arange(trials), pos] = needle.astype(np.float32)
+    return np.ascontiguousarray(hay), q, pos.astype(np.int64)
 
 
 def tiny_vectors(n: int = 4096, d: int = 128, seed: int = 0, n_outliers: int = 4,
