@@ -299,8 +299,9 @@ def quality_report(torch, tq):
     queries, d = 128, temperature 1), needle trials (20 haystacks of 8192 random
     unit keys), and the cosine of tq_attend's output to exact attention over
     decoder-shaped keys and values (4 segments x 2048 tokens, 8 query heads
-    each, temperature 1/sqrt(d)).  Keys prod (b-1 MSE bits + 1 QJL bit, m = d),
-    values MSE at b bits."""
+    each, temperature 1/sqrt(d)).  Keys prod (b-1 MSE bits + 1 QJL bit, m = d)
+    and, for comparison at equal bits, MSE-only (b index bits); values MSE at b
+    bits."""
     from kv_cache_vector_02_amd import quality
     from tq_inputs import (QUERIES, gaussian_matrix, gaussian_queries, haar_orthogonal, kv_tensor,
                            needle_haystacks, unit_gaussian)
@@ -320,15 +321,25 @@ def quality_report(torch, tq):
     xv = dev(kv_tensor(1, 4, 2048, D_, seed=14, value=True)[0])
     oq = dev(gaussian_queries(32, D_, seed=14))
     rows = []
-    for bits in (2, 3, 4):
-        kp = params(bits, True, 11)
-        r = quality.attention_fidelity(kp, keys, qs)
-        found, _, _ = quality.needle(params(bits, True, 13), hay, hq)
-        cos, _, _ = quality.output_fidelity(params(bits, True, 14), params(bits, False, 14), xk, xv, oq, 8,
-                                            1.0 / np.sqrt(D_))
-        rows.append({"bits": bits, "attention_cosine": round(r["mean_cosine"], 6),
-                     "top1": round(r["top1_rate"], 3), "needle_found": int(found.sum()), "needle_trials": 20,
-                     "output_cosine": round(float(cos.mean()), 6)})
+    for keys_kind in ("prod", "mse"):
+        prod = keys_kind == "prod"
+
+        def kparams(bits, seed):
+            # MSE-only keys: b index bits and no QJL matrix, the keys' rotation stream
+            if prod:
+                return params(bits, True, seed)
+            c, b = tq.build_codebook(D_, bits)
+            pi = torch.from_numpy(haar_orthogonal(D_, seed, 2)).cuda()
+            return tq.Params(d=D_, bits=bits, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b, pi=pi)
+
+        for bits in (2, 3, 4):
+            r = quality.attention_fidelity(kparams(bits, 11), keys, qs)
+            found, _, _ = quality.needle(kparams(bits, 13), hay, hq)
+            cos, _, _ = quality.output_fidelity(kparams(bits, 14), params(bits, False, 14), xk, xv, oq, 8,
+                                                1.0 / np.sqrt(D_))
+            rows.append({"keys": keys_kind, "bits": bits, "attention_cosine": round(r["mean_cosine"], 6),
+                         "top1": round(r["top1_rate"], 3), "needle_found": int(found.sum()), "needle_trials": 20,
+                         "output_cosine": round(float(cos.mean()), 6)})
     torch.cuda.synchronize()
     return rows
 

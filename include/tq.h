@@ -33,6 +33,8 @@
  *                           scalars = { float16 n = ||x||, float16 gamma = ||r|| }
  *     value (mse,  b bits)  planes 0 .. b-1 = bit p of the b-bit index;
  *                           scalars = { float16 n }
+ *     MSE-only key (b bits) the value record in the key cache's per-record
+ *                           layout (tq_encode_mse_keys)
  *   A key cache holds the plane words of all records in one array, u32
  *   [records][d_rot/32][P], and the scalars in another, f16
  *   [records][scalars]; record r of segment s is s * seg_stride + t.
@@ -114,7 +116,9 @@ const char* tq_last_error(void);
  * centroids: host double[2^bits] (ascending), boundaries: host double[2^bits-1]. */
 tq_status tq_build_codebook(int d, int bits, double* centroids, double* boundaries);
 
-/* Number of 32-bit plane words and float16 scalars in one record. */
+/* Number of 32-bit plane words and float16 scalars in one record.  For a key
+ * quantizer without a QJL matrix (s == NULL) tq_key_layout describes MSE-only
+ * key records: b planes and one scalar. */
 tq_status tq_key_layout(const tq_params* p, int* planes, int* words_per_plane, int* scalars);
 tq_status tq_value_layout(const tq_params* p, int* planes, int* words_per_plane, int* scalars);
 
@@ -161,6 +165,18 @@ tq_status tq_encode_prod_ws(const tq_params* p, const void* x, tq_dtype dtype, i
 tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
                         int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
+/* TurboQuant-MSE encode of keys (blog notes on the paper, Q_mse: the
+ * quantizer without the QJL stage whose bias that stage removes, explainer
+ * page section 8) into the per-record key layout: b index planes (1 <= b <= 4)
+ * and one float16 n per record, written whole per record (any slot order, no
+ * atomics).  p->s is ignored (NULL by convention: tq_key_layout, tq_scores and
+ * tq_attend read a key quantizer without s as MSE-only).  Arguments as for
+ * tq_encode_prod.  Supported: d = d_rot = 128 (dense or Hadamard), and the
+ * Hadamard rotation at d_rot = 2048, where the records are those of
+ * tq_encode_mse. */
+tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+                             int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
+
 /* Workspace bytes tq_scores needs for segs segments of group query heads. */
 size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
 
@@ -168,6 +184,9 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
  * page section 8; blog notes, the prod estimator read with ||r||_2):
  *   s[h][t] = n_t ( <rot(q_h), c[idx_t]> + gamma_t sqrt(pi/2)/m <S rot(q_h), 2 z_t - 1> )
  * for query head h of segment h / group and token t < len[h / group].
+ * With kp->s == NULL the keys are MSE-only records (tq_encode_mse_keys, b
+ * index bits, b = 1..4) and the estimate is the MSE inner product
+ *   s[h][t] = n_t <rot(q_h), c[idx_t]>    (biased; no QJL term).
  * q       device f32 [segs*group][d]
  * keys    packed prod cache, segment s at records s*seg_stride + t
  * len     device int32 [segs] valid tokens per segment (<= T), or NULL for T
@@ -218,7 +237,9 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
  * Other arguments as for tq_scores (ws: tq_attend_workspace() bytes).  Three
  * launches: the query pack, the streaming pass (one log-sum-exp partial per
  * workgroup) and the per-segment merge with the inverse value rotation.
- * Supported: d = 128, group <= 16, value bits 1..4. */
+ * Supported: d = 128, group <= 16, value bits 1..4.  With kp->s == NULL the
+ * keys are MSE-only records (tq_encode_mse_keys) scored as in tq_scores;
+ * then key and value bits are 2..4, and 4-bit keys take group <= 8. */
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs,
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);

@@ -23,7 +23,7 @@ TQ_F32, TQ_F16 = 0, 1
 
 EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
-    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_workspace", "tq_encode_prod_ws",
+    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
     "tq_debug_set_pack_wait",
@@ -71,7 +71,7 @@ def lib():
         L.tq_build_codebook.argtypes = [ci, ci, vp, vp]
         L.tq_key_layout.argtypes = [P, vp, vp, vp]
         L.tq_value_layout.argtypes = [P, vp, vp, vp]
-        for f in (L.tq_encode_prod, L.tq_encode_mse):
+        for f in (L.tq_encode_prod, L.tq_encode_mse, L.tq_encode_mse_keys):
             f.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp]
         L.tq_encode_prod_ws.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp, sz, vp]
         L.tq_scores_workspace.restype = sz
@@ -227,6 +227,12 @@ def encode_prod(p: Params, x, out: Cache, slot=None, stream=None, ws=None):
 def encode_mse(p: Params, x, out: Cache, slot=None, stream=None):
     _check(lib().tq_encode_mse(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
                                _ptr(slot), _stream(stream)))
+
+
+def encode_mse_keys(p: Params, x, out: Cache, slot=None, stream=None):
+    """MSE-only keys in the per-record key layout (p.s is None; see tq_encode_mse_keys)."""
+    _check(lib().tq_encode_mse_keys(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
+                                    _ptr(slot), _stream(stream)))
 
 
 def scores_workspace(kp: Params, segs: int, group: int) -> int:

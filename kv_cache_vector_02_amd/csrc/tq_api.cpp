@@ -84,8 +84,11 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
   return TQ_OK;
 }
 
+// prod: TurboQuant-prod keys; otherwise MSE-only, as values (token-blocked
+// layout at d_rot = 128) or, with mse_keys, as per-record key records.
 tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, int64_t n,
-                 int64_t ld_x, tq_cache out, const int64_t* slot, void* ws, size_t ws_bytes, void* stream) {
+                 int64_t ld_x, tq_cache out, const int64_t* slot, void* ws, size_t ws_bytes, void* stream,
+                 bool mse_keys = false) {
   tq::EncodeArgs a;
   std::memset(&a, 0, sizeof(a));
   tq_status st = check_params(p, prod, &a.cb, false);
@@ -110,7 +113,8 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   a.eps = p->eps;
   a.s = prod ? p->s : nullptr;
   a.bq = index_bits(p, prod);
-  a.prod = prod;
+  a.prod = prod || mse_keys;
+  a.qjl = prod;
   a.planes = (uint32_t*)out.planes;
   a.scalars = (uint16_t*)out.scalars;
   a.slot = slot;
@@ -160,11 +164,12 @@ tq_status tq_build_codebook(int d, int bits, double* centroids, double* boundari
 
 tq_status tq_key_layout(const tq_params* p, int* planes, int* words, int* scalars) {
   tq::Codebook cb;
-  tq_status st = check_params(p, true, &cb, false);
+  const bool qjl = p && p->s;     // no QJL matrix: MSE-only key records
+  tq_status st = check_params(p, qjl, &cb, false);
   if (st != TQ_OK) return st;
   if (planes) *planes = p->bits;
   if (words) *words = p->d_rot / 32;
-  if (scalars) *scalars = 2;
+  if (scalars) *scalars = qjl ? 2 : 1;
   return TQ_OK;
 }
 
@@ -199,6 +204,11 @@ tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64
   return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream);
 }
 
+tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+                             tq_cache out, const int64_t* slot, void* stream) {
+  return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream, true);
+}
+
 size_t tq_scores_workspace(const tq_params* kp, int segs, int group) {
   (void)kp;
   if (segs <= 0 || group <= 0) return 0;
@@ -212,7 +222,8 @@ static tq_status score_args(const tq_params* kp, const float* q, bool need_q, in
                             bool need_scores, void* ws, size_t ws_bytes, tq::ScoreArgs* a, bool* nothing) {
   std::memset(a, 0, sizeof(*a));
   *nothing = false;
-  tq_status st = check_params(kp, true, &a->cb, true);
+  const bool qjl = kp && kp->s;     // no QJL matrix: MSE-only keys
+  tq_status st = check_params(kp, qjl, &a->cb, true);
   if (st != TQ_OK) return st;
   if (segs < 0 || group < 1 || T < 0) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
   if (segs == 0 || (need_keys && T == 0)) {
@@ -241,7 +252,8 @@ static tq_status score_args(const tq_params* kp, const float* q, bool need_q, in
   a->eps = kp->eps;
   a->rot = kp->rot;
   a->s = kp->s;
-  a->bq = kp->bits - 1;
+  a->bq = qjl ? kp->bits - 1 : kp->bits;
+  a->qjl = qjl;
   a->planes = (const uint32_t*)keys.planes;
   a->scalars = (const uint16_t*)keys.scalars;
   a->seg_stride = stride;
@@ -294,7 +306,8 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
                     float* out, void* ws, size_t ws_bytes, void* stream) {
   tq::AttendArgs a;
   std::memset(&a, 0, sizeof(a));
-  tq_status st = check_params(kp, true, &a.k.cb, true);
+  const bool qjl = kp && kp->s;     // no QJL matrix: MSE-only keys
+  tq_status st = check_params(kp, qjl, &a.k.cb, true);
   if (st != TQ_OK) return st;
   st = check_params(vp, false, &a.cb_v, true);
   if (st != TQ_OK) return st;
@@ -304,6 +317,10 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   if (kp->d != 128 || kp->d_rot != 128 || vp->d != 128 || vp->d_rot != 128)
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports d = d_rot = 128 for keys and values");
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports up to 16 query heads per segment");
+  if (!qjl && (kp->bits < 2 || vp->bits < 2))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attend with MSE-only keys supports key and value bits 2..4");
+  if (!qjl && kp->bits == 4 && group > 8)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attend with 4-bit MSE-only keys supports up to 8 query heads per segment");
   if (!q || !keys.planes || !keys.scalars || !vals.planes || !vals.scalars || !out || !ws)
     return fail(TQ_ERR_INVALID_ARG, "q, keys, vals, out and ws must be non-NULL");
   if (vals.seg_stride % 32) return fail(TQ_ERR_INVALID_ARG, "vals.seg_stride must be a multiple of 32");
@@ -327,7 +344,8 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   a.k.eps = kp->eps;
   a.k.rot = kp->rot;
   a.k.s = kp->s;
-  a.k.bq = kp->bits - 1;
+  a.k.bq = qjl ? kp->bits - 1 : kp->bits;
+  a.k.qjl = qjl;
   a.k.planes = (const uint32_t*)keys.planes;
   a.k.scalars = (const uint16_t*)keys.scalars;
   a.k.seg_stride = kstride;

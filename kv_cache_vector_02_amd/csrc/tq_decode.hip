@@ -74,6 +74,7 @@ struct PrepArgs {
   float u[8];      // Walsh coefficients of the odd-subset planes
   float usum;
   int bq;
+  int qjl;         // 1: prod keys (a QJL plane after the MSE planes); 0: MSE-only keys
   int slices;      // base-256 digits per weight: 2 (8 heads per tile) or 3 (4 heads)
   int mt;          // 16-row tiles per segment
   uint8_t* ws;
@@ -153,7 +154,7 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   const int col = lane & 15, kq = lane >> 4;
   const int G = a.group;
   const int np = mse_planes(a.bq);
-  const int F = 2 * (np + 1);
+  const int F = 2 * (np + a.qjl);
   const int fbytes = (int)pack_frag_bytes(a.mt, F);
   const rsrc_t rdst = make_rsrc(dst, (uint32_t)pack_bytes(a.mt, F));
   const int row = 16 * wave + col;        // A-operand row of this lane
@@ -167,7 +168,8 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   float4 qv = {0.f, 0.f, 0.f, 0.f};
   if (qh < G) qv = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + qh) * D)[q4];
   const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)(HAD ? 0 : row) * D);
-  const float4* srow = reinterpret_cast<const float4*>(a.s + (size_t)row * D);
+  // MSE-only keys have no QJL matrix: its rows read as zeros (q_proj = 0)
+  const float4* srow = reinterpret_cast<const float4*>(a.qjl ? a.s + (size_t)row * D : a.pi);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int k4a = 8 * ks + 2 * kq, k4b = k4a + 1;      // coordinates 32 ks + 8 kq + 0..7
@@ -178,8 +180,8 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
       mv[2 * ks] = prow[k4a];
       mv[2 * ks + 1] = prow[k4b];
     }
-    sv[2 * ks] = srow[k4a];
-    sv[2 * ks + 1] = srow[k4b];
+    sv[2 * ks] = a.qjl ? srow[k4a] : float4{0.f, 0.f, 0.f, 0.f};
+    sv[2 * ks + 1] = a.qjl ? srow[k4b] : float4{0.f, 0.f, 0.f, 0.f};
   }
   // keep all of them ahead of the first product (one memory round trip)
   __builtin_amdgcn_sched_barrier(0);
@@ -338,7 +340,7 @@ template <bool HAD, int S>
 __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void prep_queries128(PrepArgs a) {
   __shared__ PrepLds L;
-  const int F = 2 * (mse_planes(a.bq) + 1);
+  const int F = 2 * (mse_planes(a.bq) + a.qjl);
   prep_pack<HAD, S>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
 }
 
@@ -431,6 +433,22 @@ __device__ __forceinline__ float mse_digits(i32x4 acc) {
   else return (float)combine3(acc);
 }
 
+// Word of Walsh plane p (plane_subset order) from a record's stored words:
+// a single index bit, the parity of the subset's bits, or, at p == NP, the
+// QJL signs stored after the index planes.
+template <int BQ, int NP, bool QJL, typename W>
+__device__ __forceinline__ uint32_t plane_word(W w, int p) {
+  if constexpr (QJL)
+    if (p == NP) return w[BQ];
+  if (p < BQ) return w[p];
+  if constexpr (BQ == 3) return w[0] ^ w[1] ^ w[2];
+  if constexpr (BQ == 4) {
+    const uint32_t all = w[0] ^ w[1] ^ w[2] ^ w[3];
+    return all ^ w[p == 4 ? 3 : p == 5 ? 2 : p == 6 ? 1 : 0];   // subsets 7, 11, 13, 14
+  }
+  return 0u;
+}
+
 // Workgroup = 8 waves = chunk_tiles 16-token tiles of one segment.  A wave
 // takes pairs of adjacent tiles (32 tokens), pairs wave, wave + 8, ...,
 // with RING pairs of loads in flight; the 32 x 8 outputs of a 16-row tile
@@ -439,13 +457,16 @@ __device__ __forceinline__ float mse_digits(i32x4 acc) {
 constexpr int SC_WAVES = 8;
 
 // FUSED: the one-launch form (1-D grid: segs producers, then segs x chunks
-// consumers); HAD selects the producer's rotation.
-template <int BQ, int MT, int S, bool FUSED, bool HAD>
+// consumers); HAD selects the producer's rotation.  QJL: prod keys (BQ index
+// planes, the sign plane, n and gamma); without it MSE-only keys (BQ index
+// planes and n).
+template <int BQ, int MT, int S, bool FUSED, bool HAD, bool QJL>
 __global__ __launch_bounds__(SC_WAVES * 64) __attribute__((amdgpu_waves_per_eu(FUSED && MT == 1 ? 4 : 1)))
 void scores128(Score128Args a) {
-  constexpr int NP = mse_planes(BQ);      // MSE planes after the parity plane
-  constexpr int F = 2 * (NP + 1);         // MFMAs per tile per 16-row tile
-  constexpr int P = BQ + 1;               // stored planes per key record
+  constexpr int NP = mse_planes(BQ);      // Walsh planes of the index bits
+  constexpr int F = 2 * (NP + QJL);       // MFMAs per tile per 16-row tile
+  constexpr int P = BQ + QJL;             // stored planes per key record
+  constexpr int SB = QJL ? 4 : 2;         // scalar bytes per key record
   constexpr uint32_t RB = 16 * P;         // plane bytes per key record
   constexpr int RING = 4;                 // pairs of loads in flight per wave
   constexpr int ROUND = 8;                // pairs per straight-line round
@@ -495,11 +516,11 @@ void scores128(Score128Args a) {
 
   const int64_t rec0 = seg * a.seg_stride + tok0;
   const rsrc_t rk = make_rsrc(a.planes + rec0 * (P * 4), clamp_bytes((a.seg_stride - tok0) * RB));
-  const rsrc_t rs = make_rsrc(a.scalars + rec0 * 2, clamp_bytes((a.seg_stride - tok0) * 4));
+  const rsrc_t rs = make_rsrc(a.scalars + rec0 * (SB / 2), clamp_bytes((a.seg_stride - tok0) * SB));
   const rsrc_t ro = make_rsrc(a.scores + (size_t)seg * a.group * a.T + tok0,
                               clamp_bytes(((int64_t)(a.group - 1) * a.T + a.T - tok0) * 4));
   const uint32_t vk = t16 * RB + kg * (P * 4);
-  const uint32_t vs = t16 * 4;
+  const uint32_t vs = t16 * SB;
   const int ntok = (int)(len - tok0 < (int64_t)a.chunk_tiles * 16 ? len - tok0 : (int64_t)a.chunk_tiles * 16);
   const int npairs = (ntok + 31) / 32;
 
@@ -513,7 +534,9 @@ void scores128(Score128Args a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       wr[slot][h] = load_words<P>(rk, ok ? vk + (tb + 16 * h) * RB : OOB_OFFSET);
-      sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? vs + (tb + 16 * h) * 4 : OOB_OFFSET, 0, 0);
+      const uint32_t so = ok ? vs + (tb + 16 * h) * SB : OOB_OFFSET;
+      if constexpr (QJL) sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0);
+      else sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
     }
   };
   const uint8_t* pack = a.ws + (size_t)seg * pack_bytes(MT, F);
@@ -589,15 +612,8 @@ void scores128(Score128Args a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int p = 0; p <= NP; ++p) {
-      uint32_t word;
-      if (p == NP) {
-        word = w[BQ];                                  // QJL signs
-      } else if (p < BQ) {
-        word = w[p];                                   // single index bits
-      } else {
-        if constexpr (BQ == 3) word = w[0] ^ w[1] ^ w[2];   // parity of 3 bits
-      }
+    for (int p = 0; p < NP + QJL; ++p) {
+      const uint32_t word = plane_word<BQ, NP, QJL>(w, p);
       uint32_t e[8];
       expand8(word, e);
 #pragma unroll
@@ -620,7 +636,7 @@ void scores128(Score128Args a) {
         const int iq = S == 2 ? aq[mt][2 * hh] * 256 + aq[mt][2 * hh + 1] : combine3(aq[mt]);
         const float mse = fmaf(im, cst[mt][hh][0], cst[mt][hh][1]);
         const float qjl = fmaf((float)iq, cst[mt][hh][2], cst[mt][hh][3]);
-        sbuf[(4 * HL * mt + HL * kg + hh) * SROW + col0 + t16] = n * fmaf(g, qjl, mse);
+        sbuf[(4 * HL * mt + HL * kg + hh) * SROW + col0 + t16] = QJL ? n * fmaf(g, qjl, mse) : n * mse;
       }
     }
   };
@@ -675,29 +691,31 @@ int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax
 
 // Grid: (workgroups per segment, segments), sized so that the whole grid is
 // resident at once; a workgroup's span is a multiple of 8 waves x 32 tokens.
-template <int BQ, int MT, int S>
+template <int BQ, int MT, int S, bool QJL = true>
 hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
-  static const int nb = occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false>), SC_WAVES * 64);
+  static const int nb =
+      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false, QJL>), SC_WAVES * 64);
   const int64_t span = split_span(segs, s.T, nb * device_cus(), 32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   const int64_t chunks = (s.T + span - 1) / span;
-  hipLaunchKernelGGL((scores128<BQ, MT, S, false, false>), dim3((unsigned)chunks, (unsigned)segs),
+  hipLaunchKernelGGL((scores128<BQ, MT, S, false, false, QJL>), dim3((unsigned)chunks, (unsigned)segs),
                      dim3(SC_WAVES * 64), 0, stream, s);
   return hipGetLastError();
 }
 
 // One-launch form: the producers take one resident slot per segment, the
 // consumers split the tokens over the rest.
-template <int BQ, int MT, int S, bool HAD>
+template <int BQ, int MT, int S, bool HAD, bool QJL = true>
 hipError_t launch_scores_fused(Score128Args& s, int segs, hipStream_t stream) {
   static const int nb =
-      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, true, HAD>), SC_WAVES * 64);
+      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, true, HAD, QJL>), SC_WAVES * 64);
   const int resident = nb * device_cus() - segs;
   const int64_t span = split_span(segs, s.T, resident > segs ? resident : segs, 32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   s.chunks = (int)((s.T + span - 1) / span);
   const int64_t nwg = (int64_t)segs * (s.chunks + 1);
-  hipLaunchKernelGGL((scores128<BQ, MT, S, true, HAD>), dim3((unsigned)nwg), dim3(SC_WAVES * 64), 0, stream, s);
+  hipLaunchKernelGGL((scores128<BQ, MT, S, true, HAD, QJL>), dim3((unsigned)nwg), dim3(SC_WAVES * 64), 0, stream,
+                     s);
   return hipGetLastError();
 }
 
@@ -758,11 +776,12 @@ int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax
 
 }  // namespace
 
-// Query packs of every segment (sized for the widest key), then the
-// one-launch hand-over words.
+// Query packs of every segment, sized for the widest pack (4 heads per
+// 16-row tile, 16 fragments: MSE-only 4-bit keys in the attention pass; prod
+// keys take at most 10), then the one-launch hand-over words.
 static size_t scores128_pack_region(int segs, int group) {
   const int mt = (group + 3) / 4;
-  return (size_t)segs * pack_bytes(mt, 2 * (mse_planes(3) + 1));
+  return (size_t)segs * pack_bytes(mt, 2 * mse_planes(4));
 }
 
 size_t scores128_workspace(int segs, int group) {
@@ -781,9 +800,10 @@ static uint64_t next_ticket() {
   return t.fetch_add(2, std::memory_order_relaxed);
 }
 
-// Digits per quantised query weight for the score pass: 2 when the keys carry
-// 1 or 2 MSE bits, else 3 (the attention pass always takes 3).
-static int score_slices(int bq) { return bq <= 2 ? 2 : 3; }
+// Digits per quantised query weight for the score pass: 2 for MSE-only keys
+// and for prod keys with 1 or 2 MSE bits, else 3 (the attention pass always
+// takes 3).
+static int score_slices(const ScoreArgs& a) { return !a.qjl || a.bq <= 2 ? 2 : 3; }
 
 static PrepArgs make_prep(const ScoreArgs& a, int slices) {
   PrepArgs p;
@@ -798,6 +818,7 @@ static PrepArgs make_prep(const ScoreArgs& a, int slices) {
   p.s = a.s;
   walsh_coefficients(a.cb, a.bq, p.u, &p.usum);
   p.bq = a.bq;
+  p.qjl = a.qjl;
   p.slices = slices;
   p.mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   p.ws = static_cast<uint8_t*>(a.ws);
@@ -833,7 +854,7 @@ static Score128Args score_pass_args(const ScoreArgs& a) {
 }
 
 hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
-  const int slices = score_slices(a.bq);
+  const int slices = score_slices(a);
   const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   Score128Args s = score_pass_args(a);
   s.prep = make_prep(a, slices);
@@ -841,6 +862,27 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
   s.ticket = next_ticket();
   s.wait_ticks = 100LL * g_pack_wait_us.load(std::memory_order_relaxed);   // 100 MHz clock
   const bool had = a.rot == TQ_ROT_HADAMARD;
+  if (!a.qjl) {
+    switch (a.bq * 100 + mt * 10 + (had ? 1 : 0)) {
+      case 110: return launch_scores_fused<1, 1, 2, false, false>(s, a.segs, stream);
+      case 111: return launch_scores_fused<1, 1, 2, true, false>(s, a.segs, stream);
+      case 120: return launch_scores_fused<1, 2, 2, false, false>(s, a.segs, stream);
+      case 121: return launch_scores_fused<1, 2, 2, true, false>(s, a.segs, stream);
+      case 210: return launch_scores_fused<2, 1, 2, false, false>(s, a.segs, stream);
+      case 211: return launch_scores_fused<2, 1, 2, true, false>(s, a.segs, stream);
+      case 220: return launch_scores_fused<2, 2, 2, false, false>(s, a.segs, stream);
+      case 221: return launch_scores_fused<2, 2, 2, true, false>(s, a.segs, stream);
+      case 310: return launch_scores_fused<3, 1, 2, false, false>(s, a.segs, stream);
+      case 311: return launch_scores_fused<3, 1, 2, true, false>(s, a.segs, stream);
+      case 320: return launch_scores_fused<3, 2, 2, false, false>(s, a.segs, stream);
+      case 321: return launch_scores_fused<3, 2, 2, true, false>(s, a.segs, stream);
+      case 410: return launch_scores_fused<4, 1, 2, false, false>(s, a.segs, stream);
+      case 411: return launch_scores_fused<4, 1, 2, true, false>(s, a.segs, stream);
+      case 420: return launch_scores_fused<4, 2, 2, false, false>(s, a.segs, stream);
+      case 421: return launch_scores_fused<4, 2, 2, true, false>(s, a.segs, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.bq * 100 + mt * 10 + (had ? 1 : 0)) {
     case 110: return launch_scores_fused<1, 1, 2, false>(s, a.segs, stream);
     case 111: return launch_scores_fused<1, 1, 2, true>(s, a.segs, stream);
@@ -863,13 +905,26 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream) {
-  return launch_scores128_prep(a, score_slices(a.bq), stream);
+  return launch_scores128_prep(a, score_slices(a), stream);
 }
 
 hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream) {
-  const int slices = score_slices(a.bq);
+  const int slices = score_slices(a);
   const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   Score128Args s = score_pass_args(a);
+  if (!a.qjl) {
+    switch (a.bq * 10 + mt) {
+      case 11: return launch_scores<1, 1, 2, false>(s, a.segs, stream);
+      case 12: return launch_scores<1, 2, 2, false>(s, a.segs, stream);
+      case 21: return launch_scores<2, 1, 2, false>(s, a.segs, stream);
+      case 22: return launch_scores<2, 2, 2, false>(s, a.segs, stream);
+      case 31: return launch_scores<3, 1, 2, false>(s, a.segs, stream);
+      case 32: return launch_scores<3, 2, 2, false>(s, a.segs, stream);
+      case 41: return launch_scores<4, 1, 2, false>(s, a.segs, stream);
+      case 42: return launch_scores<4, 2, 2, false>(s, a.segs, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.bq * 10 + mt) {
     case 11: return launch_scores<1, 1, 2>(s, a.segs, stream);
     case 12: return launch_scores<1, 2, 2>(s, a.segs, stream);
@@ -955,11 +1010,13 @@ __device__ __forceinline__ uint32_t row_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
 }
 
-template <int BQK, int BQV, int KMT>
+// QJL: prod keys; without it MSE-only keys (BQK index planes and n).
+template <int BQK, int BQV, int KMT, bool QJL = true>
 __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args a) {
   constexpr int NPK = mse_planes(BQK);
-  constexpr int FK = 2 * (NPK + 1);
-  constexpr int PK = BQK + 1;
+  constexpr int FK = 2 * (NPK + QJL);
+  constexpr int PK = BQK + QJL;
+  constexpr int KSB = QJL ? 4 : 2;            // key scalar bytes per record
   constexpr uint32_t RBK = 16 * PK;           // key plane bytes per record
   constexpr int NPV = mse_planes(BQV);
   constexpr int PV = BQV;
@@ -1014,12 +1071,12 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
 
   const int64_t krec0 = seg * a.kstride + c0;
   const rsrc_t rk = make_rsrc(a.kplanes + krec0 * (PK * 4), clamp_bytes((a.kstride - c0) * RBK));
-  const rsrc_t rks = make_rsrc(a.kscal + krec0 * 2, clamp_bytes((a.kstride - c0) * 4));
+  const rsrc_t rks = make_rsrc(a.kscal + krec0 * (KSB / 2), clamp_bytes((a.kstride - c0) * KSB));
   const int64_t vrec0 = seg * a.vstride + c0;   // multiple of 32
   const rsrc_t rv = make_rsrc(a.vplanes + (vrec0 / 32) * (D * PV), clamp_bytes((a.vstride - c0) / 32 * VBB));
   const rsrc_t rvs = make_rsrc(a.vscal + vrec0, clamp_bytes((a.vstride - c0) * 2));
   const uint32_t vko = t16 * RBK + kg * (PK * 4);
-  const uint32_t vkso = t16 * 4;
+  const uint32_t vkso = t16 * KSB;
   const uint32_t vvo = (kg * D + t16) * (PV * 4);
   const uint32_t vno = lane * 4;
 
@@ -1038,7 +1095,10 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
     for (int tile = 0; tile < 8; ++tile) {
       const uint32_t tok = (uint32_t)(128 * g + 16 * tile);
       kw[tile] = load_words<PK>(rk, ok ? vko + tok * RBK : OOB_OFFSET);
-      ks[tile] = __builtin_amdgcn_raw_buffer_load_b32(rks, ok ? vkso + tok * 4 : OOB_OFFSET, 0, 0);
+      // (the offset written out in each branch: a shared offset variable here
+      // crashes this compiler's AGPR-copy rewrite on the 4-tile kernels)
+      if constexpr (QJL) ks[tile] = __builtin_amdgcn_raw_buffer_load_b32(rks, ok ? vkso + tok * 4 : OOB_OFFSET, 0, 0);
+      else ks[tile] = __builtin_amdgcn_raw_buffer_load_b16(rks, ok ? vkso + tok * 2 : OOB_OFFSET, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -1065,15 +1125,8 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
 #pragma unroll
       for (int mt = 0; mt < KMT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int p = 0; p <= NPK; ++p) {
-        uint32_t word;
-        if (p == NPK) {
-          word = kw[tile][BQK];
-        } else if (p < BQK) {
-          word = kw[tile][p];
-        } else {
-          if constexpr (BQK == 3) word = kw[tile][0] ^ kw[tile][1] ^ kw[tile][2];
-        }
+      for (int p = 0; p < NPK + QJL; ++p) {
+        const uint32_t word = plane_word<BQK, NPK, QJL>(kw[tile], p);
         uint32_t e8[8];
         expand8(word, e8);
 #pragma unroll
@@ -1092,7 +1145,7 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
       for (int mt = 0; mt < KMT; ++mt) {
         const float mse = fmaf(mse_digits<NPK>(am[mt]), cst[mt][0], cst[mt][1]);
         const float qjl = fmaf((float)combine3(aq[mt]), cst[mt][2], cst[mt][3]);
-        sc[tile][mt] = valid ? n * fmaf(gm, qjl, mse) : -INFINITY;
+        sc[tile][mt] = valid ? (QJL ? n * fmaf(gm, qjl, mse) : n * mse) : -INFINITY;
       }
     }
     load_keys(g + 4);
@@ -1371,14 +1424,28 @@ int64_t attend_kmax(int segs, int64_t T) {
   return k < 1 ? 1 : k;
 }
 
-template <int BQK, int BQV, int MT>
+template <int BQK, int BQV, int MT, bool QJL = true>
 hipError_t launch_attend(Attend128Args& s, int segs, hipStream_t stream) {
-  static const int nb = occupancy(reinterpret_cast<const void*>(&attend128<BQK, BQV, MT>), 256);
+  static const int nb = occupancy(reinterpret_cast<const void*>(&attend128<BQK, BQV, MT, QJL>), 256);
   s.span = split_span(segs, s.T, nb * device_cus(), AGRAN, attend_kmax(segs, s.T));
   s.nchunks = (int)((s.T + s.span - 1) / s.span);
-  hipLaunchKernelGGL((attend128<BQK, BQV, MT>), dim3((unsigned)s.nchunks, (unsigned)segs), dim3(256), 0,
+  hipLaunchKernelGGL((attend128<BQK, BQV, MT, QJL>), dim3((unsigned)s.nchunks, (unsigned)segs), dim3(256), 0,
                      stream, s);
   return hipGetLastError();
+}
+
+// MSE-only keys of BQK bits (2..4) against values of 2..4 bits; 4-bit keys
+// take at most two 16-row tiles (8 query heads: their 16 fragments per tile
+// fill the registers).
+template <int BQK, int BQV>
+hipError_t launch_attend_mse_keys(Attend128Args& s, int segs, int mt, hipStream_t stream) {
+  switch (mt) {
+    case 1: return launch_attend<BQK, BQV, 1, false>(s, segs, stream);
+    case 2: return launch_attend<BQK, BQV, 2, false>(s, segs, stream);
+    case 3: if constexpr (BQK < 4) return launch_attend<BQK, BQV, 3, false>(s, segs, stream); break;
+    case 4: if constexpr (BQK < 4) return launch_attend<BQK, BQV, 4, false>(s, segs, stream); break;
+  }
+  return hipErrorInvalidValue;
 }
 
 size_t attend_pack_bytes(int segs, int group) { return scores128_workspace(segs, group); }
@@ -1415,7 +1482,20 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   s.nchunks = 0;   // set by the launcher
   s.span = 0;
   const int mt = (a.k.group + 3) / 4;
-  switch ((a.k.bq * 10 + a.bq_v) * 10 + mt) {
+  if (!a.k.qjl) {
+    switch (a.k.bq * 10 + a.bq_v) {
+      case 22: e = launch_attend_mse_keys<2, 2>(s, a.k.segs, mt, stream); break;
+      case 23: e = launch_attend_mse_keys<2, 3>(s, a.k.segs, mt, stream); break;
+      case 24: e = launch_attend_mse_keys<2, 4>(s, a.k.segs, mt, stream); break;
+      case 32: e = launch_attend_mse_keys<3, 2>(s, a.k.segs, mt, stream); break;
+      case 33: e = launch_attend_mse_keys<3, 3>(s, a.k.segs, mt, stream); break;
+      case 34: e = launch_attend_mse_keys<3, 4>(s, a.k.segs, mt, stream); break;
+      case 42: e = launch_attend_mse_keys<4, 2>(s, a.k.segs, mt, stream); break;
+      case 43: e = launch_attend_mse_keys<4, 3>(s, a.k.segs, mt, stream); break;
+      case 44: e = launch_attend_mse_keys<4, 4>(s, a.k.segs, mt, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else switch ((a.k.bq * 10 + a.bq_v) * 10 + mt) {
     case 111: e = launch_attend<1, 1, 1>(s, a.k.segs, stream); break;
     case 112: e = launch_attend<1, 1, 2>(s, a.k.segs, stream); break;
     case 113: e = launch_attend<1, 1, 3>(s, a.k.segs, stream); break;

@@ -137,18 +137,23 @@ __device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, 
   }
 }
 
+// PROD: per-record key layout (in-lane packing); with QJL the residual's
+// sign projection follows (prod keys), without it the record holds the BQ
+// index planes and the norm only (MSE-only keys).  !PROD: values in the
+// token-blocked layout.
 // SLOTS: values written through a slot map (any record order), whose tiles
 // may take the per-bit path; without it only a ragged last tile can.
-template <bool PROD, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS>
+template <bool PROD, bool QJL, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS>
 __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
+  static_assert(PROD || !QJL, "values carry no QJL bits");
   extern __shared__ half8 lds[];
   half8* fpi = lds;
   half8* fs = lds + FRAGS;
   build_frags<64 * WAVES>(fpi, a.pi, PI_SCALE, HAD ? a.eps : nullptr);
-  if (PROD) build_frags<64 * WAVES>(fs, a.s, 1.f);
+  if (QJL) build_frags<64 * WAVES>(fs, a.s, 1.f);
   __syncthreads();
 
-  constexpr int P = PROD ? BQ + 1 : BQ;     // planes per record
+  constexpr int P = QJL ? BQ + 1 : BQ;      // planes per record
   constexpr int VT = 32 * NT;               // vectors per wave tile
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
               }
             }
           }
-          if (PROD) {
+          if (QJL) {
             const float d = y - chat;      // residual / ysc
             g2[nt] += d * d;
             _Float16 hi, lo;
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
     uint32_t sw[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sw[nt][0] = sw[nt][1] = 0u;
-    if (PROD) {
+    if (QJL) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         f32x16 acc[NT];
@@ -444,7 +449,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float g = 0.f;
-      if (PROD) {
+      if (QJL) {
         float t = g2[nt] + shfl_xor_f(g2[nt], 32);
         g = sqrtf(t) * ysc[nt];
       }
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           out[p] = __builtin_bitreverse32(iw[nt][p][0]);
           out[P + p] = __builtin_bitreverse32(iw[nt][p][1]);
         }
-        if (PROD) {
+        if (QJL) {
           out[BQ] = __builtin_bitreverse32(sw[nt][0]);
           out[P + BQ] = __builtin_bitreverse32(sw[nt][1]);
         }
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
         for (int i = 0; i < P; ++i) dst[i] = make_uint2(out[2 * i], out[2 * i + 1]);
         if (h == 0) {
-          if (PROD) {
+          if (QJL) {
             reinterpret_cast<uint32_t*>(a.scalars)[rec] =
                 (uint32_t)f16_bits(nrm[nt]) | ((uint32_t)f16_bits(g) << 16);
           } else {
@@ -491,12 +496,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   }
 }
 
-template <bool PROD, int BQ, bool F16IN, bool HAD, int WAVES>
+template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int WAVES>
 hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
   constexpr int NT = 1;
-  auto kern = PROD || !a.slot ? encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD, false>
-                              : encode_dense128<PROD, BQ, F16IN, NT, WAVES, HAD, !PROD>;
-  const size_t lds = (PROD ? 2 : 1) * FRAGS * sizeof(half8);
+  auto kern = PROD || !a.slot ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, false>
+                              : encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD>;
+  const size_t lds = (QJL ? 2 : 1) * FRAGS * sizeof(half8);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -513,46 +518,59 @@ hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
 // sequence) takes one-wave workgroups instead, so that its tiles (and, for
 // values written through a slot map, their per-bit atomics) spread over as
 // many compute units as there are tiles.
-template <bool PROD, int BQ, bool F16IN, bool HAD>
+template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   int dev = 0, cus = 256;
   hipGetDevice(&dev);
   hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t ntiles = (a.n + 31) / 32;
-  if (ntiles < 2 * (int64_t)cus) return launch_waves<PROD, BQ, F16IN, HAD, 1>(a, cus, stream);
-  return launch_waves<PROD, BQ, F16IN, HAD, 8>(a, cus, stream);
+  if (ntiles < 2 * (int64_t)cus) return launch_waves<PROD, QJL, BQ, F16IN, HAD, 1>(a, cus, stream);
+  return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8>(a, cus, stream);
+}
+
+// MSE-only keys: b index bits in the per-record layout
+template <bool F16IN, bool HAD>
+hipError_t launch_mse_keys(const EncodeArgs& a, hipStream_t stream) {
+  switch (a.bq) {
+    case 1: return launch_one<true, false, 1, F16IN, HAD>(a, stream);
+    case 2: return launch_one<true, false, 2, F16IN, HAD>(a, stream);
+    case 3: return launch_one<true, false, 3, F16IN, HAD>(a, stream);
+    case 4: return launch_one<true, false, 4, F16IN, HAD>(a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <bool HAD>
 hipError_t launch_rot(const EncodeArgs& a, hipStream_t stream) {
+  if (a.prod && !a.qjl) return a.f16_in ? launch_mse_keys<true, HAD>(a, stream) : launch_mse_keys<false, HAD>(a, stream);
   if (a.prod) {
     if (a.f16_in) {
       switch (a.bq) {
-        case 1: return launch_one<true, 1, true, HAD>(a, stream);
-        case 2: return launch_one<true, 2, true, HAD>(a, stream);
-        case 3: return launch_one<true, 3, true, HAD>(a, stream);
+        case 1: return launch_one<true, true, 1, true, HAD>(a, stream);
+        case 2: return launch_one<true, true, 2, true, HAD>(a, stream);
+        case 3: return launch_one<true, true, 3, true, HAD>(a, stream);
       }
     } else {
       switch (a.bq) {
-        case 1: return launch_one<true, 1, false, HAD>(a, stream);
-        case 2: return launch_one<true, 2, false, HAD>(a, stream);
-        case 3: return launch_one<true, 3, false, HAD>(a, stream);
+        case 1: return launch_one<true, true, 1, false, HAD>(a, stream);
+        case 2: return launch_one<true, true, 2, false, HAD>(a, stream);
+        case 3: return launch_one<true, true, 3, false, HAD>(a, stream);
       }
     }
   } else {
     if (a.f16_in) {
       switch (a.bq) {
-        case 1: return launch_one<false, 1, true, HAD>(a, stream);
-        case 2: return launch_one<false, 2, true, HAD>(a, stream);
-        case 3: return launch_one<false, 3, true, HAD>(a, stream);
-        case 4: return launch_one<false, 4, true, HAD>(a, stream);
+        case 1: return launch_one<false, false, 1, true, HAD>(a, stream);
+        case 2: return launch_one<false, false, 2, true, HAD>(a, stream);
+        case 3: return launch_one<false, false, 3, true, HAD>(a, stream);
+        case 4: return launch_one<false, false, 4, true, HAD>(a, stream);
       }
     } else {
       switch (a.bq) {
-        case 1: return launch_one<false, 1, false, HAD>(a, stream);
-        case 2: return launch_one<false, 2, false, HAD>(a, stream);
-        case 3: return launch_one<false, 3, false, HAD>(a, stream);
-        case 4: return launch_one<false, 4, false, HAD>(a, stream);
+        case 1: return launch_one<false, false, 1, false, HAD>(a, stream);
+        case 2: return launch_one<false, false, 2, false, HAD>(a, stream);
+        case 3: return launch_one<false, false, 3, false, HAD>(a, stream);
+        case 4: return launch_one<false, false, 4, false, HAD>(a, stream);
       }
     }
   }

@@ -28,7 +28,8 @@ struct EncodeArgs {
   const float* s;      // QJL matrix [d_rot][d_rot] (prod only)
   Codebook cb;
   int bq;              // index bits
-  int prod;            // 1: keys (prod), 0: values (mse)
+  int prod;            // 1: per-record key layout, 0: values (mse, token-blocked)
+  int qjl;             // with prod: 1 = QJL signs and gamma (prod keys), 0 = MSE-only keys
   int had;             // 1: sign-flipped Hadamard rotation (eps), 0: dense (pi)
   uint32_t* planes;    // [records][P][d_rot/32]
   uint16_t* scalars;   // [records][S] float16 bit patterns
@@ -89,9 +90,10 @@ struct ScoreArgs {
   const float* pi;       // rotation of the keys (dense)
   const float* eps;      // hadamard signs
   int rot;
-  const float* s;        // QJL matrix
+  const float* s;        // QJL matrix (prod keys) or NULL (MSE-only keys)
   Codebook cb;
-  int bq;
+  int bq;                // index bits
+  int qjl;               // 1: prod keys (QJL plane, n and gamma); 0: MSE-only keys (n only)
   const uint32_t* planes;
   const uint16_t* scalars;
   int64_t seg_stride;

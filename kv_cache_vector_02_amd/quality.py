@@ -13,7 +13,8 @@ table (cosine of the attention distributions and top-1 agreement at 2, 3 and
 * output fidelity: the cosine between exact softmax attention over the
   uncompressed keys and values and tq_attend over their compressed records.
 
-The compressed side runs in libtq (tq_encode_prod / tq_encode_mse, tq_scores,
+The compressed side runs in libtq (tq_encode_prod, or tq_encode_mse_keys for
+a key quantizer without a QJL matrix; tq_encode_mse for values; tq_scores,
 tq_attend).  The exact side is float32 PyTorch on the same device (the
 products, the softmax and the weighted sum), the yardstick the compressed
 results are measured against; none of it is on the hot path.  Argmax ties go
@@ -37,8 +38,9 @@ def exact_scores(keys, queries):
 
 
 def encode_keys(kp: tq.Params, keys, seg_stride: int = 0) -> tq.Cache:
+    """Prod keys, or MSE-only keys when kp has no QJL matrix."""
     cache = tq.alloc_cache(tq.key_layout(kp), keys.shape[0], seg_stride)
-    tq.encode_prod(kp, keys.contiguous(), cache)
+    (tq.encode_prod if kp.s is not None else tq.encode_mse_keys)(kp, keys.contiguous(), cache)
     return cache
 
 
@@ -129,9 +131,8 @@ def output_fidelity(kp: tq.Params, vp: tq.Params, keys, values, queries, group: 
     Returns (cosine [segs*group], exact output, compressed output)."""
     T = _torch()
     segs, L, d = keys.shape
-    kc = tq.alloc_cache(tq.key_layout(kp), segs * L, seg_stride=L)
+    kc = encode_keys(kp, keys.reshape(segs * L, d), seg_stride=L)
     vc = tq.alloc_value_cache(tq.value_layout(vp), segs * L, seg_stride=L)
-    tq.encode_prod(kp, keys.reshape(segs * L, d).contiguous(), kc)
     tq.encode_mse(vp, values.reshape(segs * L, d).contiguous(), vc)
     out = compressed_attention(kp, vp, kc, vc, L, queries, group, scale)
     ref = exact_attention(keys, values, queries, group, scale)

@@ -98,6 +98,25 @@ def test_end_to_end_fidelity_with_gpu_encode(bits):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
+def test_end_to_end_fidelity_mse_keys(bits):
+    # MSE-only keys at b index bits (no QJL matrix): GPU encode + scores,
+    # against the oracle's MSE encoder and biased inner product
+    _log(f"quality end-to-end, MSE-only keys b{bits}")
+    keys = unit_gaussian(2048, 128, seed=12)
+    qs = unit_gaussian(100, 128, seed=12, purpose=QUERIES)
+    st = Setup(bits=bits, prod=False, seed=12)
+    r = quality.attention_fidelity(st.params, _dev(keys), _dev(qs))
+    code = st.encode_oracle(keys)
+    est_o = est.mse_scores(qs, code.idx, code.n.astype(np.float16).astype(np.float64), st.rot, st.c32)
+    cos_o, top1_o = oq.attention_fidelity(qs.astype(np.float64) @ keys.astype(np.float64).T, est_o)
+    cos = r["cosine"].cpu().numpy()
+    assert np.max(np.abs(cos - cos_o)) <= 1e-4
+    assert abs(r["top1_rate"] - top1_o.mean()) <= 0.02
+    _log(f"  mean cos {r['mean_cosine']:.6f} (oracle {cos_o.mean():.6f}), top-1 {r['top1_rate']:.2f} "
+         f"(oracle {top1_o.mean():.2f})")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_needle_trials(bits):
     _log(f"quality needle b{bits}: 20 trials x 8192 keys")
     trials, L = 20, 8192
