@@ -74,7 +74,6 @@ struct PrepArgs {
   float u[8];      // Walsh coefficients of the odd-subset planes
   float usum;
   int bq;
-  int qjl;         // 1: prod keys (a QJL plane after the MSE planes); 0: MSE-only keys
   int slices;      // base-256 digits per weight: 2 (8 heads per tile) or 3 (4 heads)
   int mt;          // 16-row tiles per segment
   uint8_t* ws;
@@ -143,7 +142,7 @@ struct PrepLds {
 // number of base-256 digits per weight; CPOL the cache policy of the pack's
 // stores (the one-launch scores write it device-coherent for the workgroups
 // of other XCDs).
-template <bool HAD, int S, int CPOL = 0>
+template <bool HAD, int S, int CPOL = 0, bool QJL = true>
 __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L, uint8_t* dst) {
   float* qr = L.qr;
   float* qp = L.qp;
@@ -154,7 +153,7 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   const int col = lane & 15, kq = lane >> 4;
   const int G = a.group;
   const int np = mse_planes(a.bq);
-  const int F = 2 * (np + a.qjl);
+  const int F = 2 * (np + (QJL ? 1 : 0));
   const int fbytes = (int)pack_frag_bytes(a.mt, F);
   const rsrc_t rdst = make_rsrc(dst, (uint32_t)pack_bytes(a.mt, F));
   const int row = 16 * wave + col;        // A-operand row of this lane
@@ -169,7 +168,7 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   if (qh < G) qv = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + qh) * D)[q4];
   const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)(HAD ? 0 : row) * D);
   // MSE-only keys have no QJL matrix: its rows read as zeros (q_proj = 0)
-  const float4* srow = reinterpret_cast<const float4*>(a.qjl ? a.s + (size_t)row * D : a.pi);
+  const float4* srow = reinterpret_cast<const float4*>(QJL ? a.s + (size_t)row * D : a.pi);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int k4a = 8 * ks + 2 * kq, k4b = k4a + 1;      // coordinates 32 ks + 8 kq + 0..7
@@ -180,8 +179,12 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
       mv[2 * ks] = prow[k4a];
       mv[2 * ks + 1] = prow[k4b];
     }
-    sv[2 * ks] = a.qjl ? srow[k4a] : float4{0.f, 0.f, 0.f, 0.f};
-    sv[2 * ks + 1] = a.qjl ? srow[k4b] : float4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (QJL) {
+      sv[2 * ks] = srow[k4a];
+      sv[2 * ks + 1] = srow[k4b];
+    } else {
+      sv[2 * ks] = sv[2 * ks + 1] = float4{0.f, 0.f, 0.f, 0.f};
+    }
   }
   // keep all of them ahead of the first product (one memory round trip)
   __builtin_amdgcn_sched_barrier(0);
@@ -336,12 +339,12 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
 
 // (at most two waves per SIMD: the register budget keeps every operand load
 // of a lane in flight at once)
-template <bool HAD, int S>
+template <bool HAD, int S, bool QJL>
 __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void prep_queries128(PrepArgs a) {
   __shared__ PrepLds L;
-  const int F = 2 * (mse_planes(a.bq) + a.qjl);
-  prep_pack<HAD, S>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
+  const int F = 2 * (mse_planes(a.bq) + (QJL ? 1 : 0));
+  prep_pack<HAD, S, 0, QJL>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
 }
 
 // One-launch scores: the first workgroup of each segment builds the query
@@ -433,13 +436,12 @@ __device__ __forceinline__ float mse_digits(i32x4 acc) {
   else return (float)combine3(acc);
 }
 
-// Word of Walsh plane p (plane_subset order) from a record's stored words:
-// a single index bit, the parity of the subset's bits, or, at p == NP, the
-// QJL signs stored after the index planes.
+// Word of Walsh plane p (plane_subset order) of an MSE-only key record: a
+// single index bit, or the parity of the subset's bits.  (The prod kernels
+// spell the same selection out inline, QJL signs at p == NP.)
 template <int BQ, int NP, bool QJL, typename W>
 __device__ __forceinline__ uint32_t plane_word(W w, int p) {
-  if constexpr (QJL)
-    if (p == NP) return w[BQ];
+  static_assert(!QJL, "prod records select their words inline");
   if (p < BQ) return w[p];
   if constexpr (BQ == 3) return w[0] ^ w[1] ^ w[2];
   if constexpr (BQ == 4) {
@@ -489,8 +491,8 @@ void scores128(Score128Args a) {
     if (b < a.prep.segs) {
       // producer of segment b: the pack with device-coherent stores, every
       // store complete, then the flag
-      prep_pack<HAD, S, CPOL_SC1>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
-                                  a.prep.ws + (size_t)b * pack_bytes(MT, F));
+      prep_pack<HAD, S, CPOL_SC1, QJL>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
+                                       a.prep.ws + (size_t)b * pack_bytes(MT, F));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -534,9 +536,8 @@ void scores128(Score128Args a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       wr[slot][h] = load_words<P>(rk, ok ? vk + (tb + 16 * h) * RB : OOB_OFFSET);
-      const uint32_t so = ok ? vs + (tb + 16 * h) * SB : OOB_OFFSET;
-      if constexpr (QJL) sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0);
-      else sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+      if constexpr (QJL) sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? vs + (tb + 16 * h) * 4 : OOB_OFFSET, 0, 0);
+      else sr[slot][h] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? vs + (tb + 16 * h) * 2 : OOB_OFFSET, 0, 0);
     }
   };
   const uint8_t* pack = a.ws + (size_t)seg * pack_bytes(MT, F);
@@ -555,7 +556,7 @@ void scores128(Score128Args a) {
     if (!*got) {
       // no pack within the wait: build it here (the same bytes the producer
       // writes), then request the first keys again
-      prep_pack<HAD, S, CPOL_SC1>(a.prep, seg, *reinterpret_cast<PrepLds*>(smem), const_cast<uint8_t*>(pack));
+      prep_pack<HAD, S, CPOL_SC1, QJL>(a.prep, seg, *reinterpret_cast<PrepLds*>(smem), const_cast<uint8_t*>(pack));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
 #pragma unroll
@@ -613,7 +614,18 @@ void scores128(Score128Args a) {
     for (int mt = 0; mt < MT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int p = 0; p < NP + QJL; ++p) {
-      const uint32_t word = plane_word<BQ, NP, QJL>(w, p);
+      uint32_t word;
+      if constexpr (QJL) {
+        if (p == NP) {
+          word = w[QJL ? BQ : 0];                        // QJL signs
+        } else if (p < BQ) {
+          word = w[p];                                   // single index bits
+        } else {
+          if constexpr (BQ == 3) word = w[0] ^ w[1] ^ w[2];   // parity of 3 bits
+        }
+      } else {
+        word = plane_word<BQ, NP, false>(w, p);
+      }
       uint32_t e[8];
       expand8(word, e);
 #pragma unroll
@@ -818,7 +830,6 @@ static PrepArgs make_prep(const ScoreArgs& a, int slices) {
   p.s = a.s;
   walsh_coefficients(a.cb, a.bq, p.u, &p.usum);
   p.bq = a.bq;
-  p.qjl = a.qjl;
   p.slices = slices;
   p.mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   p.ws = static_cast<uint8_t*>(a.ws);
@@ -828,12 +839,16 @@ static PrepArgs make_prep(const ScoreArgs& a, int slices) {
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream) {
   const PrepArgs p = make_prep(a, slices);
   const bool had = a.rot == TQ_ROT_HADAMARD;
-  if (slices == 2) {
-    if (had) hipLaunchKernelGGL((prep_queries128<true, 2>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
-    else hipLaunchKernelGGL((prep_queries128<false, 2>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
-  } else {
-    if (had) hipLaunchKernelGGL((prep_queries128<true, 3>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
-    else hipLaunchKernelGGL((prep_queries128<false, 3>), dim3(a.segs), dim3(PREP_THREADS), 0, stream, p);
+  const dim3 grid(a.segs), block(PREP_THREADS);
+  switch ((slices == 2 ? 0 : 4) + (had ? 2 : 0) + (a.qjl ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((prep_queries128<false, 2, false>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((prep_queries128<false, 2, true>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prep_queries128<true, 2, false>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((prep_queries128<true, 2, true>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prep_queries128<false, 3, false>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((prep_queries128<false, 3, true>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((prep_queries128<true, 3, false>), grid, block, 0, stream, p); break;
+    case 7: hipLaunchKernelGGL((prep_queries128<true, 3, true>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }
@@ -1126,7 +1141,18 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
       for (int mt = 0; mt < KMT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
 #pragma unroll
       for (int p = 0; p < NPK + QJL; ++p) {
-        const uint32_t word = plane_word<BQK, NPK, QJL>(kw[tile], p);
+        uint32_t word;
+        if constexpr (QJL) {
+          if (p == NPK) {
+            word = kw[tile][QJL ? BQK : 0];
+          } else if (p < BQK) {
+            word = kw[tile][p];
+          } else {
+            if constexpr (BQK == 3) word = kw[tile][0] ^ kw[tile][1] ^ kw[tile][2];
+          }
+        } else {
+          word = plane_word<BQK, NPK, false>(kw[tile], p);
+        }
         uint32_t e8[8];
         expand8(word, e8);
 #pragma unroll
