@@ -300,7 +300,8 @@ def quality_report(torch, tq):
     unit keys), and the cosine of tq_attend's output to exact attention over
     decoder-shaped keys and values (4 segments x 2048 tokens, 8 query heads
     each, temperature 1/sqrt(d)).  Keys prod (b-1 MSE bits + 1 QJL bit, m = d)
-    and, for comparison at equal bits, MSE-only (b index bits); values MSE at b
+    and, for comparison at equal bits, MSE-only (b index bits), plain or with
+    EDEN's unbiased per-vector scale (then on the values too); values MSE at b
     bits."""
     from kv_cache_vector_02_amd import quality
     from tq_inputs import (QUERIES, gaussian_matrix, gaussian_queries, haar_orthogonal, kv_tensor,
@@ -321,8 +322,9 @@ def quality_report(torch, tq):
     xv = dev(kv_tensor(1, 4, 2048, D_, seed=14, value=True)[0])
     oq = dev(gaussian_queries(32, D_, seed=14))
     rows = []
-    for keys_kind in ("prod", "mse"):
+    for keys_kind in ("prod", "mse", "eden"):
         prod = keys_kind == "prod"
+        eden = keys_kind == "eden"
 
         def kparams(bits, seed):
             # MSE-only keys: b index bits and no QJL matrix, the keys' rotation stream
@@ -333,10 +335,10 @@ def quality_report(torch, tq):
             return tq.Params(d=D_, bits=bits, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b, pi=pi)
 
         for bits in (2, 3, 4):
-            r = quality.attention_fidelity(kparams(bits, 11), keys, qs)
-            found, _, _ = quality.needle(kparams(bits, 13), hay, hq)
+            r = quality.attention_fidelity(kparams(bits, 11), keys, qs, eden=eden)
+            found, _, _ = quality.needle(kparams(bits, 13), hay, hq, eden=eden)
             cos, _, _ = quality.output_fidelity(kparams(bits, 14), params(bits, False, 14), xk, xv, oq, 8,
-                                                1.0 / np.sqrt(D_))
+                                                1.0 / np.sqrt(D_), eden=eden)
             rows.append({"keys": keys_kind, "bits": bits, "attention_cosine": round(r["mean_cosine"], 6),
                          "top1": round(r["top1_rate"], 3), "needle_found": int(found.sum()), "needle_trials": 20,
                          "output_cosine": round(float(cos.mean()), 6)})

@@ -64,6 +64,8 @@ typedef enum {
 
 typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 } tq_rot;
 typedef enum { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
+/* Record layout of an MSE encode (tq_encode_eden). */
+typedef enum { TQ_LAYOUT_BLOCKS = 0, TQ_LAYOUT_RECORDS = 1 } tq_layout;
 
 /* Parameters of one quantizer (one for keys, one for values).
  *   d       input dimension
@@ -176,6 +178,22 @@ tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64
  * tq_encode_mse. */
 tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
                              int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
+
+/* MSE encode with EDEN's unbiased per-vector scale (the prior-work map of the
+ * explainer page, section 0.9: EDEN keeps S = ||x||^2 / <R x, Q(R x)>, which
+ * makes the reconstruction unbiased; at one bit it is DRIVE's unbiased scale
+ * ||x||^2 / ||R x||_1).  The codes are those of tq_encode_mse; the record's
+ * fp16 scalar holds, in place of n = ||x||,
+ *   S = n / <y, c[idx]>      (y = rot(x / n), c the unit-sphere centroids),
+ * so the dequantized vector S rot^T(c[idx]) has <x, x^> = ||x||^2 exactly and
+ * E[x^] = x over the rotation, and the score and attention calls, which read
+ * the scalar as they read n, return unbiased estimates.  S = 0 for x = 0.
+ * layout  TQ_LAYOUT_BLOCKS: values in the token-blocked layout (as
+ *         tq_encode_mse); TQ_LAYOUT_RECORDS: MSE-only keys in the per-record
+ *         key layout (as tq_encode_mse_keys)
+ * Other arguments as for tq_encode_mse.  Supported: d = d_rot = 128. */
+tq_status tq_encode_eden(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+                         tq_layout layout, tq_cache out, const int64_t* slot, void* stream);
 
 /* Workspace bytes tq_scores needs for segs segments of group query heads. */
 size_t tq_scores_workspace(const tq_params* kp, int segs, int group);

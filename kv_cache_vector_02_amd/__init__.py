@@ -20,10 +20,11 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP = 0, 1, 2, 3
 TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
 TQ_F32, TQ_F16 = 0, 1
+TQ_LAYOUT_BLOCKS, TQ_LAYOUT_RECORDS = 0, 1
 
 EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
-    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_workspace", "tq_encode_prod_ws",
+    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_eden", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
     "tq_debug_set_pack_wait",
@@ -73,6 +74,7 @@ def lib():
         L.tq_value_layout.argtypes = [P, vp, vp, vp]
         for f in (L.tq_encode_prod, L.tq_encode_mse, L.tq_encode_mse_keys):
             f.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp]
+        L.tq_encode_eden.argtypes = [P, vp, ci, i64, i64, ci, tq_cache, vp, vp]
         L.tq_encode_prod_ws.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp, sz, vp]
         L.tq_scores_workspace.restype = sz
         L.tq_scores_workspace.argtypes = [P, ci, ci]
@@ -233,6 +235,14 @@ def encode_mse_keys(p: Params, x, out: Cache, slot=None, stream=None):
     """MSE-only keys in the per-record key layout (p.s is None; see tq_encode_mse_keys)."""
     _check(lib().tq_encode_mse_keys(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c,
                                     _ptr(slot), _stream(stream)))
+
+
+def encode_eden(p: Params, x, out: Cache, keys: bool, slot=None, stream=None):
+    """MSE records with EDEN's unbiased scale n / <y, c[idx]> in place of n (see
+    tq_encode_eden): MSE-only keys in the per-record layout when keys, else values."""
+    layout = TQ_LAYOUT_RECORDS if keys else TQ_LAYOUT_BLOCKS
+    _check(lib().tq_encode_eden(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), layout, out.c,
+                                _ptr(slot), _stream(stream)))
 
 
 def scores_workspace(kp: Params, segs: int, group: int) -> int:

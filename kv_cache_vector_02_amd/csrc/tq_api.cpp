@@ -88,7 +88,7 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
 // layout at d_rot = 128) or, with mse_keys, as per-record key records.
 tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, int64_t n,
                  int64_t ld_x, tq_cache out, const int64_t* slot, void* ws, size_t ws_bytes, void* stream,
-                 bool mse_keys = false) {
+                 bool mse_keys = false, bool eden = false) {
   tq::EncodeArgs a;
   std::memset(&a, 0, sizeof(a));
   tq_status st = check_params(p, prod, &a.cb, false);
@@ -115,6 +115,9 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   a.bq = index_bits(p, prod);
   a.prod = prod || mse_keys;
   a.qjl = prod;
+  a.eden = eden;
+  if (eden && !(p->d == 128 && p->d_rot == 128))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_encode_eden supports d = d_rot = 128 (got %d, %d)", p->d, p->d_rot);
   a.planes = (uint32_t*)out.planes;
   a.scalars = (uint16_t*)out.scalars;
   a.slot = slot;
@@ -207,6 +210,13 @@ tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64
 tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
                              tq_cache out, const int64_t* slot, void* stream) {
   return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream, true);
+}
+
+tq_status tq_encode_eden(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+                         tq_layout layout, tq_cache out, const int64_t* slot, void* stream) {
+  if (layout != TQ_LAYOUT_BLOCKS && layout != TQ_LAYOUT_RECORDS)
+    return fail(TQ_ERR_INVALID_ARG, "layout must be TQ_LAYOUT_BLOCKS or TQ_LAYOUT_RECORDS");
+  return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream, layout == TQ_LAYOUT_RECORDS, true);
 }
 
 size_t tq_scores_workspace(const tq_params* kp, int segs, int group) {

@@ -143,9 +143,12 @@ __device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, 
 // token-blocked layout.
 // SLOTS: values written through a slot map (any record order), whose tiles
 // may take the per-bit path; without it only a ragged last tile can.
-template <bool PROD, bool QJL, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS>
+// EDEN: an MSE record stores the unbiased per-vector scale n / <y, c[idx]>
+// instead of n (EDEN's scale; DRIVE's at one bit).
+template <bool PROD, bool QJL, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS, bool EDEN = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   static_assert(PROD || !QJL, "values carry no QJL bits");
+  static_assert(!(EDEN && QJL), "the scale replaces the norm of MSE records only");
   extern __shared__ half8 lds[];
   half8* fpi = lds;
   half8* fs = lds + FRAGS;
@@ -271,9 +274,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
     uint32_t iw[NT][BQ][2];
     half8 rh[NT][8], rl[NT][8];
     float g2[NT];
+    float yc[NT];   // EDEN: this lane's part of <y, c[idx]> (keys: in accumulator x scaled-centroid units)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       g2[nt] = 0.f;
+      yc[nt] = 0.f;
 #pragma unroll
       for (int p = 0; p < BQ; ++p) iw[nt][p][0] = iw[nt][p][1] = 0u;
     }
@@ -319,6 +324,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             uint64_t ge[(1 << BQ) - 1];
 #pragma unroll
             for (int k = 0; k < (1 << BQ) - 1; ++k) ge[k] = __ballot(y >= cbv.b[k]);
+            if constexpr (EDEN) {
+              float cv = cbv.c[0];
+#pragma unroll
+              for (int k = 0; k < (1 << BQ) - 1; ++k) cv = select_mask(ge[k], cbv.c[k + 1], cv);
+              yc[nt] = fmaf(y, cv, yc[nt]);
+            }
 #pragma unroll
             for (int p = 0; p < BQ; ++p) {
               uint64_t m = 0;
@@ -353,6 +364,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             ge[k] = ge_mask(y, PROD ? bsc[nt][k] : cbv.b[k]);
             chat = select_mask(ge[k], PROD ? csc[nt][k + 1] : cbv.c[k + 1], chat);
           }
+          if constexpr (EDEN) yc[nt] = fmaf(y, chat, yc[nt]);
           uint64_t bit[BQ];
 #pragma unroll
           for (int p = 0; p < BQ; ++p) {
@@ -463,8 +475,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             base[(64 + lane) * BQ + p] = vhi[p];
           }
         }
-        if (vec[nt] < a.n && h == 0) a.scalars[a.slot ? a.slot[vec[nt]] : vec[nt]] = f16_bits(nrm[nt]);
+        float sv = nrm[nt];
+        if constexpr (EDEN) {
+          const float t = yc[nt] + shfl_xor_f(yc[nt], 32);    // <y, c[idx]>, y on the unit sphere
+          sv = nrm[nt] > 0.f && t > 0.f ? nrm[nt] / t : 0.f;
+        }
+        if (vec[nt] < a.n && h == 0) a.scalars[a.slot ? a.slot[vec[nt]] : vec[nt]] = f16_bits(sv);
         continue;
+      }
+      // MSE-only key scalar: n, or with EDEN n / <y, c[idx]> (the sum over both
+      // half-waves runs on every lane)
+      float ks = nrm[nt];
+      if constexpr (EDEN) {
+        const float t = (yc[nt] + shfl_xor_f(yc[nt], 32)) * (ysc[nt] * ysc[nt]);
+        ks = nrm[nt] > 0.f && t > 0.f ? nrm[nt] / t : 0.f;
       }
       if (vec[nt] < a.n) {
         const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
@@ -488,7 +512,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             reinterpret_cast<uint32_t*>(a.scalars)[rec] =
                 (uint32_t)f16_bits(nrm[nt]) | ((uint32_t)f16_bits(g) << 16);
           } else {
-            a.scalars[rec] = f16_bits(nrm[nt]);
+            a.scalars[rec] = f16_bits(ks);
           }
         }
       }
@@ -496,11 +520,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   }
 }
 
-template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int WAVES>
+template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int WAVES, bool EDEN = false>
 hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
   constexpr int NT = 1;
-  auto kern = PROD || !a.slot ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, false>
-                              : encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD>;
+  // EDEN values always take the slot-capable form (one kernel for both)
+  auto kern = EDEN ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD, EDEN>
+              : PROD || !a.slot ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, false>
+                                : encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD>;
   const size_t lds = (QJL ? 2 : 1) * FRAGS * sizeof(half8);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -528,6 +554,22 @@ hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8>(a, cus, stream);
 }
 
+// EDEN-scaled MSE records (keys in the per-record layout, or values), b
+// index bits; one launch shape (8-wave workgroups) for every batch size
+template <bool PROD, bool F16IN, bool HAD>
+hipError_t launch_eden(const EncodeArgs& a, hipStream_t stream) {
+  int dev = 0, cus = 256;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  switch (a.bq) {
+    case 1: return launch_waves<PROD, false, 1, F16IN, HAD, 8, true>(a, cus, stream);
+    case 2: return launch_waves<PROD, false, 2, F16IN, HAD, 8, true>(a, cus, stream);
+    case 3: return launch_waves<PROD, false, 3, F16IN, HAD, 8, true>(a, cus, stream);
+    case 4: return launch_waves<PROD, false, 4, F16IN, HAD, 8, true>(a, cus, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 // MSE-only keys: b index bits in the per-record layout
 template <bool F16IN, bool HAD>
 hipError_t launch_mse_keys(const EncodeArgs& a, hipStream_t stream) {
@@ -542,6 +584,10 @@ hipError_t launch_mse_keys(const EncodeArgs& a, hipStream_t stream) {
 
 template <bool HAD>
 hipError_t launch_rot(const EncodeArgs& a, hipStream_t stream) {
+  if (a.eden) {
+    if (a.prod) return a.f16_in ? launch_eden<true, true, HAD>(a, stream) : launch_eden<true, false, HAD>(a, stream);
+    return a.f16_in ? launch_eden<false, true, HAD>(a, stream) : launch_eden<false, false, HAD>(a, stream);
+  }
   if (a.prod && !a.qjl) return a.f16_in ? launch_mse_keys<true, HAD>(a, stream) : launch_mse_keys<false, HAD>(a, stream);
   if (a.prod) {
     if (a.f16_in) {

@@ -30,6 +30,7 @@ struct EncodeArgs {
   int bq;              // index bits
   int prod;            // 1: per-record key layout, 0: values (mse, token-blocked)
   int qjl;             // with prod: 1 = QJL signs and gamma (prod keys), 0 = MSE-only keys
+  int eden;            // MSE records: store n / <y, c[idx]> (EDEN's unbiased scale) instead of n
   int had;             // 1: sign-flipped Hadamard rotation (eps), 0: dense (pi)
   uint32_t* planes;    // [records][P][d_rot/32]
   uint16_t* scalars;   // [records][S] float16 bit patterns

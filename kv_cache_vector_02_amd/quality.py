@@ -14,8 +14,8 @@ table (cosine of the attention distributions and top-1 agreement at 2, 3 and
   uncompressed keys and values and tq_attend over their compressed records.
 
 The compressed side runs in libtq (tq_encode_prod, or tq_encode_mse_keys for
-a key quantizer without a QJL matrix; tq_encode_mse for values; tq_scores,
-tq_attend).  The exact side is float32 PyTorch on the same device (the
+a key quantizer without a QJL matrix; tq_encode_mse for values; with eden,
+tq_encode_eden for MSE keys and values; tq_scores, tq_attend).  The exact side is float32 PyTorch on the same device (the
 products, the softmax and the weighted sum), the yardstick the compressed
 results are measured against; none of it is on the hot path.  Argmax ties go
 to the lower key index.
@@ -37,10 +37,16 @@ def exact_scores(keys, queries):
     return queries.float() @ keys.float().t().contiguous()
 
 
-def encode_keys(kp: tq.Params, keys, seg_stride: int = 0) -> tq.Cache:
-    """Prod keys, or MSE-only keys when kp has no QJL matrix."""
+def encode_keys(kp: tq.Params, keys, seg_stride: int = 0, eden: bool = False) -> tq.Cache:
+    """Prod keys, or MSE-only keys when kp has no QJL matrix (with eden, scaled
+    by EDEN's unbiased n / <y, c[idx]>)."""
     cache = tq.alloc_cache(tq.key_layout(kp), keys.shape[0], seg_stride)
-    (tq.encode_prod if kp.s is not None else tq.encode_mse_keys)(kp, keys.contiguous(), cache)
+    if kp.s is not None:
+        tq.encode_prod(kp, keys.contiguous(), cache)
+    elif eden:
+        tq.encode_eden(kp, keys.contiguous(), cache, keys=True)
+    else:
+        tq.encode_mse_keys(kp, keys.contiguous(), cache)
     return cache
 
 
@@ -67,11 +73,11 @@ def fidelity(true_scores, est_scores, scale: float = 1.0):
     return cos, top1
 
 
-def attention_fidelity(kp: tq.Params, keys, queries, scale: float = 1.0):
+def attention_fidelity(kp: tq.Params, keys, queries, scale: float = 1.0, eden: bool = False):
     """Attention-fidelity statistics of one key set [N, d] under queries [Q, d].
 
     Returns a dict with the per-query cosine and top-1 agreement and their means."""
-    cache = encode_keys(kp, keys)
+    cache = encode_keys(kp, keys, eden=eden)
     est = estimated_scores(kp, cache, keys.shape[0], queries)
     true = exact_scores(keys, queries)
     cos, top1 = fidelity(true, est, scale)
@@ -89,13 +95,13 @@ def needle_scores(kp: tq.Params, cache: tq.Cache, queries, L: int):
     return est
 
 
-def needle(kp: tq.Params, haystacks, queries):
+def needle(kp: tq.Params, haystacks, queries, eden: bool = False):
     """Needle trials: haystacks [trials, L, d], one query [trials, d] each.
 
     Returns (found [trials] bool, exact argmax [trials], estimated argmax [trials])."""
     T = _torch()
     trials, L, d = haystacks.shape
-    cache = encode_keys(kp, haystacks.reshape(trials * L, d), seg_stride=L)
+    cache = encode_keys(kp, haystacks.reshape(trials * L, d), seg_stride=L, eden=eden)
     est = needle_scores(kp, cache, queries, L)
     true = T.bmm(haystacks.float(), queries.float()[:, :, None].contiguous())[:, :, 0]
     tb, eb = T.argmax(true, dim=-1), T.argmax(est, dim=-1)
@@ -124,16 +130,20 @@ def compressed_attention(kp: tq.Params, vp: tq.Params, kc: tq.Cache, vc: tq.Cach
     return out
 
 
-def output_fidelity(kp: tq.Params, vp: tq.Params, keys, values, queries, group: int, scale: float):
+def output_fidelity(kp: tq.Params, vp: tq.Params, keys, values, queries, group: int, scale: float,
+                    eden: bool = False):
     """Cosine per query head between exact attention and tq_attend over the compressed records.
 
     keys, values: [segs, L, d] device; queries [segs*group, d] float32.
     Returns (cosine [segs*group], exact output, compressed output)."""
     T = _torch()
     segs, L, d = keys.shape
-    kc = encode_keys(kp, keys.reshape(segs * L, d), seg_stride=L)
+    kc = encode_keys(kp, keys.reshape(segs * L, d), seg_stride=L, eden=eden)
     vc = tq.alloc_value_cache(tq.value_layout(vp), segs * L, seg_stride=L)
-    tq.encode_mse(vp, values.reshape(segs * L, d).contiguous(), vc)
+    if eden:
+        tq.encode_eden(vp, values.reshape(segs * L, d).contiguous(), vc, keys=False)
+    else:
+        tq.encode_mse(vp, values.reshape(segs * L, d).contiguous(), vc)
     out = compressed_attention(kp, vp, kc, vc, L, queries, group, scale)
     ref = exact_attention(keys, values, queries, group, scale)
     cos = T.nn.functional.cosine_similarity(ref.double(), out.double(), dim=-1)

@@ -15,7 +15,14 @@ definitions) and the explainer page (sections 6 and 8):
   decoder (explainer page section 8, the QJL encoder).  With b = 1 there is
   no MSE stage and r = y.
 
-Storage mode rounds n and gamma to float16 (round to nearest even), the
+* EDEN's per-vector scale (explainer page, section 0.9, the prior-work map:
+  EDEN stores S = ||x||^2 / <R x, Q(R x)> with its quantized rotated vector,
+  which makes the reconstruction S R^T Q unbiased; DRIVE's one-bit scale
+  ||x||^2 / ||R x||_1 is the same formula with Q = sign).  In this module's
+  unit-sphere notation, with y = Pi u and codebook c, the reconstruction is
+  S Pi^T c[idx] with S = n / <y, c[idx]> (0 for a zero vector).
+
+Storage mode rounds n, gamma and S to float16 (round to nearest even), the
 record format's precision; exact mode keeps them in float64.
 """
 from __future__ import annotations
@@ -66,6 +73,18 @@ def encode_mse(x, rot, centroids, boundaries, storage: bool = True) -> MseCode:
     y = rot.forward(u)
     idx = cell_index(y, boundaries)
     return MseCode(idx=idx, n=_store(n, storage), y=y)
+
+
+def encode_eden(x, rot, centroids, boundaries, storage: bool = True) -> MseCode:
+    """Q_mse codes with EDEN's scale in place of the norm: n = S = ||x|| / <y, c[idx]>."""
+    nrm, u = normalise(x)
+    y = rot.forward(u)
+    idx = cell_index(y, boundaries)
+    yc = np.sum(y * np.asarray(centroids, np.float64)[idx], axis=1)
+    scale = np.zeros_like(nrm)
+    ok = (nrm > 0) & (yc > 0)
+    scale[ok] = nrm[ok] / yc[ok]
+    return MseCode(idx=idx, n=_store(scale, storage), y=y)
 
 
 def encode_prod(x, rot, s_matrix, centroids, boundaries, storage: bool = True) -> ProdCode:

@@ -1,0 +1,107 @@
+"""GPU parity of tq_encode_eden: MSE codes with EDEN's unbiased per-vector scale
+S = n / <y, c[idx]> in place of the norm (explainer page section 0.9, the
+prior-work map; DRIVE's scale at one bit), in the per-record key layout and in
+the token-blocked value layout, against the oracle's encode_eden.
+
+Indices: exact except within 1e-5 of a boundary (at most 1e-4 of them).
+Scale: the GPU sums <y, c[idx]> in float32 (relative error ~1e-6), so its fp16
+rounding of S may differ from the oracle's by one unit in the last place, and
+only where the exact S lies within 1e-5 (relative) of an fp16 rounding
+midpoint; vectors with a boundary flip are excluded from that check."""
+import numpy as np
+import pytest
+
+import kv_cache_vector_02_amd as tq
+from oracle import estimator as est
+from oracle import packing as pk
+from oracle import quantizer as qz
+from tests.gpu_util import BOUNDARY_EPS, MAX_FLIP_FRAC, Setup, torch
+from tests.test_gpu_scores import check_rows, gpu_scores
+from tq_inputs import gaussian_queries, kv_tensor, tiny_vectors
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _near_mid(v, rel=1e-5):
+    v = np.asarray(v, np.float64)
+    h = v.astype(np.float16)
+    up = np.nextafter(h, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(h, np.float16(-np.inf)).astype(np.float64)
+    hv = h.astype(np.float64)
+    return (np.abs(v - (hv + up) / 2) <= rel * np.abs(v)) | (np.abs(v - (hv + dn) / 2) <= rel * np.abs(v))
+
+
+def check_eden(st, idx, s16, x):
+    """GPU indices idx [N, d] and fp16 scales s16 [N] against the oracle's EDEN code of x."""
+    oc = qz.encode_eden(np.asarray(x, np.float64), st.rot, st.c32, st.b32, storage=False)
+    mism = idx != oc.idx
+    if np.any(mism):
+        dist = np.min(np.abs(oc.y[..., None] - np.asarray(st.b32, np.float64)[None, None, :]), axis=-1)
+        assert np.all(dist[mism] < BOUNDARY_EPS)
+    assert mism.sum() <= max(1, MAX_FLIP_FRAC * mism.size)
+    ok = ~np.any(mism, axis=1)
+    g = np.asarray(s16, np.float16)
+    o = oc.n.astype(np.float16)
+    ulp = np.abs(g.view(np.int16).astype(np.int32) - o.view(np.int16).astype(np.int32))
+    bad = ok & ((ulp > 1) | ((ulp == 1) & ~_near_mid(oc.n)))
+    assert not np.any(bad), f"scale mismatch at {np.nonzero(bad)[0][:5]}"
+    return int(mism.sum()), int((ulp[ok] == 1).sum())
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("rot", ["dense", "hadamard"])
+def test_eden_keys(bits, rot):
+    _log(f"eden keys b{bits} {rot}: 1500 fp32 vectors (outlier channels, one zero vector)")
+    T = torch()
+    x = tiny_vectors(1500, 128, seed=31)
+    x[7] = 0.0
+    st = Setup(bits=bits, prod=False, rot=rot, seed=31)
+    cache = tq.alloc_cache(tq.key_layout(st.params), 1500)
+    tq.encode_eden(st.params, T.from_numpy(x).cuda(), cache, keys=True)
+    T.cuda.synchronize()
+    planes = cache.planes.cpu().numpy().view(np.uint32)
+    scal = cache.scalars.cpu().numpy()
+    idx = pk.unpack_value(planes, scal, bits)[0]
+    assert scal[7, 0] == 0.0
+    _log(f"  flips, scale ulps: {check_eden(st, idx, scal[:, 0], x)}")
+
+
+@pytest.mark.parametrize("bits", [1, 3, 4])
+@pytest.mark.parametrize("n,slots", [(4096, False), (1000, False), (700, True)])
+def test_eden_values(bits, n, slots):
+    # aligned blocks (ballot path), a ragged last block, and scattered slots
+    # (per-bit path); float16 input
+    _log(f"eden values b{bits}: {n} fp16 vectors, slots {slots}")
+    T = torch()
+    x = kv_tensor(1, 1, n, 128, seed=32, value=True)[0, 0]
+    st = Setup(bits=bits, prod=False, seed=32, purpose_pi=4, purpose_eps=6)
+    records = n + 64 if slots else n
+    slot = np.random.default_rng(32).permutation(records)[:n] if slots else np.arange(n)
+    cache = tq.alloc_value_cache(tq.value_layout(st.params), records)
+    sl = T.from_numpy(slot.astype(np.int64)).cuda() if slots else None
+    tq.encode_eden(st.params, T.from_numpy(x).cuda(), cache, keys=False, slot=sl)
+    T.cuda.synchronize()
+    idx = pk.unpack_value_blocks(cache.planes.cpu().numpy().view(np.uint32), records)[slot]
+    scal = cache.scalars.cpu().numpy()[slot, 0]
+    _log(f"  flips, scale ulps: {check_eden(st, idx, scal, x.astype(np.float64))}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_scores_read_the_eden_scale(bits):
+    # oracle-encoded EDEN key records through tq_scores: S <Pi q, c[idx]>
+    _log(f"eden keys scores b{bits}")
+    T = torch()
+    x = kv_tensor(1, 2, 600, 128, seed=33)[0].reshape(-1, 128)
+    st = Setup(bits=bits, prod=False, seed=33)
+    code = qz.encode_eden(x.astype(np.float64), st.rot, st.c32, st.b32)
+    planes, scal = pk.pack_value(code, bits)
+    cache = tq.Cache(T.from_numpy(planes.view(np.int32)).cuda(), T.from_numpy(scal).cuda(), 600)
+    q = gaussian_queries(8, 128, seed=33)
+    got = gpu_scores(st, q, 2, 4, cache, 600)
+    for s in range(2):
+        sl = slice(600 * s, 600 * (s + 1))
+        check_rows(got[4 * s:4 * s + 4], est.mse_scores(q[4 * s:4 * s + 4], code.idx[sl], code.n[sl], st.rot, st.c32))

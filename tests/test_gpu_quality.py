@@ -23,6 +23,7 @@ import kv_cache_vector_02_amd as tq
 from kv_cache_vector_02_amd import quality
 from oracle import estimator as est
 from oracle import quality as oq
+from oracle import quantizer as qz
 from tests.gpu_util import Setup, torch
 from tests.test_gpu_attend import oracle_value_cache
 from tests.test_gpu_scores import oracle_key_cache
@@ -97,16 +98,18 @@ def test_end_to_end_fidelity_with_gpu_encode(bits):
          f"(oracle {top1_o.mean():.2f})")
 
 
+@pytest.mark.parametrize("eden", [False, True])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_end_to_end_fidelity_mse_keys(bits):
-    # MSE-only keys at b index bits (no QJL matrix): GPU encode + scores,
-    # against the oracle's MSE encoder and biased inner product
-    _log(f"quality end-to-end, MSE-only keys b{bits}")
+def test_end_to_end_fidelity_mse_keys(bits, eden):
+    # MSE-only keys at b index bits (no QJL matrix), scaled by the norm or by
+    # EDEN's unbiased scale: GPU encode + scores, against the oracle's encoder
+    # and inner product
+    _log(f"quality end-to-end, MSE-only keys b{bits} eden {eden}")
     keys = unit_gaussian(2048, 128, seed=12)
     qs = unit_gaussian(100, 128, seed=12, purpose=QUERIES)
     st = Setup(bits=bits, prod=False, seed=12)
-    r = quality.attention_fidelity(st.params, _dev(keys), _dev(qs))
-    code = st.encode_oracle(keys)
+    r = quality.attention_fidelity(st.params, _dev(keys), _dev(qs), eden=eden)
+    code = (qz.encode_eden(keys, st.rot, st.c32, st.b32, storage=False) if eden else st.encode_oracle(keys))
     est_o = est.mse_scores(qs, code.idx, code.n.astype(np.float16).astype(np.float64), st.rot, st.c32)
     cos_o, top1_o = oq.attention_fidelity(qs.astype(np.float64) @ keys.astype(np.float64).T, est_o)
     cos = r["cosine"].cpu().numpy()

@@ -142,3 +142,60 @@ def test_value_blocks_hand_built_and_roundtrip():
     rg = np.random.default_rng(4)
     r = rg.integers(0, 8, size=(77, 128))
     assert np.array_equal(pk.unpack_value_blocks(pk.pack_value_blocks(r, 3), 77), r)
+
+
+def _eden_recon(code, rot, c):
+    return code.n[:, None] * rot.inverse(np.asarray(c, np.float64)[code.idx])
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_eden_reconstruction_has_exact_projection_on_x(bits):
+    # <x, S Pi^T c[idx]> = S <Pi x, c[idx]> = ||x||^2 (the scale's definition,
+    # explainer page section 0.9, EDEN), for every vector and rotation
+    d = 64
+    rg = np.random.default_rng(bits)
+    x = rg.standard_normal((50, d)) * rg.uniform(0.1, 10, size=(50, 1))
+    rot = tr.DenseRotation(haar_orthogonal(d, 3, 2))
+    c, b = cb.lloyd_max(d, bits)
+    code = qz.encode_eden(x, rot, c, b, storage=False)
+    xh = _eden_recon(code, rot, c)
+    np.testing.assert_allclose(np.sum(x * xh, axis=1), np.sum(x * x, axis=1), rtol=1e-12)
+
+
+def test_eden_one_bit_is_drive_unbiased_scale():
+    # at one bit c[idx] = +-c1 sign(y): S c1 = ||x||^2 / ||Pi x||_1 (DRIVE's unbiased scale)
+    d = 32
+    x = np.random.default_rng(5).standard_normal((20, d)) * 3.0
+    rot = tr.DenseRotation(haar_orthogonal(d, 4, 2))
+    c, b = cb.lloyd_max(d, 1)
+    code = qz.encode_eden(x, rot, c, b, storage=False)
+    drive = np.sum(x * x, axis=1) / np.sum(np.abs(x @ haar_orthogonal(d, 4, 2).astype(np.float64).T), axis=1)
+    np.testing.assert_allclose(code.n * c[1], drive, rtol=1e-12)
+
+
+def test_eden_reconstruction_unbiased_over_rotations():
+    # E over uniformly random rotations of S Pi^T c[idx] is x (EDEN's
+    # unbiasedness); 3000 Haar rotations at d = 16, b = 2: each coordinate of
+    # the mean within 4 standard errors of x
+    d, trials = 16, 3000
+    x = np.random.default_rng(7).standard_normal((1, d))
+    c, b = cb.lloyd_max(d, 2)
+    recs = []
+    for t in range(trials):
+        rot = tr.DenseRotation(haar_orthogonal(d, 1000 + t, 2))
+        recs.append(_eden_recon(qz.encode_eden(x, rot, c, b, storage=False), rot, c)[0])
+    recs = np.array(recs)
+    mean, se = recs.mean(0), recs.std(0, ddof=1) / np.sqrt(trials)
+    assert np.all(np.abs(mean - x[0]) < 4 * se), np.max(np.abs(mean - x[0]) / se)
+    # the plain MSE reconstruction n Pi^T c[idx] is shrunk: its mean falls short of x
+    mse = np.array([_eden_recon(qz.encode_mse(x, tr.DenseRotation(haar_orthogonal(d, 1000 + t, 2)), c, b,
+                                              storage=False), tr.DenseRotation(haar_orthogonal(d, 1000 + t, 2)), c)[0]
+                    for t in range(200)])
+    assert mse.mean(0) @ x[0] < 0.97 * (x[0] @ x[0])
+
+
+def test_eden_zero_vector():
+    rot = tr.DenseRotation(haar_orthogonal(8, 1, 2))
+    c, b = cb.lloyd_max(8, 2)
+    code = qz.encode_eden(np.zeros((1, 8)), rot, c, b)
+    assert code.n[0] == 0.0
