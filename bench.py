@@ -134,6 +134,48 @@ def large_cache_scores(torch, tq, pk_, ev):
     }
 
 
+def half_projection_line(torch, tq, k_dev, q, ev):
+    """The score pass over the Qwen-shaped keys with m = d / 2 = 64 QJL rows
+    (the first page's proj_dim = head_dim / 2): 44-byte key records at b = 3
+    instead of 52.  Timed like the main line: bursts of back-to-back passes over
+    12 cache copies (311 MB, past the 256 MB memory-side cache)."""
+    from tq_inputs import gaussian_matrix, haar_orthogonal
+    segs, N = L_ * H_, L_ * H_ * T_
+    c, b = tq.build_codebook(D_, BITS - 1)
+    kp = tq.Params(d=D_, m=D_ // 2, bits=BITS, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b,
+                   pi=torch.from_numpy(haar_orthogonal(D_, SEED, 2)).cuda(),
+                   s=torch.from_numpy(gaussian_matrix(D_ // 2, D_, SEED, 3)).cuda())
+    one = tq.alloc_key_cache(kp, N, seg_stride=T_)
+    tq.encode_prod(kp, k_dev, one)
+    burst = 12
+    kb = [tq.Cache(one.planes.clone(), one.scalars.clone(), T_) for _ in range(burst)]
+    del one
+    out = torch.empty((segs * G_, T_), dtype=torch.float32, device="cuda")
+    ws = tq.alloc_workspace(tq.scores_workspace(kp, segs, G_))
+    tq.scores_prepare(kp, q, segs, G_, ws)
+    per = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(2_000_000)
+        e0, e1 = ev(), ev()
+        e0.record()
+        for i in range(burst):
+            tq.scores_prepared(kp, segs, G_, kb[i], T_, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / burst)
+    t = float(np.median(per))
+    rec = 4 * tq.key_record_words(kp) + 4
+    pass_bytes = N * rec + segs * G_ * T_ * 4
+    del kb, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": "qwen2.5-3b-shaped keys (72 segments x 8192 tokens), prod b=3 with m = 64 QJL rows, G = 8",
+            "key_record_bytes": rec, "score_pass_ms": round(t, 5),
+            "score_pass_GBps": round(pass_bytes / (t * 1e-3) / 1e9, 1),
+            "score_pass_frac_hbm_peak": round(pass_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_pass": pass_bytes}
+
+
 def batched_decode_line(torch, tq, pk_, pv_, ev):
     """One serving step of a batched decode: 64 sequences x 8 KV heads x 8192
     cached tokens (keys prod b = 3, values mse b = 3), 32 query heads per
@@ -299,8 +341,8 @@ def quality_report(torch, tq):
     queries, d = 128, temperature 1), needle trials (20 haystacks of 8192 random
     unit keys), and the cosine of tq_attend's output to exact attention over
     decoder-shaped keys and values (4 segments x 2048 tokens, 8 query heads
-    each, temperature 1/sqrt(d)).  Keys prod (b-1 MSE bits + 1 QJL bit, m = d)
-    and, for comparison at equal bits, MSE-only (b index bits), plain or with
+    each, temperature 1/sqrt(d)).  Keys prod (b-1 MSE bits + 1 QJL bit, m = d,
+    and m = d / 2 as the page's examples use) and, for comparison at equal bits, MSE-only (b index bits), plain or with
     EDEN's unbiased per-vector scale (then on the values too); values MSE at b
     bits."""
     from kv_cache_vector_02_amd import quality
@@ -322,12 +364,19 @@ def quality_report(torch, tq):
     xv = dev(kv_tensor(1, 4, 2048, D_, seed=14, value=True)[0])
     oq = dev(gaussian_queries(32, D_, seed=14))
     rows = []
-    for keys_kind in ("prod", "mse", "eden"):
-        prod = keys_kind == "prod"
+    for keys_kind in ("prod", "prod_m64", "mse", "eden"):
+        prod = keys_kind.startswith("prod")
         eden = keys_kind == "eden"
 
         def kparams(bits, seed):
             # MSE-only keys: b index bits and no QJL matrix, the keys' rotation stream
+            if keys_kind == "prod_m64":
+                # m = d / 2 QJL rows (the first page's proj_dim = head_dim / 2)
+                c, b = tq.build_codebook(D_, bits - 1)
+                pi = torch.from_numpy(haar_orthogonal(D_, seed, 2)).cuda()
+                s = torch.from_numpy(gaussian_matrix(D_ // 2, D_, seed, 3)).cuda()
+                return tq.Params(d=D_, m=D_ // 2, bits=bits, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b,
+                                 pi=pi, s=s)
             if prod:
                 return params(bits, True, seed)
             c, b = tq.build_codebook(D_, bits)
@@ -564,6 +613,7 @@ def main():
         result["large_cache"] = large_cache_scores(torch, tq, pk_, ev)
         result["large_cache"]["score_pass_frac_of_measured_copy"] = round(
             result["large_cache"]["score_pass_GBps"] / copy_gbs, 4)
+    result["half_projection"] = half_projection_line(torch, tq, kx[0], q, ev)
     if not args.skip_batched:
         result["batched_decode"] = batched_decode_line(torch, tq, pk_, pv_, ev)
     if not args.skip_retrieval:

@@ -71,7 +71,9 @@ typedef enum { TQ_LAYOUT_BLOCKS = 0, TQ_LAYOUT_RECORDS = 1 } tq_layout;
  *   d       input dimension
  *   d_rot   rotated dimension: == d for the dense rotation; a power of two
  *           >= d for the Hadamard rotation (inputs are zero-padded at the end)
- *   m       QJL projection rows; must equal d_rot (prod only, else ignored)
+ *   m       QJL projection rows (prod only, else ignored): d_rot, or d_rot / 2
+ *           at d_rot = 128 (the first page's proj_dim = head_dim / 2; encode,
+ *           tq_scores and tq_attend; tq_scores_topk needs m = d_rot)
  *   bits    total bit budget b: prod uses b-1 index bits plus 1 QJL bit
  *           (2 <= b <= 4), mse uses b index bits (1 <= b <= 4)
  *   rot     TQ_ROT_DENSE or TQ_ROT_HADAMARD
@@ -120,9 +122,18 @@ tq_status tq_build_codebook(int d, int bits, double* centroids, double* boundari
 
 /* Number of 32-bit plane words and float16 scalars in one record.  For a key
  * quantizer without a QJL matrix (s == NULL) tq_key_layout describes MSE-only
- * key records: b planes and one scalar. */
+ * key records: b planes and one scalar.  With m = d_rot / 2 QJL rows the sign
+ * plane has m / 32 words (see tq_key_record_words). */
 tq_status tq_key_layout(const tq_params* p, int* planes, int* words_per_plane, int* scalars);
 tq_status tq_value_layout(const tq_params* p, int* planes, int* words_per_plane, int* scalars);
+
+/* 32-bit words of one key record, 0 for invalid parameters.  A prod record
+ * holds, for each group of 32 coordinates w = 0 .. d_rot/32 - 1, the b-1 index
+ * words of the group and then sign word w if w < m/32 (the first page's
+ * proj_dim = head_dim / 2 default gives m/32 = 2 at d = 128: 40 bytes of
+ * words at b = 3 instead of 48); with m = d_rot this is the interleaved layout
+ * above.  MSE-only key records hold b words per group. */
+size_t tq_key_record_words(const tq_params* p);
 
 /* TurboQuant-prod encode of n vectors (keys) into a packed cache.
  * Blog notes on the paper, the Q_prod definition; explainer page section 8:

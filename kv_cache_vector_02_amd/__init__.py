@@ -24,7 +24,7 @@ TQ_LAYOUT_BLOCKS, TQ_LAYOUT_RECORDS = 0, 1
 
 EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
-    "tq_value_layout", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_eden", "tq_encode_workspace", "tq_encode_prod_ws",
+    "tq_value_layout", "tq_key_record_words", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_eden", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
     "tq_debug_set_pack_wait",
@@ -72,6 +72,8 @@ def lib():
         L.tq_build_codebook.argtypes = [ci, ci, vp, vp]
         L.tq_key_layout.argtypes = [P, vp, vp, vp]
         L.tq_value_layout.argtypes = [P, vp, vp, vp]
+        L.tq_key_record_words.restype = sz
+        L.tq_key_record_words.argtypes = [P]
         for f in (L.tq_encode_prod, L.tq_encode_mse, L.tq_encode_mse_keys):
             f.argtypes = [P, vp, ci, i64, i64, tq_cache, vp, vp]
         L.tq_encode_eden.argtypes = [P, vp, ci, i64, i64, ci, tq_cache, vp, vp]
@@ -93,7 +95,7 @@ def lib():
         L.tq_debug_set_pack_wait.restype = None
         L.tq_debug_set_pack_wait.argtypes = [ci]
         for name in EXPORTED:
-            if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace",
+            if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace", "tq_key_record_words",
                             "tq_attend_workspace", "tq_encode_workspace", "tq_scores_topk_workspace",
                             "tq_debug_set_pack_wait"):
                 getattr(L, name).restype = ci
@@ -186,6 +188,26 @@ def alloc_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
     import torch
     P, W, S = layout
     return Cache(torch.zeros((records, W, P), dtype=torch.int32, device=device),
+                 torch.zeros((records, S), dtype=torch.float16, device=device), seg_stride)
+
+
+def key_record_words(p: Params) -> int:
+    """32-bit words of one key record (tq_key_record_words)."""
+    w = int(lib().tq_key_record_words(p.c))
+    if w == 0:
+        _check(lib().tq_key_layout(p.c, None, None, None))
+    return w
+
+
+def alloc_key_cache(p: Params, records: int, seg_stride: int = 0, device="cuda"):
+    """A key cache for p's records: [records, W, P] words when every coordinate
+    group carries the same planes, else (m = d / 2) [records, words]."""
+    import torch
+    P, W, S = key_layout(p)
+    words = key_record_words(p)
+    if words == P * W:
+        return alloc_cache((P, W, S), records, seg_stride, device)
+    return Cache(torch.zeros((records, words), dtype=torch.int32, device=device),
                  torch.zeros((records, S), dtype=torch.float16, device=device), seg_stride)
 
 

@@ -50,7 +50,8 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
   if (prod) {
     if (p->bits < 2 || p->bits > 4)
       return fail(TQ_ERR_INVALID_ARG, "prod bits must be in [2, 4] (got %d)", p->bits);
-    if (p->m != p->d_rot) return fail(TQ_ERR_INVALID_ARG, "m must equal d_rot");
+    if (p->m != p->d_rot && !(p->d_rot == 128 && p->m == 64))
+      return fail(TQ_ERR_INVALID_ARG, "m must equal d_rot, or be 64 at d_rot = 128 (got m = %d)", p->m);
     if (!p->s) return fail(TQ_ERR_INVALID_ARG, "prod needs the QJL matrix s");
     if (!aligned(p->s, 16)) return fail(TQ_ERR_INVALID_ARG, "s must be 16-byte aligned");
   } else if (p->bits < 1 || p->bits > 4) {
@@ -115,6 +116,7 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   a.bq = index_bits(p, prod);
   a.prod = prod || mse_keys;
   a.qjl = prod;
+  a.m = prod ? p->m : 0;
   a.eden = eden;
   if (eden && !(p->d == 128 && p->d_rot == 128))
     return fail(TQ_ERR_UNSUPPORTED, "tq_encode_eden supports d = d_rot = 128 (got %d, %d)", p->d, p->d_rot);
@@ -126,6 +128,7 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   if (p->d == 128 && p->d_rot == 128)
     return hip_status(tq::launch_encode_dense128(a, s), "encode launch");
   if (prod && p->rot == TQ_ROT_HADAMARD && p->d_rot == 2048) {
+    if (p->m != p->d_rot) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs m = d_rot");
     if (p->d % 8) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs d a multiple of 8 (got %d)", p->d);
     const size_t need = tq::encode2k_workspace(n);
     if (!ws) return fail(TQ_ERR_INVALID_ARG, "d_rot = 2048 encode needs a workspace (tq_encode_prod_ws)");
@@ -174,6 +177,14 @@ tq_status tq_key_layout(const tq_params* p, int* planes, int* words, int* scalar
   if (words) *words = p->d_rot / 32;
   if (scalars) *scalars = qjl ? 2 : 1;
   return TQ_OK;
+}
+
+size_t tq_key_record_words(const tq_params* p) {
+  tq::Codebook cb;
+  const bool qjl = p && p->s;
+  if (check_params(p, qjl, &cb, false) != TQ_OK) return 0;
+  const int w = p->d_rot / 32;
+  return qjl ? (size_t)w * (p->bits - 1) + p->m / 32 : (size_t)w * p->bits;
 }
 
 tq_status tq_value_layout(const tq_params* p, int* planes, int* words, int* scalars) {
@@ -262,6 +273,7 @@ static tq_status score_args(const tq_params* kp, const float* q, bool need_q, in
   a->eps = kp->eps;
   a->rot = kp->rot;
   a->s = kp->s;
+  a->m = qjl ? kp->m : 0;
   a->bq = qjl ? kp->bits - 1 : kp->bits;
   a->qjl = qjl;
   a->planes = (const uint32_t*)keys.planes;
@@ -327,6 +339,8 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   if (kp->d != 128 || kp->d_rot != 128 || vp->d != 128 || vp->d_rot != 128)
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports d = d_rot = 128 for keys and values");
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports up to 16 query heads per segment");
+  if (qjl && kp->m != kp->d_rot && vp->bits < 2)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attend with m = d / 2 keys supports value bits 2..4");
   if (!qjl && (kp->bits < 2 || vp->bits < 2))
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend with MSE-only keys supports key and value bits 2..4");
   if (!qjl && kp->bits == 4 && group > 8)
@@ -354,6 +368,7 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   a.k.eps = kp->eps;
   a.k.rot = kp->rot;
   a.k.s = kp->s;
+  a.k.m = qjl ? kp->m : 0;
   a.k.bq = qjl ? kp->bits - 1 : kp->bits;
   a.k.qjl = qjl;
   a.k.planes = (const uint32_t*)keys.planes;

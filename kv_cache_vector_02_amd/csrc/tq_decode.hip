@@ -142,7 +142,9 @@ struct PrepLds {
 // number of base-256 digits per weight; CPOL the cache policy of the pack's
 // stores (the one-launch scores write it device-coherent for the workgroups
 // of other XCDs).
-template <bool HAD, int S, int CPOL = 0, bool QJL = true>
+// MW: QJL sign words per key (m / 32); with MW = 2 the QJL rows past 64 are
+// zero, so the pack's QJL weights for coordinate groups 2 and 3 vanish.
+template <bool HAD, int S, int CPOL = 0, bool QJL = true, int MW = 4>
 __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L, uint8_t* dst) {
   float* qr = L.qr;
   float* qp = L.qp;
@@ -168,7 +170,10 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   if (qh < G) qv = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + qh) * D)[q4];
   const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)(HAD ? 0 : row) * D);
   // MSE-only keys have no QJL matrix: its rows read as zeros (q_proj = 0)
-  const float4* srow = reinterpret_cast<const float4*>(QJL ? a.s + (size_t)row * D : a.pi);
+  // (with m = d / 2, rows from 64 on read as zeros)
+  const bool srow_live = MW == 4 || row < 32 * MW;
+  const float4* srow =
+      reinterpret_cast<const float4*>(QJL ? a.s + (size_t)(MW == 4 ? row : srow_live ? row : 0) * D : a.pi);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int k4a = 8 * ks + 2 * kq, k4b = k4a + 1;      // coordinates 32 ks + 8 kq + 0..7
@@ -179,9 +184,12 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
       mv[2 * ks] = prow[k4a];
       mv[2 * ks + 1] = prow[k4b];
     }
-    if constexpr (QJL) {
+    if constexpr (QJL && MW == 4) {
       sv[2 * ks] = srow[k4a];
       sv[2 * ks + 1] = srow[k4b];
+    } else if constexpr (QJL) {
+      sv[2 * ks] = srow_live ? srow[k4a] : float4{0.f, 0.f, 0.f, 0.f};
+      sv[2 * ks + 1] = srow_live ? srow[k4b] : float4{0.f, 0.f, 0.f, 0.f};
     } else {
       sv[2 * ks] = sv[2 * ks + 1] = float4{0.f, 0.f, 0.f, 0.f};
     }
@@ -339,12 +347,12 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
 
 // (at most two waves per SIMD: the register budget keeps every operand load
 // of a lane in flight at once)
-template <bool HAD, int S, bool QJL>
+template <bool HAD, int S, bool QJL, int MW = 4>
 __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void prep_queries128(PrepArgs a) {
   __shared__ PrepLds L;
   const int F = 2 * (mse_planes(a.bq) + (QJL ? 1 : 0));
-  prep_pack<HAD, S, 0, QJL>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
+  prep_pack<HAD, S, 0, QJL, MW>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
 }
 
 // One-launch scores: the first workgroup of each segment builds the query
@@ -436,6 +444,17 @@ __device__ __forceinline__ float mse_digits(i32x4 acc) {
   else return (float)combine3(acc);
 }
 
+// m = d / 2 records: for the lanes of coordinate groups 2 and 3 (late),
+// words loaded one early -> index words in slots 0 .. P-2, the early word in
+// the sign slot P-1.
+template <int P, typename W>
+__device__ __forceinline__ W rotate_late_groups(W w, bool late) {
+  W r;
+#pragma unroll
+  for (int i = 0; i < P; ++i) r[i] = late ? w[(i + 1) % P] : w[i];
+  return r;
+}
+
 // Word of Walsh plane p (plane_subset order) of an MSE-only key record: a
 // single index bit, or the parity of the subset's bits.  (The prod kernels
 // spell the same selection out inline, QJL signs at p == NP.)
@@ -462,14 +481,19 @@ constexpr int SC_WAVES = 8;
 // consumers); HAD selects the producer's rotation.  QJL: prod keys (BQ index
 // planes, the sign plane, n and gamma); without it MSE-only keys (BQ index
 // planes and n).
-template <int BQ, int MT, int S, bool FUSED, bool HAD, bool QJL>
+// MW: QJL sign words per record (m / 32).  With MW = 2 (m = d / 2) the record
+// has no sign word in coordinate groups 2 and 3: their lanes load the P words
+// that end with the group's last index word (the first is the previous
+// group's last word) and rotate them into place; the sign slot then holds
+// that foreign word, and the pack's QJL weights for these groups are zero.
+template <int BQ, int MT, int S, bool FUSED, bool HAD, bool QJL, int MW = 4>
 __global__ __launch_bounds__(SC_WAVES * 64) __attribute__((amdgpu_waves_per_eu(FUSED && MT == 1 ? 4 : 1)))
 void scores128(Score128Args a) {
   constexpr int NP = mse_planes(BQ);      // Walsh planes of the index bits
   constexpr int F = 2 * (NP + QJL);       // MFMAs per tile per 16-row tile
-  constexpr int P = BQ + QJL;             // stored planes per key record
+  constexpr int P = BQ + QJL;             // planes per coordinate group (words a lane loads)
   constexpr int SB = QJL ? 4 : 2;         // scalar bytes per key record
-  constexpr uint32_t RB = 16 * P;         // plane bytes per key record
+  constexpr uint32_t RB = MW == 4 ? 16 * P : 4 * (4 * BQ + MW);   // plane bytes per key record
   constexpr int RING = 4;                 // pairs of loads in flight per wave
   constexpr int ROUND = 8;                // pairs per straight-line round
   constexpr int HL = S == 2 ? 2 : 1;      // heads per lane group per 16-row tile
@@ -491,8 +515,8 @@ void scores128(Score128Args a) {
     if (b < a.prep.segs) {
       // producer of segment b: the pack with device-coherent stores, every
       // store complete, then the flag
-      prep_pack<HAD, S, CPOL_SC1, QJL>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
-                                       a.prep.ws + (size_t)b * pack_bytes(MT, F));
+      prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
+                                           a.prep.ws + (size_t)b * pack_bytes(MT, F));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -517,11 +541,11 @@ void scores128(Score128Args a) {
   }
 
   const int64_t rec0 = seg * a.seg_stride + tok0;
-  const rsrc_t rk = make_rsrc(a.planes + rec0 * (P * 4), clamp_bytes((a.seg_stride - tok0) * RB));
+  const rsrc_t rk = make_rsrc(a.planes + rec0 * (RB / 4), clamp_bytes((a.seg_stride - tok0) * RB));
   const rsrc_t rs = make_rsrc(a.scalars + rec0 * (SB / 2), clamp_bytes((a.seg_stride - tok0) * SB));
   const rsrc_t ro = make_rsrc(a.scores + (size_t)seg * a.group * a.T + tok0,
                               clamp_bytes(((int64_t)(a.group - 1) * a.T + a.T - tok0) * 4));
-  const uint32_t vk = t16 * RB + kg * (P * 4);
+  const uint32_t vk = t16 * RB + (MW == 4 ? kg * (P * 4) : (kg < 2 ? kg * P : kg * BQ + 1) * 4);
   const uint32_t vs = t16 * SB;
   const int ntok = (int)(len - tok0 < (int64_t)a.chunk_tiles * 16 ? len - tok0 : (int64_t)a.chunk_tiles * 16);
   const int npairs = (ntok + 31) / 32;
@@ -556,7 +580,8 @@ void scores128(Score128Args a) {
     if (!*got) {
       // no pack within the wait: build it here (the same bytes the producer
       // writes), then request the first keys again
-      prep_pack<HAD, S, CPOL_SC1, QJL>(a.prep, seg, *reinterpret_cast<PrepLds*>(smem), const_cast<uint8_t*>(pack));
+      prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, seg, *reinterpret_cast<PrepLds*>(smem),
+                                           const_cast<uint8_t*>(pack));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
 #pragma unroll
@@ -609,6 +634,7 @@ void scores128(Score128Args a) {
 
   // one 16-token tile -> LDS rows (heads 4 mt + kg), columns col0 + t16
   auto compute = [&](wvec w, uint32_t scl, int col0) {
+    if constexpr (MW == 2) w = rotate_late_groups<P>(w, kg >= 2);
     i32x4 am[MT], aq[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
@@ -703,30 +729,30 @@ int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax
 
 // Grid: (workgroups per segment, segments), sized so that the whole grid is
 // resident at once; a workgroup's span is a multiple of 8 waves x 32 tokens.
-template <int BQ, int MT, int S, bool QJL = true>
+template <int BQ, int MT, int S, bool QJL = true, int MW = 4>
 hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
   static const int nb =
-      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false, QJL>), SC_WAVES * 64);
+      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false, QJL, MW>), SC_WAVES * 64);
   const int64_t span = split_span(segs, s.T, nb * device_cus(), 32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   const int64_t chunks = (s.T + span - 1) / span;
-  hipLaunchKernelGGL((scores128<BQ, MT, S, false, false, QJL>), dim3((unsigned)chunks, (unsigned)segs),
+  hipLaunchKernelGGL((scores128<BQ, MT, S, false, false, QJL, MW>), dim3((unsigned)chunks, (unsigned)segs),
                      dim3(SC_WAVES * 64), 0, stream, s);
   return hipGetLastError();
 }
 
 // One-launch form: the producers take one resident slot per segment, the
 // consumers split the tokens over the rest.
-template <int BQ, int MT, int S, bool HAD, bool QJL = true>
+template <int BQ, int MT, int S, bool HAD, bool QJL = true, int MW = 4>
 hipError_t launch_scores_fused(Score128Args& s, int segs, hipStream_t stream) {
   static const int nb =
-      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, true, HAD, QJL>), SC_WAVES * 64);
+      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, true, HAD, QJL, MW>), SC_WAVES * 64);
   const int resident = nb * device_cus() - segs;
   const int64_t span = split_span(segs, s.T, resident > segs ? resident : segs, 32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   s.chunks = (int)((s.T + span - 1) / span);
   const int64_t nwg = (int64_t)segs * (s.chunks + 1);
-  hipLaunchKernelGGL((scores128<BQ, MT, S, true, HAD, QJL>), dim3((unsigned)nwg), dim3(SC_WAVES * 64), 0, stream,
+  hipLaunchKernelGGL((scores128<BQ, MT, S, true, HAD, QJL, MW>), dim3((unsigned)nwg), dim3(SC_WAVES * 64), 0, stream,
                      s);
   return hipGetLastError();
 }
@@ -840,6 +866,15 @@ hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t str
   const PrepArgs p = make_prep(a, slices);
   const bool had = a.rot == TQ_ROT_HADAMARD;
   const dim3 grid(a.segs), block(PREP_THREADS);
+  if (a.qjl && a.m == D / 2) {
+    switch ((slices == 2 ? 0 : 2) + (had ? 1 : 0)) {
+      case 0: hipLaunchKernelGGL((prep_queries128<false, 2, true, 2>), grid, block, 0, stream, p); break;
+      case 1: hipLaunchKernelGGL((prep_queries128<true, 2, true, 2>), grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((prep_queries128<false, 3, true, 2>), grid, block, 0, stream, p); break;
+      case 3: hipLaunchKernelGGL((prep_queries128<true, 3, true, 2>), grid, block, 0, stream, p); break;
+    }
+    return hipGetLastError();
+  }
   switch ((slices == 2 ? 0 : 4) + (had ? 2 : 0) + (a.qjl ? 1 : 0)) {
     case 0: hipLaunchKernelGGL((prep_queries128<false, 2, false>), grid, block, 0, stream, p); break;
     case 1: hipLaunchKernelGGL((prep_queries128<false, 2, true>), grid, block, 0, stream, p); break;
@@ -862,7 +897,7 @@ static Score128Args score_pass_args(const ScoreArgs& a) {
   s.len = a.len;
   s.T = a.T;
   s.group = a.group;
-  s.kappa = (float)(std::sqrt(M_PI / 2.0) / D);
+  s.kappa = (float)(std::sqrt(M_PI / 2.0) / (a.qjl ? a.m : D));
   s.scores = a.scores;
   s.chunk_tiles = 0;   // set by the launcher
   return s;
@@ -877,6 +912,28 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
   s.ticket = next_ticket();
   s.wait_ticks = 100LL * g_pack_wait_us.load(std::memory_order_relaxed);   // 100 MHz clock
   const bool had = a.rot == TQ_ROT_HADAMARD;
+  if (a.qjl && a.m == D / 2) {
+    // prod keys with m = d / 2 QJL rows
+    switch (a.bq * 100 + mt * 10 + (had ? 1 : 0)) {
+      case 110: return launch_scores_fused<1, 1, 2, false, true, 2>(s, a.segs, stream);
+      case 111: return launch_scores_fused<1, 1, 2, true, true, 2>(s, a.segs, stream);
+      case 120: return launch_scores_fused<1, 2, 2, false, true, 2>(s, a.segs, stream);
+      case 121: return launch_scores_fused<1, 2, 2, true, true, 2>(s, a.segs, stream);
+      case 210: return launch_scores_fused<2, 1, 2, false, true, 2>(s, a.segs, stream);
+      case 211: return launch_scores_fused<2, 1, 2, true, true, 2>(s, a.segs, stream);
+      case 220: return launch_scores_fused<2, 2, 2, false, true, 2>(s, a.segs, stream);
+      case 221: return launch_scores_fused<2, 2, 2, true, true, 2>(s, a.segs, stream);
+      case 310: return launch_scores_fused<3, 1, 3, false, true, 2>(s, a.segs, stream);
+      case 311: return launch_scores_fused<3, 1, 3, true, true, 2>(s, a.segs, stream);
+      case 320: return launch_scores_fused<3, 2, 3, false, true, 2>(s, a.segs, stream);
+      case 321: return launch_scores_fused<3, 2, 3, true, true, 2>(s, a.segs, stream);
+      case 330: return launch_scores_fused<3, 3, 3, false, true, 2>(s, a.segs, stream);
+      case 331: return launch_scores_fused<3, 3, 3, true, true, 2>(s, a.segs, stream);
+      case 340: return launch_scores_fused<3, 4, 3, false, true, 2>(s, a.segs, stream);
+      case 341: return launch_scores_fused<3, 4, 3, true, true, 2>(s, a.segs, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   if (!a.qjl) {
     switch (a.bq * 100 + mt * 10 + (had ? 1 : 0)) {
       case 110: return launch_scores_fused<1, 1, 2, false, false>(s, a.segs, stream);
@@ -927,6 +984,19 @@ hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream) {
   const int slices = score_slices(a);
   const int mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   Score128Args s = score_pass_args(a);
+  if (a.qjl && a.m == D / 2) {
+    switch (a.bq * 10 + mt) {
+      case 11: return launch_scores<1, 1, 2, true, 2>(s, a.segs, stream);
+      case 12: return launch_scores<1, 2, 2, true, 2>(s, a.segs, stream);
+      case 21: return launch_scores<2, 1, 2, true, 2>(s, a.segs, stream);
+      case 22: return launch_scores<2, 2, 2, true, 2>(s, a.segs, stream);
+      case 31: return launch_scores<3, 1, 3, true, 2>(s, a.segs, stream);
+      case 32: return launch_scores<3, 2, 3, true, 2>(s, a.segs, stream);
+      case 33: return launch_scores<3, 3, 3, true, 2>(s, a.segs, stream);
+      case 34: return launch_scores<3, 4, 3, true, 2>(s, a.segs, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   if (!a.qjl) {
     switch (a.bq * 10 + mt) {
       case 11: return launch_scores<1, 1, 2, false>(s, a.segs, stream);
@@ -1025,14 +1095,15 @@ __device__ __forceinline__ uint32_t row_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
 }
 
-// QJL: prod keys; without it MSE-only keys (BQK index planes and n).
-template <int BQK, int BQV, int KMT, bool QJL = true>
+// QJL: prod keys; without it MSE-only keys (BQK index planes and n).  MW: QJL
+// sign words per key record (as in scores128; 2 for m = d / 2).
+template <int BQK, int BQV, int KMT, bool QJL = true, int MW = 4>
 __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args a) {
   constexpr int NPK = mse_planes(BQK);
   constexpr int FK = 2 * (NPK + QJL);
   constexpr int PK = BQK + QJL;
   constexpr int KSB = QJL ? 4 : 2;            // key scalar bytes per record
-  constexpr uint32_t RBK = 16 * PK;           // key plane bytes per record
+  constexpr uint32_t RBK = MW == 4 ? 16 * PK : 4 * (4 * BQK + MW);   // key plane bytes per record
   constexpr int NPV = mse_planes(BQV);
   constexpr int PV = BQV;
   constexpr uint32_t VBB = D * PV * 4;        // value bytes per 32-token block
@@ -1085,12 +1156,12 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
   }
 
   const int64_t krec0 = seg * a.kstride + c0;
-  const rsrc_t rk = make_rsrc(a.kplanes + krec0 * (PK * 4), clamp_bytes((a.kstride - c0) * RBK));
+  const rsrc_t rk = make_rsrc(a.kplanes + krec0 * (RBK / 4), clamp_bytes((a.kstride - c0) * RBK));
   const rsrc_t rks = make_rsrc(a.kscal + krec0 * (KSB / 2), clamp_bytes((a.kstride - c0) * KSB));
   const int64_t vrec0 = seg * a.vstride + c0;   // multiple of 32
   const rsrc_t rv = make_rsrc(a.vplanes + (vrec0 / 32) * (D * PV), clamp_bytes((a.vstride - c0) / 32 * VBB));
   const rsrc_t rvs = make_rsrc(a.vscal + vrec0, clamp_bytes((a.vstride - c0) * 2));
-  const uint32_t vko = t16 * RBK + kg * (PK * 4);
+  const uint32_t vko = t16 * RBK + (MW == 4 ? kg * (PK * 4) : (kg < 2 ? kg * PK : kg * BQK + 1) * 4);
   const uint32_t vkso = t16 * KSB;
   const uint32_t vvo = (kg * D + t16) * (PV * 4);
   const uint32_t vno = lane * 4;
@@ -1136,6 +1207,7 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
     float sc[8][KMT];
 #pragma unroll
     for (int tile = 0; tile < 8; ++tile) {
+      if constexpr (MW == 2) kw[tile] = rotate_late_groups<PK>(kw[tile], kg >= 2);
       i32x4 am[KMT], aq[KMT];
 #pragma unroll
       for (int mt = 0; mt < KMT; ++mt) am[mt] = aq[mt] = i32x4{0, 0, 0, 0};
@@ -1450,14 +1522,26 @@ int64_t attend_kmax(int segs, int64_t T) {
   return k < 1 ? 1 : k;
 }
 
-template <int BQK, int BQV, int MT, bool QJL = true>
+template <int BQK, int BQV, int MT, bool QJL = true, int MW = 4>
 hipError_t launch_attend(Attend128Args& s, int segs, hipStream_t stream) {
-  static const int nb = occupancy(reinterpret_cast<const void*>(&attend128<BQK, BQV, MT, QJL>), 256);
+  static const int nb = occupancy(reinterpret_cast<const void*>(&attend128<BQK, BQV, MT, QJL, MW>), 256);
   s.span = split_span(segs, s.T, nb * device_cus(), AGRAN, attend_kmax(segs, s.T));
   s.nchunks = (int)((s.T + s.span - 1) / s.span);
-  hipLaunchKernelGGL((attend128<BQK, BQV, MT, QJL>), dim3((unsigned)s.nchunks, (unsigned)segs), dim3(256), 0,
+  hipLaunchKernelGGL((attend128<BQK, BQV, MT, QJL, MW>), dim3((unsigned)s.nchunks, (unsigned)segs), dim3(256), 0,
                      stream, s);
   return hipGetLastError();
+}
+
+// Prod keys with m = d / 2 QJL rows against values of 2..4 bits.
+template <int BQK, int BQV>
+hipError_t launch_attend_half(Attend128Args& s, int segs, int mt, hipStream_t stream) {
+  switch (mt) {
+    case 1: return launch_attend<BQK, BQV, 1, true, 2>(s, segs, stream);
+    case 2: return launch_attend<BQK, BQV, 2, true, 2>(s, segs, stream);
+    case 3: return launch_attend<BQK, BQV, 3, true, 2>(s, segs, stream);
+    case 4: return launch_attend<BQK, BQV, 4, true, 2>(s, segs, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // MSE-only keys of BQK bits (2..4) against values of 2..4 bits; 4-bit keys
@@ -1501,14 +1585,27 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   s.len = a.k.len;
   s.T = a.k.T;
   s.group = a.k.group;
-  s.kappa = (float)(std::sqrt(M_PI / 2.0) / D);
+  s.kappa = (float)(std::sqrt(M_PI / 2.0) / (a.k.qjl ? a.k.m : D));
   s.scale2 = a.scale * 1.4426950408889634f;
   walsh_coefficients(a.cb_v, a.bq_v, s.vu, &s.vusum);
   s.part = reinterpret_cast<float*>(ws + attend_pack_bytes(a.k.segs, a.k.group));
   s.nchunks = 0;   // set by the launcher
   s.span = 0;
   const int mt = (a.k.group + 3) / 4;
-  if (!a.k.qjl) {
+  if (a.k.qjl && a.k.m == D / 2) {
+    switch (a.k.bq * 10 + a.bq_v) {
+      case 12: e = launch_attend_half<1, 2>(s, a.k.segs, mt, stream); break;
+      case 13: e = launch_attend_half<1, 3>(s, a.k.segs, mt, stream); break;
+      case 14: e = launch_attend_half<1, 4>(s, a.k.segs, mt, stream); break;
+      case 22: e = launch_attend_half<2, 2>(s, a.k.segs, mt, stream); break;
+      case 23: e = launch_attend_half<2, 3>(s, a.k.segs, mt, stream); break;
+      case 24: e = launch_attend_half<2, 4>(s, a.k.segs, mt, stream); break;
+      case 32: e = launch_attend_half<3, 2>(s, a.k.segs, mt, stream); break;
+      case 33: e = launch_attend_half<3, 3>(s, a.k.segs, mt, stream); break;
+      case 34: e = launch_attend_half<3, 4>(s, a.k.segs, mt, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (!a.k.qjl) {
     switch (a.k.bq * 10 + a.bq_v) {
       case 22: e = launch_attend_mse_keys<2, 2>(s, a.k.segs, mt, stream); break;
       case 23: e = launch_attend_mse_keys<2, 3>(s, a.k.segs, mt, stream); break;

@@ -57,6 +57,13 @@ __device__ __forceinline__ int row_coord(int rho, int mt) {
   int r = ((rho >> 3) << 2) | (rho & 3);
   return 64 * h + 16 * mt + r;
 }
+// The same for a 64-row QJL matrix (m = d / 2) in two row tiles: lane half h
+// holds projection rows 32 h + 16 mt + r, i.e. all 32 bits of sign word h.
+__device__ __forceinline__ int row_half(int rho, int mt) {
+  int h = (rho >> 2) & 1;
+  int r = ((rho >> 3) << 2) | (rho & 3);
+  return 32 * h + 16 * mt + r;
+}
 
 // M is [128][128] float32 row-major (or, with eps, the matrix H diag(eps)).
 // Fragment (mt, ks) of lane l holds scale * M[row_coord(l % 32, mt)][64 (l / 32)
@@ -64,9 +71,11 @@ __device__ __forceinline__ int row_coord(int rho, int mt) {
 // each requesting up to 8 fragments' operands before splitting any of them
 // (a small workgroup would otherwise wait out one memory round trip per
 // fragment).
-template <int NTHR>
+// HALF: a 64-row matrix in two row tiles (row_half); fragments of row tiles
+// 2 and 3 are not built.
+template <int NTHR, bool HALF = false>
 __device__ void build_frags(half8* lds, const float* __restrict__ M, float scale, const float* eps = nullptr) {
-  constexpr int TOTAL = 4 * 8 * 64;
+  constexpr int TOTAL = (HALF ? 2 : 4) * 8 * 64;
   constexpr int PER = TOTAL / NTHR;
   constexpr int U = PER < 8 ? PER : 8;
   static_assert(TOTAL % NTHR == 0 && PER % U == 0, "fragments per thread");
@@ -76,7 +85,7 @@ __device__ void build_frags(half8* lds, const float* __restrict__ M, float scale
     for (int u = 0; u < U; ++u) {
       const int f = threadIdx.x + (b0 + u) * NTHR;
       const int lane = f & 63, ks = (f >> 6) & 7, mt = f >> 9;
-      const int row = row_coord(lane & 31, mt);
+      const int row = HALF ? row_half(lane & 31, mt) : row_coord(lane & 31, mt);
       const int k0 = 64 * (lane >> 5) + 8 * ks;
       const float4* src = reinterpret_cast<const float4*>(eps ? eps + k0 : M + row * D + k0);
       p[u] = src[0];
@@ -86,7 +95,7 @@ __device__ void build_frags(half8* lds, const float* __restrict__ M, float scale
     for (int u = 0; u < U; ++u) {
       const int f = threadIdx.x + (b0 + u) * NTHR;
       const int lane = f & 63, ks = (f >> 6) & 7, mt = f >> 9;
-      const int row = row_coord(lane & 31, mt);
+      const int row = HALF ? row_half(lane & 31, mt) : row_coord(lane & 31, mt);
       const int k0 = 64 * (lane >> 5) + 8 * ks;
       float v[8] = {p[u].x, p[u].y, p[u].z, p[u].w, q[u].x, q[u].y, q[u].z, q[u].w};
       if (eps) {
@@ -145,15 +154,20 @@ __device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, 
 // may take the per-bit path; without it only a ragged last tile can.
 // EDEN: an MSE record stores the unbiased per-vector scale n / <y, c[idx]>
 // instead of n (EDEN's scale; DRIVE's at one bit).
-template <bool PROD, bool QJL, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS, bool EDEN = false>
+// MW: QJL sign words per key record, m / 32 (4: m = d; 2: m = d / 2, whose
+// record holds for each 32-coordinate group w the index words, then sign word
+// w if w < 2).
+template <bool PROD, bool QJL, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS, bool EDEN = false,
+          int MW = 4>
 __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   static_assert(PROD || !QJL, "values carry no QJL bits");
   static_assert(!(EDEN && QJL), "the scale replaces the norm of MSE records only");
+  static_assert(MW == 4 || (QJL && MW == 2), "m = d / 2 is a prod-key form");
   extern __shared__ half8 lds[];
   half8* fpi = lds;
   half8* fs = lds + FRAGS;
   build_frags<64 * WAVES>(fpi, a.pi, PI_SCALE, HAD ? a.eps : nullptr);
-  if (QJL) build_frags<64 * WAVES>(fs, a.s, 1.f);
+  if (QJL) build_frags<64 * WAVES, MW == 2>(fs, a.s, 1.f);
   __syncthreads();
 
   constexpr int P = QJL ? BQ + 1 : BQ;      // planes per record
@@ -432,8 +446,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sw[nt][0] = sw[nt][1] = 0u;
     if (QJL) {
+      // m = d: row tiles 0-3, lane half h collects sign words 2h, 2h + 1;
+      // m = d / 2: row tiles 0-1, lane half h collects sign word h
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
+      for (int it = 0; it < MW; ++it) {
         f32x16 acc[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
@@ -490,6 +506,35 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         const float t = (yc[nt] + shfl_xor_f(yc[nt], 32)) * (ysc[nt] * ysc[nt]);
         ks = nrm[nt] > 0.f && t > 0.f ? nrm[nt] / t : 0.f;
       }
+      if constexpr (QJL && MW == 2) {
+        // lane half 0 writes groups 0 and 1 with sign words 0 and 1 (the
+        // latter from lane half 1); lane half 1 writes groups 2 and 3
+        const uint32_t s1 = __shfl_xor(sw[nt][0], 32, 64);
+        if (vec[nt] < a.n) {
+          const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
+          constexpr int RW = 4 * BQ + 2;
+          uint32_t out[2 * BQ + 2];
+#pragma unroll
+          for (int p = 0; p < BQ; ++p) {
+            out[p] = __builtin_bitreverse32(iw[nt][p][0]);
+            out[BQ + 1 + p] = __builtin_bitreverse32(iw[nt][p][1]);
+          }
+          out[BQ] = __builtin_bitreverse32(sw[nt][0]);
+          out[2 * BQ + 1] = __builtin_bitreverse32(s1);
+          if (h == 1) {
+#pragma unroll
+            for (int p = 0; p < BQ; ++p) out[BQ + p] = __builtin_bitreverse32(iw[nt][p][1]);
+          }
+          uint2* dst = reinterpret_cast<uint2*>(a.planes + rec * RW + (h ? 2 * BQ + 2 : 0));
+#pragma unroll
+          for (int i = 0; i < BQ + 1; ++i)
+            if (h == 0 || i < BQ) dst[i] = make_uint2(out[2 * i], out[2 * i + 1]);
+          if (h == 0)
+            reinterpret_cast<uint32_t*>(a.scalars)[rec] =
+                (uint32_t)f16_bits(nrm[nt]) | ((uint32_t)f16_bits(g) << 16);
+        }
+        continue;
+      }
       if (vec[nt] < a.n) {
         const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
         // record order: word w of plane p at w * P + p; this lane owns words
@@ -520,11 +565,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   }
 }
 
-template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int WAVES, bool EDEN = false>
+template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int WAVES, bool EDEN = false, int MW = 4>
 hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
   constexpr int NT = 1;
   // EDEN values always take the slot-capable form (one kernel for both)
-  auto kern = EDEN ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD, EDEN>
+  auto kern = MW != 4 ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, false, false, MW>
+              : EDEN ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD, EDEN>
               : PROD || !a.slot ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, false>
                                 : encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD>;
   const size_t lds = (QJL ? 2 : 1) * FRAGS * sizeof(half8);
@@ -544,14 +590,25 @@ hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
 // sequence) takes one-wave workgroups instead, so that its tiles (and, for
 // values written through a slot map, their per-bit atomics) spread over as
 // many compute units as there are tiles.
-template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD>
+template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int MW = 4>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   int dev = 0, cus = 256;
   hipGetDevice(&dev);
   hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t ntiles = (a.n + 31) / 32;
-  if (ntiles < 2 * (int64_t)cus) return launch_waves<PROD, QJL, BQ, F16IN, HAD, 1>(a, cus, stream);
-  return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8>(a, cus, stream);
+  if (ntiles < 2 * (int64_t)cus) return launch_waves<PROD, QJL, BQ, F16IN, HAD, 1, false, MW>(a, cus, stream);
+  return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8, false, MW>(a, cus, stream);
+}
+
+// Prod keys with m = d / 2 QJL rows
+template <bool F16IN, bool HAD>
+hipError_t launch_prod_half(const EncodeArgs& a, hipStream_t stream) {
+  switch (a.bq) {
+    case 1: return launch_one<true, true, 1, F16IN, HAD, 2>(a, stream);
+    case 2: return launch_one<true, true, 2, F16IN, HAD, 2>(a, stream);
+    case 3: return launch_one<true, true, 3, F16IN, HAD, 2>(a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // EDEN-scaled MSE records (keys in the per-record layout, or values), b
@@ -589,6 +646,8 @@ hipError_t launch_rot(const EncodeArgs& a, hipStream_t stream) {
     return a.f16_in ? launch_eden<false, true, HAD>(a, stream) : launch_eden<false, false, HAD>(a, stream);
   }
   if (a.prod && !a.qjl) return a.f16_in ? launch_mse_keys<true, HAD>(a, stream) : launch_mse_keys<false, HAD>(a, stream);
+  if (a.prod && a.m == D / 2)
+    return a.f16_in ? launch_prod_half<true, HAD>(a, stream) : launch_prod_half<false, HAD>(a, stream);
   if (a.prod) {
     if (a.f16_in) {
       switch (a.bq) {

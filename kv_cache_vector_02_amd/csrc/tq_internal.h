@@ -25,7 +25,8 @@ struct EncodeArgs {
   int d;               // input dimension (<= d_rot)
   const float* pi;     // dense rotation [d_rot][d]
   const float* eps;    // hadamard signs [d_rot]
-  const float* s;      // QJL matrix [d_rot][d_rot] (prod only)
+  const float* s;      // QJL matrix [m][d_rot] (prod only)
+  int m;               // QJL rows: d_rot, or d_rot / 2 at d_rot = 128
   Codebook cb;
   int bq;              // index bits
   int prod;            // 1: per-record key layout, 0: values (mse, token-blocked)
@@ -91,7 +92,8 @@ struct ScoreArgs {
   const float* pi;       // rotation of the keys (dense)
   const float* eps;      // hadamard signs
   int rot;
-  const float* s;        // QJL matrix (prod keys) or NULL (MSE-only keys)
+  const float* s;        // QJL matrix [m][d] (prod keys) or NULL (MSE-only keys)
+  int m;                 // QJL rows: d, or d / 2
   Codebook cb;
   int bq;                // index bits
   int qjl;               // 1: prod keys (QJL plane, n and gamma); 0: MSE-only keys (n only)

@@ -40,7 +40,7 @@ def exact_scores(keys, queries):
 def encode_keys(kp: tq.Params, keys, seg_stride: int = 0, eden: bool = False) -> tq.Cache:
     """Prod keys, or MSE-only keys when kp has no QJL matrix (with eden, scaled
     by EDEN's unbiased n / <y, c[idx]>)."""
-    cache = tq.alloc_cache(tq.key_layout(kp), keys.shape[0], seg_stride)
+    cache = tq.alloc_key_cache(kp, keys.shape[0], seg_stride)
     if kp.s is not None:
         tq.encode_prod(kp, keys.contiguous(), cache)
     elif eden:

@@ -21,6 +21,12 @@ index of record 32 B + i at coordinate j.  The float16 norms stay one per
 record.  (Keys are read along coordinates, values along tokens; each layout
 puts the bits a reader needs in one word.)
 
+With fewer QJL rows than coordinates (m < d, the first page's proj_dim =
+head_dim / 2) the sign plane has m/32 words.  The general key record is: for
+each group of 32 coordinates w = 0 .. d/32 - 1, the b-1 index words of the
+group, then sign word w if w < m/32.  With m = d that is the interleaved
+record above.
+
 This matches the storage accounting the first page uses (indices packed at b
 bits per coordinate, one sign bit per projection row, float16 norms).
 """
@@ -75,11 +81,23 @@ def deinterleave(record) -> np.ndarray:
 
 
 def pack_key(code, nbits_idx: int):
-    """ProdCode -> (planes [N, d/32, nbits_idx + 1] uint32 in record order, scalars [N, 2] float16)."""
-    planes = np.concatenate([index_planes(code.idx, nbits_idx),
-                             pack_bits(code.z)[:, None, :]], axis=1)
+    """ProdCode -> (record words, scalars [N, 2] float16).
+
+    With m = d (as many QJL rows as coordinates) the words come as
+    [N, d/32, nbits_idx + 1] in record order; with m < d as [N, words per
+    record], group by group (index words, then sign word w while w < m/32)."""
+    idx_pm = index_planes(code.idx, nbits_idx)              # [N, B, W]
+    sign = pack_bits(code.z)                                # [N, m/32]
     scalars = np.stack([code.n, code.gamma], axis=1).astype(np.float16)
-    return interleave(planes), scalars
+    n, _, w = idx_pm.shape
+    if sign.shape[1] == w:
+        return interleave(np.concatenate([idx_pm, sign[:, None, :]], axis=1)), scalars
+    groups = []
+    for g in range(w):
+        groups.append(idx_pm[:, :, g])
+        if g < sign.shape[1]:
+            groups.append(sign[:, g:g + 1])
+    return np.ascontiguousarray(np.concatenate(groups, axis=1)), scalars
 
 
 def pack_value(code, nbits: int):
@@ -87,13 +105,28 @@ def pack_value(code, nbits: int):
     return interleave(index_planes(code.idx, nbits)), code.n.astype(np.float16)[:, None]
 
 
-def unpack_key(planes, scalars, nbits_idx: int):
-    """Record-order planes -> (idx [N, d], z [N, m] bool, n [N], gamma [N]), scalars as float64."""
-    pm = deinterleave(planes)
-    idx = planes_to_index(pm[:, :nbits_idx, :])
-    z = unpack_bits(pm[:, nbits_idx, :])
+def unpack_key(planes, scalars, nbits_idx: int, d: int = 0):
+    """Record words -> (idx [N, d], z [N, m] bool, n [N], gamma [N]), scalars as float64.
+
+    [N, W, P] words are the m = d record; [N, words] words the m < d record
+    of coordinate count d (which must be given)."""
     s = np.asarray(scalars, np.float16).astype(np.float64)
-    return idx, z, s[:, 0], s[:, 1]
+    planes = np.asarray(planes, np.uint32)
+    if planes.ndim == 3:
+        pm = deinterleave(planes)
+        return planes_to_index(pm[:, :nbits_idx, :]), unpack_bits(pm[:, nbits_idx, :]), s[:, 0], s[:, 1]
+    w = d // 32
+    mw = planes.shape[1] - w * nbits_idx
+    idx_pm = np.zeros((planes.shape[0], nbits_idx, w), np.uint32)
+    sign = np.zeros((planes.shape[0], mw), np.uint32)
+    pos = 0
+    for g in range(w):
+        idx_pm[:, :, g] = planes[:, pos:pos + nbits_idx]
+        pos += nbits_idx
+        if g < mw:
+            sign[:, g] = planes[:, pos]
+            pos += 1
+    return planes_to_index(idx_pm), unpack_bits(sign), s[:, 0], s[:, 1]
 
 
 def unpack_value(planes, scalars, nbits: int):

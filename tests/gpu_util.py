@@ -32,7 +32,7 @@ class Setup:
     """Seeded rotation / projection / codebooks for one quantizer, on host and device."""
 
     def __init__(self, d=128, bits=3, prod=True, rot="dense", seed=0, d_rot=None, purpose_pi=2,
-                 purpose_s=3, purpose_eps=5):
+                 purpose_s=3, purpose_eps=5, m=None):
         T = torch()
         self.d, self.bits, self.prod = d, bits, prod
         self.d_rot = d_rot or d
@@ -47,9 +47,10 @@ class Setup:
             self.eps = sign_vector(self.d_rot, seed, purpose_eps)
             self.rot = tr.HadamardRotation(self.eps, d)
             self.pi = None
-        self.s = gaussian_matrix(self.d_rot, self.d_rot, seed, purpose_s) if prod else None
+        self.m = m or self.d_rot
+        self.s = gaussian_matrix(self.m, self.d_rot, seed, purpose_s) if prod else None
         dev = lambda a: None if a is None else T.from_numpy(a).cuda()
-        self.params = tq.Params(d=d, d_rot=self.d_rot, m=self.d_rot, bits=bits,
+        self.params = tq.Params(d=d, d_rot=self.d_rot, m=self.m, bits=bits,
                                 rot=tq.TQ_ROT_DENSE if rot == "dense" else tq.TQ_ROT_HADAMARD,
                                 centroids=self.c32, boundaries=self.b32, pi=dev(self.pi),
                                 eps=dev(self.eps), s=dev(self.s))
@@ -59,7 +60,7 @@ class Setup:
 
     def alloc(self, records, seg_stride=0):
         if self.prod:
-            return tq.alloc_cache(self.layout(), records, seg_stride)
+            return tq.alloc_key_cache(self.params, records, seg_stride)
         return tq.alloc_value_cache(self.layout(), records, seg_stride)
 
     def encode_gpu(self, x_np, slot=None, records=None, cache=None):
@@ -116,7 +117,7 @@ def compare_encode(setup: Setup, planes, scal, ocode):
     n = planes.shape[0]
     stats = {}
     if setup.prod:
-        idx, z, nn, gg = pk.unpack_key(planes, scal, bq)
+        idx, z, nn, gg = pk.unpack_key(planes, scal, bq, d=setup.d_rot)
     else:
         idx = planes          # value indices, already unpacked from the block layout
     # indices

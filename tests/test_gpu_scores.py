@@ -26,7 +26,7 @@ def oracle_key_cache(st: Setup, x, seg_stride=None, segs=1):
     planes, scal = pk.pack_key(code, st.bq)
     cache = tq.Cache(T.from_numpy(planes.view(np.int32)).cuda(), T.from_numpy(scal).cuda(),
                      seg_stride or x.shape[0] // segs)
-    return cache, pk.unpack_key(planes, scal, st.bq)
+    return cache, pk.unpack_key(planes, scal, st.bq, d=st.d_rot)
 
 
 def gpu_scores(st, q, segs, group, cache, T_, length=None):

@@ -81,8 +81,13 @@ def test_encode_validation_without_launch():
     p._c.s = None
     assert _encode_raw(p) == tq.TQ_ERR_INVALID_ARG          # prod without S
     p._c.s = 0x20000
+    for m in (96, 32, 256):
+        p._c.m = m
+        assert _encode_raw(p) == tq.TQ_ERR_INVALID_ARG      # m neither d_rot nor d_rot / 2
     p._c.m = 64
-    assert _encode_raw(p) == tq.TQ_ERR_INVALID_ARG          # m != d_rot
+    assert tq.lib().tq_key_record_words(p.c) == 4 * 2 + 2  # m = d / 2: sign words in groups 0 and 1
+    p._c.m = 128
+    assert tq.lib().tq_key_record_words(p.c) == 4 * 3
     p._c.m = 128
     p._c.bits = 5
     assert _encode_raw(p) == tq.TQ_ERR_INVALID_ARG          # bits out of range

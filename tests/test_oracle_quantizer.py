@@ -199,3 +199,26 @@ def test_eden_zero_vector():
     c, b = cb.lloyd_max(8, 2)
     code = qz.encode_eden(np.zeros((1, 8)), rot, c, b)
     assert code.n[0] == 0.0
+
+
+def test_pack_key_half_projection_hand_built_and_roundtrip():
+    # m = 64 QJL rows at d = 128, b - 1 = 2 index bits: group w holds index
+    # words (plane 0, plane 1), then sign word w for w < 2
+    rg = np.random.default_rng(9)
+    idx = rg.integers(0, 4, size=(3, 128))
+    z = rg.integers(0, 2, size=(3, 64)).astype(bool)
+    code = qz.ProdCode(idx=idx, z=z, n=np.ones(3), gamma=np.ones(3), y=None, proj=None)
+    words, scal = pk.pack_key(code, 2)
+    assert words.shape == (3, 10)
+    for v in range(3):
+        for w in range(4):
+            off = 2 * w + min(w, 2)
+            for p in range(2):
+                want = sum(int((idx[v, 32 * w + j] >> p) & 1) << j for j in range(32))
+                assert int(words[v, off + p]) == want
+            if w < 2:
+                want = sum(int(z[v, 32 * w + j]) << j for j in range(32))
+                assert int(words[v, off + 2]) == want
+    i2, z2, _, _ = pk.unpack_key(words, scal, 2, d=128)
+    assert np.array_equal(i2, idx) and np.array_equal(z2, z)
+    assert pk.key_record_bytes(128, 64, 3) == 44
