@@ -45,10 +45,10 @@ INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 matrix peak (the retrieval score GE
 # HBM bytes per launch of the score kernel, read by rocprofv3 (FETCH_SIZE and
 # WRITE_SIZE, each in its own run) and scaled by the factor the same counters
 # give for a plain device copy of known size (bench.py --copy-calibration):
-# FETCH_SIZE 16591.5 KiB x 1.99982 (a 256 MiB copy reads as 131083.5 KiB) +
+# FETCH_SIZE 16597.5 KiB x 1.99982 (a 256 MiB copy reads as 131083.5 KiB) +
 # WRITE_SIZE 18432.0 KiB x 1.0.  Valid only for the decode source measured.
-SCORE_TRAFFIC = {"tq_decode.hip sha256": "853095536afadeb5085cb4043d517fa13ce94854477019c9331da9e9f2d5492c",
-                 "bytes_per_launch": 52850779}
+SCORE_TRAFFIC = {"tq_decode.hip sha256": "b3bb63f7e6aea7e1a65fdac6dae8f09253bbb0b421e3f793826c20112a431599",
+                 "bytes_per_launch": 52863066}
 
 L_, H_, T_, D_ = 36, 2, 8192, 128
 G_ = 8
