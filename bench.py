@@ -134,46 +134,71 @@ def large_cache_scores(torch, tq, pk_, ev):
     }
 
 
-def half_projection_line(torch, tq, k_dev, q, ev):
-    """The score pass over the Qwen-shaped keys with m = d / 2 = 64 QJL rows
-    (the first page's proj_dim = head_dim / 2): 44-byte key records at b = 3
-    instead of 52.  Timed like the main line: bursts of back-to-back passes over
-    12 cache copies (311 MB, past the 256 MB memory-side cache)."""
+def key_forms_line(torch, tq, k_dev, v_dev, pv_, q, ev):
+    """The Qwen-shaped score pass for the other key forms, timed like the main
+    line (bursts over 12 cache copies, past the 256 MB memory-side cache):
+    prod keys with m = d / 2 = 64 QJL rows (the first page's proj_dim =
+    head_dim / 2: 44-byte records at b = 3), and MSE-only keys at b = 3
+    (50-byte records), the latter also through tq_attend with the b = 3 values."""
     from tq_inputs import gaussian_matrix, haar_orthogonal
     segs, N = L_ * H_, L_ * H_ * T_
-    c, b = tq.build_codebook(D_, BITS - 1)
-    kp = tq.Params(d=D_, m=D_ // 2, bits=BITS, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b,
-                   pi=torch.from_numpy(haar_orthogonal(D_, SEED, 2)).cuda(),
-                   s=torch.from_numpy(gaussian_matrix(D_ // 2, D_, SEED, 3)).cuda())
-    one = tq.alloc_key_cache(kp, N, seg_stride=T_)
-    tq.encode_prod(kp, k_dev, one)
-    burst = 12
-    kb = [tq.Cache(one.planes.clone(), one.scalars.clone(), T_) for _ in range(burst)]
-    del one
+    pi = torch.from_numpy(haar_orthogonal(D_, SEED, 2)).cuda()
+    c2, b2 = tq.build_codebook(D_, BITS - 1)
+    c3, b3 = tq.build_codebook(D_, BITS)
+    forms = {
+        "prod_m64": tq.Params(d=D_, m=D_ // 2, bits=BITS, rot=tq.TQ_ROT_DENSE, centroids=c2, boundaries=b2, pi=pi,
+                              s=torch.from_numpy(gaussian_matrix(D_ // 2, D_, SEED, 3)).cuda()),
+        "mse_keys": tq.Params(d=D_, bits=BITS, rot=tq.TQ_ROT_DENSE, centroids=c3, boundaries=b3, pi=pi),
+    }
     out = torch.empty((segs * G_, T_), dtype=torch.float32, device="cuda")
-    ws = tq.alloc_workspace(tq.scores_workspace(kp, segs, G_))
-    tq.scores_prepare(kp, q, segs, G_, ws)
-    per = []
-    for _ in range(5):
-        torch.cuda.synchronize()
-        torch.cuda._sleep(2_000_000)
-        e0, e1 = ev(), ev()
-        e0.record()
-        for i in range(burst):
-            tq.scores_prepared(kp, segs, G_, kb[i], T_, out, ws)
-        e1.record()
-        torch.cuda.synchronize()
-        per.append(e0.elapsed_time(e1) / burst)
-    t = float(np.median(per))
-    rec = 4 * tq.key_record_words(kp) + 4
-    pass_bytes = N * rec + segs * G_ * T_ * 4
-    del kb, out, ws
+    res = {}
+    burst = 12
+
+    def timed(fn):
+        per = []
+        fn(0)
+        for _ in range(5):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(2_000_000)
+            e0, e1 = ev(), ev()
+            e0.record()
+            for i in range(burst):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / burst)
+        return float(np.median(per))
+
+    vc = tq.alloc_value_cache(tq.value_layout(pv_), N, seg_stride=T_)
+    tq.encode_mse(pv_, v_dev, vc)
+    for name, kp in forms.items():
+        one = tq.alloc_key_cache(kp, N, seg_stride=T_)
+        (tq.encode_prod if kp.s is not None else tq.encode_mse_keys)(kp, k_dev, one)
+        kb = [tq.Cache(one.planes.clone(), one.scalars.clone(), T_) for _ in range(burst)]
+        del one
+        ws = tq.alloc_workspace(tq.scores_workspace(kp, segs, G_))
+        tq.scores_prepare(kp, q, segs, G_, ws)
+        t = timed(lambda i: tq.scores_prepared(kp, segs, G_, kb[i], T_, out, ws))
+        rec = 4 * tq.key_record_words(kp) + (4 if kp.s is not None else 2)
+        pass_bytes = N * rec + segs * G_ * T_ * 4
+        r = {"key_record_bytes": rec, "score_pass_ms": round(t, 5),
+             "score_pass_GBps": round(pass_bytes / (t * 1e-3) / 1e9, 1),
+             "score_pass_frac_hbm_peak": round(pass_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "bytes_per_pass": pass_bytes}
+        if kp.s is None:
+            o = torch.empty((segs * G_, D_), dtype=torch.float32, device="cuda")
+            wa = tq.alloc_workspace(tq.attend_workspace(kp, pv_, segs, G_, T_))
+            r["tq_attend_call_ms"] = round(timed(lambda i: tq.attend(kp, pv_, q, segs, G_, kb[i], vc, T_,
+                                                                    1.0 / np.sqrt(D_), o, wa)), 5)
+            del o, wa
+        res[name] = r
+        del kb, ws
+        torch.cuda.empty_cache()
+    del vc, out
     torch.cuda.empty_cache()
-    return {"workload": "qwen2.5-3b-shaped keys (72 segments x 8192 tokens), prod b=3 with m = 64 QJL rows, G = 8",
-            "key_record_bytes": rec, "score_pass_ms": round(t, 5),
-            "score_pass_GBps": round(pass_bytes / (t * 1e-3) / 1e9, 1),
-            "score_pass_frac_hbm_peak": round(pass_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_pass": pass_bytes}
+    res["workload"] = ("qwen2.5-3b-shaped keys (72 segments x 8192 tokens, G = 8): prod b=3 with m = 64 QJL rows; "
+                       "MSE-only b=3 keys (attend with b=3 values)")
+    return res
 
 
 def batched_decode_line(torch, tq, pk_, pv_, ev):
@@ -613,7 +638,7 @@ def main():
         result["large_cache"] = large_cache_scores(torch, tq, pk_, ev)
         result["large_cache"]["score_pass_frac_of_measured_copy"] = round(
             result["large_cache"]["score_pass_GBps"] / copy_gbs, 4)
-    result["half_projection"] = half_projection_line(torch, tq, kx[0], q, ev)
+    result["key_forms"] = key_forms_line(torch, tq, kx[0], vx[0], pv_, q, ev)
     if not args.skip_batched:
         result["batched_decode"] = batched_decode_line(torch, tq, pk_, pv_, ev)
     if not args.skip_retrieval:
