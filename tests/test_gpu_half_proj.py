@@ -128,3 +128,23 @@ def test_attend(bk, bv, group):
                          sv.rot, sv.c32, scale)
         worst = max(worst, check_heads(got[rows], ref))
     _log(f"  worst rel {worst:.2e}")
+
+
+def test_attend_hadamard():
+    # sign-flipped Hadamard keys and values, m = 64
+    _log("m=64 attend hadamard b3")
+    segs, T_ = 2, 640
+    scale = 1 / np.sqrt(128)
+    xk = kv_tensor(1, segs, T_, 128, seed=46)[0].reshape(-1, 128)
+    xv = kv_tensor(1, segs, T_, 128, seed=46, value=True)[0].reshape(-1, 128)
+    sk = Setup(bits=3, rot="hadamard", seed=46, m=64)
+    sv = Setup(bits=3, prod=False, rot="hadamard", seed=46, purpose_pi=4, purpose_eps=6)
+    kc, (kidx, kz, kn, kg) = oracle_key_cache(sk, xk, seg_stride=T_)
+    vc, vidx, vn = oracle_value_cache(sv, xv, T_)
+    q = gaussian_queries(segs * 4, 128, seed=46)
+    got = gpu_attend(sk, sv, q, segs, 4, kc, vc, T_, scale)
+    for s in range(segs):
+        sl = slice(s * T_, (s + 1) * T_)
+        ref = est.attend(q[4 * s:4 * s + 4], (kidx[sl], kz[sl], kn[sl], kg[sl]), (vidx[sl], vn[sl]), sk.rot, sk.s,
+                         sk.c32, sv.rot, sv.c32, scale)
+        check_heads(got[4 * s:4 * s + 4], ref)

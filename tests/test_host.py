@@ -148,3 +148,20 @@ def test_needle_inputs():
     s = np.einsum("tld,td->tl", hay.astype(np.float64), q.astype(np.float64))
     assert np.array_equal(s.argmax(1), pos)
     assert np.all(s[np.arange(5), pos] > 0.5)     # about 1 / sqrt(1 + 0.01 d)
+
+
+def test_key_cache_shapes():
+    # records of prod keys (m = d and m = d / 2) and of MSE-only keys, allocated
+    # on the host here (the binding only sizes them; nothing is launched)
+    import torch
+    c2, b2 = cb.lloyd_max(128, 2)
+    c3, b3 = cb.lloyd_max(128, 3)
+    eps = torch.ones(128)
+    s128, s64 = torch.zeros(128, 128), torch.zeros(64, 128)
+    mk = lambda **kw: tq.Params(d=128, rot=tq.TQ_ROT_HADAMARD, eps=eps, **kw)
+    full = tq.alloc_key_cache(mk(bits=3, centroids=c2, boundaries=b2, s=s128), 5, device="cpu")
+    half = tq.alloc_key_cache(mk(bits=3, centroids=c2, boundaries=b2, s=s64, m=64), 5, device="cpu")
+    mse = tq.alloc_key_cache(mk(bits=3, centroids=c3, boundaries=b3), 5, device="cpu")
+    assert tuple(full.planes.shape) == (5, 4, 3) and tuple(full.scalars.shape) == (5, 2)
+    assert tuple(half.planes.shape) == (5, 10) and tuple(half.scalars.shape) == (5, 2)
+    assert tuple(mse.planes.shape) == (5, 4, 3) and tuple(mse.scalars.shape) == (5, 1)
