@@ -148,3 +148,30 @@ def test_attend_hadamard():
         ref = est.attend(q[4 * s:4 * s + 4], (kidx[sl], kz[sl], kn[sl], kg[sl]), (vidx[sl], vn[sl]), sk.rot, sk.s,
                          sk.c32, sv.rot, sv.c32, scale)
         check_heads(got[4 * s:4 * s + 4], ref)
+
+
+def test_qwen_shaped_full_size_sampled():
+    # 36 layers x 2 KV heads x 8192 tokens, G = 8, b = 3, m = 64: the score
+    # pass bench.py times, every segment in one launch; the oracle checks every
+    # head on sampled tokens (the row scale is the full row's maximum)
+    _log("m=64 scores qwen-shaped full size (sampled tokens)")
+    L_, H_, T_ = 36, 2, 8192
+    x = kv_tensor(L_, H_, T_, 128, seed=1).reshape(-1, 128)
+    st = Setup(bits=3, seed=1, m=64)
+    cache, (idx, z, n, g) = oracle_key_cache(st, x, seg_stride=T_)
+    segs, group = L_ * H_, 8
+    q = gaussian_queries(segs * group, 128, seed=1)
+    got = gpu_scores(st, q, segs, group, cache, T_)
+    assert np.isfinite(got).all()
+    tok = np.sort(np.random.default_rng(1).choice(T_, 256, replace=False))
+    tok[-1] = T_ - 1
+    worst = 0.0
+    for s in range(segs):
+        sl = s * T_ + tok
+        rows = slice(s * group, (s + 1) * group)
+        ref = est.prod_scores(q[rows], idx[sl], z[sl], n[sl], g[sl], st.rot, st.s, st.c32)
+        full = np.max(np.abs(got[rows]), axis=1)
+        err = np.max(np.abs(got[rows][:, tok] - ref), axis=1)
+        assert np.all(err <= 1e-3 * full)
+        worst = max(worst, float(np.max(err / full)))
+    _log(f"  worst rel {worst:.2e}")

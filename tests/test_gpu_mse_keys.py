@@ -173,3 +173,29 @@ def test_attend_4bit_keys_reject_16_heads():
     ws = tq.alloc_workspace(tq.attend_workspace(sk.params, sv.params, 1, 16, 64))
     with pytest.raises(tq.TQError, match="UNSUPPORTED"):
         tq.attend(sk.params, sv.params, q, 1, 16, kc, vc, 64, 1.0, out, ws)
+
+
+def test_qwen_shaped_full_size_sampled():
+    # 36 layers x 2 KV heads x 8192 tokens, G = 8, MSE-only b = 3 keys: the
+    # score pass bench.py times, every segment in one launch; sampled tokens
+    _log("mse keys scores qwen-shaped full size (sampled tokens)")
+    L_, H_, T_ = 36, 2, 8192
+    x = kv_tensor(L_, H_, T_, 128, seed=1).reshape(-1, 128)
+    st = _setup(3, seed=1)
+    cache, idx, n = oracle_mse_key_cache(st, x, T_)
+    segs, group = L_ * H_, 8
+    q = gaussian_queries(segs * group, 128, seed=1)
+    got = gpu_scores(st, q, segs, group, cache, T_)
+    assert np.isfinite(got).all()
+    tok = np.sort(np.random.default_rng(1).choice(T_, 256, replace=False))
+    tok[-1] = T_ - 1
+    worst = 0.0
+    for s in range(segs):
+        sl = s * T_ + tok
+        rows = slice(s * group, (s + 1) * group)
+        ref = est.mse_scores(q[rows], idx[sl], n[sl], st.rot, st.c32)
+        full = np.max(np.abs(got[rows]), axis=1)
+        err = np.max(np.abs(got[rows][:, tok] - ref), axis=1)
+        assert np.all(err <= 1e-3 * full)
+        worst = max(worst, float(np.max(err / full)))
+    _log(f"  worst rel {worst:.2e}")
