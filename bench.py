@@ -303,9 +303,11 @@ def retrieval_line(torch, tq, ev):
     exact = torch.cat(exact).cpu().numpy()
     eps = torch.from_numpy(sign_vector(DR, 4, 5)).cuda()
     s = torch.from_numpy(gaussian_matrix(DR, DR, 4, 3)).cuda()
-    out = {"workload": "1,000,000 x 1536 mixture embeddings -> 2048 (hadamard), prod keys (b2, b4) and "
-                       "MSE-only records (mse_b2, mse_b4), 1000 queries, top-10"}
-    for prod, bits in ((True, 2), (True, 4), (False, 2), (False, 4)):
+    out = {"workload": "1,000,000 x 1536 mixture embeddings -> 2048 (hadamard), prod keys (b2, b4), "
+                       "MSE-only records (mse_b2, mse_b4) and MSE-only records with EDEN's unbiased scale "
+                       "(eden_b2, eden_b4), 1000 queries, top-10"}
+    for kind, bits in (("b", 2), ("b", 4), ("mse_b", 2), ("mse_b", 4), ("eden_b", 2), ("eden_b", 4)):
+        prod = kind == "b"
         bq = bits - 1 if prod else bits
         c, b = tq.build_codebook(DR, bq)
         p = tq.Params(d=D, d_rot=DR, m=DR, bits=bits, rot=tq.TQ_ROT_HADAMARD, centroids=c, boundaries=b,
@@ -317,7 +319,8 @@ def retrieval_line(torch, tq, ev):
         else:
             cache = tq.alloc_value_cache(tq.value_layout(p), N)      # per-record layout at d_rot = 2048
             ws_e = None
-            enc = lambda: tq.encode_mse(p, x, cache)
+            enc = (lambda: tq.encode_eden(p, x, cache, keys=True)) if kind == "eden_b" else \
+                (lambda: tq.encode_mse(p, x, cache))
         enc()
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
@@ -344,7 +347,7 @@ def retrieval_line(torch, tq, ev):
         planes = (1 if prod else 0) + {1: 1, 2: 2, 3: 4, 4: 8}[bq]   # MSE Walsh planes (+ the QJL plane)
         digits = 2                                                    # base-256 digits per query weight
         int_ops = 2.0 * NQ * N * DR * planes * digits                # int8 MACs x 2 executed by the score GEMM
-        out[("b" if prod else "mse_b") + str(bits)] = {
+        out[kind + str(bits)] = {
             "encode_ms": round(t_enc, 4), "encoded_vectors_per_s": round(N / (t_enc * 1e-3), 1),
             "topk_ms": round(t_topk, 4), "query_records_per_s": round(NQ * N / (t_topk * 1e-3), 1),
             "score_gemm_int8_TOPS_executed": round(int_ops / (t_topk * 1e-3) / 1e12, 1),

@@ -202,7 +202,10 @@ tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, 
  * layout  TQ_LAYOUT_BLOCKS: values in the token-blocked layout (as
  *         tq_encode_mse); TQ_LAYOUT_RECORDS: MSE-only keys in the per-record
  *         key layout (as tq_encode_mse_keys)
- * Other arguments as for tq_encode_mse.  Supported: d = d_rot = 128. */
+ * Other arguments as for tq_encode_mse.  Supported: d = d_rot = 128, and the
+ * Hadamard rotation at d_rot = 2048, whose MSE records are always per record
+ * (the retrieval records of tq_scores_topk with kp->s == NULL; layout is
+ * ignored there). */
 tq_status tq_encode_eden(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
                          tq_layout layout, tq_cache out, const int64_t* slot, void* stream);
 

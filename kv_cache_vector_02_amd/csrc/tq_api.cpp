@@ -118,8 +118,8 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   a.qjl = prod;
   a.m = prod ? p->m : 0;
   a.eden = eden;
-  if (eden && !(p->d == 128 && p->d_rot == 128))
-    return fail(TQ_ERR_UNSUPPORTED, "tq_encode_eden supports d = d_rot = 128 (got %d, %d)", p->d, p->d_rot);
+  if (eden && !(p->d == 128 && p->d_rot == 128) && !(p->rot == TQ_ROT_HADAMARD && p->d_rot == 2048))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_encode_eden supports d = d_rot = 128 and the Hadamard rotation at d_rot = 2048");
   a.planes = (uint32_t*)out.planes;
   a.scalars = (uint16_t*)out.scalars;
   a.slot = slot;

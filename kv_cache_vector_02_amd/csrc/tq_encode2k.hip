@@ -57,9 +57,11 @@ __device__ __forceinline__ void quantize2k(float y, const Codebook& cb, int& idx
 
 // PROD: key records (BQ index planes + the QJL plane, written by the
 // projection pass; scalars n and gamma) with the residual to the workspace;
-// otherwise MSE records (BQ planes, scalar n) and nothing else.
-template <int BQ, bool F16IN, bool PROD>
+// otherwise MSE records (BQ planes, scalar n, or with EDEN the unbiased
+// per-vector scale n / <y, c[idx]>) and nothing else.
+template <int BQ, bool F16IN, bool PROD, bool EDEN = false>
 __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
+  static_assert(!(EDEN && PROD), "the scale replaces the norm of MSE records only");
   constexpr int P = PROD ? BQ + 1 : BQ;
   const int lane = threadIdx.x & 63;
   const int64_t vec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);    // chunk-local
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
 #pragma unroll
   for (int p = 0; p < BQ; ++p) w[p] = 0u;
   float g2 = 0.f;
+  float yc = 0.f;   // EDEN: this lane's part of <y, c[idx]>
   half8 rh[VPL / 8], rl[VPL / 8];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -115,6 +118,7 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
     quantize2k<BQ>(y, a.cb, idx, chat);
 #pragma unroll
     for (int p = 0; p < BQ; ++p) w[p] |= (uint32_t)((idx >> p) & 1) << i;
+    if (EDEN) yc = fmaf(y, chat, yc);
     if (PROD) {
       const float r = y - chat;
       g2 = fmaf(r, r, g2);
@@ -135,6 +139,12 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
       rlo[q] = rl[q];
     }
   }
+  float scale = n;
+  if (EDEN) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) yc += shfl_xor_f(yc, o);
+    scale = n > 0.f && yc > 0.f ? n / yc : 0.f;
+  }
   const int64_t rec = a.slot ? a.slot[gv] : gv;
   uint32_t* dst = a.planes + rec * (P * (D2 / 32)) + lane * P;
 #pragma unroll
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
     if (PROD)
       reinterpret_cast<uint32_t*>(a.scalars)[rec] = (uint32_t)f16_bits(n) | ((uint32_t)f16_bits(sqrtf(g2)) << 16);
     else
-      a.scalars[rec] = f16_bits(n);
+      a.scalars[rec] = f16_bits(scale);
   }
 }
 
@@ -257,12 +267,18 @@ size_t encode2k_workspace(int64_t n) {
 }
 
 template <int BQ>
-hipError_t run_mse(const Encode2kArgs& a, bool f16, hipStream_t stream) {
+hipError_t run_mse(const Encode2kArgs& a, bool f16, bool eden, hipStream_t stream) {
   const unsigned g1 = (unsigned)((a.cn + 3) / 4);
-  if (f16)
+  if (eden) {
+    if (f16)
+      hipLaunchKernelGGL((encode2k_pass1<BQ, true, false, true>), dim3(g1), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((encode2k_pass1<BQ, false, false, true>), dim3(g1), dim3(256), 0, stream, a);
+  } else if (f16) {
     hipLaunchKernelGGL((encode2k_pass1<BQ, true, false>), dim3(g1), dim3(256), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL((encode2k_pass1<BQ, false, false>), dim3(g1), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -280,10 +296,10 @@ hipError_t launch_encode2k_mse(const EncodeArgs& e, hipStream_t stream) {
   a.v0 = 0;
   a.cn = e.n;
   switch (e.bq) {
-    case 1: return run_mse<1>(a, e.f16_in, stream);
-    case 2: return run_mse<2>(a, e.f16_in, stream);
-    case 3: return run_mse<3>(a, e.f16_in, stream);
-    case 4: return run_mse<4>(a, e.f16_in, stream);
+    case 1: return run_mse<1>(a, e.f16_in, e.eden, stream);
+    case 2: return run_mse<2>(a, e.f16_in, e.eden, stream);
+    case 3: return run_mse<3>(a, e.f16_in, e.eden, stream);
+    case 4: return run_mse<4>(a, e.f16_in, e.eden, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -105,3 +105,40 @@ def test_scores_read_the_eden_scale(bits):
     for s in range(2):
         sl = slice(600 * s, 600 * (s + 1))
         check_rows(got[4 * s:4 * s + 4], est.mse_scores(q[4 * s:4 * s + 4], code.idx[sl], code.n[sl], st.rot, st.c32))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 4])
+def test_eden_retrieval_records(bits):
+    # d = 1536 embeddings through the 2048-point Hadamard rotation: per-record
+    # MSE records with EDEN's scale, then the MSE-only top-k reads them
+    _log(f"eden retrieval records b{bits}: 3000 x 1536 -> 2048")
+    T = torch()
+    from tq_inputs import mixture_database
+    db, qs = mixture_database(3000, 1536, seed=34, n_queries=9)
+    st = Setup(d=1536, d_rot=2048, bits=bits, prod=False, rot="hadamard", seed=34)
+    cache = tq.alloc_key_cache(st.params, 3000)
+    tq.encode_eden(st.params, T.from_numpy(db).cuda(), cache, keys=True)
+    T.cuda.synchronize()
+    planes = cache.planes.cpu().numpy().view(np.uint32)
+    scal = cache.scalars.cpu().numpy()
+    idx = pk.unpack_value(planes, scal, bits)[0]
+    _log(f"  flips, scale ulps: {check_eden(st, idx, scal[:, 0], db)}")
+    if bits > 1:
+        # the MSE-only top-k over oracle-encoded, oracle-packed EDEN records:
+        # the returned estimates are the oracle's MSE inner products with the
+        # stored scales, to 1e-3 of each row's largest, and they are a top 10
+        code = qz.encode_eden(db.astype(np.float64), st.rot, st.c32, st.b32)
+        words, sc = pk.pack_value(code, bits)
+        oc = tq.Cache(T.from_numpy(words.view(np.int32)).cuda(), T.from_numpy(sc).cuda(), 0)
+        k = 10
+        ws = tq.alloc_workspace(tq.topk_workspace(st.params, 9, 3000, k))
+        gi = T.full((9, k), -1, dtype=T.int64, device="cuda")
+        gv = T.full((9, k), float("nan"), dtype=T.float32, device="cuda")
+        tq.scores_topk(st.params, T.from_numpy(qs).cuda(), oc, 3000, k, gi, gv, ws)
+        T.cuda.synchronize()
+        ref = est.mse_scores(qs, code.idx, code.n, st.rot, st.c32)
+        got_i, got_v = gi.cpu().numpy(), gv.cpu().numpy()
+        for r in range(9):
+            assert np.all(np.abs(got_v[r] - ref[r, got_i[r]]) <= 1e-3 * np.abs(ref[r]).max())
+            top = np.sort(ref[r])[::-1][:k]
+            assert np.all(np.abs(np.sort(got_v[r])[::-1] - top) <= 2e-3 * np.abs(ref[r]).max())
