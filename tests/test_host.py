@@ -165,3 +165,19 @@ def test_key_cache_shapes():
     assert tuple(full.planes.shape) == (5, 4, 3) and tuple(full.scalars.shape) == (5, 2)
     assert tuple(half.planes.shape) == (5, 10) and tuple(half.scalars.shape) == (5, 2)
     assert tuple(mse.planes.shape) == (5, 4, 3) and tuple(mse.scalars.shape) == (5, 1)
+
+
+def test_eden_and_mse_keys_validation_without_launch():
+    # argument checks of the MSE-record encoders fail on the host (fake pointers)
+    c, b = cb.lloyd_max(128, 3)
+    p = tq.Params(d=128, bits=3, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b)
+    p._c.pi = 0x10000
+    L = tq.lib()
+    cache = tq.tq_cache(0x2000, 0x3000, 0)
+    x = ctypes.c_void_p(0x1000)
+    assert L.tq_encode_eden(p.c, x, tq.TQ_F16, 4, 128, 7, cache, None, None) == tq.TQ_ERR_INVALID_ARG  # layout
+    assert L.tq_encode_eden(p.c, x, tq.TQ_F16, 0, 128, tq.TQ_LAYOUT_RECORDS, cache, None, None) == tq.TQ_OK
+    assert L.tq_encode_mse_keys(p.c, x, tq.TQ_F16, 4, 100, cache, None, None) == tq.TQ_ERR_INVALID_ARG  # ld_x < d
+    p._c.d, p._c.d_rot = 96, 96
+    assert L.tq_encode_eden(p.c, x, tq.TQ_F16, 4, 96, tq.TQ_LAYOUT_BLOCKS, cache, None, None) == \
+        tq.TQ_ERR_UNSUPPORTED
