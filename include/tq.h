@@ -271,7 +271,8 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
  * workgroup) and the per-segment merge with the inverse value rotation.
  * Supported: d = 128, group <= 16, value bits 1..4.  With kp->s == NULL the
  * keys are MSE-only records (tq_encode_mse_keys) scored as in tq_scores;
- * then key and value bits are 2..4, and 4-bit keys take group <= 8. */
+ * then key and value bits are 2..4, and 4-bit keys take group <= 8.  Prod
+ * keys with m = d_rot / 2 take value bits 2..4. */
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs,
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);
