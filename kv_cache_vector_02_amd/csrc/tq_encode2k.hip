@@ -63,6 +63,14 @@ template <int BQ, bool F16IN, bool PROD, bool EDEN = false>
 __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
   static_assert(!(EDEN && PROD), "the scale replaces the norm of MSE records only");
   constexpr int P = PROD ? BQ + 1 : BQ;
+  // EDEN reads c[idx] from an LDS table (a select chain over the centroids
+  // would hold them all in registers); every wave passes the barrier before
+  // any wave leaves
+  __shared__ float ctab[16];
+  if constexpr (EDEN) {
+    if (threadIdx.x < (1 << BQ)) ctab[threadIdx.x] = a.cb.c[threadIdx.x];
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int64_t vec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);    // chunk-local
   if (vec >= a.cn) return;
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
     quantize2k<BQ>(y, a.cb, idx, chat);
 #pragma unroll
     for (int p = 0; p < BQ; ++p) w[p] |= (uint32_t)((idx >> p) & 1) << i;
-    if (EDEN) yc = fmaf(y, chat, yc);
+    if (EDEN) yc = fmaf(y, ctab[idx], yc);
     if (PROD) {
       const float r = y - chat;
       g2 = fmaf(r, r, g2);
