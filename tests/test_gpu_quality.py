@@ -75,16 +75,17 @@ def test_attention_fidelity_unit_vectors(bits):
          f"(oracle {top1_o.mean():.2f}), near-tie argmax flips {flips}")
 
 
+@pytest.mark.parametrize("m", [128, 64])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_end_to_end_fidelity_with_gpu_encode(bits):
+def test_end_to_end_fidelity_with_gpu_encode(bits, m):
     # the harness's own path: GPU encode + scores.  Index and sign bits may
     # differ from the oracle's only within 1e-5 of a decision boundary, on at
     # most 1e-4 of the coordinates; each such key moves its score by about the
     # cell width times one query coordinate, far below the softmax's scale here.
-    _log(f"quality end-to-end b{bits}")
+    _log(f"quality end-to-end b{bits} m{m}")
     keys = unit_gaussian(2048, 128, seed=12)
     qs = unit_gaussian(100, 128, seed=12, purpose=QUERIES)
-    st = Setup(bits=bits, prod=True, seed=12)
+    st = Setup(bits=bits, prod=True, seed=12, m=m)
     r = quality.attention_fidelity(st.params, _dev(keys), _dev(qs))
     code = st.encode_oracle(keys)
     n16 = code.n.astype(np.float16).astype(np.float64)
