@@ -18,9 +18,11 @@ its section or equation):
 * ``packing``    -- the bit-plane record layout both sides agree on.
 * ``estimator``  -- the asymmetric inner-product estimator, MSE dequantization,
   softmax attention over the compressed cache and top-k retrieval.
+* ``quality``    -- attention-fidelity and needle statistics of an estimated
+  score matrix against the exact one (the first page's usage patterns).
 
 Parity pins: every function is pinned in ``tests/test_oracle_*.py`` to values
 the pages print, closed forms, invariants or brute force.  Functions without
 such a pin say "parity unpinned" in their docstring.
 """
-from . import codebook, transforms, quantizer, packing, estimator  # noqa: F401
+from . import codebook, transforms, quantizer, packing, estimator, quality  # noqa: F401
