@@ -51,6 +51,51 @@ def test_qjl_unbiased_with_variance_bound():
     assert np.var(ests) <= np.pi / (2 * m) * (x @ x) * (q @ q) * 1.05
 
 
+def test_qjl_unbiased_with_half_as_many_rows():
+    # m = d / 2 projection rows (the first page's proj_dim = head_dim // 2):
+    # the constant is sqrt(pi/2) / m, not / d (explainer page section 8,
+    # Lemma 4).  A constant over d would centre the estimates on (m/d) <q, x>,
+    # half the truth, about a hundred standard errors away.
+    d, m = 16, 8
+    x, q = _pair(d, 0.6, seed=21)
+    x = 2.5 * x
+    ests = []
+    for seed in range(20000):
+        s = gaussian_matrix(m, d, seed)
+        z = (s.astype(np.float64) @ x) >= 0
+        ests.append(est.qjl_scores(q[None, :], z[None, :], np.array([np.linalg.norm(x)]), s)[0, 0])
+    mu, se = mean_se(ests)
+    assert abs(mu - q @ x) < 3 * se
+    assert abs(mu - (m / d) * (q @ x)) > 30 * se
+    # the variance bound pi / (2 m) ||x||^2 ||q||^2 holds with m rows, and the
+    # variance is larger than with m = d rows (fewer rows average less)
+    var = np.var(ests)
+    assert var <= np.pi / (2 * m) * (x @ x) * (q @ q) * 1.05
+    assert var > np.pi / (2 * d) * (x @ x) * (q @ q)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_prod_unbiased_with_half_as_many_rows(bits):
+    # prod with an m x d QJL matrix, m = d / 2: still unbiased over (Pi, S),
+    # and within the QJL variance bound applied to the residual,
+    # Var <= pi / (2 m) n^2 E||r||^2 ||q||^2
+    d, m = 32, 16
+    c, b = cb.lloyd_max(d, bits - 1)
+    x, q = _pair(d, 0.5, seed=30 + bits)
+    x = 3.0 * x
+    ests, r2 = [], []
+    for seed in range(10000):
+        rot = tr.DenseRotation(haar_orthogonal(d, seed))
+        s = gaussian_matrix(m, d, seed)
+        code = qz.encode_prod(x[None, :], rot, s, c, b, storage=False)
+        assert code.z.shape == (1, m)
+        ests.append(est.prod_scores(q[None, :], code.idx, code.z, code.n, code.gamma, rot, s, c)[0, 0])
+        r2.append(code.gamma[0] ** 2)
+    mu, se = mean_se(ests)
+    assert abs(mu - q @ x) < 3 * se
+    assert np.var(ests) <= np.pi / (2 * m) * 9.0 * np.mean(r2) * (q @ q) * 1.05
+
+
 @pytest.mark.parametrize("bits", [2, 3])
 def test_prod_estimator_unbiased_over_rotations(bits):
     # E over (Pi, S) of the prod estimate equals <q, x> (blog notes eq. (3))
