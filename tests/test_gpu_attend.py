@@ -6,7 +6,7 @@ import pytest
 import kv_cache_vector_02_amd as tq
 from oracle import estimator as est
 from oracle import packing as pk
-from tests.gpu_util import Setup, torch
+from tests.gpu_util import Setup, compare_encode, torch
 from tests.test_gpu_scores import oracle_key_cache
 from tq_inputs import gaussian_queries, kv_tensor
 
@@ -120,10 +120,10 @@ def test_hadamard_rotations():
                     oracle_attend(sk, sv, q[s * 4:(s + 1) * 4], kf, vidx, vn, sl, 1 / np.sqrt(128)))
 
 
-def test_qwen_shaped_full_size_sampled():
+def test_qwen_shaped_full_size():
     # 36 layers x 2 KV heads x 8192 tokens, 16 query heads per layer (G=8),
-    # keys prod b=3, values mse b=3, one launch; the oracle checks 8 segments
-    _log("attend qwen-shaped full size (sampled segments)")
+    # keys prod b=3, values mse b=3, one launch; every segment against the oracle
+    _log("attend qwen-shaped full size (every segment)")
     L_, H_, T_ = 36, 2, 8192
     sk, sv = _setups(3, 3, seed=1)
     xk = kv_tensor(L_, H_, T_, 128, seed=1).reshape(-1, 128)
@@ -134,16 +134,66 @@ def test_qwen_shaped_full_size_sampled():
     q = gaussian_queries(segs * group, 128, seed=1)
     scale = 1 / np.sqrt(128)
     got = gpu_attend(sk, sv, q, segs, group, kc, vc, T_, scale)
-    assert np.isfinite(got).all()
     worst = 0.0
-    for s in np.random.default_rng(2).choice(segs, 8, replace=False).tolist() + [segs - 1]:
+    for s in range(segs):
         sl = slice(s * T_, (s + 1) * T_)
         rows = slice(s * group, (s + 1) * group)
         worst = max(worst, check_heads(got[rows], oracle_attend(sk, sv, q[rows], kf, vidx, vn, sl, scale)))
     _log(f"  worst rel {worst:.2e}")
 
 
+def _flip_allowance(sk, sv, q, kcode, vcode, scale, k_idx, k_z, v_idx):
+    """Per head, how far the output may move because the encoder took the
+    other side of a decision inside the 1e-5 band (the encode tests'
+    allowance), to first order in the softmax.  k_idx / k_z / v_idx are the
+    encoder's key indices, key signs and value indices; where they differ from
+    the oracle's (each such coordinate is first checked to lie in the band),
+    the oracle re-encodes that record with the encoder's decision and takes
+    the change it makes:
+      value (t, j): o moves by at most p_t n_t |c_v[idx'] - c_v[idx]| max_i |Pi_v^T[i, j]|
+      key t: its score moves by delta_t = |s'(q, t) - s(q, t)| (neighbouring
+      cell: new residual, gamma and signs from the oracle; a flipped sign: that
+      sign), so o moves by at most |scale| p_t delta_t ||v_t - o||_inf."""
+    band = 1e-5
+    ck = np.asarray(sk.c32, np.float64)
+    cv = np.asarray(sv.c32, np.float64)
+    smat = np.asarray(sk.s, np.float64)
+    kn = kcode.n.astype(np.float16).astype(np.float64)
+    kg = kcode.gamma.astype(np.float16).astype(np.float64)
+    vn = vcode.n.astype(np.float16).astype(np.float64)
+    s = est.prod_scores(q, kcode.idx, kcode.z, kn, kg, sk.rot, sk.s, sk.c32)
+    a = scale * s
+    p = np.exp(a - a.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    v = est.dequantize(vcode.idx, vn, sv.rot, sv.c32)
+    o = p @ v
+    q_rot, q_proj = est.prepare_query(q, sk.rot, sk.s)
+    kap = est.kappa(sk.m)
+    bound = np.zeros(q.shape[0])
+    # the inverse value rotation's largest entry per rotated coordinate
+    spread = np.max(np.abs(sv.rot.inverse(np.eye(sv.d_rot))), axis=1)
+    for t, j in zip(*np.nonzero(v_idx != vcode.idx)):
+        assert np.min(np.abs(vcode.y[t, j] - np.asarray(sv.b32, np.float64))) < band
+        bound += p[:, t] * vn[t] * abs(cv[v_idx[t, j]] - cv[vcode.idx[t, j]]) * spread[j]
+    for t in np.nonzero(np.any(k_idx != kcode.idx, axis=1) | np.any(k_z != kcode.z, axis=1))[0]:
+        if np.any(k_idx[t] != kcode.idx[t]):
+            alt = k_idx[t]
+            r = kcode.y[t] - ck[alt]
+            g = np.float64(np.float16(np.sqrt(r @ r)))
+            z = (smat @ r) >= 0
+        else:
+            alt, g, z = kcode.idx[t], kg[t], k_z[t]
+        s_alt = kn[t] * (q_rot @ ck[alt] + g * kap * (q_proj @ (2.0 * z - 1.0)))
+        bound += abs(scale) * p[:, t] * np.abs(s_alt - s[:, t]) * np.max(np.abs(v[t][None, :] - o), axis=1)
+    return 2.0 * bound
+
+
 def test_end_to_end_gpu_encode_then_attend():
+    # GPU encode + GPU attend against oracle encode + oracle attend.  The
+    # encoder may take the other side of a decision within 1e-5 of a boundary
+    # (checked record by record first); the tolerance is 1e-3 of the head's
+    # largest output magnitude plus the oracle's bound on what those decisions
+    # move (zero when the encodes agree bit for bit).
     _log("attend end to end")
     Tt = torch()
     segs, T_ = 2, 1024
@@ -159,15 +209,28 @@ def test_end_to_end_gpu_encode_then_attend():
     got = gpu_attend(sk, sv, q, segs, 8, kc, vc, T_, scale)
     kcode = sk.encode_oracle(xk)
     vcode = sv.encode_oracle(xv)
+    kplanes, kscal = kc.planes.cpu().numpy().view(np.uint32), kc.scalars.cpu().numpy()
+    vidx_gpu = pk.unpack_value_blocks(vc.planes.cpu().numpy().view(np.uint32), segs * T_)
+    ks = compare_encode(sk, kplanes, kscal, kcode)
+    vs = compare_encode(sv, vidx_gpu, vc.scalars.cpu().numpy(), vcode)
+    _log(f"  encode flips: keys {ks}, values {vs}")
+    kidx_gpu, kz_gpu, _, _ = pk.unpack_key(kplanes, kscal, sk.bq, d=128)
     kf = (kcode.idx, kcode.z, kcode.n.astype(np.float16).astype(np.float64),
           kcode.gamma.astype(np.float16).astype(np.float64))
     vn = vcode.n.astype(np.float16).astype(np.float64)
     for s in range(segs):
         sl = slice(s * T_, (s + 1) * T_)
-        ref = oracle_attend(sk, sv, q[s * 8:(s + 1) * 8], kf, vcode.idx, vn, sl, scale)
-        err = np.max(np.abs(got[s * 8:(s + 1) * 8] - ref), axis=1) / np.max(np.abs(ref), axis=1)
-        _log(f"  segment {s}: worst rel {err.max():.2e}")
-        assert err.max() < 1e-2   # encode flips near boundaries allowed; reported above
+        rows = slice(s * 8, (s + 1) * 8)
+        ref = oracle_attend(sk, sv, q[rows], kf, vcode.idx, vn, sl, scale)
+        sub_k = type(kcode)(idx=kcode.idx[sl], z=kcode.z[sl], n=kcode.n[sl], gamma=kcode.gamma[sl],
+                            y=kcode.y[sl], proj=kcode.proj[sl])
+        sub_v = type(vcode)(idx=vcode.idx[sl], n=vcode.n[sl], y=vcode.y[sl])
+        extra = _flip_allowance(sk, sv, q[rows], sub_k, sub_v, scale, kidx_gpu[sl], kz_gpu[sl], vidx_gpu[sl])
+        err = np.max(np.abs(got[rows] - ref), axis=1)
+        top = np.max(np.abs(ref), axis=1)
+        _log(f"  segment {s}: worst rel {np.max(err / top):.2e}; flip allowance up to "
+             f"{np.max(extra / top):.2e} of the head's maximum")
+        assert np.all(err <= REL_TOL * top + extra)
 
 
 def smoke_attend():

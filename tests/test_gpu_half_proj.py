@@ -150,11 +150,11 @@ def test_attend_hadamard():
         check_heads(got[4 * s:4 * s + 4], ref)
 
 
-def test_qwen_shaped_full_size_sampled():
+def test_qwen_shaped_full_size():
     # 36 layers x 2 KV heads x 8192 tokens, G = 8, b = 3, m = 64: the score
-    # pass bench.py times, every segment in one launch; the oracle checks every
-    # head on sampled tokens (the row scale is the full row's maximum)
-    _log("m=64 scores qwen-shaped full size (sampled tokens)")
+    # pass bench.py times, every segment in one launch; every token of every
+    # segment against the oracle, to 1e-3 of the oracle's row maximum
+    _log("m=64 scores qwen-shaped full size (every token)")
     L_, H_, T_ = 36, 2, 8192
     x = kv_tensor(L_, H_, T_, 128, seed=1).reshape(-1, 128)
     st = Setup(bits=3, seed=1, m=64)
@@ -162,16 +162,10 @@ def test_qwen_shaped_full_size_sampled():
     segs, group = L_ * H_, 8
     q = gaussian_queries(segs * group, 128, seed=1)
     got = gpu_scores(st, q, segs, group, cache, T_)
-    assert np.isfinite(got).all()
-    tok = np.sort(np.random.default_rng(1).choice(T_, 256, replace=False))
-    tok[-1] = T_ - 1
     worst = 0.0
     for s in range(segs):
-        sl = s * T_ + tok
+        sl = slice(s * T_, (s + 1) * T_)
         rows = slice(s * group, (s + 1) * group)
         ref = est.prod_scores(q[rows], idx[sl], z[sl], n[sl], g[sl], st.rot, st.s, st.c32)
-        full = np.max(np.abs(got[rows]), axis=1)
-        err = np.max(np.abs(got[rows][:, tok] - ref), axis=1)
-        assert np.all(err <= 1e-3 * full)
-        worst = max(worst, float(np.max(err / full)))
+        worst = max(worst, check_rows(got[rows], ref))
     _log(f"  worst rel {worst:.2e}")

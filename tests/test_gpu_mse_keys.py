@@ -175,10 +175,11 @@ def test_attend_4bit_keys_reject_16_heads():
         tq.attend(sk.params, sv.params, q, 1, 16, kc, vc, 64, 1.0, out, ws)
 
 
-def test_qwen_shaped_full_size_sampled():
+def test_qwen_shaped_full_size():
     # 36 layers x 2 KV heads x 8192 tokens, G = 8, MSE-only b = 3 keys: the
-    # score pass bench.py times, every segment in one launch; sampled tokens
-    _log("mse keys scores qwen-shaped full size (sampled tokens)")
+    # score pass bench.py times, every segment in one launch; every token of
+    # every segment against the oracle, to 1e-3 of the oracle's row maximum
+    _log("mse keys scores qwen-shaped full size (every token)")
     L_, H_, T_ = 36, 2, 8192
     x = kv_tensor(L_, H_, T_, 128, seed=1).reshape(-1, 128)
     st = _setup(3, seed=1)
@@ -186,16 +187,9 @@ def test_qwen_shaped_full_size_sampled():
     segs, group = L_ * H_, 8
     q = gaussian_queries(segs * group, 128, seed=1)
     got = gpu_scores(st, q, segs, group, cache, T_)
-    assert np.isfinite(got).all()
-    tok = np.sort(np.random.default_rng(1).choice(T_, 256, replace=False))
-    tok[-1] = T_ - 1
     worst = 0.0
     for s in range(segs):
-        sl = s * T_ + tok
+        sl = slice(s * T_, (s + 1) * T_)
         rows = slice(s * group, (s + 1) * group)
-        ref = est.mse_scores(q[rows], idx[sl], n[sl], st.rot, st.c32)
-        full = np.max(np.abs(got[rows]), axis=1)
-        err = np.max(np.abs(got[rows][:, tok] - ref), axis=1)
-        assert np.all(err <= 1e-3 * full)
-        worst = max(worst, float(np.max(err / full)))
+        worst = max(worst, check_rows(got[rows], est.mse_scores(q[rows], idx[sl], n[sl], st.rot, st.c32)))
     _log(f"  worst rel {worst:.2e}")

@@ -98,10 +98,11 @@ def test_seg_stride_larger_than_T():
         check_rows(got[s * 8:(s + 1) * 8], ref)
 
 
-def test_qwen_shaped_full_size_sampled():
+def test_qwen_shaped_full_size():
     # 36 layers x 2 KV heads x 8192 tokens, G=8 (16 query heads per layer), b=3,
-    # every segment in one launch; the oracle checks every head on sampled tokens
-    _log("scores qwen-shaped full size (sampled tokens)")
+    # every segment in one launch; every score of every segment against the
+    # oracle, each row to 1e-3 of the oracle's own largest magnitude
+    _log("scores qwen-shaped full size (every token of every segment)")
     L_, H_, T_ = 36, 2, 8192
     x = kv_tensor(L_, H_, T_, 128, seed=1).reshape(-1, 128)
     st = Setup(bits=3, prod=True, seed=1)
@@ -109,19 +110,12 @@ def test_qwen_shaped_full_size_sampled():
     segs, group = L_ * H_, 8
     q = gaussian_queries(segs * group, 128, seed=1)
     got = gpu_scores(st, q, segs, group, cache, T_)
-    assert np.isfinite(got).all()
-    rg = np.random.default_rng(1)
-    tok = np.sort(rg.choice(T_, 256, replace=False))
-    tok[-1] = T_ - 1
     worst = 0.0
     for s in range(segs):
-        sl = s * T_ + tok
-        ref = est.prod_scores(q[s * group:(s + 1) * group], idx[sl], z[sl], n[sl], g[sl],
-                              st.rot, st.s, st.c32)
-        full_scale = np.max(np.abs(got[s * group:(s + 1) * group]), axis=1)
-        err = np.max(np.abs(got[s * group:(s + 1) * group][:, tok] - ref), axis=1)
-        assert np.all(err <= REL_TOL * full_scale)
-        worst = max(worst, float(np.max(err / full_scale)))
+        sl = slice(s * T_, (s + 1) * T_)
+        rows = slice(s * group, (s + 1) * group)
+        ref = est.prod_scores(q[rows], idx[sl], z[sl], n[sl], g[sl], st.rot, st.s, st.c32)
+        worst = max(worst, check_rows(got[rows], ref))
     _log(f"  worst rel {worst:.2e}")
 
 
@@ -154,10 +148,7 @@ def smoke_scores_attend():
     got = gpu_scores(st, q, 1, 8, cache, 256)
     ref = est.prod_scores(q, idx, z, n, g, st.rot, st.s, st.c32)
     print(f"smoke scores ok, worst rel {check_rows(got, ref):.2e}", flush=True)
-    try:
-        from tests.test_gpu_attend import smoke_attend
-    except ImportError:
-        return
+    from tests.test_gpu_attend import smoke_attend
     smoke_attend()
 
 

@@ -31,6 +31,7 @@ OUTLIER_CHANNELS_V = 12
 CHANNEL_SCALES_V = 13
 NEEDLE_POSITIONS = 14
 NEEDLE_NOISE = 15
+RANDOM_RECORDS = 16
 
 
 def rng(seed: int, purpose: int) -> np.random.Generator:
@@ -154,3 +155,18 @@ def mixture_database(n: int, d: int, n_components: int = 64, seed: int = 4,
     db = draw(n, MIXTURE_LABELS, DATA)
     qs = draw(n_queries, MIXTURE_LABELS + 100, QUERIES) if n_queries else np.zeros((0, d), np.float32)
     return db, qs
+
+
+def random_record_words(n: int, words_per_record: int, seed: int, scalar_ranges=((0.0, 1.0),)):
+    """n records of uniformly random 32-bit plane words and float16 scalars.
+
+    Every bit pattern is a valid code (uniformly random cell indices and sign
+    bits), so these fill a packed cache at full size without encoding
+    anything.  Returns (words [n, words_per_record] uint32, scalars [n, k]
+    float16), scalar column j uniform on scalar_ranges[j]."""
+    r = rng(seed, RANDOM_RECORDS)
+    words = r.integers(0, 1 << 32, size=(n, words_per_record), dtype=np.uint64).astype(np.uint32)
+    lo = np.array([a for a, _ in scalar_ranges])
+    hi = np.array([b for _, b in scalar_ranges])
+    sc = (lo[None, :] + (hi - lo)[None, :] * r.random((n, len(scalar_ranges)))).astype(np.float16)
+    return words, sc
