@@ -18,9 +18,8 @@
  *     implement returns TQ_ERR_UNSUPPORTED, and in both cases nothing is
  *     launched.  A failed launch returns TQ_ERR_HIP.  tq_last_error() gives a
  *     thread-local message for the last non-OK status.
- *   - Calls may be made from any thread.  The only process-wide state is an
- *     atomic counter of tq_scores tickets and the tq_debug_set_pack_wait
- *     bound (an atomic integer); nothing else outlives a call.
+ *   - Calls may be made from any thread.  The library keeps no mutable state
+ *     between calls.
  *
  * Packed records (the layout the pages' storage accounting implies: b bits
  * per coordinate of codes, one sign bit per projection row, float16 norms):
@@ -63,6 +62,8 @@ typedef enum {
 } tq_status;
 
 typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 } tq_rot;
+/* Values of the int dtype and layout arguments (passed as int so that any
+ * value a caller passes is defined and rejected when it names none of these). */
 typedef enum { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
 /* Record layout of an MSE encode (tq_encode_eden). */
 typedef enum { TQ_LAYOUT_BLOCKS = 0, TQ_LAYOUT_RECORDS = 1 } tq_layout;
@@ -100,14 +101,20 @@ typedef struct {
 
 /* A packed cache, device memory owned by the caller (layout above).
  * seg_stride is the number of records between consecutive segments; it is
- * used by tq_scores / tq_attend and ignored by the encoders. */
+ * used by tq_scores / tq_attend and ignored by the encoders.
+ * records is the capacity: the number of records planes and scalars hold (a
+ * value cache's planes hold ceil(records / 32) blocks).  The encoders write
+ * no record at or past it (a slot outside [0, records) is skipped on the
+ * device), and the decode calls return TQ_ERR_INVALID_ARG when the records
+ * they would read do not fit in it. */
 typedef struct {
   void* planes;
   void* scalars;
   int64_t seg_stride;
+  int64_t records;
 } tq_cache;
 
-const char* tq_status_string(tq_status s);
+const char* tq_status_string(int s);
 const char* tq_last_error(void);
 
 /* Lloyd-Max codebook for one coordinate of a uniformly rotated unit vector
@@ -135,6 +142,13 @@ tq_status tq_value_layout(const tq_params* p, int* planes, int* words_per_plane,
  * above.  MSE-only key records hold b words per group. */
 size_t tq_key_record_words(const tq_params* p);
 
+/* Bytes of one key record (plane words plus float16 scalars) and of one value
+ * record (its share of the block words plus its float16 norm), 0 for invalid
+ * parameters: the storage accounting of the first page's memory formula
+ * (52 and 50 bytes at d = 128, b = 3; 5.02x smaller than float16 K and V). */
+size_t tq_key_record_bytes(const tq_params* p);
+size_t tq_val_record_bytes(const tq_params* p);
+
 /* TurboQuant-prod encode of n vectors (keys) into a packed cache.
  * Blog notes on the paper, the Q_prod definition; explainer page section 8:
  *   n_x = ||x||, u = x/n_x (0 if n_x = 0), y = rot(u),
@@ -142,10 +156,11 @@ size_t tq_key_record_words(const tq_params* p);
  *   z = [S r >= 0]; stores float16 n_x and gamma (round to nearest even).
  * x      device [n][ld_x] of dtype (f32 or f16), rows are vectors, ld_x >= d
  * slot   device int64 [n] record index for each vector, or NULL for 0..n-1
- * out    cache with planes/scalars of p's key layout; every written record
- *        index must lie inside the caller's arrays (not checked on device)
+ * out    cache with planes/scalars of p's key layout and out.records >= 1;
+ *        a vector whose record index lies outside [0, out.records) is not
+ *        written
  * Supported: d_rot = 128 (dense or Hadamard) and Hadamard d_rot = 2048. */
-tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+tq_status tq_encode_prod(const tq_params* p, const void* x, int dtype, int64_t n,
                          int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
 /* Workspace bytes tq_encode_prod_ws needs for n vectors: 0 at d_rot = 128;
@@ -161,7 +176,7 @@ size_t tq_encode_workspace(const tq_params* p, int64_t n);
  * registers (one wave per vector) and quantises; pass 2 forms the QJL
  * projection S r of each chunk of residuals on the matrix cores.  Records use
  * the key layout of tq_key_layout (W = 64 words per plane). */
-tq_status tq_encode_prod_ws(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+tq_status tq_encode_prod_ws(const tq_params* p, const void* x, int dtype, int64_t n,
                             int64_t ld_x, tq_cache out, const int64_t* slot, void* ws,
                             size_t ws_bytes, void* stream);
 
@@ -175,7 +190,7 @@ tq_status tq_encode_prod_ws(const tq_params* p, const void* x, tq_dtype dtype, i
  * tq_key_layout with b planes and one fp16 scalar ||x||_2 per record (no
  * workspace, one launch, one wave per vector); these are the MSE-only
  * retrieval records read by tq_scores_topk. */
-tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+tq_status tq_encode_mse(const tq_params* p, const void* x, int dtype, int64_t n,
                         int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
 /* TurboQuant-MSE encode of keys (blog notes on the paper, Q_mse: the
@@ -187,7 +202,7 @@ tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64
  * tq_encode_prod.  Supported: d = d_rot = 128 (dense or Hadamard), and the
  * Hadamard rotation at d_rot = 2048, where the records are those of
  * tq_encode_mse. */
-tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, int64_t n,
+tq_status tq_encode_mse_keys(const tq_params* p, const void* x, int dtype, int64_t n,
                              int64_t ld_x, tq_cache out, const int64_t* slot, void* stream);
 
 /* MSE encode with EDEN's unbiased per-vector scale (the prior-work map of the
@@ -206,8 +221,8 @@ tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, 
  * Hadamard rotation at d_rot = 2048, whose MSE records are always per record
  * (the retrieval records of tq_scores_topk with kp->s == NULL; layout is
  * ignored there). */
-tq_status tq_encode_eden(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
-                         tq_layout layout, tq_cache out, const int64_t* slot, void* stream);
+tq_status tq_encode_eden(const tq_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
+                         int layout, tq_cache out, const int64_t* slot, void* stream);
 
 /* Workspace bytes tq_scores needs for segs segments of group query heads. */
 size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
@@ -230,10 +245,13 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
  *         call in flight per workspace.
  * One launch on the stream: per segment, the first workgroup builds the query
  * pack while the others already stream their first keys; they take the pack
- * when its workgroup signals it (a per-call ticket in the workspace, release
- * and acquire at device scope), or, if it has not come within a bounded wait
- * (tq_debug_set_pack_wait), build the same pack themselves.  Each call leaves
- * the hand-over words cleared, so a captured launch can be replayed. */
+ * when its builder publishes a per-call ticket in the workspace.  The pack and
+ * the ticket words are written and read with device-coherent (sc1) accesses
+ * and relaxed device-scope atomics, so no cache flush is needed.  A workgroup
+ * that has waited 200 us without the pack (its producer not yet resident)
+ * claims the pack and builds it itself; exactly one workgroup per segment and
+ * call writes the pack.  Each call leaves the ticket words cleared, so a
+ * captured launch can be replayed. */
 tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
                     const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
                     void* stream);
@@ -247,12 +265,6 @@ tq_status tq_scores_prepare(const tq_params* kp, const float* q, int segs, int g
                             size_t ws_bytes, void* stream);
 tq_status tq_scores_prepared(const tq_params* kp, int segs, int group, tq_cache keys, const int32_t* len,
                              int64_t T, float* scores, void* ws, size_t ws_bytes, void* stream);
-
-/* Testing control of tq_scores: the bound, in microseconds, on a workgroup's
- * wait for its segment's query pack (default 200; process-wide, thread-safe).
- * 0 makes every workgroup build the pack itself, the path taken when the wait
- * runs out; results are the same either way. */
-void tq_debug_set_pack_wait(int microseconds);
 
 /* Workspace bytes tq_attend needs. */
 size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T);
@@ -271,7 +283,9 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
  * workgroup) and the per-segment merge with the inverse value rotation.
  * Supported: d = 128, group <= 16, value bits 1..4.  With kp->s == NULL the
  * keys are MSE-only records (tq_encode_mse_keys) scored as in tq_scores;
- * then key and value bits are 2..4, and 4-bit keys take group <= 8.  Prod
+ * then key and value bits are 2..4, and 4-bit keys take group <= 8 or an even
+ * group <= 16 (run as two halves of group / 2 heads that each read the
+ * segment's keys and values, so such a call reads the cache twice).  Prod
  * keys with m = d_rot / 2 take value bits 2..4. */
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs,
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,

@@ -27,8 +27,10 @@ EXPORTED = (
     "tq_value_layout", "tq_key_record_words", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_eden", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
-    "tq_debug_set_pack_wait",
+    "tq_key_record_bytes", "tq_val_record_bytes",
 )
+# measurement and testing entry points (include/tq_testing.h)
+EXPORTED_TESTING = ("tq_testing_stream", "tq_testing_scores_wait")
 
 
 class TQError(RuntimeError):
@@ -50,7 +52,7 @@ class tq_params(ctypes.Structure):
 
 class tq_cache(ctypes.Structure):
     _fields_ = [("planes", ctypes.c_void_p), ("scalars", ctypes.c_void_p),
-                ("seg_stride", ctypes.c_int64)]
+                ("seg_stride", ctypes.c_int64), ("records", ctypes.c_int64)]
 
 
 _lib = None
@@ -92,12 +94,18 @@ def lib():
         L.tq_attend_workspace.argtypes = [P, P, ci, ci, i64]
         L.tq_attend.argtypes = [P, P, vp, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
                                 vp, vp, sz, vp]
-        L.tq_debug_set_pack_wait.restype = None
-        L.tq_debug_set_pack_wait.argtypes = [ci]
+        L.tq_key_record_bytes.restype = sz
+        L.tq_key_record_bytes.argtypes = [P]
+        L.tq_val_record_bytes.restype = sz
+        L.tq_val_record_bytes.argtypes = [P]
+        L.tq_testing_scores_wait.restype = ci
+        L.tq_testing_scores_wait.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp, sz, ci, vp]
+        L.tq_testing_stream.restype = ci
+        L.tq_testing_stream.argtypes = [vp, sz, vp, sz, ci, ci, vp]
         for name in EXPORTED:
             if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace", "tq_key_record_words",
                             "tq_attend_workspace", "tq_encode_workspace", "tq_scores_topk_workspace",
-                            "tq_debug_set_pack_wait"):
+                            "tq_key_record_bytes", "tq_val_record_bytes"):
                 getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -174,14 +182,19 @@ def value_layout(p: Params):
 @dataclass
 class Cache:
     """A packed cache in device memory: plane words int32 [records, W, P] (word w of
-    plane p at w * P + p), scalars float16 [records, S]."""
+    plane p at w * P + p), scalars float16 [records, S].  Its capacity (tq_cache
+    records) is the scalars' row count."""
     planes: object
     scalars: object
     seg_stride: int = 0
 
     @property
+    def records(self) -> int:
+        return int(self.scalars.shape[0])
+
+    @property
     def c(self):
-        return tq_cache(self.planes.data_ptr(), self.scalars.data_ptr(), int(self.seg_stride))
+        return tq_cache(self.planes.data_ptr(), self.scalars.data_ptr(), int(self.seg_stride), self.records)
 
 
 def alloc_cache(layout, records: int, seg_stride: int = 0, device="cuda"):
@@ -295,10 +308,14 @@ def scores_prepared(kp: Params, segs: int, group: int, keys: Cache, T: int, out,
                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def debug_set_pack_wait(microseconds: int):
-    """tq_debug_set_pack_wait: bound on a tq_scores workgroup's wait for its
-    segment's query pack (0: every workgroup builds the pack itself)."""
-    lib().tq_debug_set_pack_wait(int(microseconds))
+def key_record_bytes(p: Params) -> int:
+    """Bytes of one key record (tq_key_record_bytes)."""
+    return int(lib().tq_key_record_bytes(p.c))
+
+
+def val_record_bytes(p: Params) -> int:
+    """Bytes of one value record (tq_val_record_bytes)."""
+    return int(lib().tq_val_record_bytes(p.c))
 
 
 def attend_workspace(kp: Params, vp: Params, segs: int, group: int, T: int) -> int:
@@ -320,3 +337,19 @@ def scores_topk(kp: Params, q, keys: Cache, T: int, k: int, idx, val, ws, stream
     """tq_scores_topk: idx int64 [nq][k], val float32 [nq][k] (device tensors)."""
     _check(lib().tq_scores_topk(kp.c, _ptr(q), q.shape[0], keys.c, int(T), int(k), _ptr(idx), _ptr(val),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def testing_stream(src, read_bytes: int, dst, write_bytes: int, store_policy: int = 1, workgroups: int = 0,
+                   stream=None):
+    """tq_testing_stream: a plain HBM stream reading read_bytes of src and writing
+    write_bytes of dst side by side (the bandwidth ceiling for that mix)."""
+    _check(lib().tq_testing_stream(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes), int(store_policy),
+                                   int(workgroups), _stream(stream)))
+
+
+def testing_scores_wait(kp: Params, q, segs: int, group: int, keys: Cache, T: int, out, ws, wait_us: int,
+                        length=None, stream=None):
+    """tq_testing_scores_wait: tq_scores with an explicit bound on the wait for
+    each segment's query pack (0: the build-it-yourself path)."""
+    _check(lib().tq_testing_scores_wait(kp.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),
+                                        _ptr(ws), ws.numel() * ws.element_size(), int(wait_us), _stream(stream)))

@@ -6,6 +6,7 @@
 #include <string>
 
 #include "tq_internal.h"
+#include "../../include/tq_testing.h"
 
 namespace {
 
@@ -87,7 +88,7 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
 
 // prod: TurboQuant-prod keys; otherwise MSE-only, as values (token-blocked
 // layout at d_rot = 128) or, with mse_keys, as per-record key records.
-tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, int64_t n,
+tq_status encode(const tq_params* p, bool prod, const void* x, int dtype, int64_t n,
                  int64_t ld_x, tq_cache out, const int64_t* slot, void* ws, size_t ws_bytes, void* stream,
                  bool mse_keys = false, bool eden = false) {
   tq::EncodeArgs a;
@@ -100,6 +101,7 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   const size_t esz = dtype == TQ_F16 ? 2 : 4;
   if (n == 0) return TQ_OK;
   if (!x || !out.planes || !out.scalars) return fail(TQ_ERR_INVALID_ARG, "x and the cache arrays must be non-NULL");
+  if (out.records < 1) return fail(TQ_ERR_INVALID_ARG, "out.records (the cache's capacity) must be >= 1");
   if (!aligned(x, 16) || (ld_x * esz) % 16)
     return fail(TQ_ERR_INVALID_ARG, "x must be 16-byte aligned with rows a multiple of 16 bytes");
   if (!aligned(out.planes, 16) || !aligned(out.scalars, 4))
@@ -123,6 +125,7 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
   a.planes = (uint32_t*)out.planes;
   a.scalars = (uint16_t*)out.scalars;
   a.slot = slot;
+  a.records = out.records;
   a.had = p->rot == TQ_ROT_HADAMARD;
   hipStream_t s = (hipStream_t)stream;
   if (p->d == 128 && p->d_rot == 128)
@@ -149,7 +152,7 @@ tq_status encode(const tq_params* p, bool prod, const void* x, tq_dtype dtype, i
 
 extern "C" {
 
-const char* tq_status_string(tq_status s) {
+const char* tq_status_string(int s) {
   switch (s) {
     case TQ_OK: return "TQ_OK";
     case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
@@ -187,6 +190,17 @@ size_t tq_key_record_words(const tq_params* p) {
   return qjl ? (size_t)w * (p->bits - 1) + p->m / 32 : (size_t)w * p->bits;
 }
 
+size_t tq_key_record_bytes(const tq_params* p) {
+  const size_t w = tq_key_record_words(p);
+  return w ? 4 * w + 2 * (p->s ? 2 : 1) : 0;
+}
+
+size_t tq_val_record_bytes(const tq_params* p) {
+  tq::Codebook cb;
+  if (check_params(p, false, &cb, false) != TQ_OK) return 0;
+  return (size_t)p->d_rot * p->bits / 8 + 2;
+}
+
 tq_status tq_value_layout(const tq_params* p, int* planes, int* words, int* scalars) {
   tq::Codebook cb;
   tq_status st = check_params(p, false, &cb, false);
@@ -197,7 +211,7 @@ tq_status tq_value_layout(const tq_params* p, int* planes, int* words, int* scal
   return TQ_OK;
 }
 
-tq_status tq_encode_prod(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+tq_status tq_encode_prod(const tq_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
                          tq_cache out, const int64_t* slot, void* stream) {
   return encode(p, true, x, dtype, n, ld_x, out, slot, nullptr, 0, stream);
 }
@@ -208,23 +222,23 @@ size_t tq_encode_workspace(const tq_params* p, int64_t n) {
   return 0;
 }
 
-tq_status tq_encode_prod_ws(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+tq_status tq_encode_prod_ws(const tq_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
                             tq_cache out, const int64_t* slot, void* ws, size_t ws_bytes, void* stream) {
   return encode(p, true, x, dtype, n, ld_x, out, slot, ws, ws_bytes, stream);
 }
 
-tq_status tq_encode_mse(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+tq_status tq_encode_mse(const tq_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
                         tq_cache out, const int64_t* slot, void* stream) {
   return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream);
 }
 
-tq_status tq_encode_mse_keys(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
+tq_status tq_encode_mse_keys(const tq_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
                              tq_cache out, const int64_t* slot, void* stream) {
   return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream, true);
 }
 
-tq_status tq_encode_eden(const tq_params* p, const void* x, tq_dtype dtype, int64_t n, int64_t ld_x,
-                         tq_layout layout, tq_cache out, const int64_t* slot, void* stream) {
+tq_status tq_encode_eden(const tq_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
+                         int layout, tq_cache out, const int64_t* slot, void* stream) {
   if (layout != TQ_LAYOUT_BLOCKS && layout != TQ_LAYOUT_RECORDS)
     return fail(TQ_ERR_INVALID_ARG, "layout must be TQ_LAYOUT_BLOCKS or TQ_LAYOUT_RECORDS");
   return encode(p, false, x, dtype, n, ld_x, out, slot, nullptr, 0, stream, layout == TQ_LAYOUT_RECORDS, true);
@@ -263,6 +277,9 @@ static tq_status score_args(const tq_params* kp, const float* q, bool need_q, in
   const size_t need = tq::scores128_workspace(segs, group);
   if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
   const int64_t stride = segs == 1 && keys.seg_stride < T ? T : keys.seg_stride;
+  if (need_keys && (int64_t)(segs - 1) * stride + T > keys.records)
+    return fail(TQ_ERR_INVALID_ARG, "the keys read (%lld records) exceed keys.records (%lld)",
+                (long long)((int64_t)(segs - 1) * stride + T), (long long)keys.records);
   if (need_keys && (stride * 16 * kp->bits >= (1ll << 31) || (int64_t)group * T * 4 >= (1ll << 31)))
     return fail(TQ_ERR_UNSUPPORTED, "tq_scores addresses at most 2 GiB of keys and of scores per segment");
   a->q = q;
@@ -283,6 +300,7 @@ static tq_status score_args(const tq_params* kp, const float* q, bool need_q, in
   a->T = T;
   a->scores = scores;
   a->ws = ws;
+  a->wait_us = tq::PACK_WAIT_US;
   return TQ_OK;
 }
 
@@ -296,11 +314,23 @@ tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq
   return hip_status(tq::launch_scores128(a, (hipStream_t)stream), "scores launch");
 }
 
+tq_status tq_testing_scores_wait(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
+                                 const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
+                                 int wait_us, void* stream) {
+  tq::ScoreArgs a;
+  bool nothing;
+  if (wait_us < 0) return fail(TQ_ERR_INVALID_ARG, "wait_us must be >= 0");
+  tq_status st = score_args(kp, q, true, segs, group, keys, true, len, T, scores, true, ws, ws_bytes, &a, &nothing);
+  if (st != TQ_OK || nothing) return st;
+  a.wait_us = wait_us;
+  return hip_status(tq::launch_scores128(a, (hipStream_t)stream), "scores launch");
+}
+
 tq_status tq_scores_prepare(const tq_params* kp, const float* q, int segs, int group, void* ws,
                             size_t ws_bytes, void* stream) {
   tq::ScoreArgs a;
   bool nothing;
-  tq_cache none = {nullptr, nullptr, 0};
+  tq_cache none = {nullptr, nullptr, 0, 0};
   tq_status st = score_args(kp, q, true, segs, group, none, false, nullptr, 1, nullptr, false, ws, ws_bytes, &a,
                             &nothing);
   if (st != TQ_OK || nothing) return st;
@@ -317,10 +347,20 @@ tq_status tq_scores_prepared(const tq_params* kp, int segs, int group, tq_cache 
   return hip_status(tq::launch_scores128_prepared(a, (hipStream_t)stream), "scores launch");
 }
 
+// 4-bit MSE-only keys carry 16 key fragments per 16-row tile, so at most two
+// tiles (8 query heads) fit one attention workgroup's registers; a segment
+// with an even group of 10..16 heads runs as two query segments of group / 2
+// heads that read the same keys and values (the query and output rows of the
+// halves are the segment's rows in order).  Returns the divisor (1 or 2).
+static int attend_head_split(const tq_params* kp, int group) {
+  return kp && !kp->s && kp->bits == 4 && group > 8 ? 2 : 1;
+}
+
 size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, int group, int64_t T) {
-  (void)kp; (void)vp;
+  (void)vp;
   if (segs <= 0 || group <= 0 || T <= 0) return 0;
-  return tq::attend128_workspace(segs, group, T);
+  const int div = attend_head_split(kp, group);
+  return tq::attend128_workspace(segs * div, (group + div - 1) / div, T);
 }
 
 tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs, int group,
@@ -343,8 +383,10 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend with m = d / 2 keys supports value bits 2..4");
   if (!qjl && (kp->bits < 2 || vp->bits < 2))
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend with MSE-only keys supports key and value bits 2..4");
-  if (!qjl && kp->bits == 4 && group > 8)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_attend with 4-bit MSE-only keys supports up to 8 query heads per segment");
+  const int div = attend_head_split(kp, group);
+  if (div == 2 && group % 2)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_attend with 4-bit MSE-only keys supports up to 8, or an even number up "
+                                    "to 16, query heads per segment");
   if (!q || !keys.planes || !keys.scalars || !vals.planes || !vals.scalars || !out || !ws)
     return fail(TQ_ERR_INVALID_ARG, "q, keys, vals, out and ws must be non-NULL");
   if (vals.seg_stride % 32) return fail(TQ_ERR_INVALID_ARG, "vals.seg_stride must be a multiple of 32");
@@ -354,15 +396,18 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
       !aligned(vals.scalars, 4) || !aligned(ws, 256) || !aligned(q, 16) || !aligned(out, 4))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
   if (T == 0) return fail(TQ_ERR_INVALID_ARG, "T must be >= 1");
-  const size_t need = tq::attend128_workspace(segs, group, T);
+  const size_t need = tq::attend128_workspace(segs * div, group / div, T);
   if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
   const int64_t kstride = segs == 1 && keys.seg_stride < T ? T : keys.seg_stride;
   const int64_t vstride = segs == 1 && vals.seg_stride < T ? (T + 31) / 32 * 32 : vals.seg_stride;
+  if ((int64_t)(segs - 1) * kstride + T > keys.records || (int64_t)(segs - 1) * vstride + T > vals.records)
+    return fail(TQ_ERR_INVALID_ARG, "the keys or values read exceed keys.records / vals.records");
   if (kstride * 16 * kp->bits >= (1ll << 31) || vstride * 16 * vp->bits >= (1ll << 31))
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend addresses at most 2 GiB of keys and of values per segment");
   a.k.q = q;
-  a.k.segs = segs;
-  a.k.group = group;
+  a.k.segs = segs * div;
+  a.k.group = group / div;
+  a.kv_div = div;
   a.k.d = kp->d;
   a.k.pi = kp->pi;
   a.k.eps = kp->eps;
@@ -390,8 +435,6 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   return hip_status(tq::launch_attend128(a, (hipStream_t)stream), "attend launch");
 }
 
-void tq_debug_set_pack_wait(int microseconds) { tq::set_pack_wait_us(microseconds); }
-
 size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k) {
   if (!kp || nq <= 0 || T <= 0 || k <= 0) return 0;
   const bool qjl = kp->s != nullptr;
@@ -412,6 +455,7 @@ tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache k
   if (kp->d % 4) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk needs d a multiple of 4 (got %d)", kp->d);
   if (k > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports k <= 16");
   if (T < k) return fail(TQ_ERR_INVALID_ARG, "need T >= k");
+  if (T > keys.records) return fail(TQ_ERR_INVALID_ARG, "T exceeds keys.records");
   if (!q || !keys.planes || !keys.scalars || !idx || !val || !ws)
     return fail(TQ_ERR_INVALID_ARG, "q, keys, idx, val and ws must be non-NULL");
   if (!aligned(q, 16) || !aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(ws, 256) ||

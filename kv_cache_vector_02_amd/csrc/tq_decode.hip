@@ -357,32 +357,47 @@ void prep_queries128(PrepArgs a) {
 
 // One-launch scores: the first workgroup of each segment builds the query
 // pack while the segment's other workgroups already have their first keys in
-// flight.  Per segment two words in the workspace hand the pack over:
-//   flag  the ticket (a per-call number, odd, from the host) of the launch
-//         whose pack is complete; written by the producer after a release
-//         fence, read by the consumers before an acquire fence
-//   done  (ticket low 32 bits) << 32 | workgroups of that launch past the
-//         flag; the last one clears both words, so a replayed launch (same
-//         ticket) never finds the flag already set
-// A consumer waits a bounded time; if the flag has not come it builds the
-// pack itself (the same bytes as the producer's) and goes on.
+// flight.  Per segment three words in the workspace hand the pack over:
+//   flag   the ticket of the launch whose pack is complete (a per-call odd
+//          number from the host clock, so never the cleared value 0)
+//   claim  the ticket of the launch whose pack has a builder: the one
+//          workgroup whose exchange finds another value here builds the pack,
+//          so exactly one workgroup writes it per launch
+//   done   (ticket low 32 bits) << 32 | workgroups of that launch done with
+//          the hand-over; the last one clears all three words, so a replayed
+//          launch (a captured graph keeps its ticket) finds them clear
+// The producer claims and builds.  A consumer waits a bounded time for the
+// flag (the producer may not be resident yet); if it has not come, it claims
+// the pack itself and builds it, or, if another workgroup holds the claim
+// (a running workgroup, which will publish), waits for the flag.  The pack
+// and the words travel with device-coherent (sc1) accesses and relaxed
+// device-scope atomics: no L2 writeback or invalidate is needed, since no
+// other data is shared within the launch.
 struct ScoreSync {
   uint64_t flag;
+  uint64_t claim;
   uint64_t done;
+  uint64_t pad;
 };
 
-// Waits at most `ticks` of the 100 MHz constant clock (0: not at all).
+// Waits at most `ticks` of the 100 MHz constant clock (0: not at all; < 0:
+// without bound).
 __device__ __forceinline__ bool wait_ticket(uint64_t* flag, uint64_t ticket, long long ticks) {
-  if (ticks <= 0) return false;
+  if (ticks == 0) return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ticket;
   const long long t0 = wall_clock64();
   while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ticket) {
-    if (wall_clock64() - t0 > ticks) return false;
+    if (ticks > 0 && wall_clock64() - t0 > ticks) return false;
     __builtin_amdgcn_s_sleep(2);
   }
   return true;
 }
 
-// Counts this workgroup past the flag; the last of nwg clears the words.
+// True for the one workgroup per launch and segment whose exchange takes the claim.
+__device__ __forceinline__ bool take_claim(ScoreSync* s, uint64_t ticket) {
+  return __hip_atomic_exchange(&s->claim, ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ticket;
+}
+
+// Counts this workgroup done with the hand-over; the last of nwg clears the words.
 __device__ __forceinline__ void sync_done(ScoreSync* s, uint64_t ticket, uint32_t nwg) {
   const uint64_t tag = ticket << 32;
   uint64_t v = __hip_atomic_load(&s->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -393,6 +408,7 @@ __device__ __forceinline__ void sync_done(ScoreSync* s, uint64_t ticket, uint32_
                                                  __HIP_MEMORY_SCOPE_AGENT));
   if ((uint32_t)nv == nwg) {
     __hip_atomic_store(&s->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&s->claim, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&s->done, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -513,17 +529,23 @@ void scores128(Score128Args a) {
   if constexpr (FUSED) {
     const int b = blockIdx.x;
     if (b < a.prep.segs) {
-      // producer of segment b: the pack with device-coherent stores, every
-      // store complete, then the flag
-      prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
-                                           a.prep.ws + (size_t)b * pack_bytes(MT, F));
-      __builtin_amdgcn_s_waitcnt(0);
+      // producer of segment b: unless a consumer that gave up waiting holds
+      // the claim, the pack with device-coherent stores, every store
+      // complete, then the flag
+      int* mine = reinterpret_cast<int*>(smem + SMEM);
+      if (threadIdx.x == 0) *mine = take_claim(&a.sync[b], a.ticket) ? 1 : 0;
       __syncthreads();
-      if (threadIdx.x == 0) {
-        __hip_atomic_store(&a.sync[b].flag, a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (*mine) {
+        prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
+                                             a.prep.ws + (size_t)b * pack_bytes(MT, F));
         __builtin_amdgcn_s_waitcnt(0);
-        sync_done(&a.sync[b], a.ticket, (uint32_t)a.chunks + 1u);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          __hip_atomic_store(&a.sync[b].flag, a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(0);
+        }
       }
+      if (threadIdx.x == 0) sync_done(&a.sync[b], a.ticket, (uint32_t)a.chunks + 1u);
       return;
     }
     seg = (b - a.prep.segs) / a.chunks;
@@ -571,22 +593,34 @@ void scores128(Score128Args a) {
 #pragma unroll
   for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * j);
   if constexpr (FUSED) {
-    int* got = reinterpret_cast<int*>(smem + SMEM);
+    // 0: the pack is published; 1: this workgroup holds the claim and builds it
+    int* build = reinterpret_cast<int*>(smem + SMEM);
     if (threadIdx.x == 0) {
-      *got = wait_ticket(&a.sync[seg].flag, a.ticket, a.wait_ticks) ? 1 : 0;
-      sync_done(&a.sync[seg], a.ticket, (uint32_t)a.chunks + 1u);
+      int bld = 0;
+      if (!wait_ticket(&a.sync[seg].flag, a.ticket, a.wait_ticks)) {
+        if (take_claim(&a.sync[seg], a.ticket))
+          bld = 1;
+        else
+          wait_ticket(&a.sync[seg].flag, a.ticket, -1);   // the claimant is running and will publish
+      }
+      *build = bld;
     }
     __syncthreads();
-    if (!*got) {
-      // no pack within the wait: build it here (the same bytes the producer
-      // writes), then request the first keys again
+    if (*build) {
+      // the producer has not started: build the pack here (the only writer
+      // of this launch), publish it, then request the first keys again
       prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, seg, *reinterpret_cast<PrepLds*>(smem),
                                            const_cast<uint8_t*>(pack));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (threadIdx.x == 0) {
+        __hip_atomic_store(&a.sync[seg].flag, a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
 #pragma unroll
       for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * j);
     }
+    if (threadIdx.x == 0) sync_done(&a.sync[seg], a.ticket, (uint32_t)a.chunks + 1u);
   }
 
   // the pack: in the one-launch form it was written in this launch, possibly
@@ -826,16 +860,12 @@ size_t scores128_workspace(int segs, int group) {
   return scores128_pack_region(segs, group) + ((size_t)segs * sizeof(ScoreSync) + 255) / 256 * 256;
 }
 
-// The consumers' bound on the wait for the pack, in microseconds.
-static std::atomic<int> g_pack_wait_us{200};
-
-void set_pack_wait_us(int us) { g_pack_wait_us.store(us < 0 ? 0 : us, std::memory_order_relaxed); }
-
-// Per-call tickets of the one-launch form: odd (never the cleared value 0),
-// distinct across calls in the process.
-static uint64_t next_ticket() {
-  static std::atomic<uint64_t> t{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2 + 1};
-  return t.fetch_add(2, std::memory_order_relaxed);
+// Per-call tickets of the one-launch form: odd (never the cleared value 0)
+// and distinct from call to call, from the host's monotonic clock in
+// nanoseconds (consecutive calls on one workspace are far more than a
+// nanosecond apart).  No state is kept between calls.
+static uint64_t call_ticket() {
+  return (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2 + 1;
 }
 
 // Digits per quantised query weight for the score pass: 2 for MSE-only keys
@@ -909,8 +939,8 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
   Score128Args s = score_pass_args(a);
   s.prep = make_prep(a, slices);
   s.sync = reinterpret_cast<ScoreSync*>(static_cast<uint8_t*>(a.ws) + scores128_pack_region(a.segs, a.group));
-  s.ticket = next_ticket();
-  s.wait_ticks = 100LL * g_pack_wait_us.load(std::memory_order_relaxed);   // 100 MHz clock
+  s.ticket = call_ticket();
+  s.wait_ticks = 100LL * (a.wait_us < 0 ? 0 : a.wait_us);   // 100 MHz clock
   const bool had = a.rot == TQ_ROT_HADAMARD;
   if (a.qjl && a.m == D / 2) {
     // prod keys with m = d / 2 QJL rows
@@ -1076,6 +1106,7 @@ struct Attend128Args {
   float* part;                  // [segs][nchunks][group][PST]
   int nchunks;                  // workgroups per segment
   int64_t span;                 // tokens per workgroup (multiple of AGRAN)
+  int kv_div;                   // query segments per cache segment (1, or 2 when a segment's heads run as halves)
 };
 
 __device__ __forceinline__ float f16lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffff)); }
@@ -1116,11 +1147,12 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
   __shared__ float vnorm[4][128];
   const int seg = blockIdx.y;
   const int chunk = blockIdx.x;
+  const int kseg = seg / a.kv_div;   // the cache segment this query segment reads
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t16 = lane & 15;
   const int kg = lane >> 4;
-  const int64_t len = a.len ? (int64_t)a.len[seg] : a.T;
+  const int64_t len = a.len ? (int64_t)a.len[kseg] : a.T;
   const int64_t c0 = (int64_t)chunk * a.span;
   const int64_t c1 = len < c0 + a.span ? len : c0 + a.span;
   const int ngroups = c1 > c0 ? (int)((c1 - c0 + 127) / 128) : 0;
@@ -1155,10 +1187,10 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
     for (int c = 0; c < 4; ++c) cst[mt][c] = consts[(mt * 4 + kg) * 4 + c] * (c < 2 ? a.scale2 : a.scale2 * a.kappa);
   }
 
-  const int64_t krec0 = seg * a.kstride + c0;
+  const int64_t krec0 = kseg * a.kstride + c0;
   const rsrc_t rk = make_rsrc(a.kplanes + krec0 * (RBK / 4), clamp_bytes((a.kstride - c0) * RBK));
   const rsrc_t rks = make_rsrc(a.kscal + krec0 * (KSB / 2), clamp_bytes((a.kstride - c0) * KSB));
-  const int64_t vrec0 = seg * a.vstride + c0;   // multiple of 32
+  const int64_t vrec0 = kseg * a.vstride + c0;   // multiple of 32
   const rsrc_t rv = make_rsrc(a.vplanes + (vrec0 / 32) * (D * PV), clamp_bytes((a.vstride - c0) / 32 * VBB));
   const rsrc_t rvs = make_rsrc(a.vscal + vrec0, clamp_bytes((a.vstride - c0) * 2));
   const uint32_t vko = t16 * RBK + (MW == 4 ? kg * (PK * 4) : (kg < 2 ? kg * PK : kg * BQK + 1) * 4);
@@ -1591,6 +1623,7 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   s.part = reinterpret_cast<float*>(ws + attend_pack_bytes(a.k.segs, a.k.group));
   s.nchunks = 0;   // set by the launcher
   s.span = 0;
+  s.kv_div = a.kv_div;
   const int mt = (a.k.group + 3) / 4;
   if (a.k.qjl && a.k.m == D / 2) {
     switch (a.k.bq * 10 + a.bq_v) {

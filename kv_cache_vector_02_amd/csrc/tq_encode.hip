@@ -279,7 +279,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       // re-read it after every batch of atomics)
       vrec = vec[0] < a.n ? (a.slot ? a.slot[vec[0]] : vec[0]) : 0;
       const bool mine = vec[0] < a.n && vrec == r0 + v;
-      vfast = (r0 % 32) == 0 && __all(mine);
+      // whole-block stores only for a block inside the cache's capacity
+      vfast = (r0 % 32) == 0 && r0 >= 0 && r0 + 32 <= a.records && __all(mine);
       vblock = r0 / 32;
 #pragma unroll
       for (int p = 0; p < BQ; ++p) vlo[p] = vhi[p] = 0u;
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
     // and only the bits that change need an atomic.
     uint32_t oldw[SLOTS ? 16 * BQ : 1];
     auto load_old = [&](int mt) {
-      if (PROD || !SLOTS || vfast || vec[0] >= a.n) return;
+      if (PROD || !SLOTS || vfast || vec[0] >= a.n || (uint64_t)vrec >= (uint64_t)a.records) return;
       const uint4* src = reinterpret_cast<const uint4*>(a.planes + (vrec >> 5) * (D * BQ) + (64 * h + 16 * mt) * BQ);
 #pragma unroll
       for (int q = 0; q < 4 * BQ; ++q) {
@@ -351,18 +352,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
               for (int k = 0; k < (1 << BQ) - 1; ++k)
                 if (((k + 1) & ((1 << p) - 1)) == 0) m ^= ge[k];
               const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
-              // the mask may come straight from a VALU compare (one plane: m
-              // is the comparison itself); a writelane reading an SGPR that a
-              // VALU instruction has just written needs wait states, which the
-              // compiler does not insert in front of inline asm
-              if (p == 0)
-                asm volatile("s_nop 4\n\tv_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %4"
-                             : "+v"(vlo[p]), "+v"(vhi[p])
-                             : "s"(mlo), "s"(mhi), "i"(16 * mt + r));
-              else
-                asm volatile("v_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %4"
-                             : "+v"(vlo[p]), "+v"(vhi[p])
-                             : "s"(mlo), "s"(mhi), "i"(16 * mt + r));
+              // lane 16 mt + r takes the block's words of this coordinate (a
+              // plain select: the mask may come straight from a VALU compare,
+              // and the compiler places whatever wait states that needs)
+              const bool here = lane == 16 * mt + r;
+              vlo[p] = here ? mlo : vlo[p];
+              vhi[p] = here ? mhi : vhi[p];
             }
             return;
           }
@@ -390,7 +385,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             iw[nt][p][mt >> 1] = shift_in(iw[nt][p][mt >> 1], x);
           }
           if (!PROD) {
-            if (vec[nt] < a.n) {
+            if (vec[nt] < a.n && (uint64_t)vrec < (uint64_t)a.records) {
               // blocks shared with other vectors: an atomic for each bit
               // that changes (with a slot map), else one per bit
               uint32_t* wp = a.planes + (vrec >> 5) * (D * BQ) + (64 * h + 16 * mt + r) * BQ;
@@ -496,7 +491,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           const float t = yc[nt] + shfl_xor_f(yc[nt], 32);    // <y, c[idx]>, y on the unit sphere
           sv = nrm[nt] > 0.f && t > 0.f ? nrm[nt] / t : 0.f;
         }
-        if (vec[nt] < a.n && h == 0) a.scalars[a.slot ? a.slot[vec[nt]] : vec[nt]] = f16_bits(sv);
+        if (vec[nt] < a.n && h == 0) {
+          const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
+          if ((uint64_t)rec < (uint64_t)a.records) a.scalars[rec] = f16_bits(sv);
+        }
         continue;
       }
       // MSE-only key scalar: n, or with EDEN n / <y, c[idx]> (the sum over both
@@ -510,8 +508,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         // lane half 0 writes groups 0 and 1 with sign words 0 and 1 (the
         // latter from lane half 1); lane half 1 writes groups 2 and 3
         const uint32_t s1 = __shfl_xor(sw[nt][0], 32, 64);
-        if (vec[nt] < a.n) {
-          const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
+        const int64_t rec = vec[nt] < a.n ? (a.slot ? a.slot[vec[nt]] : vec[nt]) : -1;
+        if ((uint64_t)rec < (uint64_t)a.records) {
           constexpr int RW = 4 * BQ + 2;
           uint32_t out[2 * BQ + 2];
 #pragma unroll
@@ -535,8 +533,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         }
         continue;
       }
-      if (vec[nt] < a.n) {
-        const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
+      const int64_t rec = vec[nt] < a.n ? (a.slot ? a.slot[vec[nt]] : vec[nt]) : -1;
+      if ((uint64_t)rec < (uint64_t)a.records) {
         // record order: word w of plane p at w * P + p; this lane owns words
         // 2h and 2h+1 of every plane, i.e. the 2P contiguous u32 from 2h * P
         uint32_t out[2 * P];

@@ -25,6 +25,24 @@
 #include "tq_internal.h"
 
 namespace tq {
+
+struct Encode2kArgs {
+  const void* x;
+  int64_t ld_x;
+  int d;
+  int64_t n;           // vectors in the call
+  int64_t v0, cn;      // current chunk: first vector, count
+  int64_t chunk;       // vectors per chunk (multiple of 128 rows of residual space)
+  const float* eps;
+  Codebook cb;
+  uint32_t* planes;
+  uint16_t* scalars;
+  const int64_t* slot;
+  int64_t records;         // capacity in records (records at or past it are not written)
+  _Float16 *s_hi, *s_lo;   // [2048][2048]
+  _Float16 *r_hi, *r_lo;   // [chunk][2048], prescaled residuals
+};
+
 namespace {
 
 constexpr int D2 = 2048;
@@ -154,6 +172,7 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
     scale = n > 0.f && yc > 0.f ? n / yc : 0.f;
   }
   const int64_t rec = a.slot ? a.slot[gv] : gv;
+  if ((uint64_t)rec >= (uint64_t)a.records) return;      // past the cache's capacity: not written
   uint32_t* dst = a.planes + rec * (P * (D2 / 32)) + lane * P;
 #pragma unroll
   for (int p = 0; p < BQ; ++p) dst[p] = w[p];
@@ -240,7 +259,8 @@ __global__ __launch_bounds__(256) void encode2k_signs(Encode2kArgs a) {
         if (m < a.cn) {
           const int64_t gv = a.v0 + m;
           const int64_t rec = a.slot ? a.slot[gv] : gv;
-          a.planes[rec * (P * (D2 / 32)) + ((iw + 32 * j) / 32) * P + (P - 1)] = word;
+          if ((uint64_t)rec < (uint64_t)a.records)
+            a.planes[rec * (P * (D2 / 32)) + ((iw + 32 * j) / 32) * P + (P - 1)] = word;
         }
       }
     }
@@ -301,6 +321,7 @@ hipError_t launch_encode2k_mse(const EncodeArgs& e, hipStream_t stream) {
   a.planes = e.planes;
   a.scalars = e.scalars;
   a.slot = e.slot;
+  a.records = e.records;
   a.v0 = 0;
   a.cn = e.n;
   switch (e.bq) {
@@ -323,6 +344,7 @@ hipError_t launch_encode2k(const EncodeArgs& e, void* ws, hipStream_t stream) {
   a.planes = e.planes;
   a.scalars = e.scalars;
   a.slot = e.slot;
+  a.records = e.records;
   a.chunk = encode2k_chunk(e.n);
   _Float16* w = static_cast<_Float16*>(ws);
   a.s_hi = w;

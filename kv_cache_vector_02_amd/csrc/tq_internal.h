@@ -36,26 +36,12 @@ struct EncodeArgs {
   uint32_t* planes;    // [records][P][d_rot/32]
   uint16_t* scalars;   // [records][S] float16 bit patterns
   const int64_t* slot; // record of vector i, or null
+  int64_t records;     // capacity of planes / scalars in records: records at or past it are not written
 };
 
 hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream);
 
 // Prod encode at d_rot = 2048 (Hadamard): chunked two-pass path with a workspace.
-struct Encode2kArgs {
-  const void* x;
-  int64_t ld_x;
-  int d;
-  int64_t n;           // vectors in the call
-  int64_t v0, cn;      // current chunk: first vector, count
-  int64_t chunk;       // vectors per chunk (multiple of 128 rows of residual space)
-  const float* eps;
-  Codebook cb;
-  uint32_t* planes;
-  uint16_t* scalars;
-  const int64_t* slot;
-  _Float16 *s_hi, *s_lo;   // [2048][2048]
-  _Float16 *r_hi, *r_lo;   // [chunk][2048], prescaled residuals
-};
 size_t encode2k_workspace(int64_t n);
 
 // Walsh coefficients u_S of the odd subsets of an odd-symmetric codebook of bq
@@ -104,14 +90,17 @@ struct ScoreArgs {
   int64_t T;
   float* scores;
   void* ws;
+  int wait_us;           // one-launch scores: consumers' bound on the wait for the pack (microseconds)
 };
+
+// The bound tq_scores gives a workgroup's wait for its segment's query pack.
+constexpr int PACK_WAIT_US = 200;
 
 hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream);    // query pack only
 hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream);   // score pass only
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream);
 size_t scores128_workspace(int segs, int group);
-void set_pack_wait_us(int us);   // one-launch scores: consumers' wait bound
 
 struct AttendArgs {
   ScoreArgs k;           // query + key side (scores field unused)
@@ -126,6 +115,7 @@ struct AttendArgs {
   float scale;
   float* out;
   void* ws;
+  int kv_div;            // k.segs / cache segments: 2 when each segment's heads run as two halves
 };
 
 hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream);

@@ -529,8 +529,8 @@ size_t topk2k_workspace(int nq, int64_t T, int k, int bq, int qjl) {
   add((size_t)nrt * NCH * r_frags(bq, qjl) * 1024);   // fragments
   add((size_t)nqp * 16);                     // constants
   add((size_t)nq * rc * 4);                  // score block
-  add((size_t)nq * nch * k * 12);            // candidates
-  (void)k;
+  add((size_t)nq * nch * k * 4);             // candidate values
+  add((size_t)nq * nch * k * 8);             // candidate indices (int64)
   return s;
 }
 
@@ -568,9 +568,10 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   a.pack = take((size_t)nrt * NCH * r_frags(bq, L.qjl) * 1024);
   a.consts = reinterpret_cast<float*>(take((size_t)a.nqp * 16));
   float* block = reinterpret_cast<float*>(take((size_t)L.nq * rc * 4));
-  uint8_t* cand = take((size_t)L.nq * nch * L.k * 12);
-  float* cval = reinterpret_cast<float*>(cand);
-  int64_t* cidx = reinterpret_cast<int64_t*>(cand + (size_t)L.nq * nch * L.k * 4);
+  // candidate values and indices in regions of their own (the int64 indices
+  // 256-byte aligned whatever nq * nch * k is)
+  float* cval = reinterpret_cast<float*>(take((size_t)L.nq * nch * L.k * 4));
+  int64_t* cidx = reinterpret_cast<int64_t*>(take((size_t)L.nq * nch * L.k * 8));
 
   if (L.qjl) hipLaunchKernelGGL(r_split_s, dim3(1024), dim3(256), 0, stream, L.s, a.s_hi, a.s_lo, (int64_t)D2 * D2);
   hipLaunchKernelGGL(r_rotate, dim3((unsigned)(a.nqp / 4)), dim3(256), 0, stream, a);

@@ -153,3 +153,45 @@ def test_hadamard_rotation(prod, bits, dtype):
     if not prod:
         planes = value_indices(planes, len(x))
     _log(f"  {compare_encode(st, planes, scal, st.encode_oracle(x))}")
+
+
+@pytest.mark.parametrize("kind", ["prod", "mse", "prod_2048"])
+def test_slots_outside_the_capacity_are_not_written(kind):
+    # the cache descriptor says 64 records; slots 64.., and negative slots,
+    # name no record and must leave every byte past the capacity untouched,
+    # while the records inside it are encoded as usual
+    import kv_cache_vector_02_amd as tq
+    _log(f"encode slots outside the capacity ({kind})")
+    T = torch()
+    rg = np.random.default_rng(31)
+    if kind == "prod_2048":
+        from tq_inputs import mixture_database
+        x, _ = mixture_database(48, 1536, seed=31)
+        st = Setup(d=1536, d_rot=2048, bits=2, prod=True, rot="hadamard", seed=31)
+    else:
+        x = kv_tensor(1, 1, 48, 128, seed=31)[0, 0]
+        st = Setup(bits=3, prod=kind == "prod", seed=31, purpose_pi=2 if kind == "prod" else 4)
+    slot = rg.permutation(64)[:48].astype(np.int64)
+    out_of_range = [3, 17, 40]
+    slot[out_of_range] = [64, 100, -1]
+    full = st.alloc(128)                                   # room past the stated capacity
+    cache = tq.Cache(full.planes, full.scalars[:64], 0)    # capacity: 64 records
+    assert cache.records == 64
+    xd = T.from_numpy(np.ascontiguousarray(x)).cuda()
+    sl = T.from_numpy(slot).cuda()
+    if kind == "prod_2048":
+        tq.encode_prod(st.params, xd, cache, slot=sl, ws=tq.alloc_workspace(tq.encode_workspace(st.params, 48)))
+    else:
+        (tq.encode_prod if st.prod else tq.encode_mse)(st.params, xd, cache, slot=sl)
+    T.cuda.synchronize()
+    planes = full.planes.cpu().numpy().view(np.uint32)
+    scal = full.scalars.cpu().numpy()
+    keep = np.setdiff1d(np.arange(48), out_of_range)
+    assert not scal[64:].view(np.uint16).any(), "scalars past the capacity were written"
+    if st.prod:
+        assert not planes[64:].any(), "records past the capacity were written"
+        compare_encode(st, planes[slot[keep]], scal[slot[keep]], st.encode_oracle(x[keep]))
+    else:
+        assert not planes[2:].any(), "value blocks past the capacity were written"
+        idx = value_indices(planes[:2], 64)
+        compare_encode(st, idx[slot[keep]], scal[slot[keep]], st.encode_oracle(x[keep]))

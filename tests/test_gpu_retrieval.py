@@ -164,6 +164,22 @@ def test_topk_mse_several_blocks_k16():
     _check_topk(got_idx, got_val, ref, 16)
 
 
+@pytest.mark.parametrize("prod", [True, False])
+def test_topk_odd_query_candidate_count(prod):
+    # nq * k odd (3 queries, k = 5): the candidate indices stay 8-byte aligned
+    _log(f"retrieval top-5 for 3 queries ({'prod' if prod else 'MSE-only'})")
+    db, qs = mixture_database(5000, 1536, seed=13, n_queries=3)
+    st = _setup(2, seed=13, prod=prod)
+    if prod:
+        cache, (idx, z, n, g) = _oracle_cache(st, db)
+        ref = est.prod_scores(qs, idx, z, n, g, st.rot, st.s, st.c32)
+    else:
+        cache, (idx, n) = _oracle_mse_cache(st, db)
+        ref = est.mse_scores(qs, idx, n, st.rot, st.c32)
+    got_idx, got_val = _gpu_topk(st, qs, cache, len(db), 5)
+    _check_topk(got_idx, got_val, ref, 5)
+
+
 def test_topk_several_blocks_k16():
     # 140000 records span three score blocks of 65536; k = 16 (the largest)
     _log("retrieval top-16 over 3 score blocks")

@@ -223,11 +223,13 @@ def test_one_launch_workspace_reused_across_calls():
         _log(f"  call {i} segs {segs} G {G}: worst rel {worst:.2e}")
 
 
-def test_one_launch_pack_built_by_every_workgroup():
-    # the path a workgroup takes when its wait for the pack runs out: with a
-    # zero wait every workgroup builds the pack itself; the scores are the
-    # same bytes as with the hand-over
-    _log("scores: every workgroup builds its own pack (zero wait)")
+@pytest.mark.parametrize("wait_us", [0, 1])
+def test_one_launch_pack_claimed_by_a_consumer(wait_us):
+    # the path a workgroup takes when its wait for the pack runs out: it
+    # claims the pack and builds it, or waits for the claimant; with no wait
+    # (and with a 1 us wait, a mix of both paths) the scores are the same
+    # bytes as with the hand-over, call after call
+    _log(f"scores: consumers claim the pack (wait {wait_us} us)")
     Tt = torch()
     segs, T_, G = 5, 3000, 8
     st = Setup(bits=3, prod=True, seed=14)
@@ -235,14 +237,14 @@ def test_one_launch_pack_built_by_every_workgroup():
     cache, fields = oracle_key_cache(st, x, seg_stride=T_)
     q = gaussian_queries(segs * G, 128, seed=14)
     base = gpu_scores(st, q, segs, G, cache, T_)
-    tq.debug_set_pack_wait(0)
-    try:
-        got = gpu_scores(st, q, segs, G, cache, T_)
-        got2 = gpu_scores(st, q, segs, G, cache, T_)
-    finally:
-        tq.debug_set_pack_wait(200)
-    assert np.array_equal(got, base) and np.array_equal(got2, base)
-    check_rows(got, _oracle_rows(st, q, fields, segs, G, T_))
+    qd = Tt.from_numpy(q).cuda()
+    ws = tq.alloc_workspace(tq.scores_workspace(st.params, segs, G))
+    for _ in range(3):
+        out = Tt.full((segs * G, T_), float("nan"), dtype=Tt.float32, device="cuda")
+        tq.testing_scores_wait(st.params, qd, segs, G, cache, T_, out, ws, wait_us)
+        Tt.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), base)
+    check_rows(base, _oracle_rows(st, q, fields, segs, G, T_))
 
 
 def test_one_launch_graph_replays_see_new_queries():

@@ -13,19 +13,51 @@ from oracle import codebook as cb
 from tests.conftest import ROOT
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+def _declared(header="tq.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
 
 
-def test_library_exports_every_declared_symbol():
-    L = tq.lib()
-    names = _declared()
-    assert len(names) >= 11
-    for n in names:
-        assert hasattr(L, n), n
-    assert set(names) <= set(tq.EXPORTED) | set(names)
+def _exported():
+    """tq_* functions libtq.so defines, from its dynamic symbol table."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", tq.LIB_PATH], capture_output=True, text=True, check=True)
+    return sorted({ln.split()[-1] for ln in out.stdout.splitlines()
+                   if ln.split()[-1].startswith("tq_") and ln.split()[-2] in ("T", "t", "W")})
+
+
+def test_library_exports_exactly_the_declared_symbols():
+    # the product header, plus the measurement/testing header; nothing else
+    tq.lib()
+    product, testing = _declared("tq.h"), _declared("tq_testing.h")
+    assert len(product) >= 20 and set(product).isdisjoint(testing)
+    assert _exported() == sorted(set(product) | set(testing))
+    assert sorted(product) == sorted(tq.EXPORTED) and sorted(testing) == sorted(tq.EXPORTED_TESTING)
+    # the calls the boundary is built around are all there
+    for n in ("tq_build_codebook", "tq_encode_prod", "tq_encode_mse", "tq_scores", "tq_attend",
+              "tq_scores_topk", "tq_key_record_bytes", "tq_val_record_bytes"):
+        assert n in product
+
+
+def test_record_bytes():
+    # the storage accounting: 52 B per key and 50 B per value at d = 128, b = 3
+    # (5.02x below float16 K + V); m = d / 2 keys 44 B; MSE-only keys b planes + n
+    for bits, kb, vb in ((2, 36, 34), (3, 52, 50), (4, 68, 66)):
+        pk_ = _params(bits)
+        pk_._c.pi, pk_._c.s = 0x10000, 0x20000
+        assert tq.lib().tq_key_record_bytes(pk_.c) == kb
+        c, b = cb.lloyd_max(128, bits)
+        pv_ = tq.Params(d=128, bits=bits, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b)
+        pv_._c.pi = 0x10000
+        assert tq.lib().tq_val_record_bytes(pv_.c) == vb
+        assert tq.lib().tq_key_record_bytes(pv_.c) == vb          # an MSE-only key record
+    p = _params(3)
+    p._c.pi, p._c.s, p._c.m = 0x10000, 0x20000, 64
+    assert tq.lib().tq_key_record_bytes(p.c) == 44
+    p._c.m = 96
+    assert tq.lib().tq_key_record_bytes(p.c) == 0                  # invalid parameters
+    assert 2 * 128 * 2 / (52 + 50) == pytest.approx(5.02, abs=0.005)
 
 
 @pytest.mark.parametrize("d", [0, 2, 3, 8, 128, 2048])
@@ -67,9 +99,10 @@ def _params(bits=3, **kw):
     return p
 
 
-def _encode_raw(p, n=4, ld=128, dtype=tq.TQ_F16, x=0x1000, planes=0x2000, scalars=0x3000, slot=None):
+def _encode_raw(p, n=4, ld=128, dtype=tq.TQ_F16, x=0x1000, planes=0x2000, scalars=0x3000, slot=None,
+                records=1 << 20):
     L = tq.lib()
-    cache = tq.tq_cache(planes, scalars, 0)
+    cache = tq.tq_cache(planes, scalars, 0, records)
     return L.tq_encode_prod(p.c, ctypes.c_void_p(x), dtype, n, ld, cache,
                             ctypes.c_void_p(slot) if slot else None, None)
 
@@ -97,6 +130,7 @@ def test_encode_validation_without_launch():
     assert _encode_raw(p, dtype=7) == tq.TQ_ERR_INVALID_ARG
     assert _encode_raw(p, n=-1) == tq.TQ_ERR_INVALID_ARG
     assert _encode_raw(p, n=0) == tq.TQ_OK                  # nothing to do, nothing launched
+    assert _encode_raw(p, records=0) == tq.TQ_ERR_INVALID_ARG  # a cache with no capacity
     p._c.pi = None
     assert _encode_raw(p) == tq.TQ_ERR_INVALID_ARG          # dense without pi
     p._c.pi = 0x10000
@@ -173,7 +207,7 @@ def test_eden_and_mse_keys_validation_without_launch():
     p = tq.Params(d=128, bits=3, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b)
     p._c.pi = 0x10000
     L = tq.lib()
-    cache = tq.tq_cache(0x2000, 0x3000, 0)
+    cache = tq.tq_cache(0x2000, 0x3000, 0, 1 << 20)
     x = ctypes.c_void_p(0x1000)
     assert L.tq_encode_eden(p.c, x, tq.TQ_F16, 4, 128, 7, cache, None, None) == tq.TQ_ERR_INVALID_ARG  # layout
     assert L.tq_encode_eden(p.c, x, tq.TQ_F16, 0, 128, tq.TQ_LAYOUT_RECORDS, cache, None, None) == tq.TQ_OK
@@ -181,3 +215,38 @@ def test_eden_and_mse_keys_validation_without_launch():
     p._c.d, p._c.d_rot = 96, 96
     assert L.tq_encode_eden(p.c, x, tq.TQ_F16, 4, 96, tq.TQ_LAYOUT_BLOCKS, cache, None, None) == \
         tq.TQ_ERR_UNSUPPORTED
+
+
+def test_decode_reads_are_bounded_by_the_cache_capacity():
+    # tq_scores / tq_attend / tq_scores_topk reject a call whose records do not
+    # fit in the cache (fake pointers: the check is on the host, before a launch)
+    L = tq.lib()
+    pk_ = _params(3)
+    pk_._c.pi, pk_._c.s = 0x10000, 0x20000
+    c, b = cb.lloyd_max(128, 3)
+    pv_ = tq.Params(d=128, bits=3, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b)
+    pv_._c.pi = 0x10000
+    q, out, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x400000)
+    segs, G, T, stride = 4, 8, 1000, 1024
+    need = (segs - 1) * stride + T
+    ws_bytes = L.tq_scores_workspace(pk_.c, segs, G)
+    for records, want in ((need - 1, tq.TQ_ERR_INVALID_ARG), (need, None)):
+        keys = tq.tq_cache(0x2000, 0x3000, stride, records)
+        st = L.tq_scores(pk_.c, q, segs, G, keys, None, T, out, ws, ws_bytes, None)
+        if want is not None:
+            assert st == want and "keys.records" in L.tq_last_error().decode()
+    wa = L.tq_attend_workspace(pk_.c, pv_.c, segs, G, T)
+    keys = tq.tq_cache(0x2000, 0x3000, stride, need)
+    vals = tq.tq_cache(0x4000, 0x5000, stride, need - 1)
+    assert L.tq_attend(pk_.c, pv_.c, q, segs, G, keys, vals, None, T, ctypes.c_float(1.0), out, ws, wa,
+                       None) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_scores_wait_bound_must_be_nonnegative():
+    L = tq.lib()
+    pk_ = _params(3)
+    pk_._c.pi, pk_._c.s = 0x10000, 0x20000
+    keys = tq.tq_cache(0x2000, 0x3000, 64, 64)
+    st = L.tq_testing_scores_wait(pk_.c, ctypes.c_void_p(0x100000), 1, 8, keys, None, 64, ctypes.c_void_p(0x200000),
+                                  ctypes.c_void_p(0x400000), 1 << 20, -1, None)
+    assert st == tq.TQ_ERR_INVALID_ARG
