@@ -19,7 +19,8 @@
  *     launched.  A failed launch returns TQ_ERR_HIP.  tq_last_error() gives a
  *     thread-local message for the last non-OK status.
  *   - Calls may be made from any thread.  The library keeps no mutable state
- *     between calls.
+ *     between calls, apart from tq_scores_noalloc's per-device scratch array
+ *     (and its address, resolved once per device).
  *
  * Packed records (the layout the pages' storage accounting implies: b bits
  * per coordinate of codes, one sign bit per projection row, float16 norms):
@@ -255,6 +256,21 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
 tq_status tq_scores(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
                     const int32_t* len, int64_t T, float* scores, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* tq_scores for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same call and
+ * results without the workspace arguments.  Its workspace is a device array
+ * inside the library, tq_scores_noalloc_capacity() bytes (16 MiB) on each GPU,
+ * held until the process ends and resolved with hipGetSymbolAddress on a
+ * device's first call; nothing is allocated or freed.  Every call on a GPU
+ * uses that GPU's one array, so calls that overlap on one GPU (other streams,
+ * other threads) race: serialise them.  The array keeps the last call's
+ * contents; the hand-over words need no clearing (the per-call ticket).
+ * Returns TQ_ERR_UNSUPPORTED when segs and group need a larger workspace than
+ * the array (tq_scores_workspace > capacity), before any launch. */
+tq_status tq_scores_noalloc(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
+                            const int32_t* len, int64_t T, float* scores, void* stream);
+size_t tq_scores_noalloc_capacity(void);
 
 /* The two halves of tq_scores, for callers that time them apart or score the
  * same queries against several caches: tq_scores_prepare writes the query

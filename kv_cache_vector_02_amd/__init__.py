@@ -27,7 +27,7 @@ EXPORTED = (
     "tq_value_layout", "tq_key_record_words", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_eden", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
-    "tq_key_record_bytes", "tq_val_record_bytes",
+    "tq_key_record_bytes", "tq_val_record_bytes", "tq_scores_noalloc", "tq_scores_noalloc_capacity",
 )
 # measurement and testing entry points (include/tq_testing.h)
 EXPORTED_TESTING = ("tq_testing_stream", "tq_testing_scores_wait")
@@ -94,6 +94,9 @@ def lib():
         L.tq_attend_workspace.argtypes = [P, P, ci, ci, i64]
         L.tq_attend.argtypes = [P, P, vp, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
                                 vp, vp, sz, vp]
+        L.tq_scores_noalloc.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp]
+        L.tq_scores_noalloc_capacity.restype = sz
+        L.tq_scores_noalloc_capacity.argtypes = []
         L.tq_key_record_bytes.restype = sz
         L.tq_key_record_bytes.argtypes = [P]
         L.tq_val_record_bytes.restype = sz
@@ -105,7 +108,7 @@ def lib():
         for name in EXPORTED:
             if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace", "tq_key_record_words",
                             "tq_attend_workspace", "tq_encode_workspace", "tq_scores_topk_workspace",
-                            "tq_key_record_bytes", "tq_val_record_bytes"):
+                            "tq_key_record_bytes", "tq_val_record_bytes", "tq_scores_noalloc_capacity"):
                 getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -295,6 +298,17 @@ def scores(kp: Params, q, segs: int, group: int, keys: Cache, T: int, out, ws, l
            stream=None):
     _check(lib().tq_scores(kp.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def scores_noalloc(kp: Params, q, segs: int, group: int, keys: Cache, T: int, out, length=None, stream=None):
+    """tq_scores_noalloc: tq_scores with the library's per-device scratch array
+    as its workspace (nothing allocated; overlapping calls on one GPU race)."""
+    _check(lib().tq_scores_noalloc(kp.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),
+                                   _stream(stream)))
+
+
+def scores_noalloc_capacity() -> int:
+    return int(lib().tq_scores_noalloc_capacity())
 
 
 def scores_prepare(kp: Params, q, segs: int, group: int, ws, stream=None):

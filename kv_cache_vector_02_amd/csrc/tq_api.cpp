@@ -326,6 +326,25 @@ tq_status tq_testing_scores_wait(const tq_params* kp, const float* q, int segs, 
   return hip_status(tq::launch_scores128(a, (hipStream_t)stream), "scores launch");
 }
 
+tq_status tq_scores_noalloc(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,
+                            const int32_t* len, int64_t T, float* scores, void* stream) {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  tq_status st = hip_status(tq::scores_scratch(&ws, &ws_bytes), "resolving the scratch array");
+  if (st != TQ_OK) return st;
+  if (segs > 0 && group > 0 && tq::scores128_workspace(segs, group) > ws_bytes)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_scores_noalloc: %d segments x %d heads need %zu bytes of workspace, more "
+                "than its %zu-byte scratch array (use tq_scores with a workspace)", segs, group,
+                tq::scores128_workspace(segs, group), ws_bytes);
+  tq::ScoreArgs a;
+  bool nothing;
+  st = score_args(kp, q, true, segs, group, keys, true, len, T, scores, true, ws, ws_bytes, &a, &nothing);
+  if (st != TQ_OK || nothing) return st;
+  return hip_status(tq::launch_scores128(a, (hipStream_t)stream), "scores launch");
+}
+
+size_t tq_scores_noalloc_capacity(void) { return tq::SCORES_SCRATCH_BYTES; }
+
 tq_status tq_scores_prepare(const tq_params* kp, const float* q, int segs, int group, void* ws,
                             size_t ws_bytes, void* stream) {
   tq::ScoreArgs a;

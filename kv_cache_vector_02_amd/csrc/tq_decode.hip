@@ -38,6 +38,7 @@
 // k = 4m .. 4m+3, dword k byte i being bit 8 i + k of the word.
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <cmath>
 
 #include "tq_device.h"
@@ -858,6 +859,39 @@ static size_t scores128_pack_region(int segs, int group) {
 
 size_t scores128_workspace(int segs, int group) {
   return scores128_pack_region(segs, group) + ((size_t)segs * sizeof(ScoreSync) + 255) / 256 * 256;
+}
+
+// ---------------------------------------------------------------------------
+// tq_scores_noalloc: tq_scores with its workspace in a device array of this
+// library instead of caller memory, for callers that cannot allocate (code
+// under graph capture, tight serving loops).  The array is file-scope device
+// memory, one copy per GPU, held until the process ends.  Host code never
+// uses its name as an address: the device address is resolved once per device
+// with hipGetSymbolAddress and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[SCORES_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+}  // namespace
+
+hipError_t scores_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = SCORES_SCRATCH_BYTES;
+  return hipSuccess;
 }
 
 // Per-call tickets of the one-launch form: odd (never the cleared value 0)

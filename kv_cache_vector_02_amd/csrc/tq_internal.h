@@ -101,6 +101,10 @@ hipError_t launch_scores128_prepare(const ScoreArgs& a, hipStream_t stream);    
 hipError_t launch_scores128_prepared(const ScoreArgs& a, hipStream_t stream);   // score pass only
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream);
 size_t scores128_workspace(int segs, int group);
+// tq_scores_noalloc's workspace: a device array of this many bytes per GPU.
+constexpr size_t SCORES_SCRATCH_BYTES = 16u << 20;
+// Its address on the current device (resolved once per device) and size.
+hipError_t scores_scratch(void** ptr, size_t* bytes);
 
 struct AttendArgs {
   ScoreArgs k;           // query + key side (scores field unused)
