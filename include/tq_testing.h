@@ -26,7 +26,7 @@ extern "C" {
  *   src, dst       device, 16-byte aligned; sizes multiples of 16, each < 2 GiB
  *   store_policy   0: default write-back stores; 1: device-coherent (sc1)
  *                  stores, the score kernel's policy
- *   workgroups     grid size (256 threads each), or 0 for 8 per compute unit
+ *   workgroups     grid size (256 threads each), or 0 for 4 per compute unit
  * The bytes written are a function of the bytes read (so no load can be
  * dropped); their values carry no meaning.
  * Returns TQ_ERR_INVALID_ARG for NULL or misaligned pointers or sizes not a

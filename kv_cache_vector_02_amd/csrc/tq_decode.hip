@@ -37,6 +37,7 @@
 // 32 kg .. 32 kg + 31); MFMA m in {0, 1} of a plane takes expansion dwords
 // k = 4m .. 4m+3, dword k byte i being bit 8 i + k of the word.
 #include <atomic>
+#include <algorithm>
 #include <chrono>
 #include <mutex>
 #include <cmath>
@@ -364,16 +365,19 @@ void prep_queries128(PrepArgs a) {
 //   claim  the ticket of the launch whose pack has a builder: the one
 //          workgroup whose exchange finds another value here builds the pack,
 //          so exactly one workgroup writes it per launch
-//   done   (ticket low 32 bits) << 32 | workgroups of that launch done with
-//          the hand-over; the last one clears all three words, so a replayed
-//          launch (a captured graph keeps its ticket) finds them clear
+//   done   (ticket low 32 bits) << 32 | consumers of that launch done with
+//          the pack: set to the tag with a zero count by the builder before it
+//          publishes the flag, then one add per consumer at its end; the last
+//          of the segment's active consumers clears all three words, so a
+//          replayed launch (a captured graph keeps its ticket) finds them clear
 // The producer claims and builds.  A consumer waits a bounded time for the
 // flag (the producer may not be resident yet); if it has not come, it claims
 // the pack itself and builds it, or, if another workgroup holds the claim
 // (a running workgroup, which will publish), waits for the flag.  The pack
 // and the words travel with device-coherent (sc1) accesses and relaxed
-// device-scope atomics: no L2 writeback or invalidate is needed, since no
-// other data is shared within the launch.
+// device-scope atomics, each store waited for before the flag: no L2 writeback
+// or invalidate is needed, since no other data is shared within the launch.
+// The words may hold anything before a workspace's first call.
 struct ScoreSync {
   uint64_t flag;
   uint64_t claim;
@@ -398,16 +402,19 @@ __device__ __forceinline__ bool take_claim(ScoreSync* s, uint64_t ticket) {
   return __hip_atomic_exchange(&s->claim, ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ticket;
 }
 
-// Counts this workgroup done with the hand-over; the last of nwg clears the words.
-__device__ __forceinline__ void sync_done(ScoreSync* s, uint64_t ticket, uint32_t nwg) {
-  const uint64_t tag = ticket << 32;
-  uint64_t v = __hip_atomic_load(&s->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint64_t nv;
-  do {
-    nv = (v >> 32) == (ticket & 0xffffffffull) ? v + 1 : (tag | 1ull);
-  } while (!__hip_atomic_compare_exchange_strong(&s->done, &v, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT));
-  if ((uint32_t)nv == nwg) {
+// The builder, after its pack stores and before the flag: a zero count under
+// this launch's tag, complete before anything else is stored.
+__device__ __forceinline__ void publish(ScoreSync* s, uint64_t ticket) {
+  __hip_atomic_store(&s->done, ticket << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __hip_atomic_store(&s->flag, ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// A consumer done with the pack; the last of `active` clears the words.
+__device__ __forceinline__ void sync_done(ScoreSync* s, uint64_t ticket, uint32_t active) {
+  const uint64_t old = __hip_atomic_fetch_add(&s->done, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old >> 32) == (ticket & 0xffffffffull) && (uint32_t)old + 1u == active) {
     __hip_atomic_store(&s->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&s->claim, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&s->done, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -527,12 +534,19 @@ void scores128(Score128Args a) {
   const int t16 = lane & 15;
   const int kg = lane >> 4;
   int seg, chunk;
+  // consumers with tokens to score (the ones that count themselves done)
+  auto active_chunks = [&](int sg) -> uint32_t {
+    const int64_t l = a.len ? (int64_t)a.len[sg] : a.T;
+    const int64_t span = (int64_t)a.chunk_tiles * 16;
+    return l > 0 ? (uint32_t)((l + span - 1) / span) : 0u;
+  };
   if constexpr (FUSED) {
     const int b = blockIdx.x;
     if (b < a.prep.segs) {
-      // producer of segment b: unless a consumer that gave up waiting holds
-      // the claim, the pack with device-coherent stores, every store
-      // complete, then the flag
+      // producer of segment b (none needed when it has no tokens): unless a
+      // consumer that gave up waiting holds the claim, the pack with
+      // device-coherent stores, every store complete, then the flag
+      if (active_chunks(b) == 0) return;
       int* mine = reinterpret_cast<int*>(smem + SMEM);
       if (threadIdx.x == 0) *mine = take_claim(&a.sync[b], a.ticket) ? 1 : 0;
       __syncthreads();
@@ -541,12 +555,8 @@ void scores128(Score128Args a) {
                                              a.prep.ws + (size_t)b * pack_bytes(MT, F));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x == 0) {
-          __hip_atomic_store(&a.sync[b].flag, a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __builtin_amdgcn_s_waitcnt(0);
-        }
+        if (threadIdx.x == 0) publish(&a.sync[b], a.ticket);
       }
-      if (threadIdx.x == 0) sync_done(&a.sync[b], a.ticket, (uint32_t)a.chunks + 1u);
       return;
     }
     seg = (b - a.prep.segs) / a.chunks;
@@ -557,11 +567,7 @@ void scores128(Score128Args a) {
   }
   const int64_t len = a.len ? (int64_t)a.len[seg] : a.T;
   const int64_t tok0 = (int64_t)chunk * a.chunk_tiles * 16;
-  if (tok0 >= len) {
-    if constexpr (FUSED)
-      if (threadIdx.x == 0) sync_done(&a.sync[seg], a.ticket, (uint32_t)a.chunks + 1u);
-    return;
-  }
+  if (tok0 >= len) return;
 
   const int64_t rec0 = seg * a.seg_stride + tok0;
   const rsrc_t rk = make_rsrc(a.planes + rec0 * (RB / 4), clamp_bytes((a.seg_stride - tok0) * RB));
@@ -614,14 +620,10 @@ void scores128(Score128Args a) {
                                            const_cast<uint8_t*>(pack));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (threadIdx.x == 0) {
-        __hip_atomic_store(&a.sync[seg].flag, a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-      }
+      if (threadIdx.x == 0) publish(&a.sync[seg], a.ticket);
 #pragma unroll
       for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * j);
     }
-    if (threadIdx.x == 0) sync_done(&a.sync[seg], a.ticket, (uint32_t)a.chunks + 1u);
   }
 
   // the pack: in the one-launch form it was written in this launch, possibly
@@ -756,19 +758,35 @@ void scores128(Score128Args a) {
       flush(32 * pr);
     }
   }
+  // done with the pack (read into the LDS at the start): count this consumer
+  if constexpr (FUSED)
+    if (threadIdx.x == 0) sync_done(&a.sync[seg], a.ticket, active_chunks(seg));
 }
 
 int device_cus();
 int occupancy(const void* kernel, int threads);
 int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax);
 
-// Grid: (workgroups per segment, segments), sized so that the whole grid is
-// resident at once; a workgroup's span is a multiple of 8 waves x 32 tokens.
+// Workgroups of the score pass: enough to fill the device once, and more when
+// a segment is long, so that no workgroup takes more than one straight-line
+// round of its waves (PASS_SPAN tokens).  Many short workgroups keep every
+// channel busy to the end of the pass: at 32 layers x 8 heads x 32768 tokens,
+// 16 per segment ran 14% faster than the 2 that fill the device once, and
+// matched a plain stream with the same read/write mix.
+constexpr int64_t PASS_SPAN = (int64_t)SC_WAVES * 8 * 32;   // 8 waves x 8 pairs x 32 tokens
+int pass_workgroups(int resident, int segs, int64_t T) {
+  const int64_t by_len = (int64_t)segs * ((T + PASS_SPAN - 1) / PASS_SPAN);
+  return (int)std::min<int64_t>(std::max<int64_t>(resident, by_len), 1ll << 30);
+}
+
+// Grid: (workgroups per segment, segments); a workgroup's span is a multiple
+// of 8 waves x 32 tokens.
 template <int BQ, int MT, int S, bool QJL = true, int MW = 4>
 hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
   static const int nb =
       occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false, QJL, MW>), SC_WAVES * 64);
-  const int64_t span = split_span(segs, s.T, nb * device_cus(), 32 * SC_WAVES, (s.T + 255) / 256);
+  const int64_t span = split_span(segs, s.T, pass_workgroups(nb * device_cus(), segs, s.T), 32 * SC_WAVES,
+                                  (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   const int64_t chunks = (s.T + span - 1) / span;
   hipLaunchKernelGGL((scores128<BQ, MT, S, false, false, QJL, MW>), dim3((unsigned)chunks, (unsigned)segs),
@@ -783,7 +801,8 @@ hipError_t launch_scores_fused(Score128Args& s, int segs, hipStream_t stream) {
   static const int nb =
       occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, true, HAD, QJL, MW>), SC_WAVES * 64);
   const int resident = nb * device_cus() - segs;
-  const int64_t span = split_span(segs, s.T, resident > segs ? resident : segs, 32 * SC_WAVES, (s.T + 255) / 256);
+  const int64_t span = split_span(segs, s.T, pass_workgroups(resident > segs ? resident : segs, segs, s.T),
+                                  32 * SC_WAVES, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   s.chunks = (int)((s.T + span - 1) / span);
   const int64_t nwg = (int64_t)segs * (s.chunks + 1);

@@ -13,51 +13,47 @@ namespace tq {
 namespace {
 
 constexpr int ST_THREADS = 256;
-constexpr int ST_UNROLL = 8;      // 16-byte loads in flight per lane
+constexpr int ST_UNROLL = 8;      // 4 KB chunks in flight per workgroup
 
-// Thread g of G reads items g, g + G, ... of the read stream, ST_UNROLL at a
-// time, and after every read item adds nw to a running count, writing one
-// item of the write stream (items g, g + G, ...) each time the count passes
-// nr: every thread keeps the global read:write ratio, so both streams run
+// Workgroup w of G owns the w-th contiguous slice of each stream, in 4 KB
+// chunks (256 lanes x 16 bytes, one coalesced load or store per chunk).  It
+// reads ST_UNROLL chunks at a time and, after each batch, writes as many chunks
+// as keep its write slice in step with its read slice, so both streams run
 // side by side for the whole kernel.  The written value depends on the loads.
 __global__ __launch_bounds__(ST_THREADS) void stream_kernel(const uint8_t* src, uint32_t nr, uint8_t* dst,
                                                             uint32_t nw, int cpol) {
-  const uint32_t G = gridDim.x * ST_THREADS;
-  const uint32_t g = blockIdx.x * ST_THREADS + threadIdx.x;
+  const uint32_t G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
+  const uint32_t rc = (nr + ST_THREADS - 1) / ST_THREADS, wc = (nw + ST_THREADS - 1) / ST_THREADS;  // chunks
+  const uint32_t r0 = (uint32_t)((uint64_t)rc * w / G), r1 = (uint32_t)((uint64_t)rc * (w + 1) / G);
+  const uint32_t w0 = (uint32_t)((uint64_t)wc * w / G), w1 = (uint32_t)((uint64_t)wc * (w + 1) / G);
   const rsrc_t rs = make_rsrc(src, nr * 16u);
   const rsrc_t rd = make_rsrc(dst, nw * 16u);
   i32x4 acc = {0, 0, 0, 0};
-  uint64_t cnt = 0;
-  uint32_t w = g;
-  for (uint32_t r0 = g; r0 < nr; r0 += ST_UNROLL * G) {
+  uint32_t wnext = w0;
+  auto put = [&](uint32_t c) {
+    const uint32_t item = c * ST_THREADS + t;
+    const uint32_t off = item < nw ? item * 16u : OOB_OFFSET;
+    if (cpol)
+      __builtin_amdgcn_raw_buffer_store_b128(acc, rd, off, 0, 16);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(acc, rd, off, 0, 0);
+  };
+  for (uint32_t c0 = r0; c0 < r1; c0 += ST_UNROLL) {
     i32x4 v[ST_UNROLL];
 #pragma unroll
     for (int u = 0; u < ST_UNROLL; ++u) {
-      const uint32_t r = r0 + u * G;
-      v[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, r < nr ? r * 16u : OOB_OFFSET, 0, 0));
+      const uint32_t item = (c0 + u) * ST_THREADS + t;
+      v[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, c0 + u < r1 && item < nr ? item * 16u : OOB_OFFSET, 0, 0));
     }
 #pragma unroll
-    for (int u = 0; u < ST_UNROLL; ++u) {
-      acc ^= v[u];
-      cnt += nw;
-      if (cnt >= nr) {
-        cnt -= nr;
-        const uint32_t off = w < nw ? w * 16u : OOB_OFFSET;
-        if (cpol)
-          __builtin_amdgcn_raw_buffer_store_b128(acc, rd, off, 0, 16);
-        else
-          __builtin_amdgcn_raw_buffer_store_b128(acc, rd, off, 0, 0);
-        w += G;
-      }
-    }
+    for (int u = 0; u < ST_UNROLL; ++u) acc ^= v[u];
+    // write chunks up to the share of the read progress made so far
+    const uint32_t done = c0 + ST_UNROLL < r1 ? c0 + ST_UNROLL - r0 : r1 - r0;
+    const uint32_t target = w0 + (uint32_t)((uint64_t)(w1 - w0) * done / (r1 - r0));
+    for (; wnext < target; ++wnext) put(wnext);
   }
-  // writes left over by rounding (at most a few per thread)
-  for (; w < nw; w += G) {
-    if (cpol)
-      __builtin_amdgcn_raw_buffer_store_b128(acc, rd, w * 16u, 0, 16);
-    else
-      __builtin_amdgcn_raw_buffer_store_b128(acc, rd, w * 16u, 0, 0);
-  }
+  for (; wnext < w1; ++wnext) put(wnext);   // all of it when there is nothing to read
 }
 
 }  // namespace
@@ -73,7 +69,7 @@ extern "C" tq_status tq_testing_stream(const void* src, size_t read_bytes, void*
   if (read_bytes == 0 && write_bytes == 0) return TQ_OK;
   int cus = 256, dev = 0;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int blocks = workgroups > 0 ? workgroups : 8 * cus;
+  const int blocks = workgroups > 0 ? workgroups : 4 * cus;
   // with no reads every thread writes its share in the leftover loop
   hipLaunchKernelGGL(tq::stream_kernel, dim3(blocks), dim3(tq::ST_THREADS), 0, (hipStream_t)stream,
                      static_cast<const uint8_t*>(src), (uint32_t)(read_bytes / 16), static_cast<uint8_t*>(dst),
