@@ -62,7 +62,9 @@ typedef enum {
   TQ_ERR_HIP = 3
 } tq_status;
 
-typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 } tq_rot;
+/* Rotations: a dense orthogonal matrix; the sign-flipped Hadamard transform
+ * (one round); or two rounds of it with independent signs. */
+typedef enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1, TQ_ROT_HADAMARD2 = 2 } tq_rot;
 /* Values of the int dtype and layout arguments (passed as int so that any
  * value a caller passes is defined and rejected when it names none of these). */
 typedef enum { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
@@ -78,9 +80,14 @@ typedef enum { TQ_LAYOUT_BLOCKS = 0, TQ_LAYOUT_RECORDS = 1 } tq_layout;
  *           tq_scores and tq_attend; tq_scores_topk needs m = d_rot)
  *   bits    total bit budget b: prod uses b-1 index bits plus 1 QJL bit
  *           (2 <= b <= 4), mse uses b index bits (1 <= b <= 4)
- *   rot     TQ_ROT_DENSE or TQ_ROT_HADAMARD
+ *   rot     TQ_ROT_DENSE, TQ_ROT_HADAMARD (y = H D pad(u) / sqrt(d_rot)) or
+ *           TQ_ROT_HADAMARD2 (two rounds: y = (H D2 / sqrt(d_rot)) (H D1 /
+ *           sqrt(d_rot)) pad(u), round 1 first, D_r = diag(eps[r]); the
+ *           explainer page's randomised Hadamard transform applied twice).
+ *           Two rounds run natively at d_rot = 2048; at d_rot = 128 pass the
+ *           matrix of tq_hadamard_matrix as a dense pi instead.
  *   pi      device f32 [d_rot][d] row-major, y = pi * u   (dense; else NULL)
- *   eps     device f32 [d_rot] of +1/-1                  (hadamard; else NULL)
+ *   eps     device f32 [rounds][d_rot] of +1/-1          (hadamard; else NULL)
  *   s       device f32 [m][d_rot] row-major, the Gaussian QJL matrix (prod; NULL for mse)
  *   centroids   HOST f32 [2^bq] ascending, bq = index bits, unit-sphere units
  *   boundaries  HOST f32 [2^bq - 1], centroids[i] < boundaries[i] < centroids[i+1]
@@ -127,6 +134,20 @@ const char* tq_last_error(void);
  * odd-symmetric.  d in {0} U [2, 65536], 1 <= bits <= 4.
  * centroids: host double[2^bits] (ascending), boundaries: host double[2^bits-1]. */
 tq_status tq_build_codebook(int d, int bits, double* centroids, double* boundaries);
+
+/* The R-round sign-flipped Hadamard transform as an explicit matrix:
+ *   out[i][j] = ((H D_R / sqrt(d_rot)) ... (H D_1 / sqrt(d_rot)) e_j)_i,
+ * i < d_rot, j < d (the zero padding of inputs shorter than d_rot folded in),
+ * D_r = diag(eps[r]), H the Sylvester Hadamard matrix.  Passed as a dense
+ * rotation (rot = TQ_ROT_DENSE, pi = out, d_rot = d) it gives the encoders,
+ * scores and attention at d = 128 the multi-round transform.  The unscaled
+ * transform is exact in float32; the scale d_rot^(-R/2) is applied once, so
+ * the two-round matrix (entries integer / d_rot) is exact.
+ * eps     device f32 [rounds][d_rot] of +1/-1
+ * out     device f32 [d_rot][d] (written)
+ * Supported: d_rot a power of two in [2, 2048], 1 <= d <= d_rot, 1 <= rounds <= 2.
+ * One launch on the stream. */
+tq_status tq_hadamard_matrix(const float* eps, int rounds, int d, int d_rot, float* out, void* stream);
 
 /* Number of 32-bit plane words and float16 scalars in one record.  For a key
  * quantizer without a QJL matrix (s == NULL) tq_key_layout describes MSE-only

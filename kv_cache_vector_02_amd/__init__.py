@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP = 0, 1, 2, 3
-TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
+TQ_ROT_DENSE, TQ_ROT_HADAMARD, TQ_ROT_HADAMARD2 = 0, 1, 2
 TQ_F32, TQ_F16 = 0, 1
 TQ_LAYOUT_BLOCKS, TQ_LAYOUT_RECORDS = 0, 1
 
@@ -28,6 +28,7 @@ EXPORTED = (
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
     "tq_key_record_bytes", "tq_val_record_bytes", "tq_scores_noalloc", "tq_scores_noalloc_capacity",
+    "tq_hadamard_matrix",
 )
 # measurement and testing entry points (include/tq_testing.h)
 EXPORTED_TESTING = ("tq_testing_stream", "tq_testing_scores_wait")
@@ -95,6 +96,7 @@ def lib():
         L.tq_attend.argtypes = [P, P, vp, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
                                 vp, vp, sz, vp]
         L.tq_scores_noalloc.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp]
+        L.tq_hadamard_matrix.argtypes = [vp, ci, ci, ci, vp, vp]
         L.tq_scores_noalloc_capacity.restype = sz
         L.tq_scores_noalloc_capacity.argtypes = []
         L.tq_key_record_bytes.restype = sz
@@ -320,6 +322,12 @@ def scores_prepared(kp: Params, segs: int, group: int, keys: Cache, T: int, out,
                     stream=None):
     _check(lib().tq_scores_prepared(kp.c, segs, group, keys.c, _ptr(length), int(T), _ptr(out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hadamard_matrix(eps, rounds: int, d: int, out, stream=None):
+    """tq_hadamard_matrix: the explicit R-round sign-flipped Hadamard transform
+    (eps: device float32 [rounds, d_rot]) into out (device float32 [d_rot, d])."""
+    _check(lib().tq_hadamard_matrix(_ptr(eps), int(rounds), int(d), int(eps.shape[-1]), _ptr(out), _stream(stream)))
 
 
 def key_record_bytes(p: Params) -> int:

@@ -36,8 +36,8 @@ int index_bits(const tq_params* p, bool prod) { return prod ? p->bits - 1 : p->b
 tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool need_symmetric) {
   if (!p) return fail(TQ_ERR_INVALID_ARG, "params is NULL");
   if (p->d < 1) return fail(TQ_ERR_INVALID_ARG, "d must be >= 1 (got %d)", p->d);
-  if (p->rot != TQ_ROT_DENSE && p->rot != TQ_ROT_HADAMARD)
-    return fail(TQ_ERR_INVALID_ARG, "rot must be TQ_ROT_DENSE or TQ_ROT_HADAMARD");
+  if (p->rot != TQ_ROT_DENSE && p->rot != TQ_ROT_HADAMARD && p->rot != TQ_ROT_HADAMARD2)
+    return fail(TQ_ERR_INVALID_ARG, "rot must be TQ_ROT_DENSE, TQ_ROT_HADAMARD or TQ_ROT_HADAMARD2");
   if (p->rot == TQ_ROT_DENSE) {
     if (p->d_rot != p->d) return fail(TQ_ERR_INVALID_ARG, "dense rotation needs d_rot == d");
     if (!p->pi) return fail(TQ_ERR_INVALID_ARG, "dense rotation needs pi");
@@ -120,17 +120,22 @@ tq_status encode(const tq_params* p, bool prod, const void* x, int dtype, int64_
   a.qjl = prod;
   a.m = prod ? p->m : 0;
   a.eden = eden;
-  if (eden && !(p->d == 128 && p->d_rot == 128) && !(p->rot == TQ_ROT_HADAMARD && p->d_rot == 2048))
+  const bool fwht2k = p->rot != TQ_ROT_DENSE && p->d_rot == 2048;     // one or two rounds in registers
+  if (p->rot == TQ_ROT_HADAMARD2 && !fwht2k)
+    return fail(TQ_ERR_UNSUPPORTED, "two Hadamard rounds run natively at d_rot = 2048; at d_rot = 128 pass "
+                                    "tq_hadamard_matrix's matrix as a dense rotation");
+  if (eden && !(p->d == 128 && p->d_rot == 128) && !fwht2k)
     return fail(TQ_ERR_UNSUPPORTED, "tq_encode_eden supports d = d_rot = 128 and the Hadamard rotation at d_rot = 2048");
   a.planes = (uint32_t*)out.planes;
   a.scalars = (uint16_t*)out.scalars;
   a.slot = slot;
   a.records = out.records;
-  a.had = p->rot == TQ_ROT_HADAMARD;
+  a.had = p->rot != TQ_ROT_DENSE;
+  a.rounds = p->rot == TQ_ROT_HADAMARD2 ? 2 : 1;
   hipStream_t s = (hipStream_t)stream;
   if (p->d == 128 && p->d_rot == 128)
     return hip_status(tq::launch_encode_dense128(a, s), "encode launch");
-  if (prod && p->rot == TQ_ROT_HADAMARD && p->d_rot == 2048) {
+  if (prod && fwht2k) {
     if (p->m != p->d_rot) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs m = d_rot");
     if (p->d % 8) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs d a multiple of 8 (got %d)", p->d);
     const size_t need = tq::encode2k_workspace(n);
@@ -139,7 +144,7 @@ tq_status encode(const tq_params* p, bool prod, const void* x, int dtype, int64_
     if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
     return hip_status(tq::launch_encode2k(a, ws, s), "encode launch");
   }
-  if (!prod && p->rot == TQ_ROT_HADAMARD && p->d_rot == 2048) {
+  if (!prod && fwht2k) {
     if (p->d % 8) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs d a multiple of 8 (got %d)", p->d);
     return hip_status(tq::launch_encode2k_mse(a, s), "encode launch");
   }
@@ -216,9 +221,20 @@ tq_status tq_encode_prod(const tq_params* p, const void* x, int dtype, int64_t n
   return encode(p, true, x, dtype, n, ld_x, out, slot, nullptr, 0, stream);
 }
 
+tq_status tq_hadamard_matrix(const float* eps, int rounds, int d, int d_rot, float* out, void* stream) {
+  if (d_rot < 2 || d_rot > 2048 || (d_rot & (d_rot - 1)))
+    return fail(TQ_ERR_INVALID_ARG, "d_rot must be a power of two in [2, 2048] (got %d)", d_rot);
+  if (d < 1 || d > d_rot) return fail(TQ_ERR_INVALID_ARG, "need 1 <= d <= d_rot (got d = %d)", d);
+  if (rounds < 1 || rounds > 2) return fail(TQ_ERR_INVALID_ARG, "rounds must be 1 or 2 (got %d)", rounds);
+  if (!eps || !out) return fail(TQ_ERR_INVALID_ARG, "eps and out must be non-NULL");
+  if (!aligned(eps, 4) || !aligned(out, 4)) return fail(TQ_ERR_INVALID_ARG, "eps and out must be 4-byte aligned");
+  return hip_status(tq::launch_hadamard_matrix(eps, rounds, d, d_rot, out, (hipStream_t)stream),
+                    "hadamard matrix launch");
+}
+
 size_t tq_encode_workspace(const tq_params* p, int64_t n) {
   if (!p || n <= 0) return 0;
-  if (p->d_rot == 2048 && p->rot == TQ_ROT_HADAMARD && p->s) return tq::encode2k_workspace(n);
+  if (p->d_rot == 2048 && p->rot != TQ_ROT_DENSE && p->s) return tq::encode2k_workspace(n);
   return 0;
 }
 
@@ -267,6 +283,8 @@ static tq_status score_args(const tq_params* kp, const float* q, bool need_q, in
   }
   if (kp->d != 128 || kp->d_rot != 128)
     return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports d = d_rot = 128 (got %d, %d)", kp->d, kp->d_rot);
+  if (kp->rot == TQ_ROT_HADAMARD2)
+    return fail(TQ_ERR_UNSUPPORTED, "at d_rot = 128 pass tq_hadamard_matrix's two-round matrix as a dense rotation");
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores supports up to 16 query heads per segment");
   if ((need_q && !q) || (need_keys && (!keys.planes || !keys.scalars)) || (need_scores && !scores) || !ws)
     return fail(TQ_ERR_INVALID_ARG, "q, keys, scores and ws must be non-NULL");
@@ -397,6 +415,8 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   if (segs == 0) return TQ_OK;
   if (kp->d != 128 || kp->d_rot != 128 || vp->d != 128 || vp->d_rot != 128)
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports d = d_rot = 128 for keys and values");
+  if (kp->rot == TQ_ROT_HADAMARD2 || vp->rot == TQ_ROT_HADAMARD2)
+    return fail(TQ_ERR_UNSUPPORTED, "at d_rot = 128 pass tq_hadamard_matrix's two-round matrix as a dense rotation");
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports up to 16 query heads per segment");
   if (qjl && kp->m != kp->d_rot && vp->bits < 2)
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend with m = d / 2 keys supports value bits 2..4");
@@ -469,8 +489,8 @@ tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache k
   if (st != TQ_OK) return st;
   if (nq < 0 || T < 0 || k < 1) return fail(TQ_ERR_INVALID_ARG, "need nq >= 0, T >= 0, k >= 1");
   if (nq == 0) return TQ_OK;
-  if (kp->rot != TQ_ROT_HADAMARD || kp->d_rot != 2048)
-    return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports the Hadamard rotation at d_rot = 2048");
+  if (kp->rot == TQ_ROT_DENSE || kp->d_rot != 2048)
+    return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports the Hadamard rotation (one or two rounds) at d_rot = 2048");
   if (kp->d % 4) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk needs d a multiple of 4 (got %d)", kp->d);
   if (k > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports k <= 16");
   if (T < k) return fail(TQ_ERR_INVALID_ARG, "need T >= k");
@@ -491,6 +511,7 @@ tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache k
   L.qjl = qjl;
   L.k = k;
   L.eps = kp->eps;
+  L.rounds = kp->rot == TQ_ROT_HADAMARD2 ? 2 : 1;
   L.s = kp->s;
   tq::walsh_coefficients(cb, L.bq, L.u, &L.usum);
   L.planes = (const uint32_t*)keys.planes;

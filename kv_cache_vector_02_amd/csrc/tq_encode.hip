@@ -33,6 +33,7 @@
 // already in the B layout GEMM2 needs (K slot e of MFMA ks2 in lane half h is
 // coordinate 64 h + 8 ks2 + e, the same map GEMM1 uses for x).
 #include <algorithm>
+#include <cmath>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -684,6 +685,44 @@ hipError_t launch_rot(const EncodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream) {
   return a.had ? launch_rot<true>(a, stream) : launch_rot<false>(a, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The explicit R-round Hadamard matrix (tq_hadamard_matrix): one workgroup per
+// column j, the transform of e_j in the LDS, rounds of sign flip then an
+// in-place butterfly pass per index bit; the unscaled values are integers
+// (exact in float32 up to 2048^2), and the scale d_rot^(-R/2) is applied once.
+// ---------------------------------------------------------------------------
+namespace {
+__global__ __launch_bounds__(256) void hadamard_matrix_kernel(const float* eps, int rounds, int d, int d_rot,
+                                                              float scale, float* out) {
+  __shared__ float v[2048];
+  const int j = blockIdx.x;
+  for (int i = threadIdx.x; i < d_rot; i += 256) v[i] = i == j ? 1.f : 0.f;
+  __syncthreads();
+  for (int r = 0; r < rounds; ++r) {
+    for (int i = threadIdx.x; i < d_rot; i += 256) v[i] *= eps[(size_t)r * d_rot + i];
+    __syncthreads();
+    for (int h = 1; h < d_rot; h <<= 1) {
+      for (int p = threadIdx.x; p < d_rot / 2; p += 256) {
+        const int lo = (p / h) * 2 * h + (p % h), hi = lo + h;
+        const float a = v[lo], b = v[hi];
+        v[lo] = a + b;
+        v[hi] = a - b;
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < d_rot; i += 256) out[(size_t)i * d + j] = v[i] * scale;
+}
+}  // namespace
+
+hipError_t launch_hadamard_matrix(const float* eps, int rounds, int d, int d_rot, float* out, hipStream_t stream) {
+  double sc = 1.0;
+  for (int r = 0; r < rounds; ++r) sc /= std::sqrt((double)d_rot);
+  hipLaunchKernelGGL(hadamard_matrix_kernel, dim3((unsigned)d), dim3(256), 0, stream, eps, rounds, d, d_rot,
+                     (float)sc, out);
+  return hipGetLastError();
 }
 
 }  // namespace tq

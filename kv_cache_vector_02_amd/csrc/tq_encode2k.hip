@@ -28,6 +28,7 @@ namespace tq {
 
 struct Encode2kArgs {
   const void* x;
+  int rounds;          // Hadamard rounds (eps holds rounds x 2048 signs)
   int64_t ld_x;
   int d;
   int64_t n;           // vectors in the call
@@ -129,6 +130,18 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
     }
   }
   fwht2048_wave(v, lane);
+  // further rounds: scale, this round's signs, transform again
+#pragma unroll 1
+  for (int r = 1; r < a.rounds; ++r) {
+    const float4* er = reinterpret_cast<const float4*>(a.eps + (size_t)r * D2 + j0);
+#pragma unroll
+    for (int i = 0; i < VPL; i += 4) {
+      const float4 e = er[i / 4];
+      v[i] *= INV_SQRT_D2 * e.x; v[i + 1] *= INV_SQRT_D2 * e.y; v[i + 2] *= INV_SQRT_D2 * e.z;
+      v[i + 3] *= INV_SQRT_D2 * e.w;
+    }
+    fwht2048_wave(v, lane);
+  }
   // quantise, pack this lane's plane words, residual
   uint32_t w[BQ];
 #pragma unroll
@@ -317,6 +330,7 @@ hipError_t launch_encode2k_mse(const EncodeArgs& e, hipStream_t stream) {
   a.d = e.d;
   a.n = e.n;
   a.eps = e.eps;
+  a.rounds = e.rounds;
   a.cb = e.cb;
   a.planes = e.planes;
   a.scalars = e.scalars;
@@ -340,6 +354,7 @@ hipError_t launch_encode2k(const EncodeArgs& e, void* ws, hipStream_t stream) {
   a.d = e.d;
   a.n = e.n;
   a.eps = e.eps;
+  a.rounds = e.rounds;
   a.cb = e.cb;
   a.planes = e.planes;
   a.scalars = e.scalars;

@@ -33,6 +33,7 @@ struct EncodeArgs {
   int qjl;             // with prod: 1 = QJL signs and gamma (prod keys), 0 = MSE-only keys
   int eden;            // MSE records: store n / <y, c[idx]> (EDEN's unbiased scale) instead of n
   int had;             // 1: sign-flipped Hadamard rotation (eps), 0: dense (pi)
+  int rounds;          // Hadamard rounds (eps holds rounds x d_rot signs)
   uint32_t* planes;    // [records][P][d_rot/32]
   uint16_t* scalars;   // [records][S] float16 bit patterns
   const int64_t* slot; // record of vector i, or null
@@ -40,6 +41,8 @@ struct EncodeArgs {
 };
 
 hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream);
+// The explicit R-round Hadamard matrix [d_rot][d] (tq_hadamard_matrix).
+hipError_t launch_hadamard_matrix(const float* eps, int rounds, int d, int d_rot, float* out, hipStream_t stream);
 
 // Prod encode at d_rot = 2048 (Hadamard): chunked two-pass path with a workspace.
 size_t encode2k_workspace(int64_t n);
@@ -55,7 +58,8 @@ struct TopkLaunch {
   const float* q;          // [nq][d]
   int nq, d, bq, k;
   int qjl;
-  const float* eps;
+  const float* eps;        // [rounds][2048]
+  int rounds;
   const float* s;          // prod only
   float u[8];
   float usum;

@@ -56,7 +56,8 @@ struct RetrArgs {
   int nq, nqp, d, ld_q;    // nqp: queries padded to whole score workgroups
   int bq;
   int qjl;                 // 1: prod keys (QJL plane), 0: MSE-only records
-  const float* eps;        // [2048]
+  const float* eps;        // [rounds][2048]
+  int rounds;
   const float* s;          // [2048][2048], prod only
   float u[8];
   float usum;
@@ -107,6 +108,17 @@ __global__ __launch_bounds__(256) void r_rotate(RetrArgs a) {
     v[i] *= e.x; v[i + 1] *= e.y; v[i + 2] *= e.z; v[i + 3] *= e.w;
   }
   fwht2048_wave(v, lane);
+#pragma unroll 1
+  for (int r = 1; r < a.rounds; ++r) {     // further Hadamard rounds
+    const float4* er = reinterpret_cast<const float4*>(a.eps + (size_t)r * D2 + j0);
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const float4 e = er[i / 4];
+      v[i] *= 0.02209708691207961f * e.x; v[i + 1] *= 0.02209708691207961f * e.y;
+      v[i + 2] *= 0.02209708691207961f * e.z; v[i + 3] *= 0.02209708691207961f * e.w;
+    }
+    fwht2048_wave(v, lane);
+  }
   float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -545,6 +557,7 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   a.bq = bq;
   a.qjl = L.qjl;
   a.eps = L.eps;
+  a.rounds = L.rounds;
   a.s = L.s;
   for (int i = 0; i < 8; ++i) a.u[i] = L.u[i];
   a.usum = L.usum;

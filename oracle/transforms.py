@@ -52,13 +52,24 @@ class DenseRotation:
 
 
 class HadamardRotation:
-    """y = H (eps * pad(u)) / sqrt(d_rot)."""
+    """y = H (eps * pad(u)) / sqrt(d_rot), or with several rounds
+
+        y = (H D_R / sqrt(d_rot)) ... (H D_1 / sqrt(d_rot)) pad(u),   D_r = diag(eps[r]),
+
+    the randomised Hadamard transform applied R times with independent sign
+    vectors, round 1 first (explainer page section 0.9: the randomised
+    Hadamard transform as a cheap stand-in for a uniform rotation; more rounds
+    bring the coordinates of any input closer to the uniform rotation's law).
+    ``eps`` is [d_rot] for one round or [R, d_rot]."""
 
     kind = "hadamard"
 
     def __init__(self, eps, d: int):
-        self.eps = np.asarray(eps, dtype=np.float64)
-        self.d_rot = self.eps.shape[0]
+        eps = np.asarray(eps, dtype=np.float64)
+        self.eps_rounds = eps[None, :] if eps.ndim == 1 else eps
+        self.eps = self.eps_rounds[0]
+        self.rounds = self.eps_rounds.shape[0]
+        self.d_rot = self.eps_rounds.shape[1]
         self.d = d
         if d > self.d_rot:
             raise ValueError("d must not exceed the padded order")
@@ -66,11 +77,14 @@ class HadamardRotation:
 
     def forward(self, u):
         u = np.asarray(u, np.float64)
-        pad = np.zeros((u.shape[0], self.d_rot))
-        pad[:, : self.d] = u
-        return ((pad * self.eps[None, :]) @ self.h.T) / np.sqrt(self.d_rot)
+        v = np.zeros((u.shape[0], self.d_rot))
+        v[:, : self.d] = u
+        for r in range(self.rounds):
+            v = ((v * self.eps_rounds[r][None, :]) @ self.h.T) / np.sqrt(self.d_rot)
+        return v
 
     def inverse(self, y):
-        y = np.asarray(y, np.float64)
-        v = (y @ self.h.T) / np.sqrt(self.d_rot) * self.eps[None, :]
+        v = np.asarray(y, np.float64)
+        for r in reversed(range(self.rounds)):
+            v = (v @ self.h.T) / np.sqrt(self.d_rot) * self.eps_rounds[r][None, :]
         return v[:, : self.d]

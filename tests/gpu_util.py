@@ -43,17 +43,32 @@ class Setup:
             self.pi = haar_orthogonal(d, seed, purpose_pi)
             self.rot = tr.DenseRotation(self.pi)
             self.eps = None
+        elif rot in ("hadamard2", "hadamard2_matrix"):
+            # two rounds with independent signs; at d = 128 the library takes
+            # them as the explicit matrix of tq_hadamard_matrix (a dense pi)
+            self.eps = np.stack([sign_vector(self.d_rot, seed, purpose_eps),
+                                 sign_vector(self.d_rot, seed, purpose_eps + 100)])
+            self.rot = tr.HadamardRotation(self.eps, d)
+            self.pi = None
         else:
             self.eps = sign_vector(self.d_rot, seed, purpose_eps)
             self.rot = tr.HadamardRotation(self.eps, d)
             self.pi = None
         self.m = m or self.d_rot
         self.s = gaussian_matrix(self.m, self.d_rot, seed, purpose_s) if prod else None
-        dev = lambda a: None if a is None else T.from_numpy(a).cuda()
-        self.params = tq.Params(d=d, d_rot=self.d_rot, m=self.m, bits=bits,
-                                rot=tq.TQ_ROT_DENSE if rot == "dense" else tq.TQ_ROT_HADAMARD,
-                                centroids=self.c32, boundaries=self.b32, pi=dev(self.pi),
-                                eps=dev(self.eps), s=dev(self.s))
+        dev = lambda a: None if a is None else T.from_numpy(np.ascontiguousarray(a)).cuda()
+        if rot == "hadamard2_matrix":
+            self.eps_dev = dev(self.eps)
+            self.pi_dev = T.empty((self.d_rot, d), dtype=T.float32, device="cuda")
+            tq.hadamard_matrix(self.eps_dev, 2, d, self.pi_dev)
+            T.cuda.synchronize()
+            self.params = tq.Params(d=d, d_rot=self.d_rot, m=self.m, bits=bits, rot=tq.TQ_ROT_DENSE,
+                                    centroids=self.c32, boundaries=self.b32, pi=self.pi_dev, s=dev(self.s))
+        else:
+            kind = {"dense": tq.TQ_ROT_DENSE, "hadamard": tq.TQ_ROT_HADAMARD, "hadamard2": tq.TQ_ROT_HADAMARD2}[rot]
+            self.params = tq.Params(d=d, d_rot=self.d_rot, m=self.m, bits=bits, rot=kind,
+                                    centroids=self.c32, boundaries=self.b32, pi=dev(self.pi),
+                                    eps=dev(self.eps), s=dev(self.s))
 
     def layout(self):
         return tq.key_layout(self.params) if self.prod else tq.value_layout(self.params)
