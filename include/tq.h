@@ -91,6 +91,18 @@ typedef enum { TQ_LAYOUT_BLOCKS = 0, TQ_LAYOUT_RECORDS = 1 } tq_layout;
  *   s       device f32 [m][d_rot] row-major, the Gaussian QJL matrix (prod; NULL for mse)
  *   centroids   HOST f32 [2^bq] ascending, bq = index bits, unit-sphere units
  *   boundaries  HOST f32 [2^bq - 1], centroids[i] < boundaries[i] < centroids[i+1]
+ *   n_sets, set_div   rotation sets (0 or 1: one set).  pi, eps and s may
+ *           hold n_sets consecutive sets ([n_sets][d_rot][d], [n_sets][d_rot],
+ *           [n_sets][m][d_rot]); segment seg of tq_scores and tq_attend uses
+ *           set (seg / set_div) % n_sets: per layer, set_div = KV heads per
+ *           layer and n_sets = layers; per (layer, head), set_div = 1 and
+ *           n_sets = segments; per head shared by all layers, set_div = 1 and
+ *           n_sets = heads (segments ordered layer-major).  The encoders use
+ *           the set the pointers name: encode each set's vectors with a
+ *           tq_params whose pointers point at that set.  tq_scores_topk takes
+ *           one set.  (The first page uses one key and one value rotation for
+ *           all layers; independent per-layer or per-head rotations are the
+ *           variant its storage/variance discussion leaves open.)
  * The score and attend kernels also require the codebook to be odd-symmetric
  * (centroids[2^bq-1-i] == -centroids[i], boundaries likewise), which every
  * Lloyd-Max codebook of this density is (TQ_ERR_UNSUPPORTED otherwise). */
@@ -105,6 +117,8 @@ typedef struct {
   const float* s;
   const float* centroids;
   const float* boundaries;
+  int n_sets;
+  int set_div;
 } tq_params;
 
 /* A packed cache, device memory owned by the caller (layout above).

@@ -48,7 +48,8 @@ class tq_params(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int), ("d_rot", ctypes.c_int), ("m", ctypes.c_int),
                 ("bits", ctypes.c_int), ("rot", ctypes.c_int),
                 ("pi", ctypes.c_void_p), ("eps", ctypes.c_void_p), ("s", ctypes.c_void_p),
-                ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p)]
+                ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p),
+                ("n_sets", ctypes.c_int), ("set_div", ctypes.c_int)]
 
 
 class tq_cache(ctypes.Structure):
@@ -152,6 +153,8 @@ class Params:
     s: Optional[object] = None            # torch float32 [m][d_rot]
     d_rot: int = 0
     m: int = 0
+    n_sets: int = 1                       # rotation sets held by pi / eps / s (leading dimension)
+    set_div: int = 1                      # segment seg uses set (seg // set_div) % n_sets
     _c: tq_params = field(default=None, repr=False)
 
     def __post_init__(self):
@@ -165,11 +168,19 @@ class Params:
                             None if self.pi is None else self.pi.data_ptr(),
                             None if self.eps is None else self.eps.data_ptr(),
                             None if self.s is None else self.s.data_ptr(),
-                            self.centroids.ctypes.data, self.boundaries.ctypes.data)
+                            self.centroids.ctypes.data, self.boundaries.ctypes.data,
+                            int(self.n_sets), int(self.set_div))
 
     @property
     def c(self):
         return ctypes.byref(self._c)
+
+    def set(self, i: int) -> "Params":
+        """The parameters of rotation set i alone (views of its pi / eps / s),
+        for the encoders, which take one set per call."""
+        pick = lambda t: None if t is None else (t[i] if self.n_sets > 1 else t)
+        return Params(d=self.d, bits=self.bits, rot=self.rot, centroids=self.centroids, boundaries=self.boundaries,
+                      pi=pick(self.pi), eps=pick(self.eps), s=pick(self.s), d_rot=self.d_rot, m=self.m)
 
 
 def key_layout(p: Params):

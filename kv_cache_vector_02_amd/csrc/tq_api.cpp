@@ -60,6 +60,8 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
   }
   if (!p->centroids || !p->boundaries)
     return fail(TQ_ERR_INVALID_ARG, "codebook centroids/boundaries are NULL");
+  if (p->n_sets < 0 || p->set_div < 0)
+    return fail(TQ_ERR_INVALID_ARG, "n_sets and set_div must be >= 0 (0 and 1 mean one set)");
   const int bq = index_bits(p, prod);
   const int K = 1 << bq;
   std::memset(cb, 0, sizeof(*cb));
@@ -319,6 +321,8 @@ static tq_status score_args(const tq_params* kp, const float* q, bool need_q, in
   a->scores = scores;
   a->ws = ws;
   a->wait_us = tq::PACK_WAIT_US;
+  a->n_sets = kp->n_sets;
+  a->set_div = kp->set_div;
   return TQ_OK;
 }
 
@@ -447,6 +451,10 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   a.k.segs = segs * div;
   a.k.group = group / div;
   a.kv_div = div;
+  a.k.n_sets = kp->n_sets;
+  a.k.set_div = (kp->set_div > 1 ? kp->set_div : 1) * div;   // sets follow the cache segment
+  a.n_sets_v = vp->n_sets;
+  a.set_div_v = vp->set_div;
   a.k.d = kp->d;
   a.k.pi = kp->pi;
   a.k.eps = kp->eps;
@@ -491,6 +499,7 @@ tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache k
   if (nq == 0) return TQ_OK;
   if (kp->rot == TQ_ROT_DENSE || kp->d_rot != 2048)
     return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports the Hadamard rotation (one or two rounds) at d_rot = 2048");
+  if (kp->n_sets > 1) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk takes one rotation set");
   if (kp->d % 4) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk needs d a multiple of 4 (got %d)", kp->d);
   if (k > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_scores_topk supports k <= 16");
   if (T < k) return fail(TQ_ERR_INVALID_ARG, "need T >= k");

@@ -79,6 +79,8 @@ struct PrepArgs {
   int slices;      // base-256 digits per weight: 2 (8 heads per tile) or 3 (4 heads)
   int mt;          // 16-row tiles per segment
   uint8_t* ws;
+  int n_sets, set_div;   // rotation sets: segment seg uses set (seg / set_div) % n_sets
+  int m_rows;            // rows of one set's QJL matrix
 };
 
 // One workgroup (8 waves) per segment.  Both 128x128 products run on the
@@ -160,6 +162,11 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   const int F = 2 * (np + (QJL ? 1 : 0));
   const int fbytes = (int)pack_frag_bytes(a.mt, F);
   const rsrc_t rdst = make_rsrc(dst, (uint32_t)pack_bytes(a.mt, F));
+  // this segment's rotation set
+  const int set = a.n_sets > 1 ? (seg / a.set_div) % a.n_sets : 0;
+  const float* set_pi = a.pi ? a.pi + (size_t)set * D * D : nullptr;
+  const float* set_eps = a.eps ? a.eps + (size_t)set * D : nullptr;
+  const float* set_s = a.s ? a.s + (size_t)set * a.m_rows * D : nullptr;
   const int row = 16 * wave + col;        // A-operand row of this lane
   static_assert(MAXG * 32 == PREP_THREADS, "one float4 of the query heads per thread");
 
@@ -170,18 +177,18 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   const int qh = t >> 5, q4 = t & 31;      // head, float4 within the head (16 x 32 = 512 threads)
   float4 qv = {0.f, 0.f, 0.f, 0.f};
   if (qh < G) qv = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + qh) * D)[q4];
-  const float4* prow = reinterpret_cast<const float4*>(a.pi + (size_t)(HAD ? 0 : row) * D);
+  const float4* prow = reinterpret_cast<const float4*>(set_pi + (size_t)(HAD ? 0 : row) * D);
   // MSE-only keys have no QJL matrix: its rows read as zeros (q_proj = 0)
   // (with m = d / 2, rows from 64 on read as zeros)
   const bool srow_live = MW == 4 || row < 32 * MW;
   const float4* srow =
-      reinterpret_cast<const float4*>(QJL ? a.s + (size_t)(MW == 4 ? row : srow_live ? row : 0) * D : a.pi);
+      reinterpret_cast<const float4*>(QJL ? set_s + (size_t)(MW == 4 ? row : srow_live ? row : 0) * D : set_pi);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int k4a = 8 * ks + 2 * kq, k4b = k4a + 1;      // coordinates 32 ks + 8 kq + 0..7
     if (HAD) {
-      mv[2 * ks] = reinterpret_cast<const float4*>(a.eps)[k4a];
-      mv[2 * ks + 1] = reinterpret_cast<const float4*>(a.eps)[k4b];
+      mv[2 * ks] = reinterpret_cast<const float4*>(set_eps)[k4a];
+      mv[2 * ks + 1] = reinterpret_cast<const float4*>(set_eps)[k4b];
     } else {
       mv[2 * ks] = prow[k4a];
       mv[2 * ks + 1] = prow[k4b];
@@ -937,6 +944,9 @@ static PrepArgs make_prep(const ScoreArgs& a, int slices) {
   p.pi = a.pi;
   p.eps = a.eps;
   p.s = a.s;
+  p.n_sets = a.n_sets > 1 ? a.n_sets : 1;
+  p.set_div = a.set_div > 1 ? a.set_div : 1;
+  p.m_rows = a.qjl ? a.m : 0;
   walsh_coefficients(a.cb, a.bq, p.u, &p.usum);
   p.bq = a.bq;
   p.slices = slices;
@@ -1487,6 +1497,7 @@ struct Combine128Args {
   const float* pi_v;
   const float* eps_v;
   float* out;
+  int n_sets, set_div;   // value rotation sets: segment seg uses set (seg / set_div) % n_sets
 };
 
 // One workgroup (256 threads) per segment: log-sum-exp merge of the chunk
@@ -1502,6 +1513,9 @@ __global__ __launch_bounds__(256, 1) void attend_combine128(Combine128Args a) {
   const int seg = blockIdx.x;
   const int t = threadIdx.x;
   const bool dense = a.rot == TQ_ROT_DENSE;
+  const int set = a.n_sets > 1 ? (seg / a.set_div) % a.n_sets : 0;
+  const float* pi_v = a.pi_v ? a.pi_v + (size_t)set * D * D : nullptr;
+  const float* eps_v = a.eps_v ? a.eps_v + (size_t)set * D : nullptr;
   if (dense) {
     // Pi_v -> LDS by the direct global-to-LDS path: lane i of a wave's
     // instruction fills 16 bytes at the wave's LDS base + 16 i
@@ -1509,7 +1523,7 @@ __global__ __launch_bounds__(256, 1) void attend_combine128(Combine128Args a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(a.pi_v + (size_t)(256 * i + t) * 4),
+          (const __attribute__((address_space(1))) void*)(pi_v + (size_t)(256 * i + t) * 4),
           (__attribute__((address_space(3))) void*)(pis + (256 * i + 64 * w) * 4), 16, 0, 0);
   }
   const float* pseg = a.part + (size_t)seg * a.nchunks * a.group * PST;
@@ -1586,7 +1600,7 @@ __global__ __launch_bounds__(256, 1) void attend_combine128(Combine128Args a) {
           o[i] += neg ? -v : v;
         }
       }
-      const float sg = a.eps_v[j] * rsqrtf((float)D);
+      const float sg = eps_v[j] * rsqrtf((float)D);
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= sg;
     }
@@ -1764,6 +1778,8 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   c.rot = a.rot_v;
   c.pi_v = a.pi_v;
   c.eps_v = a.eps_v;
+  c.n_sets = a.n_sets_v > 1 ? a.n_sets_v : 1;
+  c.set_div = (a.set_div_v > 1 ? a.set_div_v : 1) * a.kv_div;
   c.out = a.out;
   hipLaunchKernelGGL(attend_combine128, dim3((unsigned)a.k.segs), dim3(256), 0, stream, c);
   return hipGetLastError();

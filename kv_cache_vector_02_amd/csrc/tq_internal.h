@@ -95,6 +95,7 @@ struct ScoreArgs {
   float* scores;
   void* ws;
   int wait_us;           // one-launch scores: consumers' bound on the wait for the pack (microseconds)
+  int n_sets, set_div;   // rotation sets of the keys: query segment seg uses set (seg / set_div) % n_sets
 };
 
 // The bound tq_scores gives a workgroup's wait for its segment's query pack.
@@ -124,6 +125,7 @@ struct AttendArgs {
   float* out;
   void* ws;
   int kv_div;            // k.segs / cache segments: 2 when each segment's heads run as two halves
+  int n_sets_v, set_div_v;   // rotation sets of the values (per cache segment)
 };
 
 hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream);
