@@ -76,8 +76,8 @@ typedef enum { TQ_LAYOUT_BLOCKS = 0, TQ_LAYOUT_RECORDS = 1 } tq_layout;
  *   d_rot   rotated dimension: == d for the dense rotation; a power of two
  *           >= d for the Hadamard rotation (inputs are zero-padded at the end)
  *   m       QJL projection rows (prod only, else ignored): d_rot, or d_rot / 2
- *           at d_rot = 128 (the first page's proj_dim = head_dim / 2; encode,
- *           tq_scores and tq_attend; tq_scores_topk needs m = d_rot)
+ *           (the first page's proj_dim = head_dim / 2) at d_rot = 128 (encode,
+ *           tq_scores, tq_attend) and d_rot = 2048 (encode, tq_scores_topk)
  *   bits    total bit budget b: prod uses b-1 index bits plus 1 QJL bit
  *           (2 <= b <= 4), mse uses b index bits (1 <= b <= 4)
  *   rot     TQ_ROT_DENSE, TQ_ROT_HADAMARD (y = H D pad(u) / sqrt(d_rot)) or
@@ -211,7 +211,8 @@ size_t tq_encode_workspace(const tq_params* p, int64_t n);
  * zero-padded): pass 1 runs the 2048-point Walsh-Hadamard transform in
  * registers (one wave per vector) and quantises; pass 2 forms the QJL
  * projection S r of each chunk of residuals on the matrix cores.  Records use
- * the key layout of tq_key_layout (W = 64 words per plane). */
+ * the key layout of tq_key_layout (W = 64 words per plane); with m = 1024 QJL
+ * rows, the tq_key_record_words layout (sign words in groups 0..31 only). */
 tq_status tq_encode_prod_ws(const tq_params* p, const void* x, int dtype, int64_t n,
                             int64_t ld_x, tq_cache out, const int64_t* slot, void* ws,
                             size_t ws_bytes, void* stream);
@@ -356,7 +357,8 @@ size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k);
  * q       device f32 [nq][d], d a multiple of 4, zero-padded to 2048
  * keys    record t at keys.planes + t * record words (seg_stride unused)
  * ws      device workspace of tq_scores_topk_workspace() bytes, 256-B aligned
- * Supported: 1 <= k <= 16, T >= k; prod keys with b = 2, 3 or 4 bits.
+ * Supported: 1 <= k <= 16, T >= k; prod keys with b = 2, 3 or 4 bits and
+ * m = 2048 or 1024 QJL rows (kappa = sqrt(pi/2) / m).
  * Launches: query transform, projection GEMM and quantisation; per block of
  * 65536 records the bit-plane score GEMM and a per-query top-k; a final merge. */
 tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache keys, int64_t T, int k,

@@ -51,8 +51,8 @@ tq_status check_params(const tq_params* p, bool prod, tq::Codebook* cb, bool nee
   if (prod) {
     if (p->bits < 2 || p->bits > 4)
       return fail(TQ_ERR_INVALID_ARG, "prod bits must be in [2, 4] (got %d)", p->bits);
-    if (p->m != p->d_rot && !(p->d_rot == 128 && p->m == 64))
-      return fail(TQ_ERR_INVALID_ARG, "m must equal d_rot, or be 64 at d_rot = 128 (got m = %d)", p->m);
+    if (p->m != p->d_rot && !(2 * p->m == p->d_rot && (p->d_rot == 128 || p->d_rot == 2048)))
+      return fail(TQ_ERR_INVALID_ARG, "m must equal d_rot, or be d_rot / 2 at d_rot = 128 or 2048 (got m = %d)", p->m);
     if (!p->s) return fail(TQ_ERR_INVALID_ARG, "prod needs the QJL matrix s");
     if (!aligned(p->s, 16)) return fail(TQ_ERR_INVALID_ARG, "s must be 16-byte aligned");
   } else if (p->bits < 1 || p->bits > 4) {
@@ -138,7 +138,6 @@ tq_status encode(const tq_params* p, bool prod, const void* x, int dtype, int64_
   if (p->d == 128 && p->d_rot == 128)
     return hip_status(tq::launch_encode_dense128(a, s), "encode launch");
   if (prod && fwht2k) {
-    if (p->m != p->d_rot) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs m = d_rot");
     if (p->d % 8) return fail(TQ_ERR_UNSUPPORTED, "d_rot = 2048 encode needs d a multiple of 8 (got %d)", p->d);
     const size_t need = tq::encode2k_workspace(n);
     if (!ws) return fail(TQ_ERR_INVALID_ARG, "d_rot = 2048 encode needs a workspace (tq_encode_prod_ws)");
@@ -522,6 +521,7 @@ tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache k
   L.eps = kp->eps;
   L.rounds = kp->rot == TQ_ROT_HADAMARD2 ? 2 : 1;
   L.s = kp->s;
+  L.m = qjl ? kp->m : 0;
   tq::walsh_coefficients(cb, L.bq, L.u, &L.usum);
   L.planes = (const uint32_t*)keys.planes;
   L.scalars = (const uint16_t*)keys.scalars;

@@ -29,6 +29,7 @@ namespace tq {
 struct Encode2kArgs {
   const void* x;
   int rounds;          // Hadamard rounds (eps holds rounds x 2048 signs)
+  int m;               // QJL rows (prod): 2048, or 1024 (sign words in coordinate groups 0..31 only)
   int64_t ld_x;
   int d;
   int64_t n;           // vectors in the call
@@ -48,6 +49,12 @@ namespace {
 
 constexpr int D2 = 2048;
 constexpr int VPL = 32;                  // coordinates per lane
+// Prod records with m QJL rows: for each 32-coordinate group g, its BQ index
+// words, then sign word g while g < m / 32.  Word offset of group g and the
+// record's length in words.
+__device__ __forceinline__ int group_offset(int g, int bq, int mw) { return g < mw ? g * (bq + 1) : mw * (bq + 1) + (g - mw) * bq; }
+__device__ __forceinline__ int record_words(int bq, int mw) { return 64 * bq + mw; }
+
 constexpr float R2_SCALE = 256.f;        // 2^8, keeps the residual's lo part normal in fp16
 constexpr float INV_SQRT_D2 = 0.02209708691207961f;   // 1 / sqrt(2048)
 constexpr int SIGN_TILE = 128;
@@ -186,7 +193,8 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
   }
   const int64_t rec = a.slot ? a.slot[gv] : gv;
   if ((uint64_t)rec >= (uint64_t)a.records) return;      // past the cache's capacity: not written
-  uint32_t* dst = a.planes + rec * (P * (D2 / 32)) + lane * P;
+  uint32_t* dst = PROD ? a.planes + rec * record_words(BQ, a.m / 32) + group_offset(lane, BQ, a.m / 32)
+                       : a.planes + rec * (P * (D2 / 32)) + lane * P;
 #pragma unroll
   for (int p = 0; p < BQ; ++p) dst[p] = w[p];
   if (lane == 0) {
@@ -273,7 +281,8 @@ __global__ __launch_bounds__(256) void encode2k_signs(Encode2kArgs a) {
           const int64_t gv = a.v0 + m;
           const int64_t rec = a.slot ? a.slot[gv] : gv;
           if ((uint64_t)rec < (uint64_t)a.records)
-            a.planes[rec * (P * (D2 / 32)) + ((iw + 32 * j) / 32) * P + (P - 1)] = word;
+            a.planes[rec * record_words(P - 1, a.m / 32) + group_offset((iw + 32 * j) / 32, P - 1, a.m / 32) + (P - 1)] =
+                word;
         }
       }
     }
@@ -290,7 +299,7 @@ hipError_t run_chunks(const Encode2kArgs& base, bool f16, hipStream_t stream) {
       hipLaunchKernelGGL((encode2k_pass1<BQ, true, true>), dim3(g1), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((encode2k_pass1<BQ, false, true>), dim3(g1), dim3(256), 0, stream, a);
-    const dim3 g2(D2 / SIGN_TILE, (unsigned)((a.cn + SIGN_TILE - 1) / SIGN_TILE));
+    const dim3 g2((unsigned)(a.m / SIGN_TILE), (unsigned)((a.cn + SIGN_TILE - 1) / SIGN_TILE));
     hipLaunchKernelGGL((encode2k_signs<BQ + 1>), g2, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -331,6 +340,7 @@ hipError_t launch_encode2k_mse(const EncodeArgs& e, hipStream_t stream) {
   a.n = e.n;
   a.eps = e.eps;
   a.rounds = e.rounds;
+  a.m = e.m > 0 ? e.m : D2;
   a.cb = e.cb;
   a.planes = e.planes;
   a.scalars = e.scalars;
@@ -355,6 +365,7 @@ hipError_t launch_encode2k(const EncodeArgs& e, void* ws, hipStream_t stream) {
   a.n = e.n;
   a.eps = e.eps;
   a.rounds = e.rounds;
+  a.m = e.m > 0 ? e.m : D2;
   a.cb = e.cb;
   a.planes = e.planes;
   a.scalars = e.scalars;
@@ -368,7 +379,7 @@ hipError_t launch_encode2k(const EncodeArgs& e, void* ws, hipStream_t stream) {
   a.r_lo = a.r_hi + (size_t)a.chunk * D2;
   a.v0 = 0;
   a.cn = 0;
-  hipLaunchKernelGGL(split_s_f16, dim3(1024), dim3(256), 0, stream, e.s, a.s_hi, a.s_lo, (int64_t)D2 * D2);
+  hipLaunchKernelGGL(split_s_f16, dim3(1024), dim3(256), 0, stream, e.s, a.s_hi, a.s_lo, (int64_t)a.m * D2);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   switch (e.bq) {

@@ -26,7 +26,7 @@ struct EncodeArgs {
   const float* pi;     // dense rotation [d_rot][d]
   const float* eps;    // hadamard signs [d_rot]
   const float* s;      // QJL matrix [m][d_rot] (prod only)
-  int m;               // QJL rows: d_rot, or d_rot / 2 at d_rot = 128
+  int m;               // QJL rows: d_rot, or d_rot / 2 (d_rot = 128 or 2048)
   Codebook cb;
   int bq;              // index bits
   int prod;            // 1: per-record key layout, 0: values (mse, token-blocked)
@@ -60,7 +60,8 @@ struct TopkLaunch {
   int qjl;
   const float* eps;        // [rounds][2048]
   int rounds;
-  const float* s;          // prod only
+  const float* s;          // prod only, [m][2048]
+  int m;                   // QJL rows: 2048 or 1024
   float u[8];
   float usum;
   const uint32_t* planes;  // records, key layout with W = 64

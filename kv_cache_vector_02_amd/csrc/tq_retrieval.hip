@@ -58,6 +58,7 @@ struct RetrArgs {
   int qjl;                 // 1: prod keys (QJL plane), 0: MSE-only records
   const float* eps;        // [rounds][2048]
   int rounds;
+  int m;                   // QJL rows: 2048, or 1024
   const float* s;          // [2048][2048], prod only
   float u[8];
   float usum;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void r_pack(RetrArgs a) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     vr[i] = live ? a.qrot[(int64_t)q * D2 + 32 * lane + i] : 0.f;
-    vp[i] = live && a.qjl ? a.qproj[(int64_t)q * D2 + 32 * lane + i] : 0.f;
+    vp[i] = live && a.qjl && 32 * lane + i < a.m ? a.qproj[(int64_t)q * D2 + 32 * lane + i] : 0.f;
     mx = fmaxf(mx, fabsf(vr[i]));
     px = fmaxf(px, fabsf(vp[i]));
     sr += vr[i];
@@ -287,10 +288,16 @@ struct ScoreBlockArgs {
   float* scores;             // [nq][rc]
 };
 
-template <int BQ, int QJL>
+// HALF: prod records with m = 1024 QJL rows (for each group g its index
+// words, then sign word g while g < 32); the lanes of groups 32..63 load the P
+// words ending with the group's last index word and rotate them into place, so
+// the sign slot holds a foreign word, whose QJL weights (rows >= 1024) are zero.
+template <int BQ, int QJL, bool HALF = false>
 __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
   constexpr int NP = r_planes(BQ), F = r_frags(BQ, QJL), QPT = RQPT;
   constexpr int P = BQ + QJL;
+  constexpr int MWD = HALF ? 32 : 64;                   // sign words per record
+  constexpr int RW = QJL ? 64 * BQ + MWD : 64 * P;     // words per record
   constexpr int HL = 2;                         // queries per lane group per row tile
   constexpr int FR = RTQ * F * 64;              // 16-byte fragment units per chunk per workgroup
   constexpr int LPT = FR / 256;                 // of them per thread
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
   const int t16 = lane & 15, kg = lane >> 4;
   const int rt0 = blockIdx.y * RTQ;              // first query row tile
   const int64_t rec0 = a.r0 + (int64_t)blockIdx.x * 128 + 32 * wave;   // this wave's 32 records
-  const rsrc_t rk = make_rsrc(a.planes + a.r0 * (P * 64), clamp_bytes((a.T - a.r0) * (int64_t)(P * 256)));
+  const rsrc_t rk = make_rsrc(a.planes + a.r0 * RW, clamp_bytes((a.T - a.r0) * (int64_t)(RW * 4)));
   const uint4* gpack = reinterpret_cast<const uint4*>(a.pack);
   auto gfrag = [&](int c, int u) {   // u-th 16-byte unit of chunk c of this workgroup's row tiles
     const int rt = u / (F * 64), rem = u % (F * 64);
@@ -312,8 +319,18 @@ __global__ __launch_bounds__(256) void r_score_block(ScoreBlockArgs a) {
   for (int i = 0; i < LPT; ++i) nxt[i] = gfrag(0, threadIdx.x + 256 * i);
   auto rec_words = [&](int c, int ct) {
     const int64_t rec = rec0 + 16 * ct + t16;
-    const uint32_t off = rec < a.T ? (uint32_t)(((rec - a.r0) * (P * 64) + (4 * c + kg) * P) * 4) : OOB_OFFSET;
-    return load_words<P>(rk, off);
+    const int g = 4 * c + kg;
+    const bool late = HALF && g >= MWD;
+    const int goff = late ? MWD * P + (g - MWD) * BQ - 1 : g * P;
+    const uint32_t off = rec < a.T ? (uint32_t)(((rec - a.r0) * RW + goff) * 4) : OOB_OFFSET;
+    wvec w = load_words<P>(rk, off);
+    if constexpr (HALF) {
+      wvec r;
+#pragma unroll
+      for (int i = 0; i < P; ++i) r[i] = late ? w[(i + 1) % P] : w[i];
+      w = r;
+    }
+    return w;
   };
   wvec wn[2];
   wn[0] = rec_words(0, 0);
@@ -509,8 +526,14 @@ __global__ __launch_bounds__(256) void r_topk(TopkArgs a) {
 }
 
 template <int BQ, int QJL>
-hipError_t score_blocks(const ScoreBlockArgs& b, int nrt, hipStream_t stream) {
+hipError_t score_blocks(const ScoreBlockArgs& b, int nrt, hipStream_t stream, bool half = false) {
   const dim3 grid((unsigned)((b.rc + 127) / 128), (unsigned)((nrt + RTQ - 1) / RTQ));
+  if constexpr (QJL == 1) {
+    if (half) {
+      hipLaunchKernelGGL((r_score_block<BQ, QJL, true>), grid, dim3(256), 0, stream, b);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((r_score_block<BQ, QJL>), grid, dim3(256), 0, stream, b);
   return hipGetLastError();
 }
@@ -561,7 +584,8 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   a.s = L.s;
   for (int i = 0; i < 8; ++i) a.u[i] = L.u[i];
   a.usum = L.usum;
-  a.kappa = (float)(std::sqrt(M_PI / 2.0) / D2);
+  a.m = L.qjl ? L.m : D2;
+  a.kappa = (float)(std::sqrt(M_PI / 2.0) / a.m);
   const int64_t rc = block_records(L.T);
   const int64_t nch = (L.T + rc - 1) / rc;
   const int nrt = padded_queries(L.nq, bq) / RQPT;
@@ -586,9 +610,9 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   float* cval = reinterpret_cast<float*>(take((size_t)L.nq * nch * L.k * 4));
   int64_t* cidx = reinterpret_cast<int64_t*>(take((size_t)L.nq * nch * L.k * 8));
 
-  if (L.qjl) hipLaunchKernelGGL(r_split_s, dim3(1024), dim3(256), 0, stream, L.s, a.s_hi, a.s_lo, (int64_t)D2 * D2);
+  if (L.qjl) hipLaunchKernelGGL(r_split_s, dim3(1024), dim3(256), 0, stream, L.s, a.s_hi, a.s_lo, (int64_t)a.m * D2);
   hipLaunchKernelGGL(r_rotate, dim3((unsigned)(a.nqp / 4)), dim3(256), 0, stream, a);
-  if (L.qjl) hipLaunchKernelGGL(r_project, dim3(D2 / 128, (unsigned)(a.nqp / 128)), dim3(256), 0, stream, a);
+  if (L.qjl) hipLaunchKernelGGL(r_project, dim3((unsigned)(a.m / 128), (unsigned)(a.nqp / 128)), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(r_pack, dim3((unsigned)(padded_queries(L.nq, bq) / 4)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -604,9 +628,9 @@ hipError_t launch_topk2k(const TopkLaunch& L, hipStream_t stream) {
   for (int64_t ch = 0; ch < nch; ++ch) {
     b.r0 = ch * rc;
     switch (bq * 2 + L.qjl) {
-      case 3: e = score_blocks<1, 1>(b, nrt, stream); break;
-      case 5: e = score_blocks<2, 1>(b, nrt, stream); break;
-      case 7: e = score_blocks<3, 1>(b, nrt, stream); break;
+      case 3: e = score_blocks<1, 1>(b, nrt, stream, a.m < D2); break;
+      case 5: e = score_blocks<2, 1>(b, nrt, stream, a.m < D2); break;
+      case 7: e = score_blocks<3, 1>(b, nrt, stream, a.m < D2); break;
       case 2: e = score_blocks<1, 0>(b, nrt, stream); break;
       case 4: e = score_blocks<2, 0>(b, nrt, stream); break;
       case 6: e = score_blocks<3, 0>(b, nrt, stream); break;

@@ -19,8 +19,8 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def _setup(bits, seed=4, prod=True):
-    return Setup(d=1536, d_rot=2048, bits=bits, prod=prod, rot="hadamard", seed=seed)
+def _setup(bits, seed=4, prod=True, m=None):
+    return Setup(d=1536, d_rot=2048, bits=bits, prod=prod, rot="hadamard", seed=seed, m=m)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
@@ -247,3 +247,26 @@ def test_topk_full_size(bits):
     ref_top = est.topk(ref, K)[0]
     same = np.mean([set(pos[a]) == set(b) for a, b in zip(ref_top, got_idx)])
     _log(f"  index sets equal to the oracle's on {same:.3f} of the queries")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_encode_2048_half_projection(bits):
+    # m = 1024 QJL rows at d' = 2048 (the first page's proj_dim = d / 2): the
+    # record holds sign words for coordinate groups 0..31 only
+    _log(f"retrieval encode b{bits} with m = 1024")
+    db, _ = mixture_database(3000, 1536, seed=14)
+    st = _setup(bits, seed=14, m=1024)
+    assert tq.key_record_words(st.params) == 64 * (bits - 1) + 32
+    planes, scal = st.encode_gpu(db)
+    _log(f"  {compare_encode(st, planes, scal, st.encode_oracle(db))}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_topk_2048_half_projection(bits):
+    _log(f"retrieval top-10 b{bits} with m = 1024: 20000 records, 30 queries")
+    db, qs = mixture_database(20000, 1536, seed=15, n_queries=30)
+    st = _setup(bits, seed=15, m=1024)
+    cache, (idx, z, n, g) = _oracle_cache(st, db)
+    got_idx, got_val = _gpu_topk(st, qs, cache, len(db), 10)
+    ref = est.prod_scores(qs, idx, z, n, g, st.rot, st.s, st.c32)
+    _check_topk(got_idx, got_val, ref, 10)
