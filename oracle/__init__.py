@@ -18,6 +18,10 @@ its section or equation):
 * ``packing``    -- the bit-plane record layout both sides agree on.
 * ``estimator``  -- the asymmetric inner-product estimator, MSE dequantization,
   softmax attention over the compressed cache and top-k retrieval.
+* ``polar``      -- PolarQuant as stage 1: the recursive polar transform of
+  the rotated vector, Lloyd-Max codebooks of each level's angle law, the
+  reconstruction and the score estimate with the optional QJL stage (FastVQ
+  README, "PolarQuant Algorithm" and "TurboQuant Combination").
 * ``quality``    -- attention-fidelity and needle statistics of an estimated
   score matrix against the exact one (the first page's usage patterns).
 
@@ -25,4 +29,4 @@ Parity pins: every function is pinned in ``tests/test_oracle_*.py`` to values
 the pages print, closed forms, invariants or brute force.  Functions without
 such a pin say "parity unpinned" in their docstring.
 """
-from . import codebook, transforms, quantizer, packing, estimator, quality  # noqa: F401
+from . import codebook, transforms, quantizer, packing, estimator, quality, polar  # noqa: F401

@@ -169,3 +169,65 @@ def unpack_value_blocks(words, n: int) -> np.ndarray:
         bits = unpack_bits(words[:, :, p].reshape(nb * d, 1)).reshape(nb, d, 32)   # [B, j, i]
         idx |= bits.transpose(0, 2, 1).reshape(nb * 32, d).astype(np.int64) << p
     return idx[:n]
+
+
+# ---- PolarQuant records ----------------------------------------------------
+#
+# A polar key record (d = 2^L) is a run of 32-bit words:
+#   level-1 stream  the d/2 level-1 cells, cell j at bits j*b1 .. j*b1+b1-1 of a
+#                   little-endian bit stream (bit k of the stream is bit k mod 32
+#                   of word k div 32), ceil(d b1 / 64) words;
+#   upper stream    the d/2 - 1 cells of levels 2 .. L, level by level and in
+#                   ascending position within a level, b bits each, packed the
+#                   same way, ceil((d/2 - 1) b / 32) words;
+#   sign words      m/32 words of QJL bits (stage 2 only), bit i of the
+#                   projection in bit i mod 32 of word i div 32.
+# Scalars: float16 n = ||x||, and float16 gamma = ||r|| with stage 2.
+
+def pack_stream(codes, width: int) -> np.ndarray:
+    """[N, K] cells of `width` bits -> [N, ceil(K width / 32)] words (little-endian stream)."""
+    codes = np.asarray(codes, np.int64)
+    n, k = codes.shape
+    bits = ((codes[:, :, None] >> np.arange(width)[None, None, :]) & 1).reshape(n, k * width)
+    words = -(-(k * width) // 32)
+    pad = np.zeros((n, words * 32), bool)
+    pad[:, :k * width] = bits
+    return pack_bits(pad)
+
+
+def unpack_stream(words, count: int, width: int) -> np.ndarray:
+    bits = unpack_bits(words)[:, :count * width].reshape(-1, count, width).astype(np.int64)
+    return (bits << np.arange(width)[None, None, :]).sum(axis=2)
+
+
+def polar_record_words(d: int, bits1: int, bits: int, m: int) -> int:
+    return -(-(d // 2) * bits1 // 32) + -(-(d // 2 - 1) * bits // 32) + m // 32
+
+
+def pack_polar(code, bits1: int, bits: int):
+    """PolarCode -> (words [N, polar_record_words], scalars [N, 1 or 2] float16)."""
+    l1 = pack_stream(code.codes[0], bits1)
+    upper = np.concatenate([np.asarray(c, np.int64) for c in code.codes[1:]], axis=1)
+    parts = [l1, pack_stream(upper, bits)]
+    scal = [code.n]
+    if code.z is not None:
+        parts.append(pack_bits(code.z))
+        scal.append(code.gamma)
+    return np.ascontiguousarray(np.concatenate(parts, axis=1)), np.stack(scal, axis=1).astype(np.float16)
+
+
+def unpack_polar(words, scalars, d: int, bits1: int, bits: int, m: int):
+    """Record words -> (codes per level, z [N, m] or None, n [N], gamma [N] or None)."""
+    words = np.asarray(words, np.uint32)
+    s = np.asarray(scalars, np.float16).astype(np.float64)
+    w1 = -(-(d // 2) * bits1 // 32)
+    wu = -(-(d // 2 - 1) * bits // 32)
+    codes = [unpack_stream(words[:, :w1], d // 2, bits1)]
+    upper = unpack_stream(words[:, w1:w1 + wu], d // 2 - 1, bits)
+    pos, size = 0, d // 4
+    while size >= 1:
+        codes.append(upper[:, pos:pos + size])
+        pos += size
+        size //= 2
+    z = unpack_bits(words[:, w1 + wu:w1 + wu + m // 32]) if m else None
+    return codes, z, s[:, 0], (s[:, 1] if m else None)
