@@ -364,6 +364,91 @@ size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k);
 tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache keys, int64_t T, int k,
                          int64_t* idx, float* val, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- PolarQuant as stage 1 -------------------------------------------------
+ * The FastVQ README ("PolarQuant Algorithm"; its "Implementation Notes" name
+ * the paper's transform as the full recursive one, which this is; its
+ * "TurboQuant Combination" for the optional QJL stage).
+ *
+ * With n = ||x||, u = x / n (0 for x = 0) and y = rot(u) (d = d_rot = 2^L):
+ *   level 1      psi = atan2(y[2j+1], y[2j]) in (-pi, pi] for each coordinate
+ *                pair, rho = the pair's length (j = 0 .. d/2 - 1)
+ *   level l > 1  psi = atan2(rho[2j+1], rho[2j]) in [0, pi/2] over the lengths
+ *                of level l - 1, rho = their combined length
+ *   level L leaves one length, ||y|| = 1: the record keeps n and d - 1 codes.
+ * Each angle's code is the number of its level's boundaries at or below it
+ * (Lloyd-Max cells of the angle's law after a uniform rotation: uniform at
+ * level 1, sin^2 psi ~ Beta(2^(l-2), 2^(l-2)) above; tq_build_polar_codebook).
+ * The reconstruction y~ splits the unit length down the levels with the
+ * centroid angles (rho cos, rho sin), so ||y~|| = 1, and x~ = n rot^T(y~).
+ * With m = d the QJL stage follows on r = y - y~ (z = [S r >= 0], gamma = ||r||),
+ * and the score estimate is
+ *   s(q, t) = n_t ( <rot(q), y~_t> + gamma_t sqrt(pi/2)/m <S rot(q), 2 z_t - 1> ).
+ *
+ * Record (u32 words, then float16 scalars in their own array):
+ *   level-1 stream  d/2 codes of bits1 bits, code j at bits j*bits1 .. of a
+ *                   little-endian bit stream (bit k in bit k%32 of word k/32):
+ *                   d*bits1/64 words
+ *   upper stream    the d/2 - 1 codes of levels 2 .. L, level by level and in
+ *                   ascending position, bits each, same packing:
+ *                   ceil((d/2 - 1) bits / 32) words
+ *   sign words      m/32 words of QJL bits (m > 0)
+ *   scalars         float16 n, and float16 gamma when m > 0
+ * At d = 128 that is 2 bits1 + 2 bits + m/32 words; planes [records][words],
+ * scalars [records][1 or 2]; record r of segment s is s * seg_stride + t. */
+typedef struct {
+  int d;                    /* 128 */
+  int rot;                  /* TQ_ROT_DENSE or TQ_ROT_HADAMARD (one round) */
+  int bits1;                /* bits of each level-1 code, 1..4 */
+  int bits;                 /* bits of each code at levels 2..L, 1..4 */
+  int m;                    /* QJL rows: 0 (no second stage) or d */
+  const float* pi;          /* device f32 [d][d] (dense; else NULL) */
+  const float* eps;         /* device f32 [d] of +1/-1 (hadamard; else NULL) */
+  const float* s;           /* device f32 [m][d] (m > 0; else NULL) */
+  const float* centroids;   /* HOST f32: 2^bits1 level-1 centroids, then 2^bits for each level 2..L */
+  const float* boundaries;  /* HOST f32: 2^bits1 - 1 level-1 boundaries, then 2^bits - 1 per level */
+} tq_polar_params;
+/* Codebook requirements (TQ_ERR_INVALID_ARG otherwise): finite centroids,
+ * boundaries strictly between their neighbouring centroids; level-1
+ * boundaries in (-pi, pi), upper-level boundaries in (0, pi/2). */
+
+/* Lloyd-Max codebook of a level's angle (host, float64, deterministic):
+ * level 1 the uniform grid of 2^bits cells from -pi; level >= 2 the Lloyd-Max
+ * quantizer of the density proportional to sin^(2^(l-1) - 1)(2 psi) on
+ * [0, pi/2], symmetric about pi/4 (explainer page section 5: midpoint
+ * boundaries, conditional-mean centroids).  1 <= level <= 16, 1 <= bits <= 4.
+ * centroids: host double[2^bits], boundaries: host double[2^bits - 1]. */
+tq_status tq_build_polar_codebook(int level, int bits, double* centroids, double* boundaries);
+
+/* Words per polar record (0 for invalid parameters). */
+size_t tq_polar_record_words(const tq_polar_params* p);
+
+/* PolarQuant encode of n vectors into polar records.
+ * x, dtype, n, ld_x, slot: as for tq_encode_prod; out.planes u32
+ * [records][tq_polar_record_words], out.scalars f16 [records][m ? 2 : 1],
+ * out.records >= 1, a vector whose record lies outside [0, out.records) is
+ * not written.  One launch: the rotation (and the QJL projection) on the
+ * matrix cores in fp16 hi/lo parts, the transform and the codes per lane.
+ * Supported: d = 128. */
+tq_status tq_polar_encode(const tq_polar_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
+                          tq_cache out, const int64_t* slot, void* stream);
+
+/* Dequantize polar records 0 .. n-1 of `in`: out[i][0..d) = x~_i (float32,
+ * device, rows ld_out >= d apart, 4-byte aligned).  The QJL bits, if any, are
+ * not used (the reconstruction is stage 1's).  Needs n <= in.records. */
+tq_status tq_polar_decode(const tq_polar_params* p, tq_cache in, int64_t n, float* out, int64_t ld_out,
+                          void* stream);
+
+/* Score estimates of query heads against polar keys (the formula above; the
+ * first term alone when m = 0), in the shapes of tq_scores:
+ * q device f32 [segs*group][d] (16-byte aligned), len device int32 [segs] or
+ * NULL, scores device f32 [segs*group][T] (t >= len not written), keys with
+ * (segs - 1) * seg_stride + T <= keys.records.  One launch; each workgroup
+ * rotates and projects its segment's query heads and builds per-head tables
+ * in the LDS (the level-1 pair terms per code, the QJL sign terms per nibble)
+ * before streaming its tokens.  Supported: d = 128, 1 <= group <= 16. */
+tq_status tq_polar_scores(const tq_polar_params* p, const float* q, int segs, int group, tq_cache keys,
+                          const int32_t* len, int64_t T, float* scores, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

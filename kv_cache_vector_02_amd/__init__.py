@@ -28,7 +28,8 @@ EXPORTED = (
     "tq_scores_workspace",
     "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
     "tq_key_record_bytes", "tq_val_record_bytes", "tq_scores_noalloc", "tq_scores_noalloc_capacity",
-    "tq_hadamard_matrix",
+    "tq_hadamard_matrix", "tq_build_polar_codebook", "tq_polar_record_words", "tq_polar_encode",
+    "tq_polar_decode", "tq_polar_scores",
 )
 # measurement and testing entry points (include/tq_testing.h)
 EXPORTED_TESTING = ("tq_testing_stream", "tq_testing_scores_wait")
@@ -50,6 +51,12 @@ class tq_params(ctypes.Structure):
                 ("pi", ctypes.c_void_p), ("eps", ctypes.c_void_p), ("s", ctypes.c_void_p),
                 ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p),
                 ("n_sets", ctypes.c_int), ("set_div", ctypes.c_int)]
+
+
+class tq_polar_params(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("rot", ctypes.c_int), ("bits1", ctypes.c_int), ("bits", ctypes.c_int),
+                ("m", ctypes.c_int), ("pi", ctypes.c_void_p), ("eps", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("centroids", ctypes.c_void_p), ("boundaries", ctypes.c_void_p)]
 
 
 class tq_cache(ctypes.Structure):
@@ -104,6 +111,13 @@ def lib():
         L.tq_key_record_bytes.argtypes = [P]
         L.tq_val_record_bytes.restype = sz
         L.tq_val_record_bytes.argtypes = [P]
+        PP = ctypes.POINTER(tq_polar_params)
+        L.tq_build_polar_codebook.argtypes = [ci, ci, vp, vp]
+        L.tq_polar_record_words.restype = sz
+        L.tq_polar_record_words.argtypes = [PP]
+        L.tq_polar_encode.argtypes = [PP, vp, ci, i64, i64, tq_cache, vp, vp]
+        L.tq_polar_decode.argtypes = [PP, tq_cache, i64, vp, i64, vp]
+        L.tq_polar_scores.argtypes = [PP, vp, ci, ci, tq_cache, vp, i64, vp, vp]
         L.tq_testing_scores_wait.restype = ci
         L.tq_testing_scores_wait.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp, sz, ci, vp]
         L.tq_testing_stream.restype = ci
@@ -111,7 +125,8 @@ def lib():
         for name in EXPORTED:
             if name not in ("tq_status_string", "tq_last_error", "tq_scores_workspace", "tq_key_record_words",
                             "tq_attend_workspace", "tq_encode_workspace", "tq_scores_topk_workspace",
-                            "tq_key_record_bytes", "tq_val_record_bytes", "tq_scores_noalloc_capacity"):
+                            "tq_key_record_bytes", "tq_val_record_bytes", "tq_scores_noalloc_capacity",
+                            "tq_polar_record_words"):
                 getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -137,6 +152,15 @@ def build_codebook(d: int, bits: int):
     c = np.zeros(2 ** bits, np.float64)
     b = np.zeros(2 ** bits - 1, np.float64)
     _check(lib().tq_build_codebook(int(d), int(bits), c.ctypes.data, b.ctypes.data))
+    return c, b
+
+
+def build_polar_codebook(level: int, bits: int):
+    """(centroids [2^bits], boundaries [2^bits - 1]) float64 of a level's angle
+    (see tq_build_polar_codebook)."""
+    c = np.zeros(2 ** bits, np.float64)
+    b = np.zeros(2 ** bits - 1, np.float64)
+    _check(lib().tq_build_polar_codebook(int(level), int(bits), c.ctypes.data, b.ctypes.data))
     return c, b
 
 
@@ -386,3 +410,71 @@ def testing_scores_wait(kp: Params, q, segs: int, group: int, keys: Cache, T: in
     each segment's query pack (0: the build-it-yourself path)."""
     _check(lib().tq_testing_scores_wait(kp.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),
                                         _ptr(ws), ws.numel() * ws.element_size(), int(wait_us), _stream(stream)))
+
+
+# ---- PolarQuant as stage 1 (tq_polar_*) ----
+
+@dataclass
+class PolarParams:
+    """Owns what a tq_polar_params points to.  centroids / boundaries are the
+    host float32 arrays of every level concatenated (level 1, then 2 .. L)."""
+    d: int
+    rot: int
+    bits1: int
+    bits: int
+    centroids: np.ndarray
+    boundaries: np.ndarray
+    pi: Optional[object] = None
+    eps: Optional[object] = None
+    s: Optional[object] = None
+    m: int = 0
+    _c: tq_polar_params = field(default=None, repr=False)
+
+    def __post_init__(self):
+        self.centroids = np.ascontiguousarray(self.centroids, np.float32)
+        self.boundaries = np.ascontiguousarray(self.boundaries, np.float32)
+        self._c = tq_polar_params(self.d, self.rot, self.bits1, self.bits, self.m,
+                                  None if self.pi is None else self.pi.data_ptr(),
+                                  None if self.eps is None else self.eps.data_ptr(),
+                                  None if self.s is None else self.s.data_ptr(),
+                                  self.centroids.ctypes.data, self.boundaries.ctypes.data)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def polar_codebooks(d: int, bits1: int, bits: int):
+    """Concatenated float64 (centroids, boundaries) of levels 1 .. log2(d) from tq_build_polar_codebook."""
+    L = int(d).bit_length() - 1
+    books = [build_polar_codebook(1, bits1)] + [build_polar_codebook(l, bits) for l in range(2, L + 1)]
+    return np.concatenate([b[0] for b in books]), np.concatenate([b[1] for b in books])
+
+
+def polar_record_words(p: PolarParams) -> int:
+    w = int(lib().tq_polar_record_words(p.c))
+    if w == 0:
+        raise TQError(TQ_ERR_INVALID_ARG, "invalid polar parameters")
+    return w
+
+
+def alloc_polar_cache(p: PolarParams, records: int, seg_stride: int = 0, device="cuda"):
+    """Polar records: words int32 [records, tq_polar_record_words], scalars float16 [records, 1 or 2]."""
+    import torch
+    return Cache(torch.zeros((records, polar_record_words(p)), dtype=torch.int32, device=device),
+                 torch.zeros((records, 2 if p.m else 1), dtype=torch.float16, device=device), seg_stride)
+
+
+def polar_encode(p: PolarParams, x, out: Cache, slot=None, stream=None):
+    _check(lib().tq_polar_encode(p.c, _ptr(x), _dtype_code(x), x.shape[0], x.stride(0), out.c, _ptr(slot),
+                                 _stream(stream)))
+
+
+def polar_decode(p: PolarParams, cache: Cache, n: int, out, stream=None):
+    """x~ of records 0 .. n-1 into out (float32 [n, >= d], row stride out.stride(0))."""
+    _check(lib().tq_polar_decode(p.c, cache.c, int(n), _ptr(out), out.stride(0), _stream(stream)))
+
+
+def polar_scores(p: PolarParams, q, segs: int, group: int, keys: Cache, T: int, out, length=None, stream=None):
+    _check(lib().tq_polar_scores(p.c, _ptr(q), segs, group, keys.c, _ptr(length), int(T), _ptr(out),
+                                 _stream(stream)))

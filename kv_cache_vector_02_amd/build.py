@@ -20,6 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtq.so")
 
 SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_encode2k.hip", "tq_decode.hip", "tq_retrieval.hip",
+           "tq_polar.hip",
            "tq_testing.hip"]
 
 ARCH = "gfx950"

@@ -154,6 +154,71 @@ tq_status encode(const tq_params* p, bool prod, const void* x, int dtype, int64_
               "(got %s, rot %d, d %d, d_rot %d)", prod ? "prod" : "mse", p->rot, p->d, p->d_rot);
 }
 
+// PolarQuant parameter block: checks, then the codebook tables in float64
+// rounded once to float32.
+tq_status polar_params(const tq_polar_params* p, tq::PolarArgs* a) {
+  std::memset(a, 0, sizeof(*a));
+  if (!p) return fail(TQ_ERR_INVALID_ARG, "params is NULL");
+  if (p->d != 128) return fail(TQ_ERR_UNSUPPORTED, "polar records support d = 128 (got %d)", p->d);
+  if (p->rot == TQ_ROT_DENSE) {
+    if (!p->pi || !aligned(p->pi, 16)) return fail(TQ_ERR_INVALID_ARG, "dense rotation needs a 16-byte aligned pi");
+  } else if (p->rot == TQ_ROT_HADAMARD) {
+    if (!p->eps || !aligned(p->eps, 16)) return fail(TQ_ERR_INVALID_ARG, "hadamard rotation needs a 16-byte aligned eps");
+  } else if (p->rot == TQ_ROT_HADAMARD2) {
+    return fail(TQ_ERR_UNSUPPORTED, "two Hadamard rounds: pass tq_hadamard_matrix's matrix as a dense rotation");
+  } else {
+    return fail(TQ_ERR_INVALID_ARG, "rot must be TQ_ROT_DENSE or TQ_ROT_HADAMARD");
+  }
+  if (p->bits1 < 1 || p->bits1 > 4 || p->bits < 1 || p->bits > 4)
+    return fail(TQ_ERR_INVALID_ARG, "bits1 and bits must be in [1, 4] (got %d, %d)", p->bits1, p->bits);
+  if (p->m != 0 && p->m != p->d) return fail(TQ_ERR_INVALID_ARG, "m must be 0 or d (got %d)", p->m);
+  if (p->m && (!p->s || !aligned(p->s, 16))) return fail(TQ_ERR_INVALID_ARG, "m > 0 needs a 16-byte aligned s");
+  if (!p->centroids || !p->boundaries) return fail(TQ_ERR_INVALID_ARG, "codebook centroids/boundaries are NULL");
+  const int L = 7;
+  int co = 0, bo = 0;   // offsets of the current level in the host arrays
+  for (int l = 1; l <= L; ++l) {
+    const int K = 1 << (l == 1 ? p->bits1 : p->bits);
+    const double lo = l == 1 ? -M_PI : 0.0, hi = l == 1 ? M_PI : M_PI / 2;
+    for (int i = 0; i < K; ++i)
+      if (!std::isfinite(p->centroids[co + i]))
+        return fail(TQ_ERR_INVALID_ARG, "level %d centroid %d is not finite", l, i);
+    for (int i = 0; i + 1 < K; ++i) {
+      const float b = p->boundaries[bo + i];
+      if (!(p->centroids[co + i] < b && b < p->centroids[co + i + 1]) || !((double)b > lo && (double)b < hi))
+        return fail(TQ_ERR_INVALID_ARG, "level %d boundary %d must lie between its centroids and inside (%g, %g)",
+                    l, i, lo, hi);
+    }
+    for (int i = 0; i < K; ++i) {
+      const double c = p->centroids[co + i];
+      float* dst = l == 1 ? a->book.c1[i] : a->book.cu[l - 2][i];
+      dst[0] = (float)std::cos(c);
+      dst[1] = (float)std::sin(c);
+    }
+    for (int i = 0; i + 1 < K; ++i) {
+      const double b = p->boundaries[bo + i];
+      if (l == 1) {
+        a->book.b1[i] = (float)b;
+      } else {
+        const double cb = std::cos(b), sb = std::sin(b);
+        a->book.bc[l - 2][i] = (float)(cb * cb);
+        a->book.bs[l - 2][i] = (float)(sb * sb);
+      }
+    }
+    co += K;
+    bo += K - 1;
+  }
+  a->pi = p->pi;
+  a->eps = p->eps;
+  a->s = p->m ? p->s : nullptr;
+  a->had = p->rot == TQ_ROT_HADAMARD;
+  a->b1 = p->bits1;
+  a->b = p->bits;
+  a->qjl = p->m ? 1 : 0;
+  return TQ_OK;
+}
+
+int polar_words(const tq_polar_params* p) { return 2 * p->bits1 + 2 * p->bits + p->m / 32; }
+
 }  // namespace
 
 extern "C" {
@@ -530,6 +595,102 @@ tq_status tq_scores_topk(const tq_params* kp, const float* q, int nq, tq_cache k
   L.val = val;
   L.ws = ws;
   return hip_status(tq::launch_topk2k(L, (hipStream_t)stream), "top-k launch");
+}
+
+tq_status tq_build_polar_codebook(int level, int bits, double* centroids, double* boundaries) {
+  if (level < 1 || level > 16) return fail(TQ_ERR_INVALID_ARG, "level must be in [1, 16]");
+  if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "bits must be in [1, 4]");
+  if (!centroids || !boundaries) return fail(TQ_ERR_INVALID_ARG, "output arrays are NULL");
+  return tq::build_polar_codebook(level, bits, centroids, boundaries);
+}
+
+size_t tq_polar_record_words(const tq_polar_params* p) {
+  tq::PolarArgs a;
+  if (polar_params(p, &a) != TQ_OK) return 0;
+  return (size_t)polar_words(p);
+}
+
+tq_status tq_polar_encode(const tq_polar_params* p, const void* x, int dtype, int64_t n, int64_t ld_x,
+                          tq_cache out, const int64_t* slot, void* stream) {
+  tq::PolarArgs a;
+  tq_status st = polar_params(p, &a);
+  if (st != TQ_OK) return st;
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n must be >= 0");
+  if (dtype != TQ_F32 && dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "dtype must be TQ_F32 or TQ_F16");
+  if (ld_x < p->d) return fail(TQ_ERR_INVALID_ARG, "ld_x must be >= d");
+  const size_t esz = dtype == TQ_F16 ? 2 : 4;
+  if (n == 0) return TQ_OK;
+  if (!x || !out.planes || !out.scalars) return fail(TQ_ERR_INVALID_ARG, "x and the cache arrays must be non-NULL");
+  if (out.records < 1) return fail(TQ_ERR_INVALID_ARG, "out.records (the cache's capacity) must be >= 1");
+  if (!aligned(x, 16) || (ld_x * esz) % 16)
+    return fail(TQ_ERR_INVALID_ARG, "x must be 16-byte aligned with rows a multiple of 16 bytes");
+  if (!aligned(out.planes, 8) || !aligned(out.scalars, 4))
+    return fail(TQ_ERR_INVALID_ARG, "cache planes must be 8-byte and scalars 4-byte aligned");
+  if (slot && !aligned(slot, 8)) return fail(TQ_ERR_INVALID_ARG, "slot must be 8-byte aligned");
+  a.x = x;
+  a.f16_in = dtype == TQ_F16;
+  a.n = n;
+  a.ld_x = ld_x;
+  a.slot = slot;
+  a.planes = (uint32_t*)out.planes;
+  a.scalars = (uint16_t*)out.scalars;
+  a.records = out.records;
+  return hip_status(tq::launch_polar_encode128(a, (hipStream_t)stream), "polar encode launch");
+}
+
+tq_status tq_polar_decode(const tq_polar_params* p, tq_cache in, int64_t n, float* out, int64_t ld_out,
+                          void* stream) {
+  tq::PolarArgs a;
+  tq_status st = polar_params(p, &a);
+  if (st != TQ_OK) return st;
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n must be >= 0");
+  if (ld_out < p->d) return fail(TQ_ERR_INVALID_ARG, "ld_out must be >= d");
+  if (n == 0) return TQ_OK;
+  if (!in.planes || !in.scalars || !out) return fail(TQ_ERR_INVALID_ARG, "the cache arrays and out must be non-NULL");
+  if (n > in.records) return fail(TQ_ERR_INVALID_ARG, "n (%lld) exceeds in.records (%lld)", (long long)n,
+                                  (long long)in.records);
+  if (!aligned(in.planes, 4) || !aligned(in.scalars, 2) || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (planes and out 4 B, scalars 2 B)");
+  a.planes = (uint32_t*)in.planes;
+  a.scalars = (uint16_t*)in.scalars;
+  a.records = in.records;
+  a.n = n;
+  a.out = out;
+  a.ld_out = ld_out;
+  return hip_status(tq::launch_polar_decode128(a, (hipStream_t)stream), "polar decode launch");
+}
+
+tq_status tq_polar_scores(const tq_polar_params* p, const float* q, int segs, int group, tq_cache keys,
+                          const int32_t* len, int64_t T, float* scores, void* stream) {
+  tq::PolarArgs a;
+  tq_status st = polar_params(p, &a);
+  if (st != TQ_OK) return st;
+  if (segs < 0 || group < 1 || T < 0) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
+  if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "polar scores support up to 16 query heads per segment");
+  if (segs == 0 || T == 0) return TQ_OK;
+  if (!q || !keys.planes || !keys.scalars || !scores)
+    return fail(TQ_ERR_INVALID_ARG, "q, keys and scores must be non-NULL");
+  if (!aligned(q, 16) || !aligned(keys.planes, 8) || !aligned(keys.scalars, 4) || !aligned(scores, 4) ||
+      (len && !aligned(len, 4)))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q 16 B, planes 8 B, scalars, scores and len 4 B)");
+  if (keys.seg_stride < T && segs > 1) return fail(TQ_ERR_INVALID_ARG, "keys.seg_stride must be >= T");
+  const int64_t stride = segs == 1 && keys.seg_stride < T ? T : keys.seg_stride;
+  if ((int64_t)(segs - 1) * stride + T > keys.records)
+    return fail(TQ_ERR_INVALID_ARG, "the keys read (%lld records) exceed keys.records (%lld)",
+                (long long)((int64_t)(segs - 1) * stride + T), (long long)keys.records);
+  if (T >= (1ll << 31) || (int64_t)segs * group * T >= (1ll << 40))
+    return fail(TQ_ERR_UNSUPPORTED, "T or the score array is too large");
+  a.q = q;
+  a.segs = segs;
+  a.group = group;
+  a.planes = (uint32_t*)keys.planes;
+  a.scalars = (uint16_t*)keys.scalars;
+  a.records = keys.records;
+  a.seg_stride = stride;
+  a.len = len;
+  a.T = T;
+  a.scores = scores;
+  return hip_status(tq::launch_polar_scores128(a, (hipStream_t)stream), "polar scores launch");
 }
 
 }  // extern "C"

@@ -124,20 +124,13 @@ struct SphereHalf : Half {
   }
 };
 
-}  // namespace
-
-tq_status build_codebook(int d, int bits, double* centroids, double* boundaries) {
-  const int K = 1 << bits;
-  const int H = K / 2;
-  const double sigma = d == 0 ? 1.0 : 1.0 / std::sqrt((double)d);
-  const double top = d == 0 ? INFINITY : 1.0;
-  GaussHalf gh;
-  SphereHalf* sh = d == 0 ? nullptr : new SphereHalf(d);
-  const Half& f = d == 0 ? (const Half&)gh : (const Half&)*sh;
-
-  // upper-half centroids, spread over [0, 3 sigma] to start
+// Lloyd-Max on the upper half line of an even density: H centroids in
+// (0, top), the first cell starting at 0 (the middle boundary of the full
+// codebook), iterated until the largest move is below tol * sigma or
+// rounding noise dominates.
+std::vector<double> lloyd_half(const Half& f, int H, double sigma, double top) {
   std::vector<double> c(H), cn(H), e(H + 1);
-  for (int i = 0; i < H; ++i) c[i] = std::fmin(sigma * 3.0 * (i + 0.5) / H, 0.999);
+  for (int i = 0; i < H; ++i) c[i] = std::fmin(sigma * 3.0 * (i + 0.5) / H, 0.999 * top);
   const double tol = 1e-13;
   double best_move = INFINITY;
   int since_best = 0;
@@ -161,6 +154,90 @@ tq_status build_codebook(int d, int bits, double* centroids, double* boundaries)
       break;
     }
   }
+  return c;
+}
+
+// The law of a level-l angle psi of the recursive polar transform, in
+// t = 2 psi - pi/2 on [-pi/2, pi/2]: with a = 2^(l-2), sin^2 psi ~ Beta(a, a)
+// gives the density of psi proportional to sin^(2a-1)(2 psi), i.e. cos^k(t)
+// with k = 2a - 1 (even in t).  Integrals over the upper half in t, unnormalised
+// (only the cells' conditional means are needed), on cumulative 16-point
+// Gauss-Legendre panels.
+struct AngleHalf : Half {
+  double k, h, tmax;
+  std::vector<double> cum_m, cum_x;
+
+  explicit AngleHalf(double k_) : k(k_) {
+    const double sigma = 1.0 / std::sqrt(k + 1.0);
+    h = std::fmin(sigma, 0.25) / 8.0;
+    tmax = k > 0 ? std::fmin(M_PI / 2, std::acos(std::exp(-700.0 / k))) : M_PI / 2;
+    int K = (int)std::ceil(tmax / h);
+    h = tmax / K;
+    cum_m.assign(K + 1, 0.0);
+    cum_x.assign(K + 1, 0.0);
+    for (int i = 0; i < K; ++i) {
+      double m, x;
+      panel(i * h, (i + 1) * h, &m, &x);
+      cum_m[i + 1] = cum_m[i] + m;
+      cum_x[i + 1] = cum_x[i] + x;
+    }
+  }
+  double w(double t) const {
+    double c = std::cos(t);
+    return c <= 0 ? 0.0 : std::exp(k * std::log(c));
+  }
+  void panel(double a, double b, double* m, double* x) const {
+    double mid = 0.5 * (a + b), half = 0.5 * (b - a);
+    double sm = 0, sx = 0;
+    for (int i = 0; i < 8; ++i) {
+      for (int sgn = -1; sgn <= 1; sgn += 2) {
+        double t = mid + sgn * half * kGLx[i];
+        double v = w(t);
+        sm += kGLw[i] * v;
+        sx += kGLw[i] * v * t;
+      }
+    }
+    *m = sm * half;
+    *x = sx * half;
+  }
+  void cum(double t, double* m, double* x) const {
+    if (t >= tmax) {
+      *m = cum_m.back();
+      *x = cum_x.back();
+      return;
+    }
+    int i = (int)std::floor(t / h);
+    if (i >= (int)cum_m.size() - 1) i = (int)cum_m.size() - 2;
+    double pm = 0, px = 0;
+    if (t > i * h) panel(i * h, t, &pm, &px);
+    *m = cum_m[i] + pm;
+    *x = cum_x[i] + px;
+  }
+  double mass(double a, double b) const override {
+    double ma, xa, mb, xb;
+    cum(a, &ma, &xa);
+    cum(b, &mb, &xb);
+    return mb - ma;
+  }
+  double moment(double a, double b) const override {
+    double ma, xa, mb, xb;
+    cum(a, &ma, &xa);
+    cum(b, &mb, &xb);
+    return xb - xa;
+  }
+};
+
+}  // namespace
+
+tq_status build_codebook(int d, int bits, double* centroids, double* boundaries) {
+  const int K = 1 << bits;
+  const int H = K / 2;
+  const double sigma = d == 0 ? 1.0 : 1.0 / std::sqrt((double)d);
+  const double top = d == 0 ? INFINITY : 1.0;
+  GaussHalf gh;
+  SphereHalf* sh = d == 0 ? nullptr : new SphereHalf(d);
+  const Half& f = d == 0 ? (const Half&)gh : (const Half&)*sh;
+  std::vector<double> c = lloyd_half(f, H, sigma, top);
   delete sh;
   for (int i = 0; i < H; ++i) {
     centroids[H + i] = c[i];
@@ -171,6 +248,36 @@ tq_status build_codebook(int d, int bits, double* centroids, double* boundaries)
     double b = 0.5 * (c[i - 1] + c[i]);
     boundaries[H - 1 + i] = b;
     boundaries[H - 1 - i] = -b;
+  }
+  return TQ_OK;
+}
+
+// Level 1: the angle is uniform on (-pi, pi], whose Lloyd-Max quantizer is
+// the uniform grid (cells of width 2 pi / K from -pi, centroids at their
+// middles).  Levels >= 2: the law above, solved in t and mapped back with
+// psi = (t + pi/2) / 2; the codebook is symmetric about pi/4.
+tq_status build_polar_codebook(int level, int bits, double* centroids, double* boundaries) {
+  const int K = 1 << bits;
+  if (level == 1) {
+    const double w = 2 * M_PI / K;
+    for (int i = 0; i < K; ++i) centroids[i] = -M_PI + (i + 0.5) * w;
+    for (int i = 1; i < K; ++i) boundaries[i - 1] = -M_PI + i * w;
+    return TQ_OK;
+  }
+  const int H = K / 2;
+  const double k = std::ldexp(1.0, level - 1) - 1.0;
+  AngleHalf f(k);
+  std::vector<double> c = lloyd_half(f, H, 1.0 / std::sqrt(k + 1.0), M_PI / 2);
+  auto psi = [](double t) { return 0.5 * (t + M_PI / 2); };
+  for (int i = 0; i < H; ++i) {
+    centroids[H + i] = psi(c[i]);
+    centroids[H - 1 - i] = psi(-c[i]);
+  }
+  boundaries[H - 1] = M_PI / 4;
+  for (int i = 1; i < H; ++i) {
+    double b = 0.5 * (c[i - 1] + c[i]);
+    boundaries[H - 1 + i] = psi(b);
+    boundaries[H - 1 - i] = psi(-b);
   }
   return TQ_OK;
 }

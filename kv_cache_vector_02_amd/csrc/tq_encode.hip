@@ -688,6 +688,330 @@ hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// PolarQuant as stage 1 at d = 128 (FastVQ README, "PolarQuant Algorithm" in
+// its recursive form; "TurboQuant Combination" for the QJL stage).
+//
+// GEMM1 is the one above, so lane (v, h) holds coordinates 64 h + i of vector
+// v, i = 16 mt + r in register r of row tile mt.  The transform therefore runs
+// inside the lane up to level 6 (its 64 coordinates), and level 7 combines the
+// lane halves.  Level-1 angles come from atan2 of the pair; an angle above
+// level 1 is coded without trigonometry, psi >= beta <=> P_b cos^2 beta >
+// P_a sin^2 beta with P the squared lengths of its two children (strict, so two
+// empty children give code 0, as atan2(0, 0) = 0 does).  Every decision is
+// scale-free, so it runs on the raw accumulators.  The reconstruction walks
+// back down with the centroid (cos, sin) pairs from the LDS, the residual
+// y - y~ feeds GEMM2 exactly as the prod residual does.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// OR code c (W bits) into a little-endian word stream at bit pos (constant
+// after unrolling), spilling into the next word when it straddles.
+template <int W, int N>
+__device__ __forceinline__ void put_code(uint32_t (&w)[N], int pos, uint32_t c) {
+  w[pos >> 5] |= c << (pos & 31);
+  if ((pos & 31) + W > 32) w[(pos >> 5) + 1] |= c >> (32 - (pos & 31));
+}
+template <int W, int N>
+__device__ __forceinline__ uint32_t get_code(const uint32_t (&w)[N], int pos) {
+  uint32_t c = w[pos >> 5] >> (pos & 31);
+  if ((pos & 31) + W > 32) c |= w[(pos >> 5) + 1] << (32 - (pos & 31));
+  return c & ((1u << W) - 1);
+}
+
+// Code the NP angles of one upper level from the 2 NP squared lengths below
+// them (children 2j, 2j+1 of angle j), into nibble slot OFF + j of uw, and
+// form the squared lengths of this level.
+template <int NP, int LI, int OFF, int KU>
+__device__ __forceinline__ void polar_level(const float (&pin)[2 * NP], float (&pout)[NP], uint32_t (&uw)[4],
+                                            const PolarBook& bk) {
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const float pa = pin[2 * j], pb = pin[2 * j + 1];
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < KU - 1; ++k) c += pb * bk.bc[LI][k] > pa * bk.bs[LI][k] ? 1u : 0u;
+    uw[(OFF + j) >> 3] |= c << (4 * ((OFF + j) & 7));
+    pout[j] = pa + pb;
+  }
+}
+
+// Split NP lengths of one level into the 2 NP lengths below with the
+// centroid pairs of the level's codes (nibble slots OFF + j of uw).
+template <int NP, int LI, int OFF>
+__device__ __forceinline__ void polar_split(const float (&rin)[NP], float (&rout)[2 * NP], const uint32_t (&uw)[4],
+                                            const float2* tabu) {
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const uint32_t c = (uw[(OFF + j) >> 3] >> (4 * ((OFF + j) & 7))) & 15u;
+    const float2 t = tabu[16 * LI + c];
+    rout[2 * j] = rin[j] * t.x;
+    rout[2 * j + 1] = rin[j] * t.y;
+  }
+}
+
+// Nibble slots of a lane's upper codes (levels 2..6) and their offsets in the
+// record's upper stream (level l starts at 64 - 128 / 2^(l-1); the lane half h
+// holds the second half of each level's positions when h = 1).
+constexpr int PL_LOCAL[5] = {0, 16, 24, 28, 30};
+constexpr int PL_STREAM[5] = {0, 32, 48, 56, 60};
+constexpr int PL_HALF[5] = {16, 8, 4, 2, 1};
+
+template <int B1, int B, bool QJL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void polar_encode128(PolarArgs a) {
+  constexpr int K1 = 1 << B1, KU = 1 << B;
+  constexpr int P = 2 * B1 + 2 * B + (QJL ? 4 : 0);     // record words
+  extern __shared__ half8 lds[];
+  half8* fpi = lds;
+  half8* fs = lds + FRAGS;
+  float2* tab1 = reinterpret_cast<float2*>(lds + (QJL ? 2 : 1) * FRAGS);   // [16] level 1
+  float2* tabu = tab1 + 16;                                                 // [6][16] levels 2..7
+  build_frags<64 * WAVES>(fpi, a.pi, PI_SCALE, a.had ? a.eps : nullptr);
+  if (QJL) build_frags<64 * WAVES>(fs, a.s, 1.f);
+  polar_tables_to_lds(a.book, tab1);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int v = lane & 31;
+  const int h = lane >> 5;
+  const float hs = a.had ? HAD_SCALE : 1.f;
+  const int64_t ntiles = (a.n + 31) / 32;
+  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += (int64_t)gridDim.x * WAVES) {
+    asm volatile("" ::: "memory");   // keep the fragment reads inside the loop
+    const int64_t vec = tile * 32 + v;
+    const bool valid = vec < a.n;
+    // ---- load, norm, GEMM1 operands (fp32 inputs normalised, in hi + lo) ----
+    half8 xh[8], xl[8];
+    float nrm, ysc, inv;
+    if (a.f16_in) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.x) +
+                                                        (valid ? vec : 0) * a.ld_x + 64 * h);
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const half8 hv = __builtin_bit_cast(half8, valid ? src[ks] : make_uint4(0, 0, 0, 0));
+        xh[ks] = hv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s4[e & 3] += (float)hv[e] * (float)hv[e];
+      }
+      float s2 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      s2 += shfl_xor_f(s2, 32);
+      nrm = sqrtf(s2);
+      ysc = nrm > 0.f ? hs / (nrm * PI_SCALE) : 1.f;
+      inv = nrm > 0.f ? (nrm * PI_SCALE) / hs : 1.f;
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) +
+                                                          (valid ? vec : 0) * a.ld_x + 64 * h);
+      float xv[64];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 w = valid ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[4 * i] = w.x; xv[4 * i + 1] = w.y; xv[4 * i + 2] = w.z; xv[4 * i + 3] = w.w;
+      }
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 64; ++i) s4[i & 3] += xv[i] * xv[i];
+      float s2 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      s2 += shfl_xor_f(s2, 32);
+      nrm = sqrtf(s2);
+      const float un = nrm > 0.f ? U_SCALE / nrm : 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          _Float16 hi, lo;
+          split_f16(xv[8 * ks + e] * un, hi, lo);
+          xh[ks][e] = hi;
+          xl[ks][e] = lo;
+        }
+      }
+      ysc = hs / (U_SCALE * PI_SCALE);
+      inv = (U_SCALE * PI_SCALE) / hs;
+    }
+    // ---- GEMM1: all four row tiles (the transform needs the lane's 64 coordinates) ----
+    f32x16 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const half8 ahi = fpi[frag_index(mt, ks, 0, lane)];
+        const half8 alo = fpi[frag_index(mt, ks, 1, lane)];
+        acc[mt] = mfma32x32x16(ahi, xh[ks], acc[mt]);
+        acc[mt] = mfma32x32x16(alo, xh[ks], acc[mt]);     // zero for the +-16 Hadamard entries
+        if (!a.f16_in) acc[mt] = mfma32x32x16(ahi, xl[ks], acc[mt]);
+      }
+    }
+    auto yv = [&](int i) { return acc[i >> 4][i & 15]; };   // coordinate 64 h + i, in accumulator units
+
+    // ---- level 1: 32 pairs; codes straight into the lane's B1 stream words ----
+    uint32_t w1[B1];
+#pragma unroll
+    for (int i = 0; i < B1; ++i) w1[i] = 0u;
+    float p1[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float y0 = yv(2 * j), y1 = yv(2 * j + 1);
+      const float psi = atan2f(y1, y0);
+      uint32_t c = 0;
+#pragma unroll
+      for (int k = 0; k < K1 - 1; ++k) c += psi >= a.book.b1[k] ? 1u : 0u;
+      put_code<B1>(w1, j * B1, c);
+      p1[j] = y0 * y0 + y1 * y1;
+    }
+    // ---- levels 2..6 in the lane, level 7 across the halves ----
+    uint32_t uw[4] = {0u, 0u, 0u, 0u};
+    float p2[16], p3[8], p4[4], p5[2], p6[1];
+    polar_level<16, 0, 0, KU>(p1, p2, uw, a.book);
+    polar_level<8, 1, 16, KU>(p2, p3, uw, a.book);
+    polar_level<4, 2, 24, KU>(p3, p4, uw, a.book);
+    polar_level<2, 3, 28, KU>(p4, p5, uw, a.book);
+    polar_level<1, 4, 30, KU>(p5, p6, uw, a.book);
+    const float po = shfl_xor_f(p6[0], 32);
+    const float pa = h ? po : p6[0], pb = h ? p6[0] : po;
+    uint32_t c7 = 0;
+#pragma unroll
+    for (int k = 0; k < KU - 1; ++k) c7 += pb * a.book.bc[5][k] > pa * a.book.bs[5][k] ? 1u : 0u;
+
+    // ---- reconstruction from the unit length down, residual fragments ----
+    const float2 t7 = tabu[16 * 5 + c7];
+    float r6[1] = {h ? t7.y : t7.x};
+    float r5[2], r4[4], r3[8], r2[16], r1[32];
+    polar_split<1, 4, 30>(r6, r5, uw, tabu);
+    polar_split<2, 3, 28>(r5, r4, uw, tabu);
+    polar_split<4, 2, 24>(r4, r3, uw, tabu);
+    polar_split<8, 1, 16>(r3, r2, uw, tabu);
+    polar_split<16, 0, 0>(r2, r1, uw, tabu);
+    float g2 = 0.f;
+    half8 rh[8], rl[8];
+    const float rsc = R_SCALE * ysc;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float2 t = tab1[get_code<B1>(w1, j * B1)];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * j + e;
+        const float d = yv(i) - r1[j] * (e ? t.y : t.x) * inv;    // (y - y~) / ysc
+        g2 += d * d;
+        if (QJL) {
+          _Float16 hi, lo;
+          split_f16(d * rsc, hi, lo);
+          rh[i >> 3][i & 7] = hi;
+          rl[i >> 3][i & 7] = lo;
+        }
+      }
+    }
+    // ---- GEMM2: QJL signs of the residual; lane half h collects words 2h, 2h + 1 ----
+    uint32_t sw[2] = {0u, 0u};
+    if (QJL) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        f32x16 acc2 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const half8 shi = fs[frag_index(it, ks, 0, lane)];
+          const half8 slo = fs[frag_index(it, ks, 1, lane)];
+          acc2 = mfma32x32x16(shi, rh[ks], acc2);
+          acc2 = mfma32x32x16(slo, rh[ks], acc2);
+          acc2 = mfma32x32x16(shi, rl[ks], acc2);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sw[it >> 1] = shift_in(sw[it >> 1], ge_mask(acc2[r], 0.f));
+      }
+    }
+    // ---- store: the lane half's level-1 words, half 0 the upper stream and scalars ----
+    uint32_t ou[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ou[i] = shfl_xor_u(uw[i], 32);
+    const float gam = sqrtf(g2 + shfl_xor_f(g2, 32)) * ysc;
+    const int64_t rec = valid ? (a.slot ? a.slot[vec] : vec) : -1;
+    if ((uint64_t)rec < (uint64_t)a.records) {
+      uint32_t* dst = a.planes + rec * P;
+#pragma unroll
+      for (int i = 0; i < B1; ++i) dst[h * B1 + i] = w1[i];
+      if (QJL) {
+        dst[2 * B1 + 2 * B + 2 * h] = __builtin_bitreverse32(sw[0]);
+        dst[2 * B1 + 2 * B + 2 * h + 1] = __builtin_bitreverse32(sw[1]);
+      }
+      if (h == 0) {
+        uint32_t us[2 * B];
+#pragma unroll
+        for (int i = 0; i < 2 * B; ++i) us[i] = 0u;
+#pragma unroll
+        for (int li = 0; li < 5; ++li) {
+#pragma unroll
+          for (int src = 0; src < 2; ++src) {
+#pragma unroll
+            for (int j = 0; j < PL_HALF[li]; ++j) {
+              const int slot = PL_LOCAL[li] + j;
+              const uint32_t c = ((src ? ou : uw)[slot >> 3] >> (4 * (slot & 7))) & 15u;
+              put_code<B>(us, (PL_STREAM[li] + src * PL_HALF[li] + j) * B, c);
+            }
+          }
+        }
+        put_code<B>(us, 62 * B, c7);
+#pragma unroll
+        for (int i = 0; i < 2 * B; ++i) dst[2 * B1 + i] = us[i];
+        if (QJL)
+          reinterpret_cast<uint32_t*>(a.scalars)[rec] = (uint32_t)f16_bits(nrm) | ((uint32_t)f16_bits(gam) << 16);
+        else
+          a.scalars[rec] = f16_bits(nrm);
+      }
+    }
+  }
+}
+
+template <int B1, int B, bool QJL>
+hipError_t launch_polar3(const PolarArgs& a, hipStream_t stream) {
+  int dev = 0, cus = 256;
+  hipGetDevice(&dev);
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const size_t lds = (QJL ? 2 : 1) * FRAGS * sizeof(half8) + 16 * 7 * sizeof(float2);
+  const int64_t ntiles = (a.n + 31) / 32;
+  auto go = [&](auto kern, int waves) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int grid = (int)std::min<int64_t>((ntiles + waves - 1) / waves, (int64_t)cus);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, stream, a);
+    return hipGetLastError();
+  };
+  // eight-wave workgroups share the fragments; a small batch spreads one-wave
+  // workgroups over the compute units instead
+  if (ntiles < 2 * (int64_t)cus) return go(polar_encode128<B1, B, QJL, 1>, 1);
+  return go(polar_encode128<B1, B, QJL, 8>, 8);
+}
+
+template <int B1, int B>
+hipError_t launch_polar2(const PolarArgs& a, hipStream_t stream) {
+  return a.qjl ? launch_polar3<B1, B, true>(a, stream) : launch_polar3<B1, B, false>(a, stream);
+}
+
+template <int B1>
+hipError_t launch_polar1(const PolarArgs& a, hipStream_t stream) {
+  switch (a.b) {
+    case 1: return launch_polar2<B1, 1>(a, stream);
+    case 2: return launch_polar2<B1, 2>(a, stream);
+    case 3: return launch_polar2<B1, 3>(a, stream);
+    case 4: return launch_polar2<B1, 4>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_polar_encode128(const PolarArgs& a, hipStream_t stream) {
+  switch (a.b1) {
+    case 1: return launch_polar1<1>(a, stream);
+    case 2: return launch_polar1<2>(a, stream);
+    case 3: return launch_polar1<3>(a, stream);
+    case 4: return launch_polar1<4>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
 // The explicit R-round Hadamard matrix (tq_hadamard_matrix): one workgroup per
 // column j, the transform of e_j in the LDS, rounds of sign flip then an
 // in-place butterfly pass per index bit; the unscaled values are integers

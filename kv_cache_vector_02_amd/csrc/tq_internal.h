@@ -9,6 +9,7 @@
 namespace tq {
 
 tq_status build_codebook(int d, int bits, double* centroids, double* boundaries);
+tq_status build_polar_codebook(int level, int bits, double* centroids, double* boundaries);
 
 // Codebook by value: it travels in the kernel argument buffer (scalar
 // registers / constant cache), never in device memory.
@@ -131,5 +132,67 @@ struct AttendArgs {
 
 hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream);
 size_t attend128_workspace(int segs, int group, int64_t T);
+
+// PolarQuant at d = 128 (levels 1..7).  The codebook tables travel in the
+// kernel argument buffer, prepared on the host in float64 from the float32
+// codebook: level-1 boundaries (compared with atan2 of the pair), the cos^2
+// and sin^2 of the upper boundaries (compared with squared lengths, no
+// trigonometry), and the cos and sin of every centroid (the reconstruction).
+struct PolarBook {
+  float b1[15];            // level-1 boundaries (radians, ascending)
+  float c1[16][2];         // level-1 centroids: cos, sin
+  float bc[6][15];         // levels 2..7: cos^2 of the boundaries
+  float bs[6][15];         // levels 2..7: sin^2 of the boundaries
+  float cu[6][16][2];      // levels 2..7 centroids: cos, sin
+};
+
+struct PolarArgs {
+  // quantizer
+  const float* pi;         // dense rotation [128][128], or NULL
+  const float* eps;        // hadamard signs [128], or NULL
+  const float* s;          // QJL matrix [128][128] when qjl
+  int had, b1, b, qjl;
+  PolarBook book;
+  // records
+  uint32_t* planes;        // [records][words]
+  uint16_t* scalars;       // [records][qjl ? 2 : 1]
+  int64_t records;
+  // encode
+  const void* x;
+  int f16_in;
+  int64_t n, ld_x;
+  const int64_t* slot;
+  // decode
+  float* out;
+  int64_t ld_out;
+  // scores
+  const float* q;          // [segs*group][128]
+  int segs, group;
+  int64_t seg_stride;
+  const int32_t* len;
+  int64_t T;
+  float* scores;           // [segs*group][T]
+  int wps;                 // workgroups per segment
+  int64_t tpw;             // tokens per workgroup (a multiple of 256)
+};
+
+// Centroid (cos, sin) tables into the LDS: tab[0..16) level 1, tab[16 + 16 (l-2)
+// + k] level l.  Every entry is read from the argument buffer at a constant
+// offset (a run-time index into a kernel argument would copy the whole
+// argument block to scratch memory).
+__device__ __forceinline__ void polar_tables_to_lds(const PolarBook& bk, float2* tab) {
+#pragma unroll
+  for (int i = 0; i < 16 * 7; ++i) {
+    if ((int)threadIdx.x == i % (int)blockDim.x) {
+      const float* c = i < 16 ? bk.c1[i] : bk.cu[(i - 16) >> 4][(i - 16) & 15];
+      tab[i] = make_float2(c[0], c[1]);
+    }
+  }
+}
+
+hipError_t launch_polar_encode128(const PolarArgs& a, hipStream_t stream);
+hipError_t launch_polar_decode128(const PolarArgs& a, hipStream_t stream);
+hipError_t launch_polar_scores128(const PolarArgs& a, hipStream_t stream);
+size_t polar_scores128_lds(int b1, int qjl, int group);
 
 }  // namespace tq

@@ -250,3 +250,95 @@ def test_scores_wait_bound_must_be_nonnegative():
     st = L.tq_testing_scores_wait(pk_.c, ctypes.c_void_p(0x100000), 1, 8, keys, None, 64, ctypes.c_void_p(0x200000),
                                   ctypes.c_void_p(0x400000), 1 << 20, -1, None)
     assert st == tq.TQ_ERR_INVALID_ARG
+
+
+# ---- PolarQuant (tq_polar_*) ----
+
+from oracle import packing as pk  # noqa: E402
+from oracle import polar as pq  # noqa: E402
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("level", [1, 2, 3, 5, 7])
+def test_polar_codebook_matches_oracle(level, bits):
+    # the library solves Lloyd-Max in t = 2 psi - pi/2 on Gauss-Legendre panels;
+    # the oracle in psi with adaptive quadrature of the closed-form density
+    c, b = tq.build_polar_codebook(level, bits)
+    oc, ob = pq.angle_codebook(level, bits)
+    assert np.allclose(c, oc, atol=1e-9) and np.allclose(b, ob, atol=1e-9)
+    if level > 1:
+        assert np.allclose(c + c[::-1], np.pi / 2, atol=1e-15)   # symmetric about pi/4
+
+
+def test_polar_codebook_rejects_bad_arguments():
+    c, b = np.zeros(16), np.zeros(15)
+    L = tq.lib()
+    assert L.tq_build_polar_codebook(0, 2, c.ctypes.data, b.ctypes.data) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_build_polar_codebook(17, 2, c.ctypes.data, b.ctypes.data) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_build_polar_codebook(2, 5, c.ctypes.data, b.ctypes.data) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_build_polar_codebook(2, 2, None, b.ctypes.data) == tq.TQ_ERR_INVALID_ARG
+
+
+def _polar_params(bits1=3, bits=2, m=128, rot=tq.TQ_ROT_DENSE):
+    c, b = tq.polar_codebooks(128, bits1, bits)
+    p = tq.PolarParams(d=128, rot=rot, bits1=bits1, bits=bits, centroids=c, boundaries=b, m=m)
+    p._c.pi, p._c.eps, p._c.s = 0x10000, 0x30000, (0x20000 if m else None)
+    return p
+
+
+@pytest.mark.parametrize("bits1,bits,m", [(1, 1, 0), (3, 2, 128), (4, 4, 128), (2, 3, 0)])
+def test_polar_record_words(bits1, bits, m):
+    p = _polar_params(bits1, bits, m)
+    assert tq.lib().tq_polar_record_words(p.c) == pk.polar_record_words(128, bits1, bits, m) \
+        == 2 * bits1 + 2 * bits + m // 32
+
+
+def _polar_encode_raw(p, n=4, ld=128, x=0x1000, planes=0x2000, scalars=0x3000, records=1 << 20):
+    cache = tq.tq_cache(planes, scalars, 0, records)
+    return tq.lib().tq_polar_encode(p.c, ctypes.c_void_p(x), tq.TQ_F16, n, ld, cache, None, None)
+
+
+def test_polar_validation_without_launch():
+    # every case fails on the host before a launch (the pointers are fake)
+    L = tq.lib()
+    p = _polar_params()
+    p._c.m = 64
+    assert _polar_encode_raw(p) == tq.TQ_ERR_INVALID_ARG          # m neither 0 nor d
+    p._c.m = 128
+    p._c.s = None
+    assert _polar_encode_raw(p) == tq.TQ_ERR_INVALID_ARG          # QJL stage without S
+    p._c.s = 0x20000
+    p._c.bits1 = 5
+    assert _polar_encode_raw(p) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_polar_record_words(p.c) == 0
+    p._c.bits1 = 3
+    p._c.d = 64
+    assert _polar_encode_raw(p, ld=64) == tq.TQ_ERR_UNSUPPORTED   # only d = 128 has kernels
+    p._c.d = 128
+    p._c.rot = tq.TQ_ROT_HADAMARD2
+    assert _polar_encode_raw(p) == tq.TQ_ERR_UNSUPPORTED
+    p._c.rot = tq.TQ_ROT_DENSE
+    assert _polar_encode_raw(p, ld=100) == tq.TQ_ERR_INVALID_ARG
+    assert _polar_encode_raw(p, x=0x1004) == tq.TQ_ERR_INVALID_ARG
+    assert _polar_encode_raw(p, records=0) == tq.TQ_ERR_INVALID_ARG
+    assert _polar_encode_raw(p, n=0) == tq.TQ_OK                  # nothing to do, nothing launched
+    # a level-1 boundary outside (-pi, pi), an upper one outside (0, pi/2), disorder
+    for level, value in ((1, -3.2), (2, 1.6), (3, -0.1)):
+        c, b = tq.polar_codebooks(128, 3, 2)
+        off = 0 if level == 1 else 7 + 3 * (level - 2)
+        b = b.astype(np.float32)
+        b[off] = value
+        q = tq.PolarParams(d=128, rot=tq.TQ_ROT_DENSE, bits1=3, bits=2, centroids=c, boundaries=b, m=0)
+        q._c.pi = 0x10000
+        assert _polar_encode_raw(q) == tq.TQ_ERR_INVALID_ARG, level
+    # scores: reads past the capacity, too many heads, misaligned q
+    cache = tq.tq_cache(0x2000, 0x3000, 100, 250)
+    f = lambda segs, group, T, q=0x1000: L.tq_polar_scores(p.c, ctypes.c_void_p(q), segs, group, cache, None, T,
+                                                           ctypes.c_void_p(0x4000), None)
+    assert f(3, 4, 100) == tq.TQ_ERR_INVALID_ARG
+    assert f(2, 17, 100) == tq.TQ_ERR_UNSUPPORTED
+    assert f(2, 4, 100, q=0x1004) == tq.TQ_ERR_INVALID_ARG
+    assert f(0, 4, 100) == tq.TQ_OK and f(2, 4, 0) == tq.TQ_OK
+    # decode: more records than the cache holds
+    assert L.tq_polar_decode(p.c, tq.tq_cache(0x2000, 0x3000, 0, 10), 11, ctypes.c_void_p(0x4000), 128,
+                             None) == tq.TQ_ERR_INVALID_ARG
