@@ -148,6 +148,12 @@ def torch_copy_rate(torch, ev):
     return round(2 * (256 << 20) * 4 / (t * 1e-3) / 1e9, 1)
 
 
+def kv_tensor_keys():
+    """The Llama-shaped keys alone, on the host ([32 * 8 * 32768, 128] fp16)."""
+    from tq_inputs import kv_tensor
+    return kv_tensor(LL, LH, LT, D_, seed=LSEED).reshape(-1, D_)
+
+
 def llama_inputs(torch):
     """The Llama-shaped keys and values on the device ([32 * 8 * 32768, 128] fp16 each)."""
     from tq_inputs import kv_tensor
@@ -203,6 +209,53 @@ def llama_line(torch, tq, ev, kx, vx, bits, rot, with_attend=True):
                   "tq_attend_bytes": at_bytes})
         del o, wa
     del kc, vc, q
+    torch.cuda.empty_cache()
+    return r
+
+
+LDS_PEAK_TBPS = 128 * 256 * 2.4e9 / 1e12    # LDS bytes per clock per compute unit x CUs x clock
+
+
+def polar_line(torch, tq, ev, kx):
+    """PolarQuant stage 1 (tq_polar_*) on the Llama-shaped keys: the encode of
+    all 8.4 M keys and tq_polar_scores over the 256 segments (G = 4), for three
+    record forms.  The score pass is bound by its LDS table reads: per token
+    and head quad, 63 centroid pairs of 8 B, 64 pair-table rows of 16 B and,
+    with the QJL stage, 32 sign-nibble rows of 16 B; their rate is reported
+    beside the HBM rate."""
+    from tq_inputs import gaussian_matrix, gaussian_queries, haar_orthogonal
+    segs, N = LL * LH, LL * LH * LT
+    pi = torch.from_numpy(haar_orthogonal(D_, LSEED, 2)).cuda()
+    s = torch.from_numpy(gaussian_matrix(D_, D_, LSEED, 3)).cuda()
+    q = torch.from_numpy(gaussian_queries(segs * LG, D_, seed=LSEED)).cuda()
+    out = torch.empty((segs * LG, LT), dtype=torch.float32, device="cuda")
+    r = {"workload": "the llama-shaped keys (32 x 8 x 32768 x 128 fp16, dense rotation) as polar records: "
+                     "b1 bits per level-1 angle, b per angle above, with or without the QJL stage (m = 128); "
+                     "tq_polar_scores for 32 query heads per layer (G = 4)"}
+    for b1, b, m in ((4, 2, 128), (3, 2, 0), (4, 3, 128)):
+        c, bd = tq.polar_codebooks(D_, b1, b)
+        p = tq.PolarParams(d=D_, rot=tq.TQ_ROT_DENSE, bits1=b1, bits=b, centroids=c, boundaries=bd, pi=pi,
+                           s=s if m else None, m=m)
+        cache = tq.alloc_polar_cache(p, N, seg_stride=LT)
+        tq.polar_encode(p, kx, cache)
+        torch.cuda.synchronize()
+        timed = burst_timer(torch, ev, 4)
+        t_enc = timed(lambda i: tq.polar_encode(p, kx, cache))
+        timed = burst_timer(torch, ev, 8)
+        t_sc = timed(lambda i: tq.polar_scores(p, q, segs, LG, cache, LT, out))
+        rec = 4 * tq.polar_record_words(p) + (4 if m else 2)
+        hbm = N * rec + segs * LG * LT * 4 + segs * LG * D_ * 4
+        lds = N * (63 * 8 + 64 * 16 + (32 * 16 if m else 0))
+        r[f"b1_{b1}_b{b}" + ("_qjl" if m else "")] = {
+            "record_bytes": rec, "bits_per_coordinate": round(8 * rec / D_, 3),
+            "encode_ms": round(t_enc, 4), "encoded_vectors_per_s": round(N / (t_enc * 1e-3), 1),
+            "tq_polar_scores_ms": round(t_sc, 5), "hbm_GBps": round(hbm / (t_sc * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(hbm / (t_sc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "lds_read_TBps": round(lds / (t_sc * 1e-3) / 1e12, 2),
+            "frac_lds_peak": round(lds / (t_sc * 1e-3) / 1e12 / LDS_PEAK_TBPS, 4)}
+        del cache
+        torch.cuda.empty_cache()
+    del out, q
     torch.cuda.empty_cache()
     return r
 
@@ -497,7 +550,8 @@ def quality_report(torch, tq):
     each, temperature 1/sqrt(d)).  Keys prod (b-1 MSE bits + 1 QJL bit, m = d,
     and m = d / 2 as the page's examples use) and, for comparison at equal bits, MSE-only (b index bits), plain or with
     EDEN's unbiased per-vector scale (then on the values too); values MSE at b
-    bits."""
+    bits.  PolarQuant keys (b bits per angle, or b - 1 and the QJL stage) in
+    the fidelity and needle columns."""
     from kv_cache_vector_02_amd import quality
     from tq_inputs import (QUERIES, gaussian_matrix, gaussian_queries, haar_orthogonal, kv_tensor,
                            needle_haystacks, unit_gaussian)
@@ -544,6 +598,24 @@ def quality_report(torch, tq):
             rows.append({"keys": keys_kind, "bits": bits, "attention_cosine": round(r["mean_cosine"], 6),
                          "top1": round(r["top1_rate"], 3), "needle_found": int(found.sum()), "needle_trials": 20,
                          "output_cosine": round(float(cos.mean()), 6)})
+    # PolarQuant keys at the same budgets: b bits per angle (polar), or b - 1
+    # bits per angle and the QJL stage (polar_qjl); about b bits per coordinate
+    for keys_kind in ("polar", "polar_qjl"):
+        for bits in (2, 3, 4):
+            w = bits if keys_kind == "polar" else bits - 1
+
+            def pparams(seed):
+                c, b = tq.polar_codebooks(D_, w, w)
+                pi = torch.from_numpy(haar_orthogonal(D_, seed, 2)).cuda()
+                s = torch.from_numpy(gaussian_matrix(D_, D_, seed, 3)).cuda() if keys_kind == "polar_qjl" else None
+                return tq.PolarParams(d=D_, rot=tq.TQ_ROT_DENSE, bits1=w, bits=w, centroids=c, boundaries=b, pi=pi,
+                                      s=s, m=D_ if s is not None else 0)
+
+            r = quality.attention_fidelity(pparams(11), keys, qs)
+            found, _, _ = quality.needle(pparams(13), hay, hq)
+            rows.append({"keys": keys_kind, "bits": bits, "attention_cosine": round(r["mean_cosine"], 6),
+                         "top1": round(r["top1_rate"], 3), "needle_found": int(found.sum()), "needle_trials": 20,
+                         "output_cosine": None})
     torch.cuda.synchronize()
     return rows
 
@@ -679,6 +751,9 @@ def main():
     ap.add_argument("--skip-sweep", action="store_true", help="skip the b x rotation sweep of the Llama-shaped cache")
     ap.add_argument("--skip-retrieval", action="store_true", help="skip the 1M x 1536 top-10 retrieval line")
     ap.add_argument("--skip-batched", action="store_true", help="skip the batched-decode step line")
+    ap.add_argument("--skip-polar", action="store_true", help="skip the PolarQuant stage-1 line")
+    ap.add_argument("--polar-only", action="store_true",
+                    help="only the PolarQuant stage-1 line on the Llama-shaped keys (for its kernel profile)")
     ap.add_argument("--quality", action="store_true",
                     help="only print the compressed-cache quality table (fidelity, needle, attention output)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -696,6 +771,11 @@ def main():
     from tq_inputs import gaussian_queries
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.polar_only:
+        k = torch.from_numpy(kv_tensor_keys()).cuda()
+        print(json.dumps({"polar": polar_line(torch, tq, lambda: torch.cuda.Event(enable_timing=True), k)}),
+              flush=True)
         return
     if args.quality:
         torch.cuda.set_device(0)
@@ -841,6 +921,8 @@ def main():
                 for rot in ("dense", "hadamard"):
                     sweep[f"b{bits}_{rot}"] = llama_line(torch, tq, ev, kx, vx, bits, rot)
             result["llama_sweep"] = sweep
+        if not args.skip_polar:
+            result["polar"] = polar_line(torch, tq, ev, kx)
         del kx, vx
         torch.cuda.empty_cache()
         result["tiny"] = tiny_line(torch, tq, ev)

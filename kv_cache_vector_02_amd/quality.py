@@ -15,7 +15,8 @@ table (cosine of the attention distributions and top-1 agreement at 2, 3 and
 
 The compressed side runs in libtq (tq_encode_prod, or tq_encode_mse_keys for
 a key quantizer without a QJL matrix; tq_encode_mse for values; with eden,
-tq_encode_eden for MSE keys and values; tq_scores, tq_attend).  The exact side is float32 PyTorch on the same device (the
+tq_encode_eden for MSE keys and values; tq_scores, tq_attend; for polar key
+parameters, tq_polar_encode and tq_polar_scores, with no attention output).  The exact side is float32 PyTorch on the same device (the
 products, the softmax and the weighted sum), the yardstick the compressed
 results are measured against; none of it is on the hot path.  Argmax ties go
 to the lower key index.
@@ -37,9 +38,13 @@ def exact_scores(keys, queries):
     return queries.float() @ keys.float().t().contiguous()
 
 
-def encode_keys(kp: tq.Params, keys, seg_stride: int = 0, eden: bool = False) -> tq.Cache:
+def encode_keys(kp, keys, seg_stride: int = 0, eden: bool = False) -> tq.Cache:
     """Prod keys, or MSE-only keys when kp has no QJL matrix (with eden, scaled
-    by EDEN's unbiased n / <y, c[idx]>)."""
+    by EDEN's unbiased n / <y, c[idx]>); polar records for tq.PolarParams."""
+    if isinstance(kp, tq.PolarParams):
+        cache = tq.alloc_polar_cache(kp, keys.shape[0], seg_stride)
+        tq.polar_encode(kp, keys.contiguous(), cache)
+        return cache
     cache = tq.alloc_key_cache(kp, keys.shape[0], seg_stride)
     if kp.s is not None:
         tq.encode_prod(kp, keys.contiguous(), cache)
@@ -55,8 +60,13 @@ def estimated_scores(kp: tq.Params, cache: tq.Cache, n_keys: int, queries):
     T = _torch()
     Q = queries.shape[0]
     out = T.empty((Q, n_keys), dtype=T.float32, device=queries.device)
-    ws = tq.alloc_workspace(tq.scores_workspace(kp, 1, MAX_GROUP))
     one = tq.Cache(cache.planes, cache.scalars, 0)
+    if isinstance(kp, tq.PolarParams):
+        for h0 in range(0, Q, MAX_GROUP):
+            g = min(MAX_GROUP, Q - h0)
+            tq.polar_scores(kp, queries[h0:h0 + g].contiguous(), 1, g, one, n_keys, out[h0:h0 + g])
+        return out
+    ws = tq.alloc_workspace(tq.scores_workspace(kp, 1, MAX_GROUP))
     for h0 in range(0, Q, MAX_GROUP):
         g = min(MAX_GROUP, Q - h0)
         tq.scores(kp, queries[h0:h0 + g].contiguous(), 1, g, one, n_keys, out[h0:h0 + g], ws)
@@ -90,8 +100,12 @@ def needle_scores(kp: tq.Params, cache: tq.Cache, queries, L: int):
     T = _torch()
     trials = queries.shape[0]
     est = T.empty((trials, L), dtype=T.float32, device=queries.device)
+    segs = tq.Cache(cache.planes, cache.scalars, L)
+    if isinstance(kp, tq.PolarParams):
+        tq.polar_scores(kp, queries.contiguous(), trials, 1, segs, L, est)
+        return est
     ws = tq.alloc_workspace(tq.scores_workspace(kp, trials, 1))
-    tq.scores(kp, queries.contiguous(), trials, 1, tq.Cache(cache.planes, cache.scalars, L), L, est, ws)
+    tq.scores(kp, queries.contiguous(), trials, 1, segs, L, est, ws)
     return est
 
 

@@ -179,3 +179,39 @@ def test_output_fidelity_decoder_shaped(bits):
 def oq_exact(k, v, q, scale):
     """Exact softmax attention of q over (k, v), float64 (the oracle's weighted sum on the raw inputs)."""
     return est.softmax_weighted_sum(q.astype(np.float64) @ k.astype(np.float64).T, v, scale)
+
+
+@pytest.mark.parametrize("qjl", [False, True])
+def test_polar_attention_fidelity_and_needle(qjl):
+    # PolarQuant keys through the harness (tq_polar_scores) against the oracle's
+    # statistics of its own polar scores, on oracle-packed records
+    from oracle import polar as pq
+    from tests.test_gpu_polar import PolarSetup
+    _log(f"quality polar{' + QJL' if qjl else ''}: fidelity and needle")
+    w = 2 if qjl else 3
+    st = PolarSetup(w, w, 128 if qjl else 0, "dense", seed=11)
+    keys = unit_gaussian(2048, 128, seed=11)
+    qs = unit_gaussian(100, 128, seed=11, purpose=QUERIES)
+    code = st.oracle(keys)
+    est_gpu = quality.estimated_scores(st.params, st.packed_cache(code), 2048, _dev(qs))
+    cos, top1 = quality.fidelity(quality.exact_scores(_dev(keys), _dev(qs)), est_gpu)
+    est_o = pq.polar_scores(qs, code, st.rot, st.s)
+    true_o = qs.astype(np.float64) @ keys.astype(np.float64).T
+    cos_o, top1_o = oq.attention_fidelity(true_o, est_o)
+    assert np.max(np.abs(cos.cpu().numpy() - cos_o)) <= 1e-4
+    flips = _check_argmax(np.argmax(est_gpu.cpu().numpy(), 1), oq.argmax_rows(est_o), est_o)
+    if flips == 0:
+        assert np.array_equal(top1.cpu().numpy(), top1_o)
+    # needle: 20 haystacks of 8192 keys, one segment each
+    hay, hq, _ = needle_haystacks(20, 8192, 128, seed=13)
+    hcode = st.oracle(hay.reshape(-1, 128))
+    cache = st.packed_cache(hcode, 8192)
+    est_n = quality.needle_scores(st.params, cache, _dev(hq), 8192).cpu().numpy()
+    for t in range(20):
+        sub = pq.PolarCode(codes=None, n=hcode.n[t * 8192:(t + 1) * 8192], y=None, angles=None,
+                           y_hat=hcode.y_hat[t * 8192:(t + 1) * 8192],
+                           z=None if hcode.z is None else hcode.z[t * 8192:(t + 1) * 8192],
+                           gamma=None if hcode.gamma is None else hcode.gamma[t * 8192:(t + 1) * 8192])
+        want = pq.polar_scores(hq[t:t + 1], sub, st.rot, st.s)[0]
+        assert np.max(np.abs(est_n[t] - want)) <= 2e-5 * np.linalg.norm(hq[t]) * np.max(sub.n)
+    _log(f"  mean cos {cos.mean().item():.6f} (oracle {cos_o.mean():.6f}), top-1 {top1.double().mean().item():.2f}")
