@@ -81,9 +81,11 @@ struct PrepArgs {
   uint8_t* ws;
   int n_sets, set_div;   // rotation sets: segment seg uses set (seg / set_div) % n_sets
   int m_rows;            // rows of one set's QJL matrix
+  int seg_per_wg;        // prep_queries128: consecutive segments per workgroup (same rotation set)
 };
 
-// One workgroup (8 waves) per segment.  Both 128x128 products run on the
+// One workgroup (8 waves) per segment, or per group of consecutive segments
+// whose heads together fill the 16 head columns.  Both 128x128 products run on the
 // matrix cores (v_mfma_f32_16x16x32_bf16) with bf16 hi/lo splits of both
 // operands (three products, ~2^-16 relative, far below the 2^-21 integer
 // quantisation that follows; bf16 keeps fp32's range, so no rescaling):
@@ -149,7 +151,7 @@ struct PrepLds {
 // MW: QJL sign words per key (m / 32); with MW = 2 the QJL rows past 64 are
 // zero, so the pack's QJL weights for coordinate groups 2 and 3 vanish.
 template <bool HAD, int S, int CPOL = 0, bool QJL = true, int MW = 4>
-__device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L, uint8_t* dst) {
+__device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, int ns, PrepLds& L, uint8_t* dst) {
   float* qr = L.qr;
   float* qp = L.qp;
   auto& part = L.part;
@@ -161,7 +163,7 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   const int np = mse_planes(a.bq);
   const int F = 2 * (np + (QJL ? 1 : 0));
   const int fbytes = (int)pack_frag_bytes(a.mt, F);
-  const rsrc_t rdst = make_rsrc(dst, (uint32_t)pack_bytes(a.mt, F));
+  const uint32_t pbytes = (uint32_t)pack_bytes(a.mt, F);
   // this segment's rotation set
   const int set = a.n_sets > 1 ? (seg / a.set_div) % a.n_sets : 0;
   const float* set_pi = a.pi ? a.pi + (size_t)set * D * D : nullptr;
@@ -176,7 +178,8 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   float4 mv[8], sv[8];
   const int qh = t >> 5, q4 = t & 31;      // head, float4 within the head (16 x 32 = 512 threads)
   float4 qv = {0.f, 0.f, 0.f, 0.f};
-  if (qh < G) qv = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + qh) * D)[q4];
+  // column c of the products: head c % G of segment seg + c / G (ns G <= 16)
+  if (qh < ns * G) qv = reinterpret_cast<const float4*>(a.q + ((size_t)seg * G + qh) * D)[q4];
   const float4* prow = reinterpret_cast<const float4*>(set_pi + (size_t)(HAD ? 0 : row) * D);
   // MSE-only keys have no QJL matrix: its rows read as zeros (q_proj = 0)
   // (with m = d / 2, rows from 64 on read as zeros)
@@ -308,6 +311,8 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
   constexpr int R = S == 2 ? 2 : 4;             // A rows per head
   constexpr int HT = 16 / R;                    // heads per 16-row tile
   const int nitems = a.mt * F * 4 * HT;
+  for (int j = 0; j < ns; ++j) {     // segment seg + j: its heads are columns j G ..
+  const rsrc_t rdst = make_rsrc(dst + (size_t)j * pbytes, pbytes);
   for (int it = t; it < nitems; it += PREP_THREADS) {
     const int hl = it % HT, rest = it / HT;
     const int kg = rest & 3;
@@ -315,7 +320,7 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
     const int p = f >> 1, m = f & 1;
     const int h = HT * mt + hl;
     const bool live = h < G;
-    const int hs = live ? h : 0;
+    const int hs = live ? j * G + h : 0;
     const float* src = (p < np ? qr : qp) + hs * QTS + 32 * kg + 4 * m;
     const float wsc = live ? L.wsc[p < np ? p : 8][hs] : 0.f;
     float4 v[4];
@@ -350,8 +355,9 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, PrepLds& L
     }
   }
   if (t < a.mt * 16 / R * 4)
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, t < G * 4 ? stat[t >> 2][t & 3] : 0.f), rdst,
-                                          (uint32_t)(fbytes + 4 * t), 0, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, t < G * 4 ? stat[j * G + (t >> 2)][t & 3] : 0.f),
+                                          rdst, (uint32_t)(fbytes + 4 * t), 0, CPOL);
+  }
 }
 
 // (at most two waves per SIMD: the register budget keeps every operand load
@@ -361,7 +367,9 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(1,
 void prep_queries128(PrepArgs a) {
   __shared__ PrepLds L;
   const int F = 2 * (mse_planes(a.bq) + (QJL ? 1 : 0));
-  prep_pack<HAD, S, 0, QJL, MW>(a, blockIdx.x, L, a.ws + (size_t)blockIdx.x * pack_bytes(a.mt, F));
+  const int seg0 = blockIdx.x * a.seg_per_wg;
+  const int ns = a.segs - seg0 < a.seg_per_wg ? a.segs - seg0 : a.seg_per_wg;
+  prep_pack<HAD, S, 0, QJL, MW>(a, seg0, ns, L, a.ws + (size_t)seg0 * pack_bytes(a.mt, F));
 }
 
 // One-launch scores: the first workgroup of each segment builds the query
@@ -558,7 +566,7 @@ void scores128(Score128Args a) {
       if (threadIdx.x == 0) *mine = take_claim(&a.sync[b], a.ticket) ? 1 : 0;
       __syncthreads();
       if (*mine) {
-        prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, b, *reinterpret_cast<PrepLds*>(smem),
+        prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, b, 1, *reinterpret_cast<PrepLds*>(smem),
                                              a.prep.ws + (size_t)b * pack_bytes(MT, F));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -623,7 +631,7 @@ void scores128(Score128Args a) {
     if (*build) {
       // the producer has not started: build the pack here (the only writer
       // of this launch), publish it, then request the first keys again
-      prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, seg, *reinterpret_cast<PrepLds*>(smem),
+      prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, seg, 1, *reinterpret_cast<PrepLds*>(smem),
                                            const_cast<uint8_t*>(pack));
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -952,13 +960,17 @@ static PrepArgs make_prep(const ScoreArgs& a, int slices) {
   p.slices = slices;
   p.mt = slices == 2 ? (a.group + 7) / 8 : (a.group + 3) / 4;
   p.ws = static_cast<uint8_t*>(a.ws);
+  p.seg_per_wg = 1;
   return p;
 }
 
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream) {
-  const PrepArgs p = make_prep(a, slices);
+  PrepArgs p = make_prep(a, slices);
+  // consecutive segments that share a rotation set fill the products' 16 head
+  // columns together (one read of Pi and S per workgroup)
+  p.seg_per_wg = p.n_sets > 1 ? 1 : MAXG / (a.group > 0 ? a.group : 1);
   const bool had = a.rot == TQ_ROT_HADAMARD;
-  const dim3 grid(a.segs), block(PREP_THREADS);
+  const dim3 grid((a.segs + p.seg_per_wg - 1) / p.seg_per_wg), block(PREP_THREADS);
   if (a.qjl && a.m == D / 2) {
     switch ((slices == 2 ? 0 : 2) + (had ? 1 : 0)) {
       case 0: hipLaunchKernelGGL((prep_queries128<false, 2, true, 2>), grid, block, 0, stream, p); break;

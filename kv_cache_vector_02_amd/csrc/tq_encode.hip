@@ -47,6 +47,7 @@ constexpr float R_SCALE = 256.f;   // 2^8
 constexpr float U_SCALE = 64.f;    // 2^6 (fp32 inputs, after normalising)
 constexpr float HAD_SCALE = 0.08838834764831845f;   // 1 / sqrt(128)
 constexpr int FRAGS = 4 * 8 * 2 * 64;  // half8 per 128x128 matrix (hi and lo)
+constexpr int64_t VSCAN_MAX = 4096;    // value records a small-batch workgroup scans for shared blocks
 
 __device__ __forceinline__ int frag_index(int mt, int ks, int part, int lane) {
   return ((mt * 8 + ks) * 2 + part) * 64 + lane;
@@ -151,15 +152,17 @@ __device__ __forceinline__ void quantize(float y, const Codebook& cb, int& idx, 
 // sign projection follows (prod keys), without it the record holds the BQ
 // index planes and the norm only (MSE-only keys).  !PROD: values in the
 // token-blocked layout.
-// SLOTS: values written through a slot map (any record order), whose tiles
-// may take the per-bit path; without it only a ragged last tile can.
+// Values of a tile that is not one aligned, fully valid 32-record block (a
+// slot map in any order, a ragged tail) set or clear their bits in the
+// epilogue, one atomic or / and per plane word with nothing read first (a
+// record's bit has one writer; other records of the block may be written at
+// the same time).
 // EDEN: an MSE record stores the unbiased per-vector scale n / <y, c[idx]>
 // instead of n (EDEN's scale; DRIVE's at one bit).
 // MW: QJL sign words per key record, m / 32 (4: m = d; 2: m = d / 2, whose
 // record holds for each 32-coordinate group w the index words, then sign word
 // w if w < 2).
-template <bool PROD, bool QJL, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool SLOTS, bool EDEN = false,
-          int MW = 4>
+template <bool PROD, bool QJL, int BQ, bool F16IN, int NT, int WAVES, bool HAD, bool EDEN = false, int MW = 4>
 __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   static_assert(PROD || !QJL, "values carry no QJL bits");
   static_assert(!(EDEN && QJL), "the scale replaces the norm of MSE records only");
@@ -167,8 +170,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   extern __shared__ half8 lds[];
   half8* fpi = lds;
   half8* fs = lds + FRAGS;
+  // values, one tile per workgroup: the tile's plane words [32][2 halves][BQ][2],
+  // records, same-block masks and shared flags, for the bit writes after the tile
+  uint32_t* vbits = reinterpret_cast<uint32_t*>(lds + FRAGS);
+  int64_t* vrecs = reinterpret_cast<int64_t*>(vbits + 32 * 2 * BQ * 2);
+  uint32_t* vmask = reinterpret_cast<uint32_t*>(vrecs + 32);
+  int* vshared = reinterpret_cast<int*>(vmask + 32);
   build_frags<64 * WAVES>(fpi, a.pi, PI_SCALE, HAD ? a.eps : nullptr);
   if (QJL) build_frags<64 * WAVES, MW == 2>(fs, a.s, 1.f);
+  if (!PROD && threadIdx.x < 32) vshared[threadIdx.x] = 0;
   __syncthreads();
 
   constexpr int P = QJL ? BQ + 1 : BQ;      // planes per record
@@ -188,7 +198,38 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
   for (int k = 0; k < (1 << BQ) - 1; ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(cbv.b[k]) : "s"(a.cb.b[k]));
 
-  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
+  // tiles: consecutive per workgroup, or (interleave) one per workgroup in
+  // wave 0 first, so that a small batch takes one tile per workgroup while all
+  // its waves build the fragments
+  // (values: `split` workgroups share each small-batch tile, each computing
+  // it and writing its share of the tile's words)
+  const int split = a.interleave ? a.split : 1;
+  const int part = (int)(blockIdx.x % split);
+  const int64_t wg = blockIdx.x / split, ngroups = gridDim.x / split;
+  if constexpr (!PROD) {
+    // one tile per workgroup (values, small batch): while wave 0 encodes it,
+    // the other waves look for records of the call outside the tile that share
+    // a block with it (the tile's records from the slot map, lane u of each
+    // wave holding record u)
+    if (a.interleave && wave > 0 && wg < ntiles && a.n <= VSCAN_MAX) {
+      const int64_t tile0 = wg * 32;
+      const int64_t iu = tile0 + (lane & 31);
+      const int64_t mine = iu < a.n ? (a.slot ? a.slot[iu] : iu) : -1;
+      // 64-record chunks per wave, the same trip count on every lane (the
+      // shuffles read lanes 0..31)
+      for (int64_t i0 = 64 * (int64_t)(wave - 1); i0 < a.n; i0 += 64 * (WAVES - 1)) {
+        const int64_t i = i0 + lane;
+        const int64_t r = i < a.n && (i < tile0 || i >= tile0 + 32) ? (a.slot ? a.slot[i] : i) : -1;
+        const bool lr = (uint64_t)r < (uint64_t)a.records;
+        for (int u = 0; u < 32; ++u) {
+          const int64_t q = __shfl((long long)mine, u, 64);
+          if (lr && (uint64_t)q < (uint64_t)a.records && (q >> 5) == (r >> 5)) vshared[u] = 1;
+        }
+      }
+    }
+  }
+  for (int64_t tile = a.interleave ? wg + ngroups * wave : (int64_t)blockIdx.x * WAVES + wave;
+       tile < ntiles; tile += stride) {
     // The fragment reads below are loop-invariant; without this barrier the
     // compiler hoists all of them (256 registers) out of the loop and spills.
     asm volatile("" ::: "memory");
@@ -276,9 +317,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
     if (!PROD) {
       static_assert(PROD || NT == 1, "value tiles are 32 vectors");
       const int64_t r0 = a.slot ? a.slot[tile * 32 < a.n ? tile * 32 : 0] : tile * 32;
-      // this lane's record, read once (the per-bit path below would otherwise
-      // re-read it after every batch of atomics)
-      vrec = vec[0] < a.n ? (a.slot ? a.slot[vec[0]] : vec[0]) : 0;
+      // this lane's record (-1 past n)
+      vrec = vec[0] < a.n ? (a.slot ? a.slot[vec[0]] : vec[0]) : -1;
       const bool mine = vec[0] < a.n && vrec == r0 + v;
       // whole-block stores only for a block inside the cache's capacity
       vfast = (r0 % 32) == 0 && r0 >= 0 && r0 + 32 <= a.records && __all(mine);
@@ -308,23 +348,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         acc[nt] = mfma32x32x16(ahi, xh[nt][ks], acc[nt]);
         if (!HAD) acc[nt] = mfma32x32x16(alo, xh[nt][ks], acc[nt]);   // +-16 has no lo part
         if (!F16IN) acc[nt] = mfma32x32x16(ahi, xl[nt][ks], acc[nt]);
-      }
-    };
-    // per-bit value path: this lane's current words of the 16 coordinates of
-    // a row tile, read before its epilogue.  Only this lane writes its bit of
-    // a word (records are distinct), so a plain read shows that bit exactly
-    // and only the bits that change need an atomic.
-    uint32_t oldw[SLOTS ? 16 * BQ : 1];
-    auto load_old = [&](int mt) {
-      if (PROD || !SLOTS || vfast || vec[0] >= a.n || (uint64_t)vrec >= (uint64_t)a.records) return;
-      const uint4* src = reinterpret_cast<const uint4*>(a.planes + (vrec >> 5) * (D * BQ) + (64 * h + 16 * mt) * BQ);
-#pragma unroll
-      for (int q = 0; q < 4 * BQ; ++q) {
-        const uint4 w = src[q];
-        oldw[4 * q] = w.x;
-        oldw[4 * q + 1] = w.y;
-        oldw[4 * q + 2] = w.z;
-        oldw[4 * q + 3] = w.w;
       }
     };
     auto epi = [&](const f32x16* acc, int mt, int nt, int r) {
@@ -385,21 +408,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
             bit[p] = x;
             iw[nt][p][mt >> 1] = shift_in(iw[nt][p][mt >> 1], x);
           }
-          if (!PROD) {
-            if (vec[nt] < a.n && (uint64_t)vrec < (uint64_t)a.records) {
-              // blocks shared with other vectors: an atomic for each bit
-              // that changes (with a slot map), else one per bit
-              uint32_t* wp = a.planes + (vrec >> 5) * (D * BQ) + (64 * h + 16 * mt + r) * BQ;
-              const uint32_t sh = (uint32_t)(vrec & 31);
+          if (!PROD && !(a.interleave && wave == 0) && vec[nt] < a.n && (uint64_t)vrec < (uint64_t)a.records) {
+            // this record's bit of each plane word of coordinate 64 h + 16 mt + r:
+            // one atomic or / and per word, nothing read first; the 64 lanes
+            // of each atomic hit 64 different words of 32 records' blocks
+            // (with one tile per workgroup, wave 0's tile, the whole workgroup
+            // issues them after the tile instead)
+            uint32_t* wp = a.planes + (vrec >> 5) * (D * BQ) + (64 * h + 16 * mt + r) * BQ;
+            const uint32_t sh = 1u << (uint32_t)(vrec & 31);
 #pragma unroll
-              for (int p = 0; p < BQ; ++p) {
-                const uint32_t nb = (uint32_t)(bit[p] >> lane) & 1u;
-                const bool change = SLOTS ? nb != ((oldw[r * BQ + p] >> sh) & 1u) : true;
-                if (change) {
-                  if (nb) atomicOr(wp + p, 1u << sh);
-                  else atomicAnd(wp + p, ~(1u << sh));
-                }
-              }
+            for (int p = 0; p < BQ; ++p) {
+              if ((bit[p] >> lane) & 1u) atomicOr(wp + p, sh);
+              else atomicAnd(wp + p, ~sh);
             }
           }
           if (QJL) {
@@ -421,7 +441,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
     for (int mt = 1; mt < 4; ++mt) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) accB[nt] = f32x16{};
-      load_old(mt - 1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if ((i & 1) == 0) mma(accB, mt, i >> 1);
@@ -431,7 +450,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) accA[nt] = accB[nt];
     }
-    load_old(3);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -478,7 +496,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
         g = sqrtf(t) * ysc[nt];
       }
       if (!PROD) {
-        if (vfast) {
+        if (vfast && part == 0) {
           // lane L holds the words of coordinates L and 64 + L, planes contiguous
           uint32_t* base = a.planes + vblock * (D * BQ);
 #pragma unroll
@@ -492,9 +510,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
           const float t = yc[nt] + shfl_xor_f(yc[nt], 32);    // <y, c[idx]>, y on the unit sphere
           sv = nrm[nt] > 0.f && t > 0.f ? nrm[nt] / t : 0.f;
         }
-        if (vec[nt] < a.n && h == 0) {
+        if (vec[nt] < a.n && h == 0 && part == 0) {
           const int64_t rec = a.slot ? a.slot[vec[nt]] : vec[nt];
           if ((uint64_t)rec < (uint64_t)a.records) a.scalars[rec] = f16_bits(sv);
+        }
+        if (a.interleave && wave == 0) {
+#pragma unroll
+          for (int p = 0; p < BQ; ++p)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) vbits[((v * 2 + h) * BQ + p) * 2 + w] = __builtin_bitreverse32(iw[nt][p][w]);
+          if (h == 0) vrecs[v] = vfast ? -1 : vrec;     // an aligned block is already written
         }
         continue;
       }
@@ -562,40 +587,112 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
       }
     }
   }
+  if constexpr (!PROD) {
+    // One tile per workgroup (wave 0's): the workgroup writes the tile's value
+    // bits.  A block that no record of the call outside this tile touches
+    // (found by scanning the call's records, for calls of up to VSCAN_MAX) has
+    // this workgroup as its only writer: one thread per plane word reads it,
+    // sets or clears the bits of every tile record in the block, and stores it.
+    // Other blocks take one atomic or / and per record and word.
+    if (a.interleave && wg < ntiles) {
+      constexpr int NW = D * BQ;    // plane words of a block
+      __syncthreads();              // wave 0's vbits, vrecs
+      const int t = threadIdx.x;
+      auto live = [&](int64_t r) { return (uint64_t)r < (uint64_t)a.records; };
+      if (t < 32) {
+        const int64_t r = vrecs[t];
+        uint32_t m = 0;
+        if (live(r)) {
+          for (int u = 0; u < 32; ++u)
+            if (live(vrecs[u]) && (vrecs[u] >> 5) == (r >> 5)) m |= 1u << u;
+        }
+        vmask[t] = m;       // the tile's records in the same block (itself included)
+      }
+      __syncthreads();
+      const bool scan = a.n <= VSCAN_MAX;
+      // this workgroup's share of the tile's words (split = 1, 2, 4 or 8), every
+      // thread's words in flight together: reads first, then the writes
+      constexpr int PER = 32 * NW / (64 * WAVES * 8);
+      static_assert(PER * 64 * WAVES * 8 == 32 * NW, "a whole number of words per thread");
+      const int per = PER * (8 / split);
+      const int fbase = part * (32 * NW / split);
+      uint32_t old[8 * PER];
+#pragma unroll
+      for (int k = 0; k < 8 * PER; ++k) {
+        if (k >= per) break;
+        const int f = fbase + t + 64 * WAVES * k, u = f & 31, w = f >> 5;
+        const int64_t rec = vrecs[u];
+        const bool rmw = live(rec) && scan && !vshared[u] && (int)__builtin_ctz(vmask[u]) == u;
+        old[k] = rmw ? a.planes[(rec >> 5) * NW + w] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < 8 * PER; ++k) {
+        if (k >= per) break;
+        const int f = fbase + t + 64 * WAVES * k, u = f & 31, w = f >> 5;
+        const int64_t rec = vrecs[u];
+        if (!live(rec)) continue;
+        const int c = w / BQ, p = w - c * BQ;
+        const int vi = (c >> 6) * BQ * 2 + p * 2 + ((c >> 5) & 1);   // (half, plane, word) within a record's vbits
+        uint32_t* wp = a.planes + (rec >> 5) * NW + w;
+        if (scan && !vshared[u]) {
+          const uint32_t m = vmask[u];
+          if ((int)__builtin_ctz(m) != u) continue;      // the block's first tile record writes its words
+          uint32_t word = old[k];
+          for (uint32_t mm = m; mm; mm &= mm - 1) {
+            const int u2 = __builtin_ctz(mm);
+            const uint32_t bit = 1u << (uint32_t)(vrecs[u2] & 31);
+            word = (vbits[u2 * 4 * BQ + vi] >> (c & 31)) & 1u ? word | bit : word & ~bit;
+          }
+          *wp = word;
+        } else {
+          const uint32_t bit = 1u << (uint32_t)(rec & 31);
+          if ((vbits[u * 4 * BQ + vi] >> (c & 31)) & 1u) atomicOr(wp, bit);
+          else atomicAnd(wp, ~bit);
+        }
+      }
+    }
+  }
 }
 
 template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int WAVES, bool EDEN = false, int MW = 4>
 hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
   constexpr int NT = 1;
-  // EDEN values always take the slot-capable form (one kernel for both)
-  auto kern = MW != 4 ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, false, false, MW>
-              : EDEN ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD, EDEN>
-              : PROD || !a.slot ? encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, false>
-                                : encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, !PROD>;
-  const size_t lds = (QJL ? 2 : 1) * FRAGS * sizeof(half8);
+  auto kern = encode_dense128<PROD, QJL, BQ, F16IN, NT, WAVES, HAD, EDEN, MW>;
+  // fragments; values also the tile's plane words and records (one tile per workgroup)
+  const size_t lds = (QJL ? 2 : 1) * FRAGS * sizeof(half8) + (PROD ? 0 : 32 * 2 * BQ * 2 * 4 + 32 * 8 + 32 * 8);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t ntiles = (a.n + 32 * NT - 1) / (32 * NT);
-  const int64_t want = (ntiles + WAVES - 1) / WAVES;
   const int blocks_per_cu = PROD ? 1 : 2;
+  EncodeArgs b = a;
+  // values in a small batch: 1, 2, 4 or 8 workgroups per tile, as the device
+  // holds them, sharing the tile's scattered bit writes
+  b.split = 1;
+  if (!PROD && a.interleave && a.slot)    // (without a slot map at most the last tile is not one block)
+    while (b.split < 8 && ntiles * b.split * 2 <= (int64_t)cus * blocks_per_cu) b.split *= 2;
+  const int64_t want = a.interleave ? ntiles * b.split : (ntiles + WAVES - 1) / WAVES;
   const int grid = (int)std::min<int64_t>(want, (int64_t)cus * blocks_per_cu);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), lds, stream, b);
   return hipGetLastError();
 }
 
-// Workgroups of 8 waves share one copy of the fragments per compute unit; a
+// Workgroups of 8 waves share one copy of the fragments per compute unit.  A
 // small batch (under two tiles per compute unit, e.g. one appended token per
-// sequence) takes one-wave workgroups instead, so that its tiles (and, for
-// values written through a slot map, their per-bit atomics) spread over as
-// many compute units as there are tiles.
+// sequence) takes one tile per workgroup instead (interleaved tile map), so
+// that its tiles spread over as many compute units as there are tiles while
+// all eight waves of each build its fragments.
 template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int MW = 4>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   int dev = 0, cus = 256;
-  hipGetDevice(&dev);
-  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t ntiles = (a.n + 31) / 32;
-  if (ntiles < 2 * (int64_t)cus) return launch_waves<PROD, QJL, BQ, F16IN, HAD, 1, false, MW>(a, cus, stream);
+  if (ntiles < 2 * (int64_t)cus) {
+    EncodeArgs b = a;
+    b.interleave = 1;
+    return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8, false, MW>(b, cus, stream);
+  }
   return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8, false, MW>(a, cus, stream);
 }
 
@@ -611,17 +708,19 @@ hipError_t launch_prod_half(const EncodeArgs& a, hipStream_t stream) {
 }
 
 // EDEN-scaled MSE records (keys in the per-record layout, or values), b
-// index bits; one launch shape (8-wave workgroups) for every batch size
+// index bits; 8-wave workgroups, one tile each for a small batch
 template <bool PROD, bool F16IN, bool HAD>
 hipError_t launch_eden(const EncodeArgs& a, hipStream_t stream) {
   int dev = 0, cus = 256;
-  hipGetDevice(&dev);
-  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  EncodeArgs b = a;
+  b.interleave = (a.n + 31) / 32 < 2 * (int64_t)cus;   // small batches: one tile per workgroup
   switch (a.bq) {
-    case 1: return launch_waves<PROD, false, 1, F16IN, HAD, 8, true>(a, cus, stream);
-    case 2: return launch_waves<PROD, false, 2, F16IN, HAD, 8, true>(a, cus, stream);
-    case 3: return launch_waves<PROD, false, 3, F16IN, HAD, 8, true>(a, cus, stream);
-    case 4: return launch_waves<PROD, false, 4, F16IN, HAD, 8, true>(a, cus, stream);
+    case 1: return launch_waves<PROD, false, 1, F16IN, HAD, 8, true>(b, cus, stream);
+    case 2: return launch_waves<PROD, false, 2, F16IN, HAD, 8, true>(b, cus, stream);
+    case 3: return launch_waves<PROD, false, 3, F16IN, HAD, 8, true>(b, cus, stream);
+    case 4: return launch_waves<PROD, false, 4, F16IN, HAD, 8, true>(b, cus, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -39,6 +39,8 @@ struct EncodeArgs {
   uint16_t* scalars;   // [records][S] float16 bit patterns
   const int64_t* slot; // record of vector i, or null
   int64_t records;     // capacity of planes / scalars in records: records at or past it are not written
+  int interleave;      // d = 128 encode launch: 1 = one tile per workgroup (set by the launcher)
+  int split;           // with interleave, values: workgroups per tile (set by the launcher)
 };
 
 hipError_t launch_encode_dense128(const EncodeArgs& a, hipStream_t stream);

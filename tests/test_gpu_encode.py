@@ -140,6 +140,28 @@ def test_value_blocks_shared_across_workgroups():
     compare_encode(st, idx[slot], scal[slot], st.encode_oracle(x))
 
 
+@pytest.mark.parametrize("n", [512, 4100])
+def test_value_append_one_record_per_block(n):
+    # a decode step's append: each vector goes to its own 32-token block of a
+    # pre-filled cache (block b gets token b % 32).  Up to 4096 vectors a call
+    # finds every block single-written and rewrites whole words; above that it
+    # sets the bits with atomics.  Every other record must keep its old bits.
+    _log(f"encode values, one record per block, n = {n}")
+    st = Setup(bits=3, prod=False, seed=21, purpose_pi=4)
+    records = 32 * n
+    old = kv_tensor(1, 1, records, 128, seed=22, value=True)[0, 0]
+    cache = st.alloc(records)
+    st.encode_gpu(old, cache=cache)
+    x = kv_tensor(1, 1, n, 128, seed=23, value=True)[0, 0]
+    b = np.arange(n)
+    slot = b * 32 + b % 32
+    planes, scal = st.encode_gpu(x, slot=slot, cache=cache)
+    idx = value_indices(planes, records)
+    compare_encode(st, idx[slot], scal[slot], st.encode_oracle(x))
+    rest = np.setdiff1d(np.arange(records), slot)[::7]
+    compare_encode(st, idx[rest], scal[rest], st.encode_oracle(old[rest]))
+
+
 @pytest.mark.parametrize("prod,bits", [(True, 2), (True, 3), (True, 4), (False, 1), (False, 2), (False, 3),
                                        (False, 4)])
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
