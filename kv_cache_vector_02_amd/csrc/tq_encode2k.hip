@@ -14,13 +14,14 @@
 // The residual goes to the workspace as fp16 hi + lo (prescaled by 2^8).
 //
 // Pass 2, the QJL projection of a chunk of residuals, C = R S^T (M = vectors,
-// N = K = 2048), on v_mfma_f32_32x32x16_f16 with fp16 hi/lo operands (three
-// products, ~2^-22 relative).  A workgroup (4 waves) owns a 128 x 128 tile of
-// C; a wave owns 64 x 64.  Lane l of a 32 x 32 accumulator holds column l % 32
-// for 16 rows, so the sign bits of a row's 32 columns are one ballot: the
-// epilogue writes whole QJL plane words.  Consecutive workgroups share an
-// M tile and the workgroup-to-XCD assignment (id mod 8) gives each XCD two
-// fixed 128-row slices of S, which stay in its L2.
+// N = m, K = 2048), on v_mfma_f32_32x32x16_f16 with fp16 hi/lo operands (three
+// products, ~2^-22 relative).  A workgroup (8 waves) owns a 256 x 128 tile of
+// C, staged through the LDS in K blocks of 32; a wave owns 64 x 64.  Lane l
+// of a 32 x 32 accumulator holds column l % 32 for 16 rows, so the sign bits
+// of a row's 32 columns are one ballot: the epilogue writes whole QJL plane
+// words.  Consecutive workgroups share an M tile and the workgroup-to-XCD
+// assignment (id mod 8) gives each XCD fixed 128-row slices of S, which stay
+// in its L2.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -57,7 +58,6 @@ __device__ __forceinline__ int record_words(int bq, int mw) { return 64 * bq + m
 
 constexpr float R2_SCALE = 256.f;        // 2^8, keeps the residual's lo part normal in fp16
 constexpr float INV_SQRT_D2 = 0.02209708691207961f;   // 1 / sqrt(2048)
-constexpr int SIGN_TILE = 128;
 
 __global__ __launch_bounds__(256) void split_s_f16(const float* __restrict__ s, _Float16* hi, _Float16* lo,
                                                     int64_t count) {
@@ -205,62 +205,95 @@ __global__ __launch_bounds__(256) void encode2k_pass1(Encode2kArgs a) {
   }
 }
 
+// Workgroup tile 256 vectors x 128 projection rows, 8 waves of 64 x 64;
+// K in stages of 32, double-buffered in the LDS (rows padded to 80 bytes, so
+// the 16-byte fragment reads of 16 lanes cover all 64 banks once), the next
+// stage's global loads in flight while the current one is multiplied.
+constexpr int SG_M = 256, SG_N = 128, SG_K = 32, SG_LD = 40, SG_THREADS = 512;
+constexpr int SG_A = SG_M * SG_LD, SG_B = SG_N * SG_LD;   // halfs per operand copy
+constexpr int SG_STAGE = 2 * SG_A + 2 * SG_B;             // A hi, A lo, B hi, B lo
+constexpr size_t SG_LDS = 2 * SG_STAGE * sizeof(_Float16);
+
 template <int P>
-__global__ __launch_bounds__(256) void encode2k_signs(Encode2kArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t mw = (int64_t)blockIdx.y * SIGN_TILE + 64 * (wave >> 1);   // chunk-local vector rows
-  const int iw = blockIdx.x * SIGN_TILE + 64 * (wave & 1);                 // output coordinates
+__global__ __launch_bounds__(SG_THREADS) void encode2k_signs(Encode2kArgs a) {
+  extern __shared__ half8 sg8[];
+  _Float16* sg = reinterpret_cast<_Float16*>(sg8);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int64_t mrow0 = (int64_t)blockIdx.y * SG_M;   // chunk-local vector rows of the tile
+  const int nrow0 = blockIdx.x * SG_N;                // projection rows of the tile
+  // copy items (16 bytes each): k = 0, 1 A hi rows 0..255; 2, 3 A lo; 4 B hi;
+  // 5 B lo.  Global offsets from the two bases, LDS offsets, per item.
+  const int crow = t >> 2, cc = (t & 3) * 8;
+  const int64_t aoff0 = (mrow0 + crow) * D2 + cc, aoff1 = aoff0 + (int64_t)128 * D2;
+  const int64_t boff = (int64_t)(nrow0 + crow) * D2 + cc;
+  const int l0 = crow * SG_LD + cc, l1 = l0 + 128 * SG_LD;
+  uint4 stg[6];
+#define SG_GLOAD(kb)                                                                                    \
+  do {                                                                                                  \
+    const int64_t ko = (int64_t)SG_K * (kb);                                                            \
+    stg[0] = *reinterpret_cast<const uint4*>(a.r_hi + aoff0 + ko);                                      \
+    stg[1] = *reinterpret_cast<const uint4*>(a.r_hi + aoff1 + ko);                                      \
+    stg[2] = *reinterpret_cast<const uint4*>(a.r_lo + aoff0 + ko);                                      \
+    stg[3] = *reinterpret_cast<const uint4*>(a.r_lo + aoff1 + ko);                                      \
+    stg[4] = *reinterpret_cast<const uint4*>(a.s_hi + boff + ko);                                       \
+    stg[5] = *reinterpret_cast<const uint4*>(a.s_lo + boff + ko);                                       \
+  } while (0)
+#define SG_LSTORE(stage)                                                                                \
+  do {                                                                                                  \
+    _Float16* d = sg + (stage) * SG_STAGE;                                                              \
+    *reinterpret_cast<uint4*>(d + l0) = stg[0];                                                         \
+    *reinterpret_cast<uint4*>(d + l1) = stg[1];                                                         \
+    *reinterpret_cast<uint4*>(d + SG_A + l0) = stg[2];                                                  \
+    *reinterpret_cast<uint4*>(d + SG_A + l1) = stg[3];                                                  \
+    *reinterpret_cast<uint4*>(d + 2 * SG_A + l0) = stg[4];                                              \
+    *reinterpret_cast<uint4*>(d + 2 * SG_A + SG_B + l0) = stg[5];                                       \
+  } while (0)
+  const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, kh = lane >> 5;
-  const _Float16* ah = a.r_hi + (mw + l32) * D2 + 8 * kh;
-  const _Float16* al = a.r_lo + (mw + l32) * D2 + 8 * kh;
-  const _Float16* bh = a.s_hi + (int64_t)(iw + l32) * D2 + 8 * kh;
-  const _Float16* bl = a.s_lo + (int64_t)(iw + l32) * D2 + 8 * kh;
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  // operands of k step s + 2 are requested before step s is multiplied:
-  // three register sets in a ring (the loop unrolled by three so that each
-  // set's role is fixed), scheduling barriers keeping every request ahead
-  half8 Ah[3][2], Al[3][2], Bh[3][2], Bl[3][2];
-  auto fetch = [&](int b, int step) {
-    const int k0 = 16 * step;
+  constexpr int KB = D2 / SG_K;
+  SG_GLOAD(0);
+  SG_LSTORE(0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    if (kb + 1 < KB) SG_GLOAD(kb + 1);
+    const _Float16* st = sg + (kb & 1) * SG_STAGE;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      Ah[b][t] = *reinterpret_cast<const half8*>(ah + (int64_t)32 * t * D2 + k0);
-      Al[b][t] = *reinterpret_cast<const half8*>(al + (int64_t)32 * t * D2 + k0);
-      Bh[b][t] = *reinterpret_cast<const half8*>(bh + (int64_t)32 * t * D2 + k0);
-      Bl[b][t] = *reinterpret_cast<const half8*>(bl + (int64_t)32 * t * D2 + k0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto mma = [&](int b) {
+    for (int ks = 0; ks < SG_K / 16; ++ks) {
+      const int k0 = 16 * ks + 8 * kh;
+      half8 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma32x32x16(Ah[b][i], Bh[b][j], acc[i][j]);
-        acc[i][j] = mfma32x32x16(Al[b][i], Bh[b][j], acc[i][j]);
-        acc[i][j] = mfma32x32x16(Ah[b][i], Bl[b][j], acc[i][j]);
+      for (int i = 0; i < 2; ++i) {
+        const int ra = (64 * wm + 32 * i + l32) * SG_LD + k0;
+        ah[i] = *reinterpret_cast<const half8*>(st + ra);
+        al[i] = *reinterpret_cast<const half8*>(st + SG_A + ra);
+        const int rb = (64 * wn + 32 * i + l32) * SG_LD + k0;
+        bh[i] = *reinterpret_cast<const half8*>(st + 2 * SG_A + rb);
+        bl[i] = *reinterpret_cast<const half8*>(st + 2 * SG_A + SG_B + rb);
       }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  constexpr int STEPS = D2 / 16;   // 128 = 3 * 42 + 2
-  fetch(0, 0);
-  fetch(1, 1);
-  for (int s0 = 0; s0 + 4 < STEPS; s0 += 3) {
-    fetch(2, s0 + 2);
-    mma(0);
-    fetch(0, s0 + 3);
-    mma(1);
-    fetch(1, s0 + 4);
-    mma(2);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma32x32x16(ah[i], bh[j], acc[i][j]);
+          acc[i][j] = mfma32x32x16(al[i], bh[j], acc[i][j]);
+          acc[i][j] = mfma32x32x16(ah[i], bl[j], acc[i][j]);
+        }
+    }
+    if (kb + 1 < KB) SG_LSTORE((kb + 1) & 1);
+    __syncthreads();
   }
-  mma(0);   // step STEPS - 2
-  mma(1);   // step STEPS - 1
+#undef SG_GLOAD
+#undef SG_LSTORE
   // signs: ballot over the 32 columns of each accumulator row
+  const int64_t mw = mrow0 + 64 * wm;    // chunk-local vector rows of this wave
+  const int iw = nrow0 + 64 * wn;        // projection rows of this wave
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -299,8 +332,11 @@ hipError_t run_chunks(const Encode2kArgs& base, bool f16, hipStream_t stream) {
       hipLaunchKernelGGL((encode2k_pass1<BQ, true, true>), dim3(g1), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((encode2k_pass1<BQ, false, true>), dim3(g1), dim3(256), 0, stream, a);
-    const dim3 g2((unsigned)(a.m / SIGN_TILE), (unsigned)((a.cn + SIGN_TILE - 1) / SIGN_TILE));
-    hipLaunchKernelGGL((encode2k_signs<BQ + 1>), g2, dim3(256), 0, stream, a);
+    const dim3 g2((unsigned)(a.m / SG_N), (unsigned)((a.cn + SG_M - 1) / SG_M));
+    hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&encode2k_signs<BQ + 1>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)SG_LDS);
+    if (e0 != hipSuccess) return e0;
+    hipLaunchKernelGGL((encode2k_signs<BQ + 1>), g2, dim3(SG_THREADS), SG_LDS, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -309,7 +345,7 @@ hipError_t run_chunks(const Encode2kArgs& base, bool f16, hipStream_t stream) {
 
 }  // namespace
 
-int64_t encode2k_chunk(int64_t n) { return n < 32768 ? (n + SIGN_TILE - 1) / SIGN_TILE * SIGN_TILE : 32768; }
+int64_t encode2k_chunk(int64_t n) { return n < 32768 ? (n + SG_M - 1) / SG_M * SG_M : 32768; }
 
 size_t encode2k_workspace(int64_t n) {
   // S hi + lo, then the residual chunk hi + lo, all fp16
