@@ -752,6 +752,8 @@ def main():
     ap.add_argument("--skip-retrieval", action="store_true", help="skip the 1M x 1536 top-10 retrieval line")
     ap.add_argument("--skip-batched", action="store_true", help="skip the batched-decode step line")
     ap.add_argument("--skip-polar", action="store_true", help="skip the PolarQuant stage-1 line")
+    ap.add_argument("--retrieval-only", action="store_true",
+                    help="only the 1M x 1536 top-10 retrieval line (for its kernel profiles)")
     ap.add_argument("--polar-only", action="store_true",
                     help="only the PolarQuant stage-1 line on the Llama-shaped keys (for its kernel profile)")
     ap.add_argument("--quality", action="store_true",
@@ -771,6 +773,10 @@ def main():
     from tq_inputs import gaussian_queries
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.retrieval_only:
+        print(json.dumps({"retrieval": retrieval_line(torch, tq, lambda: torch.cuda.Event(enable_timing=True))}),
+              flush=True)
         return
     if args.polar_only:
         k = torch.from_numpy(kv_tensor_keys()).cuda()
