@@ -220,8 +220,13 @@ tq_status tq_encode_prod_ws(const tq_params* p, const void* x, int dtype, int64_
 /* TurboQuant-MSE encode (values): as above without the QJL stage, b index
  * bits, written in the blocked value layout.  A group of 32 vectors that fills
  * one aligned block (slot NULL, or slots base + 0..31 with base a multiple of
- * 32) is written with whole-word stores; any other record is updated with
- * per-bit atomic clear/set, so partial blocks keep their other records.
+ * 32) is written with whole-word stores; any other record updates only its
+ * own bit of each word, so partial blocks keep their other records.  In calls
+ * of up to 4096 vectors a block that exactly one group of 32 consecutive
+ * vectors of the call writes is updated by reading, changing and storing
+ * whole words; other blocks take per-bit atomic clear/set.  Two calls in
+ * flight at once (different streams) must therefore not write records of the
+ * same 32-record block; calls on one stream are ordered and always safe.
  * At d_rot = 2048 with the sign-flipped Hadamard rotation (d a multiple of 8,
  * d <= 2048) the records instead use the per-record key layout of
  * tq_key_layout with b planes and one fp16 scalar ||x||_2 per record (no
