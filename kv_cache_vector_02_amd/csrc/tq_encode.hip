@@ -654,6 +654,460 @@ __global__ __launch_bounds__(64 * WAVES, 1) void encode_dense128(EncodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (an append of a few hundred vectors, the 4096-vector tiny
+// workload): one 32-vector tile per workgroup of four waves, wave mt computing
+// row tile mt of both products, so a tile takes a quarter of the matrix-core
+// chain it takes in one wave, and no workgroup builds a shared fragment copy:
+// each lane splits its own 64 entries of the matrix rows it needs (16 KB of
+// fp32 per wave and matrix, L2 hits after the first workgroup).  The
+// arithmetic is the one of encode_dense128 (same products in the same order,
+// same quantiser), so records match the large-batch path; only the norm of the
+// residual is summed in another order.
+//   keys:   the waves exchange the residual's fp16 split (the B operand of the
+//           sign product) and their 16-bit parts of the plane words in LDS;
+//           wave 0 writes the records.
+//   values: an aligned, fully valid 32-record block is written whole (each
+//           wave its 32 coordinates); otherwise every wave updates its
+//           coordinates' words of the tile's records: a block that no other
+//           record of the call touches (found by the four waves scanning the
+//           call's records, for calls of up to VSCAN_MAX) by reading,
+//           changing and storing whole words, other blocks with one atomic
+//           or / and per record and word.
+constexpr int ROWS_THREADS = 256;
+
+template <int BQ>
+struct RowsLds {
+  half8 res[8][2][64];             // keys: residual split, [k step][hi, lo][lane]
+  uint32_t part[4][BQ + 1][64];    // keys: 16-bit parts of the index (and sign) words, [row tile][plane][lane]
+  float g2[4][64];                 // keys: partial squared residual norms
+  uint32_t vb[4][32][2][BQ];       // values: [row tile][record][lane half][plane] bits r of coordinates 64 h + 16 mt + r
+  int64_t vrecs[32];               // values: the tile's records (-1: none)
+  uint32_t vmask[32];              // values: tile records in the same block
+  uint32_t vshmask;                // values: tile records whose block another record of the call shares
+};
+
+template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int MW = 4>
+__global__ __launch_bounds__(ROWS_THREADS, 1) void encode_rows128(EncodeArgs a) {
+  static_assert(PROD || !QJL, "values carry no QJL bits");
+  static_assert(MW == 4 || (QJL && MW == 2), "m = d / 2 is a prod-key form");
+  constexpr int P = QJL ? BQ + 1 : BQ;
+  __shared__ RowsLds<BQ> L;
+  const int lane = threadIdx.x & 63;
+  const int mt = threadIdx.x >> 6;      // the wave's row tile
+  const int v = lane & 31, h = lane >> 5;
+  const int64_t tile = blockIdx.x;
+  const int64_t vec = tile * 32 + v;
+  const bool valid = vec < a.n;
+  if (!PROD && threadIdx.x == 0) L.vshmask = 0u;
+
+  // ---- operands: x (coordinates 64 h .. 64 h + 63 of vector v) and this
+  // lane's rows of Pi (and S), all requested before any is used ----
+  float4 pm[16], sm[16];
+  {
+    const int row = row_coord(v, mt);
+    const float4* src = reinterpret_cast<const float4*>(HAD ? a.eps + 64 * h : a.pi + row * D + 64 * h);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pm[i] = src[i];
+  }
+  if constexpr (QJL) {
+    if (mt < MW) {
+      const int row = MW == 2 ? row_half(v, mt) : row_coord(v, mt);
+      const float4* src = reinterpret_cast<const float4*>(a.s + row * D + 64 * h);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm[i] = src[i];
+    }
+  }
+  half8 xh[8], xl[8];
+  float ysc, inv, nrm;
+  if (F16IN) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.x) + (valid ? vec : 0) * a.ld_x + 64 * h);
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      half8 hv = __builtin_bit_cast(half8, valid ? src[ks] : make_uint4(0, 0, 0, 0));
+      xh[ks] = hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s4[e & 3] += (float)hv[e] * (float)hv[e];
+    }
+    float s2 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    s2 += shfl_xor_f(s2, 32);
+    const float n = sqrtf(s2);
+    nrm = n;
+    ysc = n > 0.f ? (HAD ? HAD_SCALE : 1.f) / (n * PI_SCALE) : 1.f;
+    inv = n > 0.f ? (n * PI_SCALE) / (HAD ? HAD_SCALE : 1.f) : 1.f;
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (valid ? vec : 0) * a.ld_x + 64 * h);
+    float xv[64];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float4 w = valid ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      xv[4 * i] = w.x; xv[4 * i + 1] = w.y; xv[4 * i + 2] = w.z; xv[4 * i + 3] = w.w;
+    }
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 64; ++i) s4[i & 3] += xv[i] * xv[i];
+    float s2 = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    s2 += shfl_xor_f(s2, 32);
+    const float n = sqrtf(s2);
+    const float un = n > 0.f ? U_SCALE / n : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        _Float16 hi, lo;
+        split_f16(xv[8 * ks + e] * un, hi, lo);
+        xh[ks][e] = hi;
+        xl[ks][e] = lo;
+      }
+    }
+    nrm = n;
+    ysc = (HAD ? HAD_SCALE : 1.f) / (U_SCALE * PI_SCALE);
+    inv = (U_SCALE * PI_SCALE) / (HAD ? HAD_SCALE : 1.f);
+  }
+
+  // ---- values: this lane's record and the tile's block case; the records
+  // of the call the scan for shared blocks compares (first chunks requested
+  // now, compared after the products); the words a single writer will
+  // rewrite, requested before the products as well ----
+  constexpr int NQ = 16 * BQ / 4;    // 16-byte groups of a lane's run of plane words
+  constexpr int SPRE = 4;            // scan chunks requested up front
+  int64_t vrec = -1;
+  bool vfast = false;
+  int64_t vblock = 0;
+  int64_t spre[SPRE];
+  uint4 w4[NQ];
+  const bool scan = a.n <= VSCAN_MAX;
+  if constexpr (!PROD) {
+#pragma unroll
+    for (int c = 0; c < SPRE; ++c) {
+      const int64_t i = 64 * (int64_t)(mt + 4 * c) + lane;
+      spre[c] = i < a.n ? (a.slot ? a.slot[i] : i) : -1;
+    }
+    const int64_t r0 = a.slot ? a.slot[tile * 32 < a.n ? tile * 32 : 0] : tile * 32;
+    vrec = valid ? (a.slot ? a.slot[vec] : vec) : -1;
+    const bool mine = valid && vrec == r0 + v;
+    vfast = (r0 % 32) == 0 && r0 >= 0 && r0 + 32 <= a.records && __all(mine);
+    vblock = r0 / 32;
+    if (mt == 0 && h == 0) L.vrecs[v] = vfast || (uint64_t)vrec >= (uint64_t)a.records ? -1 : vrec;
+    __syncthreads();   // vshmask cleared, vrecs set
+    // lane (record u = lane % 32, half hh = lane / 32) owns the 16 BQ words of
+    // coordinates 64 hh + 16 mt .. + 15 in u's block
+    const int64_t rec = L.vrecs[lane & 31];
+    if (!vfast && scan && rec >= 0) {
+      const uint4* wp = reinterpret_cast<const uint4*>(a.planes + (rec >> 5) * (D * BQ) + (64 * h + 16 * mt) * BQ);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) w4[q] = wp[q];
+    }
+  }
+
+  // ---- A fragments of this wave's row tile (and of its sign row tile) ----
+  half8 ph[8], pl[8], sh[8], sl[8];
+  {
+    const int row = row_coord(v, mt);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float* f = reinterpret_cast<const float*>(&pm[2 * ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float val = f[e];
+        if (HAD) val = (__popc(row & (64 * h + 8 * ks + e)) & 1) ? -val : val;
+        _Float16 hi, lo;
+        split_f16(val * PI_SCALE, hi, lo);
+        ph[ks][e] = hi;
+        pl[ks][e] = lo;
+      }
+    }
+  }
+  if constexpr (QJL) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float* f = reinterpret_cast<const float*>(&sm[2 * ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        _Float16 hi, lo;
+        split_f16(mt < MW ? f[e] : 0.f, hi, lo);
+        sh[ks][e] = hi;
+        sl[ks][e] = lo;
+      }
+    }
+  }
+
+  // ---- GEMM1, row tile mt ----
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    acc = mfma32x32x16(ph[ks], xh[ks], acc);
+    if (!HAD) acc = mfma32x32x16(pl[ks], xh[ks], acc);   // +-16 has no lo part
+    if (!F16IN) acc = mfma32x32x16(ph[ks], xl[ks], acc);
+  }
+
+  // ---- quantise, pack, residual (as the large-batch epilogue) ----
+  Codebook cbv;
+#pragma unroll
+  for (int k = 0; k < (1 << BQ); ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(cbv.c[k]) : "s"(a.cb.c[k]));
+#pragma unroll
+  for (int k = 0; k < (1 << BQ) - 1; ++k) asm volatile("v_mov_b32 %0, %1" : "=v"(cbv.b[k]) : "s"(a.cb.b[k]));
+  float bsc[(1 << BQ) - 1], csc[1 << BQ];
+  const float rsc = R_SCALE * ysc;
+  if (PROD) {
+#pragma unroll
+    for (int k = 0; k < (1 << BQ) - 1; ++k) bsc[k] = cbv.b[k] * inv;
+#pragma unroll
+    for (int k = 0; k < (1 << BQ); ++k) csc[k] = cbv.c[k] * inv;
+  }
+  uint32_t iw[BQ];
+  uint32_t vlo[BQ], vhi[BQ];
+#pragma unroll
+  for (int p = 0; p < BQ; ++p) iw[p] = vlo[p] = vhi[p] = 0u;
+  half8 rh[2], rl[2];
+  float g2 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float y = PROD ? acc[r] : acc[r] * ysc;
+    if (!PROD && vfast) {
+      // ballots of [y >= beta_k]; the xors of the thermometer code give each
+      // plane's two block words of coordinate 16 mt + r, kept by lane 16 mt + r
+      uint64_t ge[(1 << BQ) - 1];
+#pragma unroll
+      for (int k = 0; k < (1 << BQ) - 1; ++k) ge[k] = __ballot(y >= cbv.b[k]);
+#pragma unroll
+      for (int p = 0; p < BQ; ++p) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int k = 0; k < (1 << BQ) - 1; ++k)
+          if (((k + 1) & ((1 << p) - 1)) == 0) m ^= ge[k];
+        const bool here = lane == 16 * mt + r;
+        vlo[p] = here ? (uint32_t)m : vlo[p];
+        vhi[p] = here ? (uint32_t)(m >> 32) : vhi[p];
+      }
+      continue;
+    }
+    uint64_t ge[(1 << BQ) - 1];
+    float chat = PROD ? csc[0] : cbv.c[0];
+#pragma unroll
+    for (int k = 0; k < (1 << BQ) - 1; ++k) {
+      ge[k] = ge_mask(y, PROD ? bsc[k] : cbv.b[k]);
+      chat = select_mask(ge[k], PROD ? csc[k + 1] : cbv.c[k + 1], chat);
+    }
+#pragma unroll
+    for (int p = 0; p < BQ; ++p) {
+      uint64_t x = 0;
+#pragma unroll
+      for (int k = 0; k < (1 << BQ) - 1; ++k)
+        if (((k + 1) & ((1 << p) - 1)) == 0) x ^= ge[k];
+      iw[p] = shift_in(iw[p], x);
+    }
+    if (QJL) {
+      const float d = y - chat;      // residual / ysc
+      g2 += d * d;
+      _Float16 hi, lo;
+      split_f16(d * rsc, hi, lo);
+      rh[r >> 3][r & 7] = hi;
+      rl[r >> 3][r & 7] = lo;
+    }
+  }
+  // the 16 bits of this row tile, bit r = coordinate 64 h + 16 mt + r, at
+  // bit 16 (mt % 2) + r of plane word 2 h + mt / 2
+  auto place = [&](uint32_t w16) { return (mt & 1) ? __builtin_bitreverse32(w16) : __builtin_bitreverse32(w16) >> 16; };
+
+  if constexpr (PROD) {
+#pragma unroll
+    for (int p = 0; p < BQ; ++p) L.part[mt][p][lane] = place(iw[p]);
+    if constexpr (QJL) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        L.res[2 * mt + j][0][lane] = rh[j];
+        L.res[2 * mt + j][1][lane] = rl[j];
+      }
+      L.g2[mt][lane] = g2;
+    }
+    __syncthreads();
+    // ---- GEMM2 (QJL signs), row tile mt of S ----
+    if constexpr (QJL) {
+      if (mt < MW) {
+        f32x16 acc2 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const half8 bh = L.res[ks][0][lane], bl = L.res[ks][1][lane];
+          acc2 = mfma32x32x16(sh[ks], bh, acc2);
+          acc2 = mfma32x32x16(sl[ks], bh, acc2);
+          acc2 = mfma32x32x16(sh[ks], bl, acc2);
+        }
+        uint32_t sw = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sw = shift_in(sw, ge_mask(acc2[r], 0.f));
+        L.part[mt][BQ][lane] = place(sw);
+      }
+      __syncthreads();
+    }
+    if (mt != 0) return;
+    // ---- wave 0: the records ----
+    uint32_t wd[P][2];
+#pragma unroll
+    for (int p = 0; p < BQ; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wd[p][j] = L.part[2 * j][p][lane] | L.part[2 * j + 1][p][lane];
+    float g = 0.f;
+    if constexpr (QJL) {
+      if (MW == 4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wd[BQ][j] = L.part[2 * j][BQ][lane] | L.part[2 * j + 1][BQ][lane];
+      } else {
+        // m = d / 2: sign word hh from row tiles 0, 1 of lane half hh
+        const int o = lane ^ 32;
+        wd[BQ][0] = L.part[0][BQ][lane] | L.part[1][BQ][lane];
+        wd[BQ][1] = L.part[0][BQ][o] | L.part[1][BQ][o];
+      }
+      float t = ((L.g2[0][lane] + L.g2[1][lane]) + (L.g2[2][lane] + L.g2[3][lane]));
+      t += shfl_xor_f(t, 32);
+      g = sqrtf(t) * ysc;
+    }
+    const int64_t rec = valid ? (a.slot ? a.slot[vec] : vec) : -1;
+    if ((uint64_t)rec >= (uint64_t)a.records) return;
+    if constexpr (QJL && MW == 2) {
+      // per coordinate group: the index words, then sign word w for w < 2;
+      // lane half 0 writes groups 0 and 1, lane half 1 groups 2 and 3
+      constexpr int RW = 4 * BQ + 2;
+      uint32_t out[2 * BQ + 2];
+#pragma unroll
+      for (int p = 0; p < BQ; ++p) {
+        out[p] = wd[p][0];
+        out[BQ + 1 + p] = wd[p][1];
+      }
+      out[BQ] = wd[BQ][0];
+      out[2 * BQ + 1] = wd[BQ][1];
+      if (h == 1) {
+#pragma unroll
+        for (int p = 0; p < BQ; ++p) out[BQ + p] = wd[p][1];
+      }
+      uint2* dst = reinterpret_cast<uint2*>(a.planes + rec * RW + (h ? 2 * BQ + 2 : 0));
+#pragma unroll
+      for (int i = 0; i < BQ + 1; ++i)
+        if (h == 0 || i < BQ) dst[i] = make_uint2(out[2 * i], out[2 * i + 1]);
+    } else {
+      // word w of plane p at w * P + p: this lane owns words 2 h and 2 h + 1
+      uint32_t out[2 * P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        out[p] = wd[p][0];
+        out[P + p] = wd[p][1];
+      }
+      uint2* dst = reinterpret_cast<uint2*>(a.planes + rec * (P * 4) + 2 * h * P);
+#pragma unroll
+      for (int i = 0; i < P; ++i) dst[i] = make_uint2(out[2 * i], out[2 * i + 1]);
+    }
+    if (h == 0) {
+      if (QJL)
+        reinterpret_cast<uint32_t*>(a.scalars)[rec] = (uint32_t)f16_bits(nrm) | ((uint32_t)f16_bits(g) << 16);
+      else
+        a.scalars[rec] = f16_bits(nrm);
+    }
+  } else {
+    constexpr int NW = D * BQ;    // plane words of a value block
+    if (mt == 0 && h == 0 && valid && (uint64_t)vrec < (uint64_t)a.records) a.scalars[vrec] = f16_bits(nrm);
+    if (vfast) {
+      // lane 16 mt + r holds the words of coordinates 16 mt + r and 64 + 16 mt + r
+      if ((lane >> 4) == mt) {
+        uint32_t* base = a.planes + vblock * NW;
+#pragma unroll
+        for (int p = 0; p < BQ; ++p) {
+          base[lane * BQ + p] = vlo[p];
+          base[(64 + lane) * BQ + p] = vhi[p];
+        }
+      }
+      return;
+    }
+    if (scan) {
+      // records of the call outside the tile that share a block with it:
+      // each lane compares its record's block with the tile's 32 (LDS
+      // broadcasts) and ors the hits into one mask
+      const int64_t tile0 = tile * 32;
+      int64_t tb[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int64_t q = L.vrecs[u];
+        tb[u] = q >= 0 ? q >> 5 : -1;
+      }
+      uint32_t hit = 0u;
+      for (int c = 0; 64 * (int64_t)(mt + 4 * c) < a.n; ++c) {
+        const int64_t i = 64 * (int64_t)(mt + 4 * c) + lane;
+        int64_t r = -1;
+#pragma unroll
+        for (int k = 0; k < SPRE; ++k)
+          if (k == c) r = spre[k];
+        if (c >= SPRE) r = i < a.n ? (a.slot ? a.slot[i] : i) : -1;
+        if (i >= tile0 && i < tile0 + 32) r = -1;
+        if ((uint64_t)r < (uint64_t)a.records) {
+          const int64_t blk = r >> 5;
+#pragma unroll
+          for (int u = 0; u < 32; ++u) hit |= blk == tb[u] ? 1u << u : 0u;
+        }
+      }
+      if (hit) atomicOr(&L.vshmask, hit);
+    }
+#pragma unroll
+    for (int p = 0; p < BQ; ++p) L.vb[mt][v][h][p] = __builtin_bitreverse32(iw[p]) >> 16;
+    if (threadIdx.x < 32) {
+      const int64_t r = L.vrecs[threadIdx.x];
+      uint32_t m = 0;
+      if (r >= 0) {
+        for (int u = 0; u < 32; ++u)
+          if (L.vrecs[u] >= 0 && (L.vrecs[u] >> 5) == (r >> 5)) m |= 1u << u;
+      }
+      L.vmask[threadIdx.x] = m;
+    }
+    __syncthreads();
+    const int u = lane & 31, hh = lane >> 5;
+    const int64_t rec = L.vrecs[u];
+    if (rec < 0) return;
+    const uint32_t m = L.vmask[u];
+    uint32_t* wp = a.planes + (rec >> 5) * NW + (64 * hh + 16 * mt) * BQ;
+    if (scan && !((L.vshmask >> u) & 1u)) {
+      // the block's first tile record merges the bits of every tile record
+      // in the block into the words it read and stores them
+      if ((int)__builtin_ctz(m) != u) return;
+      for (uint32_t mm = m; mm; mm &= mm - 1) {
+        const int u2 = __builtin_ctz(mm);
+        const uint32_t bit = 1u << (uint32_t)(L.vrecs[u2] & 31);
+        uint32_t bits[BQ];
+#pragma unroll
+        for (int p = 0; p < BQ; ++p) bits[p] = L.vb[mt][u2][hh][p];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int w = 4 * q + e, ci = w / BQ, p = w % BQ;
+            uint32_t& word = e == 0 ? w4[q].x : e == 1 ? w4[q].y : e == 2 ? w4[q].z : w4[q].w;
+            word = (bits[p] >> ci) & 1u ? word | bit : word & ~bit;
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) reinterpret_cast<uint4*>(wp)[q] = w4[q];
+    } else {
+      const uint32_t bit = 1u << (uint32_t)(rec & 31);
+      uint32_t bits[BQ];
+#pragma unroll
+      for (int p = 0; p < BQ; ++p) bits[p] = L.vb[mt][u][hh][p];
+#pragma unroll
+      for (int w = 0; w < 16 * BQ; ++w) {
+        const int ci = w / BQ, p = w % BQ;
+        if ((bits[p] >> ci) & 1u) atomicOr(wp + w, bit);
+        else atomicAnd(wp + w, ~bit);
+      }
+    }
+  }
+}
+
+template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int MW = 4>
+hipError_t launch_rows(const EncodeArgs& a, hipStream_t stream) {
+  const int64_t ntiles = (a.n + 31) / 32;
+  hipLaunchKernelGGL((encode_rows128<PROD, QJL, BQ, F16IN, HAD, MW>), dim3((unsigned)ntiles), dim3(ROWS_THREADS), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int WAVES, bool EDEN = false, int MW = 4>
 hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
   constexpr int NT = 1;
@@ -679,20 +1133,15 @@ hipError_t launch_waves(const EncodeArgs& a, int cus, hipStream_t stream) {
 
 // Workgroups of 8 waves share one copy of the fragments per compute unit.  A
 // small batch (under two tiles per compute unit, e.g. one appended token per
-// sequence) takes one tile per workgroup instead (interleaved tile map), so
-// that its tiles spread over as many compute units as there are tiles while
-// all eight waves of each build its fragments.
+// sequence) takes the row-split kernel instead: one tile per four-wave
+// workgroup, spread over as many compute units as there are tiles.
 template <bool PROD, bool QJL, int BQ, bool F16IN, bool HAD, int MW = 4>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t ntiles = (a.n + 31) / 32;
-  if (ntiles < 2 * (int64_t)cus) {
-    EncodeArgs b = a;
-    b.interleave = 1;
-    return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8, false, MW>(b, cus, stream);
-  }
+  if (ntiles < 2 * (int64_t)cus) return launch_rows<PROD, QJL, BQ, F16IN, HAD, MW>(a, stream);
   return launch_waves<PROD, QJL, BQ, F16IN, HAD, 8, false, MW>(a, cus, stream);
 }
 
