@@ -1182,6 +1182,14 @@ struct Attend128Args {
   int nchunks;                  // workgroups per segment
   int64_t span;                 // tokens per workgroup (multiple of AGRAN)
   int kv_div;                   // query segments per cache segment (1, or 2 when a segment's heads run as halves)
+  // one workgroup per segment (nchunks = 1): the workgroup normalises and
+  // applies the value rotation itself, as attend_combine128 would
+  int solo;
+  float* out;                   // [segs][group][128]
+  const float* pi_v;            // value rotations (dense), [sets][128][128]
+  const float* eps_v;           // or their signs (Hadamard), [sets][128]
+  int rot_v;
+  int n_sets_v, set_div_v;      // value rotation set of query segment seg: (seg / set_div_v) % n_sets_v
 };
 
 __device__ __forceinline__ float f16lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffff)); }
@@ -1477,6 +1485,59 @@ __global__ __launch_bounds__(256, KMT <= 2 ? 2 : 1) void attend128(Attend128Args
   }
   __syncthreads();
   const int nh = a.group < NH ? a.group : NH;
+  if (a.solo) {
+    // the segment's only workgroup: o~ / l per head into the LDS (the P'
+    // rows are free now), then o = Pi_v^T (o~ / l), lane (j = 32 wave +
+    // lane % 32, k half kh) summing its 64 rotation entries, the halves
+    // joined by one shuffle
+    float* ot = reinterpret_cast<float*>(&pq[0][0][0][0]);     // [nh][128]
+    static_assert(sizeof(pq) >= sizeof(float) * NH * D, "o~ fits the P' rows");
+    for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
+      const int h = i / D, k = i % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sred[w][h][0]);
+      float l = 0.f, o = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float wt = __builtin_amdgcn_exp2f(sred[w][h][0] - M);   // 0 for empty waves
+          l += wt * sred[w][h][1];
+          o += wt * sred[w][h][4 + k];
+        }
+      }
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      ot[h * D + k] = o * inv;
+    }
+    const int set = a.n_sets_v > 1 ? (seg / a.set_div_v) % a.n_sets_v : 0;
+    const int j = 32 * wave + (lane & 31), kh = lane >> 5;
+    float pj[64];
+    if (a.rot_v == TQ_ROT_DENSE) {
+      const float* pv = a.pi_v + (size_t)set * D * D + (size_t)(64 * kh) * D + j;
+#pragma unroll
+      for (int kk = 0; kk < 64; ++kk) pj[kk] = pv[(size_t)kk * D];
+    } else {
+      const float sg = a.eps_v[(size_t)set * D + j] * rsqrtf((float)D);
+#pragma unroll
+      for (int kk = 0; kk < 64; ++kk) pj[kk] = (__popc(j & (64 * kh + kk)) & 1) ? -sg : sg;
+    }
+    __syncthreads();
+    for (int h = 0; h < nh; ++h) {
+      const float4* src = reinterpret_cast<const float4*>(ot + h * D + 64 * kh);
+      float acc = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < 16; ++k4) {
+        const float4 x = src[k4];
+        acc = fmaf(pj[4 * k4], x.x, acc);
+        acc = fmaf(pj[4 * k4 + 1], x.y, acc);
+        acc = fmaf(pj[4 * k4 + 2], x.z, acc);
+        acc = fmaf(pj[4 * k4 + 3], x.w, acc);
+      }
+      acc += __shfl_xor(acc, 32, 64);
+      if (kh == 0) a.out[((size_t)seg * a.group + h) * D + j] = acc;
+    }
+    return;
+  }
   float* outp = a.part + ((size_t)seg * a.nchunks + chunk) * a.group * PST;
   for (int i = threadIdx.x; i < nh * 130; i += blockDim.x) {
     const int h = i / 130, c = i % 130;
@@ -1638,6 +1699,7 @@ hipError_t launch_attend(Attend128Args& s, int segs, hipStream_t stream) {
   static const int nb = occupancy(reinterpret_cast<const void*>(&attend128<BQK, BQV, MT, QJL, MW>), 256);
   s.span = split_span(segs, s.T, nb * device_cus(), AGRAN, attend_kmax(segs, s.T));
   s.nchunks = (int)((s.T + s.span - 1) / s.span);
+  s.solo = s.nchunks == 1;
   hipLaunchKernelGGL((attend128<BQK, BQV, MT, QJL, MW>), dim3((unsigned)s.nchunks, (unsigned)segs), dim3(256), 0,
                      stream, s);
   return hipGetLastError();
@@ -1703,6 +1765,13 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   s.nchunks = 0;   // set by the launcher
   s.span = 0;
   s.kv_div = a.kv_div;
+  s.solo = 0;   // set by the launcher
+  s.out = a.out;
+  s.pi_v = a.pi_v;
+  s.eps_v = a.eps_v;
+  s.rot_v = a.rot_v;
+  s.n_sets_v = a.n_sets_v > 1 ? a.n_sets_v : 1;
+  s.set_div_v = (a.set_div_v > 1 ? a.set_div_v : 1) * a.kv_div;
   const int mt = (a.k.group + 3) / 4;
   if (a.k.qjl && a.k.m == D / 2) {
     switch (a.k.bq * 10 + a.bq_v) {
@@ -1782,6 +1851,7 @@ hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  if (s.solo) return hipSuccess;   // each segment's workgroup finished it
   Combine128Args c;
   c.part = s.part;
   c.nchunks = s.nchunks;

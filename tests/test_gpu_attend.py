@@ -120,6 +120,51 @@ def test_hadamard_rotations():
                     oracle_attend(sk, sv, q[s * 4:(s + 1) * 4], kf, vidx, vn, sl, 1 / np.sqrt(128)))
 
 
+@pytest.mark.parametrize("rot,group", [("dense", 1), ("dense", 4), ("dense", 8), ("dense", 16), ("hadamard", 4)])
+def test_single_workgroup_segments(rot, group):
+    # T <= 512: one workgroup per segment, which normalises its heads and
+    # applies the inverse value rotation itself (no combine launch); lengths
+    # include a full segment, a ragged one, an empty one and a single token
+    _log(f"attend, one workgroup per segment, {rot} G{group}")
+    segs, T_, stride = 4, 512, 512
+    sk, sv = _setups(3, 3, rot=rot, seed=9)
+    xk = kv_tensor(1, segs, stride, 128, seed=9)[0].reshape(-1, 128)
+    xv = kv_tensor(1, segs, stride, 128, seed=9, value=True)[0].reshape(-1, 128)
+    kc, kf = oracle_key_cache(sk, xk, seg_stride=stride)
+    vc, vidx, vn = oracle_value_cache(sv, xv, stride)
+    q = gaussian_queries(segs * group, 128, seed=9)
+    length = [512, 300, 0, 1]
+    scale = 1 / np.sqrt(128)
+    got = gpu_attend(sk, sv, q, segs, group, kc, vc, T_, scale, length=length)
+    for s in range(segs):
+        rows = slice(s * group, (s + 1) * group)
+        if length[s] == 0:
+            assert np.all(got[rows] == 0.0), "an empty segment gives zeros"
+            continue
+        sl = slice(s * stride, s * stride + length[s])
+        check_heads(got[rows], oracle_attend(sk, sv, q[rows], kf, vidx, vn, sl, scale))
+
+
+def test_many_segments_one_workgroup_each():
+    # more segments than the device holds workgroups at once: each 768-token
+    # segment gets a single workgroup (the batched-decode launch shape);
+    # sampled segments against the oracle
+    _log("attend, 1024 segments x 768 tokens, one workgroup each")
+    segs, T_, group = 1024, 768, 4
+    sk, sv = _setups(3, 3, seed=10)
+    xk = kv_tensor(1, segs, T_, 128, seed=10)[0].reshape(-1, 128)
+    xv = kv_tensor(1, segs, T_, 128, seed=10, value=True)[0].reshape(-1, 128)
+    kc, kf = oracle_key_cache(sk, xk, seg_stride=T_)
+    vc, vidx, vn = oracle_value_cache(sv, xv, T_)
+    q = gaussian_queries(segs * group, 128, seed=10)
+    scale = 1 / np.sqrt(128)
+    got = gpu_attend(sk, sv, q, segs, group, kc, vc, T_, scale)
+    for s in [0, 1, 511, 777, 1023]:
+        rows = slice(s * group, (s + 1) * group)
+        sl = slice(s * T_, (s + 1) * T_)
+        check_heads(got[rows], oracle_attend(sk, sv, q[rows], kf, vidx, vn, sl, scale))
+
+
 def test_qwen_shaped_full_size():
     # 36 layers x 2 KV heads x 8192 tokens, 16 query heads per layer (G=8),
     # keys prod b=3, values mse b=3, one launch; every segment against the oracle

@@ -115,12 +115,14 @@ def test_scores_with_rotation_sets(layout, rot):
                                               ks.rots[i], ks.ss[i], ks.c32))
 
 
+@pytest.mark.parametrize("T_", [600, 480])
 @pytest.mark.parametrize("kbits,group", [(3, 8), (4, 16)])
-def test_attend_with_rotation_sets(kbits, group):
+def test_attend_with_rotation_sets(kbits, group, T_):
     # per-layer key and value rotations; the second case uses MSE-only 4-bit
     # keys at 16 heads, whose segments run as two head halves (the halves of a
-    # segment must use that segment's set)
-    L, H, T_ = 2, 2, 600
+    # segment must use that segment's set).  At T = 480 each segment has one
+    # workgroup, which applies its set's value rotation itself.
+    L, H = 2, 2
     segs, stride = L * H, 608
     prod = kbits == 3
     _log(f"attend with per-layer rotation sets ({'prod' if prod else 'MSE-only'} keys b{kbits}, G{group})")
