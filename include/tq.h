@@ -348,6 +348,22 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
                     int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
                     float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* The two parts of tq_attend, for callers that overlap the query side with
+ * other work (a decode step can prepare the new queries on a second stream
+ * while it appends the step's keys and values, which the pack does not
+ * read): tq_attend_prepare writes the query pack of every segment into ws
+ * (kp, q, segs, group and ws as for tq_attend; ws_bytes at least the pack's
+ * share, which tq_attend_workspace covers); tq_attend_prepared runs the rest
+ * of tq_attend against the pack ws holds, from the last tq_attend_prepare
+ * with the same kp, segs and group on this workspace (other arguments as for
+ * tq_attend).  A prepare must not run while an attention that reads the same
+ * workspace is still in flight.  The result equals tq_attend's. */
+tq_status tq_attend_prepare(const tq_params* kp, const float* q, int segs, int group, void* ws,
+                            size_t ws_bytes, void* stream);
+tq_status tq_attend_prepared(const tq_params* kp, const tq_params* vp, int segs, int group,
+                             tq_cache keys, tq_cache vals, const int32_t* len, int64_t T,
+                             float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes tq_scores_topk needs. */
 size_t tq_scores_topk_workspace(const tq_params* kp, int nq, int64_t T, int k);
 

@@ -26,7 +26,7 @@ EXPORTED = (
     "tq_status_string", "tq_last_error", "tq_build_codebook", "tq_key_layout",
     "tq_value_layout", "tq_key_record_words", "tq_encode_prod", "tq_encode_mse", "tq_encode_mse_keys", "tq_encode_eden", "tq_encode_workspace", "tq_encode_prod_ws",
     "tq_scores_workspace",
-    "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_scores_topk_workspace", "tq_scores_topk",
+    "tq_scores", "tq_scores_prepare", "tq_scores_prepared", "tq_attend_workspace", "tq_attend", "tq_attend_prepare", "tq_attend_prepared", "tq_scores_topk_workspace", "tq_scores_topk",
     "tq_key_record_bytes", "tq_val_record_bytes", "tq_scores_noalloc", "tq_scores_noalloc_capacity",
     "tq_hadamard_matrix", "tq_build_polar_codebook", "tq_polar_record_words", "tq_polar_encode",
     "tq_polar_decode", "tq_polar_scores",
@@ -103,6 +103,9 @@ def lib():
         L.tq_attend_workspace.argtypes = [P, P, ci, ci, i64]
         L.tq_attend.argtypes = [P, P, vp, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
                                 vp, vp, sz, vp]
+        L.tq_attend_prepare.argtypes = [P, vp, ci, ci, vp, sz, vp]
+        L.tq_attend_prepared.argtypes = [P, P, ci, ci, tq_cache, tq_cache, vp, i64, ctypes.c_float,
+                                         vp, vp, sz, vp]
         L.tq_scores_noalloc.argtypes = [P, vp, ci, ci, tq_cache, vp, i64, vp, vp]
         L.tq_hadamard_matrix.argtypes = [vp, ci, ci, ci, vp, vp]
         L.tq_scores_noalloc_capacity.restype = sz
@@ -384,6 +387,19 @@ def attend(kp: Params, vp: Params, q, segs: int, group: int, keys: Cache, vals: 
     _check(lib().tq_attend(kp.c, vp.c, _ptr(q), segs, group, keys.c, vals.c, _ptr(length), int(T),
                            float(scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)))
+
+
+def attend_prepare(kp: Params, q, segs: int, group: int, ws, stream=None):
+    """tq_attend_prepare: the query pack of tq_attend into ws."""
+    _check(lib().tq_attend_prepare(kp.c, _ptr(q), segs, group, _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+def attend_prepared(kp: Params, vp: Params, segs: int, group: int, keys: Cache, vals: Cache, T: int,
+                    scale: float, out, ws, length=None, stream=None):
+    """tq_attend_prepared: tq_attend against the pack of the last attend_prepare on ws."""
+    _check(lib().tq_attend_prepared(kp.c, vp.c, segs, group, keys.c, vals.c, _ptr(length), int(T), float(scale),
+                                    _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def topk_workspace(kp: Params, nq: int, T: int, k: int) -> int:

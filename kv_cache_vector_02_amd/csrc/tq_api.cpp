@@ -468,39 +468,75 @@ size_t tq_attend_workspace(const tq_params* kp, const tq_params* vp, int segs, i
   return tq::attend128_workspace(segs * div, (group + div - 1) / div, T);
 }
 
-tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs, int group,
-                    tq_cache keys, tq_cache vals, const int32_t* len, int64_t T, float scale,
-                    float* out, void* ws, size_t ws_bytes, void* stream) {
-  tq::AttendArgs a;
+// tq_attend and its two halves.  ATT_PREPARE checks and fills the query side
+// only (vp, keys, vals, len, T, scale and out unused); ATT_PREPARED takes the
+// pack from ws (q unused).
+enum { ATT_FULL = 0, ATT_PREPARE = 1, ATT_PREPARED = 2 };
+
+static tq_status attend_args(int mode, const tq_params* kp, const tq_params* vp, const float* q, int segs,
+                             int group, tq_cache keys, tq_cache vals, const int32_t* len, int64_t T, float scale,
+                             float* out, void* ws, size_t ws_bytes, tq::AttendArgs* ap, bool* nothing) {
+  tq::AttendArgs& a = *ap;
   std::memset(&a, 0, sizeof(a));
+  *nothing = false;
+  const bool with_kv = mode != ATT_PREPARE;
   const bool qjl = kp && kp->s;     // no QJL matrix: MSE-only keys
   tq_status st = check_params(kp, qjl, &a.k.cb, true);
   if (st != TQ_OK) return st;
-  st = check_params(vp, false, &a.cb_v, true);
-  if (st != TQ_OK) return st;
-  if (segs < 0 || group < 1 || T < 0) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
-  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "scale must be finite");
-  if (segs == 0) return TQ_OK;
-  if (kp->d != 128 || kp->d_rot != 128 || vp->d != 128 || vp->d_rot != 128)
+  if (with_kv) {
+    st = check_params(vp, false, &a.cb_v, true);
+    if (st != TQ_OK) return st;
+  }
+  if (segs < 0 || group < 1 || (with_kv && T < 0)) return fail(TQ_ERR_INVALID_ARG, "need segs >= 0, group >= 1, T >= 0");
+  if (with_kv && !std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "scale must be finite");
+  if (segs == 0) {
+    *nothing = true;
+    return TQ_OK;
+  }
+  if (kp->d != 128 || kp->d_rot != 128 || (with_kv && (vp->d != 128 || vp->d_rot != 128)))
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports d = d_rot = 128 for keys and values");
-  if (kp->rot == TQ_ROT_HADAMARD2 || vp->rot == TQ_ROT_HADAMARD2)
+  if (kp->rot == TQ_ROT_HADAMARD2 || (with_kv && vp->rot == TQ_ROT_HADAMARD2))
     return fail(TQ_ERR_UNSUPPORTED, "at d_rot = 128 pass tq_hadamard_matrix's two-round matrix as a dense rotation");
   if (group > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_attend supports up to 16 query heads per segment");
-  if (qjl && kp->m != kp->d_rot && vp->bits < 2)
+  if (with_kv && qjl && kp->m != kp->d_rot && vp->bits < 2)
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend with m = d / 2 keys supports value bits 2..4");
-  if (!qjl && (kp->bits < 2 || vp->bits < 2))
+  if (!qjl && (kp->bits < 2 || (with_kv && vp->bits < 2)))
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend with MSE-only keys supports key and value bits 2..4");
   const int div = attend_head_split(kp, group);
   if (div == 2 && group % 2)
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend with 4-bit MSE-only keys supports up to 8, or an even number up "
                                     "to 16, query heads per segment");
-  if (!q || !keys.planes || !keys.scalars || !vals.planes || !vals.scalars || !out || !ws)
-    return fail(TQ_ERR_INVALID_ARG, "q, keys, vals, out and ws must be non-NULL");
+  if (mode != ATT_PREPARED && (!q || !aligned(q, 16))) return fail(TQ_ERR_INVALID_ARG, "q must be non-NULL and 16-byte aligned");
+  if (!ws || !aligned(ws, 256)) return fail(TQ_ERR_INVALID_ARG, "ws must be non-NULL and 256-byte aligned");
+  a.k.q = q;
+  a.k.segs = segs * div;
+  a.k.group = group / div;
+  a.kv_div = div;
+  a.k.n_sets = kp->n_sets;
+  a.k.set_div = (kp->set_div > 1 ? kp->set_div : 1) * div;   // sets follow the cache segment
+  a.k.d = kp->d;
+  a.k.pi = kp->pi;
+  a.k.eps = kp->eps;
+  a.k.rot = kp->rot;
+  a.k.s = kp->s;
+  a.k.m = qjl ? kp->m : 0;
+  a.k.bq = qjl ? kp->bits - 1 : kp->bits;
+  a.k.qjl = qjl;
+  a.k.ws = ws;
+  a.ws = ws;
+  a.prepared = mode == ATT_PREPARED;
+  if (!with_kv) {
+    const size_t need = tq::scores128_workspace(segs * div, group / div);
+    if (ws_bytes < need) return fail(TQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", ws_bytes, need);
+    return TQ_OK;
+  }
+  if (!keys.planes || !keys.scalars || !vals.planes || !vals.scalars || !out)
+    return fail(TQ_ERR_INVALID_ARG, "keys, vals and out must be non-NULL");
   if (vals.seg_stride % 32) return fail(TQ_ERR_INVALID_ARG, "vals.seg_stride must be a multiple of 32");
   if (segs > 1 && (keys.seg_stride < T || vals.seg_stride < T))
     return fail(TQ_ERR_INVALID_ARG, "seg_stride must be >= T for keys and values");
   if (!aligned(keys.planes, 16) || !aligned(keys.scalars, 4) || !aligned(vals.planes, 16) ||
-      !aligned(vals.scalars, 4) || !aligned(ws, 256) || !aligned(q, 16) || !aligned(out, 4))
+      !aligned(vals.scalars, 4) || !aligned(out, 4))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (q and planes 16 B, scalars 4 B, ws 256 B)");
   if (T == 0) return fail(TQ_ERR_INVALID_ARG, "T must be >= 1");
   const size_t need = tq::attend128_workspace(segs * div, group / div, T);
@@ -511,28 +547,13 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
     return fail(TQ_ERR_INVALID_ARG, "the keys or values read exceed keys.records / vals.records");
   if (kstride * 16 * kp->bits >= (1ll << 31) || vstride * 16 * vp->bits >= (1ll << 31))
     return fail(TQ_ERR_UNSUPPORTED, "tq_attend addresses at most 2 GiB of keys and of values per segment");
-  a.k.q = q;
-  a.k.segs = segs * div;
-  a.k.group = group / div;
-  a.kv_div = div;
-  a.k.n_sets = kp->n_sets;
-  a.k.set_div = (kp->set_div > 1 ? kp->set_div : 1) * div;   // sets follow the cache segment
   a.n_sets_v = vp->n_sets;
   a.set_div_v = vp->set_div;
-  a.k.d = kp->d;
-  a.k.pi = kp->pi;
-  a.k.eps = kp->eps;
-  a.k.rot = kp->rot;
-  a.k.s = kp->s;
-  a.k.m = qjl ? kp->m : 0;
-  a.k.bq = qjl ? kp->bits - 1 : kp->bits;
-  a.k.qjl = qjl;
   a.k.planes = (const uint32_t*)keys.planes;
   a.k.scalars = (const uint16_t*)keys.scalars;
   a.k.seg_stride = kstride;
   a.k.len = len;
   a.k.T = T;
-  a.k.ws = ws;
   a.pi_v = vp->pi;
   a.eps_v = vp->eps;
   a.rot_v = vp->rot;
@@ -542,7 +563,39 @@ tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, in
   a.seg_stride_v = vstride;
   a.scale = scale;
   a.out = out;
-  a.ws = ws;
+  return TQ_OK;
+}
+
+tq_status tq_attend(const tq_params* kp, const tq_params* vp, const float* q, int segs, int group,
+                    tq_cache keys, tq_cache vals, const int32_t* len, int64_t T, float scale,
+                    float* out, void* ws, size_t ws_bytes, void* stream) {
+  tq::AttendArgs a;
+  bool nothing;
+  tq_status st = attend_args(ATT_FULL, kp, vp, q, segs, group, keys, vals, len, T, scale, out, ws, ws_bytes, &a,
+                             &nothing);
+  if (st != TQ_OK || nothing) return st;
+  return hip_status(tq::launch_attend128(a, (hipStream_t)stream), "attend launch");
+}
+
+tq_status tq_attend_prepare(const tq_params* kp, const float* q, int segs, int group, void* ws, size_t ws_bytes,
+                            void* stream) {
+  tq::AttendArgs a;
+  bool nothing;
+  tq_cache none = {nullptr, nullptr, 0, 0};
+  tq_status st = attend_args(ATT_PREPARE, kp, nullptr, q, segs, group, none, none, nullptr, 0, 0.f, nullptr, ws,
+                             ws_bytes, &a, &nothing);
+  if (st != TQ_OK || nothing) return st;
+  return hip_status(tq::launch_attend128_prepare(a, (hipStream_t)stream), "attend prepare launch");
+}
+
+tq_status tq_attend_prepared(const tq_params* kp, const tq_params* vp, int segs, int group, tq_cache keys,
+                             tq_cache vals, const int32_t* len, int64_t T, float scale, float* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  tq::AttendArgs a;
+  bool nothing;
+  tq_status st = attend_args(ATT_PREPARED, kp, vp, nullptr, segs, group, keys, vals, len, T, scale, out, ws,
+                             ws_bytes, &a, &nothing);
+  if (st != TQ_OK || nothing) return st;
   return hip_status(tq::launch_attend128(a, (hipStream_t)stream), "attend launch");
 }
 

@@ -1743,9 +1743,13 @@ size_t attend128_workspace(int segs, int group, int64_t T) {
   return attend_pack_bytes(segs, group) + attend_part_bytes(segs, group, T);
 }
 
+hipError_t launch_attend128_prepare(const AttendArgs& a, hipStream_t stream) {
+  return launch_scores128_prep(a.k, 3, stream);
+}
+
 hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(a.ws);
-  hipError_t e = launch_scores128_prep(a.k, 3, stream);
+  hipError_t e = a.prepared ? hipSuccess : launch_scores128_prep(a.k, 3, stream);
   if (e != hipSuccess) return e;
   Attend128Args s;
   s.pack = ws;

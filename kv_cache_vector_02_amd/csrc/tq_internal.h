@@ -130,9 +130,12 @@ struct AttendArgs {
   void* ws;
   int kv_div;            // k.segs / cache segments: 2 when each segment's heads run as two halves
   int n_sets_v, set_div_v;   // rotation sets of the values (per cache segment)
+  int prepared;          // 1: ws already holds the query pack (tq_attend_prepare)
 };
 
 hipError_t launch_attend128(const AttendArgs& a, hipStream_t stream);
+// The attention query pack alone (the first of launch_attend128's launches).
+hipError_t launch_attend128_prepare(const AttendArgs& a, hipStream_t stream);
 size_t attend128_workspace(int segs, int group, int64_t T);
 
 // PolarQuant at d = 128 (levels 1..7).  The codebook tables travel in the

@@ -165,6 +165,34 @@ def test_many_segments_one_workgroup_each():
         check_heads(got[rows], oracle_attend(sk, sv, q[rows], kf, vidx, vn, sl, scale))
 
 
+@pytest.mark.parametrize("T_", [512, 1500])
+def test_prepare_then_prepared_equals_attend(T_):
+    # tq_attend_prepare on a second stream, then tq_attend_prepared twice on
+    # the pack (one workgroup per segment at T = 512, several at 1500): both
+    # equal tq_attend bit for bit
+    _log(f"attend prepare / prepared, T = {T_}")
+    Tt = torch()
+    segs, group = 3, 4
+    sk, sv = _setups(3, 3, seed=11)
+    xk = kv_tensor(1, segs, T_, 128, seed=11)[0].reshape(-1, 128)
+    xv = kv_tensor(1, segs, (T_ + 31) // 32 * 32, 128, seed=11, value=True)[0].reshape(-1, 128)
+    kc, _ = oracle_key_cache(sk, xk, seg_stride=T_)
+    vc, _, _ = oracle_value_cache(sv, xv, (T_ + 31) // 32 * 32)
+    q = Tt.from_numpy(gaussian_queries(segs * group, 128, seed=11)).cuda()
+    scale = 1 / np.sqrt(128)
+    ref = gpu_attend(sk, sv, q.cpu().numpy(), segs, group, kc, vc, T_, scale)
+    ws = Tt.zeros(tq.attend_workspace(sk.params, sv.params, segs, group, T_), dtype=Tt.uint8, device="cuda")
+    side = Tt.cuda.Stream()
+    side.wait_stream(Tt.cuda.current_stream())
+    tq.attend_prepare(sk.params, q, segs, group, ws, stream=side)
+    Tt.cuda.current_stream().wait_stream(side)
+    for _ in range(2):
+        out = Tt.full((segs * group, 128), float("nan"), dtype=Tt.float32, device="cuda")
+        tq.attend_prepared(sk.params, sv.params, segs, group, kc, vc, T_, scale, out, ws)
+        Tt.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_qwen_shaped_full_size():
     # 36 layers x 2 KV heads x 8192 tokens, 16 query heads per layer (G=8),
     # keys prod b=3, values mse b=3, one launch; every segment against the oracle

@@ -242,6 +242,38 @@ def test_decode_reads_are_bounded_by_the_cache_capacity():
                        None) == tq.TQ_ERR_INVALID_ARG
 
 
+def test_attend_halves_validate_on_the_host():
+    # tq_attend_prepare checks the query side only (q, ws and the pack's
+    # share of it); tq_attend_prepared checks everything tq_attend checks but
+    # q.  Fake pointers: every case fails before a launch.
+    L = tq.lib()
+    pk_ = _params(3)
+    pk_._c.pi, pk_._c.s = 0x10000, 0x20000
+    c, b = cb.lloyd_max(128, 3)
+    pv_ = tq.Params(d=128, bits=3, rot=tq.TQ_ROT_DENSE, centroids=c, boundaries=b)
+    pv_._c.pi = 0x10000
+    q, out, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x400000)
+    segs, G, T, stride = 4, 8, 1000, 1024
+    pack = L.tq_scores_workspace(pk_.c, segs, G)
+    assert L.tq_attend_prepare(pk_.c, None, segs, G, ws, pack, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_attend_prepare(pk_.c, ctypes.c_void_p(0x100004), segs, G, ws, pack, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_attend_prepare(pk_.c, q, segs, G, ctypes.c_void_p(0x400010), pack, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_attend_prepare(pk_.c, q, segs, G, ws, pack - 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert "workspace too small" in L.tq_last_error().decode()
+    assert L.tq_attend_prepare(pk_.c, q, segs, 17, ws, pack, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_attend_prepare(pk_.c, q, 0, G, ws, 0, None) == tq.TQ_OK          # nothing to do
+    wa = L.tq_attend_workspace(pk_.c, pv_.c, segs, G, T)
+    need = (segs - 1) * stride + T
+    keys = tq.tq_cache(0x2000, 0x3000, stride, need)
+    vals = tq.tq_cache(0x4000, 0x5000, stride, need - 1)
+    assert L.tq_attend_prepared(pk_.c, pv_.c, segs, G, keys, vals, None, T, ctypes.c_float(1.0), out, ws, wa,
+                                None) == tq.TQ_ERR_INVALID_ARG
+    assert "vals.records" in L.tq_last_error().decode()
+    vals = tq.tq_cache(0x4000, 0x5000, stride, need)
+    assert L.tq_attend_prepared(pk_.c, pv_.c, segs, G, keys, vals, None, T, ctypes.c_float(1.0), out, ws, wa - 1,
+                                None) == tq.TQ_ERR_INVALID_ARG
+
+
 def test_scores_wait_bound_must_be_nonnegative():
     L = tq.lib()
     pk_ = _params(3)
