@@ -136,12 +136,22 @@ __device__ __forceinline__ uint32_t pack4(int b0, int b1, int b2, int b3) {
          ((uint32_t)b3 << 24);
 }
 
+// The one-launch scores' hand-over words of one segment (their protocol is
+// described with the hand-over helpers below).
+struct ScoreSync {
+  uint64_t flag;
+  uint64_t claim;
+  uint64_t done;
+  uint64_t pad;
+};
+
 struct PrepLds {
   float qr[MAXG * QTS];      // q_rot[head][coordinate]
   float qp[MAXG * QTS];      // q_proj[head][coordinate]
   float part[8][MAXG][4];
   float stat[MAXG][4];
   float wsc[9][MAXG];        // weight scale per (plane, head); row 8 is the QJL plane
+  int own;                   // the claim was taken (one-launch producer)
 };
 
 // Segment seg's query pack -> dst (all 512 threads of the workgroup); S is the
@@ -150,8 +160,14 @@ struct PrepLds {
 // of other XCDs).
 // MW: QJL sign words per key (m / 32); with MW = 2 the QJL rows past 64 are
 // zero, so the pack's QJL weights for coordinate groups 2 and 3 vanish.
+// With cs (the one-launch producer of segment seg, ns = 1): the claim is
+// exchanged at the start, its answer needed only before the first pack store
+// (false: a consumer holds it and builds; nothing is stored), and the pack's
+// zero count under this launch's tag is stored with the pack.  Returns
+// whether the pack was written.
 template <bool HAD, int S, int CPOL = 0, bool QJL = true, int MW = 4>
-__device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, int ns, PrepLds& L, uint8_t* dst) {
+__device__ __forceinline__ bool prep_pack(const PrepArgs& a, int seg, int ns, PrepLds& L, uint8_t* dst,
+                                          ScoreSync* cs = nullptr, uint64_t ticket = 0) {
   float* qr = L.qr;
   float* qp = L.qp;
   auto& part = L.part;
@@ -171,6 +187,8 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, int ns, Pr
   const float* set_s = a.s ? a.s + (size_t)set * a.m_rows * D : nullptr;
   const int row = 16 * wave + col;        // A-operand row of this lane
   static_assert(MAXG * 32 == PREP_THREADS, "one float4 of the query heads per thread");
+  uint64_t prev = 0;
+  if (cs && t == 0) prev = __hip_atomic_exchange(&cs->claim, ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- every global operand in flight together: the segment's query heads
   // once per workgroup (one float4 per thread, for the LDS), this lane's rows
@@ -303,7 +321,10 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, int ns, Pr
     for (int p = 0; p < 8; ++p) L.wsc[p][t] = 2.f * a.u[p] / sm;
     L.wsc[8][t] = 2.f / sq;
   }
+  if (cs && t == 0) L.own = prev != ticket;
   __syncthreads();
+  if (cs && !L.own) return false;
+  if (cs && t == 0) __hip_atomic_store(&cs->done, ticket << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // ---- quantise: one item = (tile mt, fragment f = 2 p + m, lane group kg,
   // head hl of the tile) covers the 16 coordinates 32 kg + 8 bi + 4 m + k
   // (bi, k = 0..3), byte bi of dword k of the A operand of lanes
@@ -358,6 +379,7 @@ __device__ __forceinline__ void prep_pack(const PrepArgs& a, int seg, int ns, Pr
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, t < G * 4 ? stat[j * G + (t >> 2)][t & 3] : 0.f),
                                           rdst, (uint32_t)(fbytes + 4 * t), 0, CPOL);
   }
+  return true;
 }
 
 // (at most two waves per SIMD: the register budget keeps every operand load
@@ -385,20 +407,19 @@ void prep_queries128(PrepArgs a) {
 //          publishes the flag, then one add per consumer at its end; the last
 //          of the segment's active consumers clears all three words, so a
 //          replayed launch (a captured graph keeps its ticket) finds them clear
-// The producer claims and builds.  A consumer waits a bounded time for the
-// flag (the producer may not be resident yet); if it has not come, it claims
-// the pack itself and builds it, or, if another workgroup holds the claim
-// (a running workgroup, which will publish), waits for the flag.  The pack
-// and the words travel with device-coherent (sc1) accesses and relaxed
+// The producer issues its claim exchange with its operand loads and reads the
+// answer only before its first pack store, so the exchange adds no round trip
+// to its chain; the tagged zero count goes out with the pack stores, and one
+// wait for all of them precedes the flag.  A consumer waits a bounded time for
+// the flag (the producer may not be resident yet); if it has not come, it
+// claims the pack itself and builds it, or, if another workgroup holds the
+// claim (a running workgroup, which will publish), waits for the flag.  The
+// pack and the words travel with device-coherent (sc1) accesses and relaxed
 // device-scope atomics, each store waited for before the flag: no L2 writeback
 // or invalidate is needed, since no other data is shared within the launch.
-// The words may hold anything before a workspace's first call.
-struct ScoreSync {
-  uint64_t flag;
-  uint64_t claim;
-  uint64_t done;
-  uint64_t pad;
-};
+// The words may hold anything before a workspace's first call.  (ScoreSync,
+// the four words of a segment, is defined above prep_pack, which takes the
+// producer's claim.)
 
 // Waits at most `ticks` of the 100 MHz constant clock (0: not at all; < 0:
 // without bound).
@@ -562,15 +583,13 @@ void scores128(Score128Args a) {
       // consumer that gave up waiting holds the claim, the pack with
       // device-coherent stores, every store complete, then the flag
       if (active_chunks(b) == 0) return;
-      int* mine = reinterpret_cast<int*>(smem + SMEM);
-      if (threadIdx.x == 0) *mine = take_claim(&a.sync[b], a.ticket) ? 1 : 0;
-      __syncthreads();
-      if (*mine) {
-        prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, b, 1, *reinterpret_cast<PrepLds*>(smem),
-                                             a.prep.ws + (size_t)b * pack_bytes(MT, F));
+      if (prep_pack<HAD, S, CPOL_SC1, QJL, MW>(a.prep, b, 1, *reinterpret_cast<PrepLds*>(smem),
+                                               a.prep.ws + (size_t)b * pack_bytes(MT, F), &a.sync[b], a.ticket)) {
+        // the pack and the tagged count complete, then the flag
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x == 0) publish(&a.sync[b], a.ticket);
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&a.sync[b].flag, a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       return;
     }
