@@ -117,7 +117,8 @@ def burst_timer(torch, ev, burst, rounds=5):
 
 def stream_ceiling(torch, tq, ev, read_bytes, write_bytes):
     """The best GB/s of tq_testing_stream with the given read/write sizes over
-    grids of 4 to 128 workgroups per compute unit and both store policies,
+    grids of 4 to 128 workgroups per compute unit, both store policies and
+    both load policies (default and non-temporal),
     on two buffer sets past the Infinity Cache: the attainable bandwidth of a
     plain stream with that mix.  Returns (GB/s, the settings that gave it)."""
     rb = (read_bytes + 15) // 16 * 16
@@ -128,11 +129,12 @@ def stream_ceiling(torch, tq, ev, read_bytes, write_bytes):
     best = (0.0, None)
     timed = burst_timer(torch, ev, 8)
     for per_cu in (4, 8, 16, 32, 64, 128):
-        for pol in (0, 1):
+        for pol in (0, 1, 2, 3):
             t = timed(lambda i: tq.testing_stream(srcs[i % 2], rb, dsts[i % 2], wb, pol, per_cu * cus))
             gbs = (rb + wb) / (t * 1e-3) / 1e9
             if gbs > best[0]:
-                best = (gbs, {"workgroups_per_cu": per_cu, "sc1_stores": bool(pol), "ms": round(t, 5)})
+                best = (gbs, {"workgroups_per_cu": per_cu, "sc1_stores": bool(pol & 1),
+                              "nontemporal_loads": bool(pol & 2), "ms": round(t, 5)})
     del srcs, dsts
     torch.cuda.empty_cache()
     return round(best[0], 1), best[1]

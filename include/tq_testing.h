@@ -24,8 +24,10 @@ extern "C" {
  * kernel uses.  This is the attainable-bandwidth ceiling for a kernel with the
  * same read/write mix.
  *   src, dst       device, 16-byte aligned; sizes multiples of 16, each < 2 GiB
- *   store_policy   0: default write-back stores; 1: device-coherent (sc1)
- *                  stores, the score kernel's policy
+ *   store_policy   bit 0 set: device-coherent (sc1) stores, else default
+ *                  write-back stores; bit 1 set: non-temporal loads, else
+ *                  default loads (the score kernel's policy is 3: sc1 stores,
+ *                  non-temporal key loads)
  *   workgroups     grid size (256 threads each), or 0 for 4 per compute unit
  * The bytes written are a function of the bytes read (so no load can be
  * dropped); their values carry no meaning.

@@ -80,19 +80,23 @@ __device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
   return b <= 0 ? 0u : (b >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)b);
 }
 
-template <int P>
+// Cache-policy bits of a buffer access (the aux operand): CPOL_NT marks a
+// non-temporal (streaming) access, for data read once.
+constexpr int CPOL_NT = 2;
+
+template <int P, int CPOL = 0>
 __device__ __forceinline__ typename Words<P>::v load_words(rsrc_t r, uint32_t voff) {
   typedef typename Words<P>::v wv;
   if constexpr (P == 1) {
     wv w;
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, CPOL);
     return w;
   } else if constexpr (P == 2) {
-    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, CPOL));
   } else if constexpr (P == 3) {
-    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, 0));
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b96(r, voff, 0, CPOL));
   } else {
-    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    return __builtin_bit_cast(wv, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, CPOL));
   }
 }
 

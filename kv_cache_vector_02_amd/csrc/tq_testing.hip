@@ -2,7 +2,7 @@
 // the method.  tq_testing_stream is the attainable-bandwidth yardstick the
 // score pass is compared with: a plain stream that reads and writes HBM in a
 // given ratio with the same 16-byte-per-lane buffer accesses and the same
-// store cache policy, and no arithmetic.
+// load and store cache policies, and no arithmetic.
 #include <atomic>
 
 #include "tq_device.h"
@@ -20,6 +20,7 @@ constexpr int ST_UNROLL = 8;      // 4 KB chunks in flight per workgroup
 // reads ST_UNROLL chunks at a time and, after each batch, writes as many chunks
 // as keep its write slice in step with its read slice, so both streams run
 // side by side for the whole kernel.  The written value depends on the loads.
+template <int LOAD_CPOL>
 __global__ __launch_bounds__(ST_THREADS) void stream_kernel(const uint8_t* src, uint32_t nr, uint8_t* dst,
                                                             uint32_t nw, int cpol) {
   const uint32_t G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(ST_THREADS) void stream_kernel(const uint8_t* src, 
     for (int u = 0; u < ST_UNROLL; ++u) {
       const uint32_t item = (c0 + u) * ST_THREADS + t;
       v[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rs, c0 + u < r1 && item < nr ? item * 16u : OOB_OFFSET, 0, 0));
+                                           rs, c0 + u < r1 && item < nr ? item * 16u : OOB_OFFSET, 0, LOAD_CPOL));
     }
 #pragma unroll
     for (int u = 0; u < ST_UNROLL; ++u) acc ^= v[u];
@@ -65,14 +66,19 @@ extern "C" tq_status tq_testing_stream(const void* src, size_t read_bytes, void*
   if (read_bytes % 16 || write_bytes % 16 || ((uintptr_t)src % 16) || ((uintptr_t)dst % 16))
     return TQ_ERR_INVALID_ARG;
   if (read_bytes >= (1ull << 31) || write_bytes >= (1ull << 31)) return TQ_ERR_UNSUPPORTED;
-  if (store_policy != 0 && store_policy != 1) return TQ_ERR_INVALID_ARG;
+  if (store_policy < 0 || store_policy > 3) return TQ_ERR_INVALID_ARG;
   if (read_bytes == 0 && write_bytes == 0) return TQ_OK;
   int cus = 256, dev = 0;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int blocks = workgroups > 0 ? workgroups : 4 * cus;
   // with no reads every thread writes its share in the leftover loop
-  hipLaunchKernelGGL(tq::stream_kernel, dim3(blocks), dim3(tq::ST_THREADS), 0, (hipStream_t)stream,
-                     static_cast<const uint8_t*>(src), (uint32_t)(read_bytes / 16), static_cast<uint8_t*>(dst),
-                     (uint32_t)(write_bytes / 16), store_policy);
+  if (store_policy & 2)
+    hipLaunchKernelGGL(tq::stream_kernel<tq::CPOL_NT>, dim3(blocks), dim3(tq::ST_THREADS), 0, (hipStream_t)stream,
+                       static_cast<const uint8_t*>(src), (uint32_t)(read_bytes / 16), static_cast<uint8_t*>(dst),
+                       (uint32_t)(write_bytes / 16), store_policy & 1);
+  else
+    hipLaunchKernelGGL(tq::stream_kernel<0>, dim3(blocks), dim3(tq::ST_THREADS), 0, (hipStream_t)stream,
+                       static_cast<const uint8_t*>(src), (uint32_t)(read_bytes / 16), static_cast<uint8_t*>(dst),
+                       (uint32_t)(write_bytes / 16), store_policy & 1);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

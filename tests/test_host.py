@@ -284,6 +284,17 @@ def test_scores_wait_bound_must_be_nonnegative():
     assert st == tq.TQ_ERR_INVALID_ARG
 
 
+def test_stream_policy_is_validated_without_launch():
+    # bit 0: sc1 stores, bit 1: non-temporal loads; anything else is rejected
+    # before the launch (fake device addresses: nothing is dereferenced)
+    L = tq.lib()
+    src, dst = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    for bad in (-1, 4, 7):
+        assert L.tq_testing_stream(src, 4096, dst, 1024, bad, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_testing_stream(src, 4095, dst, 1024, 3, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_testing_stream(src, 0, dst, 0, 3, 0, None) == tq.TQ_OK
+
+
 # ---- PolarQuant (tq_polar_*) ----
 
 from oracle import packing as pk  # noqa: E402
