@@ -283,10 +283,14 @@ size_t tq_scores_workspace(const tq_params* kp, int segs, int group);
  * ws      device workspace of at least tq_scores_workspace() bytes, 256-B
  *         aligned, no initial contents required; it receives each segment's
  *         query pack (rotated and projected query heads quantised to the
- *         matrix-core operand) and two hand-over words per segment, so one
+ *         matrix-core operand) and four hand-over words per segment, so one
  *         call in flight per workspace.
- * One launch on the stream: per segment, the first workgroup builds the query
- * pack while the others already stream their first keys; they take the pack
+ * One launch on the stream when the pass fits in one dispatch of the device's
+ * 8-wave workgroups (one per 2048 tokens of each segment); a longer pass runs
+ * as two launches on the stream, the query packs and then the pass, and leaves
+ * the hand-over words untouched.  In the one launch, per segment, the first
+ * workgroup builds the query pack while the others already stream their first
+ * keys; they take the pack
  * when its builder publishes a per-call ticket in the workspace.  The pack and
  * the ticket words are written and read with device-coherent (sc1) accesses
  * and relaxed device-scope atomics, so no cache flush is needed.  A workgroup

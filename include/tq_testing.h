@@ -40,6 +40,7 @@ tq_status tq_testing_stream(const void* src, size_t read_bytes, void* dst, size_
  * given in microseconds instead of 200: 0 makes every consumer workgroup that
  * does not find the pack published at once claim it or wait for its
  * claimant, the path tq_scores takes when a producer is not yet resident.
+ * It always takes the one-launch form, whatever the pass's length.
  * Results are the same bytes as tq_scores.  Other arguments and errors as for
  * tq_scores; wait_us < 0 gives TQ_ERR_INVALID_ARG. */
 tq_status tq_testing_scores_wait(const tq_params* kp, const float* q, int segs, int group, tq_cache keys,

@@ -409,6 +409,7 @@ tq_status tq_testing_scores_wait(const tq_params* kp, const float* q, int segs, 
   tq_status st = score_args(kp, q, true, segs, group, keys, true, len, T, scores, true, ws, ws_bytes, &a, &nothing);
   if (st != TQ_OK || nothing) return st;
   a.wait_us = wait_us;
+  a.one_launch = 1;
   return hip_status(tq::launch_scores128(a, (hipStream_t)stream), "scores launch");
 }
 

@@ -474,6 +474,7 @@ struct Score128Args {
   ScoreSync* sync;   // [segs]
   uint64_t ticket;
   long long wait_ticks;   // consumers' bound on the wait for the pack
+  int one_launch;         // keep the one-launch form for a long pass
 };
 
 __device__ __forceinline__ void expand8(uint32_t w, uint32_t e[8]) {
@@ -535,7 +536,8 @@ __device__ __forceinline__ uint32_t plane_word(W w, int p) {
 // with RING pairs of loads in flight; the 32 x 8 outputs of a 16-row tile
 // pass through a per-wave LDS tile so that each lane stores 4 consecutive
 // tokens of one head (16 bytes) and a store covers whole 128-byte lines.
-constexpr int SC_WAVES = 8;
+constexpr int SC_WAVES = 8;     // waves per workgroup of the one-launch form (and of short passes)
+constexpr int PASS_WAVES = 4;   // waves per workgroup of a long score pass
 
 // FUSED: the one-launch form (1-D grid: segs producers, then segs x chunks
 // consumers); HAD selects the producer's rotation.  QJL: prod keys (BQ index
@@ -546,9 +548,10 @@ constexpr int SC_WAVES = 8;
 // that end with the group's last index word (the first is the previous
 // group's last word) and rotate them into place; the sign slot then holds
 // that foreign word, and the pack's QJL weights for these groups are zero.
-template <int BQ, int MT, int S, bool FUSED, bool HAD, bool QJL, int MW = 4>
-__global__ __launch_bounds__(SC_WAVES * 64) __attribute__((amdgpu_waves_per_eu(FUSED && MT == 1 ? 4 : 1)))
+template <int BQ, int MT, int S, bool FUSED, bool HAD, bool QJL, int MW = 4, int NWV = SC_WAVES>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(FUSED && MT == 1 ? 4 : 1)))
 void scores128(Score128Args a) {
+  static_assert(!FUSED || NWV == SC_WAVES, "the one-launch producers build the pack with 8 waves");
   constexpr int NP = mse_planes(BQ);      // Walsh planes of the index bits
   constexpr int F = 2 * (NP + QJL);       // MFMAs per tile per 16-row tile
   constexpr int P = BQ + QJL;             // planes per coordinate group (words a lane loads)
@@ -559,7 +562,7 @@ void scores128(Score128Args a) {
   constexpr int HL = S == 2 ? 2 : 1;      // heads per lane group per 16-row tile
   constexpr int NH = MT * 4 * HL;         // heads covered by the tiles
   typedef typename Words<P>::v wvec;
-  constexpr int SBUF = SC_WAVES * NH * SROW;                    // floats of the output tiles
+  constexpr int SBUF = NWV * NH * SROW;                    // floats of the output tiles
   constexpr int PREPF = (int)((sizeof(PrepLds) + 15) / 16 * 4);   // floats of the producer's scratch
   constexpr int PACKF = (int)(pack_bytes(MT, F) / 4);                  // floats of one query pack
   constexpr int SMEM0 = FUSED && PREPF > SBUF ? PREPF : SBUF;
@@ -632,11 +635,11 @@ void scores128(Score128Args a) {
     }
   };
   const uint8_t* pack = a.ws + (size_t)seg * pack_bytes(MT, F);
-  const int mine = npairs > wave ? (npairs - wave + SC_WAVES - 1) / SC_WAVES : 0;
+  const int mine = npairs > wave ? (npairs - wave + NWV - 1) / NWV : 0;
   // the first round's keys go out before the pack is read (pairs past the
   // span read zeros without memory traffic)
 #pragma unroll
-  for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * j);
+  for (int j = 0; j < RING; ++j) load_pair(j, wave + NWV * j);
   if constexpr (FUSED) {
     // 0: the pack is published; 1: this workgroup holds the claim and builds it
     int* build = reinterpret_cast<int*>(smem + SMEM);
@@ -660,7 +663,7 @@ void scores128(Score128Args a) {
       __syncthreads();
       if (threadIdx.x == 0) publish(&a.sync[seg], a.ticket);
 #pragma unroll
-      for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * j);
+      for (int j = 0; j < RING; ++j) load_pair(j, wave + NWV * j);
     }
   }
 
@@ -671,7 +674,7 @@ void scores128(Score128Args a) {
   const rsrc_t rp = make_rsrc(pack, (uint32_t)pack_bytes(MT, F));
   const uint8_t* lpack = reinterpret_cast<const uint8_t*>(smem);
   if constexpr (FUSED) {
-    for (int u = threadIdx.x; u < PACKF / 4; u += SC_WAVES * 64)
+    for (int u = threadIdx.x; u < PACKF / 4; u += NWV * 64)
       reinterpret_cast<i32x4*>(smem)[u] =
           __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)(16 * u), 0, CPOL_SC1));
     __syncthreads();
@@ -784,15 +787,15 @@ void scores128(Score128Args a) {
   for (int r0 = 0; r0 < mine; r0 += ROUND) {
     if (r0 > 0) {
 #pragma unroll
-      for (int j = 0; j < RING; ++j) load_pair(j, wave + SC_WAVES * (r0 + j));
+      for (int j = 0; j < RING; ++j) load_pair(j, wave + NWV * (r0 + j));
     }
 #pragma unroll
     for (int j = 0; j < ROUND; ++j) {
       if (r0 + j >= mine) break;
-      const int pr = wave + SC_WAVES * (r0 + j);
+      const int pr = wave + NWV * (r0 + j);
       compute(wr[j % RING][0], sr[j % RING][0], 0);
       compute(wr[j % RING][1], sr[j % RING][1], 16);
-      if (j + RING < ROUND) load_pair(j % RING, pr + SC_WAVES * RING);
+      if (j + RING < ROUND) load_pair(j % RING, pr + NWV * RING);
       flush(32 * pr);
     }
   }
@@ -807,35 +810,68 @@ int64_t split_span(int segs, int64_t T, int resident, int64_t gran, int64_t kmax
 
 // Workgroups of the score pass: enough to fill the device once, and more when
 // a segment is long, so that no workgroup takes more than one straight-line
-// round of its waves (PASS_SPAN tokens).  Many short workgroups keep every
-// channel busy to the end of the pass: at 32 layers x 8 heads x 32768 tokens,
-// 16 per segment ran 14% faster than the 2 that fill the device once, and
-// matched a plain stream with the same read/write mix.
+// round of its waves (pspan tokens: 8 pairs of 32 tokens per wave).  Many
+// short workgroups keep every channel busy to the end of the pass: at 32
+// layers x 8 heads x 32768 tokens, 16 8-wave workgroups per segment ran 14%
+// faster than the 2 that fill the device once.
 constexpr int64_t PASS_SPAN = (int64_t)SC_WAVES * 8 * 32;   // 8 waves x 8 pairs x 32 tokens
-int pass_workgroups(int resident, int segs, int64_t T) {
-  const int64_t by_len = (int64_t)segs * ((T + PASS_SPAN - 1) / PASS_SPAN);
+int pass_workgroups(int resident, int segs, int64_t T, int64_t pspan = PASS_SPAN) {
+  const int64_t by_len = (int64_t)segs * ((T + pspan - 1) / pspan);
   return (int)std::min<int64_t>(std::max<int64_t>(resident, by_len), 1ll << 30);
 }
 
 // Grid: (workgroups per segment, segments); a workgroup's span is a multiple
-// of 8 waves x 32 tokens.
-template <int BQ, int MT, int S, bool QJL = true, int MW = 4>
-hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
+// of its waves x 32 tokens.  A pass that takes more than one dispatch of
+// 8-wave workgroups runs 4-wave workgroups with the same work per wave: at 92
+// VGPRs a SIMD holds 5 waves, of which 8-wave workgroups use 4 (32 layers x 8
+// heads x 32768 tokens: 87-89 us against 93-95 us); a shorter pass keeps the
+// 8-wave form, whose workgroups fill the device once with longer spans
+// (72 segments x 8192 tokens: 11.6 us against 12.3 us).
+template <int BQ, int MT, int S, bool QJL, int MW, int NW>
+hipError_t launch_scores_waves(Score128Args& s, int segs, hipStream_t stream) {
   static const int nb =
-      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false, QJL, MW>), SC_WAVES * 64);
-  const int64_t span = split_span(segs, s.T, pass_workgroups(nb * device_cus(), segs, s.T), 32 * SC_WAVES,
-                                  (s.T + 255) / 256);
+      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false, QJL, MW, NW>), NW * 64);
+  const int64_t span = split_span(segs, s.T, pass_workgroups(nb * device_cus(), segs, s.T, (int64_t)NW * 8 * 32),
+                                  32 * NW, (s.T + 255) / 256);
   s.chunk_tiles = (int)(span / 16);
   const int64_t chunks = (s.T + span - 1) / span;
-  hipLaunchKernelGGL((scores128<BQ, MT, S, false, false, QJL, MW>), dim3((unsigned)chunks, (unsigned)segs),
-                     dim3(SC_WAVES * 64), 0, stream, s);
+  hipLaunchKernelGGL((scores128<BQ, MT, S, false, false, QJL, MW, NW>), dim3((unsigned)chunks, (unsigned)segs),
+                     dim3(NW * 64), 0, stream, s);
   return hipGetLastError();
+}
+
+// True when the pass takes more than one dispatch of 8-wave workgroups.
+template <int BQ, int MT, int S, bool QJL, int MW>
+bool long_pass(int segs, int64_t T) {
+  static const int nb8 =
+      occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, false, false, QJL, MW, SC_WAVES>), SC_WAVES * 64);
+  const int64_t by_len = (int64_t)segs * ((T + PASS_SPAN - 1) / PASS_SPAN);
+  return by_len > (int64_t)nb8 * device_cus();
+}
+
+template <int BQ, int MT, int S, bool QJL = true, int MW = 4>
+hipError_t launch_scores(Score128Args& s, int segs, hipStream_t stream) {
+  if (long_pass<BQ, MT, S, QJL, MW>(segs, s.T)) return launch_scores_waves<BQ, MT, S, QJL, MW, PASS_WAVES>(s, segs, stream);
+  return launch_scores_waves<BQ, MT, S, QJL, MW, SC_WAVES>(s, segs, stream);
 }
 
 // One-launch form: the producers take one resident slot per segment, the
 // consumers split the tokens over the rest.
+// A long pass runs as two launches instead, the query packs and then the
+// pass: its 4-wave pass kernel outruns the one-launch form by more than the
+// packs' own launch costs (32 layers x 8 heads x 32768 tokens: 97-99 us
+// against 106-108 us per call), while a short pass keeps the one launch.
 template <int BQ, int MT, int S, bool HAD, bool QJL = true, int MW = 4>
 hipError_t launch_scores_fused(Score128Args& s, int segs, hipStream_t stream) {
+  if (!s.one_launch && long_pass<BQ, MT, S, QJL, MW>(segs, s.T)) {
+    PrepArgs p = s.prep;
+    p.seg_per_wg = p.n_sets > 1 ? 1 : MAXG / (p.group > 0 ? p.group : 1);
+    hipLaunchKernelGGL((prep_queries128<HAD, S, QJL, MW>), dim3((unsigned)((segs + p.seg_per_wg - 1) / p.seg_per_wg)),
+                       dim3(PREP_THREADS), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_scores<BQ, MT, S, QJL, MW>(s, segs, stream);
+  }
   static const int nb =
       occupancy(reinterpret_cast<const void*>(&scores128<BQ, MT, S, true, HAD, QJL, MW>), SC_WAVES * 64);
   const int resident = nb * device_cus() - segs;
@@ -1039,6 +1075,7 @@ hipError_t launch_scores128(const ScoreArgs& a, hipStream_t stream) {
   s.sync = reinterpret_cast<ScoreSync*>(static_cast<uint8_t*>(a.ws) + scores128_pack_region(a.segs, a.group));
   s.ticket = call_ticket();
   s.wait_ticks = 100LL * (a.wait_us < 0 ? 0 : a.wait_us);   // 100 MHz clock
+  s.one_launch = a.one_launch;
   const bool had = a.rot == TQ_ROT_HADAMARD;
   if (a.qjl && a.m == D / 2) {
     // prod keys with m = d / 2 QJL rows

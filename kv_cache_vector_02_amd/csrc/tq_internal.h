@@ -99,6 +99,7 @@ struct ScoreArgs {
   float* scores;
   void* ws;
   int wait_us;           // one-launch scores: consumers' bound on the wait for the pack (microseconds)
+  int one_launch = 0;    // tq_scores: keep the one-launch form for a long pass too (test control)
   int n_sets, set_div;   // rotation sets of the keys: query segment seg uses set (seg / set_div) % n_sets
 };
 

@@ -247,6 +247,29 @@ def test_one_launch_pack_claimed_by_a_consumer(wait_us):
     check_rows(base, _oracle_rows(st, q, fields, segs, G, T_))
 
 
+def test_long_pass_two_launches_match_one_launch():
+    # 80 segments x 24576 tokens: more 2048-token spans (960) than one dispatch
+    # of the pass's 8-wave workgroups holds, so tq_scores runs the query packs
+    # and a 4-wave pass as two launches; the one-launch form (forced by the
+    # testing entry) gives the same bytes, and every token of every segment
+    # matches the oracle on oracle-packed keys
+    _log("scores: long pass as two launches (80 x 24576 tokens)")
+    Tt = torch()
+    segs, T_, G = 80, 24576, 4
+    st = Setup(bits=3, prod=True, seed=16)
+    x = kv_tensor(1, segs, T_, 128, seed=16)[0].reshape(-1, 128)
+    cache, fields = oracle_key_cache(st, x, seg_stride=T_)
+    q = gaussian_queries(segs * G, 128, seed=16)
+    got = gpu_scores(st, q, segs, G, cache, T_)
+    qd = Tt.from_numpy(q).cuda()
+    ws = tq.alloc_workspace(tq.scores_workspace(st.params, segs, G))
+    out = Tt.full((segs * G, T_), float("nan"), dtype=Tt.float32, device="cuda")
+    tq.testing_scores_wait(st.params, qd, segs, G, cache, T_, out, ws, 200)
+    Tt.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), got)
+    check_rows(got, _oracle_rows(st, q, fields, segs, G, T_))
+
+
 def test_one_launch_graph_replays_see_new_queries():
     # a captured tq_scores replayed with new query values between replays (the
     # same launch, so the same ticket): each replay must use its own pack
