@@ -914,7 +914,7 @@ def main():
         "config": {
             "workload": "llama-3.1-8b-shaped kv cache: 32 layers x 8 kv heads x 32768 tokens x 128, fp16; keys prod "
                         "b=3, values mse b=3, dense rotation; batch 1, 32 query heads per layer (gqa 4); value = "
-                        "the tq_scores call (query prep + score pass, one launch over all 256 segments)",
+                        "the tq_scores call (query packs + score pass over all 256 segments; at this length two launches)",
             "tokens": LT, "layers": LL, "kv_heads": LH, "head_dim": D_, "query_heads_per_kv_head": LG,
             "bits": BITS,
         },
