@@ -48,8 +48,8 @@ INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 matrix peak (the retrieval score GE
 # rocprofv3 (FETCH_SIZE and WRITE_SIZE, each in its own run) and scaled by the
 # factor the same counters give for a plain device copy of known size
 # (bench.py --copy-calibration).  Valid only for the decode source measured.
-SCORE_TRAFFIC = {"tq_decode.hip sha256": "43b15f31d24edda2e5927e7957536374fc3fad26df441da03bb56ebe13ca889a",
-                 "bytes_per_launch": 583427185}
+SCORE_TRAFFIC = {"tq_decode.hip sha256": "6c53085345e8e1eacf29ad8e8fbcd4889f7571ae4b2ab06dadedc4eaf88cf5d1",
+                 "bytes_per_launch": 583437834}
 
 D_ = 128
 # Llama-3.1-8B-shaped cache (the headline)
