@@ -15,7 +15,7 @@ from oracle import estimator as est
 from oracle import packing as pk
 from tests.gpu_util import Setup, compare_encode, torch
 from tests.test_gpu_attend import check_heads, gpu_attend, oracle_value_cache
-from tests.test_gpu_scores import check_rows, gpu_scores, oracle_key_cache
+from tests.test_gpu_scores import check_ragged, check_rows, gpu_scores, long_pass_lengths, oracle_key_cache
 from tq_inputs import gaussian_queries, kv_tensor, tiny_vectors
 
 pytestmark = pytest.mark.gpu
@@ -169,3 +169,23 @@ def test_qwen_shaped_full_size():
         ref = est.prod_scores(q[rows], idx[sl], z[sl], n[sl], g[sl], st.rot, st.s, st.c32)
         worst = max(worst, check_rows(got[rows], ref))
     _log(f"  worst rel {worst:.2e}")
+
+
+def test_long_pass_ragged_lengths():
+    # prod b = 3 keys with m = 64 QJL rows through the 4-wave pass of a long
+    # call (80 segments x 24576 tokens, G = 4) with ragged lengths, every valid
+    # token against the oracle
+    _log("m=64 scores: long pass, ragged lengths (80 x 24576 tokens)")
+    segs, T_, G = 80, 24576, 4
+    x = kv_tensor(1, segs, T_, 128, seed=19)[0].reshape(-1, 128)
+    st = Setup(bits=3, seed=19, m=64)
+    cache, (idx, z, n, g) = oracle_key_cache(st, x, seg_stride=T_)
+    q = gaussian_queries(segs * G, 128, seed=19)
+    ln = long_pass_lengths(segs, T_, 19)
+    got = gpu_scores(st, q, segs, G, cache, T_, length=ln)
+    ref = np.empty((segs * G, T_))
+    for s in range(segs):
+        sl = slice(s * T_, (s + 1) * T_)
+        rows = slice(s * G, (s + 1) * G)
+        ref[rows] = est.prod_scores(q[rows], idx[sl], z[sl], n[sl], g[sl], st.rot, st.s, st.c32)
+    _log(f"  worst rel {check_ragged(got, ref, ln, G):.2e}")

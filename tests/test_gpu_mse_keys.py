@@ -18,7 +18,7 @@ from oracle import estimator as est
 from oracle import packing as pk
 from tests.gpu_util import Setup, compare_encode, torch
 from tests.test_gpu_attend import check_heads, gpu_attend, oracle_value_cache
-from tests.test_gpu_scores import check_rows, gpu_scores
+from tests.test_gpu_scores import check_ragged, check_rows, gpu_scores, long_pass_lengths
 from tq_inputs import gaussian_queries, kv_tensor, tiny_vectors
 
 pytestmark = pytest.mark.gpu
@@ -192,3 +192,23 @@ def test_qwen_shaped_full_size():
         rows = slice(s * group, (s + 1) * group)
         worst = max(worst, check_rows(got[rows], est.mse_scores(q[rows], idx[sl], n[sl], st.rot, st.c32)))
     _log(f"  worst rel {worst:.2e}")
+
+
+def test_long_pass_ragged_lengths():
+    # MSE-only b = 3 keys through the 4-wave pass of a long call (80 segments
+    # x 24576 tokens, G = 8) with ragged lengths, every valid token against the
+    # oracle's MSE inner product
+    _log("mse keys scores: long pass, ragged lengths (80 x 24576 tokens)")
+    segs, T_, G = 80, 24576, 8
+    x = kv_tensor(1, segs, T_, 128, seed=18)[0].reshape(-1, 128)
+    st = _setup(3, seed=18)
+    cache, idx, n = oracle_mse_key_cache(st, x, T_)
+    q = gaussian_queries(segs * G, 128, seed=18)
+    ln = long_pass_lengths(segs, T_, 18)
+    got = gpu_scores(st, q, segs, G, cache, T_, length=ln)
+    ref = np.empty((segs * G, T_))
+    for s in range(segs):
+        sl = slice(s * T_, (s + 1) * T_)
+        rows = slice(s * G, (s + 1) * G)
+        ref[rows] = est.mse_scores(q[rows], idx[sl], n[sl], st.rot, st.c32)
+    _log(f"  worst rel {check_ragged(got, ref, ln, G):.2e}")

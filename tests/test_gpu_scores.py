@@ -270,6 +270,40 @@ def test_long_pass_two_launches_match_one_launch():
     check_rows(got, _oracle_rows(st, q, fields, segs, G, T_))
 
 
+def long_pass_lengths(segs, T_, seed):
+    """Ragged valid lengths for a long pass: random in [1, T], with an empty
+    segment, a full one and lengths at and around the 4-wave spans' edges."""
+    ln = np.random.default_rng(seed).integers(1, T_ + 1, segs).astype(np.int32)
+    ln[:9] = [0, T_, 1, 1023, 1024, 1025, 2047, 2048, T_ - 1]
+    return ln
+
+
+def check_ragged(got, ref, ln, G):
+    """Rows of segment s checked on t < ln[s] (to 1e-3 of the oracle's row
+    maximum); entries at t >= ln[s] are not written (still NaN)."""
+    worst = 0.0
+    for s, l in enumerate(ln):
+        rows = slice(s * G, (s + 1) * G)
+        assert np.all(np.isnan(got[rows, l:])), f"segment {s}: entries past its length {l} were written"
+        if l:
+            worst = max(worst, check_rows(got[rows, :l], ref[rows, :l]))
+    return worst
+
+
+def test_long_pass_ragged_lengths():
+    # the 4-wave pass of a long call (80 segments x 24576 tokens) with ragged
+    # lengths: every valid token against the oracle, nothing past a length
+    _log("scores: long pass, ragged lengths (80 x 24576 tokens)")
+    segs, T_, G = 80, 24576, 4
+    st = Setup(bits=3, prod=True, seed=17)
+    x = kv_tensor(1, segs, T_, 128, seed=17)[0].reshape(-1, 128)
+    cache, fields = oracle_key_cache(st, x, seg_stride=T_)
+    q = gaussian_queries(segs * G, 128, seed=17)
+    ln = long_pass_lengths(segs, T_, 17)
+    got = gpu_scores(st, q, segs, G, cache, T_, length=ln)
+    _log(f"  worst rel {check_ragged(got, _oracle_rows(st, q, fields, segs, G, T_), ln, G):.2e}")
+
+
 def test_one_launch_graph_replays_see_new_queries():
     # a captured tq_scores replayed with new query values between replays (the
     # same launch, so the same ticket): each replay must use its own pack
