@@ -48,8 +48,8 @@ INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 matrix peak (the retrieval score GE
 # rocprofv3 (FETCH_SIZE and WRITE_SIZE, each in its own run) and scaled by the
 # factor the same counters give for a plain device copy of known size
 # (bench.py --copy-calibration).  Valid only for the decode source measured.
-SCORE_TRAFFIC = {"tq_decode.hip sha256": "6c53085345e8e1eacf29ad8e8fbcd4889f7571ae4b2ab06dadedc4eaf88cf5d1",
-                 "bytes_per_launch": 583437834}
+SCORE_TRAFFIC = {"tq_decode.hip sha256": "6bb25df02d850a4bafb94139d6bcbdddaf1a8bf5f7199f3bd2b2b6aff85382dc",
+                 "bytes_per_launch": 583437629}
 
 D_ = 128
 # Llama-3.1-8B-shaped cache (the headline)

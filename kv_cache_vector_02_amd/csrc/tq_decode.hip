@@ -840,6 +840,17 @@ hipError_t launch_scores_waves(Score128Args& s, int segs, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Segments per query-prep workgroup: one while the segments fit one workgroup
+// per compute unit (more compute units at work: 256 segments of 4 heads,
+// 98.2 us per call against 99.1-99.5 us); beyond that, consecutive segments
+// that share a rotation set fill the products' 16 head columns together (one
+// read of Pi and S per workgroup: 512 segments of 4 heads, a 149.6 us batched
+// step against 152.2 us).
+int prep_segments_per_workgroup(int n_sets, int group, int segs) {
+  if (n_sets > 1 || segs <= device_cus()) return 1;
+  return MAXG / (group > 0 ? group : 1);
+}
+
 // True when the pass takes more than one dispatch of 8-wave workgroups.
 template <int BQ, int MT, int S, bool QJL, int MW>
 bool long_pass(int segs, int64_t T) {
@@ -865,7 +876,7 @@ template <int BQ, int MT, int S, bool HAD, bool QJL = true, int MW = 4>
 hipError_t launch_scores_fused(Score128Args& s, int segs, hipStream_t stream) {
   if (!s.one_launch && long_pass<BQ, MT, S, QJL, MW>(segs, s.T)) {
     PrepArgs p = s.prep;
-    p.seg_per_wg = p.n_sets > 1 ? 1 : MAXG / (p.group > 0 ? p.group : 1);
+    p.seg_per_wg = prep_segments_per_workgroup(p.n_sets, p.group, segs);
     hipLaunchKernelGGL((prep_queries128<HAD, S, QJL, MW>), dim3((unsigned)((segs + p.seg_per_wg - 1) / p.seg_per_wg)),
                        dim3(PREP_THREADS), 0, stream, p);
     const hipError_t e = hipGetLastError();
@@ -1025,9 +1036,7 @@ static PrepArgs make_prep(const ScoreArgs& a, int slices) {
 
 hipError_t launch_scores128_prep(const ScoreArgs& a, int slices, hipStream_t stream) {
   PrepArgs p = make_prep(a, slices);
-  // consecutive segments that share a rotation set fill the products' 16 head
-  // columns together (one read of Pi and S per workgroup)
-  p.seg_per_wg = p.n_sets > 1 ? 1 : MAXG / (a.group > 0 ? a.group : 1);
+  p.seg_per_wg = prep_segments_per_workgroup(p.n_sets, a.group, a.segs);
   const bool had = a.rot == TQ_ROT_HADAMARD;
   const dim3 grid((a.segs + p.seg_per_wg - 1) / p.seg_per_wg), block(PREP_THREADS);
   if (a.qjl && a.m == D / 2) {
